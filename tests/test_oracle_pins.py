@@ -1,0 +1,280 @@
+"""Pins for the fp64 oracle, each against something other than the oracle's
+own formula: the bucket structure the pages describe, a hand-worked example,
+textbook recurrences and matrix products, and the recurrent (decode) form.
+
+Pages: "Log-Linear Attention" summaries (pt and fr, gist.science 2506.04761).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _rand_inputs(rng, B, H, T, dk, dv, L, a_scale=0.3):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    a = -np.abs(rng.standard_normal((B, H, T))) * a_scale
+    lam = rng.random((B, H, T, L))
+    return q, k, v, a, lam
+
+
+def _L(T):
+    return 1 if T <= 1 else 1 + (T - 1).bit_length()
+
+
+# --- level function: the Fenwick buckets (pt §2 "Particionamento Hierárquico",
+# fr §2 "Partitionnement par Arbre de Fenwick"): sizes 1, 2, 4, 8, ...; recent
+# tokens in small buckets; O(log T) buckets per position. ----------------------
+
+def test_level_buckets_partition_prefix(oracle_mod):
+    for t in range(0, 300):
+        buckets = {}
+        for s in range(t + 1):
+            buckets.setdefault(oracle_mod.level(t, s), []).append(s)
+        assert buckets[0] == [t]
+        covered = []
+        # walk from the finest (rightmost) bucket to the coarsest
+        right_edge = t  # exclusive upper end for the next-coarser bucket
+        for lev in sorted(buckets):
+            members = buckets[lev]
+            assert members == list(range(members[0], members[-1] + 1)), "bucket not contiguous"
+            if lev == 0:
+                continue
+            assert (t >> (lev - 1)) & 1 == 1, "non-empty bucket on a clear bit"
+            assert len(members) == 2 ** (lev - 1), "bucket size is not 2^(l-1)"
+            assert members[-1] == right_edge - 1, "buckets not ordered finer-to-the-right"
+            right_edge = members[0]
+            covered += members
+        assert right_edge == 0 or t == 0
+        assert sorted(covered + [t]) == list(range(t + 1))
+        # number of non-empty buckets = 1 + popcount(t) <= 1 + ceil(log2(t+1))
+        assert len(buckets) == 1 + bin(t).count("1")
+
+
+def test_level_hand_examples(oracle_mod):
+    lv = oracle_mod.level
+    # t = 3: {3} level 0, {2} level 1, {0,1} level 2
+    assert [lv(3, s) for s in range(4)] == [2, 2, 1, 0]
+    # t = 6: {6} level 0, level 1 empty, {4,5} level 2, {0..3} level 3
+    assert [lv(6, s) for s in range(7)] == [3, 3, 3, 3, 2, 2, 0]
+    # large positions: top level is the bit length of t XOR s
+    assert lv(1 << 20, 0) == 21
+    assert lv((1 << 20) + 5, (1 << 20) + 4) == 1
+
+
+# --- hand-worked example ------------------------------------------------------
+
+def test_hand_example_forward(oracle_mod):
+    g = json.load(open(os.path.join(HERE, "golden", "hand_T4.json")))
+    T = 4
+    q = np.array(g["q"]).reshape(1, 1, T, 1)
+    k = np.array(g["k"]).reshape(1, 1, T, 1)
+    v = np.array(g["v"]).reshape(1, 1, T, 2)
+    a = np.array(g["a"]).reshape(1, 1, T)
+    lam = np.array(g["lam"]).reshape(1, 1, T, 3)
+    o = oracle_mod.fwd(q, k, v, a, lam)[0, 0]
+    np.testing.assert_allclose(o, np.array(g["expected_o"]), rtol=1e-13, atol=1e-13)
+    # the recurrent form gives the same rows
+    o2 = oracle_mod.decode_sequence(q, k, v, a, lam)[0, 0]
+    np.testing.assert_allclose(o2, np.array(g["expected_o"]), rtol=1e-13, atol=1e-13)
+
+
+def test_hand_example_decode_stack(oracle_mod):
+    g = json.load(open(os.path.join(HERE, "golden", "hand_T4.json")))
+    T, Lcap = 4, 3
+    q = np.array(g["q"]).reshape(T, 1)
+    k = np.array(g["k"]).reshape(T, 1)
+    v = np.array(g["v"]).reshape(T, 2)
+    a = np.array(g["a"])
+    lam = np.array(g["lam"])
+    state = np.zeros((1, 1, Lcap, 1, 2))
+    logscale = np.zeros((1, 1, Lcap))
+    for t in range(T):
+        o, state, occ = oracle_mod.decode_step(
+            state, logscale, np.array([t]), q[t].reshape(1, 1, 1), k[t].reshape(1, 1, 1),
+            v[t].reshape(1, 1, 2), a[t].reshape(1, 1), lam[t].reshape(1, 1, Lcap))
+        np.testing.assert_allclose(o[0, 0], g["expected_o"][t], rtol=1e-13, atol=1e-13)
+    assert occ[0].tolist() == [True, True, True]
+    for slot, want in g["expected_stack_after_t3"].items():
+        np.testing.assert_allclose(state[0, 0, int(slot)], np.array(want), rtol=1e-13, atol=1e-15)
+
+
+# --- reductions to textbook operators -----------------------------------------
+
+def test_lambda_one_is_mamba2_recurrence(oracle_mod):
+    """lambda == 1 removes the hierarchy: decayed linear attention, whose
+    scalar recurrence is S_t = exp(a_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t."""
+    rng = np.random.default_rng(1)
+    B, H, T, dk, dv = 1, 2, 45, 5, 3
+    q, k, v, a, _ = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    lam = np.ones((B, H, T, _L(T)))
+    o = oracle_mod.fwd(q, k, v, a, lam)
+    ref = np.zeros_like(o)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((dk, dv))
+            for t in range(T):
+                S = np.exp(a[b, h, t]) * S + np.outer(k[b, h, t], v[b, h, t])
+                ref[b, h, t] = q[b, h, t] @ S
+    np.testing.assert_allclose(o, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_lambda_onehot_level0_is_diagonal(oracle_mod):
+    rng = np.random.default_rng(2)
+    B, H, T, dk, dv = 1, 1, 33, 4, 6
+    q, k, v, a, _ = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    lam = np.zeros((B, H, T, _L(T)))
+    lam[..., 0] = 1.0
+    o = oracle_mod.fwd(q, k, v, a, lam)
+    ref = np.sum(q * k, axis=-1)[..., None] * v
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_no_decay_unit_lambda_is_causal_linear_attention(oracle_mod):
+    """a == 0 and lambda == 1: O = tril(Q K^T) V, a plain matrix product."""
+    rng = np.random.default_rng(3)
+    B, H, T, dk, dv = 2, 1, 40, 7, 3
+    q, k, v, _, _ = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    a = np.zeros((B, H, T))
+    lam = np.ones((B, H, T, _L(T)))
+    o = oracle_mod.fwd(q, k, v, a, lam)
+    for b in range(B):
+        ref = np.tril(q[b, 0] @ k[b, 0].T) @ v[b, 0]
+        np.testing.assert_allclose(o[b, 0], ref, rtol=1e-11, atol=1e-11)
+
+
+def test_onehot_level_reads_only_its_bucket(oracle_mod):
+    """With lambda = one-hot(l), row t sums exactly the keys of bucket l,
+    built here from t's binary digits: [(t>>l)<<l, (t>>l)<<l + 2^(l-1)) when
+    bit l-1 of t is set.  Summing over l recovers the full lambda (linearity)."""
+    rng = np.random.default_rng(4)
+    B, H, T, dk, dv = 1, 1, 70, 3, 2
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, L)
+    total = np.zeros((B, H, T, dv))
+    for lev in range(L):
+        lam1 = np.zeros_like(lam)
+        lam1[..., lev] = lam[..., lev]
+        o = oracle_mod.fwd(q, k, v, a, lam1)
+        total += o
+        ref = np.zeros((T, dv))
+        for t in range(T):
+            if lev == 0:
+                members = [t]
+            elif (t >> (lev - 1)) & 1:
+                lo = (t >> lev) << lev
+                members = range(lo, lo + 2 ** (lev - 1))
+            else:
+                members = []
+            for s in members:
+                decay = np.exp(np.sum(a[0, 0, s + 1:t + 1]))
+                ref[t] += decay * lam[0, 0, t, lev] * (q[0, 0, t] @ k[0, 0, s]) * v[0, 0, s]
+        np.testing.assert_allclose(o[0, 0], ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(total, oracle_mod.fwd(q, k, v, a, lam), rtol=1e-11, atol=1e-12)
+
+
+def test_prefix_consistency(oracle_mod):
+    rng = np.random.default_rng(5)
+    B, H, T, dk, dv = 1, 2, 50, 4, 4
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    full = oracle_mod.fwd(q, k, v, a, lam)
+    for Tp in (1, 7, 32, 33):
+        Lp = _L(Tp)
+        part = oracle_mod.fwd(q[:, :, :Tp], k[:, :, :Tp], v[:, :, :Tp], a[:, :, :Tp], lam[:, :, :Tp, :Lp])
+        np.testing.assert_allclose(part, full[:, :, :Tp], rtol=1e-13, atol=1e-13)
+
+
+def test_rows_match_full(oracle_mod):
+    rng = np.random.default_rng(6)
+    B, H, T, dk, dv = 2, 2, 64, 8, 4
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    full = oracle_mod.fwd(q, k, v, a, lam)
+    rows = np.array([[0, 0], [1, 63], [3, 17], [2, 32]])
+    got = oracle_mod.fwd_rows(q, k, v, a, lam, rows)
+    for i, (bh, t) in enumerate(rows):
+        np.testing.assert_array_equal(got[i], full.reshape(B * H, T, dv)[bh, t])
+
+
+def test_too_narrow_lambda_is_an_error(oracle_mod):
+    rng = np.random.default_rng(7)
+    q, k, v, a, lam = _rand_inputs(rng, 1, 1, 9, 2, 2, 4)
+    with pytest.raises(ValueError):
+        oracle_mod.fwd(q, k, v, a, lam[..., :3])
+
+
+# --- forward (O(T^2) sum) versus the recurrent decode form ----------------------
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16, 37, 64])
+def test_forward_equals_serial_fenwick_recurrence(oracle_mod, T):
+    rng = np.random.default_rng(10 + T)
+    B, H, dk, dv = 1, 2, 5, 3
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, _L(T))
+    o1 = oracle_mod.fwd(q, k, v, a, lam)
+    o2 = oracle_mod.decode_sequence(q, k, v, a, lam)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-12)
+
+
+def test_decode_stack_holds_decayed_bucket_sums(oracle_mod):
+    """After step t, slot l holds sum over bucket l of t of
+    exp(sum_{r=s+1..t} a_r) k_s v_s^T (bucket built from t's digits)."""
+    rng = np.random.default_rng(20)
+    T, dk, dv, Lcap = 37, 3, 2, 7
+    q, k, v, a, lam = _rand_inputs(rng, 1, 1, T, dk, dv, Lcap)
+    q, k, v, a, lam = q[0, 0], k[0, 0], v[0, 0], a[0, 0], lam[0, 0]
+    state = np.zeros((1, 1, Lcap, dk, dv))
+    logscale = np.zeros((1, 1, Lcap))
+    for t in range(T):
+        _, state, occ = oracle_mod.decode_step(
+            state, logscale, np.array([t]), q[t][None, None], k[t][None, None], v[t][None, None],
+            a[t].reshape(1, 1), lam[t][None, None])
+        for lev in range(Lcap):
+            if lev == 0:
+                members = [t]
+            elif (t >> (lev - 1)) & 1:
+                lo = (t >> lev) << lev
+                members = list(range(lo, lo + 2 ** (lev - 1)))
+            else:
+                members = []
+            assert occ[0, lev] == bool(members)
+            want = np.zeros((dk, dv))
+            for s in members:
+                want += np.exp(np.sum(a[s + 1:t + 1])) * np.outer(k[s], v[s])
+            np.testing.assert_allclose(state[0, 0, lev], want, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_uses_logscale(oracle_mod):
+    """A stored pair (hat S, g) is the state exp(g) hat S: scaling hat S by
+    e^c and g by -c changes nothing."""
+    rng = np.random.default_rng(21)
+    S, H, Lcap, dk, dv = 3, 2, 6, 4, 3
+    state = rng.standard_normal((S, H, Lcap, dk, dv))
+    logscale = rng.standard_normal((S, H, Lcap)) * 0.5
+    pos = np.array([5, 12, 31])
+    q = rng.standard_normal((S, H, dk)); k = rng.standard_normal((S, H, dk))
+    v = rng.standard_normal((S, H, dv)); a = -np.abs(rng.standard_normal((S, H)))
+    lam = rng.random((S, H, Lcap))
+    o1, n1, _ = oracle_mod.decode_step(state, logscale, pos, q, k, v, a, lam)
+    c = rng.standard_normal((S, H, Lcap))
+    o2, n2, _ = oracle_mod.decode_step(state * np.exp(c)[..., None, None], logscale - c, pos, q, k, v, a, lam)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(n1, n2, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_out_of_range_position(oracle_mod):
+    rng = np.random.default_rng(22)
+    S, H, Lcap, dk, dv = 2, 1, 4, 2, 2
+    state = rng.standard_normal((S, H, Lcap, dk, dv))
+    logscale = np.zeros((S, H, Lcap))
+    pos = np.array([8, 3])  # 8 >= 2^(Lcap-1) is out of range
+    q = rng.standard_normal((S, H, dk)); k = rng.standard_normal((S, H, dk))
+    v = rng.standard_normal((S, H, dv)); a = -np.abs(rng.standard_normal((S, H)))
+    lam = rng.random((S, H, Lcap))
+    o, new, _ = oracle_mod.decode_step(state, logscale, pos, q, k, v, a, lam)
+    assert np.all(np.isnan(o[0])) and np.all(np.isfinite(o[1]))
+    for l in oracle_mod.occupied(7, Lcap):
+        np.testing.assert_array_equal(new[0, 0, l], state[0, 0, l])
