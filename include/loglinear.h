@@ -1,0 +1,165 @@
+/*
+ * loglinear.h — C ABI of the MI355X (gfx950) log-linear attention library.
+ *
+ * The operation.  Log-linear attention in its Mamba-2 form.  For every batch
+ * b, head h and position t (0-indexed):
+ *
+ *   o[t,:] = sum_{s <= t} exp(sum_{r=s+1..t} a[r]) * lambda[t, level(t,s)]
+ *                         * (q[t,:] . k[s,:]) * v[s,:]
+ *   level(t,s) = 0 if s == t, else bit_length(t XOR s)
+ *
+ * This is O = (Q K^T ⊙ M_H) V with a hierarchical mask M_H ("Log-Linear
+ * Attention" summary page, French, §2 "Matrice de Masque Hiérarchique";
+ * Portuguese page §2 "Máscara Hierárquica"), whose levels are the Fenwick-tree
+ * buckets of sizes 1, 2, 4, 8, ... of the prefix (Portuguese page §2
+ * "Particionamento Hierárquico"), each level weighted by a per-token,
+ * data-dependent lambda_t^(l) (French page §2), composed with Mamba-2's
+ * decay exp(sum a) (both pages: Mamba-2 is one of the two instances built).
+ * The forward is the chunkwise parallel form, O(T log T) (Portuguese page
+ * §2 "Forma Recorrente e Paralela", training bullet); the decode step is the
+ * recurrent form over O(log T) states (same section, decoding bullet; French
+ * page §2 "Algorithmes Efficaces").
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *    tensors), contiguous and row-major.  q, k, v, out and state must be
+ *    16-byte aligned, the workspace 256-byte aligned, pos 8-byte aligned and
+ *    the float32 vectors (a, lambda, logscale) 4-byte aligned.  Host pointers
+ *    are an error the library cannot detect; the kernels would fault.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream); nothing is synchronised.  Results are visible after the caller
+ *    synchronises that stream.  A kernel fault surfaces at that sync.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates or frees device memory in these calls and keeps no pointer
+ *    after returning.  Inputs are never written.
+ *  - Errors: validation happens on the host before any launch; a non-zero
+ *    status is returned and a message is available from loglinear_last_error()
+ *    (thread-local).  No call aborts, throws across the ABI or prints.
+ *  - Zero-sized problems (B, H, T or S equal to 0) are valid and launch nothing.
+ */
+#ifndef LOGLINEAR_H
+#define LOGLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LL_OK = 0,
+    LL_EINVAL = -1,       /* null/misaligned pointer, negative size, bad dtype  */
+    LL_EUNSUPPORTED = -2, /* valid request outside the compiled shape set       */
+    LL_EDEVICE = -3,      /* a HIP launch or runtime call failed                */
+    LL_EWORKSPACE = -4    /* workspace missing or smaller than required         */
+} ll_status;
+
+typedef enum {
+    LL_F32 = 0, /* q, k, v, out are float32                                  */
+    LL_BF16 = 1 /* q, k, v, out are bfloat16; accumulation is float32        */
+} ll_dtype;
+
+/* Number of lambda entries per token for a sequence of T tokens:
+ * 1 + ceil(log2 T) (1 for T <= 1): level 0 plus one per possible bucket.
+ * Returns -1 for T < 0. */
+int loglinear_num_levels(int64_t T);
+
+/* Bytes of device workspace loglinear_fwd needs for this shape (0 when no
+ * workspace is needed).  Depends only on the arguments.  Returns 0 for
+ * invalid or unsupported shapes (loglinear_fwd reports those). */
+size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+
+/* Forward pass (chunkwise parallel form).
+ *  q      [B,H,T,dk]  dtype
+ *  k      [B,H,T,dk]  dtype
+ *  v      [B,H,T,dv]  dtype
+ *  a      [B,H,T]     float32, per-token log-decay (a[...,0] never enters;
+ *                     values are expected <= 0 as in Mamba-2)
+ *  lambda [B,H,T,L]   float32, L = loglinear_num_levels(T); entries for
+ *                     levels that are empty for a row are ignored
+ *  out    [B,H,T,dv]  dtype, written; must not alias any input
+ *  chunk  tokens per chunk: 16, 32 or 64.  The result does not depend on it
+ *         beyond rounding.  T need not be a multiple of chunk.
+ *  workspace / workspace_bytes: caller-owned device scratch of at least
+ *         loglinear_fwd_workspace_bytes(...) bytes (may be NULL when that is
+ *         0).  Its contents on entry do not matter and are clobbered.
+ * Supported: dtype F32 with dk, dv in {16, 32, 64, 128}; dtype BF16 with
+ * dk in {32, 64, 128} and dv in {16, 32, 64, 128}; T < 2^31.  Anything else
+ * returns LL_EUNSUPPORTED.
+ * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
+ll_status loglinear_fwd(const void *q, const void *k, const void *v,
+                        const float *a, const float *lambda, void *out,
+                        int B, int H, int T, int dk, int dv, int chunk,
+                        ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Same as loglinear_fwd / loglinear_fwd_workspace_bytes with an explicit
+ * group size: the chunk walk carries the levels inside groups of
+ * 2^group_log2 consecutive chunks in registers and reads coarser levels from
+ * the workspace.  group_log2 < 0 selects automatically (what the plain calls
+ * do); values above 3 return LL_EUNSUPPORTED.  The result does not depend on
+ * it beyond rounding; it exists for tuning and for tests.  The workspace
+ * size must be queried with the same group_log2. */
+size_t loglinear_fwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int chunk, int group_log2);
+ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v,
+                           const float *a, const float *lambda, void *out,
+                           int B, int H, int T, int dk, int dv, int chunk,
+                           ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                           void *stream, int group_log2);
+
+/* One decode step for S sequences x H heads (the recurrent form).
+ * Stack convention: for a sequence whose previous token sat at position p,
+ * slot 0 holds that token's own state k v^T and slot l >= 1 holds the
+ * level-l bucket state iff bit l-1 of p is set (Fenwick occupancy); other
+ * slots are free and never read.  A slot stores (hat S, g) meaning the state
+ * exp(g) * hat S, so buckets that only decay are never rewritten.
+ *  q, k   [S,H,dk]          dtype, the new token
+ *  v      [S,H,dv]          dtype
+ *  a      [S,H]             float32 log-decay of the new token
+ *  lambda [S,H,Lcap]        float32 per-level weights of the new token
+ *  state  [S,H,Lcap,dk,dv]  float32 hat S, updated in place
+ *  logscale [S,H,Lcap]      float32 g, updated in place
+ *  pos    [S]               int64, 0-indexed position of the new token
+ *                           (read only; the caller advances it).  pos == 0
+ *                           means the stack is empty.
+ *  out    [S,H,dv]          dtype, written
+ * The step merges the levels below the lowest set bit of pos into one
+ * bucket, puts the new token in slot 0, and reads out
+ * o = sum over occupied levels l of lambda[l] * q^T S_l.
+ * A position outside [0, 2^(Lcap-1)) cannot be represented: that sequence
+ * gets NaN outputs and its stack is left unchanged (checked on the device,
+ * since pos lives there).
+ * Supported: dk, dv in {16, 32, 64, 128}, 2 <= Lcap <= 32, both dtypes.
+ * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EDEVICE. */
+ll_status loglinear_decode_step(const void *q, const void *k, const void *v,
+                                const float *a, const float *lambda,
+                                float *state, float *logscale, const int64_t *pos,
+                                void *out, int S, int H, int dk, int dv, int Lcap,
+                                ll_dtype dtype, void *stream);
+
+/* Message for the last failing call on this thread ("" if none).  Valid
+ * until the next call into the library on the same thread. */
+const char *loglinear_last_error(void);
+
+/* ---- measurement support -------------------------------------------------
+ * While profiling is on, every kernel the library launches is bracketed by a
+ * pair of HIP events recorded on the launch stream (no synchronisation).
+ * loglinear_profile_end synchronises those events and returns, per kernel
+ * name, the number of launches and the summed device time.  Process-wide
+ * state, not thread-safe; meant for benchmarks.  Creating the event pool in
+ * loglinear_profile_begin may allocate host/driver resources. */
+typedef struct {
+    char name[48];
+    int launches;
+    double total_ms;
+} ll_kernel_stat;
+
+ll_status loglinear_profile_begin(int max_launches);
+ll_status loglinear_profile_end(ll_kernel_stat *stats, int max_stats, int *n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGLINEAR_H */

@@ -1,0 +1,187 @@
+"""Python binding of libloglinear.so (gfx950 log-linear attention).
+
+Argument marshalling only: every step of the forward and the decode runs in
+the library's HIP kernels.  torch is used for device memory and streams; the
+functions take torch CUDA tensors, check dtype/device/contiguity, and pass raw
+pointers.  If the library has not been built this module raises on first use;
+there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloglinear.so")
+
+LL_OK, LL_EINVAL, LL_EUNSUPPORTED, LL_EDEVICE, LL_EWORKSPACE = 0, -1, -2, -3, -4
+LL_F32, LL_BF16 = 0, 1
+
+_STATUS_NAMES = {
+    LL_EINVAL: "LL_EINVAL",
+    LL_EUNSUPPORTED: "LL_EUNSUPPORTED",
+    LL_EDEVICE: "LL_EDEVICE",
+    LL_EWORKSPACE: "LL_EWORKSPACE",
+}
+
+
+class LLError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (loads it on first call)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m log_linear_attention_amd.build`"
+            )
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_int64
+        L.loglinear_num_levels.argtypes = [I64]
+        L.loglinear_num_levels.restype = I
+        L.loglinear_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.loglinear_fwd_workspace_bytes.restype = Z
+        L.loglinear_fwd_workspace_bytes_ex.argtypes = [I, I, I, I, I, I, I]
+        L.loglinear_fwd_workspace_bytes_ex.restype = Z
+        L.loglinear_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+        L.loglinear_fwd.restype = I
+        L.loglinear_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P, I]
+        L.loglinear_fwd_ex.restype = I
+        L.loglinear_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+        L.loglinear_decode_step.restype = I
+        L.loglinear_last_error.argtypes = []
+        L.loglinear_last_error.restype = ctypes.c_char_p
+        L.loglinear_profile_begin.argtypes = [I]
+        L.loglinear_profile_begin.restype = I
+        L.loglinear_profile_end.argtypes = [ctypes.POINTER(KernelStat), I, ctypes.POINTER(I)]
+        L.loglinear_profile_end.restype = I
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().loglinear_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != LL_OK:
+        raise LLError(status, last_error())
+
+
+def num_levels(T: int) -> int:
+    return int(lib().loglinear_num_levels(int(T)))
+
+
+def fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int, group_log2: int = -1) -> int:
+    return int(lib().loglinear_fwd_workspace_bytes_ex(B, H, T, dk, dv, chunk, group_log2))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LL_F32
+    if t.dtype == torch.bfloat16:
+        return LL_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def alloc_workspace(B, H, T, dk, dv, chunk, group_log2=-1, device="cuda") -> torch.Tensor | None:
+    n = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: int = -1, stream=None):
+    """Forward pass.  q,k [B,H,T,dk], v [B,H,T,dv] (float32 or bfloat16, same
+    dtype), a [B,H,T] float32, lam [B,H,T,L] float32 with L = num_levels(T).
+    Returns out [B,H,T,dv] in the input dtype.  Asynchronous on ``stream``."""
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    L = num_levels(T)
+    if tuple(a.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
+        raise ValueError(f"a must be [B,H,T] and lam [B,H,T,{L}]")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, H, T, dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    need = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().loglinear_fwd_ex(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+        _dev(out, "out"), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    _check(st)
+    return out
+
+
+def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
+    """One decode step.  q,k [S,H,dk], v [S,H,dv] (float32 or bfloat16),
+    a [S,H], lam [S,H,Lcap], state [S,H,Lcap,dk,dv] and logscale [S,H,Lcap]
+    float32 (updated in place), pos [S] int64.  Returns out [S,H,dv]."""
+    S, H, dk = q.shape
+    dv = v.shape[-1]
+    Lcap = state.shape[2]
+    code = _dtype_code(q)
+    if tuple(state.shape) != (S, H, Lcap, dk, dv) or tuple(logscale.shape) != (S, H, Lcap):
+        raise ValueError("state must be [S,H,Lcap,dk,dv] and logscale [S,H,Lcap]")
+    if tuple(lam.shape) != (S, H, Lcap) or tuple(a.shape) != (S, H) or tuple(pos.shape) != (S,):
+        raise ValueError("lam must be [S,H,Lcap], a [S,H], pos [S]")
+    if out is None:
+        out = torch.empty((S, H, dv), dtype=q.dtype, device=q.device)
+    st = lib().loglinear_decode_step(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+        _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
+        _dev(pos, "pos", torch.int64), _dev(out, "out"), S, H, dk, dv, Lcap, code, _stream(stream))
+    _check(st)
+    return out
+
+
+def profile_begin(max_launches: int = 4096) -> None:
+    _check(lib().loglinear_profile_begin(max_launches))
+
+
+def profile_end() -> dict:
+    """Per-kernel {name: (launches, total_ms)} for launches since profile_begin."""
+    arr = (KernelStat * 64)()
+    n = ctypes.c_int(0)
+    _check(lib().loglinear_profile_end(arr, 64, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}

@@ -1,0 +1,310 @@
+// C ABI of the log-linear attention library: argument validation, error
+// reporting, dispatch to the gfx950 kernels and optional launch profiling.
+// Validation runs entirely on the host and makes no HIP call, so every error
+// path can be exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/loglinear.h"
+#include "ll_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ll_status fail(ll_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+ll_status ok()
+{
+    g_err.clear();
+    return LL_OK;
+}
+
+bool aligned(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+int levels_for(int64_t T)
+{
+    if (T <= 1)
+        return 1;
+    int n = 0;
+    for (int64_t x = T - 1; x > 0; x >>= 1)
+        ++n;
+    return 1 + n;
+}
+
+// ---- profiling -------------------------------------------------------------
+struct ProfRecord {
+    const char *name;
+    hipEvent_t start, stop;
+};
+
+struct Profiler {
+    bool on = false;
+    int used = 0;
+    bool overflow = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<ProfRecord> recs;
+    const char *pending = nullptr;
+};
+
+Profiler g_prof;
+
+}  // namespace
+
+namespace ll {
+
+void prof_before(const char *name, hipStream_t s)
+{
+    if (!g_prof.on)
+        return;
+    if (g_prof.used + 2 > (int)g_prof.pool.size()) {
+        g_prof.overflow = true;
+        g_prof.pending = nullptr;
+        return;
+    }
+    ProfRecord r{name, g_prof.pool[g_prof.used], g_prof.pool[g_prof.used + 1]};
+    g_prof.used += 2;
+    (void)hipEventRecord(r.start, s);
+    g_prof.recs.push_back(r);
+    g_prof.pending = name;
+}
+
+void prof_after(hipStream_t s)
+{
+    if (!g_prof.on || !g_prof.pending)
+        return;
+    (void)hipEventRecord(g_prof.recs.back().stop, s);
+    g_prof.pending = nullptr;
+}
+
+}  // namespace ll
+
+extern "C" {
+
+int loglinear_num_levels(int64_t T)
+{
+    if (T < 0)
+        return -1;
+    return levels_for(T);
+}
+
+static ll_status check_fwd_shape(int B, int H, int T, int dk, int dv, int chunk)
+{
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0)
+        return fail(LL_EINVAL, "loglinear_fwd: negative or zero size (B=%d H=%d T=%d dk=%d dv=%d)", B, H, T, dk, dv);
+    if (chunk != 16 && chunk != 32 && chunk != 64)
+        return fail(LL_EUNSUPPORTED, "loglinear_fwd: chunk must be 16, 32 or 64 (got %d)", chunk);
+    const int64_t BH = (int64_t)B * H;
+    if (BH * ((int64_t)T / chunk + 1) > INT_MAX)
+        return fail(LL_EUNSUPPORTED, "loglinear_fwd: B*H*T/chunk too large for one launch");
+    return LL_OK;
+}
+
+size_t loglinear_fwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int chunk, int group_log2)
+{
+    if (check_fwd_shape(B, H, T, dk, dv, chunk) != LL_OK)
+        return 0;
+    if ((int64_t)B * H * T == 0)
+        return 0;
+    return ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4).bytes;
+}
+
+size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
+{
+    return loglinear_fwd_workspace_bytes_ex(B, H, T, dk, dv, chunk, -1);
+}
+
+ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                           void *out, int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                           void *workspace, size_t workspace_bytes, void *stream, int group_log2)
+{
+    if (dtype != LL_F32 && dtype != LL_BF16)
+        return fail(LL_EINVAL, "loglinear_fwd: unknown dtype %d", (int)dtype);
+    ll_status st = check_fwd_shape(B, H, T, dk, dv, chunk);
+    if (st != LL_OK)
+        return st;
+    if (group_log2 > ll::kMaxGroupLog2)
+        return fail(LL_EUNSUPPORTED, "loglinear_fwd: group_log2 %d above %d", group_log2, ll::kMaxGroupLog2);
+    const bool bf16 = dtype == LL_BF16;
+    if (!ll::fwd_supported(bf16, dk, dv, chunk))
+        return fail(LL_EUNSUPPORTED, "loglinear_fwd: no kernel for dtype=%s dk=%d dv=%d chunk=%d",
+                    bf16 ? "bf16" : "f32", dk, dv, chunk);
+    const int64_t rows = (int64_t)B * H * T;
+    if (rows == 0)
+        return ok();
+    const size_t es = bf16 ? 2 : 4;
+    const size_t nq = (size_t)rows * dk * es, nv = (size_t)rows * dv * es;
+    const void *ptrs[] = {q, k, v, out};
+    const char *names[] = {"q", "k", "v", "out"};
+    for (int i = 0; i < 4; ++i) {
+        if (!ptrs[i])
+            return fail(LL_EINVAL, "loglinear_fwd: %s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16))
+            return fail(LL_EINVAL, "loglinear_fwd: %s is not 16-byte aligned", names[i]);
+    }
+    if (!a || !lambda)
+        return fail(LL_EINVAL, "loglinear_fwd: %s is NULL", !a ? "a" : "lambda");
+    if (!aligned(a, 4) || !aligned(lambda, 4))
+        return fail(LL_EINVAL, "loglinear_fwd: a and lambda must be 4-byte aligned");
+    const int L = levels_for(T);
+    if (L > ll::kMaxLevels)
+        return fail(LL_EUNSUPPORTED, "loglinear_fwd: T=%d needs %d levels (max %d)", T, L, ll::kMaxLevels);
+    const size_t na = (size_t)rows * 4, nl = (size_t)rows * L * 4;
+    if (overlaps(out, nv, q, nq) || overlaps(out, nv, k, nq) || overlaps(out, nv, v, nv) ||
+        overlaps(out, nv, a, na) || overlaps(out, nv, lambda, nl))
+        return fail(LL_EINVAL, "loglinear_fwd: out aliases an input");
+    const ll::FwdPlan plan = ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4);
+    if (plan.bytes > 0) {
+        if (!workspace)
+            return fail(LL_EWORKSPACE, "loglinear_fwd: workspace of %zu bytes required, got NULL", plan.bytes);
+        if (workspace_bytes < plan.bytes)
+            return fail(LL_EWORKSPACE, "loglinear_fwd: workspace of %zu bytes required, got %zu", plan.bytes,
+                        workspace_bytes);
+        if (!aligned(workspace, 256))
+            return fail(LL_EINVAL, "loglinear_fwd: workspace must be 256-byte aligned");
+        if (overlaps(workspace, plan.bytes, out, nv) || overlaps(workspace, plan.bytes, q, nq) ||
+            overlaps(workspace, plan.bytes, k, nq) || overlaps(workspace, plan.bytes, v, nv))
+            return fail(LL_EINVAL, "loglinear_fwd: workspace aliases an input or the output");
+    }
+    ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
+    hipError_t e = ll::fwd_launch(args, plan, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(LL_EDEVICE, "loglinear_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float *a, const float *lambda, void *out,
+                        int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    return loglinear_fwd_ex(q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
+                            stream, -1);
+}
+
+ll_status loglinear_decode_step(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                                float *state, float *logscale, const int64_t *pos, void *out, int S, int H, int dk,
+                                int dv, int Lcap, ll_dtype dtype, void *stream)
+{
+    if (dtype != LL_F32 && dtype != LL_BF16)
+        return fail(LL_EINVAL, "loglinear_decode_step: unknown dtype %d", (int)dtype);
+    if (S < 0 || H < 0 || dk <= 0 || dv <= 0)
+        return fail(LL_EINVAL, "loglinear_decode_step: bad size (S=%d H=%d dk=%d dv=%d)", S, H, dk, dv);
+    if (Lcap < 1)
+        return fail(LL_EINVAL, "loglinear_decode_step: Lcap must be >= 1 (got %d)", Lcap);
+    if (Lcap < 2 || Lcap > ll::kMaxLevels)
+        return fail(LL_EUNSUPPORTED, "loglinear_decode_step: Lcap must be in [2, %d] (got %d)", ll::kMaxLevels, Lcap);
+    const bool bf16 = dtype == LL_BF16;
+    if (!ll::decode_supported(bf16, dk, dv))
+        return fail(LL_EUNSUPPORTED, "loglinear_decode_step: no kernel for dk=%d dv=%d", dk, dv);
+    if ((int64_t)S * H > INT_MAX)
+        return fail(LL_EUNSUPPORTED, "loglinear_decode_step: S*H too large");
+    if ((int64_t)S * H == 0)
+        return ok();
+    const void *ptrs[] = {q, k, v, out, state};
+    const char *names[] = {"q", "k", "v", "out", "state"};
+    for (int i = 0; i < 5; ++i) {
+        if (!ptrs[i])
+            return fail(LL_EINVAL, "loglinear_decode_step: %s is NULL", names[i]);
+        if (!aligned(ptrs[i], 16))
+            return fail(LL_EINVAL, "loglinear_decode_step: %s is not 16-byte aligned", names[i]);
+    }
+    if (!a || !lambda || !logscale || !pos)
+        return fail(LL_EINVAL, "loglinear_decode_step: a, lambda, logscale and pos must be non-NULL");
+    if (!aligned(a, 4) || !aligned(lambda, 4) || !aligned(logscale, 4) || !aligned(pos, 8))
+        return fail(LL_EINVAL, "loglinear_decode_step: misaligned a/lambda/logscale/pos");
+    const size_t sh = (size_t)S * H;
+    const size_t es = bf16 ? 2 : 4;
+    const size_t nst = sh * Lcap * dk * dv * 4, nout = sh * dv * es;
+    if (overlaps(state, nst, out, nout) || overlaps(state, nst, logscale, sh * Lcap * 4) ||
+        overlaps(out, nout, q, sh * dk * es) || overlaps(out, nout, k, sh * dk * es) ||
+        overlaps(out, nout, v, nout) || overlaps(out, nout, logscale, sh * Lcap * 4))
+        return fail(LL_EINVAL, "loglinear_decode_step: state, logscale and out must not alias each other or inputs");
+    ll::DecodeArgs args{q, k, v, a, lambda, state, logscale, pos, out, S, H, dk, dv, Lcap, bf16};
+    hipError_t e = ll::decode_launch(args, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(LL_EDEVICE, "loglinear_decode_step: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+const char *loglinear_last_error(void) { return g_err.c_str(); }
+
+ll_status loglinear_profile_begin(int max_launches)
+{
+    if (max_launches <= 0)
+        return fail(LL_EINVAL, "loglinear_profile_begin: max_launches must be positive");
+    for (hipEvent_t e : g_prof.pool)
+        (void)hipEventDestroy(e);
+    g_prof = Profiler();
+    g_prof.pool.resize(2 * (size_t)max_launches);
+    for (size_t i = 0; i < g_prof.pool.size(); ++i) {
+        hipError_t e = hipEventCreate(&g_prof.pool[i]);
+        if (e != hipSuccess) {
+            g_prof.pool.resize(i);
+            return fail(LL_EDEVICE, "loglinear_profile_begin: hipEventCreate failed: %s", hipGetErrorString(e));
+        }
+    }
+    g_prof.recs.reserve(max_launches);
+    g_prof.on = true;
+    return ok();
+}
+
+ll_status loglinear_profile_end(ll_kernel_stat *stats, int max_stats, int *n_stats)
+{
+    if (!g_prof.on)
+        return fail(LL_EINVAL, "loglinear_profile_end: profiling is not on");
+    g_prof.on = false;
+    std::vector<ll_kernel_stat> out;
+    for (const ProfRecord &r : g_prof.recs) {
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess)
+            return fail(LL_EDEVICE, "loglinear_profile_end: %s", hipGetErrorString(e));
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, r.start, r.stop);
+        size_t i = 0;
+        for (; i < out.size(); ++i)
+            if (std::strcmp(out[i].name, r.name) == 0)
+                break;
+        if (i == out.size()) {
+            ll_kernel_stat s{};
+            std::snprintf(s.name, sizeof s.name, "%s", r.name);
+            out.push_back(s);
+        }
+        out[i].launches += 1;
+        out[i].total_ms += ms;
+    }
+    const int n = (int)out.size() < max_stats ? (int)out.size() : max_stats;
+    for (int i = 0; i < n; ++i)
+        stats[i] = out[i];
+    if (n_stats)
+        *n_stats = n;
+    const bool overflow = g_prof.overflow;
+    for (hipEvent_t e : g_prof.pool)
+        (void)hipEventDestroy(e);
+    g_prof = Profiler();
+    if (overflow)
+        return fail(LL_EINVAL, "loglinear_profile_end: event pool overflowed; some launches were not timed");
+    return ok();
+}
+
+}  // extern "C"

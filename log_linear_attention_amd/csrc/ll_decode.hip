@@ -1,0 +1,245 @@
+// Batched decode step of log-linear attention (Mamba-2 form) for gfx950.
+//
+// The recurrent form keeps O(log T) states per sequence; each new token goes
+// into the finest level and the levels are merged and promoted the way a
+// Fenwick tree carries ("Log-Linear Attention", Portuguese page §2 "Forma
+// Recorrente e Paralela", decoding bullet; French page §2 "Algorithmes
+// Efficaces", inference bullet).  With the new token at position t and
+// kc = number of trailing zero bits of t, the buckets of levels 0..kc of the
+// previous position merge into level kc+1, every older bucket only decays, and
+// the new token alone forms level 0.
+//
+// Each slot stores (hat S, g) with true state exp(g) hat S, so buckets that
+// only decay cost one scalar update instead of a 32 KiB rewrite; the step
+// reads each occupied slot once and writes two (the merged bucket and the new
+// token).  The work is memory-bound: one workgroup per (sequence, head) streams
+// its occupied slots with 16-byte loads, accumulates q^T S per column group in
+// registers and reduces over dk in LDS.
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+
+template <class DT, int DK_, int DV_>
+struct Dec {
+    using T = typename DT::T;
+    static constexpr int DK = DK_, DV = DV_;
+    static constexpr int NT = 256;
+    static constexpr int NV4 = DK * DV / 4;                  // float4 vectors per slot
+    static constexpr int NPT = (NV4 + NT - 1) / NT;          // vectors per thread
+    static constexpr int CG = DV / 4;                        // column groups
+    static_assert((NT * 4) % DV == 0, "a thread must keep one column group");
+};
+
+template <class D>
+__global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict__ q,
+                                                 const typename D::T *__restrict__ k,
+                                                 const typename D::T *__restrict__ v,
+                                                 const float *__restrict__ a, const float *__restrict__ lam,
+                                                 float *__restrict__ state, float *__restrict__ logscale,
+                                                 const int64_t *__restrict__ pos, typename D::T *__restrict__ out,
+                                                 int H, int Lcap)
+{
+    using T = typename D::T;
+    constexpr int DK = D::DK, DV = D::DV;
+    __shared__ float qs[DK], ks[DK], vs[DV];
+    __shared__ float lam_s[kMaxLevels], g_s[kMaxLevels];
+    __shared__ float red[D::NT][4];
+    __shared__ float qk_s;
+
+    const int tid = threadIdx.x;
+    const int sh = blockIdx.x;          // sequence * H + head
+    const int s = sh / H;
+    const int64_t t = pos[s];
+    T *o = out + (size_t)sh * DV;
+
+    if (t < 0 || t >= ((int64_t)1 << (Lcap - 1))) {
+        // Not representable with Lcap slots: NaN output, stack untouched.
+        for (int e = tid; e < DV; e += D::NT)
+            o[e] = from_f32<T>(__builtin_nanf(""));
+        return;
+    }
+
+    for (int d = tid; d < DK; d += D::NT) {
+        qs[d] = to_f32(q[(size_t)sh * DK + d]);
+        ks[d] = to_f32(k[(size_t)sh * DK + d]);
+    }
+    for (int e = tid; e < DV; e += D::NT)
+        vs[e] = to_f32(v[(size_t)sh * DV + e]);
+    for (int l = tid; l < Lcap; l += D::NT) {
+        lam_s[l] = lam[(size_t)sh * Lcap + l];
+        g_s[l] = logscale[(size_t)sh * Lcap + l];
+    }
+    __syncthreads();
+    if (tid < 64) {
+        float x = 0.f;
+        for (int d = tid; d < DK; d += 64)
+            x += qs[d] * ks[d];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+            x += __shfl_xor(x, m, 64);
+        if (tid == 0)
+            qk_s = x;
+    }
+
+    const float at = a[sh];
+    float *st = state + (size_t)sh * Lcap * DK * DV;
+    const int c0 = (tid * 4) % DV;  // this thread's four output columns
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+
+    float4 fresh[D::NPT];  // k v^T for the new token, this thread's share
+#pragma unroll
+    for (int r = 0; r < D::NPT; ++r) {
+        const int idx = tid + D::NT * r;
+        if (idx < D::NV4) {
+            const int row = idx * 4 / DV;
+            fresh[r] = make_float4(ks[row] * vs[c0], ks[row] * vs[c0 + 1], ks[row] * vs[c0 + 2], ks[row] * vs[c0 + 3]);
+        }
+    }
+
+    if (t == 0) {
+#pragma unroll
+        for (int r = 0; r < D::NPT; ++r) {
+            const int idx = tid + D::NT * r;
+            if (idx < D::NV4)
+                reinterpret_cast<float4 *>(st)[idx] = fresh[r];
+        }
+    } else {
+        const int64_t prev = t - 1;
+        const int kc = __builtin_ctzll((unsigned long long)t);  // levels 0..kc merge into kc+1
+        float4 M[D::NPT];
+#pragma unroll
+        for (int r = 0; r < D::NPT; ++r)
+            M[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int l = 0; l < Lcap; ++l) {
+            const bool occ = (l == 0) || ((prev >> (l - 1)) & 1);
+            if (!occ)
+                continue;
+            const float4 *src = reinterpret_cast<const float4 *>(st + (size_t)l * DK * DV);
+            float4 x[D::NPT];
+#pragma unroll
+            for (int r = 0; r < D::NPT; ++r) {
+                const int idx = tid + D::NT * r;
+                if (idx < D::NV4)
+                    x[r] = src[idx];
+            }
+            if (l <= kc) {
+                const float sc = __expf(g_s[l]);
+#pragma unroll
+                for (int r = 0; r < D::NPT; ++r) {
+                    const int idx = tid + D::NT * r;
+                    if (idx < D::NV4) {
+                        M[r].x += sc * x[r].x; M[r].y += sc * x[r].y;
+                        M[r].z += sc * x[r].z; M[r].w += sc * x[r].w;
+                    }
+                }
+            } else {
+                const float coef = lam_s[l] * __expf(g_s[l] + at);
+#pragma unroll
+                for (int r = 0; r < D::NPT; ++r) {
+                    const int idx = tid + D::NT * r;
+                    if (idx < D::NV4) {
+                        const float qc = coef * qs[idx * 4 / DV];
+                        part[0] += qc * x[r].x; part[1] += qc * x[r].y;
+                        part[2] += qc * x[r].z; part[3] += qc * x[r].w;
+                    }
+                }
+            }
+        }
+        const float dec = __expf(at);
+        const float lm = lam_s[kc + 1];
+        float4 *dstM = reinterpret_cast<float4 *>(st + (size_t)(kc + 1) * DK * DV);
+        float4 *dst0 = reinterpret_cast<float4 *>(st);
+#pragma unroll
+        for (int r = 0; r < D::NPT; ++r) {
+            const int idx = tid + D::NT * r;
+            if (idx < D::NV4) {
+                float4 m = make_float4(dec * M[r].x, dec * M[r].y, dec * M[r].z, dec * M[r].w);
+                dstM[idx] = m;
+                dst0[idx] = fresh[r];
+                const float qc = lm * qs[idx * 4 / DV];
+                part[0] += qc * m.x; part[1] += qc * m.y; part[2] += qc * m.z; part[3] += qc * m.w;
+            }
+        }
+    }
+
+    red[tid][0] = part[0];
+    red[tid][1] = part[1];
+    red[tid][2] = part[2];
+    red[tid][3] = part[3];
+    __syncthreads();
+    if (tid < D::CG) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int x = tid; x < D::NT; x += D::CG) {
+            acc[0] += red[x][0]; acc[1] += red[x][1]; acc[2] += red[x][2]; acc[3] += red[x][3];
+        }
+        const float d0 = lam_s[0] * qk_s;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            o[4 * tid + c] = from_f32<T>(acc[c] + d0 * vs[4 * tid + c]);
+    }
+    if (tid == 0) {
+        float *gl = logscale + (size_t)sh * Lcap;
+        gl[0] = 0.f;
+        if (t > 0) {
+            const int64_t prev = t - 1;
+            const int kc = __builtin_ctzll((unsigned long long)t);
+            for (int l = kc + 2; l < Lcap; ++l)
+                if ((prev >> (l - 1)) & 1)
+                    gl[l] = g_s[l] + at;
+            gl[kc + 1] = 0.f;
+        }
+    }
+}
+
+typedef hipError_t (*DecLauncher)(const DecodeArgs &, hipStream_t);
+
+template <class DT, int DK, int DV>
+static hipError_t launch_dec_t(const DecodeArgs &A, hipStream_t s)
+{
+    using D = Dec<DT, DK, DV>;
+    using T = typename D::T;
+    prof_before("ll_decode", s);
+    hipLaunchKernelGGL(ll_decode<D>, dim3(A.S * A.H), dim3(D::NT), 0, s, (const T *)A.q, (const T *)A.k,
+                       (const T *)A.v, A.a, A.lam, A.state, A.logscale, A.pos, (T *)A.out, A.H, A.Lcap);
+    prof_after(s);
+    return hipGetLastError();
+}
+
+template <class DT, int DK>
+static DecLauncher dec_pick_dv(int dv)
+{
+    switch (dv) {
+    case 16: return &launch_dec_t<DT, DK, 16>;
+    case 32: return &launch_dec_t<DT, DK, 32>;
+    case 64: return &launch_dec_t<DT, DK, 64>;
+    case 128: return &launch_dec_t<DT, DK, 128>;
+    default: return nullptr;
+    }
+}
+
+template <class DT>
+static DecLauncher dec_pick(int dk, int dv)
+{
+    switch (dk) {
+    case 16: return dec_pick_dv<DT, 16>(dv);
+    case 32: return dec_pick_dv<DT, 32>(dv);
+    case 64: return dec_pick_dv<DT, 64>(dv);
+    case 128: return dec_pick_dv<DT, 128>(dv);
+    default: return nullptr;
+    }
+}
+
+static DecLauncher find_dec(bool bf16, int dk, int dv) { return bf16 ? dec_pick<TBF16>(dk, dv) : dec_pick<TF32>(dk, dv); }
+
+bool decode_supported(bool bf16, int dk, int dv) { return find_dec(bf16, dk, dv) != nullptr; }
+
+hipError_t decode_launch(const DecodeArgs &args, hipStream_t stream)
+{
+    DecLauncher f = find_dec(args.bf16, args.dk, args.dv);
+    if (!f)
+        return hipErrorInvalidValue;
+    return f(args, stream);
+}
+
+}  // namespace ll

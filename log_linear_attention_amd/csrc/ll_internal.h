@@ -1,0 +1,56 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ll {
+
+constexpr int kMaxLevels = 32;     // lambda entries per token the kernels stage (T < 2^31)
+constexpr int kMaxGroupLog2 = 3;   // local Fenwick stack depth of the chunk walk (<= 8 chunks)
+
+// How the chunked forward splits a sequence.
+//  N chunks of C tokens; groups of G = 2^g consecutive chunks, nG groups.
+//  Levels whose buckets stay inside a group are carried in registers by the
+//  chunk walk; coarser ones come from left-child block states built over the
+//  nL = nG - 1 complete groups that can precede another group.
+struct FwdPlan {
+    int N = 0, g = 0, G = 1, nG = 0, nL = 0, Plev = 0, nLeft = 0;
+    size_t off_Sg = 0, off_Gam = 0, off_Dg = 0, bytes = 0;
+};
+
+// group_log2 < 0 picks automatically.  elem_bytes is the size used for the
+// stored block states (4 covers both dtypes).
+FwdPlan fwd_plan(int B, int H, int T, int dk, int dv, int chunk, int group_log2, int elem_bytes);
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    const float *a, *lam;
+    void *out;
+    int B, H, T, dk, dv, chunk, L;
+    bool bf16;
+    void *workspace;
+};
+
+// Profiling hooks (implemented by the ABI layer).
+void prof_before(const char *name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+bool fwd_supported(bool bf16, int dk, int dv, int chunk);
+hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *a, *lam;
+    float *state, *logscale;
+    const int64_t *pos;
+    void *out;
+    int S, H, dk, dv, Lcap;
+    bool bf16;
+};
+
+bool decode_supported(bool bf16, int dk, int dv);
+hipError_t decode_launch(const DecodeArgs &args, hipStream_t stream);
+
+}  // namespace ll

@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments on the host with the
+documented status codes before any device call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import log_linear_attention_amd as ll
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loglinear.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ll.LIB_PATH):
+        from log_linear_attention_amd import build
+
+        build.build(verbose=False)
+    return ll.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(loglinear_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("loglinear_fwd", "loglinear_decode_step", "loglinear_last_error",
+                 "loglinear_num_levels", "loglinear_fwd_workspace_bytes"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), f"{name} declared in loglinear.h but not exported"
+
+
+def test_num_levels(L):
+    assert [ll.num_levels(T) for T in (0, 1, 2, 3, 4, 5, 256, 257, 2048, 16384, 65536)] == \
+        [1, 1, 2, 3, 3, 4, 9, 10, 12, 15, 17]
+    assert L.loglinear_num_levels(-1) == -1
+
+
+def test_workspace_bytes_is_deterministic_and_zero_when_unneeded(L):
+    a = ll.fwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
+    b = ll.fwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
+    assert a == b and a > 0 and a % 256 == 0
+    # a single chunk needs no inter-chunk state
+    assert ll.fwd_workspace_bytes(1, 1, 64, 128, 64, 64) == 0
+    assert ll.fwd_workspace_bytes(0, 16, 16384, 128, 64, 64) == 0
+    # invalid shapes report 0
+    assert ll.fwd_workspace_bytes(1, 1, 100, 128, 64, 48) == 0
+
+
+FAKE = 1 << 20  # 16-byte aligned fake device address; never dereferenced on error paths
+
+
+def _fwd(L, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, lam=FAKE + 0x400000,
+                out=FAKE + 0x8000000, B=1, H=1, T=128, dk=128, dv=64, chunk=64, dtype=ll.LL_BF16,
+                ws=None, wsb=0, stream=None, g=-1)
+    args.update(kw)
+    return L.loglinear_fwd_ex(args["q"], args["k"], args["v"], args["a"], args["lam"], args["out"],
+                              args["B"], args["H"], args["T"], args["dk"], args["dv"], args["chunk"],
+                              args["dtype"], args["ws"], args["wsb"], args["stream"], args["g"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), ll.LL_EINVAL),
+    (dict(B=-1), ll.LL_EINVAL),
+    (dict(T=-5), ll.LL_EINVAL),
+    (dict(dk=0), ll.LL_EINVAL),
+    (dict(chunk=48), ll.LL_EUNSUPPORTED),
+    (dict(chunk=128), ll.LL_EUNSUPPORTED),
+    (dict(dk=96), ll.LL_EUNSUPPORTED),
+    (dict(dv=48), ll.LL_EUNSUPPORTED),
+    (dict(dk=16), ll.LL_EUNSUPPORTED),           # bf16 needs dk >= 32
+    (dict(dk=256, dtype=ll.LL_F32), ll.LL_EUNSUPPORTED),
+    (dict(g=4), ll.LL_EUNSUPPORTED),
+    (dict(q=None), ll.LL_EINVAL),
+    (dict(out=None), ll.LL_EINVAL),
+    (dict(q=FAKE + 8), ll.LL_EINVAL),            # misaligned
+    (dict(a=FAKE + 0x300002), ll.LL_EINVAL),     # misaligned float vector
+    (dict(lam=None), ll.LL_EINVAL),
+    (dict(out=FAKE + 0x100), ll.LL_EINVAL),      # out overlaps q
+    (dict(T=1000), ll.LL_EWORKSPACE),            # needs a workspace, none given
+    (dict(T=1000, ws=FAKE + 0x10000000, wsb=16), ll.LL_EWORKSPACE),
+])
+def test_fwd_rejects_bad_arguments(L, kw, status):
+    assert _fwd(L, **kw) == status
+    assert ll.last_error() != ""
+
+
+def test_fwd_misaligned_workspace(L):
+    need = ll.fwd_workspace_bytes(1, 1, 1000, 128, 64, 64)
+    assert _fwd(L, T=1000, ws=FAKE + 0x10000010, wsb=need) == ll.LL_EINVAL
+
+
+def test_fwd_empty_problem_is_a_no_op(L):
+    # zero sizes: valid, nothing launched, pointers not touched
+    assert _fwd(L, B=0, q=None, k=None, v=None, out=None, a=None, lam=None) == ll.LL_OK
+    assert _fwd(L, T=0, q=None, k=None, v=None, out=None, a=None, lam=None) == ll.LL_OK
+
+
+def _dec(L, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, lam=FAKE + 0x400000,
+                state=FAKE + 0x1000000, logscale=FAKE + 0x9000000, pos=FAKE + 0xa000000,
+                out=FAKE + 0xb000000, S=2, H=2, dk=128, dv=64, Lcap=17, dtype=ll.LL_BF16, stream=None)
+    args.update(kw)
+    return L.loglinear_decode_step(args["q"], args["k"], args["v"], args["a"], args["lam"], args["state"],
+                                   args["logscale"], args["pos"], args["out"], args["S"], args["H"], args["dk"],
+                                   args["dv"], args["Lcap"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), ll.LL_EINVAL),
+    (dict(S=-1), ll.LL_EINVAL),
+    (dict(Lcap=0), ll.LL_EINVAL),
+    (dict(Lcap=1), ll.LL_EUNSUPPORTED),
+    (dict(Lcap=33), ll.LL_EUNSUPPORTED),
+    (dict(dk=96), ll.LL_EUNSUPPORTED),
+    (dict(dv=256), ll.LL_EUNSUPPORTED),
+    (dict(state=None), ll.LL_EINVAL),
+    (dict(pos=None), ll.LL_EINVAL),
+    (dict(pos=FAKE + 0xa000004), ll.LL_EINVAL),
+    (dict(state=FAKE + 4), ll.LL_EINVAL),
+    (dict(out=FAKE + 0x1000000), ll.LL_EINVAL),  # out inside state
+])
+def test_decode_rejects_bad_arguments(L, kw, status):
+    assert _dec(L, **kw) == status
+    assert ll.last_error() != ""
+
+
+def test_decode_empty_is_a_no_op(L):
+    assert _dec(L, S=0, q=None, state=None) == ll.LL_OK
+
+
+def test_profile_end_without_begin(L):
+    n = ctypes.c_int(0)
+    arr = (ll.KernelStat * 4)()
+    assert L.loglinear_profile_end(arr, 4, ctypes.byref(n)) == ll.LL_EINVAL
+    assert L.loglinear_profile_begin(0) == ll.LL_EINVAL

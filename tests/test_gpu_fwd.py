@@ -1,0 +1,151 @@
+"""GPU parity of loglinear_fwd against the fp64 oracle.
+
+Inputs come from the seeded generator; the oracle sees the exact device input
+values (bf16 inputs are upcast, not re-drawn).  Small workloads are compared
+on every output; the 16K and 64K workloads on a seeded row sample plus every
+row of the first, a middle and the last chunk, in the same launch
+configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_util import TOL, announce, f64, per_head_max, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+ll = pytest.importorskip("log_linear_attention_amd")
+
+
+def _run(inp, chunk, group_log2=-1, workspace=None, out=None):
+    d = to_dev(inp)
+    o = ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=chunk, group_log2=group_log2,
+               workspace=workspace, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+def _check_full(inp, got, dtype):
+    ref = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["lam"])
+    g = f64(got)
+    assert np.all(np.isfinite(g))
+    e_all, e_head = rel_l2(g, ref), per_head_max(g, ref)
+    print(f"rel_l2={e_all:.3e} worst_head={e_head:.3e}")
+    assert e_all <= TOL[dtype] and e_head <= TOL[dtype]
+    return ref
+
+
+def test_tiny_f32_workload():
+    cfg = synth.WORKLOADS["tiny_f32_T256"]
+    announce(cfg.name)
+    inp = synth.make_fwd_inputs(cfg)
+    got = _run(inp, cfg.chunk)
+    _check_full(inp, got, "f32")
+
+
+@pytest.mark.parametrize("T", [1, 2, 16, 17, 64, 100, 1000])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_f32_ragged_lengths(T, chunk):
+    cfg = synth.FwdConfig("f32_ragged", 1, 2, T, 64, 32, chunk, "f32", 0.05, 2000 + T)
+    announce(f"f32 T={T} chunk={chunk}")
+    inp = synth.make_fwd_inputs(cfg)
+    got = _run(inp, chunk)
+    _check_full(inp, got, "f32")
+
+
+@pytest.mark.parametrize("group_log2", [0, 1, 2, 3])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_f32_full_head_dims_every_group_size(chunk, group_log2):
+    """dk=128, dv=64 in fp32: the chunk and group algebra at the tight
+    tolerance, with a ragged tail (T not a multiple of the chunk)."""
+    cfg = synth.FwdConfig("f32_groups", 1, 2, 1500, 128, 64, chunk, "f32", 0.05, 3000 + chunk)
+    announce(f"f32 dk128 dv64 T=1500 chunk={chunk} g={group_log2}")
+    inp = synth.make_fwd_inputs(cfg)
+    got = _run(inp, chunk, group_log2)
+    _check_full(inp, got, "f32")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (64, 128), (128, 128), (16, 64)])
+def test_f32_other_head_dims(dk, dv):
+    cfg = synth.FwdConfig("f32_dims", 1, 2, 700, dk, dv, 32, "f32", 0.05, 4000 + dk + dv)
+    announce(f"f32 dk={dk} dv={dv}")
+    inp = synth.make_fwd_inputs(cfg)
+    _check_full(inp, _run(inp, 32), "f32")
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (64, 32), (128, 128)])
+def test_bf16_other_head_dims(dk, dv):
+    cfg = synth.FwdConfig("bf16_dims", 2, 2, 900, dk, dv, 64, "bf16", 0.05, 5000 + dk + dv)
+    announce(f"bf16 dk={dk} dv={dv}")
+    inp = synth.make_fwd_inputs(cfg)
+    _check_full(inp, _run(inp, 64), "bf16")
+
+
+def test_bf16_T2K_workload():
+    cfg = synth.WORKLOADS["fwd_bf16_T2K"]
+    announce(cfg.name)
+    inp = synth.make_fwd_inputs(cfg)
+    _check_full(inp, _run(inp, cfg.chunk), "bf16")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("group_log2", [0, 2, 3])
+def test_bf16_chunk_and_group_invariance(chunk, group_log2):
+    cfg = synth.FwdConfig("bf16_inv", 1, 2, 3000, 128, 64, chunk, "bf16", 0.05, 6000)
+    announce(f"bf16 invariance chunk={chunk} g={group_log2}")
+    inp = synth.make_fwd_inputs(cfg)
+    _check_full(inp, _run(inp, chunk, group_log2), "bf16")
+
+
+def test_single_chunk_needs_no_workspace():
+    cfg = synth.FwdConfig("bf16_one_chunk", 2, 3, 64, 128, 64, 64, "bf16", 0.05, 6100)
+    announce("single chunk")
+    assert ll.fwd_workspace_bytes(2, 3, 64, 128, 64, 64) == 0
+    inp = synth.make_fwd_inputs(cfg)
+    _check_full(inp, _run(inp, 64), "bf16")
+
+
+@pytest.mark.parametrize("name", ["fwd_bf16_T16K", "fwd_bf16_T64K"])
+def test_large_workloads_sampled_rows(name):
+    cfg = synth.WORKLOADS[name]
+    announce(cfg.name)
+    inp = synth.make_fwd_inputs(cfg)
+    got = f64(_run(inp, cfg.chunk)).reshape(cfg.B * cfg.H, cfg.T, cfg.dv)
+    assert np.all(np.isfinite(got))
+    rows = synth.sample_rows(cfg.B, cfg.H, cfg.T, cfg.chunk, 256, seed=cfg.seed + 7)
+    ref = oracle.fwd_rows(inp["q"], inp["k"], inp["v"], inp["a"], inp["lam"], rows)
+    sel = got[rows[:, 0], rows[:, 1]]
+    e = rel_l2(sel, ref)
+    worst = max(rel_l2(sel[rows[:, 0] == bh], ref[rows[:, 0] == bh]) for bh in range(cfg.B * cfg.H))
+    print(f"{len(rows)} rows rel_l2={e:.3e} worst_head={worst:.3e}")
+    assert e <= TOL["bf16"] and worst <= TOL["bf16"]
+
+
+def test_deterministic_and_workspace_contents_ignored():
+    cfg = synth.FwdConfig("bf16_det", 1, 4, 4096, 128, 64, 64, "bf16", 0.05, 6200)
+    announce("determinism + NaN-poisoned workspace")
+    inp = synth.make_fwd_inputs(cfg)
+    n = ll.fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(float("nan"))
+    o1 = _run(inp, cfg.chunk, workspace=ws.view(torch.uint8)).clone()
+    ws.fill_(float("nan"))
+    o2 = _run(inp, cfg.chunk, workspace=ws.view(torch.uint8)).clone()
+    o3 = _run(inp, cfg.chunk)
+    assert torch.isfinite(o1.float()).all()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_output_guard_bands_untouched():
+    cfg = synth.FwdConfig("bf16_guard", 1, 2, 1000, 128, 64, 64, "bf16", 0.05, 6300)
+    announce("guard bands")
+    inp = synth.make_fwd_inputs(cfg)
+    n = cfg.B * cfg.H * cfg.T * cfg.dv
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + n].view(cfg.B, cfg.H, cfg.T, cfg.dv)
+    _run(inp, cfg.chunk, out=out)
+    assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
+    _check_full(inp, out, "bf16")
