@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the log-linear attention (Mamba-2 form) hot path on one MI355X.
+
+One step = one loglinear_fwd over the 16K-token workload (B=1, H=16, T=16384,
+dk=128, dv=64, bf16 q/k/v, fp32 decay and lambda, chunk 64) followed, in a
+second timed region, by one loglinear_decode_step over the batched decode
+workload (64 sequences x 16 heads at positions drawn from U{1..32768}, fp32
+Fenwick stacks of 17 slots).  Prints ONE JSON line on stdout.
+
+  value        forward tokens/s (B*T / forward time), inputs resident in HBM
+  roofline     of the dominant kernel (ll_chunk_walk): algorithmic HBM bytes
+               per launch / its mean launch time (HIP events on the launch
+               stream, inside the timed region) against 8 TB/s
+  decode       decode GB/s (algorithmic bytes / step time), tokens/s and its
+               own roofline
+  cpu_baseline the fp64 oracle on a bounded row sample of the same workload
+
+Three input sets (3 x 218 MB) rotate through the forward steps and two
+decode stacks (2 x 570 MB) through the decode steps, so no step finds its
+inputs in the 256 MB MALL left there by the previous one.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_chunk_walk_fwd_bf16_T16K.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
+                  for f in ("ll_fwd.hip", "ll_device.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_algorithmic(cfg):
+    """Mandatory HBM bytes and algorithmic flops of one forward.
+
+    Bytes per (b, h): T*(2*dk + dv)*e (q, k, v) + 4T (a) + 4T*L (lambda) +
+    T*dv*e (out).  Flops per (b, h): intra-chunk causal N*C(C+1)/2*2(dk+dv),
+    chunk states N*2C*dk*dv, inter-chunk reads (sum over chunks c of
+    popcount(c)) * 2C*dk*dv."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    T, C, dk, dv, L = cfg.T, cfg.chunk, cfg.dk, cfg.dv, cfg.L
+    BH = cfg.B * cfg.H
+    per_bh_bytes = T * (2 * dk + dv) * e + 4 * T + 4 * T * L + T * dv * e
+    N = (T + C - 1) // C
+    pop = sum(bin(c).count("1") for c in range(N))
+    per_bh_flops = N * C * (C + 1) // 2 * 2 * (dk + dv) + N * 2 * C * dk * dv + pop * 2 * C * dk * dv
+    return BH * per_bh_bytes, BH * per_bh_flops
+
+
+def decode_algorithmic(cfg, positions):
+    """Algorithmic bytes of one decode step: every occupied incoming slot read
+    once, the merged slot and the new token's slot written, plus the token,
+    a, lambda, logscale (read + write) and the output."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    slot = cfg.dk * cfg.dv * 4
+    total = 0
+    for t in positions:
+        occ = 1 + bin(int(t) - 1).count("1") if t >= 1 else 0
+        per_head = slot * (occ + (2 if t >= 1 else 1)) + (2 * cfg.dk + cfg.dv) * e + 4 * (1 + cfg.Lcap) \
+            + 8 * cfg.Lcap + cfg.dv * e
+        total += cfg.H * per_head
+    return total
+
+
+def read_traffic():
+    """Counter-measured HBM bytes per ll_chunk_walk launch from the committed
+    profile summary, or None if absent or taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, cfg, n_rows: int, seed: int):
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = np.stack([rng.integers(0, cfg.B * cfg.H, n_rows), rng.integers(0, cfg.T, n_rows)], axis=1)
+    q, k, v, a, lam = (oracle._f64(inp[x]) for x in ("q", "k", "v", "a", "lam"))
+    t0 = time.perf_counter()
+    oracle.fwd_rows(q, k, v, a, lam, rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": n_rows / dt,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{n_rows} uniformly drawn (head, position) rows of the fwd_bf16_T16K workload "
+                  f"(fp64 O(T^2) row sums, mean cost equal to a full-workload row); {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="oracle rows timed for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy first (reference kernel for counter scaling)")
+    ap.add_argument("--group-log2", type=int, default=-1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import log_linear_attention_amd as ll
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.WORKLOADS["fwd_bf16_T16K"]
+    dcfg = synth.WORKLOADS["decode_bf16_S64"]
+
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    log("generating inputs ...")
+    host_sets = [synth.make_fwd_inputs(cfg, seed=cfg.seed + i) for i in range(3)]
+    dsets = [{k: v.to(dev) for k, v in s.items()} for s in host_sets]
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=cfg.torch_dtype, device=dev)
+    ws = ll.alloc_workspace(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk, args.group_log2)
+
+    def fwd(i):
+        d = dsets[i % 3]
+        ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=cfg.chunk, out=out, workspace=ws,
+               group_log2=args.group_log2)
+
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+
+    ll.profile_begin(8 * args.steps + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        fwd(i)
+    e1.record()
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    kstats = ll.profile_end()
+    fwd_ms = e0.elapsed_time(e1) / args.steps
+    log(f"forward: {fwd_ms:.4f} ms/step (wall {(w1 - w0) * 1e3 / args.steps:.4f}); kernels: {kstats}")
+
+    fbytes, fflops = fwd_algorithmic(cfg)
+    walk_launches, walk_ms = kstats["ll_chunk_walk"]
+    walk_avg_ms = walk_ms / walk_launches
+    achieved = fbytes / (walk_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic()
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "kernel": "ll_chunk_walk", "kernel_avg_ms": round(walk_avg_ms, 5),
+    }
+    whole_gbs = fbytes / (fwd_ms * 1e-3) / 1e9
+    mfma_tflops = fflops / (fwd_ms * 1e-3) / 1e12
+
+    # ---- decode ---------------------------------------------------------
+    log("generating decode stacks ...")
+    dec_host = [synth.make_decode_inputs(dcfg, seed=dcfg.seed + i) for i in range(2)]
+    pos0 = dec_host[0]["pos"].numpy()
+    for s in dec_host[1:]:
+        s["pos"] = dec_host[0]["pos"].clone()  # same positions: same work per step
+    dec = [{k: v.to(dev) for k, v in s.items()} for s in dec_host]
+    del dec_host
+    dout = torch.empty((dcfg.S, dcfg.H, dcfg.dv), dtype=dcfg.torch_dtype, device=dev)
+
+    def dstep(i):
+        d = dec[i % 2]
+        ll.decode_step(d["q"], d["k"], d["v"], d["a"], d["lam"], d["state"], d["logscale"], d["pos"], out=dout)
+
+    for i in range(args.warmup):
+        dstep(i)
+    torch.cuda.synchronize()
+    ll.profile_begin(4 * args.steps + 4)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        dstep(i)
+    e1.record()
+    torch.cuda.synchronize()
+    dstats = ll.profile_end()
+    dec_ms = e0.elapsed_time(e1) / args.steps
+    dbytes = decode_algorithmic(dcfg, pos0)
+    dl, dms = dstats["ll_decode"]
+    dec_kernel_ms = dms / dl
+    dec_gbs = dbytes / (dec_kernel_ms * 1e-3) / 1e9
+    log(f"decode: {dec_ms:.4f} ms/step, kernel {dec_kernel_ms:.4f} ms, {dec_gbs:.1f} GB/s")
+
+    result = {
+        "metric": "tokens/s, log-linear Mamba-2 fwd at T=16K (% MFMA peak); decode GB/s",
+        "value": round(cfg.B * cfg.T / (fwd_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fwd_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fwd_bf16_T16K", "B": cfg.B, "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv,
+            "chunk": cfg.chunk, "levels": cfg.L, "group_log2": args.group_log2,
+            "inputs": "q,k,v bf16; a,lambda fp32; out bf16",
+        },
+        "roofline": roofline,
+        "forward": {
+            "kernels_ms": {k: round(v[1] / v[0], 5) for k, v in kstats.items()},
+            "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
+            "hbm_frac_whole_call": round(whole_gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac_whole_call": round(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+        },
+        "decode": {
+            "workload": "decode_bf16_S64", "metric": "decode GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(dec_ms, 5), "tokens_per_s": round(dcfg.S / (dec_ms * 1e-3), 1),
+            "algorithmic_bytes": dbytes,
+            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "ll_decode", "kernel_avg_ms": round(dec_kernel_ms, 5)},
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(host_sets[0], cfg, args.cpu_rows, seed=123)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

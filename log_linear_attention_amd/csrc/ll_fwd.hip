@@ -15,20 +15,23 @@
 // for each set bit m-1 of c, the decayed state sum k v^T of the left block of
 // 2^(m-1) chunks just below that bit.
 //
-// Three kernels, all on the caller's stream:
+// Kernels, all on the caller's stream:
 //  A  ll_group_state: for every group of G = 2^g consecutive chunks that can
 //     precede another group, the group's state decayed to its end
-//     (sum exp(decay) k v^T, fp32, dk x dv) and its total log-decay.  MFMA.
-//  B  ll_left_blocks: from those, every left-child block state of the tree
-//     over groups, stored in the exact register order the consuming MFMA
-//     reads (bf16 or fp32).  Memory-bound, VALU.
+//     (sum exp(decay) k v^T, fp32, dk x dv) and its total log-decay.  MFMA,
+//     with the next chunk's k/v prefetched into registers.
+//  B  ll_left_tree: the left-child block states of the binary tree over
+//     groups, 64 leaves per thread in registers (one launch per 64x of tree
+//     height), written in the exact register order the consuming MFMA reads.
 //  C  ll_chunk_walk: one workgroup per (head, group) walks its G chunks in
 //     order.  Per chunk it computes the intra-chunk part
 //     (Q K^T ⊙ decay ⊙ lambda-level mask) V on MFMA, adds the levels inside
 //     the group from a Fenwick stack of chunk states held in registers (the
 //     recurrent decode rule applied at chunk granularity), adds the levels
 //     above the group from B's block states, writes the output rows, and
-//     folds the chunk's own state K^T diag(w) V into the stack.
+//     folds the chunk's own state K^T diag(w) V into the stack.  The next
+//     chunk's q/k/v/lambda/a are loaded into registers while the current one
+//     computes.
 // Nothing but the inputs, the output and the small group/block states touches
 // HBM; the per-chunk states of the levels inside a group never leave
 // registers.
@@ -46,7 +49,10 @@ struct Fwd {
     static constexpr int KB = DT::KB, EPL = DT::EPL;
     static constexpr int NW = DV / 16;           // waves: one 16-column slice of dv each
     static constexpr int NT = 64 * NW;
+    static constexpr int WPE = 1;                 // resident waves per SIMD the walk is built for
+    static constexpr int NRES = DT::is_bf16 ? 4 : 2;  // inter-group levels kept in registers per group
     static constexpr int NMT = C / 16;           // 16-row tiles per chunk
+    static constexpr int NCT = NMT * (NMT + 1) / 2;  // causal 16x16 score tiles
     static constexpr int CP = (C < KB) ? KB : C; // chunk contraction length (zero padded)
     static constexpr int NUC = CP / KB;          // units over chunk tokens
     static constexpr int NUK = DK / KB;          // units over dk
@@ -55,9 +61,17 @@ struct Fwd {
     static constexpr int LDK = DK + PADE;        // LDS row stride of Q, K tiles
     static constexpr int LDC = CP + PADE;        // LDS row stride of K^T, V^T, P tiles
     static constexpr int VEC = 16 / (int)sizeof(T);
+    // register prefetch of one chunk
+    static constexpr int QVEC = C * (DK / VEC);              // 16-byte vectors of a q (or k) chunk
+    static constexpr int NQ = (QVEC + NT - 1) / NT;
+    static constexpr int KPAIR = (C / 2) * (DK / VEC);       // k row-pair vectors
+    static constexpr int NKP = (KPAIR + NT - 1) / NT;
+    static constexpr int VPAIR = (C / 2) * (DV / VEC);       // v row-pair vectors
+    static constexpr int NVP = (VPAIR + NT - 1) / NT;
+    static constexpr int NLAM = (C * kMaxLevels + NT - 1) / NT;
     static_assert(DK % KB == 0, "dk must be a multiple of the MFMA unit");
     static_assert(DV % 16 == 0 && DV <= 128, "dv must be 16..128 in steps of 16");
-    static_assert(C <= 64, "chunk scan handles at most one wave of tokens");
+    static_assert(C <= 64, "the decay scan handles at most one wave of tokens");
 };
 
 template <class F>
@@ -67,10 +81,12 @@ struct alignas(16) WalkSmem {
     T Ks[F::C * F::LDK];
     T Kts[F::DK * F::LDC];
     T Vts[F::DV * F::LDC];
-    T Ps[F::C * F::LDC];
     float lam[F::C * kMaxLevels];
     float Aloc[F::C];
-    float off[32];
+    float off[32];          // log-decay from each inter-group block's end to the group start
+    size_t blk[32];         // element offset of each inter-group block state
+    int plist[32];          // set bits of the group index, low to high
+    int npop;
     float gch;
 };
 
@@ -84,84 +100,26 @@ struct alignas(16) StateSmem {
 };
 
 // ---------------------------------------------------------------------------
-// Staging helpers (all threads of the workgroup call them).
+// Shared device pieces.
 // ---------------------------------------------------------------------------
 
-// Rows [t0, t0 + C) of a [*, D] tensor into a row-major LDS tile; rows past
-// `valid` are zero.
-template <class F, int D>
-__device__ __forceinline__ void stage_rows(typename F::T *dst, const typename F::T *src, int valid, int tid)
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0, 0, 0, 0); }
+
+// Zero a whole LDS array (used once per workgroup).
+template <class F, class E>
+__device__ __forceinline__ void lds_zero(E *dst, int n, int tid)
 {
-    using T = typename F::T;
-    constexpr int VPR = D / F::VEC;
-    for (int idx = tid; idx < F::C * VPR; idx += F::NT) {
-        const int j = idx / VPR, c = idx % VPR;
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (j < valid)
-            x = *reinterpret_cast<const uint4 *>(src + (size_t)j * D + c * F::VEC);
-        *reinterpret_cast<uint4 *>(dst + j * F::LDK + c * F::VEC) = x;
-    }
-    (void)sizeof(T);
+    for (int i = tid; i < n; i += F::NT)
+        dst[i] = E(0.f);
 }
 
-// Transposed staging: dst[d][j] = scale_j * src[j][d] for d < D, j < C, from
-// rows with stride src_ld (global or LDS); rows past `valid` are zero.  Two
-// rows at a time so each LDS store writes a pair of elements.
-template <class F, int D, bool SCALE>
-__device__ __forceinline__ void stage_transposed(typename F::T *dst, const typename F::T *src, int src_ld,
-                                                 int valid, const float *Aloc, float gch, int tid)
-{
-    using T = typename F::T;
-    constexpr int VPR = D / F::VEC;
-    for (int idx = tid; idx < (F::C / 2) * VPR; idx += F::NT) {
-        const int j = 2 * (idx / VPR), c = idx % VPR;
-        uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-        if (j < valid)
-            x0 = *reinterpret_cast<const uint4 *>(src + (size_t)j * src_ld + c * F::VEC);
-        if (j + 1 < valid)
-            x1 = *reinterpret_cast<const uint4 *>(src + (size_t)(j + 1) * src_ld + c * F::VEC);
-        const T *e0 = reinterpret_cast<const T *>(&x0);
-        const T *e1 = reinterpret_cast<const T *>(&x1);
-        float w0 = 1.f, w1 = 1.f;
-        if (SCALE) {
-            w0 = __expf(gch - Aloc[j]);
-            w1 = __expf(gch - Aloc[j + 1]);
-        }
-#pragma unroll
-        for (int x = 0; x < F::VEC; ++x) {
-            T p0, p1;
-            if (SCALE) {
-                p0 = from_f32<T>(to_f32(e0[x]) * w0);
-                p1 = from_f32<T>(to_f32(e1[x]) * w1);
-            } else {
-                p0 = e0[x];
-                p1 = e1[x];
-            }
-            T *d = dst + (c * F::VEC + x) * F::LDC + j;
-            d[0] = p0;
-            d[1] = p1;
-        }
-    }
-}
-
-// Zero the padding columns [C, CP) of a transposed tile (bf16 with C < 32).
-template <class F, int ROWS>
-__device__ __forceinline__ void zero_pad_cols(typename F::T *dst, int tid)
-{
-    if constexpr (F::CP > F::C) {
-        constexpr int W = F::CP - F::C;
-        for (int idx = tid; idx < ROWS * W; idx += F::NT)
-            dst[(idx / W) * F::LDC + F::C + idx % W] = from_f32<typename F::T>(0.f);
-    }
-}
-
-// Inclusive within-chunk cumulative log-decay Aloc[i] = sum_{r=t0..t0+i} a_r
-// (wave 0; tokens past `valid` contribute 0) and the chunk total.
+// Inclusive within-chunk cumulative log-decay of wave 0's `x` (lane i holds
+// a at token i of the chunk, 0 past the end): Aloc[i] = sum_{r<=i} a_r, and
+// the chunk total.
 template <class F>
-__device__ __forceinline__ void stage_decay(float *Aloc, float *gch, const float *a, int valid, int tid)
+__device__ __forceinline__ void scan_decay(float x, float *Aloc, float *gch, int tid)
 {
     if (tid < 64) {
-        float x = (tid < valid) ? a[tid] : 0.f;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             float y = __shfl_up(x, d, 64);
@@ -175,23 +133,112 @@ __device__ __forceinline__ void stage_decay(float *Aloc, float *gch, const float
     }
 }
 
+// Store a pair of rows j, j+1 (given as two 16-byte vectors of VEC elements
+// starting at column c*VEC) transposed into dst[col][j], optionally scaled.
+template <class F>
+__device__ __forceinline__ void store_pair_t(typename F::T *dst, const uint4 &x0, const uint4 &x1, int j, int c,
+                                             float w0, float w1, bool scale)
+{
+    using T = typename F::T;
+    const T *e0 = reinterpret_cast<const T *>(&x0);
+    const T *e1 = reinterpret_cast<const T *>(&x1);
+#pragma unroll
+    for (int x = 0; x < F::VEC; ++x) {
+        T p0 = e0[x], p1 = e1[x];
+        if (scale) {
+            p0 = from_f32<T>(to_f32(e0[x]) * w0);
+            p1 = from_f32<T>(to_f32(e1[x]) * w1);
+        }
+        T *d = dst + (c * F::VEC + x) * F::LDC + j;
+        d[0] = p0;
+        d[1] = p1;
+    }
+}
+
+// K^T (row-major LDS K tile, scaled per token by w_j = exp(g - Aloc[j]))
+// into the transposed tile Kts.
+template <class F>
+__device__ __forceinline__ void stage_kt_from_lds(typename F::T *Kts, const typename F::T *Ks, const float *Aloc,
+                                                  float gch, int tid)
+{
+    constexpr int VPR = F::DK / F::VEC;
+    for (int idx = tid; idx < F::KPAIR; idx += F::NT) {
+        const int j = 2 * (idx / VPR), c = idx % VPR;
+        const uint4 x0 = *reinterpret_cast<const uint4 *>(Ks + j * F::LDK + c * F::VEC);
+        const uint4 x1 = *reinterpret_cast<const uint4 *>(Ks + (j + 1) * F::LDK + c * F::VEC);
+        store_pair_t<F>(Kts, x0, x1, j, c, __expf(gch - Aloc[j]), __expf(gch - Aloc[j + 1]), true);
+    }
+}
+
+// Unpack a B-operand fragment of unit u back into fp32 accumulator tiles,
+// adding s * value (inverse of acc_frag).
+__device__ __forceinline__ void frag_axpy(floatx4 *tiles, const floatx4 &f, int u, float s, TF32)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        tiles[u][e] += s * f[e];
+}
+
+__device__ __forceinline__ void frag_axpy(floatx4 *tiles, const bf16x8 &f, int u, float s, TBF16)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        tiles[2 * u][e] += s * (float)f[e];
+        tiles[2 * u + 1][e] += s * (float)f[e + 4];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel A: group states.
 // ---------------------------------------------------------------------------
+template <class F>
+struct StateRegs {
+    uint4 k0[F::NKP], k1[F::NKP], v0[F::NVP], v1[F::NVP];
+    float a;
+};
+
+template <class F>
+__device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T *k, const typename F::T *v,
+                                           const float *a, size_t row0, int tid)
+{
+    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NKP; ++i) {
+        const int idx = tid + i * F::NT;
+        const int j = 2 * (idx / KPR), c = idx % KPR;
+        r.k0[i] = r.k1[i] = zero16();
+        if (idx < F::KPAIR) {
+            r.k0[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j) * F::DK + c * F::VEC);
+            r.k1[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j + 1) * F::DK + c * F::VEC);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NVP; ++i) {
+        const int idx = tid + i * F::NT;
+        const int j = 2 * (idx / VPR), c = idx % VPR;
+        r.v0[i] = r.v1[i] = zero16();
+        if (idx < F::VPAIR) {
+            r.v0[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j) * F::DV + c * F::VEC);
+            r.v1[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j + 1) * F::DV + c * F::VEC);
+        }
+    }
+    r.a = (tid < F::C) ? a[row0 + tid] : 0.f;
+}
+
 template <class F>
 __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__restrict__ k,
                                                         const typename F::T *__restrict__ v,
                                                         const float *__restrict__ a, int Tlen, int g, int nG,
                                                         int nL, float *__restrict__ Sg, float *__restrict__ Gam)
 {
-    using T = typename F::T;
     __shared__ StateSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x / nL, sg = blockIdx.x % nL;
     const int G = 1 << g;
+    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 
-    zero_pad_cols<F, F::DK>(sm.Kts, tid);
-    zero_pad_cols<F, F::DV>(sm.Vts, tid);
+    lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
+    lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
 
     floatx4 S[F::NDT];
 #pragma unroll
@@ -199,15 +246,30 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
         S[rt] = zero4();
     float gsum = 0.f;
 
+    StateRegs<F> pf;
+    state_load<F>(pf, k, v, a, (size_t)bh * Tlen + (size_t)sg * G * F::C, tid);
     for (int ci = 0; ci < G; ++ci) {
-        const int t0 = (sg * G + ci) * F::C;
-        const size_t row0 = (size_t)bh * Tlen + t0;
         __syncthreads();
-        stage_decay<F>(sm.Aloc, &sm.gch, a + row0, F::C, tid);
-        stage_transposed<F, F::DV, false>(sm.Vts, v + row0 * F::DV, F::DV, F::C, nullptr, 0.f, tid);
+#pragma unroll
+        for (int i = 0; i < F::NVP; ++i) {
+            const int idx = tid + i * F::NT;
+            if (idx < F::VPAIR)
+                store_pair_t<F>(sm.Vts, pf.v0[i], pf.v1[i], 2 * (idx / VPR), idx % VPR, 1.f, 1.f, false);
+        }
+        scan_decay<F>(pf.a, sm.Aloc, &sm.gch, tid);
         __syncthreads();
         const float gch = sm.gch;
-        stage_transposed<F, F::DK, true>(sm.Kts, k + row0 * F::DK, F::DK, F::C, sm.Aloc, gch, tid);
+#pragma unroll
+        for (int i = 0; i < F::NKP; ++i) {
+            const int idx = tid + i * F::NT;
+            if (idx < F::KPAIR) {
+                const int j = 2 * (idx / KPR);
+                store_pair_t<F>(sm.Kts, pf.k0[i], pf.k1[i], j, idx % KPR, __expf(gch - sm.Aloc[j]),
+                                __expf(gch - sm.Aloc[j + 1]), true);
+            }
+        }
+        if (ci + 1 < G)
+            state_load<F>(pf, k, v, a, (size_t)bh * Tlen + ((size_t)sg * G + ci + 1) * F::C, tid);
         __syncthreads();
         const float dec = __expf(gch);
 #pragma unroll
@@ -231,60 +293,183 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
 }
 
 // ---------------------------------------------------------------------------
-// Kernel B: left-child block states over groups, in MFMA B-operand order.
-// One thread per (head, left block, 16-byte fragment).
+// Kernel B: left-child block states of the tree over groups.
+//
+// Leaves are states of consecutive blocks at level p0 (groups for p0 = 0,
+// blocks of 64 groups for p0 = 6, ...), each with its total log-decay.  One
+// thread owns one state element of one tile of 64 leaves; it loads the 64
+// leaves into registers, builds the six tree levels above them in registers
+// (merge: exp(decay of the right half) * left + right), writes every
+// complete left child in MFMA B-operand order, and the tile total for the
+// next launch.  A block J at level p is complete when it ends at or before
+// the last complete group: (J + 1) * 2^p <= nL.
 // ---------------------------------------------------------------------------
 template <class F>
-__global__ __launch_bounds__(256) void ll_left_blocks(const float *__restrict__ Sg, const float *__restrict__ Gam,
-                                                      int BH, int nG, int nL, int nLeft,
-                                                      typename F::T *__restrict__ Dg)
+__global__ __launch_bounds__(256) void ll_left_tree(const float *__restrict__ leaves,
+                                                    const float *__restrict__ gleaves, int nleaves, int lstride,
+                                                    int gstride, int p0, int nL, int nLeft,
+                                                    typename F::T *__restrict__ Dg, float *__restrict__ tot,
+                                                    float *__restrict__ gtot, int tstride)
 {
     using T = typename F::T;
-    constexpr int NFV = F::DK * F::DV / F::EPL;
-    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (size_t)BH * nLeft * NFV)
+    constexpr int DKV = F::DK * F::DV;
+    __shared__ float gsh[64];
+    const int tid = threadIdx.x;
+    const int elem = blockIdx.x * 256 + tid;
+    const int tile = blockIdx.y, bh = blockIdx.z;
+    const int base = tile * 64;
+    if (tid < 64)
+        gsh[tid] = (base + tid < nleaves) ? gleaves[(size_t)bh * gstride + base + tid] : 0.f;
+    float x[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+        x[i] = (base + i < nleaves && elem < DKV) ? leaves[((size_t)bh * lstride + base + i) * DKV + elem] : 0.f;
+    __syncthreads();
+    if (elem >= DKV)
         return;
-    const int fv = (int)(gid % NFV);
-    const int lbg = (int)((gid / NFV) % nLeft);
-    const int bh = (int)(gid / ((size_t)NFV * nLeft));
-    int p = 0, lb = lbg;
-    for (;;) {
-        const int cnt = ((nL >> p) + 1) >> 1;
-        if (lb < cnt)
-            break;
-        lb -= cnt;
-        ++p;
+    float G[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+        G[i] = gsh[i];
+
+    // Where this element sits inside a block state stored in B-operand order.
+    const int d = elem / F::DV, c = elem % F::DV;
+    const int u = d / F::KB, r = d % F::KB;
+    const int e = 4 * (r >> 4) + (r & 3), qd = (r & 15) >> 2;
+    const int fv = ((c >> 4) * F::NUK + u) * 64 + qd * 16 + (c & 15);
+    const size_t frag_off = (size_t)fv * F::EPL + e;
+
+    size_t offp = 0;  // first left block of level p0 + lv for this head
+    for (int pp = 0; pp < p0; ++pp)
+        offp += ((nL >> pp) + 1) >> 1;
+#pragma unroll
+    for (int lv = 0; lv < 6; ++lv) {
+        const int p = p0 + lv;
+        const int width = 64 >> lv;
+        const int J0 = base >> lv;
+#pragma unroll
+        for (int j = 0; j < width; ++j) {
+            const int J = J0 + j;
+            if (((J & 1) == 0) && ((int64_t)(J + 1) << p) <= nL)
+                Dg[((size_t)bh * nLeft + offp + (J >> 1)) * DKV + frag_off] = from_f32<T>(x[j]);
+        }
+        offp += ((nL >> p) + 1) >> 1;
+#pragma unroll
+        for (int j = 0; j < width / 2; ++j) {
+            x[j] = __expf(G[2 * j + 1]) * x[2 * j] + x[2 * j + 1];
+            G[j] = G[2 * j] + G[2 * j + 1];
+        }
     }
-    const int first = (2 * lb) << p;             // first group of the block
-    const int last = first + (1 << p) - 1;       // last group of the block
-    const int w = fv / (F::NUK * 64), u = (fv / 64) % F::NUK, lane = fv % 64;
-    const int qd = lane >> 4, col = 16 * w + (lane & 15);
-    float acc[F::EPL];
-#pragma unroll
-    for (int e = 0; e < F::EPL; ++e)
-        acc[e] = 0.f;
-    float grun = 0.f;  // log-decay from the end of group gam to the end of the block
-    for (int gam = last; gam >= first; --gam) {
-        const float *src = Sg + ((size_t)bh * nL + gam) * F::DK * F::DV;
-        const float dec = __expf(grun);
-#pragma unroll
-        for (int e = 0; e < F::EPL; ++e)
-            acc[e] += dec * src[(u * F::KB + unit_row(e, qd)) * F::DV + col];
-        grun += Gam[(size_t)bh * nG + gam];
+    if (base + 64 <= nleaves && tot != nullptr) {
+        tot[((size_t)bh * tstride + tile) * DKV + elem] = x[0];
+        if (elem == 0)
+            gtot[(size_t)bh * tstride + tile] = G[0];
     }
-    T vals[F::EPL];
-#pragma unroll
-    for (int e = 0; e < F::EPL; ++e)
-        vals[e] = from_f32<T>(acc[e]);
-    *reinterpret_cast<uint4 *>(Dg + ((size_t)bh * nLeft + lbg) * F::DK * F::DV + (size_t)fv * F::EPL) =
-        *reinterpret_cast<const uint4 *>(vals);
 }
 
 // ---------------------------------------------------------------------------
 // Kernel C: the chunk walk.
 // ---------------------------------------------------------------------------
 template <class F>
-__global__ __launch_bounds__(F::NT) void ll_chunk_walk(
+struct WalkRegs {
+    uint4 q[F::NQ], k[F::NQ], v0[F::NVP], v1[F::NVP];
+    float lam[F::NLAM];
+    float a;
+};
+
+template <class F>
+__device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q, const typename F::T *k,
+                                          const typename F::T *v, const float *a, const float *lam, size_t row0,
+                                          int valid, int L, int tid)
+{
+    constexpr int QPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NQ; ++i) {
+        const int idx = tid + i * F::NT;
+        const int j = idx / QPR, c = idx % QPR;
+        r.q[i] = r.k[i] = zero16();
+        if (idx < F::QVEC && j < valid) {
+            r.q[i] = *reinterpret_cast<const uint4 *>(q + (row0 + j) * F::DK + c * F::VEC);
+            r.k[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j) * F::DK + c * F::VEC);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NVP; ++i) {
+        const int idx = tid + i * F::NT;
+        const int j = 2 * (idx / VPR), c = idx % VPR;
+        r.v0[i] = r.v1[i] = zero16();
+        if (idx < F::VPAIR && j < valid)
+            r.v0[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j) * F::DV + c * F::VEC);
+        if (idx < F::VPAIR && j + 1 < valid)
+            r.v1[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j + 1) * F::DV + c * F::VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = tid + i * F::NT;
+        const int j = idx / kMaxLevels, l = idx % kMaxLevels;
+        r.lam[i] = (idx < F::C * kMaxLevels && j < valid && l < L) ? lam[(row0 + j) * L + l] : 0.f;
+    }
+    r.a = (tid < valid) ? a[row0 + tid] : 0.f;
+}
+
+template <class F>
+__device__ __forceinline__ void walk_store(const WalkRegs<F> &r, WalkSmem<F> &sm, int tid)
+{
+    constexpr int QPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NQ; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < F::QVEC) {
+            const int j = idx / QPR, c = idx % QPR;
+            *reinterpret_cast<uint4 *>(sm.Qs + j * F::LDK + c * F::VEC) = r.q[i];
+            *reinterpret_cast<uint4 *>(sm.Ks + j * F::LDK + c * F::VEC) = r.k[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NVP; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < F::VPAIR)
+            store_pair_t<F>(sm.Vts, r.v0[i], r.v1[i], 2 * (idx / VPR), idx % VPR, 1.f, 1.f, false);
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < F::C * kMaxLevels)
+            sm.lam[idx] = r.lam[i];
+    }
+    scan_decay<F>(r.a, sm.Aloc, &sm.gch, tid);
+}
+
+// The walk works in transposed form: it forms S^T = K Q^T, so the masked
+// tiles P^T are already in the register layout the B operand of
+// O^T = V^T P^T needs (no LDS round trip for P), and every level adds
+// D^T Q^T with the same Q^T fragments, which each wave loads from LDS once
+// per chunk.  A wave owns 16 rows of O^T (16 output columns) and all query
+// rows of the chunk; the per-query factors then vary along the accumulator's
+// column, one value per lane and tile.
+
+// O^T += (D^T Q^T) * f, f_i = lambda[i, lev] * exp(Aloc[i] + base), for one
+// level whose state D is given as fragments (B operand of Q D, which is the
+// A operand of D^T Q^T).
+template <class F>
+__device__ __forceinline__ void level_update(floatx4 *O, const typename F::Frag (*qf)[F::NUK],
+                                             const typename F::Frag *d, const float *lam_s, const float *ai,
+                                             int lev, float base, int li)
+{
+#pragma unroll
+    for (int it = 0; it < F::NMT; ++it) {
+        floatx4 tmp = zero4();
+#pragma unroll
+        for (int u = 0; u < F::NUK; ++u)
+            mma_unit(tmp, d[u], qf[it][u]);
+        const int i = 16 * it + li;
+        const float f = lam_s[i * kMaxLevels + lev] * __expf(ai[it] + base);
+        O[it] += f * tmp;
+    }
+}
+
+template <class F>
+__global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
     int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
@@ -292,16 +477,33 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
 {
     using T = typename F::T;
     using Frag = typename F::Frag;
+    using DTag = typename F::DTag;
+    constexpr int NJT = F::CP / 16;  // key tiles covered by the PV units (zero padded past C)
     __shared__ WalkSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x / nG, sg = blockIdx.x % nG;
     const int G = 1 << g;
     const int nchunk = min(G, N - sg * G);
 
-    zero_pad_cols<F, F::DK>(sm.Kts, tid);
-    zero_pad_cols<F, F::DV>(sm.Vts, tid);
-    zero_pad_cols<F, F::C>(sm.Ps, tid);
+    WalkRegs<F> pf;
+    walk_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
+                 min(F::C, Tlen - sg * G * F::C), L, tid);
 
+    lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
+    lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
+    if (tid == 0) {
+        int n = 0;
+        size_t off = 0;
+        for (int p = 0; p < Plev; ++p) {
+            if ((sg >> p) & 1) {
+                sm.plist[n] = p;
+                sm.blk[n] = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * F::DK * F::DV;
+                ++n;
+            }
+            off += ((nL >> p) + 1) >> 1;
+        }
+        sm.npop = n;
+    }
     // Log-decay from the end of each inter-group block to the start of this
     // group: the sum of the group totals strictly between them.
     if (w == 0) {
@@ -320,12 +522,31 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
         }
     }
 
-    floatx4 stack[kMaxGroupLog2][F::NDT];
+    __syncthreads();
+    const int npop = sm.npop;
+    // The first NRES inter-group levels stay in registers for the whole
+    // group; further levels stream from L2.
+    Frag bres[F::NRES][F::NUK];
 #pragma unroll
-    for (int m = 0; m < kMaxGroupLog2; ++m)
+    for (int ii = 0; ii < F::NRES; ++ii)
 #pragma unroll
-        for (int rt = 0; rt < F::NDT; ++rt)
-            stack[m][rt] = zero4();
+        for (int u = 0; u < F::NUK; ++u)
+            bres[ii][u] = (ii < npop)
+                ? *reinterpret_cast<const Frag *>(Dg + sm.blk[ii] + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL)
+                : Frag{};
+
+    // Fenwick stack of the levels inside the group, in fragment form.  Slot
+    // m holds the bucket of bit m of the local chunk index, decayed to its own
+    // end; gap[m] is the log-decay from that end to the current chunk start.
+    Frag stk[kMaxGroupLog2][F::NUK];
+    float gap[kMaxGroupLog2];
+#pragma unroll
+    for (int m = 0; m < kMaxGroupLog2; ++m) {
+        gap[m] = 0.f;
+#pragma unroll
+        for (int u = 0; u < F::NUK; ++u)
+            stk[m][u] = Frag{};
+    }
     float agrun = 0.f;  // log-decay from the group start to the current chunk start
 
     for (int ci = 0; ci < nchunk; ++ci) {
@@ -333,145 +554,157 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
         const int valid = min(F::C, Tlen - t0);
         const size_t row0 = (size_t)bh * Tlen + t0;
         __syncthreads();
-        stage_rows<F, F::DK>(sm.Qs, q + row0 * F::DK, valid, tid);
-        stage_rows<F, F::DK>(sm.Ks, k + row0 * F::DK, valid, tid);
-        stage_transposed<F, F::DV, false>(sm.Vts, v + row0 * F::DV, F::DV, valid, nullptr, 0.f, tid);
-        stage_decay<F>(sm.Aloc, &sm.gch, a + row0, valid, tid);
-        for (int idx = tid; idx < F::C * kMaxLevels; idx += F::NT) {
-            const int j = idx / kMaxLevels, l = idx % kMaxLevels;
-            sm.lam[idx] = (j < valid && l < L) ? lam[(row0 + j) * L + l] : 0.f;
-        }
+        walk_store<F>(pf, sm, tid);
+        if (ci + 1 < nchunk)
+            walk_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, tid);
         __syncthreads();
         const float gch = sm.gch;
-        stage_transposed<F, F::DK, true>(sm.Kts, sm.Ks, F::LDK, valid, sm.Aloc, gch, tid);
+        stage_kt_from_lds<F>(sm.Kts, sm.Ks, sm.Aloc, gch, tid);
 
-        // Intra-chunk scores, masked by decay and the level weight.
-        for (int tile = w; tile < F::NMT * F::NMT; tile += F::NW) {
-            const int mt = tile / F::NMT, nt = tile % F::NMT;
-            floatx4 s = zero4();
-            if (nt <= mt) {
+        // Fragments reused for the whole chunk: Q^T (B operand, every query
+        // tile), V^T (A operand of the PV product, this wave's columns), and
+        // the decay of this lane's query rows.
+        Frag qf[F::NMT][F::NUK];
+        float ai[F::NMT];
 #pragma unroll
-                for (int u = 0; u < F::NUK; ++u)
-                    mma_unit(s, lds_frag(sm.Qs, F::LDK, 16 * mt + li, u * F::KB, qd),
-                             lds_frag(sm.Ks, F::LDK, 16 * nt + li, u * F::KB, qd));
-                const int j = 16 * nt + li;
-                const float aj = sm.Aloc[j];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * qd + r;
-                    float m = 0.f;
-                    if (j <= i) {
-                        const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                        m = __expf(sm.Aloc[i] - aj) * sm.lam[i * kMaxLevels + lev];
-                    }
-                    s[r] *= m;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm.Ps[(16 * mt + 4 * qd + r) * F::LDC + 16 * nt + li] = from_f32<T>(s[r]);
-        }
-        __syncthreads();
-
-        // O = P V for this wave's 16 output columns.
-        floatx4 O[F::NMT];
-#pragma unroll
-        for (int mt = 0; mt < F::NMT; ++mt) {
-            O[mt] = zero4();
-#pragma unroll
-            for (int u = 0; u < F::NUC; ++u)
-                if (u * F::KB <= 16 * mt + 15)
-                    mma_unit(O[mt], lds_frag(sm.Ps, F::LDC, 16 * mt + li, u * F::KB, qd),
-                             lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd));
-        }
-
-        // Levels inside the group: stack slot m holds the bucket of bit m of
-        // ci, decayed to the end of the previous chunk.
-#pragma unroll
-        for (int m = 0; m < kMaxGroupLog2; ++m) {
-            if (m < g && ((ci >> m) & 1)) {
-                const int lev = log2C + m + 1;
-#pragma unroll
-                for (int mt = 0; mt < F::NMT; ++mt) {
-                    floatx4 tmp = zero4();
-#pragma unroll
-                    for (int u = 0; u < F::NUK; ++u)
-                        mma_unit(tmp, lds_frag(sm.Qs, F::LDK, 16 * mt + li, u * F::KB, qd),
-                                 acc_frag(stack[m], u, typename F::DTag{}));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int i = 16 * mt + 4 * qd + r;
-                        O[mt][r] += sm.lam[i * kMaxLevels + lev] * __expf(sm.Aloc[i]) * tmp[r];
-                    }
-                }
-            }
-        }
-
-        // Levels above the group: left-child block states from kernel B.
-        for (int p = 0; p < Plev; ++p) {
-            if (!((sg >> p) & 1))
-                continue;
-            int offp = 0;
-            for (int pp = 0; pp < p; ++pp)
-                offp += ((nL >> pp) + 1) >> 1;
-            const T *blk = Dg + ((size_t)bh * nLeft + offp + (sg >> (p + 1))) * F::DK * F::DV;
-            Frag bfr[F::NUK];
+        for (int it = 0; it < F::NMT; ++it) {
+            ai[it] = sm.Aloc[16 * it + li];
 #pragma unroll
             for (int u = 0; u < F::NUK; ++u)
-                bfr[u] = *reinterpret_cast<const Frag *>(blk + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL);
-            const int lev = log2C + g + 1 + p;
-            const float base = agrun + sm.off[p];
+                qf[it][u] = lds_frag(sm.Qs, F::LDK, 16 * it + li, u * F::KB, qd);
+        }
+        Frag vf[F::NUC];
 #pragma unroll
-            for (int mt = 0; mt < F::NMT; ++mt) {
-                floatx4 tmp = zero4();
+        for (int u = 0; u < F::NUC; ++u)
+            vf[u] = lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd);
+
+        // Intra-chunk: P^T tiles (key tile jt, query tile it), jt <= it.
+        floatx4 pt[F::NMT][NJT];
+#pragma unroll
+        for (int it = 0; it < F::NMT; ++it)
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt)
+                pt[it][jt] = zero4();
+#pragma unroll
+        for (int jt = 0; jt < F::NMT; ++jt) {
+            Frag kf[F::NUK];
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                kf[u] = lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd);
+            float aj[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                aj[r] = sm.Aloc[16 * jt + 4 * qd + r];
+#pragma unroll
+            for (int it = jt; it < F::NMT; ++it) {
+                floatx4 s = zero4();
 #pragma unroll
                 for (int u = 0; u < F::NUK; ++u)
-                    mma_unit(tmp, lds_frag(sm.Qs, F::LDK, 16 * mt + li, u * F::KB, qd), bfr[u]);
+                    mma_unit(s, kf[u], qf[it][u]);
+                const int i = 16 * it + li;
+                if (jt < it) {
+                    // every key of the tile sits in one bucket of query i
+                    const float lm = sm.lam[i * kMaxLevels + 4 + bitlen_u32((uint32_t)(it ^ jt))];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * mt + 4 * qd + r;
-                    O[mt][r] += sm.lam[i * kMaxLevels + lev] * __expf(sm.Aloc[i] + base) * tmp[r];
+                    for (int r = 0; r < 4; ++r)
+                        pt[it][jt][r] = s[r] * __expf(ai[it] - aj[r]) * lm;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * jt + 4 * qd + r;
+                        float m = 0.f;
+                        if (j <= i) {
+                            const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
+                            m = __expf(ai[it] - aj[r]) * sm.lam[i * kMaxLevels + lev];
+                        }
+                        pt[it][jt][r] = s[r] * m;
+                    }
                 }
             }
         }
 
-        // Output rows.
+        // O^T = V^T P^T for this wave's 16 output columns.
+        floatx4 O[F::NMT];
 #pragma unroll
-        for (int mt = 0; mt < F::NMT; ++mt)
+        for (int it = 0; it < F::NMT; ++it) {
+            O[it] = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * mt + 4 * qd + r;
-                if (i < valid)
-                    out[(row0 + i) * F::DV + 16 * w + li] = from_f32<T>(O[mt][r]);
-            }
+            for (int u = 0; u < F::NUC; ++u)
+                if (u * F::KB <= 16 * it + 15)
+                    mma_unit(O[it], vf[u], acc_frag(pt[it], u, DTag{}));
+        }
 
-        // Fold this chunk's state into the stack (Fenwick carry on ci + 1).
+        // Levels inside the group.
+#pragma unroll
+        for (int m = 0; m < kMaxGroupLog2; ++m)
+            if (m < g && ((ci >> m) & 1))
+                level_update<F>(O, qf, stk[m], sm.lam, ai, log2C + m + 1, gap[m], li);
+
+        // Levels above the group.
+#pragma unroll
+        for (int ii = 0; ii < F::NRES; ++ii)
+            if (ii < npop) {
+                const int p = sm.plist[ii];
+                level_update<F>(O, qf, bres[ii], sm.lam, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
+            }
+        for (int ii = F::NRES; ii < npop; ++ii) {
+            Frag bcur[F::NUK];
+            const T *blk = Dg + sm.blk[ii];
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                bcur[u] = *reinterpret_cast<const Frag *>(blk + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL);
+            const int p = sm.plist[ii];
+            level_update<F>(O, qf, bcur, sm.lam, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
+        }
+
+        // Output: lane holds O[i][16w + 4qd .. 16w + 4qd + 3] for i = 16it + li.
+#pragma unroll
+        for (int it = 0; it < F::NMT; ++it) {
+            const int i = 16 * it + li;
+            if (i < valid) {
+                T vals[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    vals[r] = from_f32<T>(O[it][r]);
+                T *dst = out + (row0 + i) * F::DV + 16 * w + 4 * qd;
+                if constexpr (sizeof(T) == 2)
+                    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(vals);
+                else
+                    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(vals);
+            }
+        }
+
+        // Fold this chunk's state into the stack (Fenwick carry on ci + 1):
+        // slots below the lowest zero bit of ci merge with it into slot kc.
         if (ci + 1 < nchunk) {
+            __syncthreads();  // K^T staged by every wave
             floatx4 Hn[F::NDT];
 #pragma unroll
             for (int rt = 0; rt < F::NDT; ++rt) {
                 Hn[rt] = zero4();
 #pragma unroll
                 for (int u = 0; u < F::NUC; ++u)
-                    mma_unit(Hn[rt], lds_frag(sm.Kts, F::LDC, 16 * rt + li, u * F::KB, qd),
-                             lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd));
+                    mma_unit(Hn[rt], lds_frag(sm.Kts, F::LDC, 16 * rt + li, u * F::KB, qd), vf[u]);
             }
-            const float dec = __expf(gch);
             const int kc = __builtin_ctz((unsigned)(ci + 1));
 #pragma unroll
-            for (int m = 0; m < kMaxGroupLog2; ++m)
+            for (int m = 0; m < kMaxGroupLog2; ++m) {
+                gap[m] += gch;
+                if (m < kc) {
+                    const float s = __expf(gap[m]);
 #pragma unroll
-                for (int rt = 0; rt < F::NDT; ++rt) {
-                    stack[m][rt] *= dec;
-                    if (m < kc)
-                        Hn[rt] += stack[m][rt];
+                    for (int u = 0; u < F::NUK; ++u)
+                        frag_axpy(Hn, stk[m][u], u, s, DTag{});
                 }
+            }
 #pragma unroll
             for (int m = 0; m < kMaxGroupLog2; ++m)
-                if (m == kc)
+                if (m == kc) {
 #pragma unroll
-                    for (int rt = 0; rt < F::NDT; ++rt)
-                        stack[m][rt] = Hn[rt];
+                    for (int u = 0; u < F::NUK; ++u)
+                        stk[m][u] = acc_frag(Hn, u, DTag{});
+                    gap[m] = 0.f;
+                }
         }
         agrun += gch;
     }
@@ -500,9 +733,9 @@ FwdPlan fwd_plan(int B, int H, int T, int dk, int dv, int chunk, int group_log2,
     p.N = (T + chunk - 1) / chunk;
     int g = group_log2;
     if (g < 0) {
-        // Largest group that still gives about four workgroups per CU.
+        // Largest group that still gives two resident workgroups per CU.
         g = 0;
-        while (g < kMaxGroupLog2 && (2 << g) <= p.N && BH * ((p.N + (2 << g) - 1) / (2 << g)) >= 1024)
+        while (g < kMaxGroupLog2 && (2 << g) <= p.N && BH * ((p.N + (2 << g) - 1) / (2 << g)) >= 512)
             ++g;
     }
     if (g > kMaxGroupLog2)
@@ -516,10 +749,13 @@ FwdPlan fwd_plan(int B, int H, int T, int dk, int dv, int chunk, int group_log2,
     for (int lv = 0; lv < p.Plev; ++lv)
         p.nLeft += ((p.nL >> lv) + 1) >> 1;
     const size_t state = (size_t)dk * dv;
+    const size_t ntile = (size_t)(p.nL + 63) / 64;
     p.off_Sg = 0;
     p.off_Gam = align256(p.off_Sg + (size_t)BH * p.nL * state * 4);
     p.off_Dg = align256(p.off_Gam + (size_t)BH * p.nG * 4);
-    p.bytes = (p.nL > 0) ? align256(p.off_Dg + (size_t)BH * p.nLeft * state * elem_bytes) : 0;
+    p.off_tot = align256(p.off_Dg + (size_t)BH * p.nLeft * state * elem_bytes);
+    p.off_gtot = align256(p.off_tot + 2 * (size_t)BH * ntile * state * 4);
+    p.bytes = (p.nL > 0) ? align256(p.off_gtot + 2 * (size_t)BH * ntile * 4) : 0;
     return p;
 }
 
@@ -541,15 +777,34 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-        constexpr int NFV = F::DK * F::DV / F::EPL;
-        const size_t threads = (size_t)BH * P.nLeft * NFV;
-        prof_before("ll_left_blocks", s);
-        hipLaunchKernelGGL(ll_left_blocks<F>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                           (const float *)Sg, (const float *)Gam, BH, P.nG, P.nL, P.nLeft, Dg);
-        prof_after(s);
-        e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
+        // Tree over groups, 64 leaves per tile and six levels per launch.
+        const size_t ntile_max = (size_t)(P.nL + 63) / 64;
+        float *tot[2] = {reinterpret_cast<float *>(ws + P.off_tot),
+                         reinterpret_cast<float *>(ws + P.off_tot) + (size_t)BH * ntile_max * F::DK * F::DV};
+        float *gtot[2] = {reinterpret_cast<float *>(ws + P.off_gtot),
+                          reinterpret_cast<float *>(ws + P.off_gtot) + (size_t)BH * ntile_max};
+        const float *leaves = Sg, *gleaves = Gam;
+        int nleaves = P.nL, lstride = P.nL, gstride = P.nG, p0 = 0, ping = 0;
+        while (nleaves > 0) {
+            const int ntiles = (nleaves + 63) / 64;
+            const int complete = nleaves / 64;
+            prof_before("ll_left_tree", s);
+            hipLaunchKernelGGL(ll_left_tree<F>, dim3((F::DK * F::DV + 255) / 256, ntiles, BH), dim3(256), 0, s,
+                               leaves, gleaves, nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg,
+                               complete > 0 ? tot[ping] : nullptr, gtot[ping], ntiles);
+            prof_after(s);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            if (complete == 0)
+                break;
+            leaves = tot[ping];
+            gleaves = gtot[ping];
+            lstride = gstride = ntiles;
+            nleaves = complete;
+            p0 += 6;
+            ping ^= 1;
+        }
     }
     prof_before("ll_chunk_walk", s);
     hipLaunchKernelGGL(ll_chunk_walk<F>, dim3(BH * P.nG), dim3(F::NT), 0, s, (const T *)A.q, (const T *)A.k,

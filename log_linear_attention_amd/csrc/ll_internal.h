@@ -17,7 +17,7 @@ constexpr int kMaxGroupLog2 = 3;   // local Fenwick stack depth of the chunk wal
 //  nL = nG - 1 complete groups that can precede another group.
 struct FwdPlan {
     int N = 0, g = 0, G = 1, nG = 0, nL = 0, Plev = 0, nLeft = 0;
-    size_t off_Sg = 0, off_Gam = 0, off_Dg = 0, bytes = 0;
+    size_t off_Sg = 0, off_Gam = 0, off_Dg = 0, off_tot = 0, off_gtot = 0, bytes = 0;
 };
 
 // group_log2 < 0 picks automatically.  elem_bytes is the size used for the

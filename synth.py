@@ -163,7 +163,7 @@ def make_decode_inputs(cfg: DecodeConfig, seed: int | None = None, positions=Non
         w = np.exp(-0.04 * np.arange(m))
         kk = _unit_rows(rng.standard_normal((S, H, m, dk)))
         vv = rng.standard_normal((S, H, m, dv))
-        state[:, :, slot] = np.einsum("shmd,shme->shde", kk * w[None, None, :, None], vv).astype(np.float32)
+        state[:, :, slot] = np.matmul(np.swapaxes(kk * w[None, None, :, None], -1, -2), vv).astype(np.float32)
     return {
         "q": _cast(q, cfg.dtype),
         "k": _cast(k, cfg.dtype),
