@@ -35,10 +35,50 @@
 // Nothing but the inputs, the output and the small group/block states touches
 // HBM; the per-chunk states of the levels inside a group never leave
 // registers.
+//
+// Operands whose contraction runs over tokens (K^T and V^T) are read on the
+// bf16 path straight from the row-major tiles with the CDNA4 LDS transpose
+// read (ds_read_b64_tr_b16); the fp32 path has no such instruction for 32-bit
+// elements and stores transposed copies instead.
 #include "ll_device.h"
 #include "ll_internal.h"
 
 namespace ll {
+
+// Row stride (in 16-bit elements) of a bf16 LDS tile with `cols` columns:
+// a multiple of 8 elements (16-byte rows) chosen so that (a) the 16 lanes of
+// a fragment read (rows li, 8 bytes each) and (b) the four 8-dword row
+// segments of a transpose read fall in distinct banks of the 64-bank LDS.
+constexpr bool stride_ok(int s, bool normal)
+{
+    bool used[64] = {};
+    if (normal) {
+        for (int li = 0; li < 16; ++li)
+            for (int d = 0; d < 2; ++d) {
+                const int b = (li * s + d) % 64;
+                if (used[b])
+                    return false;
+                used[b] = true;
+            }
+    }
+    bool used2[64] = {};
+    for (int r = 0; r < 4; ++r)
+        for (int d = 0; d < 8; ++d) {
+            const int b = (r * s + d) % 64;
+            if (used2[b])
+                return false;
+            used2[b] = true;
+        }
+    return true;
+}
+
+constexpr int bf16_stride(int cols, bool normal)
+{
+    int s = cols / 2;  // dwords
+    while (s % 4 != 0 || !stride_ok(s, normal))
+        ++s;
+    return 2 * s;
+}
 
 template <class DT, int DK_, int DV_, int C_>
 struct Fwd {
@@ -46,42 +86,44 @@ struct Fwd {
     using Frag = typename DT::Frag;
     using DTag = DT;
     static constexpr int DK = DK_, DV = DV_, C = C_;
+    static constexpr bool TR = DT::is_bf16;          // transpose reads available
     static constexpr int KB = DT::KB, EPL = DT::EPL;
     static constexpr int NW = DV / 16;           // waves: one 16-column slice of dv each
     static constexpr int NT = 64 * NW;
     static constexpr int WPE = 1;                 // resident waves per SIMD the walk is built for
-    static constexpr int NRES = DT::is_bf16 ? 4 : 2;  // inter-group levels kept in registers per group
+    static constexpr int NRES = TR ? 4 : 2;       // inter-group levels kept in registers per group
     static constexpr int NMT = C / 16;           // 16-row tiles per chunk
-    static constexpr int NCT = NMT * (NMT + 1) / 2;  // causal 16x16 score tiles
     static constexpr int CP = (C < KB) ? KB : C; // chunk contraction length (zero padded)
     static constexpr int NUC = CP / KB;          // units over chunk tokens
     static constexpr int NUK = DK / KB;          // units over dk
     static constexpr int NDT = DK / 16;          // accumulator tiles over dk rows
-    static constexpr int PADE = DT::is_bf16 ? 8 : 4;
-    static constexpr int LDK = DK + PADE;        // LDS row stride of Q, K tiles
-    static constexpr int LDC = CP + PADE;        // LDS row stride of K^T, V^T, P tiles
+    static constexpr int LDK = TR ? bf16_stride(DK, true) : DK + 4;   // Q, K row stride
+    static constexpr int LDV = TR ? bf16_stride(DV, false) : DV + 4;  // V row stride
+    static constexpr int LDC = CP + 4;           // fp32 transposed tiles K^T, V^T
+    static constexpr int LDL = C + 1;            // lambda^T row stride
     static constexpr int VEC = 16 / (int)sizeof(T);
     // register prefetch of one chunk
-    static constexpr int QVEC = C * (DK / VEC);              // 16-byte vectors of a q (or k) chunk
+    static constexpr int QVEC = C * (DK / VEC);  // 16-byte vectors of a q (or k) chunk
     static constexpr int NQ = (QVEC + NT - 1) / NT;
-    static constexpr int KPAIR = (C / 2) * (DK / VEC);       // k row-pair vectors
-    static constexpr int NKP = (KPAIR + NT - 1) / NT;
-    static constexpr int VPAIR = (C / 2) * (DV / VEC);       // v row-pair vectors
-    static constexpr int NVP = (VPAIR + NT - 1) / NT;
+    static constexpr int VVEC = C * (DV / VEC);
+    static constexpr int NV = (VVEC + NT - 1) / NT;
     static constexpr int NLAM = (C * kMaxLevels + NT - 1) / NT;
     static_assert(DK % KB == 0, "dk must be a multiple of the MFMA unit");
     static_assert(DV % 16 == 0 && DV <= 128, "dv must be 16..128 in steps of 16");
     static_assert(C <= 64, "the decay scan handles at most one wave of tokens");
 };
 
+// Row-major q/k/v tiles (k and v padded with zero rows up to CP), lambda^T,
+// and on the fp32 path the transposed copies of k and v.
 template <class F>
 struct alignas(16) WalkSmem {
     using T = typename F::T;
     T Qs[F::C * F::LDK];
-    T Ks[F::C * F::LDK];
-    T Kts[F::DK * F::LDC];
-    T Vts[F::DV * F::LDC];
-    float lam[F::C * kMaxLevels];
+    T Ks[F::CP * F::LDK];
+    T Vs[F::TR ? F::CP * F::LDV : 8];
+    T Kts[F::TR ? 8 : F::DK * F::LDC];
+    T Vts[F::TR ? 8 : F::DV * F::LDC];
+    float lamT[kMaxLevels * F::LDL];
     float Aloc[F::C];
     float off[32];          // log-decay from each inter-group block's end to the group start
     size_t blk[32];         // element offset of each inter-group block state
@@ -93,8 +135,10 @@ struct alignas(16) WalkSmem {
 template <class F>
 struct alignas(16) StateSmem {
     using T = typename F::T;
-    T Kts[F::DK * F::LDC];
-    T Vts[F::DV * F::LDC];
+    T Ks[F::TR ? F::CP * F::LDK : 8];
+    T Vs[F::TR ? F::CP * F::LDV : 8];
+    T Kts[F::TR ? 8 : F::DK * F::LDC];
+    T Vts[F::TR ? 8 : F::DV * F::LDC];
     float Aloc[F::C];
     float gch;
 };
@@ -105,7 +149,6 @@ struct alignas(16) StateSmem {
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0, 0, 0, 0); }
 
-// Zero a whole LDS array (used once per workgroup).
 template <class F, class E>
 __device__ __forceinline__ void lds_zero(E *dst, int n, int tid)
 {
@@ -133,45 +176,90 @@ __device__ __forceinline__ void scan_decay(float x, float *Aloc, float *gch, int
     }
 }
 
-// Store a pair of rows j, j+1 (given as two 16-byte vectors of VEC elements
-// starting at column c*VEC) transposed into dst[col][j], optionally scaled.
-template <class F>
-__device__ __forceinline__ void store_pair_t(typename F::T *dst, const uint4 &x0, const uint4 &x1, int j, int c,
-                                             float w0, float w1, bool scale)
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Fragment whose k-index runs over tokens (rows of a row-major bf16 LDS
+// tile): rows jb .. jb+31, columns c0 + li.  Lane (li, qd) gets rows
+// jb + 16*(e/4) + 4*qd + e%4 of column c0 + li, the same permuted k order as
+// lds_frag.  Each half is one transpose read in which lane p of a 16-lane
+// block addresses the 4-element row segment (row jb + 4*qd + p/4, columns
+// c0 + 4*(p%4) ..).
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *base, int ld, int jb, int c0, int li, int qd)
 {
-    using T = typename F::T;
-    const T *e0 = reinterpret_cast<const T *>(&x0);
-    const T *e1 = reinterpret_cast<const T *>(&x1);
+    const __bf16 *p = base + (jb + 4 * qd + (li >> 2)) * ld + c0 + 4 * (li & 3);
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 16 * ld));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Scale the token-indexed fragment f of unit u by w_j = exp(g - Aloc[j])
+// (the decay from token j to the chunk end); padding tokens j >= C get 0.
+template <class F>
+__device__ __forceinline__ floatx4 scale_tokens(const floatx4 &f, int u, const float *Aloc, float gch, int qd)
+{
+    floatx4 r;
 #pragma unroll
-    for (int x = 0; x < F::VEC; ++x) {
-        T p0 = e0[x], p1 = e1[x];
-        if (scale) {
-            p0 = from_f32<T>(to_f32(e0[x]) * w0);
-            p1 = from_f32<T>(to_f32(e1[x]) * w1);
-        }
-        T *d = dst + (c * F::VEC + x) * F::LDC + j;
-        d[0] = p0;
-        d[1] = p1;
+    for (int e = 0; e < 4; ++e) {
+        const int j = u * F::KB + unit_row(e, qd);
+        r[e] = (j < F::C) ? f[e] * __expf(gch - Aloc[j]) : 0.f;
     }
+    return r;
 }
 
-// K^T (row-major LDS K tile, scaled per token by w_j = exp(g - Aloc[j]))
-// into the transposed tile Kts.
 template <class F>
-__device__ __forceinline__ void stage_kt_from_lds(typename F::T *Kts, const typename F::T *Ks, const float *Aloc,
-                                                  float gch, int tid)
+__device__ __forceinline__ bf16x8 scale_tokens(const bf16x8 &f, int u, const float *Aloc, float gch, int qd)
 {
-    constexpr int VPR = F::DK / F::VEC;
-    for (int idx = tid; idx < F::KPAIR; idx += F::NT) {
-        const int j = 2 * (idx / VPR), c = idx % VPR;
-        const uint4 x0 = *reinterpret_cast<const uint4 *>(Ks + j * F::LDK + c * F::VEC);
-        const uint4 x1 = *reinterpret_cast<const uint4 *>(Ks + (j + 1) * F::LDK + c * F::VEC);
-        store_pair_t<F>(Kts, x0, x1, j, c, __expf(gch - Aloc[j]), __expf(gch - Aloc[j + 1]), true);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int j = u * F::KB + unit_row(e, qd);
+        r[e] = (__bf16)((j < F::C) ? (float)f[e] * __expf(gch - Aloc[j]) : 0.f);
+    }
+    return r;
+}
+
+// Fragments over tokens for the current chunk: K^T with rows d = 16*rt + li
+// (A operand of the chunk state) and V with column e = 16*w + li (A operand
+// of O^T = V^T P^T and B operand of the chunk state).
+template <class F, class S>
+__device__ __forceinline__ typename F::Frag kt_frag(const S &sm, int rt, int u, int li, int qd)
+{
+    if constexpr (F::TR)
+        return tr_frag(sm.Ks, F::LDK, u * F::KB, 16 * rt, li, qd);
+    else
+        return lds_frag(sm.Kts, F::LDC, 16 * rt + li, u * F::KB, qd);
+}
+
+template <class F, class S>
+__device__ __forceinline__ typename F::Frag v_frag(const S &sm, int w, int u, int li, int qd)
+{
+    if constexpr (F::TR)
+        return tr_frag(sm.Vs, F::LDV, u * F::KB, 16 * w, li, qd);
+    else
+        return lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd);
+}
+
+// Store a 16-byte vector holding row j, columns c*VEC .. of a tile: row-major
+// (transpose-read path) or into the transposed copy (fp32 path).
+template <class F>
+__device__ __forceinline__ void store_row_vec(typename F::T *rowmajor, int ld, typename F::T *transposed, int j,
+                                              int c, const uint4 &x)
+{
+    if constexpr (F::TR) {
+        *reinterpret_cast<uint4 *>(rowmajor + j * ld + c * F::VEC) = x;
+    } else {
+        const typename F::T *e = reinterpret_cast<const typename F::T *>(&x);
+#pragma unroll
+        for (int i = 0; i < F::VEC; ++i)
+            transposed[(c * F::VEC + i) * F::LDC + j] = e[i];
     }
 }
 
-// Unpack a B-operand fragment of unit u back into fp32 accumulator tiles,
-// adding s * value (inverse of acc_frag).
+// Unpack a fragment of unit u back into fp32 accumulator tiles, adding
+// s * value (inverse of acc_frag).
 __device__ __forceinline__ void frag_axpy(floatx4 *tiles, const floatx4 &f, int u, float s, TF32)
 {
 #pragma unroll
@@ -193,7 +281,7 @@ __device__ __forceinline__ void frag_axpy(floatx4 *tiles, const bf16x8 &f, int u
 // ---------------------------------------------------------------------------
 template <class F>
 struct StateRegs {
-    uint4 k0[F::NKP], k1[F::NKP], v0[F::NVP], v1[F::NVP];
+    uint4 k[F::NQ], v[F::NV];
     float a;
 };
 
@@ -203,24 +291,18 @@ __device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T 
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
-    for (int i = 0; i < F::NKP; ++i) {
+    for (int i = 0; i < F::NQ; ++i) {
         const int idx = tid + i * F::NT;
-        const int j = 2 * (idx / KPR), c = idx % KPR;
-        r.k0[i] = r.k1[i] = zero16();
-        if (idx < F::KPAIR) {
-            r.k0[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j) * F::DK + c * F::VEC);
-            r.k1[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j + 1) * F::DK + c * F::VEC);
-        }
+        r.k[i] = zero16();
+        if (idx < F::QVEC)
+            r.k[i] = *reinterpret_cast<const uint4 *>(k + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
     }
 #pragma unroll
-    for (int i = 0; i < F::NVP; ++i) {
+    for (int i = 0; i < F::NV; ++i) {
         const int idx = tid + i * F::NT;
-        const int j = 2 * (idx / VPR), c = idx % VPR;
-        r.v0[i] = r.v1[i] = zero16();
-        if (idx < F::VPAIR) {
-            r.v0[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j) * F::DV + c * F::VEC);
-            r.v1[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j + 1) * F::DV + c * F::VEC);
-        }
+        r.v[i] = zero16();
+        if (idx < F::VVEC)
+            r.v[i] = *reinterpret_cast<const uint4 *>(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
     }
     r.a = (tid < F::C) ? a[row0 + tid] : 0.f;
 }
@@ -231,14 +313,20 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
                                                         const float *__restrict__ a, int Tlen, int g, int nG,
                                                         int nL, float *__restrict__ Sg, float *__restrict__ Gam)
 {
+    using Frag = typename F::Frag;
     __shared__ StateSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x / nL, sg = blockIdx.x % nL;
     const int G = 1 << g;
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 
-    lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
-    lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
+    if constexpr (F::TR) {
+        lds_zero<F>(sm.Ks, F::CP * F::LDK, tid);
+        lds_zero<F>(sm.Vs, F::CP * F::LDV, tid);
+    } else {
+        lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
+        lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
+    }
 
     floatx4 S[F::NDT];
 #pragma unroll
@@ -251,34 +339,33 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
     for (int ci = 0; ci < G; ++ci) {
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < F::NVP; ++i) {
+        for (int i = 0; i < F::NQ; ++i) {
             const int idx = tid + i * F::NT;
-            if (idx < F::VPAIR)
-                store_pair_t<F>(sm.Vts, pf.v0[i], pf.v1[i], 2 * (idx / VPR), idx % VPR, 1.f, 1.f, false);
+            if (idx < F::QVEC)
+                store_row_vec<F>(sm.Ks, F::LDK, sm.Kts, idx / KPR, idx % KPR, pf.k[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < F::NV; ++i) {
+            const int idx = tid + i * F::NT;
+            if (idx < F::VVEC)
+                store_row_vec<F>(sm.Vs, F::LDV, sm.Vts, idx / VPR, idx % VPR, pf.v[i]);
         }
         scan_decay<F>(pf.a, sm.Aloc, &sm.gch, tid);
-        __syncthreads();
-        const float gch = sm.gch;
-#pragma unroll
-        for (int i = 0; i < F::NKP; ++i) {
-            const int idx = tid + i * F::NT;
-            if (idx < F::KPAIR) {
-                const int j = 2 * (idx / KPR);
-                store_pair_t<F>(sm.Kts, pf.k0[i], pf.k1[i], j, idx % KPR, __expf(gch - sm.Aloc[j]),
-                                __expf(gch - sm.Aloc[j + 1]), true);
-            }
-        }
         if (ci + 1 < G)
             state_load<F>(pf, k, v, a, (size_t)bh * Tlen + ((size_t)sg * G + ci + 1) * F::C, tid);
         __syncthreads();
+        const float gch = sm.gch;
         const float dec = __expf(gch);
+        Frag vs[F::NUC];
+#pragma unroll
+        for (int u = 0; u < F::NUC; ++u)
+            vs[u] = scale_tokens<F>(v_frag<F>(sm, w, u, li, qd), u, sm.Aloc, gch, qd);
 #pragma unroll
         for (int rt = 0; rt < F::NDT; ++rt) {
             S[rt] *= dec;
 #pragma unroll
             for (int u = 0; u < F::NUC; ++u)
-                mma_unit(S[rt], lds_frag(sm.Kts, F::LDC, 16 * rt + li, u * F::KB, qd),
-                         lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd));
+                mma_unit(S[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
         }
         gsum += gch;
     }
@@ -369,10 +456,18 @@ __global__ __launch_bounds__(256) void ll_left_tree(const float *__restrict__ le
 
 // ---------------------------------------------------------------------------
 // Kernel C: the chunk walk.
+//
+// The walk works in transposed form: it forms S^T = K Q^T, so the masked
+// tiles P^T are already in the register layout the B operand of
+// O^T = V^T P^T needs (no LDS round trip for P), and every level adds
+// D^T Q^T with the same Q^T fragments, which each wave loads from LDS once
+// per chunk.  A wave owns 16 rows of O^T (16 output columns) and all query
+// rows of the chunk; the per-query factors vary along the accumulator's
+// column, one value per lane and tile.
 // ---------------------------------------------------------------------------
 template <class F>
 struct WalkRegs {
-    uint4 q[F::NQ], k[F::NQ], v0[F::NVP], v1[F::NVP];
+    uint4 q[F::NQ], k[F::NQ], v[F::NV];
     float lam[F::NLAM];
     float a;
 };
@@ -380,7 +475,7 @@ struct WalkRegs {
 template <class F>
 __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q, const typename F::T *k,
                                           const typename F::T *v, const float *a, const float *lam, size_t row0,
-                                          int valid, int L, int tid)
+                                          int valid, int L, float invL, int tid)
 {
     constexpr int QPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -394,26 +489,25 @@ __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q
         }
     }
 #pragma unroll
-    for (int i = 0; i < F::NVP; ++i) {
+    for (int i = 0; i < F::NV; ++i) {
         const int idx = tid + i * F::NT;
-        const int j = 2 * (idx / VPR), c = idx % VPR;
-        r.v0[i] = r.v1[i] = zero16();
-        if (idx < F::VPAIR && j < valid)
-            r.v0[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j) * F::DV + c * F::VEC);
-        if (idx < F::VPAIR && j + 1 < valid)
-            r.v1[i] = *reinterpret_cast<const uint4 *>(v + (row0 + j + 1) * F::DV + c * F::VEC);
+        r.v[i] = zero16();
+        if (idx < F::VVEC && idx / VPR < valid)
+            r.v[i] = *reinterpret_cast<const uint4 *>(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
     }
+    // lambda rows of the chunk are one contiguous block of valid * L floats
 #pragma unroll
     for (int i = 0; i < F::NLAM; ++i) {
         const int idx = tid + i * F::NT;
-        const int j = idx / kMaxLevels, l = idx % kMaxLevels;
-        r.lam[i] = (idx < F::C * kMaxLevels && j < valid && l < L) ? lam[(row0 + j) * L + l] : 0.f;
+        r.lam[i] = (idx < valid * L) ? lam[row0 * L + idx] : 0.f;
     }
     r.a = (tid < valid) ? a[row0 + tid] : 0.f;
+    (void)invL;
 }
 
 template <class F>
-__device__ __forceinline__ void walk_store(const WalkRegs<F> &r, WalkSmem<F> &sm, int tid)
+__device__ __forceinline__ void walk_store(const WalkRegs<F> &r, WalkSmem<F> &sm, int valid, int L, float invL,
+                                           int tid)
 {
     constexpr int QPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -423,37 +517,35 @@ __device__ __forceinline__ void walk_store(const WalkRegs<F> &r, WalkSmem<F> &sm
             const int j = idx / QPR, c = idx % QPR;
             *reinterpret_cast<uint4 *>(sm.Qs + j * F::LDK + c * F::VEC) = r.q[i];
             *reinterpret_cast<uint4 *>(sm.Ks + j * F::LDK + c * F::VEC) = r.k[i];
+            if constexpr (!F::TR)
+                store_row_vec<F>(sm.Ks, F::LDK, sm.Kts, j, c, r.k[i]);
         }
     }
 #pragma unroll
-    for (int i = 0; i < F::NVP; ++i) {
+    for (int i = 0; i < F::NV; ++i) {
         const int idx = tid + i * F::NT;
-        if (idx < F::VPAIR)
-            store_pair_t<F>(sm.Vts, r.v0[i], r.v1[i], 2 * (idx / VPR), idx % VPR, 1.f, 1.f, false);
+        if (idx < F::VVEC)
+            store_row_vec<F>(sm.Vs, F::LDV, sm.Vts, idx / VPR, idx % VPR, r.v[i]);
     }
+    // lambda^T: only the valid entries are written; levels >= L stay zero
+    // from the start of the kernel, and rows past a ragged chunk's end only
+    // feed query rows that are never stored.
 #pragma unroll
     for (int i = 0; i < F::NLAM; ++i) {
         const int idx = tid + i * F::NT;
-        if (idx < F::C * kMaxLevels)
-            sm.lam[idx] = r.lam[i];
+        if (idx < valid * L) {
+            const int j = (int)(((float)idx + 0.5f) * invL);
+            sm.lamT[(idx - j * L) * F::LDL + j] = r.lam[i];
+        }
     }
     scan_decay<F>(r.a, sm.Aloc, &sm.gch, tid);
 }
 
-// The walk works in transposed form: it forms S^T = K Q^T, so the masked
-// tiles P^T are already in the register layout the B operand of
-// O^T = V^T P^T needs (no LDS round trip for P), and every level adds
-// D^T Q^T with the same Q^T fragments, which each wave loads from LDS once
-// per chunk.  A wave owns 16 rows of O^T (16 output columns) and all query
-// rows of the chunk; the per-query factors then vary along the accumulator's
-// column, one value per lane and tile.
-
 // O^T += (D^T Q^T) * f, f_i = lambda[i, lev] * exp(Aloc[i] + base), for one
-// level whose state D is given as fragments (B operand of Q D, which is the
-// A operand of D^T Q^T).
+// level whose state D is given as fragments (A operand of D^T Q^T).
 template <class F>
 __device__ __forceinline__ void level_update(floatx4 *O, const typename F::Frag (*qf)[F::NUK],
-                                             const typename F::Frag *d, const float *lam_s, const float *ai,
+                                             const typename F::Frag *d, const float *lamT, const float *ai,
                                              int lev, float base, int li)
 {
 #pragma unroll
@@ -462,8 +554,7 @@ __device__ __forceinline__ void level_update(floatx4 *O, const typename F::Frag 
 #pragma unroll
         for (int u = 0; u < F::NUK; ++u)
             mma_unit(tmp, d[u], qf[it][u]);
-        const int i = 16 * it + li;
-        const float f = lam_s[i * kMaxLevels + lev] * __expf(ai[it] + base);
+        const float f = lamT[lev * F::LDL + 16 * it + li] * __expf(ai[it] + base);
         O[it] += f * tmp;
     }
 }
@@ -484,13 +575,21 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
     const int bh = blockIdx.x / nG, sg = blockIdx.x % nG;
     const int G = 1 << g;
     const int nchunk = min(G, N - sg * G);
+    const float invL = 1.f / (float)L;
 
     WalkRegs<F> pf;
     walk_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
-                 min(F::C, Tlen - sg * G * F::C), L, tid);
+                 min(F::C, Tlen - sg * G * F::C), L, invL, tid);
 
-    lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
-    lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
+    // Padding rows (CP > C) and the transposed copies start at zero.
+    lds_zero<F>(sm.Ks, F::CP * F::LDK, tid);
+    lds_zero<F>(sm.lamT, kMaxLevels * F::LDL, tid);
+    if constexpr (F::TR) {
+        lds_zero<F>(sm.Vs, F::CP * F::LDV, tid);
+    } else {
+        lds_zero<F>(sm.Kts, F::DK * F::LDC, tid);
+        lds_zero<F>(sm.Vts, F::DV * F::LDC, tid);
+    }
     if (tid == 0) {
         int n = 0;
         size_t off = 0;
@@ -554,16 +653,15 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
         const int valid = min(F::C, Tlen - t0);
         const size_t row0 = (size_t)bh * Tlen + t0;
         __syncthreads();
-        walk_store<F>(pf, sm, tid);
+        walk_store<F>(pf, sm, valid, L, invL, tid);
         if (ci + 1 < nchunk)
-            walk_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, tid);
+            walk_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, invL, tid);
         __syncthreads();
         const float gch = sm.gch;
-        stage_kt_from_lds<F>(sm.Kts, sm.Ks, sm.Aloc, gch, tid);
 
         // Fragments reused for the whole chunk: Q^T (B operand, every query
-        // tile), V^T (A operand of the PV product, this wave's columns), and
-        // the decay of this lane's query rows.
+        // tile), V (this wave's columns), and the decay of this lane's
+        // query rows.
         Frag qf[F::NMT][F::NUK];
         float ai[F::NMT];
 #pragma unroll
@@ -576,7 +674,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
         Frag vf[F::NUC];
 #pragma unroll
         for (int u = 0; u < F::NUC; ++u)
-            vf[u] = lds_frag(sm.Vts, F::LDC, 16 * w + li, u * F::KB, qd);
+            vf[u] = v_frag<F>(sm, w, u, li, qd);
 
         // Intra-chunk: P^T tiles (key tile jt, query tile it), jt <= it.
         floatx4 pt[F::NMT][NJT];
@@ -604,7 +702,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
                 const int i = 16 * it + li;
                 if (jt < it) {
                     // every key of the tile sits in one bucket of query i
-                    const float lm = sm.lam[i * kMaxLevels + 4 + bitlen_u32((uint32_t)(it ^ jt))];
+                    const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         pt[it][jt][r] = s[r] * __expf(ai[it] - aj[r]) * lm;
@@ -615,7 +713,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
                         float m = 0.f;
                         if (j <= i) {
                             const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                            m = __expf(ai[it] - aj[r]) * sm.lam[i * kMaxLevels + lev];
+                            m = __expf(ai[it] - aj[r]) * sm.lamT[lev * F::LDL + i];
                         }
                         pt[it][jt][r] = s[r] * m;
                     }
@@ -638,14 +736,14 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
 #pragma unroll
         for (int m = 0; m < kMaxGroupLog2; ++m)
             if (m < g && ((ci >> m) & 1))
-                level_update<F>(O, qf, stk[m], sm.lam, ai, log2C + m + 1, gap[m], li);
+                level_update<F>(O, qf, stk[m], sm.lamT, ai, log2C + m + 1, gap[m], li);
 
         // Levels above the group.
 #pragma unroll
         for (int ii = 0; ii < F::NRES; ++ii)
             if (ii < npop) {
                 const int p = sm.plist[ii];
-                level_update<F>(O, qf, bres[ii], sm.lam, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
+                level_update<F>(O, qf, bres[ii], sm.lamT, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
             }
         for (int ii = F::NRES; ii < npop; ++ii) {
             Frag bcur[F::NUK];
@@ -654,7 +752,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
             for (int u = 0; u < F::NUK; ++u)
                 bcur[u] = *reinterpret_cast<const Frag *>(blk + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL);
             const int p = sm.plist[ii];
-            level_update<F>(O, qf, bcur, sm.lam, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
+            level_update<F>(O, qf, bcur, sm.lamT, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
         }
 
         // Output: lane holds O[i][16w + 4qd .. 16w + 4qd + 3] for i = 16it + li.
@@ -674,17 +772,21 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
             }
         }
 
-        // Fold this chunk's state into the stack (Fenwick carry on ci + 1):
-        // slots below the lowest zero bit of ci merge with it into slot kc.
+        // Fold this chunk's state K^T diag(w) V into the stack (Fenwick carry
+        // on ci + 1): slots below the lowest zero bit of ci merge with it into
+        // slot kc.
         if (ci + 1 < nchunk) {
-            __syncthreads();  // K^T staged by every wave
+            Frag vs[F::NUC];
+#pragma unroll
+            for (int u = 0; u < F::NUC; ++u)
+                vs[u] = scale_tokens<F>(vf[u], u, sm.Aloc, gch, qd);
             floatx4 Hn[F::NDT];
 #pragma unroll
             for (int rt = 0; rt < F::NDT; ++rt) {
                 Hn[rt] = zero4();
 #pragma unroll
                 for (int u = 0; u < F::NUC; ++u)
-                    mma_unit(Hn[rt], lds_frag(sm.Kts, F::LDC, 16 * rt + li, u * F::KB, qd), vf[u]);
+                    mma_unit(Hn[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
             }
             const int kc = __builtin_ctz((unsigned)(ci + 1));
 #pragma unroll
