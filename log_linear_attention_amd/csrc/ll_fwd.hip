@@ -80,7 +80,10 @@ constexpr int bf16_stride(int cols, bool normal)
     return 2 * s;
 }
 
-template <class DT, int DK_, int DV_, int C_>
+// Tile geometry.  SPLIT (the chunk walk) gives each 16-column slice of dv
+// two waves that share the slice's state work and split the query tiles, so
+// one workgroup keeps two waves per SIMD within the 256-register budget.
+template <class DT, int DK_, int DV_, int C_, bool SPLIT = false>
 struct Fwd {
     using T = typename DT::T;
     using Frag = typename DT::Frag;
@@ -88,11 +91,12 @@ struct Fwd {
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr bool TR = DT::is_bf16;          // transpose reads available
     static constexpr int KB = DT::KB, EPL = DT::EPL;
-    static constexpr int NW = DV / 16;           // waves: one 16-column slice of dv each
-    static constexpr int NT = 64 * NW;
-    static constexpr int WPE = 1;                 // resident waves per SIMD the walk is built for
-    static constexpr int NRES = TR ? 4 : 2;       // inter-group levels kept in registers per group
     static constexpr int NMT = C / 16;           // 16-row tiles per chunk
+    static constexpr int NWC = DV / 16;          // 16-column slices of dv
+    static constexpr int NH = (SPLIT && NMT >= 2 && DV <= 64) ? 2 : 1;  // waves per slice
+    static constexpr int NW = NWC * NH;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NQT = NMT / NH;         // query tiles per wave
     static constexpr int CP = (C < KB) ? KB : C; // chunk contraction length (zero padded)
     static constexpr int NUC = CP / KB;          // units over chunk tokens
     static constexpr int NUK = DK / KB;          // units over dk
@@ -108,9 +112,21 @@ struct Fwd {
     static constexpr int VVEC = C * (DV / VEC);
     static constexpr int NV = (VVEC + NT - 1) / NT;
     static constexpr int NLAM = (C * kMaxLevels + NT - 1) / NT;
+    // LDS bytes of everything but the resident inter-group states, and how
+    // many of those states (one per level above the group) fit beside it.
+    static constexpr int BASE_LDS = (int)sizeof(T) * (C * LDK + CP * LDK + (TR ? CP * LDV : 8) +
+                                                       (TR ? 8 : DK * LDC) + (TR ? 8 : DV * LDC)) +
+                                    4 * (kMaxLevels * LDL + C) + 1024;
+    static constexpr int STATE_BYTES = DK * DV * (int)sizeof(T);
+    static constexpr int NRES_FIT = (160 * 1024 - BASE_LDS) / STATE_BYTES;
+    static constexpr int NRES = NRES_FIT < 0 ? 0 : (NRES_FIT > 8 ? 8 : NRES_FIT);
+    // query tile x (0 .. NQT-1) of half h: pairs {0, NMT-1}, {1, NMT-2}
+    // balance the causal work of the two halves.
+    __device__ static constexpr int qtile(int h, int x) { return NH == 1 ? x : (x == 0 ? h : NMT - 1 - h); }
     static_assert(DK % KB == 0, "dk must be a multiple of the MFMA unit");
     static_assert(DV % 16 == 0 && DV <= 128, "dv must be 16..128 in steps of 16");
     static_assert(C <= 64, "the decay scan handles at most one wave of tokens");
+    static_assert(NMT % NH == 0 && (NH == 1 || NQT <= 2), "query tiles split in pairs");
 };
 
 // Row-major q/k/v tiles (k and v padded with zero rows up to CP), lambda^T,
@@ -125,6 +141,7 @@ struct alignas(16) WalkSmem {
     T Vts[F::TR ? 8 : F::DV * F::LDC];
     float lamT[kMaxLevels * F::LDL];
     float Aloc[F::C];
+    T Dres[F::NRES > 0 ? F::NRES * F::DK * F::DV : 8];  // inter-group states, fragment order
     float off[32];          // log-decay from each inter-group block's end to the group start
     size_t blk[32];         // element offset of each inter-group block state
     int plist[32];          // set bits of the group index, low to high
@@ -542,25 +559,79 @@ __device__ __forceinline__ void walk_store(const WalkRegs<F> &r, WalkSmem<F> &sm
 }
 
 // O^T += (D^T Q^T) * f, f_i = lambda[i, lev] * exp(Aloc[i] + base), for one
-// level whose state D is given as fragments (A operand of D^T Q^T).
+// level whose state D is given as fragments (A operand of D^T Q^T), over this
+// wave's query tiles.
 template <class F>
 __device__ __forceinline__ void level_update(floatx4 *O, const typename F::Frag (*qf)[F::NUK],
                                              const typename F::Frag *d, const float *lamT, const float *ai,
-                                             int lev, float base, int li)
+                                             int lev, float base, int h, int li)
 {
 #pragma unroll
-    for (int it = 0; it < F::NMT; ++it) {
+    for (int x = 0; x < F::NQT; ++x) {
         floatx4 tmp = zero4();
 #pragma unroll
         for (int u = 0; u < F::NUK; ++u)
-            mma_unit(tmp, d[u], qf[it][u]);
-        const float f = lamT[lev * F::LDL + 16 * it + li] * __expf(ai[it] + base);
-        O[it] += f * tmp;
+            mma_unit(tmp, d[u], qf[x][u]);
+        const float f = lamT[lev * F::LDL + 16 * F::qtile(h, x) + li] * __expf(ai[x] + base);
+        O[x] += f * tmp;
+    }
+}
+
+// Intra-chunk part for the query tiles of half H (compile-time, so every
+// tile index below is static): P^T = mask ⊙ (K Q^T) on the causal tiles and
+// O^T = V^T P^T.
+template <class F, int H>
+__device__ __forceinline__ void intra_chunk(floatx4 *O, const typename F::Frag (*qf)[F::NUK], const float *ai,
+                                            const typename F::Frag *vf, const WalkSmem<F> &sm, int li, int qd)
+{
+    using DTag = typename F::DTag;
+    constexpr int NJT = F::CP / 16;
+#pragma unroll
+    for (int x = 0; x < F::NQT; ++x) {
+        const int it = F::qtile(H, x);
+        floatx4 pt[NJT];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+            pt[jt] = zero4();
+#pragma unroll
+        for (int jt = 0; jt < F::NMT; ++jt) {
+            if (jt > it)
+                break;
+            __builtin_amdgcn_sched_barrier(0);  // keep one key tile's fragments live at a time
+            floatx4 s = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd), qf[x][u]);
+            const int i = 16 * it + li;
+            if (jt < it) {
+                // every key of the tile sits in one bucket of query i
+                const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pt[jt][r] = s[r] * __expf(ai[x] - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * jt + 4 * qd + r;
+                    float m = 0.f;
+                    if (j <= i) {
+                        const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
+                        m = __expf(ai[x] - sm.Aloc[j]) * sm.lamT[lev * F::LDL + i];
+                    }
+                    pt[jt][r] = s[r] * m;
+                }
+            }
+        }
+        O[x] = zero4();
+#pragma unroll
+        for (int u = 0; u < F::NUC; ++u)
+            if (u * F::KB <= 16 * it + 15)
+                mma_unit(O[x], vf[u], acc_frag(pt, u, DTag{}));
     }
 }
 
 template <class F>
-__global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
+__global__ __launch_bounds__(F::NT) void ll_chunk_walk(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
     int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
@@ -570,8 +641,11 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
     using Frag = typename F::Frag;
     using DTag = typename F::DTag;
     constexpr int NJT = F::CP / 16;  // key tiles covered by the PV units (zero padded past C)
+    constexpr int DKV = F::DK * F::DV;
     __shared__ WalkSmem<F> sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qd = lane >> 4, li = lane & 15;
+    const int w = wave % F::NWC;   // this wave's 16 output columns
+    const int h = wave / F::NWC;   // which half of the query tiles
     const int bh = blockIdx.x / nG, sg = blockIdx.x % nG;
     const int G = 1 << g;
     const int nchunk = min(G, N - sg * G);
@@ -596,7 +670,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
         for (int p = 0; p < Plev; ++p) {
             if ((sg >> p) & 1) {
                 sm.plist[n] = p;
-                sm.blk[n] = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * F::DK * F::DV;
+                sm.blk[n] = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * DKV;
                 ++n;
             }
             off += ((nL >> p) + 1) >> 1;
@@ -605,7 +679,7 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
     }
     // Log-decay from the end of each inter-group block to the start of this
     // group: the sum of the group totals strictly between them.
-    if (w == 0) {
+    if (wave == 0) {
         for (int p = 0; p < Plev; ++p) {
             if (!((sg >> p) & 1))
                 continue;
@@ -620,23 +694,21 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
                 sm.off[p] = s;
         }
     }
-
     __syncthreads();
     const int npop = sm.npop;
-    // The first NRES inter-group levels stay in registers for the whole
-    // group; further levels stream from L2.
-    Frag bres[F::NRES][F::NUK];
-#pragma unroll
-    for (int ii = 0; ii < F::NRES; ++ii)
-#pragma unroll
-        for (int u = 0; u < F::NUK; ++u)
-            bres[ii][u] = (ii < npop)
-                ? *reinterpret_cast<const Frag *>(Dg + sm.blk[ii] + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL)
-                : Frag{};
+    // The inter-group level states are the same for every chunk of the group:
+    // the first NRES are copied into LDS once, further ones stream from L2.
+    const int nres = min(npop, F::NRES);
+    for (int idx = tid; idx < nres * (DKV / F::VEC); idx += F::NT) {
+        const int ii = idx / (DKV / F::VEC), e = idx % (DKV / F::VEC);
+        *reinterpret_cast<uint4 *>(sm.Dres + (size_t)ii * DKV + e * F::VEC) =
+            *reinterpret_cast<const uint4 *>(Dg + sm.blk[ii] + (size_t)e * F::VEC);
+    }
 
     // Fenwick stack of the levels inside the group, in fragment form.  Slot
     // m holds the bucket of bit m of the local chunk index, decayed to its own
     // end; gap[m] is the log-decay from that end to the current chunk start.
+    // Both waves of a column slice keep identical copies.
     Frag stk[kMaxGroupLog2][F::NUK];
     float gap[kMaxGroupLog2];
 #pragma unroll
@@ -659,111 +731,57 @@ __global__ __launch_bounds__(F::NT, F::WPE) void ll_chunk_walk(
         __syncthreads();
         const float gch = sm.gch;
 
-        // Fragments reused for the whole chunk: Q^T (B operand, every query
-        // tile), V (this wave's columns), and the decay of this lane's
-        // query rows.
-        Frag qf[F::NMT][F::NUK];
-        float ai[F::NMT];
+        // Q^T fragments of this wave's query tiles and the decay of this
+        // lane's query rows, reused by every product of the chunk.
+        Frag qf[F::NQT][F::NUK];
+        float ai[F::NQT];
 #pragma unroll
-        for (int it = 0; it < F::NMT; ++it) {
-            ai[it] = sm.Aloc[16 * it + li];
+        for (int x = 0; x < F::NQT; ++x) {
+            const int it = F::qtile(h, x);
+            ai[x] = sm.Aloc[16 * it + li];
 #pragma unroll
             for (int u = 0; u < F::NUK; ++u)
-                qf[it][u] = lds_frag(sm.Qs, F::LDK, 16 * it + li, u * F::KB, qd);
+                qf[x][u] = lds_frag(sm.Qs, F::LDK, 16 * it + li, u * F::KB, qd);
         }
         Frag vf[F::NUC];
 #pragma unroll
         for (int u = 0; u < F::NUC; ++u)
             vf[u] = v_frag<F>(sm, w, u, li, qd);
 
-        // Intra-chunk: P^T tiles (key tile jt, query tile it), jt <= it.
-        floatx4 pt[F::NMT][NJT];
-#pragma unroll
-        for (int it = 0; it < F::NMT; ++it)
-#pragma unroll
-            for (int jt = 0; jt < NJT; ++jt)
-                pt[it][jt] = zero4();
-#pragma unroll
-        for (int jt = 0; jt < F::NMT; ++jt) {
-            Frag kf[F::NUK];
-#pragma unroll
-            for (int u = 0; u < F::NUK; ++u)
-                kf[u] = lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd);
-            float aj[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                aj[r] = sm.Aloc[16 * jt + 4 * qd + r];
-#pragma unroll
-            for (int it = jt; it < F::NMT; ++it) {
-                floatx4 s = zero4();
-#pragma unroll
-                for (int u = 0; u < F::NUK; ++u)
-                    mma_unit(s, kf[u], qf[it][u]);
-                const int i = 16 * it + li;
-                if (jt < it) {
-                    // every key of the tile sits in one bucket of query i
-                    const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        pt[it][jt][r] = s[r] * __expf(ai[it] - aj[r]) * lm;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * jt + 4 * qd + r;
-                        float m = 0.f;
-                        if (j <= i) {
-                            const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                            m = __expf(ai[it] - aj[r]) * sm.lamT[lev * F::LDL + i];
-                        }
-                        pt[it][jt][r] = s[r] * m;
-                    }
-                }
-            }
-        }
-
-        // O^T = V^T P^T for this wave's 16 output columns.
-        floatx4 O[F::NMT];
-#pragma unroll
-        for (int it = 0; it < F::NMT; ++it) {
-            O[it] = zero4();
-#pragma unroll
-            for (int u = 0; u < F::NUC; ++u)
-                if (u * F::KB <= 16 * it + 15)
-                    mma_unit(O[it], vf[u], acc_frag(pt[it], u, DTag{}));
-        }
+        // Intra-chunk: P^T tiles (key tile jt, query tile it), jt <= it, and
+        // O^T = V^T P^T for this wave's columns.
+        floatx4 O[F::NQT];
+        if (h == 0)
+            intra_chunk<F, 0>(O, qf, ai, vf, sm, li, qd);
+        else
+            intra_chunk<F, 1>(O, qf, ai, vf, sm, li, qd);
 
         // Levels inside the group.
 #pragma unroll
         for (int m = 0; m < kMaxGroupLog2; ++m)
             if (m < g && ((ci >> m) & 1))
-                level_update<F>(O, qf, stk[m], sm.lamT, ai, log2C + m + 1, gap[m], li);
+                level_update<F>(O, qf, stk[m], sm.lamT, ai, log2C + m + 1, gap[m], h, li);
 
         // Levels above the group.
-#pragma unroll
-        for (int ii = 0; ii < F::NRES; ++ii)
-            if (ii < npop) {
-                const int p = sm.plist[ii];
-                level_update<F>(O, qf, bres[ii], sm.lamT, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
-            }
-        for (int ii = F::NRES; ii < npop; ++ii) {
-            Frag bcur[F::NUK];
-            const T *blk = Dg + sm.blk[ii];
+        for (int ii = 0; ii < npop; ++ii) {
+            Frag d[F::NUK];
+            const T *src = (ii < F::NRES) ? sm.Dres + (size_t)ii * DKV : Dg + sm.blk[ii];
 #pragma unroll
             for (int u = 0; u < F::NUK; ++u)
-                bcur[u] = *reinterpret_cast<const Frag *>(blk + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL);
+                d[u] = *reinterpret_cast<const Frag *>(src + ((size_t)(w * F::NUK + u) * 64 + lane) * F::EPL);
             const int p = sm.plist[ii];
-            level_update<F>(O, qf, bcur, sm.lamT, ai, log2C + g + 1 + p, agrun + sm.off[p], li);
+            level_update<F>(O, qf, d, sm.lamT, ai, log2C + g + 1 + p, agrun + sm.off[p], h, li);
         }
 
         // Output: lane holds O[i][16w + 4qd .. 16w + 4qd + 3] for i = 16it + li.
 #pragma unroll
-        for (int it = 0; it < F::NMT; ++it) {
-            const int i = 16 * it + li;
+        for (int x = 0; x < F::NQT; ++x) {
+            const int i = 16 * F::qtile(h, x) + li;
             if (i < valid) {
                 T vals[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    vals[r] = from_f32<T>(O[it][r]);
+                    vals[r] = from_f32<T>(O[x][r]);
                 T *dst = out + (row0 + i) * F::DV + 16 * w + 4 * qd;
                 if constexpr (sizeof(T) == 2)
                     *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(vals);
@@ -908,8 +926,9 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             ping ^= 1;
         }
     }
+    using FW = Fwd<typename F::DTag, F::DK, F::DV, F::C, true>;
     prof_before("ll_chunk_walk", s);
-    hipLaunchKernelGGL(ll_chunk_walk<F>, dim3(BH * P.nG), dim3(F::NT), 0, s, (const T *)A.q, (const T *)A.k,
+    hipLaunchKernelGGL(ll_chunk_walk<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, (const T *)A.q, (const T *)A.k,
                        (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL,
                        P.nLeft, (const float *)Gam, (const T *)Dg);
     prof_after(s);
@@ -923,7 +942,7 @@ static FwdLauncher pick_c()
 {
     if constexpr (DK % DT::KB != 0) {
         return nullptr;
-    } else if constexpr (sizeof(WalkSmem<Fwd<DT, DK, DV, C>>) > 160 * 1024) {
+    } else if constexpr (sizeof(WalkSmem<Fwd<DT, DK, DV, C, true>>) > 160 * 1024) {
         return nullptr;
     } else {
         return &launch_fwd_t<Fwd<DT, DK, DV, C>>;
