@@ -31,6 +31,41 @@ struct Dec {
     static_assert((NT * 4) % DV == 0, "a thread must keep one column group");
 };
 
+// Stack slots are touched once per step: stream them past the caches.
+__device__ __forceinline__ float4 nt_load(const float4 *p)
+{
+    const floatx4 x = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ __forceinline__ void nt_store(float4 *p, const float4 &v)
+{
+    const floatx4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<floatx4 *>(p));
+}
+
+// Accumulate one slot's share x (this thread's float4 vectors) either into
+// the merged bucket M (levels <= kc) or into the read-out partial sums.
+template <class D>
+__device__ __forceinline__ void decode_slot(const float4 *x, float4 *M, float *part, bool merge, float scale,
+                                            const float *qs, int tid)
+{
+#pragma unroll
+    for (int r = 0; r < D::NPT; ++r) {
+        const int idx = tid + D::NT * r;
+        if (idx < D::NV4) {
+            if (merge) {
+                M[r].x += scale * x[r].x; M[r].y += scale * x[r].y;
+                M[r].z += scale * x[r].z; M[r].w += scale * x[r].w;
+            } else {
+                const float qc = scale * qs[idx * 4 / D::DV];
+                part[0] += qc * x[r].x; part[1] += qc * x[r].y;
+                part[2] += qc * x[r].z; part[3] += qc * x[r].w;
+            }
+        }
+    }
+}
+
 template <class D>
 __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict__ q,
                                                  const typename D::T *__restrict__ k,
@@ -45,6 +80,8 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
     __shared__ float qs[DK], ks[DK], vs[DV];
     __shared__ float lam_s[kMaxLevels], g_s[kMaxLevels];
     __shared__ float red[D::NT][4];
+    __shared__ int slots[kMaxLevels];
+    __shared__ int nslots;
     __shared__ float qk_s;
 
     const int tid = threadIdx.x;
@@ -70,6 +107,19 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
         lam_s[l] = lam[(size_t)sh * Lcap + l];
         g_s[l] = logscale[(size_t)sh * Lcap + l];
     }
+    if (tid == 0) {
+        // occupied slots of the previous position: 0, and l >= 1 for each set
+        // bit l-1 of t-1 (none when the stack is empty, t == 0)
+        int n = 0;
+        if (t > 0) {
+            const int64_t prev = t - 1;
+            slots[n++] = 0;
+            for (int l = 1; l < Lcap; ++l)
+                if ((prev >> (l - 1)) & 1)
+                    slots[n++] = l;
+        }
+        nslots = n;
+    }
     __syncthreads();
     if (tid < 64) {
         float x = 0.f;
@@ -85,79 +135,59 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
     const float at = a[sh];
     float *st = state + (size_t)sh * Lcap * DK * DV;
     const int c0 = (tid * 4) % DV;  // this thread's four output columns
+    const int kc = t > 0 ? __builtin_ctzll((unsigned long long)t) : -1;  // levels 0..kc merge into kc+1
+    const int n = nslots;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float4 M[D::NPT];
+#pragma unroll
+    for (int r = 0; r < D::NPT; ++r)
+        M[r] = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    float4 fresh[D::NPT];  // k v^T for the new token, this thread's share
+    // Stream the occupied slots two at a time.
+    for (int i = 0; i < n; i += 2) {
+        const int l0 = slots[i];
+        const int l1 = (i + 1 < n) ? slots[i + 1] : -1;
+        float4 x0[D::NPT], x1[D::NPT];
+        const float4 *s0 = reinterpret_cast<const float4 *>(st + (size_t)l0 * DK * DV);
+#pragma unroll
+        for (int r = 0; r < D::NPT; ++r) {
+            const int idx = tid + D::NT * r;
+            if (idx < D::NV4)
+                x0[r] = nt_load(s0 + idx);
+        }
+        if (l1 >= 0) {
+            const float4 *s1 = reinterpret_cast<const float4 *>(st + (size_t)l1 * DK * DV);
+#pragma unroll
+            for (int r = 0; r < D::NPT; ++r) {
+                const int idx = tid + D::NT * r;
+                if (idx < D::NV4)
+                    x1[r] = nt_load(s1 + idx);
+            }
+        }
+        decode_slot<D>(x0, M, part, l0 <= kc, l0 <= kc ? __expf(g_s[l0]) : lam_s[l0] * __expf(g_s[l0] + at), qs,
+                       tid);
+        if (l1 >= 0)
+            decode_slot<D>(x1, M, part, l1 <= kc,
+                           l1 <= kc ? __expf(g_s[l1]) : lam_s[l1] * __expf(g_s[l1] + at), qs, tid);
+    }
+
+    // Merged bucket (true state, stored with logscale 0) and the new token's
+    // own state in slot 0.
+    const float dec = __expf(at);
+    float4 *dst0 = reinterpret_cast<float4 *>(st);
+    float4 *dstM = reinterpret_cast<float4 *>(st + (size_t)(kc + 1) * DK * DV);
+    const float lm = t > 0 ? lam_s[kc + 1] : 0.f;
 #pragma unroll
     for (int r = 0; r < D::NPT; ++r) {
         const int idx = tid + D::NT * r;
         if (idx < D::NV4) {
             const int row = idx * 4 / DV;
-            fresh[r] = make_float4(ks[row] * vs[c0], ks[row] * vs[c0 + 1], ks[row] * vs[c0 + 2], ks[row] * vs[c0 + 3]);
-        }
-    }
-
-    if (t == 0) {
-#pragma unroll
-        for (int r = 0; r < D::NPT; ++r) {
-            const int idx = tid + D::NT * r;
-            if (idx < D::NV4)
-                reinterpret_cast<float4 *>(st)[idx] = fresh[r];
-        }
-    } else {
-        const int64_t prev = t - 1;
-        const int kc = __builtin_ctzll((unsigned long long)t);  // levels 0..kc merge into kc+1
-        float4 M[D::NPT];
-#pragma unroll
-        for (int r = 0; r < D::NPT; ++r)
-            M[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int l = 0; l < Lcap; ++l) {
-            const bool occ = (l == 0) || ((prev >> (l - 1)) & 1);
-            if (!occ)
-                continue;
-            const float4 *src = reinterpret_cast<const float4 *>(st + (size_t)l * DK * DV);
-            float4 x[D::NPT];
-#pragma unroll
-            for (int r = 0; r < D::NPT; ++r) {
-                const int idx = tid + D::NT * r;
-                if (idx < D::NV4)
-                    x[r] = src[idx];
-            }
-            if (l <= kc) {
-                const float sc = __expf(g_s[l]);
-#pragma unroll
-                for (int r = 0; r < D::NPT; ++r) {
-                    const int idx = tid + D::NT * r;
-                    if (idx < D::NV4) {
-                        M[r].x += sc * x[r].x; M[r].y += sc * x[r].y;
-                        M[r].z += sc * x[r].z; M[r].w += sc * x[r].w;
-                    }
-                }
-            } else {
-                const float coef = lam_s[l] * __expf(g_s[l] + at);
-#pragma unroll
-                for (int r = 0; r < D::NPT; ++r) {
-                    const int idx = tid + D::NT * r;
-                    if (idx < D::NV4) {
-                        const float qc = coef * qs[idx * 4 / DV];
-                        part[0] += qc * x[r].x; part[1] += qc * x[r].y;
-                        part[2] += qc * x[r].z; part[3] += qc * x[r].w;
-                    }
-                }
-            }
-        }
-        const float dec = __expf(at);
-        const float lm = lam_s[kc + 1];
-        float4 *dstM = reinterpret_cast<float4 *>(st + (size_t)(kc + 1) * DK * DV);
-        float4 *dst0 = reinterpret_cast<float4 *>(st);
-#pragma unroll
-        for (int r = 0; r < D::NPT; ++r) {
-            const int idx = tid + D::NT * r;
-            if (idx < D::NV4) {
-                float4 m = make_float4(dec * M[r].x, dec * M[r].y, dec * M[r].z, dec * M[r].w);
-                dstM[idx] = m;
-                dst0[idx] = fresh[r];
-                const float qc = lm * qs[idx * 4 / DV];
+            const float kr = ks[row];
+            nt_store(dst0 + idx, make_float4(kr * vs[c0], kr * vs[c0 + 1], kr * vs[c0 + 2], kr * vs[c0 + 3]));
+            if (t > 0) {
+                const float4 m = make_float4(dec * M[r].x, dec * M[r].y, dec * M[r].z, dec * M[r].w);
+                nt_store(dstM + idx, m);
+                const float qc = lm * qs[row];
                 part[0] += qc * m.x; part[1] += qc * m.y; part[2] += qc * m.z; part[3] += qc * m.w;
             }
         }
@@ -183,7 +213,6 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
         gl[0] = 0.f;
         if (t > 0) {
             const int64_t prev = t - 1;
-            const int kc = __builtin_ctzll((unsigned long long)t);
             for (int l = kc + 2; l < Lcap; ++l)
                 if ((prev >> (l - 1)) & 1)
                     gl[l] = g_s[l] + at;
