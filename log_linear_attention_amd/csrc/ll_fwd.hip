@@ -166,6 +166,17 @@ struct alignas(16) StateSmem {
 
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0, 0, 0, 0); }
 
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+
+// Streaming 16-byte global access for data touched once (q, k, v, lambda in
+// the chunk walk; the output rows).
+__device__ __forceinline__ uint4 ld_stream(const void *p)
+{
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+
 template <class F, class E>
 __device__ __forceinline__ void lds_zero(E *dst, int n, int tid)
 {
@@ -501,8 +512,8 @@ __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q
         const int j = idx / QPR, c = idx % QPR;
         r.q[i] = r.k[i] = zero16();
         if (idx < F::QVEC && j < valid) {
-            r.q[i] = *reinterpret_cast<const uint4 *>(q + (row0 + j) * F::DK + c * F::VEC);
-            r.k[i] = *reinterpret_cast<const uint4 *>(k + (row0 + j) * F::DK + c * F::VEC);
+            r.q[i] = ld_stream(q + (row0 + j) * F::DK + c * F::VEC);
+            r.k[i] = ld_stream(k + (row0 + j) * F::DK + c * F::VEC);
         }
     }
 #pragma unroll
@@ -510,13 +521,13 @@ __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q
         const int idx = tid + i * F::NT;
         r.v[i] = zero16();
         if (idx < F::VVEC && idx / VPR < valid)
-            r.v[i] = *reinterpret_cast<const uint4 *>(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
+            r.v[i] = ld_stream(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
     }
     // lambda rows of the chunk are one contiguous block of valid * L floats
 #pragma unroll
     for (int i = 0; i < F::NLAM; ++i) {
         const int idx = tid + i * F::NT;
-        r.lam[i] = (idx < valid * L) ? lam[row0 * L + idx] : 0.f;
+        r.lam[i] = (idx < valid * L) ? __builtin_nontemporal_load(lam + row0 * L + idx) : 0.f;
     }
     r.a = (tid < valid) ? a[row0 + tid] : 0.f;
     (void)invL;
@@ -631,7 +642,7 @@ __device__ __forceinline__ void intra_chunk(floatx4 *O, const typename F::Frag (
 }
 
 template <class F>
-__global__ __launch_bounds__(F::NT) void ll_chunk_walk(
+__global__ __launch_bounds__(F::NT) void ll_chunk_walk_rs(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
     int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
@@ -783,10 +794,12 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
                 for (int r = 0; r < 4; ++r)
                     vals[r] = from_f32<T>(O[x][r]);
                 T *dst = out + (row0 + i) * F::DV + 16 * w + 4 * qd;
-                if constexpr (sizeof(T) == 2)
-                    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(vals);
-                else
-                    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(vals);
+                if constexpr (sizeof(T) == 2) {
+                    typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x2 *>(vals), reinterpret_cast<u32x2 *>(dst));
+                } else {
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(vals), reinterpret_cast<u32x4 *>(dst));
+                }
             }
         }
 
@@ -825,6 +838,385 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
                         stk[m][u] = acc_frag(Hn, u, DTag{});
                     gap[m] = 0.f;
                 }
+        }
+        agrun += gch;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel C' (bf16): the chunk walk with shared score tiles and an LDS stack.
+//
+// Same algorithm as ll_chunk_walk_rs, mapped so that no work is repeated
+// across waves: every causal score tile of a chunk is formed once (by one of
+// the waves that own its query tile) and shared through LDS as P[i][j];
+// wave (it, cg) owns query tile it and CPW of the 16-column output tiles;
+// the Fenwick stack of the levels inside the group lives in LDS in fragment
+// order, and each wave builds its own fragments of a new stack slot.  Q^T
+// fragments are loaded straight from global memory into registers (one
+// chunk ahead), so LDS holds only K, V, P, lambda^T, the stack and the
+// inter-group states.
+// ---------------------------------------------------------------------------
+template <class DT, int DK_, int DV_, int C_>
+struct Walk4 {
+    using T = typename DT::T;
+    using Frag = typename DT::Frag;
+    using DTag = DT;
+    static constexpr int DK = DK_, DV = DV_, C = C_;
+    static constexpr bool TR = true;
+    static constexpr int KB = DT::KB, EPL = DT::EPL;
+    static constexpr int NMT = C / 16;                 // query (and key) tiles per chunk
+    static constexpr int NWC = DV / 16;                // 16-column output tiles
+    static constexpr int WMAX = 16;                    // waves per workgroup
+    static constexpr int CPW0 = NMT * NWC / WMAX;
+    static constexpr int CPW = CPW0 < 1 ? 1 : CPW0;    // output column tiles per wave
+    static constexpr int NCG = NWC / CPW;              // column groups (waves per query tile)
+    static constexpr int NW = NMT * NCG;
+    static constexpr int NT = 64 * NW;
+    static constexpr int CP = (C < KB) ? KB : C;
+    static constexpr int NUC = CP / KB;
+    static constexpr int NUK = DK / KB;
+    static constexpr int LDK = bf16_stride(DK, true);
+    static constexpr int LDV = bf16_stride(DV, false);
+    static constexpr int LDP = bf16_stride(CP, true);
+    static constexpr int LDL = C + 1;
+    static constexpr int VEC = 8;
+    static constexpr int SLOT = DK * DV;               // elements of one state
+    static constexpr int NFRAG = NUK * NWC;            // 16-byte fragments per lane per state
+    static constexpr int KVEC = C * (DK / VEC);
+    static constexpr int NK = (KVEC + NT - 1) / NT;
+    static constexpr int VVEC = C * (DV / VEC);
+    static constexpr int NV = (VVEC + NT - 1) / NT;
+    static constexpr int NLAM = (C * kMaxLevels + NT - 1) / NT;
+    static constexpr int BASE_LDS = 2 * (C * LDK + CP * LDK + CP * LDV + C * LDP + kMaxGroupLog2 * SLOT) +
+                                    4 * (kMaxLevels * LDL + C + CP) + 1024;
+    static constexpr int NRES_FIT = (160 * 1024 - BASE_LDS) / (2 * SLOT);
+    static constexpr int NRES = NRES_FIT < 0 ? 0 : (NRES_FIT > 8 ? 8 : NRES_FIT);
+    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NMT * NCG <= 16 && NWC % CPW == 0;
+};
+
+template <class F>
+struct alignas(16) Walk4Smem {
+    using T = typename F::T;
+    T Qs[F::C * F::LDK];
+    T Ks[F::CP * F::LDK];
+    T Vs[F::CP * F::LDV];
+    T Ps[F::C * F::LDP];
+    T stk[kMaxGroupLog2 * F::SLOT];
+    T Dres[F::NRES > 0 ? F::NRES * F::SLOT : 8];
+    float lamT[kMaxLevels * F::LDL];
+    float Aloc[F::C];
+    float wdec[F::CP];      // exp(chunk total - Aloc[j]): decay from token j to the chunk end
+    float off[32];
+    size_t blk[32];
+    int plist[32];
+    int npop;
+    float gch;
+};
+
+template <class F>
+struct Walk4Regs {
+    uint4 q[F::NK], k[F::NK], v[F::NV];
+    float lam[F::NLAM];
+    float a;
+};
+
+template <class F>
+__device__ __forceinline__ void walk4_load(Walk4Regs<F> &r, const typename F::T *q, const typename F::T *k,
+                                           const typename F::T *v, const float *a, const float *lam, size_t row0,
+                                           int valid, int L, int it, int tid, int li, int qd)
+{
+    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = tid + i * F::NT;
+        r.q[i] = r.k[i] = zero16();
+        if (idx < F::KVEC && idx / KPR < valid) {
+            r.q[i] = ld_stream(q + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
+            r.k[i] = ld_stream(k + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = tid + i * F::NT;
+        r.v[i] = zero16();
+        if (idx < F::VVEC && idx / VPR < valid)
+            r.v[i] = ld_stream(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = tid + i * F::NT;
+        r.lam[i] = (idx < valid * L) ? __builtin_nontemporal_load(lam + row0 * L + idx) : 0.f;
+    }
+    r.a = (tid < valid) ? a[row0 + tid] : 0.f;
+}
+
+template <class F>
+__device__ __forceinline__ void walk4_store(const Walk4Regs<F> &r, Walk4Smem<F> &sm, int valid, int L, float invL,
+                                            int tid)
+{
+    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < F::KVEC) {
+            *reinterpret_cast<uint4 *>(sm.Qs + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.q[i];
+            *reinterpret_cast<uint4 *>(sm.Ks + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.k[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < F::VVEC)
+            *reinterpret_cast<uint4 *>(sm.Vs + (idx / VPR) * F::LDV + (idx % VPR) * F::VEC) = r.v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = tid + i * F::NT;
+        if (idx < valid * L) {
+            const int j = (int)(((float)idx + 0.5f) * invL);
+            sm.lamT[(idx - j * L) * F::LDL + j] = r.lam[i];
+        }
+    }
+    if (tid < 64) {
+        float x = r.a;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            float y = __shfl_up(x, d, 64);
+            if (tid >= d)
+                x += y;
+        }
+        const float g = __shfl(x, F::C - 1, 64);
+        if (tid < F::C)
+            sm.Aloc[tid] = x;
+        if (tid < F::CP)
+            sm.wdec[tid] = (tid < F::C) ? __expf(g - x) : 0.f;
+        if (tid == 0)
+            sm.gch = g;
+    }
+}
+
+// Fragment (c, u) of a state stored in fragment order.
+template <class F>
+__device__ __forceinline__ typename F::Frag state_frag(const typename F::T *st, int c, int u, int lane)
+{
+    return *reinterpret_cast<const typename F::Frag *>(st + ((size_t)(c * F::NUK + u) * 64 + lane) * F::EPL);
+}
+
+// O^T[cc] += f * (D^T Q^T) for the wave's column tiles; f is this lane's
+// query-row factor lambda[i, lev] * exp(Aloc[i] + base).
+template <class F>
+__device__ __forceinline__ void walk4_level(floatx4 *O, const typename F::Frag *qf, const typename F::T *st,
+                                            int cg, float f, int lane)
+{
+#pragma unroll
+    for (int cc = 0; cc < F::CPW; ++cc) {
+        const int c = cg * F::CPW + cc;
+        floatx4 tmp = zero4();
+#pragma unroll
+        for (int u = 0; u < F::NUK; ++u)
+            mma_unit(tmp, state_frag<F>(st, c, u, lane), qf[u]);
+        O[cc] += f * tmp;
+    }
+}
+
+template <class F>
+__global__ __launch_bounds__(F::NT) void ll_chunk_walk(
+    const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
+    const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
+    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
+    const typename F::T *__restrict__ Dg)
+{
+    using T = typename F::T;
+    using Frag = typename F::Frag;
+    using DTag = typename F::DTag;
+    __shared__ Walk4Smem<F> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qd = lane >> 4, li = lane & 15;
+    const int it = wave % F::NMT;   // query tile of this wave
+    const int cg = wave / F::NMT;   // column group of this wave
+    const int bh = blockIdx.x / nG, sg = blockIdx.x % nG;
+    const int G = 1 << g;
+    const int nchunk = min(G, N - sg * G);
+    const float invL = 1.f / (float)L;
+
+    Walk4Regs<F> pf;
+    walk4_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
+                  min(F::C, Tlen - sg * G * F::C), L, it, tid, li, qd);
+
+    // Padding rows of K and V, P (its upper tiles and padding columns are
+    // never written) and lambda^T (levels >= L) start at zero.
+    lds_zero<F>(sm.Ks, F::CP * F::LDK, tid);
+    lds_zero<F>(sm.Vs, F::CP * F::LDV, tid);
+    lds_zero<F>(sm.Ps, F::C * F::LDP, tid);
+    lds_zero<F>(sm.lamT, kMaxLevels * F::LDL, tid);
+    if (tid == 0) {
+        int n = 0;
+        size_t off = 0;
+        for (int p = 0; p < Plev; ++p) {
+            if ((sg >> p) & 1) {
+                sm.plist[n] = p;
+                sm.blk[n] = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * F::SLOT;
+                ++n;
+            }
+            off += ((nL >> p) + 1) >> 1;
+        }
+        sm.npop = n;
+    }
+    if (wave == 0) {
+        for (int p = 0; p < Plev; ++p) {
+            if (!((sg >> p) & 1))
+                continue;
+            const int lo = ((sg >> (p + 1)) << (p + 1)) + (1 << p);
+            float s = 0.f;
+            for (int gam = lo + lane; gam < sg; gam += 64)
+                s += Gam[(size_t)bh * nG + gam];
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1)
+                s += __shfl_xor(s, d, 64);
+            if (lane == 0)
+                sm.off[p] = s;
+        }
+    }
+    __syncthreads();
+    const int npop = sm.npop;
+    const int nres = min(npop, F::NRES);
+    for (int idx = tid; idx < nres * (F::SLOT / F::VEC); idx += F::NT) {
+        const int ii = idx / (F::SLOT / F::VEC), e = idx % (F::SLOT / F::VEC);
+        *reinterpret_cast<uint4 *>(sm.Dres + (size_t)ii * F::SLOT + e * F::VEC) =
+            *reinterpret_cast<const uint4 *>(Dg + sm.blk[ii] + (size_t)e * F::VEC);
+    }
+
+    float gap[kMaxGroupLog2];
+#pragma unroll
+    for (int m = 0; m < kMaxGroupLog2; ++m)
+        gap[m] = 0.f;
+    float agrun = 0.f;
+
+    for (int ci = 0; ci < nchunk; ++ci) {
+        const int t0 = (sg * G + ci) * F::C;
+        const int valid = min(F::C, Tlen - t0);
+        const size_t row0 = (size_t)bh * Tlen + t0;
+        __syncthreads();
+        walk4_store<F>(pf, sm, valid, L, invL, tid);
+        if (ci + 1 < nchunk)
+            walk4_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, it, tid, li, qd);
+        __syncthreads();
+        const float gch = sm.gch;
+        const int i = 16 * it + li;      // this lane's query row
+        const float ai = sm.Aloc[i];
+        Frag qf[F::NUK];                 // Q^T fragments of query tile it
+#pragma unroll
+        for (int u = 0; u < F::NUK; ++u)
+            qf[u] = lds_frag(sm.Qs, F::LDK, i, u * F::KB, qd);
+
+        // Causal score tiles of query tile it, split over its column-group
+        // waves; masked by decay and level weight, stored as P[i][j].
+        for (int jt = cg; jt <= it; jt += F::NCG) {
+            floatx4 s = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd), qf[u]);
+            float p[4];
+            if (jt < it) {
+                const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[r] = s[r] * __expf(ai - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * jt + 4 * qd + r;
+                    float m = 0.f;
+                    if (j <= i) {
+                        const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
+                        m = __expf(ai - sm.Aloc[j]) * sm.lamT[lev * F::LDL + i];
+                    }
+                    p[r] = s[r] * m;
+                }
+            }
+            bf16x4 pb;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pb[r] = (__bf16)p[r];
+            *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 16 * jt + 4 * qd) = pb;
+        }
+        __syncthreads();
+
+        // O^T = V^T P^T for this wave's column tiles.
+        floatx4 O[F::CPW];
+#pragma unroll
+        for (int cc = 0; cc < F::CPW; ++cc) {
+            const int c = cg * F::CPW + cc;
+            O[cc] = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUC; ++u)
+                if (u * F::KB <= 16 * it + 15)
+                    mma_unit(O[cc], tr_frag(sm.Vs, F::LDV, u * F::KB, 16 * c, li, qd),
+                             lds_frag(sm.Ps, F::LDP, i, u * F::KB, qd));
+        }
+
+        // Levels inside the group (stack slots in LDS).
+#pragma unroll
+        for (int m = 0; m < kMaxGroupLog2; ++m)
+            if (m < g && ((ci >> m) & 1)) {
+                const float f = sm.lamT[(log2C + m + 1) * F::LDL + i] * __expf(ai + gap[m]);
+                walk4_level<F>(O, qf, sm.stk + m * F::SLOT, cg, f, lane);
+            }
+        // Levels above the group.
+        for (int ii = 0; ii < npop; ++ii) {
+            const int p = sm.plist[ii];
+            const float f = sm.lamT[(log2C + g + 1 + p) * F::LDL + i] * __expf(ai + agrun + sm.off[p]);
+            const T *st = (ii < F::NRES) ? sm.Dres + (size_t)ii * F::SLOT : Dg + sm.blk[ii];
+            walk4_level<F>(O, qf, st, cg, f, lane);
+        }
+
+        // Output: lane holds O[i][16c + 4qd .. 16c + 4qd + 3].
+        if (i < valid) {
+#pragma unroll
+            for (int cc = 0; cc < F::CPW; ++cc) {
+                const int c = cg * F::CPW + cc;
+                typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+                bf16x4 ob;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ob[r] = (__bf16)O[cc][r];
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x2 *>(&ob),
+                                            reinterpret_cast<u32x2 *>(out + (row0 + i) * F::DV + 16 * c + 4 * qd));
+            }
+        }
+
+        // Fold this chunk's state into the stack: slot kc (not read during
+        // this chunk) becomes the chunk state plus the decayed slots below it
+        // (read, never written, during this chunk).  Each wave builds whole
+        // fragments (c, u) of the new slot.
+        if (ci + 1 < nchunk) {
+            const int kc = __builtin_ctz((unsigned)(ci + 1));
+#pragma unroll
+            for (int m = 0; m < kMaxGroupLog2; ++m)
+                gap[m] += gch;
+            for (int fr = wave; fr < F::NFRAG; fr += F::NW) {
+                const int u = fr / F::NWC, c = fr % F::NWC;
+                floatx4 Hn[2] = {zero4(), zero4()};
+#pragma unroll
+                for (int uj = 0; uj < F::NUC; ++uj) {
+                    Frag vsf = tr_frag(sm.Vs, F::LDV, uj * F::KB, 16 * c, li, qd);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        vsf[e] = (__bf16)((float)vsf[e] * sm.wdec[uj * F::KB + unit_row(e, qd)]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        mma_unit(Hn[t], tr_frag(sm.Ks, F::LDK, uj * F::KB, 16 * (2 * u + t), li, qd), vsf);
+                }
+#pragma unroll
+                for (int m = 0; m < kMaxGroupLog2; ++m)
+                    if (m < kc)
+                        frag_axpy(Hn, state_frag<F>(sm.stk + m * F::SLOT, c, u, lane), 0, __expf(gap[m]), DTag{});
+                *reinterpret_cast<Frag *>(sm.stk + kc * F::SLOT + ((size_t)(c * F::NUK + u) * 64 + lane) * F::EPL) =
+                    acc_frag(Hn, 0, DTag{});
+            }
+#pragma unroll
+            for (int m = 0; m < kMaxGroupLog2; ++m)
+                if (m == kc)
+                    gap[m] = 0.f;
         }
         agrun += gch;
     }
@@ -926,11 +1318,18 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             ping ^= 1;
         }
     }
-    using FW = Fwd<typename F::DTag, F::DK, F::DV, F::C, true>;
+    using W4 = Walk4<typename F::DTag, F::DK, F::DV, F::C>;
     prof_before("ll_chunk_walk", s);
-    hipLaunchKernelGGL(ll_chunk_walk<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, (const T *)A.q, (const T *)A.k,
-                       (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL,
-                       P.nLeft, (const float *)Gam, (const T *)Dg);
+    if constexpr (F::TR && W4::FITS) {
+        hipLaunchKernelGGL(ll_chunk_walk<W4>, dim3(BH * P.nG), dim3(W4::NT), 0, s, (const T *)A.q, (const T *)A.k,
+                           (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL,
+                           P.nLeft, (const float *)Gam, (const T *)Dg);
+    } else {
+        using FW = Fwd<typename F::DTag, F::DK, F::DV, F::C, true>;
+        hipLaunchKernelGGL(ll_chunk_walk_rs<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, (const T *)A.q,
+                           (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG,
+                           P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
+    }
     prof_after(s);
     return hipGetLastError();
 }
