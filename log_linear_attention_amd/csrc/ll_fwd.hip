@@ -866,11 +866,11 @@ struct Walk4 {
     static constexpr int KB = DT::KB, EPL = DT::EPL;
     static constexpr int NMT = C / 16;                 // query (and key) tiles per chunk
     static constexpr int NWC = DV / 16;                // 16-column output tiles
-    static constexpr int WMAX = 16;                    // waves per workgroup
-    static constexpr int CPW0 = NMT * NWC / WMAX;
-    static constexpr int CPW = CPW0 < 1 ? 1 : CPW0;    // output column tiles per wave
-    static constexpr int NCG = NWC / CPW;              // column groups (waves per query tile)
-    static constexpr int NW = NMT * NCG;
+    static constexpr int QPW = NMT >= 2 ? 2 : 1;       // query tiles per wave (pairs {g, NMT-1-g})
+    static constexpr int NQG = NMT / QPW;              // query groups
+    static constexpr int CPW = NQG * NWC > 16 ? 2 : 1; // output column tiles per wave
+    static constexpr int NCG = NWC / CPW;              // column groups
+    static constexpr int NW = NQG * NCG;
     static constexpr int NT = 64 * NW;
     static constexpr int CP = (C < KB) ? KB : C;
     static constexpr int NUC = CP / KB;
@@ -891,7 +891,8 @@ struct Walk4 {
                                     4 * (kMaxLevels * LDL + C + CP) + 1024;
     static constexpr int NRES_FIT = (160 * 1024 - BASE_LDS) / (2 * SLOT);
     static constexpr int NRES = NRES_FIT < 0 ? 0 : (NRES_FIT > 8 ? 8 : NRES_FIT);
-    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NMT * NCG <= 16 && NWC % CPW == 0;
+    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NW <= 16 && NWC % CPW == 0;
+    __device__ static constexpr int qtile(int qg, int x) { return x == 0 ? qg : NMT - 1 - qg; }
 };
 
 template <class F>
@@ -923,7 +924,7 @@ struct Walk4Regs {
 template <class F>
 __device__ __forceinline__ void walk4_load(Walk4Regs<F> &r, const typename F::T *q, const typename F::T *k,
                                            const typename F::T *v, const float *a, const float *lam, size_t row0,
-                                           int valid, int L, int it, int tid, int li, int qd)
+                                           int valid, int L, int tid)
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -1002,20 +1003,29 @@ __device__ __forceinline__ typename F::Frag state_frag(const typename F::T *st, 
     return *reinterpret_cast<const typename F::Frag *>(st + ((size_t)(c * F::NUK + u) * 64 + lane) * F::EPL);
 }
 
-// O^T[cc] += f * (D^T Q^T) for the wave's column tiles; f is this lane's
-// query-row factor lambda[i, lev] * exp(Aloc[i] + base).
+// O^T[x][cc] += f[x] * (D^T Q^T) for the wave's query tiles x and column
+// tiles cc; f[x] is this lane's query-row factor lambda[i, lev] *
+// exp(Aloc[i] + base).  Each state fragment is loaded once and used for
+// every query tile of the wave.
 template <class F>
-__device__ __forceinline__ void walk4_level(floatx4 *O, const typename F::Frag *qf, const typename F::T *st,
-                                            int cg, float f, int lane)
+__device__ __forceinline__ void walk4_level(floatx4 (*O)[F::CPW], const typename F::Frag (*qf)[F::NUK],
+                                            const typename F::T *st, int cg, const float *f, int lane)
 {
 #pragma unroll
     for (int cc = 0; cc < F::CPW; ++cc) {
         const int c = cg * F::CPW + cc;
-        floatx4 tmp = zero4();
+        typename F::Frag d[F::NUK];
 #pragma unroll
         for (int u = 0; u < F::NUK; ++u)
-            mma_unit(tmp, state_frag<F>(st, c, u, lane), qf[u]);
-        O[cc] += f * tmp;
+            d[u] = state_frag<F>(st, c, u, lane);
+#pragma unroll
+        for (int x = 0; x < F::QPW; ++x) {
+            floatx4 tmp = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                mma_unit(tmp, d[u], qf[x][u]);
+            O[x][cc] += f[x] * tmp;
+        }
     }
 }
 
@@ -1031,8 +1041,8 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
     using DTag = typename F::DTag;
     __shared__ Walk4Smem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qd = lane >> 4, li = lane & 15;
-    const int it = wave % F::NMT;   // query tile of this wave
-    const int cg = wave / F::NMT;   // column group of this wave
+    const int qg = wave % F::NQG;   // query group of this wave (query tiles qtile(qg, x))
+    const int cg = wave / F::NQG;   // column group of this wave
     const int bh = blockIdx.x / nG, sg = blockIdx.x % nG;
     const int G = 1 << g;
     const int nchunk = min(G, N - sg * G);
@@ -1040,7 +1050,7 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
 
     Walk4Regs<F> pf;
     walk4_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
-                  min(F::C, Tlen - sg * G * F::C), L, it, tid, li, qd);
+                  min(F::C, Tlen - sg * G * F::C), L, tid);
 
     // Padding rows of K and V, P (its upper tiles and padding columns are
     // never written) and lambda^T (levels >= L) start at zero.
@@ -1098,89 +1108,121 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
         __syncthreads();
         walk4_store<F>(pf, sm, valid, L, invL, tid);
         if (ci + 1 < nchunk)
-            walk4_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, it, tid, li, qd);
+            walk4_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, tid);
         __syncthreads();
         const float gch = sm.gch;
-        const int i = 16 * it + li;      // this lane's query row
-        const float ai = sm.Aloc[i];
-        Frag qf[F::NUK];                 // Q^T fragments of query tile it
+        // This lane's query rows (one per query tile of the wave), their
+        // decay and their Q^T fragments.
+        int iq[F::QPW];
+        float ai[F::QPW];
+        Frag qf[F::QPW][F::NUK];
 #pragma unroll
-        for (int u = 0; u < F::NUK; ++u)
-            qf[u] = lds_frag(sm.Qs, F::LDK, i, u * F::KB, qd);
-
-        // Causal score tiles of query tile it, split over its column-group
-        // waves; masked by decay and level weight, stored as P[i][j].
-        for (int jt = cg; jt <= it; jt += F::NCG) {
-            floatx4 s = zero4();
+        for (int x = 0; x < F::QPW; ++x) {
+            iq[x] = 16 * F::qtile(qg, x) + li;
+            ai[x] = sm.Aloc[iq[x]];
 #pragma unroll
             for (int u = 0; u < F::NUK; ++u)
-                mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd), qf[u]);
-            float p[4];
-            if (jt < it) {
-                const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+                qf[x][u] = lds_frag(sm.Qs, F::LDK, iq[x], u * F::KB, qd);
+        }
+
+        // Causal score tiles (jt, it) of the group's query tiles, dealt
+        // round-robin to its column-group waves; masked by decay and level
+        // weight and stored as P[i][j].
+        {
+            int n = 0;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p[r] = s[r] * __expf(ai - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
-            } else {
+            for (int x = 0; x < F::QPW; ++x) {
+                const int it = F::qtile(qg, x);
+                const int i = iq[x];
+                for (int jt = 0; jt <= it; ++jt, ++n) {
+                    if (n % F::NCG != cg)
+                        continue;
+                    floatx4 s = zero4();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * jt + 4 * qd + r;
-                    float m = 0.f;
-                    if (j <= i) {
-                        const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                        m = __expf(ai - sm.Aloc[j]) * sm.lamT[lev * F::LDL + i];
+                    for (int u = 0; u < F::NUK; ++u)
+                        mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, u * F::KB, qd), qf[x][u]);
+                    float p[4];
+                    if (jt < it) {
+                        const float lm = sm.lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            p[r] = s[r] * __expf(ai[x] - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = 16 * jt + 4 * qd + r;
+                            float m = 0.f;
+                            if (j <= i) {
+                                const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
+                                m = __expf(ai[x] - sm.Aloc[j]) * sm.lamT[lev * F::LDL + i];
+                            }
+                            p[r] = s[r] * m;
+                        }
                     }
-                    p[r] = s[r] * m;
+                    bf16x4 pb;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        pb[r] = (__bf16)p[r];
+                    *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 16 * jt + 4 * qd) = pb;
                 }
             }
-            bf16x4 pb;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                pb[r] = (__bf16)p[r];
-            *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 16 * jt + 4 * qd) = pb;
         }
         __syncthreads();
 
-        // O^T = V^T P^T for this wave's column tiles.
-        floatx4 O[F::CPW];
+        // O^T = V^T P^T for this wave's query and column tiles.
+        floatx4 O[F::QPW][F::CPW];
 #pragma unroll
         for (int cc = 0; cc < F::CPW; ++cc) {
             const int c = cg * F::CPW + cc;
-            O[cc] = zero4();
 #pragma unroll
-            for (int u = 0; u < F::NUC; ++u)
-                if (u * F::KB <= 16 * it + 15)
-                    mma_unit(O[cc], tr_frag(sm.Vs, F::LDV, u * F::KB, 16 * c, li, qd),
-                             lds_frag(sm.Ps, F::LDP, i, u * F::KB, qd));
+            for (int x = 0; x < F::QPW; ++x)
+                O[x][cc] = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUC; ++u) {
+                const Frag vt = tr_frag(sm.Vs, F::LDV, u * F::KB, 16 * c, li, qd);
+#pragma unroll
+                for (int x = 0; x < F::QPW; ++x)
+                    if (u * F::KB <= 16 * F::qtile(qg, x) + 15)
+                        mma_unit(O[x][cc], vt, lds_frag(sm.Ps, F::LDP, iq[x], u * F::KB, qd));
+            }
         }
 
         // Levels inside the group (stack slots in LDS).
 #pragma unroll
         for (int m = 0; m < kMaxGroupLog2; ++m)
             if (m < g && ((ci >> m) & 1)) {
-                const float f = sm.lamT[(log2C + m + 1) * F::LDL + i] * __expf(ai + gap[m]);
+                float f[F::QPW];
+#pragma unroll
+                for (int x = 0; x < F::QPW; ++x)
+                    f[x] = sm.lamT[(log2C + m + 1) * F::LDL + iq[x]] * __expf(ai[x] + gap[m]);
                 walk4_level<F>(O, qf, sm.stk + m * F::SLOT, cg, f, lane);
             }
         // Levels above the group.
         for (int ii = 0; ii < npop; ++ii) {
             const int p = sm.plist[ii];
-            const float f = sm.lamT[(log2C + g + 1 + p) * F::LDL + i] * __expf(ai + agrun + sm.off[p]);
+            float f[F::QPW];
+#pragma unroll
+            for (int x = 0; x < F::QPW; ++x)
+                f[x] = sm.lamT[(log2C + g + 1 + p) * F::LDL + iq[x]] * __expf(ai[x] + agrun + sm.off[p]);
             const T *st = (ii < F::NRES) ? sm.Dres + (size_t)ii * F::SLOT : Dg + sm.blk[ii];
             walk4_level<F>(O, qf, st, cg, f, lane);
         }
 
-        // Output: lane holds O[i][16c + 4qd .. 16c + 4qd + 3].
-        if (i < valid) {
+        // Output: lane holds O[i][16c + 4qd .. 16c + 4qd + 3] for i = iq[x].
 #pragma unroll
-            for (int cc = 0; cc < F::CPW; ++cc) {
-                const int c = cg * F::CPW + cc;
-                typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
-                bf16x4 ob;
+        for (int x = 0; x < F::QPW; ++x) {
+            if (iq[x] < valid) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    ob[r] = (__bf16)O[cc][r];
-                __builtin_nontemporal_store(*reinterpret_cast<const u32x2 *>(&ob),
-                                            reinterpret_cast<u32x2 *>(out + (row0 + i) * F::DV + 16 * c + 4 * qd));
+                for (int cc = 0; cc < F::CPW; ++cc) {
+                    const int c = cg * F::CPW + cc;
+                    typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+                    bf16x4 ob;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ob[r] = (__bf16)O[x][cc][r];
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x2 *>(&ob),
+                                                reinterpret_cast<u32x2 *>(out + (row0 + iq[x]) * F::DV + 16 * c + 4 * qd));
+                }
             }
         }
 
