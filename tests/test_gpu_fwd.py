@@ -149,3 +149,44 @@ def test_output_guard_bands_untouched():
     _run(inp, cfg.chunk, out=out)
     assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
     _check_full(inp, out, "bf16")
+
+
+def _exact_bf16_inputs(B, H, T, dk, dv, seed):
+    """Inputs on which the bf16 path rounds nothing: a = 0 (every decay is
+    exactly 1), q, k, v sparse in {-1, 0, 1}, lambda a power of two per level.
+    Scores, masked scores, chunk and block states and the outputs are then
+    small multiples of 1/4, exact in bf16 and fp32 (the test checks this of
+    the outputs), so any error is an algebra error."""
+    rng = np.random.default_rng(seed)
+    L = synth.num_levels(T)
+
+    def sparse(shape, density):
+        x = rng.integers(-1, 2, size=shape).astype(np.float32)
+        return x * (rng.random(shape) < density)
+
+    q = sparse((B, H, T, dk), 0.08)
+    k = sparse((B, H, T, dk), 0.08)
+    v = sparse((B, H, T, dv), 0.25)
+    lam = np.broadcast_to(2.0 ** -(np.arange(L) % 3), (B, H, T, L)).astype(np.float32).copy()
+    return {
+        "q": torch.from_numpy(q).to(torch.bfloat16),
+        "k": torch.from_numpy(k).to(torch.bfloat16),
+        "v": torch.from_numpy(v).to(torch.bfloat16),
+        "a": torch.zeros((B, H, T), dtype=torch.float32),
+        "lam": torch.from_numpy(lam),
+    }
+
+
+@pytest.mark.parametrize("T,chunk,group_log2", [(4096, 64, 3), (4096, 64, 2), (1500, 32, 3), (777, 16, 1),
+                                                 (4096, 64, 0)])
+def test_bf16_walk_exact_on_exactly_representable_inputs(T, chunk, group_log2):
+    """A tight check of the bf16 kernels' chunk, level and stack algebra
+    (the 2e-2 bf16 tolerance alone would hide a small misplaced term)."""
+    announce(f"bf16 exact-arithmetic T={T} chunk={chunk} g={group_log2}")
+    inp = _exact_bf16_inputs(1, 3, T, 128, 64, 8000 + T)
+    got = f64(_run(inp, chunk, group_log2))
+    ref = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["lam"])
+    assert np.array_equal(torch.from_numpy(ref).to(torch.bfloat16).double().numpy(), ref)
+    e = rel_l2(got, ref)
+    print(f"rel_l2={e:.3e}")
+    assert e <= 1e-5
