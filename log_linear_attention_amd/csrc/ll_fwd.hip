@@ -1265,6 +1265,613 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
 }
 
 // ---------------------------------------------------------------------------
+// Kernel C'' (bf16): the chunk walk with specialised waves.
+//
+// The same per-chunk algebra as ll_chunk_walk, split over two kinds of wave
+// so that the two halves of a chunk's work overlap on every SIMD instead of
+// following each other:
+//  * NX compute waves own the output tiles (query-tile pairs x 16-column
+//    slices): masked score tiles -> P (shared through LDS), O^T = V^T P^T,
+//    the levels inside and above the group, the output rows;
+//  * NY helper waves fold each chunk's state into the Fenwick stack and move
+//    the next chunk's q, k, v, lambda, a from HBM through registers into LDS
+//    (and form its decay prefix).
+// Two workgroup barriers per chunk: A (chunk staged, stack slots ready) and
+// B (P complete).  What the helpers rewrite for chunk ci+1 while the compute
+// waves still read chunk ci after B (V, lambda^T, the token weights, the
+// chunk total) is double-buffered; Q, K and the decay prefix are read by the
+// compute waves only before B and are single-buffered.
+// ---------------------------------------------------------------------------
+template <class DT, int DK_, int DV_, int C_>
+struct WalkWS {
+    using T = typename DT::T;
+    using Frag = typename DT::Frag;
+    using DTag = DT;
+    static constexpr int DK = DK_, DV = DV_, C = C_;
+    static constexpr int KB = DT::KB, EPL = DT::EPL;
+    static constexpr int NMT = C / 16;                 // query (and key) tiles per chunk
+    static constexpr int NWC = DV / 16;                // 16-column output tiles
+    static constexpr int QPW = NMT >= 2 ? 2 : 1;       // query tiles per compute wave
+    static constexpr int NQG = NMT / QPW;              // query groups
+    static constexpr int CPW = NQG * NWC > 8 ? 2 : 1;  // output column tiles per compute wave
+    static constexpr int NCG = NWC / CPW;              // column groups
+    static constexpr int NX = NQG * NCG;               // compute waves
+    static constexpr int NY = 4;                       // helper waves
+    static constexpr int NW = NX + NY;
+    static constexpr int NT = 64 * NW;
+    static constexpr int NTY = 64 * NY;
+    static constexpr int CP = (C < KB) ? KB : C;
+    static constexpr int NUC = CP / KB;
+    static constexpr int NUK = DK / KB;
+    static constexpr int LDK = bf16_stride(DK, true);
+    static constexpr int LDV = bf16_stride(DV, false);
+    static constexpr int LDP = bf16_stride(CP, true);
+    static constexpr int LDL = C + 1;
+    static constexpr int NLV = 24;                     // lambda levels staged (T <= 2^23)
+    static constexpr int VEC = 8;
+    static constexpr int SLOT = DK * DV;               // elements of one state
+    // A helper wave folds the fragments of unit u = yw % NUK for the columns
+    // c = yw / NUK + (NY / NUK) * kk, so its K^T fragments are loaded once.
+    static constexpr int CSTEP = NY / NUK;
+    static constexpr int NFY = (NWC + CSTEP - 1) / CSTEP;
+    static constexpr int NFY1 = NFY;                   // folded before barrier B
+    static constexpr int KVEC = C * (DK / VEC);
+    static constexpr int NK = (KVEC + NTY - 1) / NTY;
+    static constexpr int VVEC = C * (DV / VEC);
+    static constexpr int NV = (VVEC + NTY - 1) / NTY;
+    static constexpr int NLAM = (C * NLV + NTY - 1) / NTY;
+    static constexpr int BASE_LDS = 2 * (C * LDK + CP * LDK + 2 * CP * LDV + C * LDP + kMaxGroupLog2 * SLOT) +
+                                    4 * (2 * NLV * LDL + C + 2 * CP) + 1024;
+    static constexpr int NRES_FIT = (160 * 1024 - BASE_LDS) / (2 * SLOT);
+    static constexpr int NRES = NRES_FIT < 0 ? 0 : (NRES_FIT > 8 ? 8 : NRES_FIT);
+    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NWC % CPW == 0 && NY % NUK == 0;
+    __device__ static constexpr int qtile(int qg, int x) { return x == 0 ? qg : NMT - 1 - qg; }
+};
+
+template <class F>
+struct alignas(16) WalkWSSmem {
+    using T = typename F::T;
+    T Qs[F::C * F::LDK];
+    T Ks[F::CP * F::LDK];
+    T Vs[2][F::CP * F::LDV];
+    T Ps[F::C * F::LDP];
+    T stk[kMaxGroupLog2 * F::SLOT];
+    T Dres[F::NRES > 0 ? F::NRES * F::SLOT : 8];
+    float lamT[2][F::NLV * F::LDL];
+    alignas(16) float wdec[2][F::CP];  // exp(chunk total - Aloc[j]): decay from token j to the chunk end
+    float Aloc[F::C];
+    float off[32];
+    size_t blk[32];
+    int plist[32];
+    int npop;
+    float gch[2];
+};
+
+template <class F>
+struct WalkWSRegs {
+    uint4 q[F::NK], k[F::NK], v[F::NV];
+    float lam[F::NLAM];
+    float a;
+};
+
+// Inclusive prefix sum over the 64 lanes of a fully active wave, with DPP
+// row shifts inside each 16-lane row and row broadcasts across rows (no LDS
+// round trips).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_shift(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, true));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x)
+{
+    x += dpp_shift<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_shift<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_shift<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_shift<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_shift<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_shift<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Per-head buffer descriptors of the walk's streamed inputs.  Loads through
+// them take 32-bit offsets, and every byte past the head's last token reads
+// as zero, which supplies the zero padding of a ragged last chunk.
+struct WSBuf {
+    __amdgpu_buffer_rsrc_t q, k, v, lam, a;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Streaming (non-temporal) 16- and 4-byte loads through a descriptor.
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ __forceinline__ float buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2));
+}
+
+// Helper thread ty (0 .. NTY-1) loads its share of the chunk starting at
+// token t0 of the head (rows past the head's end read as zero).
+template <class F>
+__device__ __forceinline__ void ws_load(WalkWSRegs<F> &r, const WSBuf &bf, int t0, int L, int ty)
+{
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = ty + i * F::NTY;
+        r.q[i] = r.k[i] = zero16();
+        if (idx < F::KVEC) {
+            const uint32_t off = (uint32_t)t0 * (F::DK * 2) + (uint32_t)idx * 16;
+            r.q[i] = buf_ld16(bf.q, off);
+            r.k[i] = buf_ld16(bf.k, off);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = ty + i * F::NTY;
+        r.v[i] = zero16();
+        if (idx < F::VVEC)
+            r.v[i] = buf_ld16(bf.v, (uint32_t)t0 * (F::DV * 2) + (uint32_t)idx * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = ty + i * F::NTY;
+        r.lam[i] = (idx < F::C * L) ? buf_ld4(bf.lam, ((uint32_t)t0 * L + idx) * 4) : 0.f;
+    }
+    r.a = (ty < F::C) ? buf_ld4(bf.a, (uint32_t)(t0 + ty) * 4) : 0.f;
+}
+
+// Stage a loaded chunk into LDS buffer b (Q and K rows, V rows, lambda^T),
+// and from helper wave 0 its decay prefix, token weights and total.
+template <class F>
+__device__ __forceinline__ void ws_store(const WalkWSRegs<F> &r, WalkWSSmem<F> &sm, int b, int valid, int L,
+                                         float invL, int ty)
+{
+    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < F::KVEC) {
+            *reinterpret_cast<uint4 *>(sm.Qs + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.q[i];
+            *reinterpret_cast<uint4 *>(sm.Ks + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.k[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < F::VVEC)
+            *reinterpret_cast<uint4 *>(sm.Vs[b] + (idx / VPR) * F::LDV + (idx % VPR) * F::VEC) = r.v[i];
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < valid * L) {
+            const int j = (int)(((float)idx + 0.5f) * invL);
+            sm.lamT[b][(idx - j * L) * F::LDL + j] = r.lam[i];
+        }
+    }
+    if (ty < 64) {
+        const float x = wave_prefix_sum(r.a);
+        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), F::C - 1));
+        if (ty < F::C)
+            sm.Aloc[ty] = x;
+        if (ty < F::CP)
+            sm.wdec[b][ty] = (ty < F::C) ? __expf(g - x) : 0.f;
+        if (ty == 0)
+            sm.gch[b] = g;
+    }
+}
+
+// Helper wave yw: fold the fragments kk in [K0, K1) of chunk ci's new stack
+// slot kc (chunk state K^T diag(w) V plus the slots below it, decayed to the
+// chunk end).  kf holds the wave's weighted K^T fragments of unit u.  All
+// V^T fragment reads are issued before the products so their latencies
+// overlap.
+template <class F, int K0, int K1>
+__device__ __forceinline__ void ws_fold(WalkWSSmem<F> &sm, const typename F::Frag (*kf)[2], int b, int kc,
+                                        const float *gapc, int yw, int lane, int li, int qd)
+{
+    using Frag = typename F::Frag;
+    if constexpr (K1 > K0) {
+        const int u = yw % F::NUK;
+        const int c0 = yw / F::NUK;
+        Frag vf[K1 - K0][F::NUC];
+#pragma unroll
+        for (int kk = K0; kk < K1; ++kk) {
+            const int c = min(c0 + F::CSTEP * kk, F::NWC - 1);
+#pragma unroll
+            for (int uj = 0; uj < F::NUC; ++uj)
+                vf[kk - K0][uj] = tr_frag(sm.Vs[b], F::LDV, uj * F::KB, 16 * c, li, qd);
+        }
+        floatx4 Hn[K1 - K0][2];
+#pragma unroll
+        for (int kk = K0; kk < K1; ++kk) {
+            Hn[kk - K0][0] = Hn[kk - K0][1] = zero4();
+#pragma unroll
+            for (int uj = 0; uj < F::NUC; ++uj)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    mma_unit(Hn[kk - K0][t], kf[uj][t], vf[kk - K0][uj]);
+        }
+#pragma unroll
+        for (int kk = K0; kk < K1; ++kk) {
+            const int c = c0 + F::CSTEP * kk;
+            if (c < F::NWC) {
+#pragma unroll
+                for (int m = 0; m < kMaxGroupLog2; ++m)
+                    if (m < kc)
+                        frag_axpy(Hn[kk - K0], state_frag<F>(sm.stk + m * F::SLOT, c, u, lane), 0, gapc[m], TBF16{});
+                *reinterpret_cast<Frag *>(sm.stk + kc * F::SLOT + ((size_t)(c * F::NUK + u) * 64 + lane) * F::EPL) =
+                    acc_frag(Hn[kk - K0], 0, TBF16{});
+            }
+        }
+    }
+}
+
+template <class F, class E>
+__device__ __forceinline__ void ws_zero(E *dst, int n, int t, int nt)
+{
+    for (int i = t; i < n; i += nt)
+        dst[i] = E(0.f);
+}
+
+// The groups one workgroup walks: a group sg and its mirror nG-1-sg of the
+// same head (their numbers of set bits, and so of levels above the group,
+// add up to about the same for every pair).
+struct WSGroups {
+    int n;          // 1 or 2
+    int sg0, sg1;   // group indices
+    int n0, n1;     // chunks in each (n1 = 0 when n = 1)
+    __device__ int sg(int i) const { return i ? sg1 : sg0; }
+    __device__ int nch(int i) const { return i ? n1 : n0; }
+};
+
+template <class F>
+__device__ __forceinline__ int ws_token(const WSGroups &gr, int G, int kk)
+{
+    return kk < gr.n0 ? (gr.sg0 * G + kk) * F::C : (gr.sg1 * G + kk - gr.n0) * F::C;
+}
+
+template <class F>
+__device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T *q, const typename F::T *k,
+                                          const typename F::T *v, const float *a, const float *lam, int Tlen, int L,
+                                          float invL, int bh, const WSGroups &gr, int G, int ty)
+{
+    using Frag = typename F::Frag;
+    const int lane = ty & 63, yw = ty >> 6, qd = lane >> 4, li = lane & 15;
+    const int u = yw % F::NUK;
+    const size_t hrow = (size_t)bh * Tlen;
+    const WSBuf bf = {head_rsrc(q + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
+                      head_rsrc(k + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
+                      head_rsrc(v + hrow * F::DV, (uint32_t)Tlen * F::DV * 2),
+                      head_rsrc(lam + hrow * L, (uint32_t)Tlen * L * 4), head_rsrc(a + hrow, (uint32_t)Tlen * 4)};
+    // The chunks of both groups form one stream kk = 0 .. K-1: chunk kk+1
+    // is staged (LDS buffer (kk+1)&1) and chunk kk+2 loaded while chunk kk
+    // is walked.
+    const int K = gr.n0 + gr.n1;
+    WalkWSRegs<F> pf;
+    ws_load<F>(pf, bf, ws_token<F>(gr, G, 0), L, ty);
+    // Padding rows of K and V, P (its upper tiles and padding columns are
+    // never written) and lambda^T (levels >= L) start at zero.
+    ws_zero<F>(sm.Ks, F::CP * F::LDK, ty, F::NTY);
+    ws_zero<F>(&sm.Vs[0][0], 2 * F::CP * F::LDV, ty, F::NTY);
+    ws_zero<F>(sm.Ps, F::C * F::LDP, ty, F::NTY);
+    ws_zero<F>(&sm.lamT[0][0], 2 * F::NLV * F::LDL, ty, F::NTY);
+    __syncthreads();  // prologue
+    {
+        const int t0 = ws_token<F>(gr, G, 0);
+        ws_store<F>(pf, sm, 0, min(F::C, Tlen - t0), L, invL, ty);
+    }
+    if (K > 1)
+        ws_load<F>(pf, bf, ws_token<F>(gr, G, 1), L, ty);
+    int kk = 0;
+    for (int gi = 0; gi < gr.n; ++gi) {
+        if (gi > 0)
+            __syncthreads();  // group boundary
+        const int nchunk = gr.nch(gi);
+        float gap[kMaxGroupLog2];
+#pragma unroll
+        for (int m = 0; m < kMaxGroupLog2; ++m)
+            gap[m] = 0.f;
+        for (int ci = 0; ci < nchunk; ++ci, ++kk) {
+            const int b = kk & 1;
+            const bool more = ci + 1 < nchunk;
+            const int kc = more ? __builtin_ctz((unsigned)(ci + 1)) : 0;
+            __syncthreads();  // A
+            const float gch = sm.gch[b];
+            float gapc[kMaxGroupLog2];
+            Frag kf[F::NUC][2];
+            if (more) {
+#pragma unroll
+                for (int m = 0; m < kMaxGroupLog2; ++m)
+                    gapc[m] = __expf(gap[m] + gch);
+#pragma unroll
+                for (int uj = 0; uj < F::NUC; ++uj) {
+                    const floatx4 w0 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 4 * qd]);
+                    const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 16 + 4 * qd]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        Frag f = tr_frag(sm.Ks, F::LDK, uj * F::KB, 16 * (2 * u + t), li, qd);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            f[e] = (__bf16)((float)f[e] * w0[e]);
+                            f[e + 4] = (__bf16)((float)f[e + 4] * w1[e]);
+                        }
+                        kf[uj][t] = f;
+                    }
+                }
+                ws_fold<F, 0, (F::NFY1 + 1) / 2>(sm, kf, b, kc, gapc, yw, lane, li, qd);
+                __builtin_amdgcn_sched_barrier(0);
+                ws_fold<F, (F::NFY1 + 1) / 2, F::NFY1>(sm, kf, b, kc, gapc, yw, lane, li, qd);
+            }
+            __syncthreads();  // B
+            if (more)
+                ws_fold<F, F::NFY1, F::NFY>(sm, kf, b, kc, gapc, yw, lane, li, qd);
+            if (kk + 1 < K) {
+                const int t1 = ws_token<F>(gr, G, kk + 1);
+                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty);
+                if (kk + 2 < K)
+                    ws_load<F>(pf, bf, ws_token<F>(gr, G, kk + 2), L, ty);
+            }
+            if (more) {
+#pragma unroll
+                for (int m = 0; m < kMaxGroupLog2; ++m)
+                    gap[m] = (m == kc) ? 0.f : gap[m] + gch;
+            }
+        }
+    }
+}
+
+template <class F>
+__device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out, int Tlen, int log2C, int g,
+                                           int bh, const WSGroups &gr, int nG, int Plev, int nL, int nLeft,
+                                           const float *Gam, const typename F::T *Dg, int tid)
+{
+    using T = typename F::T;
+    using Frag = typename F::Frag;
+    const int lane = tid & 63, wave = tid >> 6, qd = lane >> 4, li = lane & 15;
+    const int qg = wave % F::NQG;   // query group of this wave (query tiles qtile(qg, x))
+    const int cg = wave / F::NQG;   // column group of this wave
+    int kk = 0;   // chunk index in the workgroup's stream (LDS buffer parity)
+    for (int gi = 0; gi < gr.n; ++gi) {
+        const int sg = gr.sg(gi), nchunk = gr.nch(gi);
+        const int t0g = sg * (1 << g) * F::C;
+        const size_t rowg = (size_t)bh * Tlen + t0g;
+        if (gi > 0)
+            __syncthreads();  // group boundary: the previous group's Dres, off and plist are no longer read
+        // The group's blocks above it: one per set bit p of the group index,
+        // with the block state's offset and the log-decay from its end to the
+        // group start.  Every thread walks the bits itself, so the loads of the
+        // LDS-resident block states are issued at once.
+        constexpr int DPT = (F::SLOT / F::VEC + 64 * F::NX - 1) / (64 * F::NX);
+        const int npop = __builtin_popcount((unsigned)sg);   // every set bit of sg is below Plev
+        if (tid == 0) {
+            int n = 0;
+            size_t off = 0;
+            for (int p = 0; p < Plev; ++p) {
+                if ((sg >> p) & 1) {
+                    sm.plist[n] = p;
+                    sm.blk[n] = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * F::SLOT;
+                    ++n;
+                }
+                off += ((nL >> p) + 1) >> 1;
+            }
+        }
+        // Resident block states, copied straight to LDS (no wave reads Dres
+        // between the group boundary and the group's first barrier A).
+#pragma unroll
+        for (int ii = 0; ii < F::NRES; ++ii) {
+            if (ii < npop) {
+                unsigned x = (unsigned)sg;
+#pragma unroll
+                for (int k = 0; k < ii; ++k)
+                    x &= x - 1;
+                const int p = __builtin_ctz(x);   // the ii-th set bit
+                size_t off = 0;
+                for (int r = 0; r < p; ++r)
+                    off += ((nL >> r) + 1) >> 1;
+                const size_t blk = ((size_t)bh * nLeft + off + (sg >> (p + 1))) * F::SLOT;
+#pragma unroll
+                for (int e = 0; e < DPT; ++e) {
+                    const int idx = tid + e * 64 * F::NX;
+                    if (idx < F::SLOT / F::VEC)
+                        *reinterpret_cast<uint4 *>(sm.Dres + (size_t)ii * F::SLOT + (size_t)idx * F::VEC) =
+                            *reinterpret_cast<const uint4 *>(Dg + blk + (size_t)idx * F::VEC);
+                }
+            }
+        }
+        // off[p] = sum of the group log-decays over [lo_p, sg), lo_p the end of
+        // the block of bit p; the ranges nest, so one pass over the longest one
+        // (from 2^(top bit)) serves every bit.
+        if (wave == 0 && sg > 0) {
+            const int top = 31 - __builtin_clz((unsigned)sg);
+            for (int p = 0; p < Plev; ++p)
+                if (lane == p)
+                    sm.off[p] = 0.f;
+            for (int base = 1 << top; base < sg; base += 64) {
+                const int j = base + lane;
+                const float gj = (j < sg) ? Gam[(size_t)bh * nG + j] : 0.f;
+                for (int p = 0; p <= top; ++p) {
+                    if (!((sg >> p) & 1))
+                        continue;
+                    const int lo = ((sg >> (p + 1)) << (p + 1)) + (1 << p);
+                    const float t = wave_prefix_sum(j >= lo ? gj : 0.f);
+                    if (lane == 63)
+                        sm.off[p] += t;
+                }
+            }
+        }
+        if (gi == 0)
+            __syncthreads();  // prologue
+        float gap[kMaxGroupLog2];
+#pragma unroll
+        for (int m = 0; m < kMaxGroupLog2; ++m)
+            gap[m] = 0.f;
+        float agrun = 0.f;
+        for (int ci = 0; ci < nchunk; ++ci, ++kk) {
+            const int b = kk & 1;
+            const int valid = min(F::C, Tlen - t0g - ci * F::C);
+            const size_t row0 = rowg + (size_t)ci * F::C;
+            __syncthreads();  // A
+            const float gch = sm.gch[b];
+            const float *lamT = sm.lamT[b];
+            int iq[F::QPW];
+            float ai[F::QPW];
+            Frag qf[F::QPW][F::NUK];
+#pragma unroll
+            for (int x = 0; x < F::QPW; ++x) {
+                iq[x] = 16 * F::qtile(qg, x) + li;
+                ai[x] = sm.Aloc[iq[x]];
+#pragma unroll
+                for (int uk = 0; uk < F::NUK; ++uk)
+                    qf[x][uk] = lds_frag(sm.Qs, F::LDK, iq[x], uk * F::KB, qd);
+            }
+            // Causal score tiles (jt, it) of the group's query tiles, dealt
+            // round-robin to its column-group waves; masked by decay and level
+            // weight and stored as P[i][j].
+            {
+                int n = 0;
+#pragma unroll
+                for (int x = 0; x < F::QPW; ++x) {
+                    const int it = F::qtile(qg, x);
+                    const int i = iq[x];
+                    for (int jt = 0; jt <= it; ++jt, ++n) {
+                        if (n % F::NCG != cg)
+                            continue;
+                        floatx4 s = zero4();
+#pragma unroll
+                        for (int uk = 0; uk < F::NUK; ++uk)
+                            mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, uk * F::KB, qd), qf[x][uk]);
+                        float p[4];
+                        if (jt < it) {
+                            const float lm = lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                p[r] = s[r] * __expf(ai[x] - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int j = 16 * jt + 4 * qd + r;
+                                float m = 0.f;
+                                if (j <= i) {
+                                    const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
+                                    m = __expf(ai[x] - sm.Aloc[j]) * lamT[lev * F::LDL + i];
+                                }
+                                p[r] = s[r] * m;
+                            }
+                        }
+                        bf16x4 pb;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            pb[r] = (__bf16)p[r];
+                        *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 16 * jt + 4 * qd) = pb;
+                    }
+                }
+            }
+            __syncthreads();  // B
+
+            // O^T = V^T P^T for this wave's query and column tiles.
+            floatx4 O[F::QPW][F::CPW];
+#pragma unroll
+            for (int cc = 0; cc < F::CPW; ++cc) {
+                const int c = cg * F::CPW + cc;
+#pragma unroll
+                for (int x = 0; x < F::QPW; ++x)
+                    O[x][cc] = zero4();
+#pragma unroll
+                for (int uc = 0; uc < F::NUC; ++uc) {
+                    const Frag vt = tr_frag(sm.Vs[b], F::LDV, uc * F::KB, 16 * c, li, qd);
+#pragma unroll
+                    for (int x = 0; x < F::QPW; ++x)
+                        if (uc * F::KB <= 16 * F::qtile(qg, x) + 15)
+                            mma_unit(O[x][cc], vt, lds_frag(sm.Ps, F::LDP, iq[x], uc * F::KB, qd));
+                }
+            }
+            // Levels inside the group (stack slots in LDS).
+#pragma unroll
+            for (int m = 0; m < kMaxGroupLog2; ++m)
+                if (m < g && ((ci >> m) & 1)) {
+                    float f[F::QPW];
+#pragma unroll
+                    for (int x = 0; x < F::QPW; ++x)
+                        f[x] = lamT[(log2C + m + 1) * F::LDL + iq[x]] * __expf(ai[x] + gap[m]);
+                    walk4_level<F>(O, qf, sm.stk + m * F::SLOT, cg, f, lane);
+                }
+            // Levels above the group.
+            for (int ii = 0; ii < npop; ++ii) {
+                const int p = sm.plist[ii];
+                float f[F::QPW];
+#pragma unroll
+                for (int x = 0; x < F::QPW; ++x)
+                    f[x] = lamT[(log2C + g + 1 + p) * F::LDL + iq[x]] * __expf(ai[x] + agrun + sm.off[p]);
+                const T *st = (ii < F::NRES) ? sm.Dres + (size_t)ii * F::SLOT : Dg + sm.blk[ii];
+                walk4_level<F>(O, qf, st, cg, f, lane);
+            }
+            // Output: lane holds O[i][16c + 4qd .. 16c + 4qd + 3] for i = iq[x].
+#pragma unroll
+            for (int x = 0; x < F::QPW; ++x) {
+                if (iq[x] < valid) {
+#pragma unroll
+                    for (int cc = 0; cc < F::CPW; ++cc) {
+                        const int c = cg * F::CPW + cc;
+                        typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+                        bf16x4 ob;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            ob[r] = (__bf16)O[x][cc][r];
+                        __builtin_nontemporal_store(*reinterpret_cast<const u32x2 *>(&ob),
+                                                    reinterpret_cast<u32x2 *>(out + (row0 + iq[x]) * F::DV + 16 * c + 4 * qd));
+                    }
+                }
+            }
+            if (ci + 1 < nchunk) {
+                const int kc = __builtin_ctz((unsigned)(ci + 1));
+#pragma unroll
+                for (int m = 0; m < kMaxGroupLog2; ++m)
+                    gap[m] = (m == kc) ? 0.f : gap[m] + gch;
+            }
+            agrun += gch;
+        }
+    }
+}
+
+template <class F>
+__global__ __launch_bounds__(F::NT) void ll_chunk_walk_ws(
+    const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
+    const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
+    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
+    const typename F::T *__restrict__ Dg)
+{
+    __shared__ WalkWSSmem<F> sm;
+    const int tid = threadIdx.x, wave = tid >> 6;
+    // Work item of this workgroup.  Workgroups b, b+8, b+16, ... run on the
+    // same XCD (and share its L2); each XCD gets a contiguous range of items,
+    // so the block states a head's groups read stay in one L2.
+    const int nb = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int per = nb >> 3, rem = nb & 7, xcd = bid & 7;
+    const int wid = xcd * per + min(xcd, rem) + (bid >> 3);
+    const int npair = (nG + 1) >> 1;
+    const int bh = wid / npair, pr = wid % npair;
+    const int G = 1 << g;
+    WSGroups gr;
+    gr.sg0 = pr;
+    gr.sg1 = nG - 1 - pr;
+    gr.n = (gr.sg1 != pr) ? 2 : 1;
+    gr.n0 = min(G, N - pr * G);
+    gr.n1 = (gr.n == 2) ? min(G, N - gr.sg1 * G) : 0;
+    if (wave >= F::NX)
+        ws_helper<F>(sm, q, k, v, a, lam, Tlen, L, 1.f / (float)L, bh, gr, G, tid - 64 * F::NX);
+    else
+        ws_compute<F>(sm, out, Tlen, log2C, g, bh, gr, nG, Plev, nL, nLeft, Gam, Dg, tid);
+}
+
+// ---------------------------------------------------------------------------
 // Host side: plan and launch.
 // ---------------------------------------------------------------------------
 
@@ -1361,7 +1968,20 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         }
     }
     using W4 = Walk4<typename F::DTag, F::DK, F::DV, F::C>;
+    using WS = WalkWS<typename F::DTag, F::DK, F::DV, F::C>;
     prof_before("ll_chunk_walk", s);
+    if constexpr (F::TR && WS::FITS) {
+        // 32-bit buffer offsets within one head.
+        const bool fits32 = (int64_t)A.T * (F::DK > F::DV ? F::DK : F::DV) * 2 < ((int64_t)1 << 31) &&
+                            (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
+        if (A.L <= WS::NLV && fits32) {
+            hipLaunchKernelGGL(ll_chunk_walk_ws<WS>, dim3(BH * ((P.nG + 1) / 2)), dim3(WS::NT), 0, s, (const T *)A.q,
+                               (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N,
+                               P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
+            prof_after(s);
+            return hipGetLastError();
+        }
+    }
     if constexpr (F::TR && W4::FITS) {
         hipLaunchKernelGGL(ll_chunk_walk<W4>, dim3(BH * P.nG), dim3(W4::NT), 0, s, (const T *)A.q, (const T *)A.k,
                            (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL,
