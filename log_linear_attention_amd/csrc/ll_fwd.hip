@@ -411,74 +411,111 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
 // Kernel B: left-child block states of the tree over groups.
 //
 // Leaves are states of consecutive blocks at level p0 (groups for p0 = 0,
-// blocks of 64 groups for p0 = 6, ...), each with its total log-decay.  One
-// thread owns one state element of one tile of 64 leaves; it loads the 64
-// leaves into registers, builds the six tree levels above them in registers
-// (merge: exp(decay of the right half) * left + right), writes every
-// complete left child in MFMA B-operand order, and the tile total for the
-// next launch.  A block J at level p is complete when it ends at or before
-// the last complete group: (J + 1) * 2^p <= nL.
+// blocks of 64 groups for p0 = 6, ...), each with its total log-decay.  A
+// workgroup owns the state elements that make up one row of 16-byte
+// fragments (unit u, lane quad qd: EPL rows x all dv columns) of one tile of
+// 64 leaves; each thread loads its elements of the 64 leaves into registers
+// and builds the six tree levels above them (merge: exp(decay of the right
+// half) * left + right).  Every complete left child is staged in LDS in
+// fragment order and then written with 16-byte stores, and the tile total
+// goes out for the next launch.  A block J at level p is complete when it
+// ends at or before the last complete group: (J + 1) * 2^p <= nL.
 // ---------------------------------------------------------------------------
 template <class F>
-__global__ __launch_bounds__(256) void ll_left_tree(const float *__restrict__ leaves,
-                                                    const float *__restrict__ gleaves, int nleaves, int lstride,
-                                                    int gstride, int p0, int nL, int nLeft,
-                                                    typename F::T *__restrict__ Dg, float *__restrict__ tot,
-                                                    float *__restrict__ gtot, int tstride)
+struct TreeGeom {
+    static constexpr int NE = F::EPL / 4;          // elements per thread (rows e and e + 4)
+    static constexpr int NTH = 4 * F::DV;          // threads: 4 row slots x dv columns
+    static constexpr int NSLOT = 63;               // left children of six levels over 64 leaves
+    static constexpr int CHUNK = F::EPL * (int)sizeof(typename F::T);   // bytes of one fragment lane
+    static_assert(CHUNK == 16, "one fragment lane is 16 bytes");
+};
+
+template <class F>
+__global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
+    const float *__restrict__ leaves, const float *__restrict__ gleaves, int nleaves, int lstride, int gstride,
+    int p0, int nL, int nLeft, typename F::T *__restrict__ Dg, float *__restrict__ tot, float *__restrict__ gtot,
+    int tstride)
 {
     using T = typename F::T;
+    using TG = TreeGeom<F>;
     constexpr int DKV = F::DK * F::DV;
     __shared__ float gsh[64];
+    __shared__ uint4 stage[TG::NSLOT * F::DV];   // [slot][column] fragment lanes
     const int tid = threadIdx.x;
-    const int elem = blockIdx.x * 256 + tid;
+    const int u = blockIdx.x >> 2, qd = blockIdx.x & 3;
     const int tile = blockIdx.y, bh = blockIdx.z;
     const int base = tile * 64;
+    const int r = tid / F::DV, c = tid % F::DV;
+    int dd[TG::NE];
+#pragma unroll
+    for (int h = 0; h < TG::NE; ++h)
+        dd[h] = F::KB * u + unit_row(r + 4 * h, qd);
     if (tid < 64)
         gsh[tid] = (base + tid < nleaves) ? gleaves[(size_t)bh * gstride + base + tid] : 0.f;
-    float x[64];
+    float x[TG::NE][64];
 #pragma unroll
     for (int i = 0; i < 64; ++i)
-        x[i] = (base + i < nleaves && elem < DKV) ? leaves[((size_t)bh * lstride + base + i) * DKV + elem] : 0.f;
+#pragma unroll
+        for (int h = 0; h < TG::NE; ++h)
+            x[h][i] = (base + i < nleaves)
+                          ? leaves[((size_t)bh * lstride + base + i) * DKV + (size_t)dd[h] * F::DV + c]
+                          : 0.f;
     __syncthreads();
-    if (elem >= DKV)
-        return;
     float G[64];
 #pragma unroll
     for (int i = 0; i < 64; ++i)
         G[i] = gsh[i];
 
-    // Where this element sits inside a block state stored in B-operand order.
-    const int d = elem / F::DV, c = elem % F::DV;
-    const int u = d / F::KB, r = d % F::KB;
-    const int e = 4 * (r >> 4) + (r & 3), qd = (r & 15) >> 2;
-    const int fv = ((c >> 4) * F::NUK + u) * 64 + qd * 16 + (c & 15);
-    const size_t frag_off = (size_t)fv * F::EPL + e;
-
-    size_t offp = 0;  // first left block of level p0 + lv for this head
-    for (int pp = 0; pp < p0; ++pp)
-        offp += ((nL >> pp) + 1) >> 1;
+    // Fragment lane of this thread's elements: lane (qd, c % 16) of
+    // fragment (c / 16, u); element e = r + 4h.
+    T *st = reinterpret_cast<T *>(stage);
+    int slot = 0;
 #pragma unroll
     for (int lv = 0; lv < 6; ++lv) {
-        const int p = p0 + lv;
         const int width = 64 >> lv;
-        const int J0 = base >> lv;
 #pragma unroll
-        for (int j = 0; j < width; ++j) {
-            const int J = J0 + j;
-            if (((J & 1) == 0) && ((int64_t)(J + 1) << p) <= nL)
-                Dg[((size_t)bh * nLeft + offp + (J >> 1)) * DKV + frag_off] = from_f32<T>(x[j]);
-        }
-        offp += ((nL >> p) + 1) >> 1;
+        for (int j = 0; j < width; j += 2, ++slot)
+#pragma unroll
+            for (int h = 0; h < TG::NE; ++h)
+                st[((size_t)slot * F::DV + c) * F::EPL + r + 4 * h] = from_f32<T>(x[h][j]);
 #pragma unroll
         for (int j = 0; j < width / 2; ++j) {
-            x[j] = __expf(G[2 * j + 1]) * x[2 * j] + x[2 * j + 1];
+#pragma unroll
+            for (int h = 0; h < TG::NE; ++h)
+                x[h][j] = __expf(G[2 * j + 1]) * x[h][2 * j] + x[h][2 * j + 1];
             G[j] = G[2 * j] + G[2 * j + 1];
         }
     }
     if (base + 64 <= nleaves && tot != nullptr) {
-        tot[((size_t)bh * tstride + tile) * DKV + elem] = x[0];
-        if (elem == 0)
+#pragma unroll
+        for (int h = 0; h < TG::NE; ++h)
+            tot[((size_t)bh * tstride + tile) * DKV + (size_t)dd[h] * F::DV + c] = x[h][0];
+        if (tid == 0)
             gtot[(size_t)bh * tstride + tile] = G[0];
+    }
+    __syncthreads();
+    // Complete left children, one 16-byte fragment lane per thread and
+    // column: slot s is child J = J0 + 2 * jj of level lv.
+    size_t offp0 = 0;   // first left block of level p0 for this head
+    for (int pp = 0; pp < p0; ++pp)
+        offp0 += ((nL >> pp) + 1) >> 1;
+    for (int idx = tid; idx < TG::NSLOT * F::DV; idx += TG::NTH) {
+        const int s = idx / F::DV, cc = idx % F::DV;
+        int lv = 0, first = 0;
+        while (s >= first + (32 >> lv)) {
+            first += 32 >> lv;
+            ++lv;
+        }
+        const int p = p0 + lv;
+        const int J = (base >> lv) + 2 * (s - first);
+        if (((int64_t)(J + 1) << p) > nL)
+            continue;
+        size_t offp = offp0;
+        for (int pp = p0; pp < p; ++pp)
+            offp += ((nL >> pp) + 1) >> 1;
+        const int fv = ((cc >> 4) * F::NUK + u) * 64 + qd * 16 + (cc & 15);
+        *reinterpret_cast<uint4 *>(Dg + ((size_t)bh * nLeft + offp + (J >> 1)) * DKV + (size_t)fv * F::EPL) =
+            stage[idx];
     }
 }
 
@@ -1950,7 +1987,7 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             const int ntiles = (nleaves + 63) / 64;
             const int complete = nleaves / 64;
             prof_before("ll_left_tree", s);
-            hipLaunchKernelGGL(ll_left_tree<F>, dim3((F::DK * F::DV + 255) / 256, ntiles, BH), dim3(256), 0, s,
+            hipLaunchKernelGGL(ll_left_tree<F>, dim3(4 * F::NUK, ntiles, BH), dim3(TreeGeom<F>::NTH), 0, s,
                                leaves, gleaves, nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg,
                                complete > 0 ? tot[ping] : nullptr, gtot[ping], ntiles);
             prof_after(s);
