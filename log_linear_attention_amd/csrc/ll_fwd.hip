@@ -223,6 +223,33 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *base, int ld, int jb, in
     return r;
 }
 
+// Paired-quad column layout of a bf16 LDS tile (used by the specialised
+// walk for Q, K and P).  Inside every 32-column unit, logical column
+// 16h + 4q + r is stored at 8q + 4h + r, so the two 4-element halves of a
+// lane's operand fragment (columns 4q.. and 16 + 4q..) are adjacent and the
+// fragment is one 16-byte read.  The contraction order is unchanged.
+__device__ __forceinline__ bf16x8 pq_frag(const __bf16 *base, int ld, int row, int col0, int qd)
+{
+    return *reinterpret_cast<const bf16x8 *>(base + row * ld + col0 + 8 * qd);
+}
+
+// Position of the 4-column group starting at logical column 16h + 4q of a
+// unit (relative to the unit start).
+__device__ __forceinline__ constexpr int pq_pos(int h, int q) { return 8 * q + 4 * h; }
+
+// Transpose-read fragment (as tr_frag) of the 16 logical columns
+// 32u + 16t .. 32u + 16t + 15 of a paired-quad tile: rows jb .. jb+31.
+__device__ __forceinline__ bf16x8 pq_tr_frag(const __bf16 *base, int ld, int jb, int u, int t, int li, int qd)
+{
+    const __bf16 *p = base + (jb + 4 * qd + (li >> 2)) * ld + 32 * u + pq_pos(t, li & 3);
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 16 * ld));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
 // Scale the token-indexed fragment f of unit u by w_j = exp(g - Aloc[j])
 // (the decay from token j to the chunk end); padding tokens j >= C get 0.
 template <class F>
@@ -997,8 +1024,14 @@ __device__ __forceinline__ void walk4_store(const Walk4Regs<F> &r, Walk4Smem<F> 
     for (int i = 0; i < F::NK; ++i) {
         const int idx = tid + i * F::NT;
         if (idx < F::KVEC) {
-            *reinterpret_cast<uint4 *>(sm.Qs + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.q[i];
-            *reinterpret_cast<uint4 *>(sm.Ks + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.k[i];
+            // 8 logical columns 8m .. 8m+7 = two 4-column groups (q = 2(m%2), 2(m%2)+1; h = (m/2)%2)
+            const int m = idx % KPR;
+            const int pos = (idx / KPR) * F::LDK + 32 * (m >> 2) + pq_pos((m >> 1) & 1, 2 * (m & 1));
+            typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+            *reinterpret_cast<u32x2 *>(sm.Qs + pos) = u32x2{r.q[i].x, r.q[i].y};
+            *reinterpret_cast<u32x2 *>(sm.Qs + pos + 8) = u32x2{r.q[i].z, r.q[i].w};
+            *reinterpret_cast<u32x2 *>(sm.Ks + pos) = u32x2{r.k[i].x, r.k[i].y};
+            *reinterpret_cast<u32x2 *>(sm.Ks + pos + 8) = u32x2{r.k[i].z, r.k[i].w};
         }
     }
 #pragma unroll
@@ -1475,8 +1508,14 @@ __device__ __forceinline__ void ws_store(const WalkWSRegs<F> &r, WalkWSSmem<F> &
     for (int i = 0; i < F::NK; ++i) {
         const int idx = ty + i * F::NTY;
         if (idx < F::KVEC) {
-            *reinterpret_cast<uint4 *>(sm.Qs + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.q[i];
-            *reinterpret_cast<uint4 *>(sm.Ks + (idx / KPR) * F::LDK + (idx % KPR) * F::VEC) = r.k[i];
+            // 8 logical columns 8m .. 8m+7 = two 4-column groups (q = 2(m%2), 2(m%2)+1; h = (m/2)%2)
+            const int m = idx % KPR;
+            const int pos = (idx / KPR) * F::LDK + 32 * (m >> 2) + pq_pos((m >> 1) & 1, 2 * (m & 1));
+            typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+            *reinterpret_cast<u32x2 *>(sm.Qs + pos) = u32x2{r.q[i].x, r.q[i].y};
+            *reinterpret_cast<u32x2 *>(sm.Qs + pos + 8) = u32x2{r.q[i].z, r.q[i].w};
+            *reinterpret_cast<u32x2 *>(sm.Ks + pos) = u32x2{r.k[i].x, r.k[i].y};
+            *reinterpret_cast<u32x2 *>(sm.Ks + pos + 8) = u32x2{r.k[i].z, r.k[i].w};
         }
     }
 #pragma unroll
@@ -1634,7 +1673,7 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
                     const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 16 + 4 * qd]);
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
-                        Frag f = tr_frag(sm.Ks, F::LDK, uj * F::KB, 16 * (2 * u + t), li, qd);
+                        Frag f = pq_tr_frag(sm.Ks, F::LDK, uj * F::KB, u, t, li, qd);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             f[e] = (__bf16)((float)f[e] * w0[e]);
@@ -1767,7 +1806,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                 ai[x] = sm.Aloc[iq[x]];
 #pragma unroll
                 for (int uk = 0; uk < F::NUK; ++uk)
-                    qf[x][uk] = lds_frag(sm.Qs, F::LDK, iq[x], uk * F::KB, qd);
+                    qf[x][uk] = pq_frag(sm.Qs, F::LDK, iq[x], uk * F::KB, qd);
             }
             // Causal score tiles (jt, it) of the group's query tiles, dealt
             // round-robin to its column-group waves; masked by decay and level
@@ -1784,7 +1823,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                         floatx4 s = zero4();
 #pragma unroll
                         for (int uk = 0; uk < F::NUK; ++uk)
-                            mma_unit(s, lds_frag(sm.Ks, F::LDK, 16 * jt + li, uk * F::KB, qd), qf[x][uk]);
+                            mma_unit(s, pq_frag(sm.Ks, F::LDK, 16 * jt + li, uk * F::KB, qd), qf[x][uk]);
                         float p[4];
                         if (jt < it) {
                             const float lm = lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
@@ -1807,7 +1846,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             pb[r] = (__bf16)p[r];
-                        *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 16 * jt + 4 * qd) = pb;
+                        *reinterpret_cast<bf16x4 *>(sm.Ps + i * F::LDP + 32 * (jt >> 1) + pq_pos(jt & 1, qd)) = pb;
                     }
                 }
             }
@@ -1827,7 +1866,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
 #pragma unroll
                     for (int x = 0; x < F::QPW; ++x)
                         if (uc * F::KB <= 16 * F::qtile(qg, x) + 15)
-                            mma_unit(O[x][cc], vt, lds_frag(sm.Ps, F::LDP, iq[x], uc * F::KB, qd));
+                            mma_unit(O[x][cc], vt, pq_frag(sm.Ps, F::LDP, iq[x], uc * F::KB, qd));
                 }
             }
             // Levels inside the group (stack slots in LDS).
