@@ -1497,41 +1497,23 @@ __device__ __forceinline__ void ws_load(WalkWSRegs<F> &r, const WSBuf &bf, int t
     r.a = (ty < F::C) ? buf_ld4(bf.a, (uint32_t)(t0 + ty) * 4) : 0.f;
 }
 
-// Stage a loaded chunk into LDS buffer b (Q and K rows, V rows, lambda^T),
-// and from helper wave 0 its decay prefix, token weights and total.
+// Quad-lane exchange: the value of lane l ^ 2 of the same 4-lane quad.
+__device__ __forceinline__ unsigned int quad_swap2(unsigned int x)
+{
+    return (unsigned int)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+}
+
+// Stage a loaded chunk into LDS buffer b (Q and K rows in paired-quad
+// order, V rows, lambda^T), and from helper wave 0 its decay prefix, token
+// weights and total.  With `next`, each register is reloaded with the chunk
+// at token t_next as soon as it has been stored, so the next chunk's loads
+// are issued while the stores drain.
 template <class F>
-__device__ __forceinline__ void ws_store(const WalkWSRegs<F> &r, WalkWSSmem<F> &sm, int b, int valid, int L,
-                                         float invL, int ty)
+__device__ __forceinline__ void ws_store(WalkWSRegs<F> &r, WalkWSSmem<F> &sm, int b, int valid, int L, float invL,
+                                         int ty, bool next, const WSBuf &bf, int t_next)
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
-#pragma unroll
-    for (int i = 0; i < F::NK; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < F::KVEC) {
-            // 8 logical columns 8m .. 8m+7 = two 4-column groups (q = 2(m%2), 2(m%2)+1; h = (m/2)%2)
-            const int m = idx % KPR;
-            const int pos = (idx / KPR) * F::LDK + 32 * (m >> 2) + pq_pos((m >> 1) & 1, 2 * (m & 1));
-            typedef unsigned int u32x2 __attribute__((__vector_size__(2 * sizeof(unsigned int))));
-            *reinterpret_cast<u32x2 *>(sm.Qs + pos) = u32x2{r.q[i].x, r.q[i].y};
-            *reinterpret_cast<u32x2 *>(sm.Qs + pos + 8) = u32x2{r.q[i].z, r.q[i].w};
-            *reinterpret_cast<u32x2 *>(sm.Ks + pos) = u32x2{r.k[i].x, r.k[i].y};
-            *reinterpret_cast<u32x2 *>(sm.Ks + pos + 8) = u32x2{r.k[i].z, r.k[i].w};
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < F::NV; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < F::VVEC)
-            *reinterpret_cast<uint4 *>(sm.Vs[b] + (idx / VPR) * F::LDV + (idx % VPR) * F::VEC) = r.v[i];
-    }
-#pragma unroll
-    for (int i = 0; i < F::NLAM; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < valid * L) {
-            const int j = (int)(((float)idx + 0.5f) * invL);
-            sm.lamT[b][(idx - j * L) * F::LDL + j] = r.lam[i];
-        }
-    }
+    static_assert(KPR % 4 == 0, "a unit spans four 16-byte row vectors");
     if (ty < 64) {
         const float x = wave_prefix_sum(r.a);
         const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), F::C - 1));
@@ -1541,6 +1523,52 @@ __device__ __forceinline__ void ws_store(const WalkWSRegs<F> &r, WalkWSSmem<F> &
             sm.wdec[b][ty] = (ty < F::C) ? __expf(g - x) : 0.f;
         if (ty == 0)
             sm.gch[b] = g;
+    }
+    if (next)
+        r.a = (ty < F::C) ? buf_ld4(bf.a, (uint32_t)(t_next + ty) * 4) : 0.f;
+    // Row vector m (logical columns 8m .. 8m+7) and its quad partner m ^ 2
+    // hold the two halves of the paired-quad chunks q = 2(m%2) (written by
+    // the lane with m%4 < 2) and q = 2(m%2) + 1 (by its partner).
+    const bool lowpair = ((ty >> 1) & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < F::NK; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < F::KVEC) {
+            const int m = idx % KPR;
+            const int pos = (idx / KPR) * F::LDK + 32 * (m >> 2) + 16 * (m & 1) + (lowpair ? 0 : 8);
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const uint4 x = w ? r.k[i] : r.q[i];
+                const unsigned int px = quad_swap2(x.x), py = quad_swap2(x.y);
+                const unsigned int pz = quad_swap2(x.z), pw = quad_swap2(x.w);
+                const uint4 c = lowpair ? make_uint4(x.x, x.y, px, py) : make_uint4(pz, pw, x.z, x.w);
+                *reinterpret_cast<uint4 *>((w ? sm.Ks : sm.Qs) + pos) = c;
+            }
+            if (next) {
+                const uint32_t off = (uint32_t)t_next * (F::DK * 2) + (uint32_t)idx * 16;
+                r.q[i] = buf_ld16(bf.q, off);
+                r.k[i] = buf_ld16(bf.k, off);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NV; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < F::VVEC) {
+            *reinterpret_cast<uint4 *>(sm.Vs[b] + (idx / VPR) * F::LDV + (idx % VPR) * F::VEC) = r.v[i];
+            if (next)
+                r.v[i] = buf_ld16(bf.v, (uint32_t)t_next * (F::DV * 2) + (uint32_t)idx * 16);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < F::NLAM; ++i) {
+        const int idx = ty + i * F::NTY;
+        if (idx < valid * L) {
+            const int j = (int)(((float)idx + 0.5f) * invL);
+            sm.lamT[b][(idx - j * L) * F::LDL + j] = r.lam[i];
+        }
+        if (next)
+            r.lam[i] = (idx < F::C * L) ? buf_ld4(bf.lam, ((uint32_t)t_next * L + idx) * 4) : 0.f;
     }
 }
 
@@ -1642,10 +1670,8 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
     __syncthreads();  // prologue
     {
         const int t0 = ws_token<F>(gr, G, 0);
-        ws_store<F>(pf, sm, 0, min(F::C, Tlen - t0), L, invL, ty);
+        ws_store<F>(pf, sm, 0, min(F::C, Tlen - t0), L, invL, ty, K > 1, bf, K > 1 ? ws_token<F>(gr, G, 1) : 0);
     }
-    if (K > 1)
-        ws_load<F>(pf, bf, ws_token<F>(gr, G, 1), L, ty);
     int kk = 0;
     for (int gi = 0; gi < gr.n; ++gi) {
         if (gi > 0)
@@ -1691,9 +1717,8 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
                 ws_fold<F, F::NFY1, F::NFY>(sm, kf, b, kc, gapc, yw, lane, li, qd);
             if (kk + 1 < K) {
                 const int t1 = ws_token<F>(gr, G, kk + 1);
-                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty);
-                if (kk + 2 < K)
-                    ws_load<F>(pf, bf, ws_token<F>(gr, G, kk + 2), L, ty);
+                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty, kk + 2 < K, bf,
+                            kk + 2 < K ? ws_token<F>(gr, G, kk + 2) : 0);
             }
             if (more) {
 #pragma unroll
