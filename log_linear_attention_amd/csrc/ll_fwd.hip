@@ -80,6 +80,18 @@ constexpr int bf16_stride(int cols, bool normal)
     return 2 * s;
 }
 
+// Row stride (in 16-bit elements) of a bf16 LDS tile read only by transpose
+// reads and written by whole rows: the eight rows a half-wave's transpose
+// read touches (8 dwords each) must fall in disjoint bank ranges, which
+// holds when the stride in dwords is an odd multiple of 8.
+constexpr int tr_stride(int cols)
+{
+    int s = cols / 2;
+    while (s % 16 != 8)
+        ++s;
+    return 2 * s;
+}
+
 // Tile geometry.  SPLIT (the chunk walk) gives each 16-column slice of dv
 // two waves that share the slice's state work and split the query tiles, so
 // one workgroup keeps two waves per SIMD within the 256-register budget.
@@ -1374,10 +1386,10 @@ struct WalkWS {
     static constexpr int NUC = CP / KB;
     static constexpr int NUK = DK / KB;
     static constexpr int LDK = bf16_stride(DK, true);
-    static constexpr int LDV = bf16_stride(DV, false);
+    static constexpr int LDV = tr_stride(DV);
     static constexpr int LDP = bf16_stride(CP, true);
     static constexpr int LDL = C + 1;
-    static constexpr int NLV = 24;                     // lambda levels staged (T <= 2^23)
+    static constexpr int NLV = 22;                     // lambda levels staged (T <= 2^21)
     static constexpr int VEC = 8;
     static constexpr int SLOT = DK * DV;               // elements of one state
     // A helper wave folds the fragments of unit u = yw % NUK for the columns
@@ -1409,7 +1421,7 @@ struct alignas(16) WalkWSSmem {
     T Dres[F::NRES > 0 ? F::NRES * F::SLOT : 8];
     float lamT[2][F::NLV * F::LDL];
     alignas(16) float wdec[2][F::CP];  // exp(chunk total - Aloc[j]): decay from token j to the chunk end
-    float Aloc[F::C];
+    alignas(16) float Aloc[F::C];
     float off[32];
     size_t blk[32];
     int plist[32];
@@ -1850,11 +1862,12 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                         for (int uk = 0; uk < F::NUK; ++uk)
                             mma_unit(s, pq_frag(sm.Ks, F::LDK, 16 * jt + li, uk * F::KB, qd), qf[x][uk]);
                         float p[4];
+                        const floatx4 aj = *reinterpret_cast<const floatx4 *>(sm.Aloc + 16 * jt + 4 * qd);
                         if (jt < it) {
                             const float lm = lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
-                                p[r] = s[r] * __expf(ai[x] - sm.Aloc[16 * jt + 4 * qd + r]) * lm;
+                                p[r] = s[r] * __expf(ai[x] - aj[r]) * lm;
                         } else {
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
@@ -1862,7 +1875,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                                 float m = 0.f;
                                 if (j <= i) {
                                     const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                                    m = __expf(ai[x] - sm.Aloc[j]) * lamT[lev * F::LDL + i];
+                                    m = __expf(ai[x] - aj[r]) * lamT[lev * F::LDL + i];
                                 }
                                 p[r] = s[r] * m;
                             }
