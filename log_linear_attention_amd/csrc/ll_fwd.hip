@@ -1698,6 +1698,10 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
             const bool more = ci + 1 < nchunk;
             const int kc = more ? __builtin_ctz((unsigned)(ci + 1)) : 0;
             __syncthreads();  // A
+            // Chunk kk+1 is loaded now (its registers were freed when chunk kk
+            // was staged) and staged after barrier B.
+            if (kk >= 1 && kk + 1 < K)
+                ws_load<F>(pf, bf, ws_token<F>(gr, G, kk + 1), L, ty);
             const float gch = sm.gch[b];
             float gapc[kMaxGroupLog2];
             Frag kf[F::NUC][2];
@@ -1729,8 +1733,7 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
                 ws_fold<F, F::NFY1, F::NFY>(sm, kf, b, kc, gapc, yw, lane, li, qd);
             if (kk + 1 < K) {
                 const int t1 = ws_token<F>(gr, G, kk + 1);
-                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty, kk + 2 < K, bf,
-                            kk + 2 < K ? ws_token<F>(gr, G, kk + 2) : 0);
+                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty, false, bf, 0);
             }
             if (more) {
 #pragma unroll
@@ -1847,14 +1850,18 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
             }
             // Causal score tiles (jt, it) of the group's query tiles, dealt
             // round-robin to its column-group waves; masked by decay and level
-            // weight and stored as P[i][j].
+            // weight and stored as P[i][j].  The diagonal tiles (dearer to
+            // mask) take positions 1 .. QPW of the deal and the others fill
+            // the rest, so no wave gets two diagonal tiles.
             {
-                int n = 0;
+                int noff = 0;
 #pragma unroll
                 for (int x = 0; x < F::QPW; ++x) {
                     const int it = F::qtile(qg, x);
                     const int i = iq[x];
-                    for (int jt = 0; jt <= it; ++jt, ++n) {
+                    for (int jt = 0; jt <= it; ++jt) {
+                        const int n = (jt == it) ? 1 + x : (noff == 0 ? 0 : noff + F::QPW);
+                        noff += (jt != it);
                         if (n % F::NCG != cg)
                             continue;
                         floatx4 s = zero4();
