@@ -9,8 +9,11 @@ Fenwick stacks of 17 slots).  Prints ONE JSON line on stdout.
 
   value        forward tokens/s (B*T / forward time), inputs resident in HBM
   roofline     of the dominant kernel (ll_chunk_walk): algorithmic HBM bytes
-               per launch / its mean launch time (HIP events on the launch
-               stream, inside the timed region) against 8 TB/s
+               per launch / its mean launch time against 8 TB/s.  The launch
+               times come from HIP events that the library records as part of
+               each kernel's dispatch on the launch stream (timing-only, no
+               system fence), over a second pass of the same K steps; the
+               first pass, with no events between launches, gives `value`
   decode       decode GB/s (algorithmic bytes / step time), tokens/s and its
                own roofline
   cpu_baseline the fp64 oracle on a bounded row sample of the same workload
@@ -171,7 +174,8 @@ def main():
         fwd(i)
     torch.cuda.synchronize()
 
-    ll.profile_begin(8 * args.steps + 8)
+    # Timed region: K forward steps with nothing between the library's own
+    # launches.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
@@ -181,9 +185,19 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     w1 = time.perf_counter()
-    kstats = ll.profile_end()
     fwd_ms = e0.elapsed_time(e1) / args.steps
-    log(f"forward: {fwd_ms:.4f} ms/step (wall {(w1 - w0) * 1e3 / args.steps:.4f}); kernels: {kstats}")
+    # Per-kernel durations: the same K steps again, with HIP events recorded
+    # around each launch on the launch stream by the library's profiler.
+    ll.profile_begin(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        fwd(i)
+    e1.record()
+    torch.cuda.synchronize()
+    kstats = ll.profile_end()
+    log(f"forward: {fwd_ms:.4f} ms/step (with per-kernel events {e0.elapsed_time(e1) / args.steps:.4f}; "
+        f"wall {(w1 - w0) * 1e3 / args.steps:.4f}); kernels: {kstats}")
 
     fbytes, fflops = fwd_algorithmic(cfg)
     walk_launches, walk_ms = kstats["ll_chunk_walk"]
@@ -215,15 +229,19 @@ def main():
     for i in range(args.warmup):
         dstep(i)
     torch.cuda.synchronize()
-    ll.profile_begin(4 * args.steps + 4)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
         dstep(i)
     e1.record()
     torch.cuda.synchronize()
-    dstats = ll.profile_end()
     dec_ms = e0.elapsed_time(e1) / args.steps
+    ll.profile_begin(4 * args.steps + 4)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        dstep(i)
+    torch.cuda.synchronize()
+    dstats = ll.profile_end()
     dbytes = decode_algorithmic(dcfg, pos0)
     dl, dms = dstats["ll_decode"]
     dec_kernel_ms = dms / dl

@@ -143,8 +143,10 @@ ll_status loglinear_decode_step(const void *q, const void *k, const void *v,
 const char *loglinear_last_error(void);
 
 /* ---- measurement support -------------------------------------------------
- * While profiling is on, every kernel the library launches is bracketed by a
- * pair of HIP events recorded on the launch stream (no synchronisation).
+ * While profiling is on, every kernel the library launches carries a pair of
+ * HIP events that its own dispatch records on the launch stream
+ * (hipExtLaunchKernelGGL; timing-only events without a system-scope fence,
+ * no synchronisation).
  * loglinear_profile_end synchronises those events and returns, per kernel
  * name, the number of launches and the summed device time.  Process-wide
  * state, not thread-safe; meant for benchmarks.  Creating the event pool in

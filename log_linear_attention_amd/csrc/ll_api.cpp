@@ -65,7 +65,6 @@ struct Profiler {
     bool overflow = false;
     std::vector<hipEvent_t> pool;
     std::vector<ProfRecord> recs;
-    const char *pending = nullptr;
 };
 
 Profiler g_prof;
@@ -74,28 +73,18 @@ Profiler g_prof;
 
 namespace ll {
 
-void prof_before(const char *name, hipStream_t s)
+ProfEvents prof_events(const char *name)
 {
     if (!g_prof.on)
-        return;
+        return {};
     if (g_prof.used + 2 > (int)g_prof.pool.size()) {
         g_prof.overflow = true;
-        g_prof.pending = nullptr;
-        return;
+        return {};
     }
     ProfRecord r{name, g_prof.pool[g_prof.used], g_prof.pool[g_prof.used + 1]};
     g_prof.used += 2;
-    (void)hipEventRecord(r.start, s);
     g_prof.recs.push_back(r);
-    g_prof.pending = name;
-}
-
-void prof_after(hipStream_t s)
-{
-    if (!g_prof.on || !g_prof.pending)
-        return;
-    (void)hipEventRecord(g_prof.recs.back().stop, s);
-    g_prof.pending = nullptr;
+    return {r.start, r.stop};
 }
 
 }  // namespace ll
@@ -258,7 +247,9 @@ ll_status loglinear_profile_begin(int max_launches)
     g_prof = Profiler();
     g_prof.pool.resize(2 * (size_t)max_launches);
     for (size_t i = 0; i < g_prof.pool.size(); ++i) {
-        hipError_t e = hipEventCreate(&g_prof.pool[i]);
+        // Timing-only events: no system-scope fence, so recording them adds no
+        // cache writeback or invalidation to the launches they time.
+        hipError_t e = hipEventCreateWithFlags(&g_prof.pool[i], hipEventDisableSystemFence);
         if (e != hipSuccess) {
             g_prof.pool.resize(i);
             return fail(LL_EDEVICE, "loglinear_profile_begin: hipEventCreate failed: %s", hipGetErrorString(e));

@@ -15,6 +15,8 @@
 // token).  The work is memory-bound: one workgroup per (sequence, head) streams
 // its occupied slots with 16-byte loads, accumulates q^T S per column group in
 // registers and reduces over dk in LDS.
+#include <hip/hip_ext.h>
+
 #include "ll_device.h"
 #include "ll_internal.h"
 
@@ -228,10 +230,10 @@ static hipError_t launch_dec_t(const DecodeArgs &A, hipStream_t s)
 {
     using D = Dec<DT, DK, DV>;
     using T = typename D::T;
-    prof_before("ll_decode", s);
-    hipLaunchKernelGGL(ll_decode<D>, dim3(A.S * A.H), dim3(D::NT), 0, s, (const T *)A.q, (const T *)A.k,
-                       (const T *)A.v, A.a, A.lam, A.state, A.logscale, A.pos, (T *)A.out, A.H, A.Lcap);
-    prof_after(s);
+    const ProfEvents pe = prof_events("ll_decode");
+    hipExtLaunchKernelGGL(ll_decode<D>, dim3(A.S * A.H), dim3(D::NT), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
+                          (const T *)A.k, (const T *)A.v, A.a, A.lam, A.state, A.logscale, A.pos, (T *)A.out, A.H,
+                          A.Lcap);
     return hipGetLastError();
 }
 

@@ -40,6 +40,8 @@
 // bf16 path straight from the row-major tiles with the CDNA4 LDS transpose
 // read (ds_read_b64_tr_b16); the fp32 path has no such instruction for 32-bit
 // elements and stores transposed copies instead.
+#include <hip/hip_ext.h>
+
 #include "ll_device.h"
 #include "ll_internal.h"
 
@@ -2052,10 +2054,9 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     T *Dg = reinterpret_cast<T *>(ws + P.off_Dg);
     const int log2C = bit_length(F::C) - 1;
     if (P.nL > 0) {
-        prof_before("ll_group_state", s);
-        hipLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, (const T *)A.k, (const T *)A.v,
-                           A.a, A.T, P.g, P.nG, P.nL, Sg, Gam);
-        prof_after(s);
+        ProfEvents pe = prof_events("ll_group_state");
+        hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
+                              (const T *)A.k, (const T *)A.v, A.a, A.T, P.g, P.nG, P.nL, Sg, Gam);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -2070,11 +2071,10 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         while (nleaves > 0) {
             const int ntiles = (nleaves + 63) / 64;
             const int complete = nleaves / 64;
-            prof_before("ll_left_tree", s);
-            hipLaunchKernelGGL(ll_left_tree<F>, dim3(4 * F::NUK, ntiles, BH), dim3(TreeGeom<F>::NTH), 0, s,
-                               leaves, gleaves, nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg,
-                               complete > 0 ? tot[ping] : nullptr, gtot[ping], ntiles);
-            prof_after(s);
+            pe = prof_events("ll_left_tree");
+            hipExtLaunchKernelGGL(ll_left_tree<F>, dim3(4 * F::NUK, ntiles, BH), dim3(TreeGeom<F>::NTH), 0, s,
+                                  pe.start, pe.stop, 0, leaves, gleaves, nleaves, lstride, gstride, p0, P.nL,
+                                  P.nLeft, Dg, complete > 0 ? tot[ping] : nullptr, gtot[ping], ntiles);
             e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -2090,30 +2090,29 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     }
     using W4 = Walk4<typename F::DTag, F::DK, F::DV, F::C>;
     using WS = WalkWS<typename F::DTag, F::DK, F::DV, F::C>;
-    prof_before("ll_chunk_walk", s);
+    const ProfEvents pw = prof_events("ll_chunk_walk");
     if constexpr (F::TR && WS::FITS) {
         // 32-bit buffer offsets within one head.
         const bool fits32 = (int64_t)A.T * (F::DK > F::DV ? F::DK : F::DV) * 2 < ((int64_t)1 << 31) &&
                             (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
         if (A.L <= WS::NLV && fits32) {
-            hipLaunchKernelGGL(ll_chunk_walk_ws<WS>, dim3(BH * ((P.nG + 1) / 2)), dim3(WS::NT), 0, s, (const T *)A.q,
-                               (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N,
-                               P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
-            prof_after(s);
+            hipExtLaunchKernelGGL(ll_chunk_walk_ws<WS>, dim3(BH * ((P.nG + 1) / 2)), dim3(WS::NT), 0, s, pw.start,
+                                  pw.stop, 0, (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out,
+                                  A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam,
+                                  (const T *)Dg);
             return hipGetLastError();
         }
     }
     if constexpr (F::TR && W4::FITS) {
-        hipLaunchKernelGGL(ll_chunk_walk<W4>, dim3(BH * P.nG), dim3(W4::NT), 0, s, (const T *)A.q, (const T *)A.k,
-                           (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL,
-                           P.nLeft, (const float *)Gam, (const T *)Dg);
+        hipExtLaunchKernelGGL(ll_chunk_walk<W4>, dim3(BH * P.nG), dim3(W4::NT), 0, s, pw.start, pw.stop, 0,
+                              (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L,
+                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
     } else {
         using FW = Fwd<typename F::DTag, F::DK, F::DV, F::C, true>;
-        hipLaunchKernelGGL(ll_chunk_walk_rs<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, (const T *)A.q,
-                           (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L, log2C, P.g, P.N, P.nG,
-                           P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
+        hipExtLaunchKernelGGL(ll_chunk_walk_rs<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, pw.start, pw.stop, 0,
+                              (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L,
+                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
     }
-    prof_after(s);
     return hipGetLastError();
 }
 

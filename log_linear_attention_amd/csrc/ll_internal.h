@@ -33,9 +33,14 @@ struct FwdArgs {
     void *workspace;
 };
 
-// Profiling hooks (implemented by the ABI layer).
-void prof_before(const char *name, hipStream_t s);
-void prof_after(hipStream_t s);
+// Profiling hook (implemented by the ABI layer): while profiling is on, a
+// pair of events that the next launch records as part of its own dispatch
+// (hipExtLaunchKernelGGL), so they time the kernel and nothing else; null
+// events otherwise.
+struct ProfEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents prof_events(const char *name);
 
 bool fwd_supported(bool bf16, int dk, int dv, int chunk);
 hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream);
