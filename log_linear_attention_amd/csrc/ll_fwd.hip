@@ -21,20 +21,21 @@
 //     (sum exp(decay) k v^T, fp32, dk x dv) and its total log-decay.  MFMA,
 //     with the next chunk's k/v prefetched into registers.
 //  B  ll_left_tree: the left-child block states of the binary tree over
-//     groups, 64 leaves per thread in registers (one launch per 64x of tree
+//     groups, 64 leaves in registers per thread (one launch per 64x of tree
 //     height), written in the exact register order the consuming MFMA reads.
-//  C  ll_chunk_walk: one workgroup per (head, group) walks its G chunks in
-//     order.  Per chunk it computes the intra-chunk part
-//     (Q K^T ⊙ decay ⊙ lambda-level mask) V on MFMA, adds the levels inside
-//     the group from a Fenwick stack of chunk states held in registers (the
-//     recurrent decode rule applied at chunk granularity), adds the levels
-//     above the group from B's block states, writes the output rows, and
-//     folds the chunk's own state K^T diag(w) V into the stack.  The next
-//     chunk's q/k/v/lambda/a are loaded into registers while the current one
-//     computes.
+//  C  ll_chunk_walk: walks the chunks of a group in order.  Per chunk it
+//     computes the intra-chunk part (Q K^T ⊙ decay ⊙ lambda-level mask) V on
+//     MFMA, adds the levels inside the group from a Fenwick stack of chunk
+//     states (the recurrent decode rule applied at chunk granularity), adds
+//     the levels above the group from B's block states, writes the output
+//     rows, and folds the chunk's own state K^T diag(w) V into the stack.
+//     The next chunk's q/k/v/lambda/a are loaded while the current one
+//     computes.  Three versions: fp32 with the stack in registers
+//     (ll_chunk_walk_rs); bf16 with specialised compute and helper waves
+//     (ll_chunk_walk_ws, each workgroup walking a group and its mirror);
+//     and a bf16 fallback for shapes or lengths the latter does not take.
 // Nothing but the inputs, the output and the small group/block states touches
-// HBM; the per-chunk states of the levels inside a group never leave
-// registers.
+// HBM; the per-chunk states of the levels inside a group stay on chip.
 //
 // Operands whose contraction runs over tokens (K^T and V^T) are read on the
 // bf16 path straight from the row-major tiles with the CDNA4 LDS transpose
