@@ -461,7 +461,10 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
 // half) * left + right).  Every complete left child is staged in LDS in
 // fragment order and then written with 16-byte stores, and the tile total
 // goes out for the next launch.  A block J at level p is complete when it
-// ends at or before the last complete group: (J + 1) * 2^p <= nL.
+// ends at or before the last complete group: (J + 1) * 2^p <= nL.  NAT
+// selects the dk order of a fragment lane: the natural one (lane quad qd
+// holds dk 32u + 8qd ..; the specialised bf16 walk) or unit_row's (the other
+// walks).
 // ---------------------------------------------------------------------------
 template <class F>
 struct TreeGeom {
@@ -472,7 +475,7 @@ struct TreeGeom {
     static_assert(CHUNK == 16, "one fragment lane is 16 bytes");
 };
 
-template <class F>
+template <class F, bool NAT>
 __global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
     const float *__restrict__ leaves, const float *__restrict__ gleaves, int nleaves, int lstride, int gstride,
     int p0, int nL, int nLeft, typename F::T *__restrict__ Dg, float *__restrict__ tot, float *__restrict__ gtot,
@@ -491,7 +494,7 @@ __global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
     int dd[TG::NE];
 #pragma unroll
     for (int h = 0; h < TG::NE; ++h)
-        dd[h] = F::KB * u + unit_row(r + 4 * h, qd);
+        dd[h] = F::KB * u + (NAT ? 8 * qd + r + 4 * h : unit_row(r + 4 * h, qd));
     if (tid < 64)
         gsh[tid] = (base + tid < nleaves) ? gleaves[(size_t)bh * gstride + base + tid] : 0.f;
     float x[TG::NE][64];
@@ -1114,6 +1117,25 @@ __device__ __forceinline__ void walk4_level(floatx4 (*O)[F::CPW], const typename
     }
 }
 
+// As walk4_level, with the wave's state fragments already in registers
+// (d[cc][u]: column tile cg * CPW + cc, dk unit u).
+template <class F>
+__device__ __forceinline__ void walk4_level_regs(floatx4 (*O)[F::CPW], const typename F::Frag (*qf)[F::NUK],
+                                                 const typename F::Frag (*d)[F::NUK], const float *f)
+{
+#pragma unroll
+    for (int cc = 0; cc < F::CPW; ++cc) {
+#pragma unroll
+        for (int x = 0; x < F::QPW; ++x) {
+            floatx4 tmp = zero4();
+#pragma unroll
+            for (int u = 0; u < F::NUK; ++u)
+                mma_unit(tmp, d[cc][u], qf[x][u]);
+            O[x][cc] += f[x] * tmp;
+        }
+    }
+}
+
 template <class F>
 __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
@@ -1353,19 +1375,29 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
 // Kernel C'' (bf16): the chunk walk with specialised waves.
 //
 // The same per-chunk algebra as ll_chunk_walk, split over two kinds of wave
-// so that the two halves of a chunk's work overlap on every SIMD instead of
+// so that the parts of a chunk's work overlap on every SIMD instead of
 // following each other:
 //  * NX compute waves own the output tiles (query-tile pairs x 16-column
 //    slices): masked score tiles -> P (shared through LDS), O^T = V^T P^T,
-//    the levels inside and above the group, the output rows;
-//  * NY helper waves fold each chunk's state into the Fenwick stack and move
-//    the next chunk's q, k, v, lambda, a from HBM through registers into LDS
-//    (and form its decay prefix).
-// Two workgroup barriers per chunk: A (chunk staged, stack slots ready) and
-// B (P complete).  What the helpers rewrite for chunk ci+1 while the compute
-// waves still read chunk ci after B (V, lambda^T, the token weights, the
-// chunk total) is double-buffered; Q, K and the decay prefix are read by the
-// compute waves only before B and are single-buffered.
+//    the levels inside and above the group, the output rows, and (when dk
+//    has at least two units per query group) part of the state fold;
+//  * NY helper waves fold each chunk's state into the Fenwick stack and
+//    stream the chunks from HBM straight into LDS with LDS-direct buffer
+//    loads (no register staging), and form each chunk's decay prefix.
+// Every per-chunk LDS tile is double-buffered by chunk parity.  Two
+// workgroup barriers per chunk: A (chunk staged, stack slots ready) and B (P
+// complete).  Q and K of chunk kk+2 are requested right after barrier B of
+// chunk kk (nobody reads chunk kk's Q/K after B); V, lambda and a of chunk
+// kk+1 right after barrier A of chunk kk (chunk kk-1's copies are read until
+// then).
+//
+// LDS layouts.  Q and K rows are unpadded with the 16-byte chunks of a row
+// XOR-swizzled (qk_swz), so the sixteen rows of an operand-fragment read hit
+// distinct banks; their dk order is the natural one (lane quad qd supplies
+// dk 32u + 8qd .. 32u + 8qd + 7, one 16-byte read).  The Fenwick stack and
+// the block states use the same dk order.  V keeps padded rows (read only by
+// transpose reads); P uses the paired-quad order; lambda is row-major
+// [token][level].
 // ---------------------------------------------------------------------------
 template <class DT, int DK_, int DV_, int C_>
 struct WalkWS {
@@ -1384,60 +1416,106 @@ struct WalkWS {
     static constexpr int NY = 4;                       // helper waves
     static constexpr int NW = NX + NY;
     static constexpr int NT = 64 * NW;
-    static constexpr int NTY = 64 * NY;
     static constexpr int CP = (C < KB) ? KB : C;
     static constexpr int NUC = CP / KB;
     static constexpr int NUK = DK / KB;
-    static constexpr int LDK = bf16_stride(DK, true);
-    static constexpr int LDV = tr_stride(DV);
+    static constexpr int CPR = DK / 8;                 // 16-byte chunks per Q/K row
+    static constexpr int G4 = CPR / 4;                 // groups of four chunks per row
+    static constexpr int RW = CPR >= 16 ? 1 : 16 / CPR;  // rows sharing one pass over the 64 banks
+    static constexpr int LDV = tr_stride(DV);          // V row stride (padded)
+    static constexpr int VCR = LDV / 8;                // 16-byte chunks per V row, padding included
     static constexpr int LDP = bf16_stride(CP, true);
-    static constexpr int LDL = C + 1;
     static constexpr int NLV = 22;                     // lambda levels staged (T <= 2^21)
-    static constexpr int VEC = 8;
     static constexpr int SLOT = DK * DV;               // elements of one state
-    // A helper wave folds the fragments of unit u = yw % NUK for the columns
-    // c = yw / NUK + (NY / NUK) * kk, so its K^T fragments are loaded once.
-    static constexpr int CSTEP = NY / NUK;
+    static constexpr int VEC = 8;                      // bf16 elements per 16 bytes
+    static constexpr int QKB = C * CPR / 64;           // 1-KB LDS-direct blocks of a Q (or K) tile
+    static constexpr int VBLK = (C * VCR + 63) / 64;   // blocks of a V tile
+    // The fold of a chunk's state is split by dk unit: when dk has at least
+    // two units per query group, compute wave (qg, cg) folds unit XU0 + qg of
+    // its own output columns (it has slack before barrier B) and the helpers
+    // fold units 0 .. YU-1.  A helper wave folds unit u = yw % YU for the
+    // columns c = yw / YU + (NY / YU) * kk, so its K^T fragments are loaded
+    // once.
+    static constexpr bool XF = (NUK >= 2 * NQG) && (NY % (NUK - NQG) == 0);
+    static constexpr int XU0 = XF ? NUK - NQG : NUK;
+    static constexpr int YU = XU0;
+    static constexpr int CSTEP = NY / YU;
     static constexpr int NFY = (NWC + CSTEP - 1) / CSTEP;
-    static constexpr int NFY1 = NFY;                   // folded before barrier B
-    static constexpr int KVEC = C * (DK / VEC);
-    static constexpr int NK = (KVEC + NTY - 1) / NTY;
-    static constexpr int VVEC = C * (DV / VEC);
-    static constexpr int NV = (VVEC + NTY - 1) / NTY;
-    static constexpr int NLAM = (C * NLV + NTY - 1) / NTY;
-    static constexpr int BASE_LDS = 2 * (C * LDK + CP * LDK + 2 * CP * LDV + C * LDP + kMaxGroupLog2 * SLOT) +
-                                    4 * (2 * NLV * LDL + C + 2 * CP) + 1024;
+    // Q/K blocks each helper wave requests after barrier B (equal for every
+    // wave when they divide evenly; then the wave can wait for everything
+    // older than them).
+    static constexpr int NQKW = (2 * QKB) % NY == 0 ? 2 * QKB / NY : -1;
+    static constexpr int BASE_LDS = 2 * (2 * C * DK + 2 * CP * DK + 2 * CP * LDV + C * LDP + kMaxGroupLog2 * SLOT) +
+                                    4 * (2 * C * NLV + 2 * 64 + 2 * CP + 2 * C) + 1024;
     static constexpr int NRES_FIT = (160 * 1024 - BASE_LDS) / (2 * SLOT);
     static constexpr int NRES = NRES_FIT < 0 ? 0 : (NRES_FIT > 8 ? 8 : NRES_FIT);
-    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NWC % CPW == 0 && NY % NUK == 0;
+    static constexpr bool FITS = BASE_LDS <= 160 * 1024 && NWC % CPW == 0 && NY % YU == 0 && C * CPR % 64 == 0;
+    static constexpr int NPF = 2;                      // block states above the group prefetched into registers
     __device__ static constexpr int qtile(int qg, int x) { return x == 0 ? qg : NMT - 1 - qg; }
 };
 
 template <class F>
 struct alignas(16) WalkWSSmem {
     using T = typename F::T;
-    T Qs[F::C * F::LDK];
-    T Ks[F::CP * F::LDK];
+    T Qs[2][F::C * F::DK];
+    T Ks[2][F::CP * F::DK];
     T Vs[2][F::CP * F::LDV];
     T Ps[F::C * F::LDP];
     T stk[kMaxGroupLog2 * F::SLOT];
     T Dres[F::NRES > 0 ? F::NRES * F::SLOT : 8];
-    float lamT[2][F::NLV * F::LDL];
-    alignas(16) float wdec[2][F::CP];  // exp(chunk total - Aloc[j]): decay from token j to the chunk end
-    alignas(16) float Aloc[F::C];
+    alignas(16) float lam[2][F::C * F::NLV];  // [token][level], row length L
+    alignas(16) float abuf[2][64];
+    alignas(16) float wdec[2][F::CP];         // exp(chunk total - Aloc[j]): decay from token j to the chunk end
+    alignas(16) float Aloc[2][F::C];
     float off[32];
     size_t blk[32];
     int plist[32];
-    int npop;
     float gch[2];
 };
 
+// XOR swizzle of the 16-byte chunks of Q/K row r: a bit rotation of the
+// row's index within CPR consecutive bank passes, so that (a) the sixteen
+// rows of a fragment read land on distinct chunks of the 64 banks and (b)
+// the rows of a transpose read fall in different 4-chunk groups.
 template <class F>
-struct WalkWSRegs {
-    uint4 q[F::NK], k[F::NK], v[F::NV];
-    float lam[F::NLAM];
-    float a;
-};
+__device__ __forceinline__ int qk_swz(int r)
+{
+    const int x = (r / F::RW) % F::CPR;
+    return ((x % F::G4) << 2) | (x / F::G4);
+}
+
+// Element offset of logical 16-byte chunk lc of Q/K row r.
+template <class F>
+__device__ __forceinline__ int qk_off(int r, int lc)
+{
+    return r * F::DK + ((lc ^ qk_swz<F>(r)) << 3);
+}
+
+// Operand fragment (unit u, lane quad qd) of Q/K row r: dk 32u + 8qd ..
+template <class F>
+__device__ __forceinline__ bf16x8 qk_frag(const __bf16 *tile, int r, int u, int qd)
+{
+    return *reinterpret_cast<const bf16x8 *>(tile + qk_off<F>(r, 4 * u + qd));
+}
+
+// Transpose-read fragment of K^T for the chunk state: token rows jb ..
+// jb+31 (k index, in the unit_row order of tr_frag), and for tile t of dk
+// unit u the 16 rows of the result are dk 32u + 8(m/4) + 4t + m%4 (m = 0..15),
+// so that the tile pair of an accumulator packs into a fragment in natural
+// dk order.
+template <class F>
+__device__ __forceinline__ bf16x8 kt_frag_nat(const __bf16 *tile, int jb, int u, int t, int li, int qd)
+{
+    const int r = jb + 4 * qd + (li >> 2);
+    const __bf16 *p0 = tile + qk_off<F>(r, 4 * u + (li & 3)) + 4 * t;
+    const __bf16 *p1 = tile + qk_off<F>(r + 16, 4 * u + (li & 3)) + 4 * t;
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p0);
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1);
+    bf16x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return v;
+}
 
 // Inclusive prefix sum over the 64 lanes of a fully active wave, with DPP
 // row shifts inside each 16-lane row and row broadcasts across rows (no LDS
@@ -1470,140 +1548,133 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Streaming (non-temporal) 16- and 4-byte loads through a descriptor.
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS-direct streaming load: lane l of the wave writes `size` bytes read at
+// byte offset `off` of the descriptor's range to LDS address dst + l * size
+// (dst is wave-uniform).  Completion is counted by vmcnt.
+template <int SIZE>
+__device__ __forceinline__ void ld_lds(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t off)
 {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
-    return make_uint4(x[0], x[1], x[2], x[3]);
+    static_assert(SIZE == 4 || SIZE == 16, "LDS-direct sizes used here");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, (int)off, 0, 0, 2);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, (int)off, 0, 0, 2);
 }
 
-__device__ __forceinline__ float buf_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in order).
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2));
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Helper thread ty (0 .. NTY-1) loads its share of the chunk starting at
-// token t0 of the head (rows past the head's end read as zero).
+// Helper wave yw's share of the Q and K rows of the chunk at token t0 into
+// buffer `slot` (swizzled; rows past the head's end arrive as zeros).
 template <class F>
-__device__ __forceinline__ void ws_load(WalkWSRegs<F> &r, const WSBuf &bf, int t0, int L, int ty)
+__device__ __forceinline__ void ws_ld_qk(WalkWSSmem<F> &sm, const WSBuf &bf, int slot, int t0, int yw, int lane)
 {
 #pragma unroll
-    for (int i = 0; i < F::NK; ++i) {
-        const int idx = ty + i * F::NTY;
-        r.q[i] = r.k[i] = zero16();
-        if (idx < F::KVEC) {
-            const uint32_t off = (uint32_t)t0 * (F::DK * 2) + (uint32_t)idx * 16;
-            r.q[i] = buf_ld16(bf.q, off);
-            r.k[i] = buf_ld16(bf.k, off);
+    for (int i = 0; i < (2 * F::QKB + F::NY - 1) / F::NY; ++i) {
+        const int blk = yw + i * F::NY;
+        if (blk < 2 * F::QKB) {
+            const bool isk = blk >= F::QKB;
+            const int bb = isk ? blk - F::QKB : blk;
+            const int pc = bb * 64 + lane;   // physical 16-byte chunk of the tile
+            const int r = pc / F::CPR;
+            const int lc = (pc % F::CPR) ^ qk_swz<F>(r);
+            const uint32_t off = ((uint32_t)(t0 + r) * F::DK + (uint32_t)lc * 8) * 2;
+            __bf16 *dst = (isk ? sm.Ks[slot] : sm.Qs[slot]) + bb * 512;
+            ld_lds<16>(isk ? bf.k : bf.q, dst, off);
         }
     }
-#pragma unroll
-    for (int i = 0; i < F::NV; ++i) {
-        const int idx = ty + i * F::NTY;
-        r.v[i] = zero16();
-        if (idx < F::VVEC)
-            r.v[i] = buf_ld16(bf.v, (uint32_t)t0 * (F::DV * 2) + (uint32_t)idx * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < F::NLAM; ++i) {
-        const int idx = ty + i * F::NTY;
-        r.lam[i] = (idx < F::C * L) ? buf_ld4(bf.lam, ((uint32_t)t0 * L + idx) * 4) : 0.f;
-    }
-    r.a = (ty < F::C) ? buf_ld4(bf.a, (uint32_t)(t0 + ty) * 4) : 0.f;
 }
 
-// Quad-lane exchange: the value of lane l ^ 2 of the same 4-lane quad.
-__device__ __forceinline__ unsigned int quad_swap2(unsigned int x)
-{
-    return (unsigned int)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
-}
-
-// Stage a loaded chunk into LDS buffer b (Q and K rows in paired-quad
-// order, V rows, lambda^T), and from helper wave 0 its decay prefix, token
-// weights and total.  With `next`, each register is reloaded with the chunk
-// at token t_next as soon as it has been stored, so the next chunk's loads
-// are issued while the stores drain.
+// Helper wave yw's share of the V rows (padded; the padding lanes load a
+// copy of the row's first chunk), the lambda rows and the decays a of the
+// chunk at token t0 into buffer `slot`.
 template <class F>
-__device__ __forceinline__ void ws_store(WalkWSRegs<F> &r, WalkWSSmem<F> &sm, int b, int valid, int L, float invL,
-                                         int ty, bool next, const WSBuf &bf, int t_next)
+__device__ __forceinline__ void ws_ld_vla(WalkWSSmem<F> &sm, const WSBuf &bf, int slot, int t0, int L, int yw,
+                                          int lane)
 {
-    constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
-    static_assert(KPR % 4 == 0, "a unit spans four 16-byte row vectors");
-    if (ty < 64) {
-        const float x = wave_prefix_sum(r.a);
-        const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), F::C - 1));
-        if (ty < F::C)
-            sm.Aloc[ty] = x;
-        if (ty < F::CP)
-            sm.wdec[b][ty] = (ty < F::C) ? __expf(g - x) : 0.f;
-        if (ty == 0)
-            sm.gch[b] = g;
+#pragma unroll
+    for (int i = 0; i < (F::VBLK + F::NY - 1) / F::NY; ++i) {
+        const int blk = yw + i * F::NY;
+        if (blk < F::VBLK) {
+            const int pc = blk * 64 + lane;
+            const int r = pc / F::VCR, cc = pc % F::VCR;
+            const uint32_t off = ((uint32_t)(t0 + r) * F::DV + (uint32_t)(cc < F::DV / 8 ? cc : 0) * 8) * 2;
+            if (pc < F::C * F::VCR)
+                ld_lds<16>(bf.v, sm.Vs[slot] + blk * 512, off);
+        }
     }
-    if (next)
-        r.a = (ty < F::C) ? buf_ld4(bf.a, (uint32_t)(t_next + ty) * 4) : 0.f;
-    // Row vector m (logical columns 8m .. 8m+7) and its quad partner m ^ 2
-    // hold the two halves of the paired-quad chunks q = 2(m%2) (written by
-    // the lane with m%4 < 2) and q = 2(m%2) + 1 (by its partner).
-    const bool lowpair = ((ty >> 1) & 1) == 0;
+    // lambda rows are contiguous (C * L floats): 16 bytes per lane.
+    const int nlv = (F::C * L + 3) / 4;   // 16-byte pieces
+    for (int blk = yw; blk * 64 < nlv; blk += F::NY) {
+        const int idx = blk * 64 + lane;
+        if (idx < nlv)
+            ld_lds<16>(bf.lam, sm.lam[slot] + blk * 256, ((uint32_t)t0 * L + 4 * idx) * 4);
+    }
+    if (yw == F::NY - 1 && lane < F::C)
+        ld_lds<4>(bf.a, sm.abuf[slot], (uint32_t)(t0 + lane) * 4);
+}
+
+// Decay prefix of the chunk in buffer `slot` (one helper wave, after its a
+// has arrived): Aloc, the token weights w_j = exp(total - Aloc[j]) and the
+// chunk total.
+template <class F>
+__device__ __forceinline__ void ws_scan(WalkWSSmem<F> &sm, int slot, int lane)
+{
+    const float x = wave_prefix_sum(lane < F::C ? sm.abuf[slot][lane] : 0.f);
+    const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), F::C - 1));
+    if (lane < F::C)
+        sm.Aloc[slot][lane] = x;
+    if (lane < F::CP)
+        sm.wdec[slot][lane] = (lane < F::C) ? __expf(g - x) : 0.f;
+    if (lane == 0)
+        sm.gch[slot] = g;
+}
+
+// Weighted K^T fragments of dk unit u for the chunk state K^T diag(w) V.
+template <class F>
+__device__ __forceinline__ void ws_kfrags(const WalkWSSmem<F> &sm, int b, int u, int li, int qd,
+                                          typename F::Frag (*kf)[2])
+{
+    using Frag = typename F::Frag;
 #pragma unroll
-    for (int i = 0; i < F::NK; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < F::KVEC) {
-            const int m = idx % KPR;
-            const int pos = (idx / KPR) * F::LDK + 32 * (m >> 2) + 16 * (m & 1) + (lowpair ? 0 : 8);
+    for (int uj = 0; uj < F::NUC; ++uj) {
+        const floatx4 w0 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 4 * qd]);
+        const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 16 + 4 * qd]);
 #pragma unroll
-            for (int w = 0; w < 2; ++w) {
-                const uint4 x = w ? r.k[i] : r.q[i];
-                const unsigned int px = quad_swap2(x.x), py = quad_swap2(x.y);
-                const unsigned int pz = quad_swap2(x.z), pw = quad_swap2(x.w);
-                const uint4 c = lowpair ? make_uint4(x.x, x.y, px, py) : make_uint4(pz, pw, x.z, x.w);
-                *reinterpret_cast<uint4 *>((w ? sm.Ks : sm.Qs) + pos) = c;
+        for (int t = 0; t < 2; ++t) {
+            Frag f = kt_frag_nat<F>(sm.Ks[b], uj * F::KB, u, t, li, qd);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = (__bf16)((float)f[e] * w0[e]);
+                f[e + 4] = (__bf16)((float)f[e + 4] * w1[e]);
             }
-            if (next) {
-                const uint32_t off = (uint32_t)t_next * (F::DK * 2) + (uint32_t)idx * 16;
-                r.q[i] = buf_ld16(bf.q, off);
-                r.k[i] = buf_ld16(bf.k, off);
-            }
+            kf[uj][t] = f;
         }
-    }
-#pragma unroll
-    for (int i = 0; i < F::NV; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < F::VVEC) {
-            *reinterpret_cast<uint4 *>(sm.Vs[b] + (idx / VPR) * F::LDV + (idx % VPR) * F::VEC) = r.v[i];
-            if (next)
-                r.v[i] = buf_ld16(bf.v, (uint32_t)t_next * (F::DV * 2) + (uint32_t)idx * 16);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < F::NLAM; ++i) {
-        const int idx = ty + i * F::NTY;
-        if (idx < valid * L) {
-            const int j = (int)(((float)idx + 0.5f) * invL);
-            sm.lamT[b][(idx - j * L) * F::LDL + j] = r.lam[i];
-        }
-        if (next)
-            r.lam[i] = (idx < F::C * L) ? buf_ld4(bf.lam, ((uint32_t)t_next * L + idx) * 4) : 0.f;
     }
 }
 
-// Helper wave yw: fold the fragments kk in [K0, K1) of chunk ci's new stack
-// slot kc (chunk state K^T diag(w) V plus the slots below it, decayed to the
-// chunk end).  kf holds the wave's weighted K^T fragments of unit u.  All
-// V^T fragment reads are issued before the products so their latencies
-// overlap.
-template <class F, int K0, int K1>
+// Fragments kk in [K0, K1) of chunk ci's new stack slot kc for dk unit u
+// (columns c0 + CS * kk): the chunk state plus the slots below it, decayed to
+// the chunk end (gapc[m] = their decay factors).  The V^T reads are issued
+// before the products.
+template <class F, int K0, int K1, int CS>
 __device__ __forceinline__ void ws_fold(WalkWSSmem<F> &sm, const typename F::Frag (*kf)[2], int b, int kc,
-                                        const float *gapc, int yw, int lane, int li, int qd)
+                                        const float *gapc, int u, int c0, int lane, int li, int qd)
 {
     using Frag = typename F::Frag;
     if constexpr (K1 > K0) {
-        const int u = yw % F::NUK;
-        const int c0 = yw / F::NUK;
         Frag vf[K1 - K0][F::NUC];
 #pragma unroll
         for (int kk = K0; kk < K1; ++kk) {
-            const int c = min(c0 + F::CSTEP * kk, F::NWC - 1);
+            const int c = min(c0 + CS * kk, F::NWC - 1);
 #pragma unroll
             for (int uj = 0; uj < F::NUC; ++uj)
                 vf[kk - K0][uj] = tr_frag(sm.Vs[b], F::LDV, uj * F::KB, 16 * c, li, qd);
@@ -1620,7 +1691,7 @@ __device__ __forceinline__ void ws_fold(WalkWSSmem<F> &sm, const typename F::Fra
         }
 #pragma unroll
         for (int kk = K0; kk < K1; ++kk) {
-            const int c = c0 + F::CSTEP * kk;
+            const int c = c0 + CS * kk;
             if (c < F::NWC) {
 #pragma unroll
                 for (int m = 0; m < kMaxGroupLog2; ++m)
@@ -1660,33 +1731,36 @@ __device__ __forceinline__ int ws_token(const WSGroups &gr, int G, int kk)
 template <class F>
 __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T *q, const typename F::T *k,
                                           const typename F::T *v, const float *a, const float *lam, int Tlen, int L,
-                                          float invL, int bh, const WSGroups &gr, int G, int ty)
+                                          int bh, const WSGroups &gr, int G, int ty)
 {
     using Frag = typename F::Frag;
     const int lane = ty & 63, yw = ty >> 6, qd = lane >> 4, li = lane & 15;
-    const int u = yw % F::NUK;
+    const int u = yw % F::YU, c0 = yw / F::YU;
     const size_t hrow = (size_t)bh * Tlen;
     const WSBuf bf = {head_rsrc(q + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
                       head_rsrc(k + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
                       head_rsrc(v + hrow * F::DV, (uint32_t)Tlen * F::DV * 2),
                       head_rsrc(lam + hrow * L, (uint32_t)Tlen * L * 4), head_rsrc(a + hrow, (uint32_t)Tlen * 4)};
-    // The chunks of both groups form one stream kk = 0 .. K-1: chunk kk+1
-    // is staged (LDS buffer (kk+1)&1) and chunk kk+2 loaded while chunk kk
-    // is walked.
+    // The chunks of both groups form one stream kk = 0 .. K-1, chunk kk in
+    // LDS buffer kk & 1.
     const int K = gr.n0 + gr.n1;
-    WalkWSRegs<F> pf;
-    ws_load<F>(pf, bf, ws_token<F>(gr, G, 0), L, ty);
-    // Padding rows of K and V, P (its upper tiles and padding columns are
-    // never written) and lambda^T (levels >= L) start at zero.
-    ws_zero<F>(sm.Ks, F::CP * F::LDK, ty, F::NTY);
-    ws_zero<F>(&sm.Vs[0][0], 2 * F::CP * F::LDV, ty, F::NTY);
-    ws_zero<F>(sm.Ps, F::C * F::LDP, ty, F::NTY);
-    ws_zero<F>(&sm.lamT[0][0], 2 * F::NLV * F::LDL, ty, F::NTY);
-    __syncthreads();  // prologue
-    {
-        const int t0 = ws_token<F>(gr, G, 0);
-        ws_store<F>(pf, sm, 0, min(F::C, Tlen - t0), L, invL, ty, K > 1, bf, K > 1 ? ws_token<F>(gr, G, 1) : 0);
+    // Rows past the chunk (K and V when C < 32) and P (its upper tiles and
+    // padding columns) are never loaded and stay zero.
+    if constexpr (F::CP > F::C) {
+        ws_zero<F>(&sm.Ks[0][F::C * F::DK], (F::CP - F::C) * F::DK, ty, 64 * F::NY);
+        ws_zero<F>(&sm.Ks[1][F::C * F::DK], (F::CP - F::C) * F::DK, ty, 64 * F::NY);
+        ws_zero<F>(&sm.Vs[0][F::C * F::LDV], (F::CP - F::C) * F::LDV, ty, 64 * F::NY);
+        ws_zero<F>(&sm.Vs[1][F::C * F::LDV], (F::CP - F::C) * F::LDV, ty, 64 * F::NY);
     }
+    ws_zero<F>(sm.Ps, F::C * F::LDP, ty, 64 * F::NY);
+    ws_ld_qk<F>(sm, bf, 0, ws_token<F>(gr, G, 0), yw, lane);
+    ws_ld_vla<F>(sm, bf, 0, ws_token<F>(gr, G, 0), L, yw, lane);
+    wait_vm<0>();
+    if (yw == F::NY - 1)
+        ws_scan<F>(sm, 0, lane);
+    if (K > 1)
+        ws_ld_qk<F>(sm, bf, 1, ws_token<F>(gr, G, 1), yw, lane);
+    __syncthreads();  // prologue
     int kk = 0;
     for (int gi = 0; gi < gr.n; ++gi) {
         if (gi > 0)
@@ -1701,43 +1775,39 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
             const bool more = ci + 1 < nchunk;
             const int kc = more ? __builtin_ctz((unsigned)(ci + 1)) : 0;
             __syncthreads();  // A
-            // Chunk kk+1 is loaded now (its registers were freed when chunk kk
-            // was staged) and staged after barrier B.
-            if (kk >= 1 && kk + 1 < K)
-                ws_load<F>(pf, bf, ws_token<F>(gr, G, kk + 1), L, ty);
             const float gch = sm.gch[b];
-            float gapc[kMaxGroupLog2];
-            Frag kf[F::NUC][2];
+            if (kk + 1 < K)
+                ws_ld_vla<F>(sm, bf, b ^ 1, ws_token<F>(gr, G, kk + 1), L, yw, lane);
             if (more) {
+                float gapc[kMaxGroupLog2];
 #pragma unroll
                 for (int m = 0; m < kMaxGroupLog2; ++m)
                     gapc[m] = __expf(gap[m] + gch);
-#pragma unroll
-                for (int uj = 0; uj < F::NUC; ++uj) {
-                    const floatx4 w0 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 4 * qd]);
-                    const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sm.wdec[b][uj * F::KB + 16 + 4 * qd]);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        Frag f = pq_tr_frag(sm.Ks, F::LDK, uj * F::KB, u, t, li, qd);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            f[e] = (__bf16)((float)f[e] * w0[e]);
-                            f[e + 4] = (__bf16)((float)f[e + 4] * w1[e]);
-                        }
-                        kf[uj][t] = f;
-                    }
+                Frag kf[F::NUC][2];
+                ws_kfrags<F>(sm, b, u, li, qd, kf);
+                if constexpr (F::NFY <= 2) {
+                    ws_fold<F, 0, F::NFY, F::CSTEP>(sm, kf, b, kc, gapc, u, c0, lane, li, qd);
+                } else {
+                    ws_fold<F, 0, (F::NFY + 1) / 2, F::CSTEP>(sm, kf, b, kc, gapc, u, c0, lane, li, qd);
+                    __builtin_amdgcn_sched_barrier(0);
+                    ws_fold<F, (F::NFY + 1) / 2, F::NFY, F::CSTEP>(sm, kf, b, kc, gapc, u, c0, lane, li, qd);
                 }
-                ws_fold<F, 0, (F::NFY1 + 1) / 2>(sm, kf, b, kc, gapc, yw, lane, li, qd);
-                __builtin_amdgcn_sched_barrier(0);
-                ws_fold<F, (F::NFY1 + 1) / 2, F::NFY1>(sm, kf, b, kc, gapc, yw, lane, li, qd);
             }
             __syncthreads();  // B
-            if (more)
-                ws_fold<F, F::NFY1, F::NFY>(sm, kf, b, kc, gapc, yw, lane, li, qd);
-            if (kk + 1 < K) {
-                const int t1 = ws_token<F>(gr, G, kk + 1);
-                ws_store<F>(pf, sm, b ^ 1, min(F::C, Tlen - t1), L, invL, ty, false, bf, 0);
+            if (kk + 2 < K)
+                ws_ld_qk<F>(sm, bf, b, ws_token<F>(gr, G, kk + 2), yw, lane);
+            // Everything but the Q/K requests just made (in flight over the
+            // next chunk) must have landed before barrier A.
+            if constexpr (F::NQKW >= 0) {
+                if (kk + 2 < K)
+                    wait_vm<F::NQKW>();
+                else
+                    wait_vm<0>();
+            } else {
+                wait_vm<0>();
             }
+            if (kk + 1 < K && yw == F::NY - 1)
+                ws_scan<F>(sm, b ^ 1, lane);
             if (more) {
 #pragma unroll
                 for (int m = 0; m < kMaxGroupLog2; ++m)
@@ -1748,8 +1818,8 @@ __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T
 }
 
 template <class F>
-__device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out, int Tlen, int log2C, int g,
-                                           int bh, const WSGroups &gr, int nG, int Plev, int nL, int nLeft,
+__device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out, int Tlen, int L, int log2C,
+                                           int g, int bh, const WSGroups &gr, int nG, int Plev, int nL, int nLeft,
                                            const float *Gam, const typename F::T *Dg, int tid)
 {
     using T = typename F::T;
@@ -1839,17 +1909,18 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
             const size_t row0 = rowg + (size_t)ci * F::C;
             __syncthreads();  // A
             const float gch = sm.gch[b];
-            const float *lamT = sm.lamT[b];
+            const float *lamr = sm.lam[b];   // lambda of token i, level l at i * L + l
+            const float *Aloc = sm.Aloc[b];
             int iq[F::QPW];
             float ai[F::QPW];
             Frag qf[F::QPW][F::NUK];
 #pragma unroll
             for (int x = 0; x < F::QPW; ++x) {
                 iq[x] = 16 * F::qtile(qg, x) + li;
-                ai[x] = sm.Aloc[iq[x]];
+                ai[x] = Aloc[iq[x]];
 #pragma unroll
                 for (int uk = 0; uk < F::NUK; ++uk)
-                    qf[x][uk] = pq_frag(sm.Qs, F::LDK, iq[x], uk * F::KB, qd);
+                    qf[x][uk] = qk_frag<F>(sm.Qs[b], iq[x], uk, qd);
             }
             // Causal score tiles (jt, it) of the group's query tiles, dealt
             // round-robin to its column-group waves; masked by decay and level
@@ -1870,11 +1941,11 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                         floatx4 s = zero4();
 #pragma unroll
                         for (int uk = 0; uk < F::NUK; ++uk)
-                            mma_unit(s, pq_frag(sm.Ks, F::LDK, 16 * jt + li, uk * F::KB, qd), qf[x][uk]);
+                            mma_unit(s, qk_frag<F>(sm.Ks[b], 16 * jt + li, uk, qd), qf[x][uk]);
                         float p[4];
-                        const floatx4 aj = *reinterpret_cast<const floatx4 *>(sm.Aloc + 16 * jt + 4 * qd);
+                        const floatx4 aj = *reinterpret_cast<const floatx4 *>(Aloc + 16 * jt + 4 * qd);
                         if (jt < it) {
-                            const float lm = lamT[(4 + bitlen_u32((uint32_t)(it ^ jt))) * F::LDL + i];
+                            const float lm = lamr[i * L + 4 + bitlen_u32((uint32_t)(it ^ jt))];
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 p[r] = s[r] * __expf(ai[x] - aj[r]) * lm;
@@ -1885,7 +1956,7 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                                 float m = 0.f;
                                 if (j <= i) {
                                     const int lev = (i == j) ? 0 : bitlen_u32((uint32_t)(i ^ j));
-                                    m = __expf(ai[x] - aj[r]) * lamT[lev * F::LDL + i];
+                                    m = __expf(ai[x] - aj[r]) * lamr[i * L + lev];
                                 }
                                 p[r] = s[r] * m;
                             }
@@ -1898,6 +1969,34 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                     }
                 }
             }
+            // This wave's share of the fold (dk unit XU0 + qg of its own
+            // output columns) while the helpers finish theirs.
+            if constexpr (F::XF) {
+                if (ci + 1 < nchunk) {
+                    const int kc = __builtin_ctz((unsigned)(ci + 1));
+                    float gapc[kMaxGroupLog2];
+#pragma unroll
+                    for (int m = 0; m < kMaxGroupLog2; ++m)
+                        gapc[m] = __expf(gap[m] + gch);
+                    Frag kf[F::NUC][2];
+                    ws_kfrags<F>(sm, b, F::XU0 + qg, li, qd, kf);
+                    ws_fold<F, 0, F::CPW, 1>(sm, kf, b, kc, gapc, F::XU0 + qg, cg * F::CPW, lane, li, qd);
+                }
+            }
+            // The first NPF block states above the group that are not
+            // LDS-resident are requested now, so their L2 latency is spent
+            // across barrier B and the products before their level.
+            Frag dpf[F::NPF][F::CPW][F::NUK];
+#pragma unroll
+            for (int j = 0; j < F::NPF; ++j)
+                if (F::NRES + j < npop) {
+                    const T *st = Dg + sm.blk[F::NRES + j];
+#pragma unroll
+                    for (int cc = 0; cc < F::CPW; ++cc)
+#pragma unroll
+                        for (int uk = 0; uk < F::NUK; ++uk)
+                            dpf[j][cc][uk] = state_frag<F>(st, cg * F::CPW + cc, uk, lane);
+                }
             __syncthreads();  // B
 
             // O^T = V^T P^T for this wave's query and column tiles.
@@ -1924,19 +2023,32 @@ __device__ __forceinline__ void ws_compute(WalkWSSmem<F> &sm, typename F::T *out
                     float f[F::QPW];
 #pragma unroll
                     for (int x = 0; x < F::QPW; ++x)
-                        f[x] = lamT[(log2C + m + 1) * F::LDL + iq[x]] * __expf(ai[x] + gap[m]);
+                        f[x] = lamr[iq[x] * L + log2C + m + 1] * __expf(ai[x] + gap[m]);
                     walk4_level<F>(O, qf, sm.stk + m * F::SLOT, cg, f, lane);
                 }
-            // Levels above the group.
+            // Levels above the group: LDS-resident states, then the
+            // prefetched ones, then any others straight from L2.
             for (int ii = 0; ii < npop; ++ii) {
+                if (ii >= F::NRES && ii < F::NRES + F::NPF)
+                    continue;
                 const int p = sm.plist[ii];
                 float f[F::QPW];
 #pragma unroll
                 for (int x = 0; x < F::QPW; ++x)
-                    f[x] = lamT[(log2C + g + 1 + p) * F::LDL + iq[x]] * __expf(ai[x] + agrun + sm.off[p]);
+                    f[x] = lamr[iq[x] * L + log2C + g + 1 + p] * __expf(ai[x] + agrun + sm.off[p]);
                 const T *st = (ii < F::NRES) ? sm.Dres + (size_t)ii * F::SLOT : Dg + sm.blk[ii];
                 walk4_level<F>(O, qf, st, cg, f, lane);
             }
+#pragma unroll
+            for (int j = 0; j < F::NPF; ++j)
+                if (F::NRES + j < npop) {
+                    const int p = sm.plist[F::NRES + j];
+                    float f[F::QPW];
+#pragma unroll
+                    for (int x = 0; x < F::QPW; ++x)
+                        f[x] = lamr[iq[x] * L + log2C + g + 1 + p] * __expf(ai[x] + agrun + sm.off[p]);
+                    walk4_level_regs<F>(O, qf, dpf[j], f);
+                }
             // Output: lane holds O[i][16c + 4qd .. 16c + 4qd + 3] for i = iq[x].
 #pragma unroll
             for (int x = 0; x < F::QPW; ++x) {
@@ -1990,9 +2102,9 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk_ws(
     gr.n0 = min(G, N - pr * G);
     gr.n1 = (gr.n == 2) ? min(G, N - gr.sg1 * G) : 0;
     if (wave >= F::NX)
-        ws_helper<F>(sm, q, k, v, a, lam, Tlen, L, 1.f / (float)L, bh, gr, G, tid - 64 * F::NX);
+        ws_helper<F>(sm, q, k, v, a, lam, Tlen, L, bh, gr, G, tid - 64 * F::NX);
     else
-        ws_compute<F>(sm, out, Tlen, log2C, g, bh, gr, nG, Plev, nL, nLeft, Gam, Dg, tid);
+        ws_compute<F>(sm, out, Tlen, L, log2C, g, bh, gr, nG, Plev, nL, nLeft, Gam, Dg, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -2054,6 +2166,15 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     float *Gam = reinterpret_cast<float *>(ws + P.off_Gam);
     T *Dg = reinterpret_cast<T *>(ws + P.off_Dg);
     const int log2C = bit_length(F::C) - 1;
+    using W4 = Walk4<typename F::DTag, F::DK, F::DV, F::C>;
+    using WS = WalkWS<typename F::DTag, F::DK, F::DV, F::C>;
+    bool use_ws = false;
+    if constexpr (F::TR && WS::FITS) {
+        // 32-bit buffer offsets within one head.
+        const bool fits32 = (int64_t)A.T * (F::DK > F::DV ? F::DK : F::DV) * 2 < ((int64_t)1 << 31) &&
+                            (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
+        use_ws = A.L <= WS::NLV && fits32;
+    }
     if (P.nL > 0) {
         ProfEvents pe = prof_events("ll_group_state");
         hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
@@ -2073,9 +2194,18 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             const int ntiles = (nleaves + 63) / 64;
             const int complete = nleaves / 64;
             pe = prof_events("ll_left_tree");
-            hipExtLaunchKernelGGL(ll_left_tree<F>, dim3(4 * F::NUK, ntiles, BH), dim3(TreeGeom<F>::NTH), 0, s,
-                                  pe.start, pe.stop, 0, leaves, gleaves, nleaves, lstride, gstride, p0, P.nL,
-                                  P.nLeft, Dg, complete > 0 ? tot[ping] : nullptr, gtot[ping], ntiles);
+            const dim3 tg(4 * F::NUK, ntiles, BH), tb(TreeGeom<F>::NTH);
+            float *tt = complete > 0 ? tot[ping] : nullptr;
+            bool nat = false;
+            if constexpr (F::TR) {
+                nat = use_ws;
+                if (nat)
+                    hipExtLaunchKernelGGL(ll_left_tree<F, true>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
+                                          nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg, tt, gtot[ping], ntiles);
+            }
+            if (!nat)
+                hipExtLaunchKernelGGL(ll_left_tree<F, false>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
+                                      nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg, tt, gtot[ping], ntiles);
             e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
@@ -2089,14 +2219,9 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             ping ^= 1;
         }
     }
-    using W4 = Walk4<typename F::DTag, F::DK, F::DV, F::C>;
-    using WS = WalkWS<typename F::DTag, F::DK, F::DV, F::C>;
     const ProfEvents pw = prof_events("ll_chunk_walk");
     if constexpr (F::TR && WS::FITS) {
-        // 32-bit buffer offsets within one head.
-        const bool fits32 = (int64_t)A.T * (F::DK > F::DV ? F::DK : F::DV) * 2 < ((int64_t)1 << 31) &&
-                            (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
-        if (A.L <= WS::NLV && fits32) {
+        if (use_ws) {
             hipExtLaunchKernelGGL(ll_chunk_walk_ws<WS>, dim3(BH * ((P.nG + 1) / 2)), dim3(WS::NT), 0, s, pw.start,
                                   pw.stop, 0, (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out,
                                   A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam,
