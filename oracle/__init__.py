@@ -25,6 +25,10 @@ carries [LLA-pt §2 "Forma Recorrente e Paralela", decoding bullet; LLA-fr §2
 "Algorithmes Efficaces", inference bullet].  Written from that description
 in numpy fp64, one (sequence, head) at a time.
 
+Prefill (``prefill_stack``): the stack that a whole prompt leaves for the
+decode of the next token, summed bucket by bucket from the same definition
+the forward uses.
+
 Stack convention for decode: slot l holds the state of level-l bucket of the
 most recent query position.  Occupancy follows the position's bits: for
 position p, slot 0 is always occupied and slot l >= 1 is occupied iff bit
@@ -221,6 +225,44 @@ def decode_sequence(q, k, v, a, lam, Lcap: int | None = None) -> np.ndarray:
         out[:, :, t] = o
         state = new
     return out.reshape(B, H, T, dv)
+
+
+def prefill_stack(k, v, a, Lcap: int):
+    """The decode stack a prompt of T tokens leaves for the next token, fp64.
+
+    The prompt's last token sits at position p = T - 1.  Slot l holds the true
+    state of that position's level-l bucket, straight from the definition of
+    the buckets: every key s <= p lands in slot level(p, s) with the weight
+    exp(sum_{r=s+1..p} a_r) it carries in the forward [LLA-fr §2 "Matrice de
+    Masque Hiérarchique"; LLA-pt §2 "Particionamento Hierárquico"], so
+    sum_l lambda_p[l] q_p^T S_l is row p of the forward.
+
+    k [B,H,T,dk], v [B,H,T,dv], a [B,H,T].  Returns (true_state
+    [B,H,Lcap,dk,dv] with unoccupied slots zero, occ [Lcap] bool).
+    """
+    k, v, a = (_f64(x) for x in (k, v, a))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    state = np.zeros((B, H, Lcap, dk, dv))
+    occ = np.zeros(Lcap, dtype=bool)
+    if T == 0:
+        return state, occ
+    p = T - 1
+    # log-weight of key s: sum of a over (s, p]
+    logw = np.zeros((B, H, T))
+    for s in range(p - 1, -1, -1):
+        logw[:, :, s] = logw[:, :, s + 1] + a[:, :, s + 1]
+    lev = np.array([level(p, s) for s in range(T)])
+    if lev.max() >= Lcap:
+        raise ValueError(f"position {p} needs {lev.max() + 1} slots, Lcap is {Lcap}")
+    for l in range(Lcap):
+        sel = np.nonzero(lev == l)[0]
+        if sel.size == 0:
+            continue
+        occ[l] = True
+        kw = k[:, :, sel, :] * np.exp(logw[:, :, sel])[..., None]
+        state[:, :, l] = np.swapaxes(kw, -1, -2) @ v[:, :, sel, :]
+    return state, occ
 
 
 def rel_l2(x, ref) -> float:

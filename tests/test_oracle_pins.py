@@ -278,3 +278,90 @@ def test_decode_out_of_range_position(oracle_mod):
     assert np.all(np.isnan(o[0])) and np.all(np.isfinite(o[1]))
     for l in oracle_mod.occupied(7, Lcap):
         np.testing.assert_array_equal(new[0, 0, l], state[0, 0, l])
+
+
+# --- prefill: the stack a prompt leaves for the next token -----------------------
+
+def test_prefill_stack_hand_example(oracle_mod):
+    """The hand-worked stack after the fourth token of the T=4 example."""
+    g = json.load(open(os.path.join(HERE, "golden", "hand_T4.json")))
+    T, Lcap = 4, 3
+    k = np.array(g["k"]).reshape(1, 1, T, 1)
+    v = np.array(g["v"]).reshape(1, 1, T, 2)
+    a = np.array(g["a"]).reshape(1, 1, T)
+    st, occ = oracle_mod.prefill_stack(k, v, a, Lcap)
+    assert occ.tolist() == [True, True, True]
+    for slot, want in g["expected_stack_after_t3"].items():
+        np.testing.assert_allclose(st[0, 0, int(slot)], np.array(want), rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 9, 37, 64, 65])
+def test_prefill_stack_equals_decode_recurrence(oracle_mod, T):
+    """The stack summed bucket by bucket equals the one the recurrent form
+    builds by merging and promoting token by token."""
+    rng = np.random.default_rng(30 + T)
+    H, dk, dv, Lcap = 2, 3, 2, 8
+    q, k, v, a, lam = _rand_inputs(rng, 1, H, T, dk, dv, Lcap)
+    state = np.zeros((1, H, Lcap, dk, dv))
+    logscale = np.zeros((1, H, Lcap))
+    for t in range(T):
+        _, state, occ = oracle_mod.decode_step(state, logscale, np.array([t]), q[:, :, t], k[:, :, t], v[:, :, t],
+                                               a[:, :, t], lam[:, :, t])
+    st, occ2 = oracle_mod.prefill_stack(k, v, a, Lcap)
+    assert occ2.tolist() == occ[0].tolist()
+    np.testing.assert_allclose(st, state, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_occupancy_follows_position_bits(oracle_mod):
+    rng = np.random.default_rng(31)
+    for T in list(range(1, 70)) + [127, 128, 129, 255, 256, 300]:
+        k = rng.standard_normal((1, 1, T, 1))
+        v = rng.standard_normal((1, 1, T, 1))
+        a = np.zeros((1, 1, T))
+        _, occ = oracle_mod.prefill_stack(k, v, a, 10)
+        assert np.nonzero(occ)[0].tolist() == oracle_mod.occupied(T - 1, 10), T
+
+
+def test_prefill_readout_is_last_forward_row(oracle_mod):
+    """Reading the stack with the last token's query and weights gives the
+    forward's last row: sum_l lambda_p[l] q_p^T S_l = o_p."""
+    rng = np.random.default_rng(32)
+    T, dk, dv = 45, 4, 3
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, 2, 2, T, dk, dv, L)
+    st, occ = oracle_mod.prefill_stack(k, v, a, L)
+    o = oracle_mod.fwd(q, k, v, a, lam)[:, :, T - 1]
+    read = np.einsum("bhl,bhd,bhlde->bhe", lam[:, :, T - 1] * occ, q[:, :, T - 1], st)
+    np.testing.assert_allclose(read, o, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_without_decay_sums_to_kv(oracle_mod):
+    """With a == 0 the buckets partition the prefix: the slots add up to K^T V."""
+    rng = np.random.default_rng(33)
+    T, dk, dv = 29, 5, 3
+    k = rng.standard_normal((1, 1, T, dk))
+    v = rng.standard_normal((1, 1, T, dv))
+    st, _ = oracle_mod.prefill_stack(k, v, np.zeros((1, 1, T)), 6)
+    np.testing.assert_allclose(st.sum(axis=2)[0, 0], k[0, 0].T @ v[0, 0], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 6, 16, 31, 40])
+def test_prefill_then_decode_continues_the_forward(oracle_mod, T):
+    """Decoding token T from the stack of tokens 0..T-1 gives row T of the
+    forward over tokens 0..T."""
+    rng = np.random.default_rng(34 + T)
+    H, dk, dv, Lcap = 2, 4, 3, 8
+    q, k, v, a, lam = _rand_inputs(rng, 1, H, T + 1, dk, dv, _L(T + 1))
+    st, _ = oracle_mod.prefill_stack(k[:, :, :T], v[:, :, :T], a[:, :, :T], Lcap)
+    lam_pad = np.zeros((1, H, Lcap))
+    lam_pad[..., :lam.shape[-1]] = lam[:, :, T]
+    o, _, _ = oracle_mod.decode_step(st, np.zeros((1, H, Lcap)), np.array([T]), q[:, :, T], k[:, :, T],
+                                     v[:, :, T], a[:, :, T], lam_pad)
+    want = oracle_mod.fwd(q, k, v, a, lam)[:, :, T]
+    np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_stack_too_few_slots_is_an_error(oracle_mod):
+    k = np.zeros((1, 1, 9, 1)); v = np.zeros((1, 1, 9, 1)); a = np.zeros((1, 1, 9))
+    with pytest.raises(ValueError):
+        oracle_mod.prefill_stack(k, v, a, 4)  # position 8 needs slot 4
