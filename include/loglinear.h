@@ -138,6 +138,39 @@ ll_status loglinear_decode_step(const void *q, const void *k, const void *v,
                                 void *out, int S, int H, int dk, int dv, int Lcap,
                                 ll_dtype dtype, void *stream);
 
+/* Prefill: the forward of loglinear_fwd_ex over a prompt of T tokens, which
+ * also writes the decode stack the prompt leaves for its next token, so that
+ * decoding can continue at position T (the recurrent form takes over from
+ * the parallel one: Portuguese page §2 "Forma Recorrente e Paralela";
+ * buckets: same page §2 "Particionamento Hierárquico").
+ *  q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace,
+ *  workspace_bytes, stream, group_log2: as for loglinear_fwd_ex (the same
+ *         workspace size, loglinear_fwd_workspace_bytes_ex).
+ *  state    [B,H,Lcap,dk,dv] float32, written: the stack of position T-1 in
+ *           loglinear_decode_step's convention (slot 0 = token T-1's k v^T;
+ *           slot l >= 1 = its level-l bucket iff bit l-1 of T-1 is set).
+ *           Free slots are not written.
+ *  logscale [B,H,Lcap] float32, written for the occupied slots (each slot is
+ *           stored decayed to its own last key; g is the decay from there to
+ *           position T-1).
+ *  Lcap     slots per (sequence, head): 2 <= Lcap <= 32 and
+ *           Lcap >= loglinear_num_levels(T) (else LL_EINVAL).
+ * Sequence b of the forward is decode sequence b: call
+ * loglinear_decode_step next with pos[b] = T.  T == 0 leaves an empty stack
+ * (pos = 0) and writes nothing.  state and logscale must not alias the
+ * inputs, out or the workspace.  Supported: the shapes loglinear_fwd supports
+ * with dk, dv in {16, 32, 64, 128}.
+ * In bf16, the stack's coarse slots (buckets of at least one chunk group)
+ * carry the rounding of the forward's bf16 products; finer slots are summed
+ * in float32.
+ * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
+ll_status loglinear_prefill(const void *q, const void *k, const void *v,
+                            const float *a, const float *lambda, void *out,
+                            float *state, float *logscale,
+                            int B, int H, int T, int dk, int dv, int chunk, int Lcap,
+                            ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                            void *stream, int group_log2);
+
 /* Message for the last failing call on this thread ("" if none).  Valid
  * until the next call into the library on the same thread. */
 const char *loglinear_last_error(void);

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.loglinear_fwd.restype = I
         L.loglinear_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_fwd_ex.restype = I
+        L.loglinear_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P, I]
+        L.loglinear_prefill.restype = I
         L.loglinear_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
         L.loglinear_decode_step.restype = I
         L.loglinear_last_error.argtypes = []
@@ -149,6 +151,44 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
     st = lib().loglinear_fwd_ex(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
         _dev(out, "out"), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    _check(st)
+    return out
+
+
+def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspace=None, group_log2: int = -1,
+            stream=None):
+    """Forward over a prompt that also writes the decode stack of its last
+    position.  Inputs as for ``fwd``; state [B,H,Lcap,dk,dv] and logscale
+    [B,H,Lcap] float32 are written (free slots untouched).  Decoding continues
+    with ``decode_step`` at pos = T.  Returns out [B,H,T,dv]."""
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    L = num_levels(T)
+    if tuple(a.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
+        raise ValueError(f"a must be [B,H,T] and lam [B,H,T,{L}]")
+    if state.dim() != 5:
+        raise ValueError("state must be [B,H,Lcap,dk,dv]")
+    Lcap = state.shape[2]
+    if tuple(state.shape) != (B, H, Lcap, dk, dv) or tuple(logscale.shape) != (B, H, Lcap):
+        raise ValueError("state must be [B,H,Lcap,dk,dv] and logscale [B,H,Lcap]")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (B, H, T, dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    need = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().loglinear_prefill(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+        _dev(out, "out"), _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
+        B, H, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
     _check(st)
     return out
 

@@ -98,21 +98,21 @@ int loglinear_num_levels(int64_t T)
     return levels_for(T);
 }
 
-static ll_status check_fwd_shape(int B, int H, int T, int dk, int dv, int chunk)
+static ll_status check_fwd_shape(const char *who, int B, int H, int T, int dk, int dv, int chunk)
 {
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0)
-        return fail(LL_EINVAL, "loglinear_fwd: negative or zero size (B=%d H=%d T=%d dk=%d dv=%d)", B, H, T, dk, dv);
+        return fail(LL_EINVAL, "%s: negative or zero size (B=%d H=%d T=%d dk=%d dv=%d)", who, B, H, T, dk, dv);
     if (chunk != 16 && chunk != 32 && chunk != 64)
-        return fail(LL_EUNSUPPORTED, "loglinear_fwd: chunk must be 16, 32 or 64 (got %d)", chunk);
+        return fail(LL_EUNSUPPORTED, "%s: chunk must be 16, 32 or 64 (got %d)", who, chunk);
     const int64_t BH = (int64_t)B * H;
     if (BH * ((int64_t)T / chunk + 1) > INT_MAX)
-        return fail(LL_EUNSUPPORTED, "loglinear_fwd: B*H*T/chunk too large for one launch");
+        return fail(LL_EUNSUPPORTED, "%s: B*H*T/chunk too large for one launch", who);
     return LL_OK;
 }
 
 size_t loglinear_fwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int chunk, int group_log2)
 {
-    if (check_fwd_shape(B, H, T, dk, dv, chunk) != LL_OK)
+    if (check_fwd_shape("loglinear_fwd_workspace_bytes", B, H, T, dk, dv, chunk) != LL_OK)
         return 0;
     if ((int64_t)B * H * T == 0)
         return 0;
@@ -124,21 +124,41 @@ size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
     return loglinear_fwd_workspace_bytes_ex(B, H, T, dk, dv, chunk, -1);
 }
 
-ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v, const float *a, const float *lambda,
-                           void *out, int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
-                           void *workspace, size_t workspace_bytes, void *stream, int group_log2)
+// Decode stack a prefill writes (NULL: a plain forward).
+struct StackOut {
+    float *state, *logscale;
+    int Lcap;
+};
+
+static ll_status run_fwd(const char *who, const void *q, const void *k, const void *v, const float *a,
+                         const float *lambda, void *out, int B, int H, int T, int dk, int dv, int chunk,
+                         ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, int group_log2,
+                         const StackOut *so)
 {
     if (dtype != LL_F32 && dtype != LL_BF16)
-        return fail(LL_EINVAL, "loglinear_fwd: unknown dtype %d", (int)dtype);
-    ll_status st = check_fwd_shape(B, H, T, dk, dv, chunk);
+        return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
+    ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
     if (st != LL_OK)
         return st;
     if (group_log2 > ll::kMaxGroupLog2)
-        return fail(LL_EUNSUPPORTED, "loglinear_fwd: group_log2 %d above %d", group_log2, ll::kMaxGroupLog2);
+        return fail(LL_EUNSUPPORTED, "%s: group_log2 %d above %d", who, group_log2, ll::kMaxGroupLog2);
     const bool bf16 = dtype == LL_BF16;
     if (!ll::fwd_supported(bf16, dk, dv, chunk))
-        return fail(LL_EUNSUPPORTED, "loglinear_fwd: no kernel for dtype=%s dk=%d dv=%d chunk=%d",
+        return fail(LL_EUNSUPPORTED, "%s: no kernel for dtype=%s dk=%d dv=%d chunk=%d", who,
                     bf16 ? "bf16" : "f32", dk, dv, chunk);
+    if (so) {
+        if (so->Lcap < 1)
+            return fail(LL_EINVAL, "%s: Lcap must be >= 1 (got %d)", who, so->Lcap);
+        if (so->Lcap < 2 || so->Lcap > ll::kMaxLevels)
+            return fail(LL_EUNSUPPORTED, "%s: Lcap must be in [2, %d] (got %d)", who, ll::kMaxLevels, so->Lcap);
+        if (levels_for(T) > so->Lcap)
+            return fail(LL_EINVAL, "%s: the stack of position %d needs %d slots, Lcap is %d", who, T - 1,
+                        levels_for(T), so->Lcap);
+        if (!ll::stack_supported(bf16, dk, dv))
+            return fail(LL_EUNSUPPORTED, "%s: no stack kernel for dk=%d dv=%d", who, dk, dv);
+        if ((int64_t)B * H * (dk / 16) > INT_MAX)
+            return fail(LL_EUNSUPPORTED, "%s: B*H too large for the stack launch", who);
+    }
     const int64_t rows = (int64_t)B * H * T;
     if (rows == 0)
         return ok();
@@ -148,39 +168,84 @@ ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v, const fl
     const char *names[] = {"q", "k", "v", "out"};
     for (int i = 0; i < 4; ++i) {
         if (!ptrs[i])
-            return fail(LL_EINVAL, "loglinear_fwd: %s is NULL", names[i]);
+            return fail(LL_EINVAL, "%s: %s is NULL", who, names[i]);
         if (!aligned(ptrs[i], 16))
-            return fail(LL_EINVAL, "loglinear_fwd: %s is not 16-byte aligned", names[i]);
+            return fail(LL_EINVAL, "%s: %s is not 16-byte aligned", who, names[i]);
     }
     if (!a || !lambda)
-        return fail(LL_EINVAL, "loglinear_fwd: %s is NULL", !a ? "a" : "lambda");
+        return fail(LL_EINVAL, "%s: %s is NULL", who, !a ? "a" : "lambda");
     if (!aligned(a, 4) || !aligned(lambda, 4))
-        return fail(LL_EINVAL, "loglinear_fwd: a and lambda must be 4-byte aligned");
+        return fail(LL_EINVAL, "%s: a and lambda must be 4-byte aligned", who);
     const int L = levels_for(T);
     if (L > ll::kMaxLevels)
-        return fail(LL_EUNSUPPORTED, "loglinear_fwd: T=%d needs %d levels (max %d)", T, L, ll::kMaxLevels);
+        return fail(LL_EUNSUPPORTED, "%s: T=%d needs %d levels (max %d)", who, T, L, ll::kMaxLevels);
     const size_t na = (size_t)rows * 4, nl = (size_t)rows * L * 4;
     if (overlaps(out, nv, q, nq) || overlaps(out, nv, k, nq) || overlaps(out, nv, v, nv) ||
         overlaps(out, nv, a, na) || overlaps(out, nv, lambda, nl))
-        return fail(LL_EINVAL, "loglinear_fwd: out aliases an input");
+        return fail(LL_EINVAL, "%s: out aliases an input", who);
     const ll::FwdPlan plan = ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4);
     if (plan.bytes > 0) {
         if (!workspace)
-            return fail(LL_EWORKSPACE, "loglinear_fwd: workspace of %zu bytes required, got NULL", plan.bytes);
+            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, plan.bytes);
         if (workspace_bytes < plan.bytes)
-            return fail(LL_EWORKSPACE, "loglinear_fwd: workspace of %zu bytes required, got %zu", plan.bytes,
+            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, plan.bytes,
                         workspace_bytes);
         if (!aligned(workspace, 256))
-            return fail(LL_EINVAL, "loglinear_fwd: workspace must be 256-byte aligned");
+            return fail(LL_EINVAL, "%s: workspace must be 256-byte aligned", who);
         if (overlaps(workspace, plan.bytes, out, nv) || overlaps(workspace, plan.bytes, q, nq) ||
             overlaps(workspace, plan.bytes, k, nq) || overlaps(workspace, plan.bytes, v, nv))
-            return fail(LL_EINVAL, "loglinear_fwd: workspace aliases an input or the output");
+            return fail(LL_EINVAL, "%s: workspace aliases an input or the output", who);
+    }
+    const size_t bh = (size_t)B * H;
+    if (so) {
+        if (!so->state || !so->logscale)
+            return fail(LL_EINVAL, "%s: %s is NULL", who, !so->state ? "state" : "logscale");
+        if (!aligned(so->state, 16) || !aligned(so->logscale, 4))
+            return fail(LL_EINVAL, "%s: state must be 16-byte and logscale 4-byte aligned", who);
+        const size_t nst = bh * so->Lcap * dk * dv * 4, nls = bh * so->Lcap * 4;
+        const void *others[] = {q, k, v, a, lambda, out, workspace};
+        const size_t sizes[] = {nq, nq, nv, na, nl, nv, plan.bytes};
+        for (int i = 0; i < 7; ++i)
+            if (overlaps(so->state, nst, others[i], sizes[i]) || overlaps(so->logscale, nls, others[i], sizes[i]))
+                return fail(LL_EINVAL, "%s: state and logscale must not alias the inputs, out or the workspace", who);
+        if (overlaps(so->state, nst, so->logscale, nls))
+            return fail(LL_EINVAL, "%s: state and logscale overlap", who);
     }
     ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
-    hipError_t e = ll::fwd_launch(args, plan, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = ll::fwd_launch(args, plan, s);
     if (e != hipSuccess)
-        return fail(LL_EDEVICE, "loglinear_fwd: launch failed: %s", hipGetErrorString(e));
+        return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+    if (so) {
+        const char *ws = static_cast<const char *>(workspace);
+        const int lgc = plan.g + (chunk == 16 ? 4 : chunk == 32 ? 5 : 6);
+        ll::StackArgs sa{k, v, a,
+                         plan.nL > 0 ? reinterpret_cast<const float *>(ws + plan.off_Sg) : nullptr,
+                         plan.nL > 0 ? reinterpret_cast<const float *>(ws + plan.off_Gam) : nullptr,
+                         so->state, so->logscale, (int)bh, T, dk, dv, lgc, plan.nG, plan.nL, so->Lcap, bf16};
+        e = ll::stack_launch(sa, s);
+        if (e != hipSuccess)
+            return fail(LL_EDEVICE, "%s: stack launch failed: %s", who, hipGetErrorString(e));
+    }
     return ok();
+}
+
+ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                           void *out, int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                           void *workspace, size_t workspace_bytes, void *stream, int group_log2)
+{
+    return run_fwd("loglinear_fwd", q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace,
+                   workspace_bytes, stream, group_log2, nullptr);
+}
+
+ll_status loglinear_prefill(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                            void *out, float *state, float *logscale, int B, int H, int T, int dk, int dv,
+                            int chunk, int Lcap, ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                            void *stream, int group_log2)
+{
+    const StackOut so{state, logscale, Lcap};
+    return run_fwd("loglinear_prefill", q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace,
+                   workspace_bytes, stream, group_log2, &so);
 }
 
 ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float *a, const float *lambda, void *out,

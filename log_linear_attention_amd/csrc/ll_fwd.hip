@@ -733,7 +733,6 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk_rs(
     using T = typename F::T;
     using Frag = typename F::Frag;
     using DTag = typename F::DTag;
-    constexpr int NJT = F::CP / 16;  // key tiles covered by the PV units (zero padded past C)
     constexpr int DKV = F::DK * F::DV;
     __shared__ WalkSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, qd = lane >> 4, li = lane & 15;

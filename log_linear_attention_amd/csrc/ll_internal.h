@@ -58,4 +58,19 @@ struct DecodeArgs {
 bool decode_supported(bool bf16, int dk, int dv);
 hipError_t decode_launch(const DecodeArgs &args, hipStream_t stream);
 
+// Decode stack of the prompt's last position, written after the forward
+// from its group states (Sg, Gam: NULL when the prompt is one group) and the
+// keys of the last group.  lgc = log2 of the group length in tokens.
+struct StackArgs {
+    const void *k, *v;
+    const float *a;
+    const float *Sg, *Gam;
+    float *state, *logscale;
+    int BH, T, dk, dv, lgc, nG, nL, Lcap;
+    bool bf16;
+};
+
+bool stack_supported(bool bf16, int dk, int dv);
+hipError_t stack_launch(const StackArgs &args, hipStream_t stream);
+
 }  // namespace ll

@@ -147,3 +147,49 @@ def test_profile_end_without_begin(L):
     arr = (ll.KernelStat * 4)()
     assert L.loglinear_profile_end(arr, 4, ctypes.byref(n)) == ll.LL_EINVAL
     assert L.loglinear_profile_begin(0) == ll.LL_EINVAL
+
+
+def _pre(L, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, lam=FAKE + 0x400000,
+                out=FAKE + 0x8000000, state=FAKE + 0x10000000, logscale=FAKE + 0x20000000,
+                B=1, H=1, T=64, dk=128, dv=64, chunk=64, Lcap=17, dtype=ll.LL_BF16,
+                ws=None, wsb=0, stream=None, g=-1)
+    args.update(kw)
+    return L.loglinear_prefill(args["q"], args["k"], args["v"], args["a"], args["lam"], args["out"],
+                               args["state"], args["logscale"], args["B"], args["H"], args["T"], args["dk"],
+                               args["dv"], args["chunk"], args["Lcap"], args["dtype"], args["ws"], args["wsb"],
+                               args["stream"], args["g"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), ll.LL_EINVAL),
+    (dict(T=-1), ll.LL_EINVAL),
+    (dict(chunk=8), ll.LL_EUNSUPPORTED),
+    (dict(Lcap=0), ll.LL_EINVAL),
+    (dict(Lcap=1), ll.LL_EUNSUPPORTED),
+    (dict(Lcap=33), ll.LL_EUNSUPPORTED),
+    (dict(T=129, Lcap=8), ll.LL_EINVAL),         # position 128 needs slot 8
+    (dict(dk=256, dtype=ll.LL_F32), ll.LL_EUNSUPPORTED),
+    (dict(state=None), ll.LL_EINVAL),
+    (dict(logscale=None), ll.LL_EINVAL),
+    (dict(state=FAKE + 0x10000004), ll.LL_EINVAL),  # misaligned
+    (dict(logscale=FAKE + 0x20000002), ll.LL_EINVAL),
+    (dict(state=FAKE + 0x100), ll.LL_EINVAL),        # state overlaps q
+    (dict(logscale=FAKE + 0x8000000), ll.LL_EINVAL),  # logscale overlaps out
+    (dict(logscale=FAKE + 0x10000100), ll.LL_EINVAL),  # logscale inside state
+    (dict(T=1000), ll.LL_EWORKSPACE),
+])
+def test_prefill_rejects_bad_arguments(L, kw, status):
+    assert _pre(L, **kw) == status
+    assert ll.last_error().startswith("loglinear_prefill")
+
+
+def test_prefill_lcap_fits_exactly(L):
+    # position 127 uses slots 0..7: Lcap = 8 passes validation (B = 0, so
+    # nothing is launched), Lcap = 7 does not
+    assert _pre(L, T=128, Lcap=8, B=0) == ll.LL_OK
+    assert _pre(L, T=128, Lcap=7, B=0) == ll.LL_EINVAL
+
+
+def test_prefill_empty_prompt_is_a_no_op(L):
+    assert _pre(L, T=0, q=None, k=None, v=None, out=None, a=None, lam=None, state=None, logscale=None) == ll.LL_OK
