@@ -16,6 +16,9 @@ Fenwick stacks of 17 slots).  Prints ONE JSON line on stdout.
                first pass, with no events between launches, gives `value`
   decode       decode GB/s (algorithmic bytes / step time), tokens/s and its
                own roofline
+  prefill      the forward that also writes the decode stack of the last
+               position (loglinear_prefill, 17 slots): step time and the
+               stack kernel's roofline
   cpu_baseline the fp64 oracle on a bounded row sample of the same workload
 
 Three input sets (3 x 218 MB) rotate through the forward steps and two
@@ -89,6 +92,35 @@ def decode_algorithmic(cfg, positions):
             + 8 * cfg.Lcap + cfg.dv * e
         total += cfg.H * per_head
     return total
+
+
+def auto_group_log2(cfg) -> int:
+    """The forward's automatic group size: the largest g <= 3 whose groups of
+    2^g chunks still give at least 512 workgroups of two groups each."""
+    N = (cfg.T + cfg.chunk - 1) // cfg.chunk
+    g = 0
+    while g < 3 and (2 << g) <= N and cfg.B * cfg.H * ((N + (2 << g) - 1) // (2 << g)) >= 512:
+        g += 1
+    return g
+
+
+def stack_algorithmic(cfg, g: int, Lcap: int):
+    """Algorithmic bytes of the prefill's stack export for the prompt's last
+    position p = T-1: one stored block state (input dtype) per occupied
+    bucket of whole groups, the group decay totals between those buckets and
+    the last group, k, v and a of the keys of the last group (the finer
+    buckets and the decays inside it), and the occupied slots and their
+    log-scales written in fp32."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    p = cfg.T - 1
+    lgc = (cfg.chunk << g).bit_length() - 1
+    t0 = (p >> lgc) << lgc
+    n_groups = t0 >> lgc
+    whole = bin(p >> lgc).count("1")
+    occ = 1 + bin(p).count("1")
+    per_head = whole * cfg.dk * cfg.dv * e + 4 * n_groups + (p + 1 - t0) * ((cfg.dk + cfg.dv) * e + 4) \
+        + occ * (cfg.dk * cfg.dv * 4 + 4)
+    return cfg.B * cfg.H * per_head
 
 
 def read_traffic():
@@ -253,6 +285,39 @@ def main():
     dec_gbs = dbytes / (dec_kernel_ms * 1e-3) / 1e9
     log(f"decode: {dec_ms:.4f} ms/step, kernel {dec_kernel_ms:.4f} ms, {dec_gbs:.1f} GB/s")
 
+    # ---- prefill: the forward plus the decode stack of the last position ----
+    Lcap = 17
+    g_used = args.group_log2 if args.group_log2 >= 0 else auto_group_log2(cfg)
+    pstate = torch.empty((cfg.B, cfg.H, Lcap, cfg.dk, cfg.dv), dtype=torch.float32, device=dev)
+    plog = torch.empty((cfg.B, cfg.H, Lcap), dtype=torch.float32, device=dev)
+
+    def pstep(i):
+        d = dsets[i % 3]
+        ll.prefill(d["q"], d["k"], d["v"], d["a"], d["lam"], pstate, plog, chunk=cfg.chunk, out=out,
+                   workspace=ws, group_log2=args.group_log2)
+
+    for i in range(args.warmup):
+        pstep(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        pstep(i)
+    e1.record()
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1) / args.steps
+    ll.profile_begin(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        pstep(i)
+    torch.cuda.synchronize()
+    pstats = ll.profile_end()
+    sl, sms = pstats["ll_prefill_stack"]
+    stack_ms = sms / sl
+    sbytes = stack_algorithmic(cfg, g_used, Lcap)
+    stack_gbs = sbytes / (stack_ms * 1e-3) / 1e9
+    log(f"prefill: {pre_ms:.4f} ms/step (forward alone {fwd_ms:.4f}); stack kernel {stack_ms:.4f} ms, "
+        f"{stack_gbs:.1f} GB/s")
+
     result = {
         "metric": "tokens/s, log-linear Mamba-2 fwd at T=16K (% MFMA peak); decode GB/s",
         "value": round(cfg.B * cfg.T / (fwd_ms * 1e-3), 1),
@@ -285,6 +350,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "ll_decode", "kernel_avg_ms": round(dec_kernel_ms, 5)},
+        },
+        "prefill": {
+            "workload": "fwd_bf16_T16K + stack (Lcap 17)", "ms_per_step": round(pre_ms, 5),
+            "tokens_per_s": round(cfg.B * cfg.T / (pre_ms * 1e-3), 1),
+            "stack_algorithmic_bytes": sbytes,
+            "roofline": {"bound": "hbm", "achieved": round(stack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(stack_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
         },
         "cpu_baseline": None,
     }

@@ -213,16 +213,18 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
     }
     ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = ll::fwd_launch(args, plan, s);
+    bool nat = false;
+    hipError_t e = ll::fwd_launch(args, plan, s, &nat);
     if (e != hipSuccess)
         return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
     if (so) {
         const char *ws = static_cast<const char *>(workspace);
         const int lgc = plan.g + (chunk == 16 ? 4 : chunk == 32 ? 5 : 6);
         ll::StackArgs sa{k, v, a,
-                         plan.nL > 0 ? reinterpret_cast<const float *>(ws + plan.off_Sg) : nullptr,
+                         plan.nL > 0 ? static_cast<const void *>(ws + plan.off_Dg) : nullptr,
                          plan.nL > 0 ? reinterpret_cast<const float *>(ws + plan.off_Gam) : nullptr,
-                         so->state, so->logscale, (int)bh, T, dk, dv, lgc, plan.nG, plan.nL, so->Lcap, bf16};
+                         so->state, so->logscale, (int)bh, T, dk, dv, lgc, plan.nG, plan.nL, plan.nLeft, so->Lcap,
+                         bf16, nat};
         e = ll::stack_launch(sa, s);
         if (e != hipSuccess)
             return fail(LL_EDEVICE, "%s: stack launch failed: %s", who, hipGetErrorString(e));

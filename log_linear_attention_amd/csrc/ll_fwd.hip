@@ -2156,7 +2156,7 @@ FwdPlan fwd_plan(int B, int H, int T, int dk, int dv, int chunk, int group_log2,
 }
 
 template <class F>
-static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s)
+static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s, bool *nat_blocks)
 {
     using T = typename F::T;
     const int BH = A.B * A.H;
@@ -2174,6 +2174,8 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
                             (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
         use_ws = A.L <= WS::NLV && fits32;
     }
+    if (nat_blocks)
+        *nat_blocks = use_ws;
     if (P.nL > 0) {
         ProfEvents pe = prof_events("ll_group_state");
         hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
@@ -2241,7 +2243,7 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     return hipGetLastError();
 }
 
-typedef hipError_t (*FwdLauncher)(const FwdArgs &, const FwdPlan &, hipStream_t);
+typedef hipError_t (*FwdLauncher)(const FwdArgs &, const FwdPlan &, hipStream_t, bool *);
 
 template <class DT, int DK, int DV, int C>
 static FwdLauncher pick_c()
@@ -2297,12 +2299,12 @@ static FwdLauncher find_fwd(bool bf16, int dk, int dv, int chunk)
 
 bool fwd_supported(bool bf16, int dk, int dv, int chunk) { return find_fwd(bf16, dk, dv, chunk) != nullptr; }
 
-hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream)
+hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream, bool *nat_blocks)
 {
     FwdLauncher f = find_fwd(args.bf16, args.dk, args.dv, args.chunk);
     if (!f)
         return hipErrorInvalidValue;
-    return f(args, plan, stream);
+    return f(args, plan, stream, nat_blocks);
 }
 
 }  // namespace ll

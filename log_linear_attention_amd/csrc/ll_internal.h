@@ -43,7 +43,10 @@ struct ProfEvents {
 ProfEvents prof_events(const char *name);
 
 bool fwd_supported(bool bf16, int dk, int dv, int chunk);
-hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream);
+// nat_blocks (optional) receives the dk order of the stored block states:
+// true for the natural order inside each 16-byte fragment lane (lane quad qd
+// of unit u holds dk KB*u + 8*qd + e), false for unit_row's.
+hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream, bool *nat_blocks = nullptr);
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -59,15 +62,17 @@ bool decode_supported(bool bf16, int dk, int dv);
 hipError_t decode_launch(const DecodeArgs &args, hipStream_t stream);
 
 // Decode stack of the prompt's last position, written after the forward
-// from its group states (Sg, Gam: NULL when the prompt is one group) and the
-// keys of the last group.  lgc = log2 of the group length in tokens.
+// from its left-child block states (Dg, Gam: NULL when the prompt is one
+// group) and the keys of the last group.  lgc = log2 of the group length in
+// tokens; nat = the block states' dk order (see fwd_launch).
 struct StackArgs {
     const void *k, *v;
     const float *a;
-    const float *Sg, *Gam;
+    const void *Dg;        // left-child block states (fragment order, input dtype)
+    const float *Gam;      // per-group log-decay totals
     float *state, *logscale;
-    int BH, T, dk, dv, lgc, nG, nL, Lcap;
-    bool bf16;
+    int BH, T, dk, dv, lgc, nG, nL, nLeft, Lcap;
+    bool bf16, nat;
 };
 
 bool stack_supported(bool bf16, int dk, int dv);
