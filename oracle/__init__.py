@@ -25,6 +25,10 @@ carries [LLA-pt §2 "Forma Recorrente e Paralela", decoding bullet; LLA-fr §2
 "Algorithmes Efficaces", inference bullet].  Written from that description
 in numpy fp64, one (sequence, head) at a time.
 
+Backward (``bwd``, ``bwd_rows``): the gradients of sum(do * o) with respect
+to q, k, v, a and lambda, each differentiated term by term from the forward
+definition and evaluated plainly in C (``ll_oracle.c``, backward section).
+
 Prefill (``prefill_stack``): the stack that a whole prompt leaves for the
 decode of the next token, summed bucket by bucket from the same definition
 the forward uses.
@@ -75,6 +79,12 @@ def _load():
         lib.ll_oracle_fwd.restype = ctypes.c_int
         lib.ll_oracle_fwd_rows.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
         lib.ll_oracle_fwd_rows.restype = ctypes.c_int
+        lib.ll_oracle_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, P, P, P]
+        lib.ll_oracle_bwd.restype = ctypes.c_int
+        lib.ll_oracle_bwd_qrows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
+        lib.ll_oracle_bwd_qrows.restype = ctypes.c_int
+        lib.ll_oracle_bwd_krows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
+        lib.ll_oracle_bwd_krows.restype = ctypes.c_int
         lib.ll_oracle_num_threads.argtypes = []
         lib.ll_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -128,6 +138,51 @@ def fwd_rows(q, k, v, a, lam, rows) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle fwd_rows failed (code {rc})")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Backward: gradients of the forward definition.
+# ---------------------------------------------------------------------------
+
+def bwd(q, k, v, a, lam, do):
+    """Gradients of sum(do * fwd(q, k, v, a, lam)) with respect to every
+    input, by the term-by-term derivative of the definition (C, fp64,
+    O(T^2)).  Returns dict(dq, dk, dv, da, dlam) shaped like the inputs;
+    da[..., 0] is 0 because a_0 never enters."""
+    q, k, v, a, lam, do = (_f64(x) for x in (q, k, v, a, lam, do))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "da": np.zeros_like(a), "dlam": np.zeros_like(lam)}
+    rc = _load().ll_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam), _ptr(do), B * H, T, dk, dv, L,
+                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["da"]),
+                               _ptr(out["dlam"]))
+    if rc != 0:
+        raise ValueError(f"oracle bwd failed (code {rc})")
+    return out
+
+
+def bwd_rows(q, k, v, a, lam, do, qrows, krows):
+    """Selected rows of the gradients: ``qrows`` [n, 2] of (b*H + h, t) for
+    dq [n, dk] and dlam [n, L]; ``krows`` [m, 2] of (b*H + h, s) for
+    dk [m, dk] and dv [m, dv]."""
+    q, k, v, a, lam, do = (_f64(x) for x in (q, k, v, a, lam, do))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    qrows = np.ascontiguousarray(np.asarray(qrows, dtype=np.int64).reshape(-1, 2))
+    krows = np.ascontiguousarray(np.asarray(krows, dtype=np.int64).reshape(-1, 2))
+    dq = np.zeros((qrows.shape[0], dk)); dlam = np.zeros((qrows.shape[0], L))
+    dkk = np.zeros((krows.shape[0], dk)); dvv = np.zeros((krows.shape[0], dv))
+    lib = _load()
+    rc = lib.ll_oracle_bwd_qrows(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam), _ptr(do), B * H, T, dk, dv, L,
+                                 qrows.shape[0], _ptr(qrows), _ptr(dq), _ptr(dlam))
+    rc = rc or lib.ll_oracle_bwd_krows(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam), _ptr(do), B * H, T, dk, dv,
+                                       L, krows.shape[0], _ptr(krows), _ptr(dkk), _ptr(dvv))
+    if rc != 0:
+        raise ValueError(f"oracle bwd_rows failed (code {rc})")
+    return {"dq": dq, "dlam": dlam, "dk": dkk, "dv": dvv}
 
 
 # ---------------------------------------------------------------------------

@@ -39,11 +39,14 @@
  *
  * Layouts (all row-major, contiguous, fp64):
  *   q, k [BH, T, dk]; v [BH, T, dv]; a [BH, T]; lam [BH, T, L]; out [n, dv].
+ *
+ * The backward section further down differentiates the same sum.
  */
 #include <math.h>
 #include <omp.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* Fenwick level of key s as seen from query t (both 0-indexed, s <= t). */
 int ll_oracle_level(int64_t t, int64_t s)
@@ -131,6 +134,188 @@ int ll_oracle_fwd(const double *q, const double *k, const double *v,
 #pragma omp critical
                 status = rc;
             }
+        }
+    }
+    return status;
+}
+
+/* ---- backward --------------------------------------------------------------
+ *
+ * Gradients of the scalar sum_t do[t,:] . o[t,:] with respect to every input,
+ * by differentiating the definition above term by term.  With
+ *   w(t,s) = exp(sum_{r=s+1..t} a_r) * lambda[t, level(t,s)]   (s <= t)
+ *   P(t,s) = w(t,s) * (q_t . k_s) * (do_t . v_s):
+ *   dq_t           = sum_{s<=t} w(t,s) (do_t . v_s) k_s
+ *   dk_s           = sum_{t>=s} w(t,s) (do_t . v_s) q_t
+ *   dv_s           = sum_{t>=s} w(t,s) (q_t . k_s) do_t
+ *   dlambda_t[l]   = sum_{s<=t, level(t,s)=l} exp(sum_{r=s+1..t} a_r) (q_t . k_s)(do_t . v_s)
+ *   da_r (r >= 1)  = sum_{t>=r} sum_{s<r} P(t,s)     (a_r sits in the decay of
+ *                    exactly the pairs s < r <= t); da_0 = 0 (a_0 never enters)
+ * The last one is evaluated as da_r = sum_{t>=r} (Pq_t - Pk_t) with
+ * Pq_t = sum_{s<=t} P(t,s) and Pk_t = sum_{t'>=t} P(t',t): the pairs with
+ * s >= r cancel between the two sums.  Backpropagation through the
+ * per-level weights lambda is the part the French page names as needing
+ * custom kernels ([LLA-fr §5 "Signification et Limites", limits list]).
+ *
+ * Layouts: do [BH, T, dv]; dq, dk [BH, T, dk]; dv [BH, T, dv]; da [BH, T];
+ * dlam [BH, T, L].
+ */
+
+/* Query-side row t of head bh: dq_t, dlam_t and Pq_t. */
+static int oracle_bwd_qrow(const double *q, const double *k, const double *v, const double *a,
+                           const double *lam, const double *dout, int64_t T, int64_t dk, int64_t dv,
+                           int64_t L, int64_t bh, int64_t t, double *dq, double *dlam, double *pq)
+{
+    const double *qt = q + (bh * T + t) * dk;
+    const double *dot = dout + (bh * T + t) * dv;
+    const double *lt = lam + (bh * T + t) * L;
+    const double *ah = a + bh * T;
+    for (int64_t d = 0; d < dk; ++d)
+        dq[d] = 0.0;
+    for (int64_t l = 0; l < L; ++l)
+        dlam[l] = 0.0;
+    double psum = 0.0, logdecay = 0.0;
+    for (int64_t s = t; s >= 0; --s) {
+        if (s < t)
+            logdecay += ah[s + 1];
+        int lev = ll_oracle_level(t, s);
+        if (lev >= L)
+            return -1;
+        const double *ks = k + (bh * T + s) * dk;
+        const double *vs = v + (bh * T + s) * dv;
+        double qk = 0.0, dov = 0.0;
+        for (int64_t d = 0; d < dk; ++d)
+            qk += qt[d] * ks[d];
+        for (int64_t e = 0; e < dv; ++e)
+            dov += dot[e] * vs[e];
+        double dec = exp(logdecay);
+        double w = dec * lt[lev];
+        for (int64_t d = 0; d < dk; ++d)
+            dq[d] += w * dov * ks[d];
+        dlam[lev] += dec * qk * dov;
+        psum += w * qk * dov;
+    }
+    *pq = psum;
+    return 0;
+}
+
+/* Key-side row s of head bh: dk_s, dv_s and Pk_s. */
+static int oracle_bwd_krow(const double *q, const double *k, const double *v, const double *a,
+                           const double *lam, const double *dout, int64_t T, int64_t dk, int64_t dv,
+                           int64_t L, int64_t bh, int64_t s, double *dks, double *dvs, double *pk)
+{
+    const double *ks = k + (bh * T + s) * dk;
+    const double *vs = v + (bh * T + s) * dv;
+    const double *ah = a + bh * T;
+    for (int64_t d = 0; d < dk; ++d)
+        dks[d] = 0.0;
+    for (int64_t e = 0; e < dv; ++e)
+        dvs[e] = 0.0;
+    double psum = 0.0, logdecay = 0.0;
+    for (int64_t t = s; t < T; ++t) {
+        if (t > s)
+            logdecay += ah[t];
+        int lev = ll_oracle_level(t, s);
+        if (lev >= L)
+            return -1;
+        const double *qt = q + (bh * T + t) * dk;
+        const double *dot = dout + (bh * T + t) * dv;
+        double qk = 0.0, dov = 0.0;
+        for (int64_t d = 0; d < dk; ++d)
+            qk += qt[d] * ks[d];
+        for (int64_t e = 0; e < dv; ++e)
+            dov += dot[e] * vs[e];
+        double w = exp(logdecay) * lam[(bh * T + t) * L + lev];
+        for (int64_t d = 0; d < dk; ++d)
+            dks[d] += w * dov * qt[d];
+        for (int64_t e = 0; e < dv; ++e)
+            dvs[e] += w * qk * dot[e];
+        psum += w * qk * dov;
+    }
+    *pk = psum;
+    return 0;
+}
+
+/* Every gradient of every head. */
+int ll_oracle_bwd(const double *q, const double *k, const double *v, const double *a, const double *lam,
+                  const double *dout, int64_t BH, int64_t T, int64_t dk, int64_t dv, int64_t L, double *dq,
+                  double *dkk, double *dvv, double *da, double *dlam)
+{
+    int status = 0;
+    double *pq = (double *)calloc((size_t)(BH * T > 0 ? BH * T : 1), sizeof(double));
+    double *pk = (double *)calloc((size_t)(BH * T > 0 ? BH * T : 1), sizeof(double));
+    if (!pq || !pk) {
+        free(pq);
+        free(pk);
+        return -3;
+    }
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        for (int64_t t = 0; t < T; ++t) {
+            int rc = oracle_bwd_qrow(q, k, v, a, lam, dout, T, dk, dv, L, bh, t, dq + (bh * T + t) * dk,
+                                     dlam + (bh * T + t) * L, pq + bh * T + t);
+            if (rc == 0)
+                rc = oracle_bwd_krow(q, k, v, a, lam, dout, T, dk, dv, L, bh, t, dkk + (bh * T + t) * dk,
+                                     dvv + (bh * T + t) * dv, pk + bh * T + t);
+            if (rc != 0) {
+#pragma omp critical
+                status = rc;
+            }
+        }
+    }
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        double run = 0.0;
+        for (int64_t r = T - 1; r >= 1; --r) {
+            run += pq[bh * T + r] - pk[bh * T + r];
+            da[bh * T + r] = run;
+        }
+        if (T > 0)
+            da[bh * T] = 0.0;
+    }
+    free(pq);
+    free(pk);
+    return status;
+}
+
+/* Selected query-side rows (rows[2i] = bh, rows[2i+1] = t): dq [n, dk],
+ * dlam [n, L]. */
+int ll_oracle_bwd_qrows(const double *q, const double *k, const double *v, const double *a, const double *lam,
+                        const double *dout, int64_t BH, int64_t T, int64_t dk, int64_t dv, int64_t L,
+                        int64_t nrows, const int64_t *rows, double *dq, double *dlam)
+{
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t bh = rows[2 * i], t = rows[2 * i + 1];
+        double pq;
+        int rc = (bh < 0 || bh >= BH || t < 0 || t >= T)
+                     ? -2
+                     : oracle_bwd_qrow(q, k, v, a, lam, dout, T, dk, dv, L, bh, t, dq + i * dk, dlam + i * L, &pq);
+        if (rc != 0) {
+#pragma omp critical
+            status = rc;
+        }
+    }
+    return status;
+}
+
+/* Selected key-side rows (rows[2i] = bh, rows[2i+1] = s): dk [n, dk],
+ * dv [n, dv]. */
+int ll_oracle_bwd_krows(const double *q, const double *k, const double *v, const double *a, const double *lam,
+                        const double *dout, int64_t BH, int64_t T, int64_t dk, int64_t dv, int64_t L,
+                        int64_t nrows, const int64_t *rows, double *dkk, double *dvv)
+{
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t bh = rows[2 * i], s = rows[2 * i + 1];
+        double pk;
+        int rc = (bh < 0 || bh >= BH || s < 0 || s >= T)
+                     ? -2
+                     : oracle_bwd_krow(q, k, v, a, lam, dout, T, dk, dv, L, bh, s, dkk + i * dk, dvv + i * dv, &pk);
+        if (rc != 0) {
+#pragma omp critical
+            status = rc;
         }
     }
     return status;

@@ -365,3 +365,106 @@ def test_prefill_stack_too_few_slots_is_an_error(oracle_mod):
     k = np.zeros((1, 1, 9, 1)); v = np.zeros((1, 1, 9, 1)); a = np.zeros((1, 1, 9))
     with pytest.raises(ValueError):
         oracle_mod.prefill_stack(k, v, a, 4)  # position 8 needs slot 4
+
+
+# --- backward: gradients of sum(do * o) -------------------------------------------
+
+def _loss(oracle_mod, q, k, v, a, lam, do):
+    return float(np.sum(do * oracle_mod.fwd(q, k, v, a, lam)))
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 16, 23])
+def test_bwd_matches_finite_differences(oracle_mod, T):
+    """Central differences of the forward oracle along random directions,
+    input by input (the step keeps the fp64 truncation error near 1e-9)."""
+    rng = np.random.default_rng(40 + T)
+    B, H, dk, dv = 1, 2, 3, 2
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, L)
+    do = rng.standard_normal((B, H, T, dv))
+    g = oracle_mod.bwd(q, k, v, a, lam, do)
+    args = {"q": q, "k": k, "v": v, "a": a, "lam": lam}
+    eps = 1e-5
+    for name, x in args.items():
+        for _ in range(3):
+            d = rng.standard_normal(x.shape)
+            if name == "a":
+                d[..., 0] = 0.0  # a_0 never enters: its gradient is 0 by construction
+            plus = dict(args); plus[name] = x + eps * d
+            minus = dict(args); minus[name] = x - eps * d
+            fd = (_loss(oracle_mod, **plus, do=do) - _loss(oracle_mod, **minus, do=do)) / (2 * eps)
+            an = float(np.sum(g["d" + name] * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+    assert np.all(g["da"][..., 0] == 0.0)
+
+
+def _torch_masked_forward(torch, q, k, v, a, lam):
+    """O = ((Q K^T) ⊙ M) V with M[t,s] = exp(A_t - A_s) * lam[t, level(t,s)]
+    for s <= t (A = prefix sums of a from index 1), built with plain torch
+    ops so that autograd differentiates it independently of the oracle."""
+    T = q.shape[-2]
+    A = torch.cumsum(torch.cat([torch.zeros_like(a[..., :1]), a[..., 1:]], dim=-1), dim=-1)
+    t_idx = torch.arange(T).view(T, 1)
+    s_idx = torch.arange(T).view(1, T)
+    x = (t_idx ^ s_idx).clamp(min=0)
+    lev = torch.zeros((T, T), dtype=torch.int64)
+    for b in range(max(T, 1).bit_length() + 1):
+        lev = torch.where(x >= (1 << b), torch.full_like(lev, b + 1), lev)
+    causal = s_idx <= t_idx
+    lev = torch.where(causal, lev, torch.zeros_like(lev))
+    lam_ts = torch.gather(lam, -1, lev.expand(*lam.shape[:-2], T, T))
+    decay = torch.exp(torch.where(causal, A.unsqueeze(-1) - A.unsqueeze(-2), torch.full_like(lam_ts, -1e300)))
+    M = decay * lam_ts * causal
+    return ((q @ k.transpose(-1, -2)) * M) @ v
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 33])
+def test_bwd_matches_torch_autograd_of_masked_form(oracle_mod, T):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(50 + T)
+    B, H, dk, dv = 2, 1, 4, 3
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, L)
+    do = rng.standard_normal((B, H, T, dv))
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, a, lam)]
+    o = _torch_masked_forward(torch, *ts)
+    np.testing.assert_allclose(o.detach().numpy(), oracle_mod.fwd(q, k, v, a, lam), rtol=1e-12, atol=1e-12)
+    (o * torch.tensor(do)).sum().backward()
+    g = oracle_mod.bwd(q, k, v, a, lam, do)
+    for name, t in zip(("dq", "dk", "dv", "da", "dlam"), ts):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
+
+
+def test_bwd_decay_shift_invariance(oracle_mod):
+    """Adding a constant c to every a_r (r >= 1) multiplies each pair's
+    weight by exp(c (t - s)); the derivative in c at 0 is sum_r da_r, which
+    must equal sum_t sum_s (t - s) P(t,s) — checked against a direct sum."""
+    rng = np.random.default_rng(60)
+    T, dk, dv = 19, 3, 2
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, 1, 1, T, dk, dv, L)
+    do = rng.standard_normal((1, 1, T, dv))
+    g = oracle_mod.bwd(q, k, v, a, lam, do)
+    total = 0.0
+    for t in range(T):
+        for s in range(t + 1):
+            w = np.exp(np.sum(a[0, 0, s + 1:t + 1])) * lam[0, 0, t, oracle_mod.level(t, s)]
+            total += (t - s) * w * (q[0, 0, t] @ k[0, 0, s]) * (do[0, 0, t] @ v[0, 0, s])
+    np.testing.assert_allclose(np.sum(g["da"]), total, rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_rows_match_full(oracle_mod):
+    rng = np.random.default_rng(61)
+    T, dk, dv = 40, 5, 3
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, 2, 2, T, dk, dv, L)
+    do = rng.standard_normal((2, 2, T, dv))
+    g = oracle_mod.bwd(q, k, v, a, lam, do)
+    rows = np.array([[0, 0], [1, 17], [3, 39], [2, 5]])
+    r = oracle_mod.bwd_rows(q, k, v, a, lam, do, rows, rows)
+    for i, (bh, t) in enumerate(rows):
+        b, h = divmod(bh, 2)
+        np.testing.assert_allclose(r["dq"][i], g["dq"][b, h, t], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(r["dlam"][i], g["dlam"][b, h, t], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(r["dk"][i], g["dk"][b, h, t], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(r["dv"][i], g["dv"][b, h, t], rtol=1e-13, atol=1e-13)
