@@ -138,6 +138,38 @@ ll_status loglinear_decode_step(const void *q, const void *k, const void *v,
                                 void *out, int S, int H, int dk, int dv, int Lcap,
                                 ll_dtype dtype, void *stream);
 
+/* Backward: gradients of the scalar sum over (b, h, t) of dout[t,:] . out[t,:]
+ * with respect to q, k, v, a and lambda, for the forward above (the pages
+ * name backpropagation through the per-level weights lambda as needing
+ * custom kernels: French page §5 "Signification et Limites").  With
+ * w(t,s) = exp(sum_{r=s+1..t} a[r]) * lambda[t, level(t,s)] for s <= t:
+ *   dq[t]        = sum_s w(t,s) (dout[t].v[s]) k[s]
+ *   dk[s]        = sum_t w(t,s) (dout[t].v[s]) q[t]
+ *   dv[s]        = sum_t w(t,s) (q[t].k[s]) dout[t]
+ *   dlambda[t,l] = sum over keys s of level l: exp(decay) (q[t].k[s]) (dout[t].v[s])
+ *   da[r]        = sum over pairs s < r <= t of w(t,s) (q[t].k[s]) (dout[t].v[s]),
+ *                  da[...,0] = 0 (a[...,0] never enters)
+ *  q, k, v, a, lambda: the forward's inputs (same shapes and dtype)
+ *  dout   [B,H,T,dv]  dtype, the gradient of the loss with respect to out
+ *  dq, dk [B,H,T,dk]  dtype, written
+ *  dv     [B,H,T,dv]  dtype, written
+ *  da     [B,H,T]     float32, written
+ *  dlambda [B,H,T,L]  float32, written (0 for levels that are empty for a row)
+ *  workspace: caller-owned device scratch of loglinear_bwd_workspace_bytes
+ *         bytes, 256-byte aligned; contents on entry do not matter.
+ * Outputs must not alias each other, the inputs or the workspace.
+ * Supported: chunk 32 or 64; dk, dv in {32, 64, 128}; both dtypes, where the
+ * kernels fit in LDS (bf16 chunk 64 and 32; float32 chunk 32).  Anything
+ * else returns LL_EUNSUPPORTED.  Accumulation is float32 throughout; in bf16
+ * the operands of the matrix products are bf16, as in the forward.
+ * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
+size_t loglinear_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
+ll_status loglinear_bwd(const void *q, const void *k, const void *v,
+                        const float *a, const float *lambda, const void *dout,
+                        void *dq, void *dk_out, void *dv_out, float *da, float *dlambda,
+                        int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Prefill: the forward of loglinear_fwd_ex over a prompt of T tokens, which
  * also writes the decode stack the prompt leaves for its next token, so that
  * decoding can continue at position T (the recurrent form takes over from

@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.loglinear_fwd_ex.restype = I
         L.loglinear_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_prefill.restype = I
+        L.loglinear_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.loglinear_bwd_workspace_bytes.restype = Z
+        L.loglinear_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+        L.loglinear_bwd.restype = I
         L.loglinear_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
         L.loglinear_decode_step.restype = I
         L.loglinear_last_error.argtypes = []
@@ -191,6 +195,42 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
         B, H, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
     _check(st)
     return out
+
+
+def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int) -> int:
+    return int(lib().loglinear_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def bwd(q, k, v, a, lam, dout, chunk: int = 64, workspace=None, stream=None):
+    """Backward of ``fwd``: gradients of sum(dout * fwd(q, k, v, a, lam)).
+    Returns (dq, dk, dv, da, dlam): dq, dk, dv in the input dtype, da and
+    dlam float32.  Asynchronous on ``stream``."""
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
+        raise TypeError("q, k, v, dout must share one dtype")
+    L = num_levels(T)
+    if tuple(a.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L) or tuple(dout.shape) != (B, H, T, dv):
+        raise ValueError(f"a must be [B,H,T], lam [B,H,T,{L}] and dout [B,H,T,dv]")
+    dq = torch.empty_like(q)
+    dk_ = torch.empty_like(k)
+    dv_ = torch.empty_like(v)
+    da = torch.empty_like(a)
+    dlam = torch.empty_like(lam)
+    need = bwd_workspace_bytes(B, H, T, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().loglinear_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+        _dev(dout, "dout"), _dev(dq, "dq"), _dev(dk_, "dk"), _dev(dv_, "dv"), _dev(da, "da", torch.float32),
+        _dev(dlam, "dlam", torch.float32), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream))
+    _check(st)
+    return dq, dk_, dv_, da, dlam
 
 
 def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):

@@ -258,6 +258,84 @@ ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float
                             stream, -1);
 }
 
+size_t loglinear_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
+{
+    if (check_fwd_shape("loglinear_bwd_workspace_bytes", B, H, T, dk, dv, chunk) != LL_OK)
+        return 0;
+    if ((int64_t)B * H * T == 0)
+        return 0;
+    return ll::bwd_plan(B, H, T, dk, dv, chunk).bytes;
+}
+
+ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                        const void *dout, void *dq, void *dk_out, void *dv_out, float *da, float *dlambda, int B,
+                        int H, int T, int dk, int dv, int chunk, ll_dtype dtype, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    const char *who = "loglinear_bwd";
+    if (dtype != LL_F32 && dtype != LL_BF16)
+        return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
+    ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
+    if (st != LL_OK)
+        return st;
+    const bool bf16 = dtype == LL_BF16;
+    if (!ll::bwd_supported(bf16, dk, dv, chunk))
+        return fail(LL_EUNSUPPORTED, "%s: no kernel for dtype=%s dk=%d dv=%d chunk=%d", who, bf16 ? "bf16" : "f32",
+                    dk, dv, chunk);
+    const int64_t rows = (int64_t)B * H * T;
+    if (rows == 0)
+        return ok();
+    const int L = levels_for(T);
+    if (L > ll::kMaxLevels)
+        return fail(LL_EUNSUPPORTED, "%s: T=%d needs %d levels (max %d)", who, T, L, ll::kMaxLevels);
+    const size_t es = bf16 ? 2 : 4;
+    const size_t nq = (size_t)rows * dk * es, nv = (size_t)rows * dv * es, na = (size_t)rows * 4,
+                 nl = (size_t)rows * L * 4;
+    const void *ins[] = {q, k, v, dout};
+    const char *inames[] = {"q", "k", "v", "dout"};
+    void *outs[] = {dq, dk_out, dv_out};
+    const char *onames[] = {"dq", "dk", "dv"};
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i])
+            return fail(LL_EINVAL, "%s: %s is NULL", who, inames[i]);
+        if (!aligned(ins[i], 16))
+            return fail(LL_EINVAL, "%s: %s is not 16-byte aligned", who, inames[i]);
+    }
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i])
+            return fail(LL_EINVAL, "%s: %s is NULL", who, onames[i]);
+        if (!aligned(outs[i], 16))
+            return fail(LL_EINVAL, "%s: %s is not 16-byte aligned", who, onames[i]);
+    }
+    if (!a || !lambda || !da || !dlambda)
+        return fail(LL_EINVAL, "%s: a, lambda, da and dlambda must be non-NULL", who);
+    if (!aligned(a, 4) || !aligned(lambda, 4) || !aligned(da, 4) || !aligned(dlambda, 4))
+        return fail(LL_EINVAL, "%s: a, lambda, da and dlambda must be 4-byte aligned", who);
+    const ll::BwdPlan plan = ll::bwd_plan(B, H, T, dk, dv, chunk);
+    if (!workspace)
+        return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, plan.bytes);
+    if (workspace_bytes < plan.bytes)
+        return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, plan.bytes, workspace_bytes);
+    if (!aligned(workspace, 256))
+        return fail(LL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    // every output must be disjoint from every input, every other output and the workspace
+    const void *all[] = {q, k, v, dout, a, lambda, workspace, dq, dk_out, dv_out, da, dlambda};
+    const size_t sz[] = {nq, nq, nv, nv, na, nl, plan.bytes, nq, nq, nv, na, nl};
+    for (int i = 7; i < 12; ++i)
+        for (int j = 0; j < 12; ++j)
+            if (j != i && overlaps(all[i], sz[i], all[j], sz[j]))
+                return fail(LL_EINVAL, "%s: outputs must not alias each other, an input or the workspace", who);
+    if (overlaps(workspace, plan.bytes, q, nq) || overlaps(workspace, plan.bytes, k, nq) ||
+        overlaps(workspace, plan.bytes, v, nv) || overlaps(workspace, plan.bytes, dout, nv))
+        return fail(LL_EINVAL, "%s: workspace aliases an input", who);
+    ll::BwdArgs args{q, k, v, dout, a, lambda, dq, dk_out, dv_out, da, dlambda, B, H, T, dk, dv, chunk, L, bf16,
+                     workspace};
+    hipError_t e = ll::bwd_launch(args, plan, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return ok();
+}
+
 ll_status loglinear_decode_step(const void *q, const void *k, const void *v, const float *a, const float *lambda,
                                 float *state, float *logscale, const int64_t *pos, void *out, int S, int H, int dk,
                                 int dv, int Lcap, ll_dtype dtype, void *stream)

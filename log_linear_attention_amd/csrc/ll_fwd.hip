@@ -2174,6 +2174,8 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
                             (int64_t)A.T * A.L * 4 < ((int64_t)1 << 31);
         use_ws = A.L <= WS::NLV && fits32;
     }
+    if (A.tree_only)
+        use_ws = A.tree_nat;
     if (nat_blocks)
         *nat_blocks = use_ws;
     if (P.nL > 0) {
@@ -2220,6 +2222,8 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             ping ^= 1;
         }
     }
+    if (A.tree_only)
+        return hipSuccess;
     const ProfEvents pw = prof_events("ll_chunk_walk");
     if constexpr (F::TR && WS::FITS) {
         if (use_ws) {

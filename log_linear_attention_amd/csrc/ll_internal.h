@@ -31,6 +31,11 @@ struct FwdArgs {
     int B, H, T, dk, dv, chunk, L;
     bool bf16;
     void *workspace;
+    // Only the group states and the tree over groups (no chunk walk, q,
+    // lambda and out unused), with the block states in the natural dk order
+    // when tree_nat is set (bf16 only).
+    bool tree_only = false;
+    bool tree_nat = false;
 };
 
 // Profiling hook (implemented by the ABI layer): while profiling is on, a
@@ -76,6 +81,31 @@ struct StackArgs {
 };
 
 bool stack_supported(bool bf16, int dk, int dv);
+
+// Backward.  Gradients gq, gk, gv in the input dtype; ga [BH, T] and
+// glam [BH, T, L] fp32.
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *a, *lam;
+    void *gq, *gk, *gv;
+    float *ga, *glam;
+    int B, H, T, dk, dv, chunk, L;
+    bool bf16;
+    void *workspace;
+};
+
+// Workspace of the backward: the tree over chunks (one chunk per group) of
+// k, v; the forward that forms dq; the W pieces and sums; the in-chunk part
+// of da and the per-level pair masses of every chunk.
+struct BwdPlan {
+    FwdPlan tree, fq;
+    int NP = 0, NB = 0;
+    size_t off_tree = 0, off_fq = 0, off_wp = 0, off_w1 = 0, off_w2 = 0, off_pq = 0, off_mq = 0, off_mk = 0, bytes = 0;
+};
+
+BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk);
+bool bwd_supported(bool bf16, int dk, int dv, int chunk);
+hipError_t bwd_launch(const BwdArgs &args, const BwdPlan &plan, hipStream_t stream);
 hipError_t stack_launch(const StackArgs &args, hipStream_t stream);
 
 }  // namespace ll

@@ -85,6 +85,8 @@ def _load():
         lib.ll_oracle_bwd_qrows.restype = ctypes.c_int
         lib.ll_oracle_bwd_krows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, P, P]
         lib.ll_oracle_bwd_krows.restype = ctypes.c_int
+        lib.ll_oracle_da_window.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, I, P]
+        lib.ll_oracle_da_window.restype = ctypes.c_int
         lib.ll_oracle_num_threads.argtypes = []
         lib.ll_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -183,6 +185,22 @@ def bwd_rows(q, k, v, a, lam, do, qrows, krows):
     if rc != 0:
         raise ValueError(f"oracle bwd_rows failed (code {rc})")
     return {"dq": dq, "dlam": dlam, "dk": dkk, "dv": dvv}
+
+
+def da_window(q, k, v, a, lam, do, rows, W: int) -> np.ndarray:
+    """da at selected (b*H + h, r) rows (r >= 1) from the pairs s < r <= t
+    with both ends within W tokens of r (exact when W >= T)."""
+    q, k, v, a, lam, do = (_f64(x) for x in (q, k, v, a, lam, do))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    out = np.zeros(rows.shape[0])
+    rc = _load().ll_oracle_da_window(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam), _ptr(do), B * H, T, dk, dv, L,
+                                     rows.shape[0], _ptr(rows), int(W), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle da_window failed (code {rc})")
+    return out
 
 
 # ---------------------------------------------------------------------------

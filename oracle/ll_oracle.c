@@ -321,6 +321,58 @@ int ll_oracle_bwd_krows(const double *q, const double *k, const double *v, const
     return status;
 }
 
+/* da at selected positions from the pairs within W tokens of r:
+ * sum over s in [max(0, r-W), r) and t in [r, min(T, r+W)) of P(t,s), at
+ * the pairs' absolute positions (levels depend on them).  With W >= T this
+ * is the exact da_r; for long sequences the omitted pairs carry a decay of
+ * at least W consecutive a's, which the caller bounds.  rows[2i] = bh,
+ * rows[2i+1] = r (r >= 1). */
+int ll_oracle_da_window(const double *q, const double *k, const double *v, const double *a, const double *lam,
+                        const double *dout, int64_t BH, int64_t T, int64_t dk, int64_t dv, int64_t L,
+                        int64_t nrows, const int64_t *rows, int64_t W, double *out)
+{
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t bh = rows[2 * i], r = rows[2 * i + 1];
+        if (bh < 0 || bh >= BH || r < 1 || r >= T) {
+#pragma omp critical
+            status = -2;
+            continue;
+        }
+        const double *ah = a + bh * T;
+        const int64_t s0 = r - W > 0 ? r - W : 0, t1 = r + W < T ? r + W : T;
+        double total = 0.0;
+        for (int64_t t = r; t < t1; ++t) {
+            const double *qt = q + (bh * T + t) * dk;
+            const double *dot = dout + (bh * T + t) * dv;
+            double logdecay = 0.0; /* sum of a over (s, t] */
+            for (int64_t rr = r; rr <= t; ++rr)
+                logdecay += ah[rr];
+            for (int64_t s = r - 1; s >= s0; --s) {
+                if (s < r - 1)
+                    logdecay += ah[s + 1];
+                const int lev = ll_oracle_level(t, s);
+                if (lev >= L) {
+#pragma omp critical
+                    status = -1;
+                    break;
+                }
+                const double *ks = k + (bh * T + s) * dk;
+                const double *vs = v + (bh * T + s) * dv;
+                double qk = 0.0, dov = 0.0;
+                for (int64_t d = 0; d < dk; ++d)
+                    qk += qt[d] * ks[d];
+                for (int64_t e = 0; e < dv; ++e)
+                    dov += dot[e] * vs[e];
+                total += exp(logdecay) * lam[(bh * T + t) * L + lev] * qk * dov;
+            }
+        }
+        out[i] = total;
+    }
+    return status;
+}
+
 /* Number of threads OpenMP will use (reported with the CPU baseline). */
 int ll_oracle_num_threads(void)
 {

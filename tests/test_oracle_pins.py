@@ -468,3 +468,22 @@ def test_bwd_rows_match_full(oracle_mod):
         np.testing.assert_allclose(r["dlam"][i], g["dlam"][b, h, t], rtol=1e-13, atol=1e-13)
         np.testing.assert_allclose(r["dk"][i], g["dk"][b, h, t], rtol=1e-13, atol=1e-13)
         np.testing.assert_allclose(r["dv"][i], g["dv"][b, h, t], rtol=1e-13, atol=1e-13)
+
+
+def test_da_window_is_exact_with_full_window(oracle_mod):
+    rng = np.random.default_rng(62)
+    T, dk, dv = 37, 3, 2
+    L = _L(T)
+    q, k, v, a, lam = _rand_inputs(rng, 1, 2, T, dk, dv, L)
+    do = rng.standard_normal((1, 2, T, dv))
+    g = oracle_mod.bwd(q, k, v, a, lam, do)
+    rows = np.array([[0, 1], [0, 17], [1, 36], [1, 8]])
+    got = oracle_mod.da_window(q, k, v, a, lam, do, rows, W=T)
+    want = np.array([g["da"][0, bh, r] for bh, r in rows])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # a short window drops the far pairs: with a strong decay they are tiny
+    a_strong = a * 40.0
+    g2 = oracle_mod.bwd(q, k, v, a_strong, lam, do)
+    got2 = oracle_mod.da_window(q, k, v, a_strong, lam, do, rows, W=8)
+    want2 = np.array([g2["da"][0, bh, r] for bh, r in rows])
+    np.testing.assert_allclose(got2, want2, rtol=1e-6, atol=1e-9)
