@@ -282,6 +282,8 @@ ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float
     if (!ll::bwd_supported(bf16, dk, dv, chunk))
         return fail(LL_EUNSUPPORTED, "%s: no kernel for dtype=%s dk=%d dv=%d chunk=%d", who, bf16 ? "bf16" : "f32",
                     dk, dv, chunk);
+    if ((int64_t)B * H > 65535)
+        return fail(LL_EUNSUPPORTED, "%s: B*H above 65535", who);
     const int64_t rows = (int64_t)B * H * T;
     if (rows == 0)
         return ok();

@@ -58,13 +58,18 @@ struct Bw {
     static constexpr int LQ = DK + PAD, LV = DV + PAD, LC = C + PAD;
     static constexpr int CT = C / 16, DKT = DK / 16, DVT = DV / 16;
     static constexpr int NUK = DK / KB, NUV = DV / KB, NUC = C / KB;
-    static constexpr int NCG = 4 / CT;                    // column groups per token tile (4 waves)
+    // Chunk kernel: 8 waves when the dk and dv tiles split evenly over the
+    // column groups, else 4.
+    static constexpr int NW = (DKT % (8 / CT) == 0 && DVT % (8 / CT) == 0) ? 8 : 4;
+    static constexpr int NTC = 64 * NW;
+    static constexpr int NCG = NW / CT;                   // column groups per token tile
     static constexpr int KPW = DKT / NCG, VPW = DVT / NCG;  // dk / dv tiles per wave
     static constexpr int LOGC = C == 16 ? 4 : C == 32 ? 5 : 6;
     static constexpr int WP = 8;                          // chunks per W piece
     static constexpr int VEC = 16 / (int)sizeof(T);
     static_assert(C % KB == 0 && DK % KB == 0 && DV % KB == 0, "units");
     static_assert(CT >= 1 && CT <= 4 && 4 % CT == 0 && DKT % NCG == 0 && DVT % NCG == 0, "wave layout");
+    static_assert((C * kMaxLevels) % NTC == 0, "lambda staging");
 };
 
 template <class B>
@@ -79,13 +84,13 @@ struct BwSmem {
     __attribute__((aligned(16))) T PdT[B::C][B::LC];   // (M . dP)^T, [key][query]
     __attribute__((aligned(16))) T PsT[B::C][B::LC];   // (M . S)^T
     float G[B::C][B::C + 1];                            // exp(decay) S dP, [query][key]
-    float lam[B::C][kMaxLevels];
-    float dlam[B::C][kMaxLevels];
+    float lam[B::C][kMaxLevels + 1];                    // odd row stride: per-thread rows hit distinct banks
+    float dlam[B::C][kMaxLevels + 1];
     float Aloc[B::C];                                   // inclusive prefix of a inside the chunk
-    float part[4][B::C];                                // cross-wave row partial sums
+    float part[8][B::C];                                // cross-wave row partial sums
     float off[kMaxLevels];                              // per-level log-decay offsets (chunk totals)
     float km[kMaxLevels];                               // key-side pair mass of this chunk per level
-    float kw[4];
+    float kw[8];
     float u[B::C], w[B::C];                             // per-token terms of the in-chunk part of da
 };
 
@@ -110,26 +115,50 @@ __device__ __forceinline__ void put(T *p, float x)
     *p = from_f32<T>(x);
 }
 
-// Sum of the chunk log-decay totals gam[c0 .. c1) over one wave.
-__device__ __forceinline__ float wave_range_sum(const float *gam, int c0, int c1, int lane)
+// Store element e (a compile-time index after unrolling) of a 16-byte piece
+// as raw bits.
+__device__ __forceinline__ void store_elem(float *dst, const uint4 &u, int e)
 {
-    float x = 0.f;
-    for (int c = c0 + lane; c < c1; c += 64)
-        x += gam[c];
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        x += __shfl_xor(x, m, 64);
-    return x;
+    const uint32_t w = e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+    *reinterpret_cast<uint32_t *>(dst) = w;
+}
+
+__device__ __forceinline__ void store_elem(__bf16 *dst, const uint4 &u, int e)
+{
+    const uint32_t w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+    *reinterpret_cast<unsigned short *>(dst) = (unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// Four consecutive elements of LDS as floats (one 8- or 16-byte read).
+__device__ __forceinline__ floatx4 ld4(const float *p) { return *reinterpret_cast<const floatx4 *>(p); }
+
+__device__ __forceinline__ floatx4 ld4(const __bf16 *p)
+{
+    const bf16x4 y = *reinterpret_cast<const bf16x4 *>(p);
+    return floatx4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+}
+
+// Four consecutive elements from an accumulator (8- or 16-byte store).
+__device__ __forceinline__ void put4(float *p, const floatx4 &x)
+{
+    *reinterpret_cast<floatx4 *>(p) = x;
+}
+
+__device__ __forceinline__ void put4(__bf16 *p, const floatx4 &x)
+{
+    bf16x4 y;
+    y[0] = (__bf16)x[0]; y[1] = (__bf16)x[1]; y[2] = (__bf16)x[2]; y[3] = (__bf16)x[3];
+    *reinterpret_cast<bf16x4 *>(p) = y;
 }
 
 // ---------------------------------------------------------------------------
 // Chunk kernel: one workgroup per (head, chunk).
 // ---------------------------------------------------------------------------
 template <class B>
-__global__ __launch_bounds__(256) void ll_bwd_chunk(
+__global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     const typename B::T *__restrict__ q, const typename B::T *__restrict__ k, const typename B::T *__restrict__ v,
     const typename B::T *__restrict__ dout, const float *__restrict__ a, const float *__restrict__ lamg,
-    const typename B::T *__restrict__ Dg, const float *__restrict__ Gam, const typename B::T *__restrict__ W1,
+    const typename B::T *__restrict__ Dg, const double *__restrict__ Gp, const typename B::T *__restrict__ W1,
     const typename B::T *__restrict__ W2, typename B::T *__restrict__ dkg, typename B::T *__restrict__ dvg,
     float *__restrict__ dlamg, float *__restrict__ daloc, float *__restrict__ Mq, float *__restrict__ Mk, int Tlen,
     int L, int N, int nL, int nLeft, int NB)
@@ -144,31 +173,83 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
     const int nv = min(C, Tlen - t0);   // valid rows of this chunk
     const size_t row0 = (size_t)bh * Tlen + t0;
 
-    // ---- stage the chunk --------------------------------------------------
-    for (int i = tid; i < C * DK; i += B::NT) {
-        const int t = i / DK, d = i % DK;
-        const T zq = t < nv ? q[(row0 + t) * DK + d] : from_f32<T>(0.f);
-        const T zk = t < nv ? k[(row0 + t) * DK + d] : from_f32<T>(0.f);
-        sm.Qs[t][d] = zq;
-        sm.QsT[d][t] = zq;
-        sm.Ks[t][d] = zk;
+    const int mtop = bitlen_u32((uint32_t)(N - 1));
+
+    // ---- stage the chunk: 16-byte pieces, every load issued first ------------
+    constexpr int VEC = B::VEC, QP = C * DK / VEC, VP = C * DV / VEC;
+    constexpr int NQP = (QP + B::NTC - 1) / B::NTC, NVP = (VP + B::NTC - 1) / B::NTC;
+    uint4 rq[NQP], rk[NQP], rv[NVP], ro[NVP];
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < NQP; ++j) {
+        const int i = tid + B::NTC * j, t = i / (DK / VEC);
+        const bool ok = i < QP && t < nv;
+        rq[j] = z4;
+        rk[j] = z4;
+        if (ok) {
+            rq[j] = *reinterpret_cast<const uint4 *>(q + row0 * DK + (size_t)i * VEC);
+            rk[j] = *reinterpret_cast<const uint4 *>(k + row0 * DK + (size_t)i * VEC);
+        }
     }
-    for (int i = tid; i < C * DV; i += B::NT) {
-        const int t = i / DV, e = i % DV;
-        const T zv = t < nv ? v[(row0 + t) * DV + e] : from_f32<T>(0.f);
-        const T zo = t < nv ? dout[(row0 + t) * DV + e] : from_f32<T>(0.f);
-        sm.Vs[t][e] = zv;
-        sm.dOs[t][e] = zo;
-        sm.dOsT[e][t] = zo;
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+        const int i = tid + B::NTC * j, t = i / (DV / VEC);
+        const bool ok = i < VP && t < nv;
+        rv[j] = z4;
+        ro[j] = z4;
+        if (ok) {
+            rv[j] = *reinterpret_cast<const uint4 *>(v + row0 * DV + (size_t)i * VEC);
+            ro[j] = *reinterpret_cast<const uint4 *>(dout + row0 * DV + (size_t)i * VEC);
+        }
     }
-    for (int i = tid; i < C * B::LC; i += B::NT) {
-        (&sm.PdT[0][0])[i] = from_f32<T>(0.f);
-        (&sm.PsT[0][0])[i] = from_f32<T>(0.f);
+#pragma unroll
+    for (int j = 0; j < NQP; ++j) {
+        const int i = tid + B::NTC * j;
+        if (i < QP) {
+            const int t = i / (DK / VEC), d0 = (i % (DK / VEC)) * VEC;
+            *reinterpret_cast<uint4 *>(&sm.Qs[t][d0]) = rq[j];
+            *reinterpret_cast<uint4 *>(&sm.Ks[t][d0]) = rk[j];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                store_elem(&sm.QsT[d0 + e][t], rq[j], e);
+        }
     }
-    for (int i = tid; i < C * kMaxLevels; i += B::NT) {
-        const int t = i / kMaxLevels, l = i % kMaxLevels;
-        sm.lam[t][l] = (t < nv && l < L) ? lamg[(row0 + t) * L + l] : 0.f;
-        sm.dlam[t][l] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NVP; ++j) {
+        const int i = tid + B::NTC * j;
+        if (i < VP) {
+            const int t = i / (DV / VEC), e0 = (i % (DV / VEC)) * VEC;
+            *reinterpret_cast<uint4 *>(&sm.Vs[t][e0]) = rv[j];
+            *reinterpret_cast<uint4 *>(&sm.dOs[t][e0]) = ro[j];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                store_elem(&sm.dOsT[e0 + e][t], ro[j], e);
+        }
+    }
+    for (int i = tid; i < C * B::LC * (int)sizeof(T) / 16; i += B::NTC) {
+        reinterpret_cast<uint4 *>(&sm.PdT[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4 *>(&sm.PsT[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // lambda rows of the chunk are contiguous: C*L floats, loaded together
+    {
+        constexpr int NLL = C * kMaxLevels / B::NTC;
+        float lv[NLL];
+#pragma unroll
+        for (int j = 0; j < NLL; ++j) {
+            const int i = tid + B::NTC * j;
+            lv[j] = i < nv * L ? lamg[row0 * L + i] : 0.f;
+        }
+        for (int i = tid; i < C * (kMaxLevels + 1); i += B::NTC) {
+            (&sm.lam[0][0])[i] = 0.f;
+            (&sm.dlam[0][0])[i] = 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NLL; ++j) {
+            const int i = tid + B::NTC * j;
+            if (i < nv * L)
+                sm.lam[i / L][i % L] = lv[j];
+        }
     }
     if (tid < kMaxLevels)
         sm.km[tid] = 0.f;
@@ -190,7 +271,7 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
     __syncthreads();
 
     // ---- in-chunk scores: S = Q K^T, dP = dO V^T, causal tile pairs ---------
-    for (int pr = wv; pr < B::CT * (B::CT + 1) / 2; pr += 4) {
+    for (int pr = wv; pr < B::CT * (B::CT + 1) / 2; pr += B::NW) {
         int tt = 0, rem = pr;
         while (rem > tt) {
             rem -= tt + 1;
@@ -227,7 +308,7 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
     __syncthreads();
 
     // ---- in-chunk levels of dlambda: row sums of G over each level's keys ----
-    for (int task = tid; task < C * (B::LOGC + 1); task += B::NT) {
+    for (int task = tid; task < C * (B::LOGC + 1); task += B::NTC) {
         const int t = task / (B::LOGC + 1), lev = task % (B::LOGC + 1);
         float x = 0.f;
         if (lev == 0) {
@@ -267,25 +348,29 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
     // ---- chunk levels -------------------------------------------------------
     // pki: this lane's part of k_s . (dk_s from later chunks), fp32
     float pki = 0.f;
-    const int mtop = bitlen_u32((uint32_t)(N - 1));
-    const float *gam = Gam + (size_t)bh * N;   // chunk log-decay totals (chunks < N-1)
+    // Per level: the log-decay between this chunk and the other block, from
+    // the fp64 prefix of chunk totals (query side: from the left block's end
+    // to this chunk's start; key side: from this chunk's end to R's start).
+    if (tid >= 1 && tid <= mtop) {
+        const int m = tid, half = 1 << (m - 1), b0 = (c >> m) << m;
+        const double *gp = Gp + (size_t)bh * N;
+        double o = 0.0;
+        if ((c >> (m - 1)) & 1)
+            o = gp[c] - gp[b0 + half];
+        else if (b0 + half < N)
+            o = gp[b0 + half] - gp[c + 1];
+        sm.off[m] = (float)o;
+    }
     for (int m = 1; m <= mtop; ++m) {
-        const int half = 1 << (m - 1);
-        const int b0 = (c >> m) << m;
         if ((c >> (m - 1)) & 1) {
-            // query side: the left block [b0, b0 + half) -> dlambda level LOGC + m
-            __syncthreads();
-            if (wv == 0) {
-                const float o = wave_range_sum(gam, b0 + half, c, lane);
-                if (lane == 0)
-                    sm.off[0] = o;
-            }
-            __syncthreads();
-            const float offB = sm.off[0];   // log-decay from the block's end to the chunk start
+            // query side: the left block [b0, b0 + half) is a stored block
+            // state -> dlambda level LOGC + m
             size_t offp = 0;
             for (int r = 0; r < m - 1; ++r)
                 offp += ((nL >> r) + 1) >> 1;
             const T *blk = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
+            __syncthreads();
+            const float offB = sm.off[m];   // log-decay from the block's end to the chunk start
             // X^T = D^T Q^T: A = D^T (rows e), B = Q (columns t); this wave
             // takes query tile kt and value tiles cg, cg + NCG, ...
             float xs = 0.f;
@@ -297,9 +382,10 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
                 for (int u = 0; u < B::NUK; ++u)
                     mma_unit(X, gfrag<B, B::NUK>(blk, et, u, lane), frag<B>(&sm.Qs[0][0], B::LQ, 16 * kt + li, u, qd));
                 // X[i] = (Q D)[t = 16 kt + li][e = 16 et + 4 qd + i]
+                const floatx4 o4 = ld4(&sm.dOs[16 * kt + li][16 * et + 4 * qd]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    xs += X[i] * to_f32(sm.dOs[16 * kt + li][16 * et + 4 * qd + i]);
+                    xs += X[i] * o4[i];
             }
             // reduce over the four lane quads (the e rows), then over column groups
             xs += __shfl_xor(xs, 16, 64);
@@ -313,24 +399,18 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
                     x += sm.part[g2][tid];
                 sm.dlam[tid][B::LOGC + m] = __expf(sm.Aloc[tid] + offB) * x;
             }
-        } else if (b0 + half < N) {
-            // key side: the right block R = [b0 + half, b0 + 2 half) sees this chunk at level m
-            __syncthreads();
-            if (wv == 0) {
-                const float o = wave_range_sum(gam, c + 1, b0 + half, lane);
-                if (lane == 0)
-                    sm.off[0] = o;
-            }
-            __syncthreads();
-            const float offR = sm.off[0];   // log-decay from the chunk's end to R's start
+        } else if (((c >> m) << m) + (1 << (m - 1)) < N) {
+            // key side: the right block R sees this chunk at level m
             size_t ob = 0;
             for (int r = 1; r < m; ++r) {
                 const int hr = 1 << (r - 1);
                 ob += N > hr ? (N - hr + (1 << r) - 1) >> r : 0;
             }
             const size_t wi = (size_t)bh * NB + ob + (c >> m);
-            const T *w1 = W1 + wi * DK * DV;   // W^T operand: k = dv, n = dk
-            const T *w2 = W2 + wi * DK * DV;   // W operand:   k = dk, n = dv
+            const T *w1 = W1 + wi * DK * DV;   // W,   [dk][dv]
+            const T *w2 = W2 + wi * DK * DV;   // W^T, [dv][dk]
+            __syncthreads();
+            const float offR = sm.off[m];   // log-decay from the chunk's end to R's start
             // this wave's key rows: decay exp(A_e - A_s)
             const float dec = __expf(sm.Aloc[C - 1] - sm.Aloc[16 * kt + li] + offR);
             float km = 0.f;   // this lane's part of the level's key-side pair mass
@@ -340,11 +420,12 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
                 floatx4 X = zero4();
 #pragma unroll
                 for (int u = 0; u < B::NUV; ++u)
-                    mma_unit(X, gfrag<B, B::NUV>(w1, dt, u, lane), frag<B>(&sm.Vs[0][0], B::LV, 16 * kt + li, u, qd));
+                    mma_unit(X, frag<B>(w1, DV, 16 * dt + li, u, qd), frag<B>(&sm.Vs[0][0], B::LV, 16 * kt + li, u, qd));
                 dK[j] += dec * X;
+                const floatx4 k4 = ld4(&sm.Ks[16 * kt + li][16 * dt + 4 * qd]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    km += dec * X[i] * to_f32(sm.Ks[16 * kt + li][16 * dt + 4 * qd + i]);
+                    km += dec * X[i] * k4[i];
             }
 #pragma unroll
             for (int j = 0; j < B::VPW; ++j) {
@@ -352,7 +433,7 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
                 floatx4 X = zero4();
 #pragma unroll
                 for (int u = 0; u < B::NUK; ++u)
-                    mma_unit(X, gfrag<B, B::NUK>(w2, et, u, lane), frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
+                    mma_unit(X, frag<B>(w2, DK, 16 * et + li, u, qd), frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
                 dV[j] += dec * X;
             }
             pki += km;
@@ -363,8 +444,12 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
             if (lane == 0)
                 sm.kw[wv] = km;
             __syncthreads();
-            if (tid == 0)
-                sm.km[m] = sm.kw[0] + sm.kw[1] + sm.kw[2] + sm.kw[3];
+            if (tid == 0) {
+                float x = 0.f;
+                for (int w2 = 0; w2 < B::NW; ++w2)
+                    x += sm.kw[w2];
+                sm.km[m] = x;
+            }
         }
     }
     __syncthreads();
@@ -373,49 +458,46 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
     // dk, dv: this wave's key tile kt, column tiles; rows are keys s = 16 kt + li
     const int s = 16 * kt + li;
     float pk = pki;
+    if (s < nv) {
 #pragma unroll
-    for (int j = 0; j < B::KPW; ++j) {
-        const int dt = cg + B::NCG * j;
+        for (int j = 0; j < B::KPW; ++j)
+            put4(&dkg[(row0 + s) * DK + 16 * (cg + B::NCG * j) + 4 * qd], dK[j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = 16 * dt + 4 * qd + i;
-            if (s < nv)
-                put(&dkg[(row0 + s) * DK + d], dK[j][i]);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < B::VPW; ++j) {
-        const int et = cg + B::NCG * j;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 16 * et + 4 * qd + i;
-            if (s < nv)
-                put(&dvg[(row0 + s) * DV + e], dV[j][i]);
-        }
+        for (int j = 0; j < B::VPW; ++j)
+            put4(&dvg[(row0 + s) * DV + 16 * (cg + B::NCG * j) + 4 * qd], dV[j]);
     }
     pk += __shfl_xor(pk, 16, 64);
     pk += __shfl_xor(pk, 32, 64);
     if (qd == 0)
         sm.part[cg][s] = pk;
     __syncthreads();
-    if (tid < C) {
+    {
         // da inside the chunk, for r = t0 + i:
         //   sum_{t >= r} (sum of P(t, s) over s <= t) - sum_{s >= r} (in-chunk P(., s))
         //   + sum_{s < r} (P(., s) over later chunks)
         // The in-chunk sums of both sides come from the same fp32 products.
-        float pki_in = 0.f;
-        for (int t = tid; t < C; ++t) {
-            const int lev = t == tid ? 0 : bitlen_u32((uint32_t)(t ^ tid));
-            pki_in += sm.lam[t][lev] * sm.G[t][tid];
+        // Four threads per token (quarters of the key / level ranges).
+        const int tk = tid >> 2, qq = tid & 3;
+        float pki_in = 0.f, pq = 0.f;
+        if (tk < C) {
+            for (int t = tk + qq; t < C; t += 4) {
+                const int lev = t == tk ? 0 : bitlen_u32((uint32_t)(t ^ tk));
+                pki_in += sm.lam[t][lev] * sm.G[t][tk];
+            }
+            for (int l = qq; l < kMaxLevels; l += 4)
+                pq += sm.lam[tk][l] * sm.dlam[tk][l];
         }
-        float pkx = 0.f;
-        for (int g2 = 0; g2 < B::NCG; ++g2)
-            pkx += sm.part[g2][tid];
-        float pq = 0.f;
-        for (int l = 0; l < kMaxLevels; ++l)
-            pq += sm.lam[tid][l] * sm.dlam[tid][l];
-        sm.u[tid] = pq - pki_in;
-        sm.w[tid] = pkx;
+        pki_in += __shfl_xor(pki_in, 1, 64);
+        pki_in += __shfl_xor(pki_in, 2, 64);
+        pq += __shfl_xor(pq, 1, 64);
+        pq += __shfl_xor(pq, 2, 64);
+        if (tk < C && qq == 0) {
+            float pkx = 0.f;
+            for (int g2 = 0; g2 < B::NCG; ++g2)
+                pkx += sm.part[g2][tk];
+            sm.u[tk] = pq - pki_in;
+            sm.w[tk] = pkx;
+        }
     }
     __syncthreads();
     if (wv == 0) {
@@ -433,24 +515,24 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
         pw -= lane < C ? sm.w[lane] : 0.f;
         if (lane < nv)
             daloc[row0 + lane] = su + pw;
-        // pair masses of this chunk per level (query side: into its left
-        // block; key side: from its right block), for the pairs that jump
-        // over other chunks
-        for (int m = 1; m <= mtop; ++m) {
-            float x = 0.f;
-            if ((c >> (m - 1)) & 1)
-                for (int t = lane; t < C; t += 64)
-                    x += sm.lam[t][B::LOGC + m] * sm.dlam[t][B::LOGC + m];
+    }
+    // pair masses of this chunk per level (query side: into its left block;
+    // key side: from its right block), for the pairs that jump over other
+    // chunks; wave w takes levels w+1, w+1+NW, ...
+    for (int m = 1 + wv; m <= mtop; m += B::NW) {
+        float x = 0.f;
+        if ((c >> (m - 1)) & 1)
+            for (int t = lane; t < C; t += 64)
+                x += sm.lam[t][B::LOGC + m] * sm.dlam[t][B::LOGC + m];
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1)
-                x += __shfl_xor(x, o, 64);
-            if (lane == 0) {
-                Mq[((size_t)bh * kMaxLevels + m) * (N + 1) + c] = x;
-                Mk[((size_t)bh * kMaxLevels + m) * (N + 1) + c] = sm.km[m];
-            }
+        for (int o = 32; o >= 1; o >>= 1)
+            x += __shfl_xor(x, o, 64);
+        if (lane == 0) {
+            Mq[((size_t)bh * kMaxLevels + m) * (N + 1) + c] = x;
+            Mk[((size_t)bh * kMaxLevels + m) * (N + 1) + c] = sm.km[m];
         }
     }
-    for (int i = tid; i < nv * L; i += B::NT) {
+    for (int i = tid; i < nv * L; i += B::NTC) {
         const int t = i / L, l = i % L;
         dlamg[(row0 + t) * L + l] = sm.dlam[t][l];
     }
@@ -458,16 +540,20 @@ __global__ __launch_bounds__(256) void ll_bwd_chunk(
 
 // ---------------------------------------------------------------------------
 // W pieces: for level m, right block R = [j 2^m + 2^(m-1), (j+1) 2^m) and its
-// piece pi (chunks R0 + pi*WP ..), the partial sum over the piece's queries of
-// exp(A_t - A_e) lambda_t[LOGC + m] q_t do_t^T, e = R0*C - 1, fp32 row-major
-// [dk][dv].  Grid: (pieces of all levels, BH).
+// piece pi (chunks R0 + pi*WP ..), the sum over the piece's queries of
+// exp(A_t - A_e) lambda_t[LOGC + m] q_t do_t^T, e = R0*C - 1.  A block of a
+// single piece writes W ([dk][dv]) and W^T ([dv][dk]) in the input dtype
+// directly; otherwise the piece goes out as an fp32 partial for ll_bwd_wsum.
+// Grid: (pieces of all levels, BH).
 // ---------------------------------------------------------------------------
 template <class B>
 struct WpSmem {
     using T = typename B::T;
     __attribute__((aligned(16))) T QwT[B::DK][B::LC];   // weighted q, [dk][token]
     __attribute__((aligned(16))) T dOT[B::DV][B::LC];   // do, [dv][token]
+    __attribute__((aligned(16))) float Wt[B::DK][B::DV + 4];   // the result, for coalesced stores
     float Aloc[B::C];
+    float wt[B::C];                                     // per-token weights
     float off;
 };
 
@@ -477,20 +563,35 @@ __device__ __forceinline__ int wnblk(int N, int m)
     return N > h ? (N - h + (1 << m) - 1) >> m : 0;
 }
 
+// Write an fp32 [DK][DV] tile from LDS as W (row-major, T) and W^T.
+template <class B>
+__device__ __forceinline__ void write_w(const float (*Wt)[B::DV + 4], typename B::T *w1, typename B::T *w2, int tid)
+{
+    for (int i = tid; i < B::DK * B::DV; i += B::NT) {
+        const int d = i / B::DV, e = i % B::DV;
+        put(&w1[i], Wt[d][e]);
+    }
+    for (int i = tid; i < B::DK * B::DV; i += B::NT) {
+        const int e = i / B::DK, d = i % B::DK;
+        put(&w2[i], Wt[d][e]);
+    }
+}
+
 template <class B>
 __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__restrict__ q,
                                                      const typename B::T *__restrict__ dout,
                                                      const float *__restrict__ a, const float *__restrict__ lamg,
-                                                     const float *__restrict__ Gam, float *__restrict__ Wp, int Tlen,
-                                                     int L, int N, int NP)
+                                                     const double *__restrict__ Gp, float *__restrict__ Wp,
+                                                     typename B::T *__restrict__ W1, typename B::T *__restrict__ W2,
+                                                     int Tlen, int L, int N, int NP, int NB)
 {
     using T = typename B::T;
-    constexpr int C = B::C, DK = B::DK, DV = B::DV;
+    constexpr int C = B::C, DK = B::DK, DV = B::DV, VEC = B::VEC;
     __shared__ WpSmem<B> sm;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, qd = lane >> 4;
     const int bh = blockIdx.y;
     // decode (m, block j, piece pi) from the piece index
-    int x = blockIdx.x, m = 1;
+    int x = blockIdx.x, m = 1, bbase = 0;
     const int mtop = bitlen_u32((uint32_t)(N - 1));
     int nb = 0, np = 0;
     for (; m <= mtop; ++m) {
@@ -499,13 +600,12 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
         if (x < nb * np)
             break;
         x -= nb * np;
+        bbase += nb;
     }
-    float *dst = Wp + ((size_t)bh * NP + blockIdx.x) * DK * DV;
     const int j = x / np, pi = x % np;
     const int half = 1 << (m - 1);
     const int R0 = j * (1 << m) + half;
     const int cA = R0 + pi * B::WP, cB = min(min(cA + B::WP, R0 + half), N);
-    const float *gam = Gam + (size_t)bh * N;
     // every wave owns dk tiles wv, wv+4, .. x all dv tiles
     constexpr int KT = (B::DKT + 3) / 4;
     floatx4 acc[KT][B::DVT];
@@ -514,43 +614,88 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
 #pragma unroll
         for (int e = 0; e < B::DVT; ++e)
             acc[r][e] = zero4();
-    if (wv == 0) {
-        const float o = wave_range_sum(gam, R0, cA, lane);
-        if (lane == 0)
-            sm.off = o;
-    }
-    __syncthreads();
-    float off = sm.off;   // log-decay from e to the current chunk's start
-    for (int cc = cA; cc < cB; ++cc) {
+    // log-decay from e to the current chunk's start
+    float off = cA < N ? (float)(Gp[(size_t)bh * N + cA] - Gp[(size_t)bh * N + R0]) : 0.f;
+    constexpr int QP = C * DK / VEC, VP = C * DV / VEC;
+    constexpr int NQP = (QP + B::NT - 1) / B::NT, NVP = (VP + B::NT - 1) / B::NT;
+    // Loads of a chunk (q, do, and a, lambda for wave 0) go into registers one
+    // chunk ahead: issued right after the previous chunk is staged, so their
+    // latency overlaps that chunk's products.
+    uint4 rq[NQP], ro[NVP];
+    float av, lv;
+    auto issue = [&](int cc) {
         const int t0 = cc * C, nv = min(C, Tlen - t0);
         const size_t row0 = (size_t)bh * Tlen + t0;
-        __syncthreads();
-        if (wv == 0) {
-            for (int base = 0; base < C; base += 64) {
-                float y = (base + lane < nv) ? a[row0 + base + lane] : 0.f;
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float z = __shfl_up(y, d, 64);
-                    if (lane >= d)
-                        y += z;
-                }
-                const float carry = base > 0 ? sm.Aloc[base - 1] : 0.f;
-                if (base + lane < C)
-                    sm.Aloc[base + lane] = y + carry;
+        for (int jj = 0; jj < NQP; ++jj) {
+            const int i = tid + B::NT * jj;
+            rq[jj] = z4;
+            if (i < QP && i / (DK / VEC) < nv)
+                rq[jj] = *reinterpret_cast<const uint4 *>(q + row0 * DK + (size_t)i * VEC);
+        }
+#pragma unroll
+        for (int jj = 0; jj < NVP; ++jj) {
+            const int i = tid + B::NT * jj;
+            ro[jj] = z4;
+            if (i < VP && i / (DV / VEC) < nv)
+                ro[jj] = *reinterpret_cast<const uint4 *>(dout + row0 * DV + (size_t)i * VEC);
+        }
+        av = 0.f;
+        lv = 0.f;
+        if (wv == 0 && lane < nv) {
+            av = a[row0 + lane];
+            lv = lamg[(row0 + lane) * L + B::LOGC + m];
+        }
+    };
+    static_assert(C <= 64, "one wave scans a chunk");
+    if (cA < cB)
+        issue(cA);
+    for (int cc = cA; cc < cB; ++cc) {
+        __syncthreads();   // the previous chunk's products are done with the tiles
+        if (wv == 0) {
+            float y = av;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const float z = __shfl_up(y, d, 64);
+                if (lane >= d)
+                    y += z;
+            }
+            if (lane < C) {
+                sm.Aloc[lane] = y;
+                sm.wt[lane] = __expf(off + y) * lv;   // lv is 0 past the end
             }
         }
         __syncthreads();
-        for (int i = tid; i < C * DK; i += B::NT) {
-            const int t = i / DK, d = i % DK;
-            float w = 0.f;
-            if (t < nv)
-                w = __expf(off + sm.Aloc[t]) * lamg[(row0 + t) * L + B::LOGC + m] * to_f32(q[(row0 + t) * DK + d]);
-            put(&sm.QwT[d][t], w);
+#pragma unroll
+        for (int jj = 0; jj < NQP; ++jj) {
+            const int i = tid + B::NT * jj;
+            if (i < QP) {
+                const int t = i / (DK / VEC), d0 = (i % (DK / VEC)) * VEC;
+                const float w = sm.wt[t];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const uint32_t wd = (VEC == 8) ? ((e >> 1) == 0 ? rq[jj].x : (e >> 1) == 1 ? rq[jj].y
+                                                      : (e >> 1) == 2 ? rq[jj].z : rq[jj].w)
+                                                   : (e == 0 ? rq[jj].x : e == 1 ? rq[jj].y : e == 2 ? rq[jj].z : rq[jj].w);
+                    const float xv = (VEC == 8) ? __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16))
+                                                : __uint_as_float(wd);
+                    put(&sm.QwT[d0 + e][t], w * xv);
+                }
+            }
         }
-        for (int i = tid; i < C * DV; i += B::NT) {
-            const int t = i / DV, e = i % DV;
-            sm.dOT[e][t] = t < nv ? dout[(row0 + t) * DV + e] : from_f32<T>(0.f);
+#pragma unroll
+        for (int jj = 0; jj < NVP; ++jj) {
+            const int i = tid + B::NT * jj;
+            if (i < VP) {
+                const int t = i / (DV / VEC), e0 = (i % (DV / VEC)) * VEC;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    store_elem(&sm.dOT[e0 + e][t], ro[jj], e);
+            }
         }
+        if (cc + 1 < cB)
+            issue(cc + 1);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < B::NUC; ++u) {
@@ -576,17 +721,26 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
             for (int e = 0; e < B::DVT; ++e)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dst[(size_t)(16 * dt + 4 * qd + i) * DV + 16 * e + li] = acc[r][e][i];
+                    sm.Wt[16 * dt + 4 * qd + i][16 * e + li] = acc[r][e][i];
+    }
+    __syncthreads();
+    if (np == 1) {
+        const size_t wi = (size_t)bh * NB + bbase + j;
+        write_w<B>(sm.Wt, W1 + wi * DK * DV, W2 + wi * DK * DV, tid);
+    } else {
+        float *dst = Wp + ((size_t)bh * NP + blockIdx.x) * DK * DV;
+        for (int i = tid; i < DK * DV; i += B::NT)
+            dst[i] = sm.Wt[i / DV][i % DV];
     }
 }
 
-// Sum of a block's pieces, written as the two operand layouts of the chunk
-// kernel: W1 (k = dv, n = dk) and W2 (k = dk, n = dv), fragment order.
+// Sum of a multi-piece block's partials, written as W and W^T.
 template <class B>
 __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp, typename B::T *__restrict__ W1,
                                                    typename B::T *__restrict__ W2, int N, int NP, int NB)
 {
-    constexpr int DK = B::DK, DV = B::DV, KB = B::KB, EPL = B::EPL;
+    constexpr int DK = B::DK, DV = B::DV;
+    __shared__ __attribute__((aligned(16))) float Wt[DK][DV + 4];
     const int bh = blockIdx.y;
     int x = blockIdx.x, m = 1, pbase = 0;
     const int mtop = bitlen_u32((uint32_t)(N - 1));
@@ -599,6 +753,8 @@ __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp,
         x -= nb;
         pbase += nb * np;
     }
+    if (np == 1)
+        return;   // written by its only piece
     const int j = x, half = 1 << (m - 1);
     const int R0 = j * (1 << m) + half;
     int npv = 0;   // pieces that start inside the sequence
@@ -606,23 +762,87 @@ __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp,
         if (R0 + pi * B::WP < N)
             npv = pi + 1;
     const float *src = Wp + ((size_t)bh * NP + pbase + (size_t)j * np) * DK * DV;
-    typename B::T *w1 = W1 + ((size_t)bh * NB + blockIdx.x) * DK * DV;
-    typename B::T *w2 = W2 + ((size_t)bh * NB + blockIdx.x) * DK * DV;
-    for (int i = threadIdx.x; i < DK * DV; i += 256) {
-        const int d = i / DV, e = i % DV;
-        float s = 0.f;
-        for (int pi = 0; pi < npv; ++pi)
-            s += src[(size_t)pi * DK * DV + i];
-        {   // W2: k = d, n = e
-            const int u = d / KB, xk = d % KB, qd = xk / EPL, ee = xk % EPL;
-            const int fv = ((e >> 4) * (DK / KB) + u) * 64 + qd * 16 + (e & 15);
-            put(&w2[(size_t)fv * EPL + ee], s);
+    constexpr int PER = DK * DV / 256;   // elements per thread, 16-byte pieces
+    static_assert(PER % 4 == 0, "thread layout");
+    float4 acc[PER / 4];
+#pragma unroll
+    for (int r = 0; r < PER / 4; ++r)
+        acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int pi = 0; pi < npv; ++pi) {
+        const float4 *sp = reinterpret_cast<const float4 *>(src + (size_t)pi * DK * DV);
+#pragma unroll
+        for (int r = 0; r < PER / 4; ++r) {
+            const float4 x = sp[threadIdx.x + 256 * r];
+            acc[r].x += x.x; acc[r].y += x.y; acc[r].z += x.z; acc[r].w += x.w;
         }
-        {   // W1: k = e, n = d
-            const int u = e / KB, xk = e % KB, qd = xk / EPL, ee = xk % EPL;
-            const int fv = ((d >> 4) * (DV / KB) + u) * 64 + qd * 16 + (d & 15);
-            put(&w1[(size_t)fv * EPL + ee], s);
-        }
+    }
+#pragma unroll
+    for (int r = 0; r < PER / 4; ++r) {
+        const int i = 4 * (threadIdx.x + 256 * r);
+        Wt[i / DV][i % DV] = acc[r].x;
+        Wt[i / DV][i % DV + 1] = acc[r].y;
+        Wt[i / DV][i % DV + 2] = acc[r].z;
+        Wt[i / DV][i % DV + 3] = acc[r].w;
+    }
+    __syncthreads();
+    const size_t wi = (size_t)bh * NB + blockIdx.x;
+    write_w<B>(Wt, W1 + wi * DK * DV, W2 + wi * DK * DV, threadIdx.x);
+}
+
+// fp64 exclusive prefix of the chunk log-decay totals: Gp[c] = sum of
+// gam[c'] over c' < c, c in [0, N) (gam is defined for the first N-1 chunks).
+// One workgroup per head.
+__global__ __launch_bounds__(256) void ll_bwd_gprefix(const float *__restrict__ Gam, double *__restrict__ Gp, int N)
+{
+    __shared__ double sums[256];
+    const int tid = threadIdx.x, bh = blockIdx.x;
+    const float *g = Gam + (size_t)bh * N;
+    double *o = Gp + (size_t)bh * N;
+    const int per = (N + 255) / 256;
+    const int lo = min(N, tid * per), hi = min(N, lo + per);
+    double x = 0.0;
+    for (int c = lo; c < hi; ++c)
+        x += c < N - 1 ? (double)g[c] : 0.0;
+    sums[tid] = x;
+    __syncthreads();
+    double b = 0.0;
+    for (int j = 0; j < tid; ++j)
+        b += sums[j];
+    for (int c = lo; c < hi; ++c) {
+        o[c] = b;
+        b += c < N - 1 ? (double)g[c] : 0.0;
+    }
+}
+
+// Exclusive prefix sums over chunks of the per-level pair masses, in place:
+// one workgroup per (level, head).
+__global__ __launch_bounds__(256) void ll_bwd_mscan(float *__restrict__ Mq, float *__restrict__ Mk, int N)
+{
+    __shared__ float sums[2][256];
+    const int tid = threadIdx.x, m = blockIdx.x + 1, bh = blockIdx.y;
+    float *q = Mq + ((size_t)bh * kMaxLevels + m) * (N + 1);
+    float *k = Mk + ((size_t)bh * kMaxLevels + m) * (N + 1);
+    const int per = (N + 1 + 255) / 256;
+    const int lo = min(N + 1, tid * per), hi = min(N + 1, lo + per);
+    float xq = 0.f, xk = 0.f;
+    for (int x = lo; x < hi; ++x) {
+        xq += x < N ? q[x] : 0.f;
+        xk += x < N ? k[x] : 0.f;
+    }
+    sums[0][tid] = xq;
+    sums[1][tid] = xk;
+    __syncthreads();
+    float bq = 0.f, bk = 0.f;
+    for (int jj = 0; jj < tid; ++jj) {
+        bq += sums[0][jj];
+        bk += sums[1][jj];
+    }
+    for (int x = lo; x < hi; ++x) {
+        const float vq = x < N ? q[x] : 0.f, vk = x < N ? k[x] : 0.f;
+        q[x] = bq;
+        k[x] = bk;
+        bq += vq;
+        bk += vk;
     }
 }
 
@@ -630,61 +850,29 @@ __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp,
 // at every chunk level m the chunk c lies in one of the two sibling blocks
 // B (left) and R (right) of the pair set of that level, and the jumping pairs
 // are R's queries after c into B (query-side masses Mq) or B's keys before c
-// seen from R (key-side masses Mk).  One workgroup per head; the masses are
-// turned into exclusive prefix sums over chunks in place, level by level.
-__global__ __launch_bounds__(256) void ll_bwd_da(const float *__restrict__ daloc, float *__restrict__ Mq,
-                                                 float *__restrict__ Mk, float *__restrict__ da, int Tlen, int N,
+// seen from R (key-side masses Mk), read from the prefix sums.  One thread per
+// position.
+__global__ __launch_bounds__(256) void ll_bwd_da(const float *__restrict__ daloc, const float *__restrict__ Mq,
+                                                 const float *__restrict__ Mk, float *__restrict__ da, int Tlen, int N,
                                                  int C, int mtop)
 {
-    __shared__ float sums[2][256];
-    const int tid = threadIdx.x, bh = blockIdx.x;
-    const int per = (N + 1 + 255) / 256;
+    const int bh = blockIdx.y;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= Tlen)
+        return;
+    const int c = r / C;
+    float X = 0.f;
     for (int m = 1; m <= mtop; ++m) {
-        float *q = Mq + ((size_t)bh * kMaxLevels + m) * (N + 1);
-        float *k = Mk + ((size_t)bh * kMaxLevels + m) * (N + 1);
-        const int lo = min(N + 1, tid * per), hi = min(N + 1, lo + per);
-        float xq = 0.f, xk = 0.f;
-        for (int x = lo; x < hi; ++x) {
-            xq += x < N ? q[x] : 0.f;
-            xk += x < N ? k[x] : 0.f;
-        }
-        sums[0][tid] = xq;
-        sums[1][tid] = xk;
-        __syncthreads();
-        float bq = 0.f, bk = 0.f;
-        for (int j = 0; j < tid; ++j) {
-            bq += sums[0][j];
-            bk += sums[1][j];
-        }
-        for (int x = lo; x < hi; ++x) {
-            const float vq = x < N ? q[x] : 0.f, vk = x < N ? k[x] : 0.f;
-            q[x] = bq;
-            k[x] = bk;
-            bq += vq;
-            bk += vk;
-        }
-        __syncthreads();
+        const float *q = Mq + ((size_t)bh * kMaxLevels + m) * (N + 1);
+        const float *k = Mk + ((size_t)bh * kMaxLevels + m) * (N + 1);
+        const int b0 = (c >> m) << m, half = 1 << (m - 1);
+        if ((c >> (m - 1)) & 1)
+            X += q[min(b0 + 2 * half, N)] - q[c + 1];
+        else
+            X += k[c] - k[b0];
     }
     const size_t h = (size_t)bh * Tlen;
-    int cprev = -1;
-    float X = 0.f;
-    for (int r = tid; r < Tlen; r += 256) {
-        const int c = r / C;
-        if (c != cprev) {
-            X = 0.f;
-            for (int m = 1; m <= mtop; ++m) {
-                const float *q = Mq + ((size_t)bh * kMaxLevels + m) * (N + 1);
-                const float *k = Mk + ((size_t)bh * kMaxLevels + m) * (N + 1);
-                const int b0 = (c >> m) << m, half = 1 << (m - 1);
-                if ((c >> (m - 1)) & 1)
-                    X += q[min(b0 + 2 * half, N)] - q[c + 1];
-                else
-                    X += k[c] - k[b0];
-            }
-            cprev = c;
-        }
-        da[h + r] = r == 0 ? 0.f : daloc[h + r] + X;
-    }
+    da[h + r] = r == 0 ? 0.f : daloc[h + r] + X;
 }
 
 // ---------------------------------------------------------------------------
@@ -737,13 +925,22 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     T *W1 = reinterpret_cast<T *>(ws + P.off_w1);
     T *W2 = reinterpret_cast<T *>(ws + P.off_w2);
     float *daloc = reinterpret_cast<float *>(ws + P.off_pq);
+    double *Gp = reinterpret_cast<double *>(ws + P.off_gp);
+    if (N > 1) {
+        ProfEvents pg = prof_events("ll_bwd_gprefix");
+        hipExtLaunchKernelGGL(ll_bwd_gprefix, dim3(BH), dim3(256), 0, s, pg.start, pg.stop, 0, Gam, Gp, N);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
     float *Mq = reinterpret_cast<float *>(ws + P.off_mq);
     float *Mk = reinterpret_cast<float *>(ws + P.off_mk);
     // 3. W pieces and their sums
     if (P.NP > 0) {
         ProfEvents pe = prof_events("ll_bwd_wpiece");
         hipExtLaunchKernelGGL(ll_bwd_wpiece<B>, dim3(P.NP, BH), dim3(256), 0, s, pe.start, pe.stop, 0,
-                              (const T *)A.q, (const T *)A.dout, A.a, A.lam, Gam, Wp, A.T, A.L, N, P.NP);
+                              (const T *)A.q, (const T *)A.dout, A.a, A.lam, (const double *)Gp, Wp, W1, W2, A.T,
+                              A.L, N, P.NP,
+                              P.NB);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
         pe = prof_events("ll_bwd_wsum");
@@ -754,16 +951,23 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     }
     // 4. chunk kernel
     ProfEvents pe = prof_events("ll_bwd_chunk");
-    hipExtLaunchKernelGGL(ll_bwd_chunk<B>, dim3(BH * N), dim3(256), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
-                          (const T *)A.k, (const T *)A.v, (const T *)A.dout, A.a, A.lam, Dg, Gam, (const T *)W1,
+    hipExtLaunchKernelGGL(ll_bwd_chunk<B>, dim3(BH * N), dim3(B::NTC), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
+                          (const T *)A.k, (const T *)A.v, (const T *)A.dout, A.a, A.lam, Dg, (const double *)Gp, (const T *)W1,
                           (const T *)W2, (T *)A.gk, (T *)A.gv, A.glam, daloc, Mq, Mk, A.T, A.L, N, P.tree.nL,
                           P.tree.nLeft, P.NB);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     // 5. da
+    const int mt = bwd_levels(N);
+    if (mt > 0) {
+        pe = prof_events("ll_bwd_mscan");
+        hipExtLaunchKernelGGL(ll_bwd_mscan, dim3(mt, BH), dim3(256), 0, s, pe.start, pe.stop, 0, Mq, Mk, N);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
     pe = prof_events("ll_bwd_da");
-    hipExtLaunchKernelGGL(ll_bwd_da, dim3(BH), dim3(256), 0, s, pe.start, pe.stop, 0, (const float *)daloc, Mq, Mk,
-                          A.ga, A.T, N, C, bwd_levels(N));
+    hipExtLaunchKernelGGL(ll_bwd_da, dim3((A.T + 255) / 256, BH), dim3(256), 0, s, pe.start, pe.stop, 0,
+                          (const float *)daloc, (const float *)Mq, (const float *)Mk, A.ga, A.T, N, C, mt);
     return hipGetLastError();
 }
 
@@ -774,7 +978,7 @@ static BwdLauncher bwd_pick_c()
     if constexpr (C % DT::KB != 0 || 4 % (C / 16) != 0 || (DK / 16) % (4 / (C / 16)) != 0 ||
                   (DV / 16) % (4 / (C / 16)) != 0) {
         return nullptr;
-    } else if constexpr (sizeof(BwSmem<B>) > 160 * 1024 || sizeof(WpSmem<B>) > 64 * 1024) {
+    } else if constexpr (sizeof(BwSmem<B>) > 160 * 1024 || sizeof(WpSmem<B>) > 160 * 1024) {
         return nullptr;
     } else {
         return &launch_bwd_t<DT, DK, DV, C>;
@@ -843,7 +1047,8 @@ BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk)
     p.off_pq = al256(p.off_w2 + BH * p.NB * st * 4);
     p.off_mq = al256(p.off_pq + BH * T * 4);
     p.off_mk = al256(p.off_mq + BH * kMaxLevels * (size_t)(N + 1) * 4);
-    p.bytes = al256(p.off_mk + BH * kMaxLevels * (size_t)(N + 1) * 4);
+    p.off_gp = al256(p.off_mk + BH * kMaxLevels * (size_t)(N + 1) * 4);
+    p.bytes = al256(p.off_gp + BH * (size_t)N * 8);
     return p;
 }
 

@@ -100,7 +100,7 @@ struct BwdArgs {
 struct BwdPlan {
     FwdPlan tree, fq;
     int NP = 0, NB = 0;
-    size_t off_tree = 0, off_fq = 0, off_wp = 0, off_w1 = 0, off_w2 = 0, off_pq = 0, off_mq = 0, off_mk = 0, bytes = 0;
+    size_t off_tree = 0, off_fq = 0, off_wp = 0, off_w1 = 0, off_w2 = 0, off_pq = 0, off_mq = 0, off_mk = 0, off_gp = 0, bytes = 0;
 };
 
 BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk);
