@@ -19,6 +19,9 @@ Fenwick stacks of 17 slots).  Prints ONE JSON line on stdout.
   prefill      the forward that also writes the decode stack of the last
                position (loglinear_prefill, 17 slots): step time and the
                stack kernel's roofline
+  backward     loglinear_bwd on the same workload (K/4 steps): step time,
+               per-kernel times and the whole call's share of HBM peak for
+               its mandatory bytes
   cpu_baseline the fp64 oracle on a bounded row sample of the same workload
 
 Three input sets (3 x 218 MB) rotate through the forward steps and two
@@ -121,6 +124,15 @@ def stack_algorithmic(cfg, g: int, Lcap: int):
     per_head = whole * cfg.dk * cfg.dv * e + 4 * n_groups + (p + 1 - t0) * ((cfg.dk + cfg.dv) * e + 4) \
         + occ * (cfg.dk * cfg.dv * 4 + 4)
     return cfg.B * cfg.H * per_head
+
+
+def bwd_algorithmic(cfg):
+    """Mandatory HBM bytes of one backward: q, k, v, do, a, lambda in and
+    dq, dk, dv, da, dlambda out, once each."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    T, dk, dv, L = cfg.T, cfg.dk, cfg.dv, cfg.L
+    per_bh = T * (2 * dk + 2 * dv) * e + 4 * T + 4 * T * L + T * (2 * dk + dv) * e + 4 * T + 4 * T * L
+    return cfg.B * cfg.H * per_bh
 
 
 def read_traffic():
@@ -318,6 +330,37 @@ def main():
     log(f"prefill: {pre_ms:.4f} ms/step (forward alone {fwd_ms:.4f}); stack kernel {stack_ms:.4f} ms, "
         f"{stack_gbs:.1f} GB/s")
 
+    # ---- backward: gradients of the forward on the same workload ----
+    bws = torch.empty(ll.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
+                      device=dev)
+    dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.dv), device=dev, generator=torch.Generator(device=dev).manual_seed(5)
+                       ).to(cfg.torch_dtype)
+
+    def bstep(i):
+        d = dsets[i % 3]
+        ll.bwd(d["q"], d["k"], d["v"], d["a"], d["lam"], dout, chunk=cfg.chunk, workspace=bws)
+
+    bsteps = max(1, args.steps // 4)
+    for i in range(min(args.warmup, 2)):
+        bstep(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(bsteps):
+        bstep(i)
+    e1.record()
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / bsteps
+    ll.profile_begin(16 * bsteps + 16)
+    torch.cuda.synchronize()
+    for i in range(bsteps):
+        bstep(i)
+    torch.cuda.synchronize()
+    bstats = ll.profile_end()
+    bk = {k: v[1] / v[0] for k, v in bstats.items()}
+    bdom = max(bk, key=bk.get)
+    bbytes = bwd_algorithmic(cfg)
+    log(f"backward: {bwd_ms:.4f} ms/step; kernels: { {k: round(v * 1e3, 1) for k, v in bk.items()} }")
+
     result = {
         "metric": "tokens/s, log-linear Mamba-2 fwd at T=16K (% MFMA peak); decode GB/s",
         "value": round(cfg.B * cfg.T / (fwd_ms * 1e-3), 1),
@@ -358,6 +401,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(stack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(stack_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
+        },
+        "backward": {
+            "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5),
+            "tokens_per_s": round(cfg.B * cfg.T / (bwd_ms * 1e-3), 1),
+            "algorithmic_bytes": bbytes,
+            "kernels_ms": {k: round(v, 5) for k, v in bk.items()},
+            "hbm_frac_whole_call": round(bbytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dominant_kernel": bdom,
         },
         "cpu_baseline": None,
     }

@@ -193,3 +193,48 @@ def test_prefill_lcap_fits_exactly(L):
 
 def test_prefill_empty_prompt_is_a_no_op(L):
     assert _pre(L, T=0, q=None, k=None, v=None, out=None, a=None, lam=None, state=None, logscale=None) == ll.LL_OK
+
+
+def _bwd(L, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, lam=FAKE + 0x400000,
+                do=FAKE + 0x500000, dq=FAKE + 0x1000000, dk=FAKE + 0x2000000, dv=FAKE + 0x3000000,
+                da=FAKE + 0x4000000, dlam=FAKE + 0x5000000, B=1, H=1, T=64, dk_=128, dv_=64, chunk=64,
+                dtype=ll.LL_BF16, ws=FAKE + 0x10000000, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return L.loglinear_bwd(args["q"], args["k"], args["v"], args["a"], args["lam"], args["do"], args["dq"],
+                           args["dk"], args["dv"], args["da"], args["dlam"], args["B"], args["H"], args["T"],
+                           args["dk_"], args["dv_"], args["chunk"], args["dtype"], args["ws"], args["wsb"],
+                           args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=9), ll.LL_EINVAL),
+    (dict(T=-2), ll.LL_EINVAL),
+    (dict(chunk=16), ll.LL_EUNSUPPORTED),
+    (dict(dk_=16), ll.LL_EUNSUPPORTED),
+    (dict(dv_=96), ll.LL_EUNSUPPORTED),
+    (dict(dtype=ll.LL_F32, chunk=64, dk_=128, dv_=128), ll.LL_EUNSUPPORTED),   # fp32 chunk 64 does not fit LDS
+    (dict(B=70000), ll.LL_EUNSUPPORTED),
+    (dict(q=None), ll.LL_EINVAL),
+    (dict(do=None), ll.LL_EINVAL),
+    (dict(dq=None), ll.LL_EINVAL),
+    (dict(da=None), ll.LL_EINVAL),
+    (dict(dk=FAKE + 0x2000008), ll.LL_EINVAL),       # misaligned
+    (dict(dlam=FAKE + 0x5000002), ll.LL_EINVAL),
+    (dict(dq=FAKE + 0x100), ll.LL_EINVAL),           # dq overlaps q
+    (dict(dv=FAKE + 0x2000000), ll.LL_EINVAL),       # dv overlaps dk
+    (dict(ws=None), ll.LL_EWORKSPACE),
+    (dict(wsb=16), ll.LL_EWORKSPACE),
+    (dict(ws=FAKE + 0x10000010), ll.LL_EINVAL),      # misaligned workspace
+])
+def test_bwd_rejects_bad_arguments(L, kw, status):
+    assert _bwd(L, **kw) == status
+    assert ll.last_error().startswith("loglinear_bwd")
+
+
+def test_bwd_workspace_and_empty(L):
+    n = ll.bwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
+    assert n > 0 and n % 256 == 0 and n == ll.bwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
+    assert ll.bwd_workspace_bytes(0, 16, 16384, 128, 64, 64) == 0
+    assert _bwd(L, T=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, da=None, dlam=None,
+                ws=None, wsb=0) == ll.LL_OK
