@@ -67,6 +67,9 @@ struct Bw {
     static constexpr int LOGC = C == 16 ? 4 : C == 32 ? 5 : 6;
     static constexpr int WP = 8;                          // chunks per W piece
     static constexpr int VEC = 16 / (int)sizeof(T);
+    // bf16: token-indexed operands are read with transpose reads from the
+    // row-major tiles; fp32 keeps transposed copies
+    static constexpr bool TRD = DT::is_bf16;
     static_assert(C % KB == 0 && DK % KB == 0 && DV % KB == 0, "units");
     static_assert(CT >= 1 && CT <= 4 && 4 % CT == 0 && DKT % NCG == 0 && DVT % NCG == 0, "wave layout");
     static_assert((C * kMaxLevels) % NTC == 0, "lambda staging");
@@ -76,11 +79,11 @@ template <class B>
 struct BwSmem {
     using T = typename B::T;
     __attribute__((aligned(16))) T Qs[B::C][B::LQ];    // q rows
-    __attribute__((aligned(16))) T QsT[B::DK][B::LC];  // q, [dk][token]
+    __attribute__((aligned(16))) T QsT[B::TRD ? 1 : B::DK][B::TRD ? 8 : B::LC];  // q, [dk][token] (fp32)
     __attribute__((aligned(16))) T Ks[B::C][B::LQ];
     __attribute__((aligned(16))) T Vs[B::C][B::LV];
     __attribute__((aligned(16))) T dOs[B::C][B::LV];
-    __attribute__((aligned(16))) T dOsT[B::DV][B::LC];
+    __attribute__((aligned(16))) T dOsT[B::TRD ? 1 : B::DV][B::TRD ? 8 : B::LC];
     __attribute__((aligned(16))) T PdT[B::C][B::LC];   // (M . dP)^T, [key][query]
     __attribute__((aligned(16))) T PsT[B::C][B::LC];   // (M . S)^T
     float G[B::C][B::C + 1];                            // exp(decay) S dP, [query][key]
@@ -90,7 +93,11 @@ struct BwSmem {
     float part[8][B::C];                                // cross-wave row partial sums
     float off[kMaxLevels];                              // per-level log-decay offsets (chunk totals)
     float km[kMaxLevels];                               // key-side pair mass of this chunk per level
-    float kw[8];
+    // per-level partial sums of the level loop (a slot per level, so the loop
+    // needs no barrier): query side [level][column group][token], key side
+    // [level][wave]
+    float lpart[kMaxLevels - B::LOGC][B::NCG][B::C];
+    float lkw[kMaxLevels - B::LOGC][B::NW];
     float u[B::C], w[B::C];                             // per-token terms of the in-chunk part of da
 };
 
@@ -168,7 +175,13 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     constexpr int C = B::C, DK = B::DK, DV = B::DV;
     __shared__ BwSmem<B> sm;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, qd = lane >> 4;
-    const int bh = blockIdx.x / N, c = blockIdx.x % N;
+    // Workgroups b, b+8, ... run on the same XCD and share its L2: give each
+    // XCD a contiguous range of (head, chunk) items, so the chunks that read
+    // the same level states read them through one L2.
+    const int nb = gridDim.x, bid = blockIdx.x;
+    const int per = nb >> 3, rem = nb & 7, xcd = bid & 7;
+    const int wid = xcd * per + min(xcd, rem) + (bid >> 3);
+    const int bh = wid / N, c = wid % N;
     const int t0 = c * C;
     const int nv = min(C, Tlen - t0);   // valid rows of this chunk
     const size_t row0 = (size_t)bh * Tlen + t0;
@@ -209,9 +222,11 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             const int t = i / (DK / VEC), d0 = (i % (DK / VEC)) * VEC;
             *reinterpret_cast<uint4 *>(&sm.Qs[t][d0]) = rq[j];
             *reinterpret_cast<uint4 *>(&sm.Ks[t][d0]) = rk[j];
+            if constexpr (!B::TRD) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                store_elem(&sm.QsT[d0 + e][t], rq[j], e);
+                for (int e = 0; e < VEC; ++e)
+                    store_elem(&sm.QsT[d0 + e][t], rq[j], e);
+            }
         }
     }
 #pragma unroll
@@ -221,9 +236,11 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             const int t = i / (DV / VEC), e0 = (i % (DV / VEC)) * VEC;
             *reinterpret_cast<uint4 *>(&sm.Vs[t][e0]) = rv[j];
             *reinterpret_cast<uint4 *>(&sm.dOs[t][e0]) = ro[j];
+            if constexpr (!B::TRD) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                store_elem(&sm.dOsT[e0 + e][t], ro[j], e);
+                for (int e = 0; e < VEC; ++e)
+                    store_elem(&sm.dOsT[e0 + e][t], ro[j], e);
+            }
         }
     }
     for (int i = tid; i < C * B::LC * (int)sizeof(T) / 16; i += B::NTC) {
@@ -333,14 +350,26 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     // in-chunk: dK = (M.dP)^T Q, dV = (M.S)^T dO (contraction over queries)
 #pragma unroll
     for (int u = 0; u < B::NUC; ++u) {
-        const Frag pd = frag<B>(&sm.PdT[0][0], B::LC, 16 * kt + li, u, qd);
-        const Frag ps = frag<B>(&sm.PsT[0][0], B::LC, 16 * kt + li, u, qd);
+        if constexpr (B::TRD) {
+            // both operands in the permuted token order of the transpose read
+            const Frag pd = lds_frag(&sm.PdT[0][0], B::LC, 16 * kt + li, B::KB * u, qd);
+            const Frag ps = lds_frag(&sm.PsT[0][0], B::LC, 16 * kt + li, B::KB * u, qd);
 #pragma unroll
-        for (int j = 0; j < B::KPW; ++j)
-            mma_unit(dK[j], frag<B>(&sm.QsT[0][0], B::LC, 16 * (cg + B::NCG * j) + li, u, qd), pd);
+            for (int j = 0; j < B::KPW; ++j)
+                mma_unit(dK[j], tr_frag(&sm.Qs[0][0], B::LQ, B::KB * u, 16 * (cg + B::NCG * j), li, qd), pd);
 #pragma unroll
-        for (int j = 0; j < B::VPW; ++j)
-            mma_unit(dV[j], frag<B>(&sm.dOsT[0][0], B::LC, 16 * (cg + B::NCG * j) + li, u, qd), ps);
+            for (int j = 0; j < B::VPW; ++j)
+                mma_unit(dV[j], tr_frag(&sm.dOs[0][0], B::LV, B::KB * u, 16 * (cg + B::NCG * j), li, qd), ps);
+        } else {
+            const Frag pd = frag<B>(&sm.PdT[0][0], B::LC, 16 * kt + li, u, qd);
+            const Frag ps = frag<B>(&sm.PsT[0][0], B::LC, 16 * kt + li, u, qd);
+#pragma unroll
+            for (int j = 0; j < B::KPW; ++j)
+                mma_unit(dK[j], frag<B>(&sm.QsT[0][0], B::LC, 16 * (cg + B::NCG * j) + li, u, qd), pd);
+#pragma unroll
+            for (int j = 0; j < B::VPW; ++j)
+                mma_unit(dV[j], frag<B>(&sm.dOsT[0][0], B::LC, 16 * (cg + B::NCG * j) + li, u, qd), ps);
+        }
     }
     // The accumulators hold dK^T and dV^T tiles: A = columns (dk / dv index,
     // rows 4*qd+i), B = keys (column li).
@@ -361,6 +390,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             o = gp[b0 + half] - gp[c + 1];
         sm.off[m] = (float)o;
     }
+    __syncthreads();
     for (int m = 1; m <= mtop; ++m) {
         if ((c >> (m - 1)) & 1) {
             // query side: the left block [b0, b0 + half) is a stored block
@@ -369,8 +399,6 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             for (int r = 0; r < m - 1; ++r)
                 offp += ((nL >> r) + 1) >> 1;
             const T *blk = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
-            __syncthreads();
-            const float offB = sm.off[m];   // log-decay from the block's end to the chunk start
             // X^T = D^T Q^T: A = D^T (rows e), B = Q (columns t); this wave
             // takes query tile kt and value tiles cg, cg + NCG, ...
             float xs = 0.f;
@@ -391,14 +419,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             xs += __shfl_xor(xs, 16, 64);
             xs += __shfl_xor(xs, 32, 64);
             if (qd == 0)
-                sm.part[cg][16 * kt + li] = xs;
-            __syncthreads();
-            if (tid < C) {
-                float x = 0.f;
-                for (int g2 = 0; g2 < B::NCG; ++g2)
-                    x += sm.part[g2][tid];
-                sm.dlam[tid][B::LOGC + m] = __expf(sm.Aloc[tid] + offB) * x;
-            }
+                sm.lpart[m][cg][16 * kt + li] = xs;
         } else if (((c >> m) << m) + (1 << (m - 1)) < N) {
             // key side: the right block R sees this chunk at level m
             size_t ob = 0;
@@ -409,7 +430,6 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             const size_t wi = (size_t)bh * NB + ob + (c >> m);
             const T *w1 = W1 + wi * DK * DV;   // W,   [dk][dv]
             const T *w2 = W2 + wi * DK * DV;   // W^T, [dv][dk]
-            __syncthreads();
             const float offR = sm.off[m];   // log-decay from the chunk's end to R's start
             // this wave's key rows: decay exp(A_e - A_s)
             const float dec = __expf(sm.Aloc[C - 1] - sm.Aloc[16 * kt + li] + offR);
@@ -442,14 +462,25 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             for (int o = 32; o >= 1; o >>= 1)
                 km += __shfl_xor(km, o, 64);
             if (lane == 0)
-                sm.kw[wv] = km;
-            __syncthreads();
-            if (tid == 0) {
-                float x = 0.f;
+                sm.lkw[m][wv] = km;
+        }
+    }
+    __syncthreads();
+    // the level loop's reductions: dlambda of the query-side levels, the
+    // key-side pair masses
+    for (int i = tid; i < mtop * C; i += B::NTC) {
+        const int m = 1 + i / C, t = i % C;
+        if ((c >> (m - 1)) & 1) {
+            float x = 0.f;
+            for (int g2 = 0; g2 < B::NCG; ++g2)
+                x += sm.lpart[m][g2][t];
+            sm.dlam[t][B::LOGC + m] = __expf(sm.Aloc[t] + sm.off[m]) * x;
+        } else if (t == 0) {
+            float x = 0.f;
+            if (((c >> m) << m) + (1 << (m - 1)) < N)
                 for (int w2 = 0; w2 < B::NW; ++w2)
-                    x += sm.kw[w2];
-                sm.km[m] = x;
-            }
+                    x += sm.lkw[m][w2];
+            sm.km[m] = x;
         }
     }
     __syncthreads();
@@ -549,8 +580,10 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
 template <class B>
 struct WpSmem {
     using T = typename B::T;
-    __attribute__((aligned(16))) T QwT[B::DK][B::LC];   // weighted q, [dk][token]
-    __attribute__((aligned(16))) T dOT[B::DV][B::LC];   // do, [dv][token]
+    // weighted q and do: bf16 row-major [token][.] (transpose reads), fp32
+    // transposed [.][token]
+    __attribute__((aligned(16))) T QwT[B::TRD ? B::C : B::DK][B::TRD ? B::LQ : B::LC];
+    __attribute__((aligned(16))) T dOT[B::TRD ? B::C : B::DV][B::TRD ? B::LV : B::LC];
     __attribute__((aligned(16))) float Wt[B::DK][B::DV + 4];   // the result, for coalesced stores
     float Aloc[B::C];
     float wt[B::C];                                     // per-token weights
@@ -670,6 +703,19 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
 #pragma unroll
         for (int jj = 0; jj < NQP; ++jj) {
             const int i = tid + B::NT * jj;
+            if constexpr (B::TRD) {
+                if (i < QP) {
+                    const int t = i / (DK / VEC), d0 = (i % (DK / VEC)) * VEC;
+                    const float w = sm.wt[t];
+                    const uint32_t wd[4] = {rq[jj].x, rq[jj].y, rq[jj].z, rq[jj].w};
+                    bf16x8 y;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        y[e] = (__bf16)(w * __uint_as_float((e & 1) ? (wd[e >> 1] & 0xffff0000u) : (wd[e >> 1] << 16)));
+                    *reinterpret_cast<bf16x8 *>(&sm.QwT[t][d0]) = y;
+                }
+                continue;
+            }
             if (i < QP) {
                 const int t = i / (DK / VEC), d0 = (i % (DK / VEC)) * VEC;
                 const float w = sm.wt[t];
@@ -689,9 +735,13 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
             const int i = tid + B::NT * jj;
             if (i < VP) {
                 const int t = i / (DV / VEC), e0 = (i % (DV / VEC)) * VEC;
+                if constexpr (B::TRD) {
+                    *reinterpret_cast<uint4 *>(&sm.dOT[t][e0]) = ro[jj];
+                } else {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    store_elem(&sm.dOT[e0 + e][t], ro[jj], e);
+                    for (int e = 0; e < VEC; ++e)
+                        store_elem(&sm.dOT[e0 + e][t], ro[jj], e);
+                }
             }
         }
         if (cc + 1 < cB)
@@ -703,10 +753,17 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
             for (int r = 0; r < KT; ++r) {
                 const int dt = wv + 4 * r;
                 if (dt < B::DKT) {
-                    const auto fa = frag<B>(&sm.QwT[0][0], B::LC, 16 * dt + li, u, qd);
+                    if constexpr (B::TRD) {
+                        const auto fa = tr_frag(&sm.QwT[0][0], B::LQ, B::KB * u, 16 * dt, li, qd);
 #pragma unroll
-                    for (int e = 0; e < B::DVT; ++e)
-                        mma_unit(acc[r][e], fa, frag<B>(&sm.dOT[0][0], B::LC, 16 * e + li, u, qd));
+                        for (int e = 0; e < B::DVT; ++e)
+                            mma_unit(acc[r][e], fa, tr_frag(&sm.dOT[0][0], B::LV, B::KB * u, 16 * e, li, qd));
+                    } else {
+                        const auto fa = frag<B>(&sm.QwT[0][0], B::LC, 16 * dt + li, u, qd);
+#pragma unroll
+                        for (int e = 0; e < B::DVT; ++e)
+                            mma_unit(acc[r][e], fa, frag<B>(&sm.dOT[0][0], B::LC, 16 * e + li, u, qd));
+                    }
                 }
             }
         }

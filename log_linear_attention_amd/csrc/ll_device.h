@@ -106,6 +106,25 @@ __device__ __forceinline__ bf16x8 acc_frag(const floatx4 *tiles, int u, TBF16)
 // Row (within a unit) of element e supplied by lane quad qd.
 __device__ __forceinline__ constexpr int unit_row(int e, int qd) { return 16 * (e >> 2) + 4 * qd + (e & 3); }
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Fragment whose k-index runs over tokens (rows of a row-major bf16 LDS
+// tile): rows jb .. jb+31, columns c0 + li.  Lane (li, qd) gets rows
+// jb + 16*(e/4) + 4*qd + e%4 of column c0 + li, the same permuted k order as
+// lds_frag.  Each half is one transpose read in which lane p of a 16-lane
+// block addresses the 4-element row segment (row jb + 4*qd + p/4, columns
+// c0 + 4*(p%4) ..).
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *base, int ld, int jb, int c0, int li, int qd)
+{
+    const __bf16 *p = base + (jb + 4 * qd + (li >> 2)) * ld + c0 + 4 * (li & 3);
+    bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+    bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + 16 * ld));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
 // Bit length of a positive integer (level of a XOR distance).
