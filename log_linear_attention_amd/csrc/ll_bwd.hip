@@ -70,13 +70,18 @@ struct Bw {
     // bf16: token-indexed operands are read with transpose reads from the
     // row-major tiles; fp32 keeps transposed copies
     static constexpr bool TRD = DT::is_bf16;
+    // LDS copy of one level's state (W and W^T with padded rows, or a block
+    // state in fragment order), shared by all waves
+    static constexpr int LW1 = DV + PAD, LW2 = DK + PAD;
+    static constexpr int SSZ = DK * LW1 + DV * LW2;
+    static constexpr int NSP = 2 * DK * DV / VEC;         // 16-byte pieces of a level's state
     static_assert(C % KB == 0 && DK % KB == 0 && DV % KB == 0, "units");
     static_assert(CT >= 1 && CT <= 4 && 4 % CT == 0 && DKT % NCG == 0 && DVT % NCG == 0, "wave layout");
     static_assert((C * kMaxLevels) % NTC == 0, "lambda staging");
 };
 
 template <class B>
-struct BwSmem {
+struct BwSmemBase {
     using T = typename B::T;
     __attribute__((aligned(16))) T Qs[B::C][B::LQ];    // q rows
     __attribute__((aligned(16))) T QsT[B::TRD ? 1 : B::DK][B::TRD ? 8 : B::LC];  // q, [dk][token] (fp32)
@@ -99,6 +104,17 @@ struct BwSmem {
     float lpart[kMaxLevels - B::LOGC][B::NCG][B::C];
     float lkw[kMaxLevels - B::LOGC][B::NW];
     float u[B::C], w[B::C];                             // per-token terms of the in-chunk part of da
+};
+
+// The shared level-state buffer when it fits next to the rest.
+template <class B>
+struct BwSt {
+    static constexpr bool SST = sizeof(BwSmemBase<B>) + (size_t)B::SSZ * sizeof(typename B::T) + 64 <= 160 * 1024;
+};
+
+template <class B>
+struct BwSmem : BwSmemBase<B> {
+    __attribute__((aligned(16))) typename B::T st[BwSt<B>::SST ? B::SSZ : 8];
 };
 
 // Operand fragment: EPL consecutive elements of row `row` starting at unit u.
@@ -391,45 +407,110 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         sm.off[m] = (float)o;
     }
     __syncthreads();
-    for (int m = 1; m <= mtop; ++m) {
-        if ((c >> (m - 1)) & 1) {
-            // query side: the left block [b0, b0 + half) is a stored block
-            // state -> dlambda level LOGC + m
+    // Level sources: kind 1 = query side (the left block is a stored block
+    // state), 2 = key side (the right block R exists), 0 = nothing.
+    auto kind_of = [&](int m) {
+        if (m > mtop)
+            return 0;
+        if ((c >> (m - 1)) & 1)
+            return 1;
+        return ((c >> m) << m) + (1 << (m - 1)) < N ? 2 : 0;
+    };
+    auto state_ptr = [&](int m, int kind, const T *&p1, const T *&p2) {
+        if (kind == 1) {
             size_t offp = 0;
             for (int r = 0; r < m - 1; ++r)
                 offp += ((nL >> r) + 1) >> 1;
-            const T *blk = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
-            // X^T = D^T Q^T: A = D^T (rows e), B = Q (columns t); this wave
-            // takes query tile kt and value tiles cg, cg + NCG, ...
-            float xs = 0.f;
-#pragma unroll
-            for (int j = 0; j < B::VPW; ++j) {
-                const int et = cg + B::NCG * j;
-                floatx4 X = zero4();
-#pragma unroll
-                for (int u = 0; u < B::NUK; ++u)
-                    mma_unit(X, gfrag<B, B::NUK>(blk, et, u, lane), frag<B>(&sm.Qs[0][0], B::LQ, 16 * kt + li, u, qd));
-                // X[i] = (Q D)[t = 16 kt + li][e = 16 et + 4 qd + i]
-                const floatx4 o4 = ld4(&sm.dOs[16 * kt + li][16 * et + 4 * qd]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xs += X[i] * o4[i];
-            }
-            // reduce over the four lane quads (the e rows), then over column groups
-            xs += __shfl_xor(xs, 16, 64);
-            xs += __shfl_xor(xs, 32, 64);
-            if (qd == 0)
-                sm.lpart[m][cg][16 * kt + li] = xs;
-        } else if (((c >> m) << m) + (1 << (m - 1)) < N) {
-            // key side: the right block R sees this chunk at level m
+            p1 = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
+            p2 = p1;
+        } else {
             size_t ob = 0;
             for (int r = 1; r < m; ++r) {
                 const int hr = 1 << (r - 1);
                 ob += N > hr ? (N - hr + (1 << r) - 1) >> r : 0;
             }
             const size_t wi = (size_t)bh * NB + ob + (c >> m);
-            const T *w1 = W1 + wi * DK * DV;   // W,   [dk][dv]
-            const T *w2 = W2 + wi * DK * DV;   // W^T, [dv][dk]
+            p1 = W1 + wi * DK * DV;   // W,   [dk][dv]
+            p2 = W2 + wi * DK * DV;   // W^T, [dv][dk]
+        }
+    };
+    constexpr bool SST = BwSt<B>::SST;
+    constexpr int NSPT = (B::NSP + B::NTC - 1) / B::NTC;
+    constexpr int HP = DK * DV / VEC;   // pieces of one state
+    // next level's state pieces, loaded one level ahead (level 0 only loads)
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 sp[NSPT];
+    for (int m = SST ? 0 : 1; m <= mtop; ++m) {
+        const int kind = m == 0 ? 0 : kind_of(m);
+        const T *g1 = nullptr, *g2 = nullptr;   // the state in global memory (no LDS copy)
+        if constexpr (SST) {
+            __syncthreads();   // the previous level's reads of the copy are done
+            if (kind != 0) {
+                const int np = kind == 1 ? HP : 2 * HP;
+#pragma unroll
+                for (int j = 0; j < NSPT; ++j) {
+                    const int i = tid + B::NTC * j;
+                    if (i < np) {
+                        T *dst;
+                        if (kind == 1) {
+                            dst = sm.st + (size_t)i * VEC;                       // fragment order
+                        } else if (i < HP) {
+                            const int e0 = i * VEC;
+                            dst = sm.st + (e0 / DV) * B::LW1 + e0 % DV;          // W rows
+                        } else {
+                            const int e0 = (i - HP) * VEC;
+                            dst = sm.st + DK * B::LW1 + (e0 / DK) * B::LW2 + e0 % DK;   // W^T rows
+                        }
+                        *reinterpret_cast<u32x4 *>(dst) = sp[j];
+                    }
+                }
+            }
+            {
+                const int nk = kind_of(m + 1);
+                if (nk != 0) {
+                    const T *p1, *p2;
+                    state_ptr(m + 1, nk, p1, p2);
+                    const int np = nk == 1 ? HP : 2 * HP;
+#pragma unroll
+                    for (int j = 0; j < NSPT; ++j) {
+                        const int i = tid + B::NTC * j;
+                        if (i < np)
+                            sp[j] = *reinterpret_cast<const u32x4 *>(i < HP ? p1 + (size_t)i * VEC
+                                                                             : p2 + (size_t)(i - HP) * VEC);
+                    }
+                }
+            }
+            __syncthreads();
+        } else if (kind != 0) {
+            state_ptr(m, kind, g1, g2);
+        }
+        if (kind == 1) {
+            // query side -> dlambda level LOGC + m.  X^T = D^T Q^T: A = D^T
+            // (rows e), B = Q (columns t); this wave takes query tile kt and
+            // value tiles cg, cg + NCG, ...
+            float xs = 0.f;
+#pragma unroll
+            for (int j = 0; j < B::VPW; ++j) {
+                const int et = cg + B::NCG * j;
+                floatx4 X = zero4();
+#pragma unroll
+                for (int u = 0; u < B::NUK; ++u) {
+                    const Frag fd = SST ? gfrag<B, B::NUK>(sm.st, et, u, lane) : gfrag<B, B::NUK>(g1, et, u, lane);
+                    mma_unit(X, fd, frag<B>(&sm.Qs[0][0], B::LQ, 16 * kt + li, u, qd));
+                }
+                // X[i] = (Q D)[t = 16 kt + li][e = 16 et + 4 qd + i]
+                const floatx4 o4 = ld4(&sm.dOs[16 * kt + li][16 * et + 4 * qd]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xs += X[i] * o4[i];
+            }
+            // reduce over the four lane quads (the e rows)
+            xs += __shfl_xor(xs, 16, 64);
+            xs += __shfl_xor(xs, 32, 64);
+            if (qd == 0)
+                sm.lpart[m][cg][16 * kt + li] = xs;
+        } else if (kind == 2) {
+            // key side: the right block R sees this chunk at level m
             const float offR = sm.off[m];   // log-decay from the chunk's end to R's start
             // this wave's key rows: decay exp(A_e - A_s)
             const float dec = __expf(sm.Aloc[C - 1] - sm.Aloc[16 * kt + li] + offR);
@@ -439,8 +520,11 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 const int dt = cg + B::NCG * j;
                 floatx4 X = zero4();
 #pragma unroll
-                for (int u = 0; u < B::NUV; ++u)
-                    mma_unit(X, frag<B>(w1, DV, 16 * dt + li, u, qd), frag<B>(&sm.Vs[0][0], B::LV, 16 * kt + li, u, qd));
+                for (int u = 0; u < B::NUV; ++u) {
+                    const Frag fw = SST ? frag<B>(sm.st, B::LW1, 16 * dt + li, u, qd)
+                                        : frag<B>(g1, DV, 16 * dt + li, u, qd);
+                    mma_unit(X, fw, frag<B>(&sm.Vs[0][0], B::LV, 16 * kt + li, u, qd));
+                }
                 dK[j] += dec * X;
                 const floatx4 k4 = ld4(&sm.Ks[16 * kt + li][16 * dt + 4 * qd]);
 #pragma unroll
@@ -452,8 +536,11 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 const int et = cg + B::NCG * j;
                 floatx4 X = zero4();
 #pragma unroll
-                for (int u = 0; u < B::NUK; ++u)
-                    mma_unit(X, frag<B>(w2, DK, 16 * et + li, u, qd), frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
+                for (int u = 0; u < B::NUK; ++u) {
+                    const Frag fw = SST ? frag<B>(sm.st + DK * B::LW1, B::LW2, 16 * et + li, u, qd)
+                                        : frag<B>(g2, DK, 16 * et + li, u, qd);
+                    mma_unit(X, fw, frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
+                }
                 dV[j] += dec * X;
             }
             pki += km;
