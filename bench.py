@@ -175,6 +175,46 @@ def cpu_baseline(inp, cfg, n_rows: int, seed: int):
     }
 
 
+def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
+    """loglinear_bwd on the forward's workload: K/4 timed steps, then the same
+    steps with per-kernel events."""
+    bws = torch.empty(ll.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
+                      device=dev)
+    dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.dv), device=dev, generator=torch.Generator(device=dev).manual_seed(5)
+                       ).to(cfg.torch_dtype)
+
+    def bstep(i):
+        d = dsets[i % 3]
+        ll.bwd(d["q"], d["k"], d["v"], d["a"], d["lam"], dout, chunk=cfg.chunk, workspace=bws)
+
+    bsteps = max(1, args.steps // 4)
+    for i in range(min(args.warmup, 2)):
+        bstep(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(bsteps):
+        bstep(i)
+    e1.record()
+    torch.cuda.synchronize()
+    bwd_ms = e0.elapsed_time(e1) / bsteps
+    ll.profile_begin(16 * bsteps + 16)
+    torch.cuda.synchronize()
+    for i in range(bsteps):
+        bstep(i)
+    torch.cuda.synchronize()
+    bk = {k: v[1] / v[0] for k, v in ll.profile_end().items()}
+    bbytes = bwd_algorithmic(cfg)
+    log(f"backward: {bwd_ms:.4f} ms/step; kernels: { {k: round(v * 1e3, 1) for k, v in bk.items()} }")
+    return {
+        "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5),
+        "tokens_per_s": round(cfg.B * cfg.T / (bwd_ms * 1e-3), 1),
+        "algorithmic_bytes": bbytes,
+        "kernels_ms": {k: round(v, 5) for k, v in bk.items()},
+        "hbm_frac_whole_call": round(bbytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "dominant_kernel": max(bk, key=bk.get),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +225,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy first (reference kernel for counter scaling)")
     ap.add_argument("--group-log2", type=int, default=-1)
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -331,35 +372,7 @@ def main():
         f"{stack_gbs:.1f} GB/s")
 
     # ---- backward: gradients of the forward on the same workload ----
-    bws = torch.empty(ll.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
-                      device=dev)
-    dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.dv), device=dev, generator=torch.Generator(device=dev).manual_seed(5)
-                       ).to(cfg.torch_dtype)
-
-    def bstep(i):
-        d = dsets[i % 3]
-        ll.bwd(d["q"], d["k"], d["v"], d["a"], d["lam"], dout, chunk=cfg.chunk, workspace=bws)
-
-    bsteps = max(1, args.steps // 4)
-    for i in range(min(args.warmup, 2)):
-        bstep(i)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(bsteps):
-        bstep(i)
-    e1.record()
-    torch.cuda.synchronize()
-    bwd_ms = e0.elapsed_time(e1) / bsteps
-    ll.profile_begin(16 * bsteps + 16)
-    torch.cuda.synchronize()
-    for i in range(bsteps):
-        bstep(i)
-    torch.cuda.synchronize()
-    bstats = ll.profile_end()
-    bk = {k: v[1] / v[0] for k, v in bstats.items()}
-    bdom = max(bk, key=bk.get)
-    bbytes = bwd_algorithmic(cfg)
-    log(f"backward: {bwd_ms:.4f} ms/step; kernels: { {k: round(v * 1e3, 1) for k, v in bk.items()} }")
+    backward = None if args.no_bwd else measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1)
 
     result = {
         "metric": "tokens/s, log-linear Mamba-2 fwd at T=16K (% MFMA peak); decode GB/s",
@@ -402,14 +415,7 @@ def main():
                          "frac": round(stack_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
         },
-        "backward": {
-            "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5),
-            "tokens_per_s": round(cfg.B * cfg.T / (bwd_ms * 1e-3), 1),
-            "algorithmic_bytes": bbytes,
-            "kernels_ms": {k: round(v, 5) for k, v in bk.items()},
-            "hbm_frac_whole_call": round(bbytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "dominant_kernel": bdom,
-        },
+        "backward": backward,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
