@@ -33,6 +33,10 @@ Prefill (``prefill_stack``): the stack that a whole prompt leaves for the
 decode of the next token, summed bucket by bucket from the same definition
 the forward uses.
 
+Shared q/k heads (``expand_heads``, ``fwd_grouped``, ``bwd_grouped``): each
+head reads its q/k head; the gradient of a shared entry sums over the heads
+that read it.
+
 Stack convention for decode: slot l holds the state of level-l bucket of the
 most recent query position.  Occupancy follows the position's bits: for
 position p, slot 0 is always occupied and slot l >= 1 is occupied iff bit
@@ -201,6 +205,42 @@ def da_window(q, k, v, a, lam, do, rows, W: int) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle da_window failed (code {rc})")
     return out
+
+
+# ---------------------------------------------------------------------------
+# q and k shared across heads (Mamba-2's groups; the pages build on Mamba-2,
+# [LLA-pt §2 "Metodologia", generalisation point], and leave open whether q
+# and k are per head).  Head h of H reads q/k head h // (H // Hqk).
+# ---------------------------------------------------------------------------
+
+def expand_heads(x, H: int) -> np.ndarray:
+    """x [B, Hqk, ...] -> [B, H, ...] with head h taken from x head
+    h // (H // Hqk) (each q/k head repeated for its consecutive heads)."""
+    x = _f64(x)
+    Hqk = x.shape[1]
+    if Hqk <= 0 or H % Hqk != 0:
+        raise ValueError(f"H={H} is not a multiple of Hqk={Hqk}")
+    return np.repeat(x, H // Hqk, axis=1)
+
+
+def fwd_grouped(q, k, v, a, lam) -> np.ndarray:
+    """Forward with q, k [B,Hqk,T,dk] shared by the heads of v [B,H,T,dv]:
+    the per-head definition applied to each head's q/k head."""
+    H = v.shape[1]
+    return fwd(expand_heads(q, H), expand_heads(k, H), v, a, lam)
+
+
+def bwd_grouped(q, k, v, a, lam, do):
+    """Gradients of sum(do * fwd_grouped(q, k, v, a, lam)).  A shared q or k
+    entry enters the output of every head that reads it, so its gradient is
+    the sum of those heads' per-head gradients (chain rule through the
+    repetition); dv, da and dlam are per head."""
+    H = v.shape[1]
+    B, Hqk, T, dk = q.shape
+    g = bwd(expand_heads(q, H), expand_heads(k, H), v, a, lam, do)
+    for n in ("dq", "dk"):
+        g[n] = g[n].reshape(B, Hqk, H // Hqk, T, dk).sum(axis=2)
+    return g
 
 
 # ---------------------------------------------------------------------------

@@ -487,3 +487,81 @@ def test_da_window_is_exact_with_full_window(oracle_mod):
     got2 = oracle_mod.da_window(q, k, v, a_strong, lam, do, rows, W=8)
     want2 = np.array([g2["da"][0, bh, r] for bh, r in rows])
     np.testing.assert_allclose(got2, want2, rtol=1e-6, atol=1e-9)
+
+
+# --- q/k shared across heads (Mamba-2 groups) --------------------------------
+
+def _brute_grouped(q, k, v, a, lam):
+    """Pure-Python loops over the definition, with head h reading q/k head
+    h // (H // Hqk): decay as an explicit sum of a, the level from the bit
+    length of t xor s."""
+    B, Hqk, T, dk = q.shape
+    H, dv = v.shape[1], v.shape[3]
+    r = H // Hqk
+    out = np.zeros((B, H, T, dv))
+    for b in range(B):
+        for h in range(H):
+            g = h // r
+            for t in range(T):
+                for s in range(t + 1):
+                    lev = 0 if s == t else (t ^ s).bit_length()
+                    w = np.exp(sum(a[b, h, x] for x in range(s + 1, t + 1))) * lam[b, h, t, lev]
+                    out[b, h, t] += w * float(np.dot(q[b, g, t], k[b, g, s])) * v[b, h, s]
+    return out
+
+
+def test_grouped_forward_brute_force(oracle_mod):
+    rng = np.random.default_rng(70)
+    B, H, Hqk, T, dk, dv = 2, 6, 2, 11, 3, 2
+    L = _L(T)
+    _, _, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, L)
+    q = rng.standard_normal((B, Hqk, T, dk))
+    k = rng.standard_normal((B, Hqk, T, dk))
+    got = oracle_mod.fwd_grouped(q, k, v, a, lam)
+    np.testing.assert_allclose(got, _brute_grouped(q, k, v, a, lam), rtol=1e-12, atol=1e-12)
+    # heads 0..2 share q/k head 0: with equal v, a and lambda they agree
+    v2, a2, lam2 = v.copy(), a.copy(), lam.copy()
+    v2[:, 1] = v2[:, 0]; a2[:, 1] = a2[:, 0]; lam2[:, 1] = lam2[:, 0]
+    o2 = oracle_mod.fwd_grouped(q, k, v2, a2, lam2)
+    np.testing.assert_array_equal(o2[:, 0], o2[:, 1])
+    # one q/k head per head is the per-head forward
+    qf = rng.standard_normal((B, H, T, dk))
+    kf = rng.standard_normal((B, H, T, dk))
+    np.testing.assert_array_equal(oracle_mod.fwd_grouped(qf, kf, v, a, lam), oracle_mod.fwd(qf, kf, v, a, lam))
+
+
+def test_grouped_bwd_matches_finite_differences(oracle_mod):
+    """The shared q/k gradients sum over the heads that read them: central
+    differences of the grouped forward along random directions."""
+    rng = np.random.default_rng(71)
+    B, H, Hqk, T, dk, dv = 1, 4, 2, 9, 3, 2
+    L = _L(T)
+    _, _, v, a, lam = _rand_inputs(rng, B, H, T, dk, dv, L)
+    q = rng.standard_normal((B, Hqk, T, dk))
+    k = rng.standard_normal((B, Hqk, T, dk))
+    do = rng.standard_normal((B, H, T, dv))
+    g = oracle_mod.bwd_grouped(q, k, v, a, lam, do)
+    assert g["dq"].shape == q.shape and g["dk"].shape == k.shape
+    args = {"q": q, "k": k, "v": v, "a": a, "lam": lam}
+
+    def loss(**kw):
+        return float(np.sum(do * oracle_mod.fwd_grouped(**kw)))
+
+    eps = 1e-5
+    for name, x in args.items():
+        for _ in range(2):
+            d = rng.standard_normal(x.shape)
+            if name == "a":
+                d[..., 0] = 0.0
+            plus = dict(args); plus[name] = x + eps * d
+            minus = dict(args); minus[name] = x - eps * d
+            fd = (loss(**plus) - loss(**minus)) / (2 * eps)
+            an = float(np.sum(g["d" + name] * d))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_expand_heads_needs_a_multiple(oracle_mod):
+    x = np.zeros((1, 3, 2, 2))
+    assert oracle_mod.expand_heads(x, 6).shape == (1, 6, 2, 2)
+    with pytest.raises(ValueError):
+        oracle_mod.expand_heads(x, 4)
