@@ -203,6 +203,44 @@ ll_status loglinear_prefill(const void *q, const void *k, const void *v,
                             ll_dtype dtype, void *workspace, size_t workspace_bytes,
                             void *stream, int group_log2);
 
+/* ---- q and k shared across heads ----------------------------------------
+ * Mamba-2 lets several heads read one q/k head (its "groups"); the pages
+ * build log-linear attention on top of Mamba-2 (Portuguese page §2
+ * "Metodologia", its point on generalisation; French page §3 "Contributions
+ * Clés") without saying whether q and k are per head.  These calls take Hqk q/k heads for H heads (H a positive multiple
+ * of Hqk; Hqk = H is the per-head case of the calls above): head h reads q/k
+ * head h / (H / Hqk), i.e. consecutive heads share one q/k head.  Everything
+ * else (arguments, layouts, workspace sizes, errors) is as in the call each
+ * one extends, except:
+ *  q, k   [B,Hqk,T,dk] (forward, prefill, backward) or [S,Hqk,dk] (decode)
+ *  dq, dk [B,Hqk,T,dk]: the backward sums the gradients of the heads that
+ *         share a q/k head (in float32, rounded once to the dtype).
+ * The backward's workspace is loglinear_bwd_grouped_workspace_bytes (the
+ * forward's and prefill's sizes do not depend on Hqk).  An H that is not a
+ * positive multiple of Hqk returns LL_EINVAL (workspace query: 0). */
+ll_status loglinear_fwd_grouped(const void *q, const void *k, const void *v,
+                                const float *a, const float *lambda, void *out,
+                                int B, int H, int Hqk, int T, int dk, int dv, int chunk,
+                                ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                                void *stream, int group_log2);
+ll_status loglinear_prefill_grouped(const void *q, const void *k, const void *v,
+                                    const float *a, const float *lambda, void *out,
+                                    float *state, float *logscale,
+                                    int B, int H, int Hqk, int T, int dk, int dv, int chunk, int Lcap,
+                                    ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                                    void *stream, int group_log2);
+ll_status loglinear_decode_step_grouped(const void *q, const void *k, const void *v,
+                                        const float *a, const float *lambda,
+                                        float *state, float *logscale, const int64_t *pos,
+                                        void *out, int S, int H, int Hqk, int dk, int dv, int Lcap,
+                                        ll_dtype dtype, void *stream);
+size_t loglinear_bwd_grouped_workspace_bytes(int B, int H, int Hqk, int T, int dk, int dv, int chunk);
+ll_status loglinear_bwd_grouped(const void *q, const void *k, const void *v,
+                                const float *a, const float *lambda, const void *dout,
+                                void *dq, void *dk_out, void *dv_out, float *da, float *dlambda,
+                                int B, int H, int Hqk, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message for the last failing call on this thread ("" if none).  Valid
  * until the next call into the library on the same thread. */
 const char *loglinear_last_error(void);

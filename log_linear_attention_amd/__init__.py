@@ -69,6 +69,16 @@ def lib() -> ctypes.CDLL:
         L.loglinear_bwd.restype = I
         L.loglinear_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P]
         L.loglinear_decode_step.restype = I
+        L.loglinear_fwd_grouped.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P, I]
+        L.loglinear_fwd_grouped.restype = I
+        L.loglinear_prefill_grouped.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P, I]
+        L.loglinear_prefill_grouped.restype = I
+        L.loglinear_decode_step_grouped.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        L.loglinear_decode_step_grouped.restype = I
+        L.loglinear_bwd_grouped_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.loglinear_bwd_grouped_workspace_bytes.restype = Z
+        L.loglinear_bwd_grouped.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P]
+        L.loglinear_bwd_grouped.restype = I
         L.loglinear_last_error.argtypes = []
         L.loglinear_last_error.restype = ctypes.c_char_p
         L.loglinear_profile_begin.argtypes = [I]
@@ -122,6 +132,18 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+def _qkv_shapes(q, k, v):
+    """(B, H, Hqk, T, dk, dv) from q, k [B,Hqk,T,dk] and v [B,H,T,dv]; H must
+    be a multiple of Hqk (Hqk = H: one q/k head per head)."""
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[0] != q.shape[0] or v.shape[2] != q.shape[2]:
+        raise ValueError("q, k must be [B,Hqk,T,dk] and v [B,H,T,dv]")
+    B, Hqk, T, dk = q.shape
+    H, dv = v.shape[1], v.shape[3]
+    if Hqk == 0 or H % Hqk != 0:
+        raise ValueError(f"the number of heads H={H} must be a multiple of the q/k heads Hqk={Hqk}")
+    return B, H, Hqk, T, dk, dv
+
+
 def alloc_workspace(B, H, T, dk, dv, chunk, group_log2=-1, device="cuda") -> torch.Tensor | None:
     n = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
     if n == 0:
@@ -130,13 +152,12 @@ def alloc_workspace(B, H, T, dk, dv, chunk, group_log2=-1, device="cuda") -> tor
 
 
 def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: int = -1, stream=None):
-    """Forward pass.  q,k [B,H,T,dk], v [B,H,T,dv] (float32 or bfloat16, same
-    dtype), a [B,H,T] float32, lam [B,H,T,L] float32 with L = num_levels(T).
-    Returns out [B,H,T,dv] in the input dtype.  Asynchronous on ``stream``."""
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    """Forward pass.  q,k [B,Hqk,T,dk], v [B,H,T,dv] (float32 or bfloat16,
+    same dtype; Hqk = H, or H a multiple of Hqk when consecutive heads share
+    a q/k head), a [B,H,T] float32, lam [B,H,T,L] float32 with
+    L = num_levels(T).  Returns out [B,H,T,dv] in the input dtype.
+    Asynchronous on ``stream``."""
+    B, H, Hqk, T, dk, dv = _qkv_shapes(q, k, v)
     code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -152,9 +173,14 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().loglinear_fwd_ex(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
-        _dev(out, "out"), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    if Hqk == H:
+        st = lib().loglinear_fwd_ex(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+            _dev(out, "out"), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    else:
+        st = lib().loglinear_fwd_grouped(
+            _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+            _dev(out, "out"), B, H, Hqk, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
     _check(st)
     return out
 
@@ -165,10 +191,7 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
     position.  Inputs as for ``fwd``; state [B,H,Lcap,dk,dv] and logscale
     [B,H,Lcap] float32 are written (free slots untouched).  Decoding continues
     with ``decode_step`` at pos = T.  Returns out [B,H,T,dv]."""
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    B, H, Hqk, T, dk, dv = _qkv_shapes(q, k, v)
     code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
@@ -189,26 +212,30 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().loglinear_prefill(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
-        _dev(out, "out"), _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
-        B, H, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+            _dev(out, "out"), _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32))
+    if Hqk == H:
+        st = lib().loglinear_prefill(*ptrs, B, H, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream),
+                                     group_log2)
+    else:
+        st = lib().loglinear_prefill_grouped(*ptrs, B, H, Hqk, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes,
+                                             _stream(stream), group_log2)
     _check(st)
     return out
 
 
-def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int) -> int:
-    return int(lib().loglinear_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+def bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int, Hqk: int | None = None) -> int:
+    if Hqk is None or Hqk == H:
+        return int(lib().loglinear_bwd_workspace_bytes(B, H, T, dk, dv, chunk))
+    return int(lib().loglinear_bwd_grouped_workspace_bytes(B, H, Hqk, T, dk, dv, chunk))
 
 
 def bwd(q, k, v, a, lam, dout, chunk: int = 64, workspace=None, stream=None):
     """Backward of ``fwd``: gradients of sum(dout * fwd(q, k, v, a, lam)).
-    Returns (dq, dk, dv, da, dlam): dq, dk, dv in the input dtype, da and
-    dlam float32.  Asynchronous on ``stream``."""
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
+    Returns (dq, dk, dv, da, dlam): dq, dk, dv in the input dtype (dq, dk
+    shaped like q, k: with shared q/k heads they sum over the heads sharing
+    each), da and dlam float32.  Asynchronous on ``stream``."""
+    B, H, Hqk, T, dk, dv = _qkv_shapes(q, k, v)
     code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype or dout.dtype != q.dtype:
         raise TypeError("q, k, v, dout must share one dtype")
@@ -220,25 +247,34 @@ def bwd(q, k, v, a, lam, dout, chunk: int = 64, workspace=None, stream=None):
     dv_ = torch.empty_like(v)
     da = torch.empty_like(a)
     dlam = torch.empty_like(lam)
-    need = bwd_workspace_bytes(B, H, T, dk, dv, chunk)
+    need = bwd_workspace_bytes(B, H, T, dk, dv, chunk, Hqk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().loglinear_bwd(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
-        _dev(dout, "dout"), _dev(dq, "dq"), _dev(dk_, "dk"), _dev(dv_, "dv"), _dev(da, "da", torch.float32),
-        _dev(dlam, "dlam", torch.float32), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream))
+    ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+            _dev(dout, "dout"), _dev(dq, "dq"), _dev(dk_, "dk"), _dev(dv_, "dv"), _dev(da, "da", torch.float32),
+            _dev(dlam, "dlam", torch.float32))
+    if Hqk == H:
+        st = lib().loglinear_bwd(*ptrs, B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream))
+    else:
+        st = lib().loglinear_bwd_grouped(*ptrs, B, H, Hqk, T, dk, dv, chunk, code, ws_ptr, ws_bytes,
+                                         _stream(stream))
     _check(st)
     return dq, dk_, dv_, da, dlam
 
 
 def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
-    """One decode step.  q,k [S,H,dk], v [S,H,dv] (float32 or bfloat16),
-    a [S,H], lam [S,H,Lcap], state [S,H,Lcap,dk,dv] and logscale [S,H,Lcap]
-    float32 (updated in place), pos [S] int64.  Returns out [S,H,dv]."""
-    S, H, dk = q.shape
-    dv = v.shape[-1]
+    """One decode step.  q,k [S,Hqk,dk], v [S,H,dv] (float32 or bfloat16;
+    Hqk = H, or H a multiple of Hqk), a [S,H], lam [S,H,Lcap],
+    state [S,H,Lcap,dk,dv] and logscale [S,H,Lcap] float32 (updated in place),
+    pos [S] int64.  Returns out [S,H,dv]."""
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError("q, k must be [S,Hqk,dk] and v [S,H,dv]")
+    S, Hqk, dk = q.shape
+    H, dv = v.shape[1], v.shape[2]
+    if Hqk == 0 or H % Hqk != 0:
+        raise ValueError(f"the number of heads H={H} must be a multiple of the q/k heads Hqk={Hqk}")
     Lcap = state.shape[2]
     code = _dtype_code(q)
     if tuple(state.shape) != (S, H, Lcap, dk, dv) or tuple(logscale.shape) != (S, H, Lcap):
@@ -247,10 +283,13 @@ def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
         raise ValueError("lam must be [S,H,Lcap], a [S,H], pos [S]")
     if out is None:
         out = torch.empty((S, H, dv), dtype=q.dtype, device=q.device)
-    st = lib().loglinear_decode_step(
-        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
-        _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
-        _dev(pos, "pos", torch.int64), _dev(out, "out"), S, H, dk, dv, Lcap, code, _stream(stream))
+    ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+            _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
+            _dev(pos, "pos", torch.int64), _dev(out, "out"))
+    if Hqk == H:
+        st = lib().loglinear_decode_step(*ptrs, S, H, dk, dv, Lcap, code, _stream(stream))
+    else:
+        st = lib().loglinear_decode_step_grouped(*ptrs, S, H, Hqk, dk, dv, Lcap, code, _stream(stream))
     _check(st)
     return out
 

@@ -110,6 +110,17 @@ static ll_status check_fwd_shape(const char *who, int B, int H, int T, int dk, i
     return LL_OK;
 }
 
+// Hqk q/k heads shared by H heads: Hqk >= 1 and H a multiple of it (with
+// H = 0 there is nothing to share and any Hqk >= 0 passes).
+static ll_status check_qk_heads(const char *who, int H, int Hqk)
+{
+    if (H == 0 && Hqk >= 0)
+        return LL_OK;
+    if (Hqk <= 0 || H % Hqk != 0)
+        return fail(LL_EINVAL, "%s: H=%d must be a positive multiple of Hqk=%d", who, H, Hqk);
+    return LL_OK;
+}
+
 size_t loglinear_fwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int chunk, int group_log2)
 {
     if (check_fwd_shape("loglinear_fwd_workspace_bytes", B, H, T, dk, dv, chunk) != LL_OK)
@@ -131,7 +142,7 @@ struct StackOut {
 };
 
 static ll_status run_fwd(const char *who, const void *q, const void *k, const void *v, const float *a,
-                         const float *lambda, void *out, int B, int H, int T, int dk, int dv, int chunk,
+                         const float *lambda, void *out, int B, int H, int Hqk, int T, int dk, int dv, int chunk,
                          ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, int group_log2,
                          const StackOut *so)
 {
@@ -139,6 +150,8 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
         return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
     ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
     if (st != LL_OK)
+        return st;
+    if ((st = check_qk_heads(who, H, Hqk)) != LL_OK)
         return st;
     if (group_log2 > ll::kMaxGroupLog2)
         return fail(LL_EUNSUPPORTED, "%s: group_log2 %d above %d", who, group_log2, ll::kMaxGroupLog2);
@@ -163,7 +176,7 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
     if (rows == 0)
         return ok();
     const size_t es = bf16 ? 2 : 4;
-    const size_t nq = (size_t)rows * dk * es, nv = (size_t)rows * dv * es;
+    const size_t nq = (size_t)B * Hqk * T * dk * es, nv = (size_t)rows * dv * es;
     const void *ptrs[] = {q, k, v, out};
     const char *names[] = {"q", "k", "v", "out"};
     for (int i = 0; i < 4; ++i) {
@@ -212,6 +225,7 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
             return fail(LL_EINVAL, "%s: state and logscale overlap", who);
     }
     ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
+    args.rqk = H / Hqk;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     bool nat = false;
     hipError_t e = ll::fwd_launch(args, plan, s, &nat);
@@ -225,6 +239,7 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
                          plan.nL > 0 ? reinterpret_cast<const float *>(ws + plan.off_Gam) : nullptr,
                          so->state, so->logscale, (int)bh, T, dk, dv, lgc, plan.nG, plan.nL, plan.nLeft, so->Lcap,
                          bf16, nat};
+        sa.rqk = H / Hqk;
         e = ll::stack_launch(sa, s);
         if (e != hipSuccess)
             return fail(LL_EDEVICE, "%s: stack launch failed: %s", who, hipGetErrorString(e));
@@ -236,7 +251,15 @@ ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v, const fl
                            void *out, int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
                            void *workspace, size_t workspace_bytes, void *stream, int group_log2)
 {
-    return run_fwd("loglinear_fwd", q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace,
+    return run_fwd("loglinear_fwd", q, k, v, a, lambda, out, B, H, H, T, dk, dv, chunk, dtype, workspace,
+                   workspace_bytes, stream, group_log2, nullptr);
+}
+
+ll_status loglinear_fwd_grouped(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                                void *out, int B, int H, int Hqk, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                                void *workspace, size_t workspace_bytes, void *stream, int group_log2)
+{
+    return run_fwd("loglinear_fwd_grouped", q, k, v, a, lambda, out, B, H, Hqk, T, dk, dv, chunk, dtype, workspace,
                    workspace_bytes, stream, group_log2, nullptr);
 }
 
@@ -246,8 +269,18 @@ ll_status loglinear_prefill(const void *q, const void *k, const void *v, const f
                             void *stream, int group_log2)
 {
     const StackOut so{state, logscale, Lcap};
-    return run_fwd("loglinear_prefill", q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace,
+    return run_fwd("loglinear_prefill", q, k, v, a, lambda, out, B, H, H, T, dk, dv, chunk, dtype, workspace,
                    workspace_bytes, stream, group_log2, &so);
+}
+
+ll_status loglinear_prefill_grouped(const void *q, const void *k, const void *v, const float *a,
+                                    const float *lambda, void *out, float *state, float *logscale, int B, int H,
+                                    int Hqk, int T, int dk, int dv, int chunk, int Lcap, ll_dtype dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream, int group_log2)
+{
+    const StackOut so{state, logscale, Lcap};
+    return run_fwd("loglinear_prefill_grouped", q, k, v, a, lambda, out, B, H, Hqk, T, dk, dv, chunk, dtype,
+                   workspace, workspace_bytes, stream, group_log2, &so);
 }
 
 ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float *a, const float *lambda, void *out,
@@ -258,25 +291,33 @@ ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float
                             stream, -1);
 }
 
-size_t loglinear_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
+size_t loglinear_bwd_grouped_workspace_bytes(int B, int H, int Hqk, int T, int dk, int dv, int chunk)
 {
     if (check_fwd_shape("loglinear_bwd_workspace_bytes", B, H, T, dk, dv, chunk) != LL_OK)
         return 0;
+    if (Hqk <= 0 || (H > 0 && H % Hqk != 0))
+        return 0;
     if ((int64_t)B * H * T == 0)
         return 0;
-    return ll::bwd_plan(B, H, T, dk, dv, chunk).bytes;
+    return ll::bwd_plan(B, H, T, dk, dv, chunk, H / Hqk).bytes;
 }
 
-ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float *a, const float *lambda,
-                        const void *dout, void *dq, void *dk_out, void *dv_out, float *da, float *dlambda, int B,
-                        int H, int T, int dk, int dv, int chunk, ll_dtype dtype, void *workspace,
-                        size_t workspace_bytes, void *stream)
+size_t loglinear_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
 {
-    const char *who = "loglinear_bwd";
+    return loglinear_bwd_grouped_workspace_bytes(B, H, H > 0 ? H : 1, T, dk, dv, chunk);
+}
+
+static ll_status run_bwd(const char *who, const void *q, const void *k, const void *v, const float *a,
+                         const float *lambda, const void *dout, void *dq, void *dk_out, void *dv_out, float *da,
+                         float *dlambda, int B, int H, int Hqk, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
     if (dtype != LL_F32 && dtype != LL_BF16)
         return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
     ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
     if (st != LL_OK)
+        return st;
+    if ((st = check_qk_heads(who, H, Hqk)) != LL_OK)
         return st;
     const bool bf16 = dtype == LL_BF16;
     if (!ll::bwd_supported(bf16, dk, dv, chunk))
@@ -291,7 +332,7 @@ ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float
     if (L > ll::kMaxLevels)
         return fail(LL_EUNSUPPORTED, "%s: T=%d needs %d levels (max %d)", who, T, L, ll::kMaxLevels);
     const size_t es = bf16 ? 2 : 4;
-    const size_t nq = (size_t)rows * dk * es, nv = (size_t)rows * dv * es, na = (size_t)rows * 4,
+    const size_t nq = (size_t)B * Hqk * T * dk * es, nv = (size_t)rows * dv * es, na = (size_t)rows * 4,
                  nl = (size_t)rows * L * 4;
     const void *ins[] = {q, k, v, dout};
     const char *inames[] = {"q", "k", "v", "dout"};
@@ -313,7 +354,7 @@ ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float
         return fail(LL_EINVAL, "%s: a, lambda, da and dlambda must be non-NULL", who);
     if (!aligned(a, 4) || !aligned(lambda, 4) || !aligned(da, 4) || !aligned(dlambda, 4))
         return fail(LL_EINVAL, "%s: a, lambda, da and dlambda must be 4-byte aligned", who);
-    const ll::BwdPlan plan = ll::bwd_plan(B, H, T, dk, dv, chunk);
+    const ll::BwdPlan plan = ll::bwd_plan(B, H, T, dk, dv, chunk, H / Hqk);
     if (!workspace)
         return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, plan.bytes);
     if (workspace_bytes < plan.bytes)
@@ -332,20 +373,41 @@ ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float
         return fail(LL_EINVAL, "%s: workspace aliases an input", who);
     ll::BwdArgs args{q, k, v, dout, a, lambda, dq, dk_out, dv_out, da, dlambda, B, H, T, dk, dv, chunk, L, bf16,
                      workspace};
+    args.rqk = H / Hqk;
     hipError_t e = ll::bwd_launch(args, plan, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
     return ok();
 }
 
-ll_status loglinear_decode_step(const void *q, const void *k, const void *v, const float *a, const float *lambda,
-                                float *state, float *logscale, const int64_t *pos, void *out, int S, int H, int dk,
-                                int dv, int Lcap, ll_dtype dtype, void *stream)
+ll_status loglinear_bwd(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                        const void *dout, void *dq, void *dk_out, void *dv_out, float *da, float *dlambda, int B,
+                        int H, int T, int dk, int dv, int chunk, ll_dtype dtype, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    return run_bwd("loglinear_bwd", q, k, v, a, lambda, dout, dq, dk_out, dv_out, da, dlambda, B, H, H, T, dk, dv,
+                   chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+ll_status loglinear_bwd_grouped(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                                const void *dout, void *dq, void *dk_out, void *dv_out, float *da, float *dlambda,
+                                int B, int H, int Hqk, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_bwd("loglinear_bwd_grouped", q, k, v, a, lambda, dout, dq, dk_out, dv_out, da, dlambda, B, H, Hqk,
+                   T, dk, dv, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+static ll_status run_decode(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                            float *state, float *logscale, const int64_t *pos, void *out, int S, int H, int Hqk,
+                            int dk, int dv, int Lcap, ll_dtype dtype, void *stream)
 {
     if (dtype != LL_F32 && dtype != LL_BF16)
         return fail(LL_EINVAL, "loglinear_decode_step: unknown dtype %d", (int)dtype);
     if (S < 0 || H < 0 || dk <= 0 || dv <= 0)
         return fail(LL_EINVAL, "loglinear_decode_step: bad size (S=%d H=%d dk=%d dv=%d)", S, H, dk, dv);
+    if (check_qk_heads("loglinear_decode_step", H, Hqk) != LL_OK)
+        return LL_EINVAL;
     if (Lcap < 1)
         return fail(LL_EINVAL, "loglinear_decode_step: Lcap must be >= 1 (got %d)", Lcap);
     if (Lcap < 2 || Lcap > ll::kMaxLevels)
@@ -371,16 +433,32 @@ ll_status loglinear_decode_step(const void *q, const void *k, const void *v, con
         return fail(LL_EINVAL, "loglinear_decode_step: misaligned a/lambda/logscale/pos");
     const size_t sh = (size_t)S * H;
     const size_t es = bf16 ? 2 : 4;
-    const size_t nst = sh * Lcap * dk * dv * 4, nout = sh * dv * es;
+    const size_t nst = sh * Lcap * dk * dv * 4, nout = sh * dv * es, nq = (size_t)S * Hqk * dk * es;
     if (overlaps(state, nst, out, nout) || overlaps(state, nst, logscale, sh * Lcap * 4) ||
-        overlaps(out, nout, q, sh * dk * es) || overlaps(out, nout, k, sh * dk * es) ||
+        overlaps(out, nout, q, nq) || overlaps(out, nout, k, nq) ||
         overlaps(out, nout, v, nout) || overlaps(out, nout, logscale, sh * Lcap * 4))
         return fail(LL_EINVAL, "loglinear_decode_step: state, logscale and out must not alias each other or inputs");
     ll::DecodeArgs args{q, k, v, a, lambda, state, logscale, pos, out, S, H, dk, dv, Lcap, bf16};
+    args.rqk = H / Hqk;
     hipError_t e = ll::decode_launch(args, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(LL_EDEVICE, "loglinear_decode_step: launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+ll_status loglinear_decode_step(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                                float *state, float *logscale, const int64_t *pos, void *out, int S, int H, int dk,
+                                int dv, int Lcap, ll_dtype dtype, void *stream)
+{
+    return run_decode(q, k, v, a, lambda, state, logscale, pos, out, S, H, H, dk, dv, Lcap, dtype, stream);
+}
+
+ll_status loglinear_decode_step_grouped(const void *q, const void *k, const void *v, const float *a,
+                                        const float *lambda, float *state, float *logscale, const int64_t *pos,
+                                        void *out, int S, int H, int Hqk, int dk, int dv, int Lcap, ll_dtype dtype,
+                                        void *stream)
+{
+    return run_decode(q, k, v, a, lambda, state, logscale, pos, out, S, H, Hqk, dk, dv, Lcap, dtype, stream);
 }
 
 const char *loglinear_last_error(void) { return g_err.c_str(); }

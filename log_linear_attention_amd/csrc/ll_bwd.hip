@@ -705,7 +705,6 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
                                                      typename B::T *__restrict__ W1, typename B::T *__restrict__ W2,
                                                      int Tlen, int L, int N, int NP, int NB)
 {
-    using T = typename B::T;
     constexpr int C = B::C, DK = B::DK, DV = B::DV, VEC = B::VEC;
     __shared__ WpSmem<B> sm;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, qd = lane >> 4;
@@ -1020,6 +1019,44 @@ __global__ __launch_bounds__(256) void ll_bwd_da(const float *__restrict__ daloc
 }
 
 // ---------------------------------------------------------------------------
+// q/k shared by several heads.  The gradient of a shared q or k row is the
+// sum of the per-head gradients of the heads that read it; the backward runs
+// per head on a copy of q and k laid out per head and then sums.
+// ---------------------------------------------------------------------------
+
+// dst row block of head bh <- src row block of q/k head bh / rqk (16-byte
+// vectors; hv vectors per head).
+__global__ __launch_bounds__(256) void ll_bcast_heads(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                      size_t hv, int rqk, size_t total)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const size_t bh = i / hv, e = i - bh * hv;
+        dst[i] = src[(bh / rqk) * hv + e];
+    }
+}
+
+// dst[qbh] = sum over the rqk heads j of src[qbh * rqk + j], four elements
+// per thread, fp32 accumulation (he elements per head).
+template <class T>
+__global__ __launch_bounds__(256) void ll_sum_heads(const T *__restrict__ src, T *__restrict__ dst, size_t he,
+                                                    int rqk, size_t total4)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (size_t)gridDim.x * 256) {
+        const size_t qbh = (4 * i) / he, e = 4 * i - qbh * he;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < rqk; ++j) {
+            const T *x = src + ((size_t)qbh * rqk + j) * he + e;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[c] += to_f32(x[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            dst[4 * i + c] = from_f32<T>(acc[c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 static int bwd_levels(int N)
@@ -1174,7 +1211,7 @@ bool bwd_supported(bool bf16, int dk, int dv, int chunk)
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk)
+BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int rqk)
 {
     BwdPlan p;
     const size_t BH = (size_t)B * H;
@@ -1193,7 +1230,22 @@ BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk)
     p.off_mk = al256(p.off_mq + BH * kMaxLevels * (size_t)(N + 1) * 4);
     p.off_gp = al256(p.off_mk + BH * kMaxLevels * (size_t)(N + 1) * 4);
     p.bytes = al256(p.off_gp + BH * (size_t)N * 8);
+    if (rqk > 1) {
+        // per-head copies of q and k and per-head dq, dk (sized for float32)
+        const size_t hq = BH * (size_t)T * dk * 4;
+        p.off_qx = p.bytes;
+        p.off_kx = al256(p.off_qx + hq);
+        p.off_gqx = al256(p.off_kx + hq);
+        p.off_gkx = al256(p.off_gqx + hq);
+        p.bytes = al256(p.off_gkx + hq);
+    }
     return p;
+}
+
+static unsigned grid_for(size_t n)
+{
+    const size_t g = (n + 255) / 256;
+    return (unsigned)(g < 16384 ? (g > 0 ? g : 1) : 16384);
 }
 
 hipError_t bwd_launch(const BwdArgs &args, const BwdPlan &plan, hipStream_t stream)
@@ -1201,7 +1253,45 @@ hipError_t bwd_launch(const BwdArgs &args, const BwdPlan &plan, hipStream_t stre
     BwdLauncher f = find_bwd(args.bf16, args.dk, args.dv, args.chunk);
     if (!f)
         return hipErrorInvalidValue;
-    return f(args, plan, stream);
+    if (args.rqk <= 1)
+        return f(args, plan, stream);
+    // Shared q/k: per-head copies in, per-head dq/dk out, then the sums.
+    char *ws = static_cast<char *>(args.workspace);
+    const size_t es = args.bf16 ? 2 : 4;
+    const size_t BH = (size_t)args.B * args.H;
+    const size_t he = (size_t)args.T * args.dk;   // elements per head
+    const size_t hv = he * es / 16, total = BH * hv;
+    BwdArgs a = args;
+    a.q = ws + plan.off_qx;
+    a.k = ws + plan.off_kx;
+    a.gq = ws + plan.off_gqx;
+    a.gk = ws + plan.off_gkx;
+    ProfEvents pe = prof_events("ll_bcast_heads");
+    hipExtLaunchKernelGGL(ll_bcast_heads, dim3(grid_for(total)), dim3(256), 0, stream, pe.start, pe.stop, 0,
+                          (const uint4 *)args.q, (uint4 *)(ws + plan.off_qx), hv, args.rqk, total);
+    pe = prof_events("ll_bcast_heads");
+    hipExtLaunchKernelGGL(ll_bcast_heads, dim3(grid_for(total)), dim3(256), 0, stream, pe.start, pe.stop, 0,
+                          (const uint4 *)args.k, (uint4 *)(ws + plan.off_kx), hv, args.rqk, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if ((e = f(a, plan, stream)) != hipSuccess)
+        return e;
+    const size_t total4 = BH / args.rqk * he / 4;
+    for (int which = 0; which < 2; ++which) {
+        const void *src = which ? a.gk : a.gq;
+        void *dst = which ? args.gk : args.gq;
+        pe = prof_events("ll_sum_heads");
+        if (args.bf16)
+            hipExtLaunchKernelGGL(ll_sum_heads<__bf16>, dim3(grid_for(total4)), dim3(256), 0, stream, pe.start,
+                                  pe.stop, 0, (const __bf16 *)src, (__bf16 *)dst, he, args.rqk, total4);
+        else
+            hipExtLaunchKernelGGL(ll_sum_heads<float>, dim3(grid_for(total4)), dim3(256), 0, stream, pe.start,
+                                  pe.stop, 0, (const float *)src, (float *)dst, he, args.rqk, total4);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ll

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
                                                  const float *__restrict__ a, const float *__restrict__ lam,
                                                  float *__restrict__ state, float *__restrict__ logscale,
                                                  const int64_t *__restrict__ pos, typename D::T *__restrict__ out,
-                                                 int H, int Lcap)
+                                                 int H, int Lcap, int rqk)
 {
     using T = typename D::T;
     constexpr int DK = D::DK, DV = D::DV;
@@ -99,9 +99,10 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
         return;
     }
 
+    const size_t qkrow = (size_t)(sh / rqk) * DK;   // q and k are shared by rqk heads
     for (int d = tid; d < DK; d += D::NT) {
-        qs[d] = to_f32(q[(size_t)sh * DK + d]);
-        ks[d] = to_f32(k[(size_t)sh * DK + d]);
+        qs[d] = to_f32(q[qkrow + d]);
+        ks[d] = to_f32(k[qkrow + d]);
     }
     for (int e = tid; e < DV; e += D::NT)
         vs[e] = to_f32(v[(size_t)sh * DV + e]);
@@ -233,7 +234,7 @@ static hipError_t launch_dec_t(const DecodeArgs &A, hipStream_t s)
     const ProfEvents pe = prof_events("ll_decode");
     hipExtLaunchKernelGGL(ll_decode<D>, dim3(A.S * A.H), dim3(D::NT), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
                           (const T *)A.k, (const T *)A.v, A.a, A.lam, A.state, A.logscale, A.pos, (T *)A.out, A.H,
-                          A.Lcap);
+                          A.Lcap, A.rqk);
     return hipGetLastError();
 }
 

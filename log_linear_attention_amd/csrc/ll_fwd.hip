@@ -338,7 +338,7 @@ struct StateRegs {
 
 template <class F>
 __device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T *k, const typename F::T *v,
-                                           const float *a, size_t row0, int tid)
+                                           const float *a, size_t row0, size_t krow0, int tid)
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -346,7 +346,7 @@ __device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T 
         const int idx = tid + i * F::NT;
         r.k[i] = zero16();
         if (idx < F::QVEC)
-            r.k[i] = *reinterpret_cast<const uint4 *>(k + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
+            r.k[i] = *reinterpret_cast<const uint4 *>(k + (krow0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
     }
 #pragma unroll
     for (int i = 0; i < F::NV; ++i) {
@@ -362,13 +362,15 @@ template <class F>
 __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__restrict__ k,
                                                         const typename F::T *__restrict__ v,
                                                         const float *__restrict__ a, int Tlen, int g, int nG,
-                                                        int nL, float *__restrict__ Sg, float *__restrict__ Gam)
+                                                        int nL, int rqk, float *__restrict__ Sg,
+                                                        float *__restrict__ Gam)
 {
     using Frag = typename F::Frag;
     __shared__ StateSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x / nL, sg = blockIdx.x % nL;
     const int G = 1 << g;
+    const size_t hrow = (size_t)bh * Tlen, krow = (size_t)(bh / rqk) * Tlen;   // k is shared by rqk heads
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 
     if constexpr (F::TR) {
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
     float gsum = 0.f;
 
     StateRegs<F> pf;
-    state_load<F>(pf, k, v, a, (size_t)bh * Tlen + (size_t)sg * G * F::C, tid);
+    state_load<F>(pf, k, v, a, hrow + (size_t)sg * G * F::C, krow + (size_t)sg * G * F::C, tid);
     for (int ci = 0; ci < G; ++ci) {
         __syncthreads();
 #pragma unroll
@@ -403,7 +405,8 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
         }
         scan_decay<F>(pf.a, sm.Aloc, &sm.gch, tid);
         if (ci + 1 < G)
-            state_load<F>(pf, k, v, a, (size_t)bh * Tlen + ((size_t)sg * G + ci + 1) * F::C, tid);
+            state_load<F>(pf, k, v, a, hrow + ((size_t)sg * G + ci + 1) * F::C, krow + ((size_t)sg * G + ci + 1) * F::C,
+                          tid);
         __syncthreads();
         const float gch = sm.gch;
         const float dec = __expf(gch);
@@ -566,7 +569,7 @@ struct WalkRegs {
 template <class F>
 __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q, const typename F::T *k,
                                           const typename F::T *v, const float *a, const float *lam, size_t row0,
-                                          int valid, int L, float invL, int tid)
+                                          size_t qrow0, int valid, int L, float invL, int tid)
 {
     constexpr int QPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -575,8 +578,8 @@ __device__ __forceinline__ void walk_load(WalkRegs<F> &r, const typename F::T *q
         const int j = idx / QPR, c = idx % QPR;
         r.q[i] = r.k[i] = zero16();
         if (idx < F::QVEC && j < valid) {
-            r.q[i] = ld_stream(q + (row0 + j) * F::DK + c * F::VEC);
-            r.k[i] = ld_stream(k + (row0 + j) * F::DK + c * F::VEC);
+            r.q[i] = ld_stream(q + (qrow0 + j) * F::DK + c * F::VEC);
+            r.k[i] = ld_stream(k + (qrow0 + j) * F::DK + c * F::VEC);
         }
     }
 #pragma unroll
@@ -708,7 +711,7 @@ template <class F>
 __global__ __launch_bounds__(F::NT) void ll_chunk_walk_rs(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
-    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
+    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, int rqk, const float *__restrict__ Gam,
     const typename F::T *__restrict__ Dg)
 {
     using T = typename F::T;
@@ -725,7 +728,8 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk_rs(
     const float invL = 1.f / (float)L;
 
     WalkRegs<F> pf;
-    walk_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
+    const size_t qkrow = (size_t)(bh / rqk) * Tlen;   // q and k are shared by rqk heads
+    walk_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C, qkrow + (size_t)sg * G * F::C,
                  min(F::C, Tlen - sg * G * F::C), L, invL, tid);
 
     // Padding rows (CP > C) and the transposed copies start at zero.
@@ -800,7 +804,8 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk_rs(
         __syncthreads();
         walk_store<F>(pf, sm, valid, L, invL, tid);
         if (ci + 1 < nchunk)
-            walk_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, invL, tid);
+            walk_load<F>(pf, q, k, v, a, lam, row0 + F::C, qkrow + t0 + F::C, min(F::C, Tlen - t0 - F::C), L, invL,
+                         tid);
         __syncthreads();
         const float gch = sm.gch;
 
@@ -986,7 +991,7 @@ struct Walk4Regs {
 template <class F>
 __device__ __forceinline__ void walk4_load(Walk4Regs<F> &r, const typename F::T *q, const typename F::T *k,
                                            const typename F::T *v, const float *a, const float *lam, size_t row0,
-                                           int valid, int L, int tid)
+                                           size_t qrow0, int valid, int L, int tid)
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
@@ -994,8 +999,8 @@ __device__ __forceinline__ void walk4_load(Walk4Regs<F> &r, const typename F::T 
         const int idx = tid + i * F::NT;
         r.q[i] = r.k[i] = zero16();
         if (idx < F::KVEC && idx / KPR < valid) {
-            r.q[i] = ld_stream(q + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
-            r.k[i] = ld_stream(k + (row0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
+            r.q[i] = ld_stream(q + (qrow0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
+            r.k[i] = ld_stream(k + (qrow0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
         }
     }
 #pragma unroll
@@ -1120,7 +1125,7 @@ template <class F>
 __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
-    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
+    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, int rqk, const float *__restrict__ Gam,
     const typename F::T *__restrict__ Dg)
 {
     using T = typename F::T;
@@ -1136,7 +1141,8 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
     const float invL = 1.f / (float)L;
 
     Walk4Regs<F> pf;
-    walk4_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C,
+    const size_t qkrow = (size_t)(bh / rqk) * Tlen;   // q and k are shared by rqk heads
+    walk4_load<F>(pf, q, k, v, a, lam, (size_t)bh * Tlen + (size_t)sg * G * F::C, qkrow + (size_t)sg * G * F::C,
                   min(F::C, Tlen - sg * G * F::C), L, tid);
 
     // Padding rows of K and V, P (its upper tiles and padding columns are
@@ -1195,7 +1201,7 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk(
         __syncthreads();
         walk4_store<F>(pf, sm, valid, L, invL, tid);
         if (ci + 1 < nchunk)
-            walk4_load<F>(pf, q, k, v, a, lam, row0 + F::C, min(F::C, Tlen - t0 - F::C), L, tid);
+            walk4_load<F>(pf, q, k, v, a, lam, row0 + F::C, qkrow + t0 + F::C, min(F::C, Tlen - t0 - F::C), L, tid);
         __syncthreads();
         const float gch = sm.gch;
         // This lane's query rows (one per query tile of the wave), their
@@ -1711,14 +1717,14 @@ __device__ __forceinline__ int ws_token(const WSGroups &gr, int G, int kk)
 template <class F>
 __device__ __forceinline__ void ws_helper(WalkWSSmem<F> &sm, const typename F::T *q, const typename F::T *k,
                                           const typename F::T *v, const float *a, const float *lam, int Tlen, int L,
-                                          int bh, const WSGroups &gr, int G, int ty)
+                                          int bh, int qbh, const WSGroups &gr, int G, int ty)
 {
     using Frag = typename F::Frag;
     const int lane = ty & 63, yw = ty >> 6, qd = lane >> 4, li = lane & 15;
     const int u = yw % F::YU, c0 = yw / F::YU;
-    const size_t hrow = (size_t)bh * Tlen;
-    const WSBuf bf = {head_rsrc(q + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
-                      head_rsrc(k + hrow * F::DK, (uint32_t)Tlen * F::DK * 2),
+    const size_t hrow = (size_t)bh * Tlen, qrow = (size_t)qbh * Tlen;
+    const WSBuf bf = {head_rsrc(q + qrow * F::DK, (uint32_t)Tlen * F::DK * 2),
+                      head_rsrc(k + qrow * F::DK, (uint32_t)Tlen * F::DK * 2),
                       head_rsrc(v + hrow * F::DV, (uint32_t)Tlen * F::DV * 2),
                       head_rsrc(lam + hrow * L, (uint32_t)Tlen * L * 4), head_rsrc(a + hrow, (uint32_t)Tlen * 4)};
     // The chunks of both groups form one stream kk = 0 .. K-1, chunk kk in
@@ -2061,19 +2067,22 @@ template <class F>
 __global__ __launch_bounds__(F::NT) void ll_chunk_walk_ws(
     const typename F::T *__restrict__ q, const typename F::T *__restrict__ k, const typename F::T *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, typename F::T *__restrict__ out, int Tlen, int L,
-    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, const float *__restrict__ Gam,
+    int log2C, int g, int N, int nG, int Plev, int nL, int nLeft, int rqk, const float *__restrict__ Gam,
     const typename F::T *__restrict__ Dg)
 {
     __shared__ WalkWSSmem<F> sm;
     const int tid = threadIdx.x, wave = tid >> 6;
     // Work item of this workgroup.  Workgroups b, b+8, b+16, ... run on the
     // same XCD (and share its L2); each XCD gets a contiguous range of items,
-    // so the block states a head's groups read stay in one L2.
+    // so the block states a head's groups read stay in one L2.  Items run
+    // over (q/k head, group pair, head of that q/k head), so the rqk heads
+    // that read the same q and k chunks run side by side on one XCD.
     const int nb = (int)gridDim.x, bid = (int)blockIdx.x;
     const int per = nb >> 3, rem = nb & 7, xcd = bid & 7;
     const int wid = xcd * per + min(xcd, rem) + (bid >> 3);
     const int npair = (nG + 1) >> 1;
-    const int bh = wid / npair, pr = wid % npair;
+    const int qbh = wid / (npair * rqk), pr = (wid / rqk) % npair;
+    const int bh = qbh * rqk + wid % rqk;
     const int G = 1 << g;
     WSGroups gr;
     gr.sg0 = pr;
@@ -2082,7 +2091,7 @@ __global__ __launch_bounds__(F::NT) void ll_chunk_walk_ws(
     gr.n0 = min(G, N - pr * G);
     gr.n1 = (gr.n == 2) ? min(G, N - gr.sg1 * G) : 0;
     if (wave >= F::NX)
-        ws_helper<F>(sm, q, k, v, a, lam, Tlen, L, bh, gr, G, tid - 64 * F::NX);
+        ws_helper<F>(sm, q, k, v, a, lam, Tlen, L, bh, qbh, gr, G, tid - 64 * F::NX);
     else
         ws_compute<F>(sm, out, Tlen, L, log2C, g, bh, gr, nG, Plev, nL, nLeft, Gam, Dg, tid);
 }
@@ -2162,7 +2171,7 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     if (P.nL > 0) {
         ProfEvents pe = prof_events("ll_group_state");
         hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
-                              (const T *)A.k, (const T *)A.v, A.a, A.T, P.g, P.nG, P.nL, Sg, Gam);
+                              (const T *)A.k, (const T *)A.v, A.a, A.T, P.g, P.nG, P.nL, A.rqk, Sg, Gam);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -2210,7 +2219,7 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         if (use_ws) {
             hipExtLaunchKernelGGL(ll_chunk_walk_ws<WS>, dim3(BH * ((P.nG + 1) / 2)), dim3(WS::NT), 0, s, pw.start,
                                   pw.stop, 0, (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out,
-                                  A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam,
+                                  A.T, A.L, log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, A.rqk, (const float *)Gam,
                                   (const T *)Dg);
             return hipGetLastError();
         }
@@ -2218,12 +2227,14 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
     if constexpr (F::TR && W4::FITS) {
         hipExtLaunchKernelGGL(ll_chunk_walk<W4>, dim3(BH * P.nG), dim3(W4::NT), 0, s, pw.start, pw.stop, 0,
                               (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L,
-                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
+                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, A.rqk, (const float *)Gam,
+                              (const T *)Dg);
     } else {
         using FW = Fwd<typename F::DTag, F::DK, F::DV, F::C, true>;
         hipExtLaunchKernelGGL(ll_chunk_walk_rs<FW>, dim3(BH * P.nG), dim3(FW::NT), 0, s, pw.start, pw.stop, 0,
                               (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.lam, (T *)A.out, A.T, A.L,
-                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, (const float *)Gam, (const T *)Dg);
+                              log2C, P.g, P.N, P.nG, P.Plev, P.nL, P.nLeft, A.rqk, (const float *)Gam,
+                              (const T *)Dg);
     }
     return hipGetLastError();
 }

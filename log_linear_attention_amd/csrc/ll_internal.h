@@ -36,6 +36,9 @@ struct FwdArgs {
     // when tree_nat is set (bf16 only).
     bool tree_only = false;
     bool tree_nat = false;
+    // Heads that share one q/k head: q and k are [B, H / rqk, T, dk] and
+    // head h reads q/k head h / rqk.
+    int rqk = 1;
 };
 
 // Profiling hook (implemented by the ABI layer): while profiling is on, a
@@ -61,6 +64,7 @@ struct DecodeArgs {
     void *out;
     int S, H, dk, dv, Lcap;
     bool bf16;
+    int rqk = 1;   // heads per q/k head: q, k are [S, H / rqk, dk]
 };
 
 bool decode_supported(bool bf16, int dk, int dv);
@@ -78,6 +82,7 @@ struct StackArgs {
     float *state, *logscale;
     int BH, T, dk, dv, lgc, nG, nL, nLeft, Lcap;
     bool bf16, nat;
+    int rqk = 1;   // heads per k head: k is [BH / rqk, T, dk]
 };
 
 bool stack_supported(bool bf16, int dk, int dv);
@@ -92,6 +97,7 @@ struct BwdArgs {
     int B, H, T, dk, dv, chunk, L;
     bool bf16;
     void *workspace;
+    int rqk = 1;   // heads per q/k head: q, k, gq, gk are [B, H / rqk, T, dk]
 };
 
 // Workspace of the backward: the tree over chunks (one chunk per group) of
@@ -101,9 +107,11 @@ struct BwdPlan {
     FwdPlan tree, fq;
     int NP = 0, NB = 0;
     size_t off_tree = 0, off_fq = 0, off_wp = 0, off_w1 = 0, off_w2 = 0, off_pq = 0, off_mq = 0, off_mk = 0, off_gp = 0, bytes = 0;
+    // shared q/k (rqk > 1): per-head copies of q, k and per-head dq, dk
+    size_t off_qx = 0, off_kx = 0, off_gqx = 0, off_gkx = 0;
 };
 
-BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk);
+BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int rqk = 1);
 bool bwd_supported(bool bf16, int dk, int dv, int chunk);
 hipError_t bwd_launch(const BwdArgs &args, const BwdPlan &plan, hipStream_t stream);
 hipError_t stack_launch(const StackArgs &args, hipStream_t stream);

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
                                                         const typename D::T *__restrict__ Dg,
                                                         const float *__restrict__ Gam, int Tlen, int lgc, int nG,
                                                         int nL, int nLeft, int nat, float *__restrict__ state,
-                                                        float *__restrict__ logscale, int Lcap)
+                                                        float *__restrict__ logscale, int Lcap, int rqk)
 {
     using T = typename D::T;
     constexpr int DK = D::DK, DV = D::DV, VEC = D::VEC;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
     const int hi = lo + n;
     const int t0 = (p >> lgc) << lgc;  // first key of the prompt's last group
     const bool whole = l >= 1 && l - 1 >= lgc;
-    const size_t head = (size_t)bh * Tlen;
+    const size_t head = (size_t)bh * Tlen, khead = (size_t)(bh / rqk) * Tlen;   // k is shared by rqk heads
     float *slot = state + (((size_t)bh * Lcap + l) * DK + row0) * DV;
 
     // Independent loads first: the tail decay's terms, the bucket's decays,
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
         for (int u = 0; u < D::NKL; ++u) {
             const int i = tid + D::NT * u;
             if (i < cnt * D::KV)
-                kq[u] = *reinterpret_cast<const uint4 *>(k + (head + lo + b0 + i / D::KV) * DK + row0 +
+                kq[u] = *reinterpret_cast<const uint4 *>(k + (khead + lo + b0 + i / D::KV) * DK + row0 +
                                                           (i % D::KV) * VEC);
         }
 #pragma unroll
@@ -317,7 +317,7 @@ static hipError_t launch_stack_t(const StackArgs &A, hipStream_t s)
     const dim3 grid(A.BH * (DK / D::RS), A.Lcap);
     hipExtLaunchKernelGGL(ll_prefill_stack<D>, grid, dim3(D::NT), 0, s, pe.start, pe.stop, 0, (const T *)A.k,
                           (const T *)A.v, A.a, (const T *)A.Dg, A.Gam, A.T, A.lgc, A.nG, A.nL, A.nLeft, (int)A.nat,
-                          A.state, A.logscale, A.Lcap);
+                          A.state, A.logscale, A.Lcap, A.rqk);
     return hipGetLastError();
 }
 

@@ -238,3 +238,71 @@ def test_bwd_workspace_and_empty(L):
     assert ll.bwd_workspace_bytes(0, 16, 16384, 128, 64, 64) == 0
     assert _bwd(L, T=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, da=None, dlam=None,
                 ws=None, wsb=0) == ll.LL_OK
+
+
+# --- q/k shared across heads ---------------------------------------------------
+
+def _fwd_g(L, **kw):
+    args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, lam=FAKE + 0x400000,
+                out=FAKE + 0x8000000, B=1, H=4, Hqk=2, T=64, dk=128, dv=64, chunk=64, dtype=ll.LL_BF16,
+                ws=None, wsb=0, stream=None, g=-1)
+    args.update(kw)
+    return L.loglinear_fwd_grouped(args["q"], args["k"], args["v"], args["a"], args["lam"], args["out"],
+                                   args["B"], args["H"], args["Hqk"], args["T"], args["dk"], args["dv"],
+                                   args["chunk"], args["dtype"], args["ws"], args["wsb"], args["stream"], args["g"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hqk=3), ll.LL_EINVAL),                 # 4 heads cannot share 3 q/k heads
+    (dict(Hqk=0), ll.LL_EINVAL),
+    (dict(Hqk=-2), ll.LL_EINVAL),
+    (dict(Hqk=8), ll.LL_EINVAL),                 # more q/k heads than heads
+    (dict(q=None), ll.LL_EINVAL),
+    (dict(out=FAKE + 0x7ff0), ll.LL_EINVAL),     # out overlaps the end of q (2 q/k heads: 32 KiB)
+    (dict(chunk=48), ll.LL_EUNSUPPORTED),
+])
+def test_fwd_grouped_rejects_bad_arguments(L, kw, status):
+    assert _fwd_g(L, **kw) == status
+    assert ll.last_error().startswith("loglinear_fwd_grouped")
+
+
+def test_fwd_grouped_q_size_follows_qk_heads(L):
+    # q of 2 heads x 64 tokens x 128 bf16 = 32 KiB: an out placed right after it is legal on the host side
+    # (the call fails only later, at the launch, which is not reached without a GPU: the workspace check
+    # comes first and T=1000 needs one)
+    assert _fwd_g(L, T=1000, out=FAKE + 2 * 1000 * 128 * 2) == ll.LL_EWORKSPACE
+    assert _fwd_g(L, T=1000, out=FAKE + 2 * 1000 * 128 * 2 - 16) == ll.LL_EINVAL
+
+
+def test_decode_grouped_rejects_bad_heads(L):
+    st = L.loglinear_decode_step_grouped(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                         FAKE + 0x1000000, FAKE + 0x9000000, FAKE + 0xa000000, FAKE + 0xb000000,
+                                         2, 6, 4, 128, 64, 17, ll.LL_BF16, None)
+    assert st == ll.LL_EINVAL
+    assert "Hqk" in ll.last_error()
+    # no heads: nothing to do
+    assert L.loglinear_decode_step_grouped(None, None, None, None, None, None, None, None, None,
+                                           2, 0, 1, 128, 64, 17, ll.LL_BF16, None) == ll.LL_OK
+
+
+def test_prefill_grouped_rejects_bad_heads(L):
+    st = L.loglinear_prefill_grouped(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                     FAKE + 0x8000000, FAKE + 0x9000000, FAKE + 0xa000000, 1, 4, 3, 64, 128, 64,
+                                     64, 17, ll.LL_BF16, None, 0, None, -1)
+    assert st == ll.LL_EINVAL
+    assert ll.last_error().startswith("loglinear_prefill_grouped")
+
+
+def test_bwd_grouped_workspace_and_heads(L):
+    per_head = ll.bwd_workspace_bytes(1, 16, 4096, 128, 64, 64)
+    shared = ll.bwd_workspace_bytes(1, 16, 4096, 128, 64, 64, Hqk=2)
+    # the shared form adds per-head copies of q, k and of their gradients
+    assert shared > per_head and shared % 256 == 0
+    assert ll.bwd_workspace_bytes(1, 16, 4096, 128, 64, 64, Hqk=16) == per_head
+    assert L.loglinear_bwd_grouped_workspace_bytes(1, 16, 3, 4096, 128, 64, 64) == 0
+    st = L.loglinear_bwd_grouped(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000,
+                                 FAKE + 0x500000, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000,
+                                 FAKE + 0x4000000, FAKE + 0x5000000, 1, 4, 3, 64, 128, 64, 64, ll.LL_BF16,
+                                 FAKE + 0x10000000, 1 << 30, None)
+    assert st == ll.LL_EINVAL
+    assert ll.last_error().startswith("loglinear_bwd_grouped")
