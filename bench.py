@@ -215,6 +215,47 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     }
 
 
+def measure_grouped(ll, torch, cfg, dsets, args, e0, e1, Hqk):
+    """The forward of the same workload with q and k shared by groups of
+    H/Hqk heads (the first Hqk q/k heads of each input set): K timed steps,
+    then per-kernel times.  Mandatory bytes drop by the q/k heads not read."""
+    gsets = [dict(d, q=d["q"][:, :Hqk].contiguous(), k=d["k"][:, :Hqk].contiguous()) for d in dsets]
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=cfg.torch_dtype, device=dsets[0]["q"].device)
+    ws = ll.alloc_workspace(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk, args.group_log2)
+
+    def step(i):
+        d = gsets[i % 3]
+        ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=cfg.chunk, out=out, workspace=ws,
+               group_log2=args.group_log2)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ll.profile_begin(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ks = {k: v[1] / v[0] for k, v in ll.profile_end().items()}
+    e = 2 if cfg.dtype == "bf16" else 4
+    fbytes, _ = fwd_algorithmic(cfg)
+    gbytes = fbytes - cfg.B * (cfg.H - Hqk) * cfg.T * 2 * cfg.dk * e
+    walk_gbs = gbytes / (ks["ll_chunk_walk"] * 1e-3) / 1e9
+    log(f"grouped forward Hqk={Hqk}: {ms:.4f} ms/step; walk {ks['ll_chunk_walk'] * 1e3:.1f} us, {walk_gbs:.1f} GB/s")
+    return {
+        "workload": f"fwd_bf16_T16K with {Hqk} q/k heads for {cfg.H} heads", "Hqk": Hqk,
+        "ms_per_step": round(ms, 5), "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+        "algorithmic_bytes": gbytes, "kernels_ms": {k: round(v, 5) for k, v in ks.items()},
+        "walk_hbm_frac": round(walk_gbs / HBM_PEAK_GBS, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +412,9 @@ def main():
     log(f"prefill: {pre_ms:.4f} ms/step (forward alone {fwd_ms:.4f}); stack kernel {stack_ms:.4f} ms, "
         f"{stack_gbs:.1f} GB/s")
 
+    # ---- q/k shared across heads: the same forward with fewer q/k heads ----
+    grouped = [measure_grouped(ll, torch, cfg, dsets, args, e0, e1, hq) for hq in (4, 1)]
+
     # ---- backward: gradients of the forward on the same workload ----
     backward = None if args.no_bwd else measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1)
 
@@ -415,6 +459,7 @@ def main():
                          "frac": round(stack_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
         },
+        "grouped_qk": grouped,
         "backward": backward,
         "cpu_baseline": None,
     }
