@@ -241,6 +241,37 @@ ll_status loglinear_bwd_grouped(const void *q, const void *k, const void *v,
                                 int B, int H, int Hqk, int T, int dk, int dv, int chunk, ll_dtype dtype,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- batches of prompts of different lengths -----------------------------
+ * A batch of B prompts padded to one length T: sequence b holds lens[b]
+ * tokens at positions 0 .. lens[b]-1, and whatever follows is padding.  The
+ * form is causal (row t of the forward reads keys s <= t only: the
+ * hierarchical mask is lower triangular, French page §2 "Matrice de Masque
+ * Hiérarchique"), so the forward and the backward of the plain calls already
+ * serve such a batch:
+ *  - rows t < lens[b] of the forward do not depend on the padding, which
+ *    must hold finite values (a <= 0 as everywhere); padded rows of out hold
+ *    unspecified values;
+ *  - with dout zero on the padded rows, the backward's gradients of the real
+ *    rows are those of each prompt alone, and those of the padded rows are 0.
+ * What differs per sequence is the decode stack a prefill leaves, which
+ * belongs to each prompt's own last position:
+ *  lens  [B] int32 on the device, 0 <= lens[b] <= T, 4-byte aligned.
+ *        lens[b] == 0 leaves an empty stack (nothing written; decode with
+ *        pos[b] = 0).  A length outside [0, T] cannot be checked on the host
+ *        (lens lives on the device): every logscale entry of that sequence
+ *        becomes NaN (so its next decode step returns NaN) and no state is
+ *        written.
+ * Then loglinear_decode_step continues sequence b at pos[b] = lens[b].
+ * Everything else is as in loglinear_prefill_grouped (Hqk = H for per-head
+ * q and k); out is the padded forward.  lens == NULL returns LL_EINVAL
+ * unless the batch is empty. */
+ll_status loglinear_prefill_varlen(const void *q, const void *k, const void *v,
+                                   const float *a, const float *lambda, void *out,
+                                   float *state, float *logscale, const int *lens,
+                                   int B, int H, int Hqk, int T, int dk, int dv, int chunk, int Lcap,
+                                   ll_dtype dtype, void *workspace, size_t workspace_bytes,
+                                   void *stream, int group_log2);
+
 /* Message for the last failing call on this thread ("" if none).  Valid
  * until the next call into the library on the same thread. */
 const char *loglinear_last_error(void);

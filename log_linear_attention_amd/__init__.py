@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.loglinear_fwd_grouped.restype = I
         L.loglinear_prefill_grouped.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_prefill_grouped.restype = I
+        L.loglinear_prefill_varlen.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P, I]
+        L.loglinear_prefill_varlen.restype = I
         L.loglinear_decode_step_grouped.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         L.loglinear_decode_step_grouped.restype = I
         L.loglinear_bwd_grouped_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -186,11 +188,15 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
 
 
 def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspace=None, group_log2: int = -1,
-            stream=None):
+            stream=None, lengths=None):
     """Forward over a prompt that also writes the decode stack of its last
     position.  Inputs as for ``fwd``; state [B,H,Lcap,dk,dv] and logscale
     [B,H,Lcap] float32 are written (free slots untouched).  Decoding continues
-    with ``decode_step`` at pos = T.  Returns out [B,H,T,dv]."""
+    with ``decode_step`` at pos = T.  Returns out [B,H,T,dv].
+
+    ``lengths`` (optional int32 GPU tensor [B]): the batch holds prompts of
+    these lengths padded to T; each sequence's stack is that of its own last
+    position, and decoding continues at pos = lengths."""
     B, H, Hqk, T, dk, dv = _qkv_shapes(q, k, v)
     code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
@@ -214,7 +220,12 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
             _dev(out, "out"), _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32))
-    if Hqk == H:
+    if lengths is not None:
+        if tuple(lengths.shape) != (B,):
+            raise ValueError("lengths must be [B]")
+        st = lib().loglinear_prefill_varlen(*ptrs, _dev(lengths, "lengths", torch.int32), B, H, Hqk, T, dk, dv,
+                                            chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    elif Hqk == H:
         st = lib().loglinear_prefill(*ptrs, B, H, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes, _stream(stream),
                                      group_log2)
     else:

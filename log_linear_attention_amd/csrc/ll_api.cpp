@@ -139,6 +139,7 @@ size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
 struct StackOut {
     float *state, *logscale;
     int Lcap;
+    const int *lens = nullptr;   // per-sequence prompt lengths (device), NULL: all T
 };
 
 static ll_status run_fwd(const char *who, const void *q, const void *k, const void *v, const float *a,
@@ -223,6 +224,11 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
                 return fail(LL_EINVAL, "%s: state and logscale must not alias the inputs, out or the workspace", who);
         if (overlaps(so->state, nst, so->logscale, nls))
             return fail(LL_EINVAL, "%s: state and logscale overlap", who);
+        if (so->lens && !aligned(so->lens, 4))
+            return fail(LL_EINVAL, "%s: lens must be 4-byte aligned", who);
+        if (so->lens && (overlaps(so->state, nst, so->lens, (size_t)B * 4) ||
+                         overlaps(so->logscale, nls, so->lens, (size_t)B * 4)))
+            return fail(LL_EINVAL, "%s: state and logscale must not alias lens", who);
     }
     ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
     args.rqk = H / Hqk;
@@ -240,6 +246,8 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
                          so->state, so->logscale, (int)bh, T, dk, dv, lgc, plan.nG, plan.nL, plan.nLeft, so->Lcap,
                          bf16, nat};
         sa.rqk = H / Hqk;
+        sa.lens = so->lens;
+        sa.H = H;
         e = ll::stack_launch(sa, s);
         if (e != hipSuccess)
             return fail(LL_EDEVICE, "%s: stack launch failed: %s", who, hipGetErrorString(e));
@@ -271,6 +279,20 @@ ll_status loglinear_prefill(const void *q, const void *k, const void *v, const f
     const StackOut so{state, logscale, Lcap};
     return run_fwd("loglinear_prefill", q, k, v, a, lambda, out, B, H, H, T, dk, dv, chunk, dtype, workspace,
                    workspace_bytes, stream, group_log2, &so);
+}
+
+ll_status loglinear_prefill_varlen(const void *q, const void *k, const void *v, const float *a,
+                                   const float *lambda, void *out, float *state, float *logscale,
+                                   const int *lens, int B, int H, int Hqk, int T, int dk, int dv, int chunk,
+                                   int Lcap, ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream,
+                                   int group_log2)
+{
+    if (!lens && (int64_t)B * H * T > 0)
+        return fail(LL_EINVAL, "loglinear_prefill_varlen: lens is NULL");
+    StackOut so{state, logscale, Lcap};
+    so.lens = lens;
+    return run_fwd("loglinear_prefill_varlen", q, k, v, a, lambda, out, B, H, Hqk, T, dk, dv, chunk, dtype,
+                   workspace, workspace_bytes, stream, group_log2, &so);
 }
 
 ll_status loglinear_prefill_grouped(const void *q, const void *k, const void *v, const float *a,

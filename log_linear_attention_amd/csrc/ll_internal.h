@@ -83,6 +83,9 @@ struct StackArgs {
     int BH, T, dk, dv, lgc, nG, nL, nLeft, Lcap;
     bool bf16, nat;
     int rqk = 1;   // heads per k head: k is [BH / rqk, T, dk]
+    // Per-sequence prompt lengths [BH / H] on the device (NULL: all T).
+    const int *lens = nullptr;
+    int H = 1;
 };
 
 bool stack_supported(bool bf16, int dk, int dv);

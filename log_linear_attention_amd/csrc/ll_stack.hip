@@ -20,7 +20,10 @@
 // are staged in LDS and contracted over keys with fp32 MFMA.
 //
 // One workgroup per (head, slot, slice of 16 dk rows).  Free slots are not
-// written.
+// written.  In a batch of prompts padded to one length, each sequence's
+// stack is that of its own last position: every bucket of a position p lies
+// in [0, p], so the padding never enters, and the whole-group buckets are
+// tree blocks that end before p's group.
 #include <hip/hip_ext.h>
 
 #include "ll_device.h"
@@ -113,7 +116,8 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
                                                         const typename D::T *__restrict__ Dg,
                                                         const float *__restrict__ Gam, int Tlen, int lgc, int nG,
                                                         int nL, int nLeft, int nat, float *__restrict__ state,
-                                                        float *__restrict__ logscale, int Lcap, int rqk)
+                                                        float *__restrict__ logscale, int Lcap, int rqk,
+                                                        const int *__restrict__ lens, int H)
 {
     using T = typename D::T;
     constexpr int DK = D::DK, DV = D::DV, VEC = D::VEC;
@@ -130,7 +134,19 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
     // down, then the shorter key buckets.
     const int lb = min(lgc, Lcap - 1), y = blockIdx.y;
     const int l = y == 0 ? lb : (y <= Lcap - 1 - lb ? Lcap - y : Lcap - 1 - y);
-    const int p = Tlen - 1;
+    // Prompt length of this sequence: Tlen, or its own length in a batch of
+    // prompts padded to Tlen.  A length outside [0, Tlen] cannot be served:
+    // every logscale entry of the sequence becomes NaN and no state is
+    // written; an empty prompt leaves an empty stack (nothing written).
+    const int Tb = lens ? lens[bh / H] : Tlen;
+    if (Tb < 0 || Tb > Tlen) {
+        if (row0 == 0 && tid == 0)
+            logscale[(size_t)bh * Lcap + l] = __builtin_nanf("");
+        return;
+    }
+    if (Tb == 0)
+        return;
+    const int p = Tb - 1;
     if (l > 0 && !((p >> (l - 1)) & 1))
         return;  // free slot
     const int lo = l == 0 ? p : (p >> l) << l;
@@ -317,7 +333,7 @@ static hipError_t launch_stack_t(const StackArgs &A, hipStream_t s)
     const dim3 grid(A.BH * (DK / D::RS), A.Lcap);
     hipExtLaunchKernelGGL(ll_prefill_stack<D>, grid, dim3(D::NT), 0, s, pe.start, pe.stop, 0, (const T *)A.k,
                           (const T *)A.v, A.a, (const T *)A.Dg, A.Gam, A.T, A.lgc, A.nG, A.nL, A.nLeft, (int)A.nat,
-                          A.state, A.logscale, A.Lcap, A.rqk);
+                          A.state, A.logscale, A.Lcap, A.rqk, A.lens, A.H);
     return hipGetLastError();
 }
 

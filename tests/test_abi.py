@@ -306,3 +306,16 @@ def test_bwd_grouped_workspace_and_heads(L):
                                  FAKE + 0x10000000, 1 << 30, None)
     assert st == ll.LL_EINVAL
     assert ll.last_error().startswith("loglinear_bwd_grouped")
+
+
+def test_prefill_varlen_needs_lens(L):
+    args = (FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x8000000,
+            FAKE + 0x9000000, FAKE + 0xa000000)
+    st = L.loglinear_prefill_varlen(*args, None, 2, 2, 2, 64, 128, 64, 64, 17, ll.LL_BF16, None, 0, None, -1)
+    assert st == ll.LL_EINVAL and "lens" in ll.last_error()
+    st = L.loglinear_prefill_varlen(*args, FAKE + 0xb000002, 2, 2, 2, 64, 128, 64, 64, 17, ll.LL_BF16, None, 0,
+                                    None, -1)
+    assert st == ll.LL_EINVAL and "lens" in ll.last_error()
+    # an empty batch needs nothing
+    assert L.loglinear_prefill_varlen(*args, None, 0, 2, 2, 64, 128, 64, 64, 17, ll.LL_BF16, None, 0, None,
+                                      -1) == ll.LL_OK
