@@ -33,6 +33,8 @@ Prefill (``prefill_stack``): the stack that a whole prompt leaves for the
 decode of the next token, summed bucket by bucket from the same definition
 the forward uses.
 
+Log-Linear Gated DeltaNet: ``oracle/gdn.py`` (its own module; numpy fp64).
+
 Shared q/k heads (``expand_heads``, ``fwd_grouped``, ``bwd_grouped``): each
 head reads its q/k head; the gradient of a shared entry sums over the heads
 that read it.
