@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
         L.loglinear_prefill_grouped.restype = I
         L.loglinear_prefill_varlen.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_prefill_varlen.restype = I
+        L.loglinear_gdn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.loglinear_gdn_fwd_workspace_bytes.restype = Z
+        L.loglinear_gdn_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P]
+        L.loglinear_gdn_fwd.restype = I
         L.loglinear_decode_step_grouped.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
         L.loglinear_decode_step_grouped.restype = I
         L.loglinear_bwd_grouped_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -301,6 +305,37 @@ def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
         st = lib().loglinear_decode_step(*ptrs, S, H, dk, dv, Lcap, code, _stream(stream))
     else:
         st = lib().loglinear_decode_step_grouped(*ptrs, S, H, Hqk, dk, dv, Lcap, code, _stream(stream))
+    _check(st)
+    return out
+
+
+def gdn_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int) -> int:
+    return int(lib().loglinear_gdn_fwd_workspace_bytes(B, H, T, dk, dv, chunk))
+
+
+def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, stream=None):
+    """Log-Linear Gated DeltaNet forward (float32).  q, k [B,H,T,dk],
+    v [B,H,T,dv], a and beta [B,H,T], lam [B,H,T,L] with L = num_levels(T).
+    Returns out [B,H,T,dv].  Asynchronous on ``stream``."""
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T)
+    if tuple(a.shape) != (B, H, T) or tuple(beta.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
+        raise ValueError(f"a and beta must be [B,H,T] and lam [B,H,T,{L}]")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    need = gdn_fwd_workspace_bytes(B, H, T, dk, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    f32 = torch.float32
+    st = lib().loglinear_gdn_fwd(
+        _dev(q, "q", f32), _dev(k, "k", f32), _dev(v, "v", f32), _dev(a, "a", f32), _dev(beta, "beta", f32),
+        _dev(lam, "lam", f32), _dev(out, "out", f32), B, H, T, dk, dv, chunk, LL_F32, ws_ptr, ws_bytes,
+        _stream(stream))
     _check(st)
     return out
 

@@ -483,6 +483,69 @@ ll_status loglinear_decode_step_grouped(const void *q, const void *k, const void
     return run_decode(q, k, v, a, lambda, state, logscale, pos, out, S, H, Hqk, dk, dv, Lcap, dtype, stream);
 }
 
+size_t loglinear_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
+{
+    if (check_fwd_shape("loglinear_gdn_fwd_workspace_bytes", B, H, T, dk, dv, chunk) != LL_OK)
+        return 0;
+    if ((int64_t)B * H * T == 0 || !ll::gdn_supported(dk, dv, chunk))
+        return 0;
+    return ll::gdn_plan(B, H, T, dk, dv, chunk).bytes;
+}
+
+ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, const float *a, const float *beta,
+                            const float *lambda, float *out, int B, int H, int T, int dk, int dv, int chunk,
+                            ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const char *who = "loglinear_gdn_fwd";
+    if (dtype != LL_F32 && dtype != LL_BF16)
+        return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
+    ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
+    if (st != LL_OK)
+        return st;
+    if (dtype != LL_F32)
+        return fail(LL_EUNSUPPORTED, "%s: float32 only", who);
+    if (!ll::gdn_supported(dk, dv, chunk))
+        return fail(LL_EUNSUPPORTED, "%s: no kernel for dk=%d dv=%d chunk=%d", who, dk, dv, chunk);
+    if ((int64_t)B * H > 65535)
+        return fail(LL_EUNSUPPORTED, "%s: B*H above 65535", who);
+    const int64_t rows = (int64_t)B * H * T;
+    if (rows == 0)
+        return ok();
+    const int L = levels_for(T);
+    if (L > ll::kMaxLevels)
+        return fail(LL_EUNSUPPORTED, "%s: T=%d needs %d levels (max %d)", who, T, L, ll::kMaxLevels);
+    const void *ptrs[] = {q, k, v, a, beta, lambda, out};
+    const char *names[] = {"q", "k", "v", "a", "beta", "lambda", "out"};
+    for (int i = 0; i < 7; ++i) {
+        if (!ptrs[i])
+            return fail(LL_EINVAL, "%s: %s is NULL", who, names[i]);
+        if (!aligned(ptrs[i], 4))
+            return fail(LL_EINVAL, "%s: %s is not 4-byte aligned", who, names[i]);
+    }
+    const ll::GdnPlan plan = ll::gdn_plan(B, H, T, dk, dv, chunk);
+    if (!workspace)
+        return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, plan.bytes);
+    if (workspace_bytes < plan.bytes)
+        return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, plan.bytes, workspace_bytes);
+    if (!aligned(workspace, 256))
+        return fail(LL_EINVAL, "%s: workspace must be 256-byte aligned", who);
+    const size_t nq = (size_t)rows * dk * 4, nv = (size_t)rows * dv * 4, na = (size_t)rows * 4,
+                 nl = (size_t)rows * L * 4;
+    const void *all[] = {q, k, v, a, beta, lambda, workspace};
+    const size_t sz[] = {nq, nq, nv, na, na, nl, plan.bytes};
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(out, nv, all[i], sz[i]))
+            return fail(LL_EINVAL, "%s: out aliases an input or the workspace", who);
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(workspace, plan.bytes, all[i], sz[i]))
+            return fail(LL_EINVAL, "%s: workspace aliases an input", who);
+    ll::GdnArgs args{q, k, v, a, beta, lambda, out, B, H, T, dk, dv, chunk, L, workspace};
+    hipError_t e = ll::gdn_launch(args, plan, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+    return ok();
+}
+
 const char *loglinear_last_error(void) { return g_err.c_str(); }
 
 ll_status loglinear_profile_begin(int max_launches)

@@ -1,0 +1,469 @@
+// Log-Linear Gated DeltaNet forward (float32), gfx950.
+//
+// The log-linear construction multiplies a linear-attention model's own
+// attention matrix elementwise with the hierarchical (Fenwick) mask,
+// P = A ⊙ M_H, O = P V ("Log-Linear Attention", Portuguese page §2
+// "Metodologia", hierarchical-mask point; French page §3 "Contributions
+// Clés"), and the pages name Gated DeltaNet as the second model so treated.
+// Gated DeltaNet's recurrence (its own publication) is
+//   S_t = S_{t-1} M_t + beta_t v_t k_t^T,  M_t = exp(a_t) (I - beta_t k_t k_t^T),
+// o_t = S_t q_t, so its attention matrix is A[t,s] = beta_s k_s^T M_{s+1}..M_t q_t
+// and the log-linear output is o_t = sum_s lambda_t[level(t,s)] A[t,s] v_s.
+//
+// Chunkwise evaluation (chunk of C tokens starting at c0; Aloc = in-chunk
+// inclusive prefix of a, gamma_i = exp(Aloc[i])):
+//  - In-chunk pairs.  With pseudo-values u (S_t = sum_s (gamma_t/gamma_s) u_s k_s^T
+//    for a zero incoming state), u solves X u = diag(beta) v where
+//    X = I + strictly-lower(beta_i (gamma_i/gamma_j) k_i.k_j); hence
+//    A = ((Q K^T) ⊙ Gamma ⊙ causal) X^{-1} diag(beta) for the chunk's pairs.
+//    Z = Y X^{-1} is formed row by row, then multiplied by the in-chunk
+//    levels' lambda.
+//  - Product of the chunk's transitions.  Without the scalar decays the
+//    product of (I - beta_r k_r k_r^T) over r = 0..i is I - sum_{r<=i} w_r k_r^T
+//    with w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) (a compact WY form), so
+//    Phi_c = M_0 .. M_{C-1} = gamma_{C-1} (I - W^T K) and the query carried to
+//    the chunk start is qt_i = M_0 .. M_i q_i = gamma_i (q_i - sum_{r<=i} (q_i.k_r) w_r).
+//  - Chunk state (keys of the chunk, at its end): H = sum_s (gamma_end/gamma_s) u_s k_s^T.
+//  - Tree over chunks (left child L, right child R): D = D_L Phi_R + D_R,
+//    Phi = Phi_L Phi_R.  Stored transposed (Phi^T [dk][dk], D^T [dk][dv]) so
+//    the walk's reads run along rows.
+//  - Walk: for chunk c and each set bit m-1 of c, the level-(log2 C + m)
+//    bucket is the left-child block at tree level m-1; its contribution to
+//    row i is lambda_i[log2 C + m] D qt_i^(m), where qt^(m) is qt carried
+//    through the finer buckets' blocks: qt^(m') = Phi(block m) qt^(m) for
+//    the next set bit m' > m.
+//
+// All arithmetic is float32 FMA; decays enter only as exp of non-positive
+// differences for a <= 0.
+#include <hip/hip_ext.h>
+
+#include "ll_device.h"
+#include "ll_internal.h"
+
+namespace ll {
+
+template <int DK_, int DV_, int C_>
+struct Gdn {
+    static constexpr int DK = DK_, DV = DV_, C = C_;
+    static constexpr int NT = 256;
+    static constexpr int LDK = DK + 1, LDV = DV + 1, LDC = C + 1;
+    static constexpr int LOGC = C == 32 ? 5 : 6;
+    static constexpr int NRO = C * DV / NT;   // walk: output rows per thread
+    static constexpr int NRY = C * DK / NT;   // walk: carried-query rows per thread
+    static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
+};
+
+template <class G>
+struct GdnChunkSmem {
+    float QW[G::C][G::LDK];   // Q, then W
+    float Ks[G::C][G::LDK];
+    float Vs[G::C][G::LDV];   // V, then the pseudo-values U
+    float M1[G::C][G::LDC];   // S = Q K^T, then Z (rows in place)
+    float M2[G::C][G::LDC];   // lower (i, j<i): k_i.k_j; upper (j, i), j<i: X[i][j]
+    float Aloc[G::C];
+    float beta[G::C];
+    float wend[G::C];         // exp(Aloc[C-1] - Aloc[s])
+    float lam[G::C][G::LOGC + 1];
+};
+
+template <class G>
+struct GdnWalkSmem {
+    float Y[2][G::C][G::LDK];
+};
+
+__device__ __forceinline__ int bitlen(unsigned x) { return x ? 32 - __builtin_clz(x) : 0; }
+
+// Tree offsets: level p holds N >> p blocks; levels are stored one after
+// another per head.
+__device__ __forceinline__ size_t gdn_level_off(int N, int p)
+{
+    size_t off = 0;
+    for (int r = 0; r < p; ++r)
+        off += (size_t)(N >> r);
+    return off;
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
+                                                      const float *__restrict__ v, const float *__restrict__ a,
+                                                      const float *__restrict__ beta, const float *__restrict__ lam,
+                                                      float *__restrict__ out, float *__restrict__ qt,
+                                                      float *__restrict__ Phit, float *__restrict__ Dt, int Tlen,
+                                                      int L, int N, int NBT)
+{
+    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
+    __shared__ GdnChunkSmem<G> sm;
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / N, c = blockIdx.x % N;
+    const int t0 = c * C, valid = min(C, Tlen - t0);
+    const size_t row0 = (size_t)bh * Tlen + t0;
+
+    // ---- stage the chunk (rows past the sequence end: zero keys, values,
+    // queries, beta and a, i.e. identity transitions and no writes) ----
+    for (int e = tid; e < C * DK; e += NT) {
+        const int i = e / DK, d = e % DK;
+        const bool ok = i < valid;
+        sm.QW[i][d] = ok ? q[(row0 + i) * DK + d] : 0.f;
+        sm.Ks[i][d] = ok ? k[(row0 + i) * DK + d] : 0.f;
+    }
+    for (int e = tid; e < C * DV; e += NT) {
+        const int i = e / DV, cc = e % DV;
+        sm.Vs[i][cc] = i < valid ? v[(row0 + i) * DV + cc] : 0.f;
+    }
+    for (int e = tid; e < C * (G::LOGC + 1); e += NT) {
+        const int i = e / (G::LOGC + 1), l = e % (G::LOGC + 1);
+        sm.lam[i][l] = (i < valid && l < L) ? lam[(row0 + i) * L + l] : 0.f;
+    }
+    if (tid < C) {
+        sm.beta[tid] = tid < valid ? beta[row0 + tid] : 0.f;
+        sm.Aloc[tid] = tid < valid ? a[row0 + tid] : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int i = 0; i < C; ++i) {
+            s += sm.Aloc[i];
+            sm.Aloc[i] = s;
+        }
+    }
+    __syncthreads();
+    if (tid < C)
+        sm.wend[tid] = __expf(sm.Aloc[C - 1] - sm.Aloc[tid]);
+
+    // ---- S = Q K^T (all pairs), k_i.k_j and X[i][j] for j < i ----
+    for (int e = tid; e < C * C; e += NT) {
+        const int i = e / C, j = e % C;
+        float s = 0.f;
+        for (int d = 0; d < DK; ++d)
+            s += sm.QW[i][d] * sm.Ks[j][d];
+        sm.M1[i][j] = s;
+        if (j < i) {
+            float g = 0.f;
+            for (int d = 0; d < DK; ++d)
+                g += sm.Ks[i][d] * sm.Ks[j][d];
+            sm.M2[i][j] = g;
+            sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * g;
+        }
+    }
+    __syncthreads();
+
+    // ---- W (over Q's storage), one column per thread: w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) ----
+    if (tid < DK) {
+        const int d = tid;
+        for (int i = 0; i < C; ++i) {
+            float acc = sm.Ks[i][d];
+            for (int j = 0; j < i; ++j)
+                acc -= sm.M2[i][j] * sm.QW[j][d];
+            sm.QW[i][d] = sm.beta[i] * acc;
+        }
+    }
+    __syncthreads();
+
+    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r) ----
+    float *qtc = qt + ((size_t)bh * N + c) * C * DK;
+    for (int e = tid; e < C * DK; e += NT) {
+        const int i = e / DK, d = e % DK;
+        float acc = i < valid ? q[(row0 + i) * DK + d] : 0.f;
+        for (int r = 0; r <= i; ++r)
+            acc -= sm.M1[i][r] * sm.QW[r][d];
+        qtc[(size_t)i * DK + d] = __expf(sm.Aloc[i]) * acc;
+    }
+    __syncthreads();
+
+    // ---- Z = Y X^{-1}, Y = S ⊙ Gamma (lower), row by row in place:
+    // Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j] ----
+    if (tid < C) {
+        const int i = tid;
+        for (int j = i; j >= 0; --j) {
+            float z = sm.M1[i][j] * __expf(sm.Aloc[i] - sm.Aloc[j]);
+            for (int r = j + 1; r <= i; ++r)
+                z -= sm.M1[i][r] * sm.M2[j][r];
+            sm.M1[i][j] = z;
+        }
+    }
+    __syncthreads();
+
+    // ---- in-chunk output: o_i = sum_{j<=i} lambda_i[level(i,j)] Z[i][j] beta_j v_j ----
+    for (int e = tid; e < C * DV; e += NT) {
+        const int i = e / DV, cc = e % DV;
+        if (i < valid) {
+            float acc = 0.f;
+            for (int j = 0; j <= i; ++j)
+                acc += sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.M1[i][j] * sm.beta[j] * sm.Vs[j][cc];
+            out[(row0 + i) * DV + cc] = acc;
+        }
+    }
+    __syncthreads();
+
+    // ---- pseudo-values in place of V: u_i = beta_i v_i - sum_{j<i} X[i][j] u_j ----
+    if (tid < DV) {
+        const int cc = tid;
+        for (int i = 0; i < C; ++i) {
+            float u = sm.beta[i] * sm.Vs[i][cc];
+            for (int j = 0; j < i; ++j)
+                u -= sm.M2[j][i] * sm.Vs[j][cc];
+            sm.Vs[i][cc] = u;
+        }
+    }
+    __syncthreads();
+
+    // ---- level-0 tree entries of this chunk: Phi^T and D^T ----
+    const size_t blk = (size_t)bh * NBT + c;
+    float *P = Phit + blk * DK * DK;
+    const float gend = __expf(sm.Aloc[C - 1]);
+    for (int e = tid; e < DK * DK; e += NT) {
+        const int kk = e / DK, n = e % DK;   // Phi^T[kk][n] = Phi[n][kk]
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r)
+            acc += sm.QW[r][n] * sm.Ks[r][kk];
+        P[e] = gend * ((kk == n ? 1.f : 0.f) - acc);
+    }
+    float *D = Dt + blk * DK * DV;
+    for (int e = tid; e < DK * DV; e += NT) {
+        const int d = e / DV, cc = e % DV;   // D^T[d][cc] = H[cc][d]
+        float acc = 0.f;
+        for (int s = 0; s < C; ++s)
+            acc += sm.wend[s] * sm.Vs[s][cc] * sm.Ks[s][d];
+        D[e] = acc;
+    }
+}
+
+// One tree level p >= 1: block j from its children 2j (L) and 2j+1 (R) at
+// level p-1:  Phi^T = Phi_R^T Phi_L^T,  D^T = Phi_R^T D_L^T + D_R^T.
+// Output [DK rows] x [DK + DV columns] in 32 x 32 tiles; operands staged in LDS.
+template <class G>
+__global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, float *__restrict__ Dt, int N, int NBT,
+                                                   int p)
+{
+    constexpr int DK = G::DK, DV = G::DV, NC = DK + DV;
+    constexpr int TR = DK / 32, TN = NC / 32;
+    __shared__ float As[32][DK + 1];
+    __shared__ float Bs[DK][33];
+    const int tid = threadIdx.x;
+    const int nb = N >> p;
+    const int bh = blockIdx.y;
+    const int tile = blockIdx.x % (TR * TN), j = blockIdx.x / (TR * TN);
+    const int tr = tile / TN, tn = tile % TN;
+    if (j >= nb)
+        return;
+    const size_t child0 = (size_t)bh * NBT + gdn_level_off(N, p - 1);
+    const size_t L = child0 + 2 * (size_t)j, R = L + 1;
+    const size_t self = (size_t)bh * NBT + gdn_level_off(N, p) + j;
+    const float *PR = Phit + R * DK * DK;
+    // A tile: rows 32*tr .. of Phi_R^T (all k)
+    for (int e = tid; e < 32 * DK; e += 256) {
+        const int r = e / DK, kk = e % DK;
+        As[r][kk] = PR[(size_t)(32 * tr + r) * DK + kk];
+    }
+    // B tile: columns 32*tn .. of [Phi_L^T | D_L^T] (all k)
+    for (int e = tid; e < DK * 32; e += 256) {
+        const int kk = e / 32, n = e % 32, col = 32 * tn + n;
+        Bs[kk][n] = col < DK ? Phit[L * DK * DK + (size_t)kk * DK + col] : Dt[L * DK * DV + (size_t)kk * DV + col - DK];
+    }
+    __syncthreads();
+    const int r = tid / 8, n0 = (tid % 8) * 4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < DK; ++kk) {
+        const float x = As[r][kk];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            acc[u] += x * Bs[kk][n0 + u];
+    }
+    const int row = 32 * tr + r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int col = 32 * tn + n0 + u;
+        if (col < DK)
+            Phit[self * DK * DK + (size_t)row * DK + col] = acc[u];
+        else
+            Dt[self * DK * DV + (size_t)row * DV + col - DK] = acc[u] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+    }
+}
+
+// Chunk-level buckets: out[i] += sum over set bits m-1 of c of
+// lambda_i[log2 C + m] D_m qt_i^(m), with the carried query moved through
+// each used block's transition before the next, coarser one.
+template <class G>
+__global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ lam, const float *__restrict__ qt,
+                                                     const float *__restrict__ Phit, const float *__restrict__ Dt,
+                                                     float *__restrict__ out, int Tlen, int L, int N, int NBT)
+{
+    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
+    __shared__ GdnWalkSmem<G> sm;
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / N, c = blockIdx.x % N;
+    if (c == 0)
+        return;   // no chunk-level bucket
+    const int t0 = c * C, valid = min(C, Tlen - t0);
+    const size_t row0 = (size_t)bh * Tlen + t0;
+    const float *qtc = qt + ((size_t)bh * N + c) * C * DK;
+    for (int e = tid; e < C * DK; e += NT)
+        sm.Y[0][e / DK][e % DK] = qtc[e];
+    __syncthreads();
+    const int no = tid % DV, go = tid / DV;   // output column, row group (rows go + r * NT/DV)
+    const int ny = tid % DK, gy = tid / DK;
+    float acc[G::NRO];
+#pragma unroll
+    for (int r = 0; r < G::NRO; ++r)
+        acc[r] = 0.f;
+    int cur = 0;
+    const int top = bitlen((unsigned)c);
+    for (int m = 1; m <= top; ++m) {
+        if (!((c >> (m - 1)) & 1))
+            continue;
+        const int p = m - 1, jb = (c >> m) << 1;
+        const size_t blk = (size_t)bh * NBT + gdn_level_off(N, p) + jb;
+        const float *D = Dt + blk * DK * DV;
+        float tmp[G::NRO];
+#pragma unroll
+        for (int r = 0; r < G::NRO; ++r)
+            tmp[r] = 0.f;
+        for (int kk = 0; kk < DK; ++kk) {
+            const float b = D[(size_t)kk * DV + no];
+#pragma unroll
+            for (int r = 0; r < G::NRO; ++r)
+                tmp[r] += sm.Y[cur][go + r * (NT / DV)][kk] * b;
+        }
+#pragma unroll
+        for (int r = 0; r < G::NRO; ++r) {
+            const int i = go + r * (NT / DV);
+            const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
+            acc[r] += lw * tmp[r];
+        }
+        if ((c >> m) == 0)
+            break;   // no coarser bucket
+        // carry the queries through this block: Y' = Y Phi^T
+        const float *P = Phit + blk * DK * DK;
+        float ny_acc[G::NRY];
+#pragma unroll
+        for (int r = 0; r < G::NRY; ++r)
+            ny_acc[r] = 0.f;
+        for (int kk = 0; kk < DK; ++kk) {
+            const float b = P[(size_t)kk * DK + ny];
+#pragma unroll
+            for (int r = 0; r < G::NRY; ++r)
+                ny_acc[r] += sm.Y[cur][gy + r * (NT / DK)][kk] * b;
+        }
+#pragma unroll
+        for (int r = 0; r < G::NRY; ++r)
+            sm.Y[cur ^ 1][gy + r * (NT / DK)][ny] = ny_acc[r];
+        __syncthreads();
+        cur ^= 1;
+    }
+#pragma unroll
+    for (int r = 0; r < G::NRO; ++r) {
+        const int i = go + r * (NT / DV);
+        if (i < valid)
+            out[(row0 + i) * DV + no] += acc[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static int host_bitlen(int x)
+{
+    int n = 0;
+    while (x > 0) {
+        ++n;
+        x >>= 1;
+    }
+    return n;
+}
+
+GdnPlan gdn_plan(int B, int H, int T, int dk, int dv, int chunk)
+{
+    GdnPlan p;
+    const size_t BH = (size_t)B * H;
+    p.N = (T + chunk - 1) / chunk;
+    p.P = p.N > 1 ? host_bitlen(p.N - 1) - 1 : 0;   // deepest tree level the walk reads
+    p.NBT = 0;
+    for (int r = 0; r <= p.P; ++r)
+        p.NBT += p.N >> r;
+    const size_t qt = BH * p.N * chunk * dk * 4;
+    const size_t ph = BH * p.NBT * (size_t)dk * dk * 4;
+    const size_t dd = BH * p.NBT * (size_t)dk * dv * 4;
+    p.off_qt = 0;
+    p.off_phi = (qt + 255) & ~(size_t)255;
+    p.off_d = (p.off_phi + ph + 255) & ~(size_t)255;
+    p.bytes = (p.off_d + dd + 255) & ~(size_t)255;
+    return p;
+}
+
+typedef hipError_t (*GdnLauncher)(const GdnArgs &, const GdnPlan &, hipStream_t);
+
+template <int DK, int DV, int C>
+static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s)
+{
+    using G = Gdn<DK, DV, C>;
+    const int BH = A.B * A.H;
+    char *ws = static_cast<char *>(A.workspace);
+    float *qt = reinterpret_cast<float *>(ws + P.off_qt);
+    float *Phit = reinterpret_cast<float *>(ws + P.off_phi);
+    float *Dt = reinterpret_cast<float *>(ws + P.off_d);
+    ProfEvents pe = prof_events("ll_gdn_chunk");
+    hipExtLaunchKernelGGL(ll_gdn_chunk<G>, dim3(BH * P.N), dim3(G::NT), 0, s, pe.start, pe.stop, 0, A.q, A.k, A.v,
+                          A.a, A.beta, A.lam, A.out, qt, Phit, Dt, A.T, A.L, P.N, P.NBT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    constexpr int tiles = (DK / 32) * ((DK + DV) / 32);
+    for (int p = 1; p <= P.P; ++p) {
+        pe = prof_events("ll_gdn_tree");
+        hipExtLaunchKernelGGL(ll_gdn_tree<G>, dim3(tiles * (P.N >> p), BH), dim3(256), 0, s, pe.start, pe.stop, 0,
+                              Phit, Dt, P.N, P.NBT, p);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    if (P.N > 1) {
+        pe = prof_events("ll_gdn_walk");
+        hipExtLaunchKernelGGL(ll_gdn_walk<G>, dim3(BH * P.N), dim3(G::NT), 0, s, pe.start, pe.stop, 0, A.lam,
+                              (const float *)qt, (const float *)Phit, (const float *)Dt, A.out, A.T, A.L, P.N,
+                              P.NBT);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+template <int DK, int DV>
+static GdnLauncher gdn_pick_c(int chunk)
+{
+    switch (chunk) {
+    case 32: return &launch_gdn_t<DK, DV, 32>;
+    case 64: return &launch_gdn_t<DK, DV, 64>;
+    default: return nullptr;
+    }
+}
+
+template <int DK>
+static GdnLauncher gdn_pick_dv(int dv, int chunk)
+{
+    switch (dv) {
+    case 32: return gdn_pick_c<DK, 32>(chunk);
+    case 64: return gdn_pick_c<DK, 64>(chunk);
+    case 128: return gdn_pick_c<DK, 128>(chunk);
+    default: return nullptr;
+    }
+}
+
+static GdnLauncher find_gdn(int dk, int dv, int chunk)
+{
+    switch (dk) {
+    case 32: return gdn_pick_dv<32>(dv, chunk);
+    case 64: return gdn_pick_dv<64>(dv, chunk);
+    case 128: return gdn_pick_dv<128>(dv, chunk);
+    default: return nullptr;
+    }
+}
+
+bool gdn_supported(int dk, int dv, int chunk) { return find_gdn(dk, dv, chunk) != nullptr; }
+
+hipError_t gdn_launch(const GdnArgs &args, const GdnPlan &plan, hipStream_t stream)
+{
+    GdnLauncher f = find_gdn(args.dk, args.dv, args.chunk);
+    if (!f)
+        return hipErrorInvalidValue;
+    return f(args, plan, stream);
+}
+
+}  // namespace ll

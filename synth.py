@@ -85,6 +85,8 @@ WORKLOADS = {
     "tiny_f32_T256": FwdConfig("tiny_f32_T256", 1, 1, 256, 16, 16, 16, "f32", 0.05, 1000),
     "fwd_bf16_T2K": FwdConfig("fwd_bf16_T2K", 2, 8, 2048, 128, 64, 64, "bf16", 0.05, 1001),
     "fwd_bf16_T16K": FwdConfig("fwd_bf16_T16K", 1, 16, 16384, 128, 64, 64, "bf16", 0.05, 1002),
+    # Log-Linear Gated DeltaNet forward at the same shape, float32
+    "gdn_f32_T16K": FwdConfig("gdn_f32_T16K", 1, 16, 16384, 128, 64, 64, "f32", 0.05, 1005),
     "fwd_bf16_T64K": FwdConfig("fwd_bf16_T64K", 1, 8, 65536, 128, 64, 64, "bf16", 0.01, 1003),
     "decode_bf16_S64": DecodeConfig("decode_bf16_S64", 64, 16, 128, 64, 17, 32768, "bf16", 0.05, 1004),
 }
@@ -131,6 +133,26 @@ def make_fwd_inputs(cfg: FwdConfig, T: int | None = None, seed: int | None = Non
         "a": torch.from_numpy(a.astype(np.float32)).contiguous(),
         "lam": torch.from_numpy(lam.astype(np.float32)).contiguous(),
     }
+
+
+def make_gdn_inputs(cfg: FwdConfig, T: int | None = None, seed: int | None = None):
+    """Inputs of the Log-Linear Gated DeltaNet forward, float32 CPU tensors:
+    q and k unit-norm rows (Gated DeltaNet normalises both), v ~ N(0, 1),
+    beta = sigmoid(N(0, 1)), a = -softplus(N(0, 1)) * a_scale,
+    lambda ~ U[0, 1).  Returns dict(q, k, v, a, beta, lam)."""
+    T = cfg.T if T is None else T
+    seed = cfg.seed if seed is None else seed
+    B, H, dk, dv = cfg.B, cfg.H, cfg.dk, cfg.dv
+    L = num_levels(T)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _unit_rows(rng.standard_normal((B, H, T, dk)))
+    k = _unit_rows(rng.standard_normal((B, H, T, dk)))
+    v = rng.standard_normal((B, H, T, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((B, H, T))))
+    a = -_softplus(rng.standard_normal((B, H, T))) * cfg.a_scale
+    lam = rng.random((B, H, T, L))
+    f = lambda x: torch.from_numpy(x.astype(np.float32)).contiguous()
+    return {"q": f(q), "k": f(k), "v": f(v), "a": f(a), "beta": f(beta), "lam": f(lam)}
 
 
 def make_decode_inputs(cfg: DecodeConfig, seed: int | None = None, positions=None):

@@ -319,3 +319,27 @@ def test_prefill_varlen_needs_lens(L):
     # an empty batch needs nothing
     assert L.loglinear_prefill_varlen(*args, None, 0, 2, 2, 64, 128, 64, 64, 17, ll.LL_BF16, None, 0, None,
                                       -1) == ll.LL_OK
+
+
+def test_gdn_rejects_bad_arguments(L):
+    def call(**kw):
+        args = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, a=FAKE + 0x300000, beta=FAKE + 0x380000,
+                    lam=FAKE + 0x400000, out=FAKE + 0x8000000, B=1, H=2, T=64, dk=128, dv=64, chunk=64,
+                    dtype=ll.LL_F32, ws=FAKE + 0x10000000, wsb=1 << 30, stream=None)
+        args.update(kw)
+        return L.loglinear_gdn_fwd(args["q"], args["k"], args["v"], args["a"], args["beta"], args["lam"],
+                                   args["out"], args["B"], args["H"], args["T"], args["dk"], args["dv"],
+                                   args["chunk"], args["dtype"], args["ws"], args["wsb"], args["stream"])
+
+    assert call(dtype=ll.LL_BF16) == ll.LL_EUNSUPPORTED
+    assert call(chunk=16) == ll.LL_EUNSUPPORTED
+    assert call(dk=16) == ll.LL_EUNSUPPORTED
+    assert call(beta=None) == ll.LL_EINVAL
+    assert call(ws=None) == ll.LL_EWORKSPACE
+    assert call(wsb=64) == ll.LL_EWORKSPACE
+    assert call(out=FAKE + 0x100) == ll.LL_EINVAL                  # out overlaps q
+    assert call(T=0, q=None, k=None, v=None, a=None, beta=None, lam=None, out=None, ws=None, wsb=0) == ll.LL_OK
+    assert ll.last_error().startswith("loglinear_gdn_fwd") or ll.last_error() == ""
+    n = ll.gdn_fwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
+    assert n > 0 and n % 256 == 0
+    assert ll.gdn_fwd_workspace_bytes(1, 16, 16384, 128, 64, 16) == 0
