@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_chunk_walk_fwd_bf16_T16K.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
                   for f in ("ll_fwd.hip", "ll_device.h")]
@@ -215,6 +216,77 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     }
 
 
+def gdn_algorithmic(cfg):
+    """Algorithmic flops per kernel of the Log-Linear Gated DeltaNet forward
+    and its mandatory bytes.  Per chunk of C (dk, dv): Q K^T and K K^T
+    (lower half), the W solve, the carried queries, the in-chunk solve
+    (C^3/3), the in-chunk output and pseudo-value solve, the transition
+    W^T K and the chunk state; per tree merge dk x (dk + dv) x dk; per
+    chunk-level bucket used by a chunk C x dk x dv plus, for each but the
+    coarsest, C x dk x dk to carry the queries on."""
+    T, C, dk, dv, L = cfg.T, cfg.chunk, cfg.dk, cfg.dv, cfg.L
+    BH = cfg.B * cfg.H
+    N = (T + C - 1) // C
+    chunk = 2 * C * C * dk + C * C * dk + C * C * dk + C * C * dk + C ** 3 // 3 + C * C * dv + C * C * dv \
+        + 2 * C * dk * dk + 2 * C * dk * dv
+    P = (N - 1).bit_length() - 1 if N > 1 else 0
+    merges = sum(N >> p for p in range(1, P + 1))
+    tree = merges * 2 * dk * (dk + dv) * dk
+    walk = 0
+    for c in range(1, N):
+        pc = bin(c).count("1")
+        walk += pc * 2 * C * dk * dv + (pc - 1) * 2 * C * dk * dk
+    flops = {"ll_gdn_chunk": BH * N * chunk, "ll_gdn_tree": BH * tree, "ll_gdn_walk": BH * walk}
+    nbytes = BH * T * (2 * dk + dv + 2 + L + dv) * 4
+    return flops, nbytes
+
+
+def measure_gdn(ll, torch, dev, args, e0, e1):
+    """The Log-Linear Gated DeltaNet forward (float32) at the 16K shape."""
+    import synth
+
+    cfg = synth.WORKLOADS["gdn_f32_T16K"]
+    d = {k: v.to(dev) for k, v in synth.make_gdn_inputs(cfg).items()}
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(ll.gdn_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        ll.gdn_fwd(d["q"], d["k"], d["v"], d["a"], d["beta"], d["lam"], chunk=cfg.chunk, out=out, workspace=ws)
+
+    n = max(1, args.steps // 4)
+    for _ in range(min(args.warmup, 2)):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    ll.profile_begin(16 * n + 16)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    stats = ll.profile_end()
+    ks = {k: v[1] / n for k, v in stats.items()}   # per step (the tree kernel runs once per level)
+    flops, nbytes = gdn_algorithmic(cfg)
+    dom = max(ks, key=ks.get)
+    launches = stats[dom][0] / n
+    achieved = flops[dom] / (ks[dom] * 1e-3) / 1e12
+    log(f"gdn: {ms:.4f} ms/step; kernels (ms per step): { {k: round(v, 4) for k, v in ks.items()} }")
+    return {
+        "workload": cfg.name, "dtype": "f32", "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+        "kernels_ms_per_step": {k: round(v, 5) for k, v in ks.items()},
+        "algorithmic_flops": flops, "mandatory_bytes": nbytes,
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP32_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom,
+                     "kernel_avg_ms": round(ks[dom] / launches, 5)},
+    }
+
+
 def measure_grouped(ll, torch, cfg, dsets, args, e0, e1, Hqk):
     """The forward of the same workload with q and k shared by groups of
     H/Hqk heads (the first Hqk q/k heads of each input set): K timed steps,
@@ -267,6 +339,7 @@ def main():
                     help="run one 1 GiB device copy first (reference kernel for counter scaling)")
     ap.add_argument("--group-log2", type=int, default=-1)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -415,6 +488,9 @@ def main():
     # ---- q/k shared across heads: the same forward with fewer q/k heads ----
     grouped = [measure_grouped(ll, torch, cfg, dsets, args, e0, e1, hq) for hq in (4, 1)]
 
+    # ---- Log-Linear Gated DeltaNet forward ----
+    gdn_res = None if args.no_gdn else measure_gdn(ll, torch, dev, args, e0, e1)
+
     # ---- backward: gradients of the forward on the same workload ----
     backward = None if args.no_bwd else measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1)
 
@@ -460,6 +536,7 @@ def main():
                          "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
         },
         "grouped_qk": grouped,
+        "gated_deltanet": gdn_res,
         "backward": backward,
         "cpu_baseline": None,
     }

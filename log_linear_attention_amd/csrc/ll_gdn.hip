@@ -48,8 +48,6 @@ struct Gdn {
     static constexpr int NT = 256;
     static constexpr int LDK = DK + 1, LDV = DV + 1, LDC = C + 1;
     static constexpr int LOGC = C == 32 ? 5 : 6;
-    static constexpr int NRO = C * DV / NT;   // walk: output rows per thread
-    static constexpr int NRY = C * DK / NT;   // walk: carried-query rows per thread
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
 };
 
@@ -64,11 +62,6 @@ struct GdnChunkSmem {
     float beta[G::C];
     float wend[G::C];         // exp(Aloc[C-1] - Aloc[s])
     float lam[G::C][G::LOGC + 1];
-};
-
-template <class G>
-struct GdnWalkSmem {
-    float Y[2][G::C][G::LDK];
 };
 
 __device__ __forceinline__ int bitlen(unsigned x) { return x ? 32 - __builtin_clz(x) : 0; }
@@ -230,53 +223,109 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
 
 // One tree level p >= 1: block j from its children 2j (L) and 2j+1 (R) at
 // level p-1:  Phi^T = Phi_R^T Phi_L^T,  D^T = Phi_R^T D_L^T + D_R^T.
-// Output [DK rows] x [DK + DV columns] in 32 x 32 tiles; operands staged in LDS.
+// Output [DK rows] x [DK + DV columns] in 64 x 64 tiles, the contraction in
+// slices of 16 staged through LDS; each thread accumulates a 4 x 4 block.
 template <class G>
 __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, float *__restrict__ Dt, int N, int NBT,
                                                    int p)
 {
     constexpr int DK = G::DK, DV = G::DV, NC = DK + DV;
-    constexpr int TR = DK / 32, TN = NC / 32;
-    __shared__ float As[32][DK + 1];
-    __shared__ float Bs[DK][33];
+    constexpr int TS = DK < 64 ? DK : 64;            // tile edge (rows and columns)
+    constexpr int TR = DK / TS, TN = (NC + TS - 1) / TS;
+    constexpr int KS = 16;                            // contraction slice
+    constexpr int TPR = TS / 4;                       // threads per tile row of 4-column groups
+    __shared__ __attribute__((aligned(16))) float As[KS][TS + 4];   // As[k][r] = Phi_R^T[row0 + r][k0 + k]
+    __shared__ __attribute__((aligned(16))) float Bs[KS][TS + 4];   // Bs[k][n] = [Phi_L^T | D_L^T][k0 + k][col0 + n]
     const int tid = threadIdx.x;
-    const int nb = N >> p;
     const int bh = blockIdx.y;
     const int tile = blockIdx.x % (TR * TN), j = blockIdx.x / (TR * TN);
     const int tr = tile / TN, tn = tile % TN;
-    if (j >= nb)
-        return;
     const size_t child0 = (size_t)bh * NBT + gdn_level_off(N, p - 1);
     const size_t L = child0 + 2 * (size_t)j, R = L + 1;
     const size_t self = (size_t)bh * NBT + gdn_level_off(N, p) + j;
     const float *PR = Phit + R * DK * DK;
-    // A tile: rows 32*tr .. of Phi_R^T (all k)
-    for (int e = tid; e < 32 * DK; e += 256) {
-        const int r = e / DK, kk = e % DK;
-        As[r][kk] = PR[(size_t)(32 * tr + r) * DK + kk];
-    }
-    // B tile: columns 32*tn .. of [Phi_L^T | D_L^T] (all k)
-    for (int e = tid; e < DK * 32; e += 256) {
-        const int kk = e / 32, n = e % 32, col = 32 * tn + n;
-        Bs[kk][n] = col < DK ? Phit[L * DK * DK + (size_t)kk * DK + col] : Dt[L * DK * DV + (size_t)kk * DV + col - DK];
-    }
-    __syncthreads();
-    const int r = tid / 8, n0 = (tid % 8) * 4;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < DK; ++kk) {
-        const float x = As[r][kk];
+    const float *PL = Phit + L * DK * DK;
+    const float *DL = Dt + L * DK * DV;
+    const int row0 = TS * tr, col0 = TS * tn;
+    // thread block of outputs: rows 4*ty .. +3, columns 4*tx .. +3 (TS = 64: 16 x 16 threads)
+    const int tx = tid % TPR, ty = tid / TPR;
+    const bool active = ty < TS / 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < DK; k0 += KS) {
+        __syncthreads();
+        for (int e = tid; e < KS * TS; e += 256) {
+            const int r = e / KS, kk = e % KS;
+            As[kk][r] = PR[(size_t)(row0 + r) * DK + k0 + kk];
+        }
+        for (int e = tid; e < KS * TS; e += 256) {
+            const int kk = e / TS, n = e % TS, col = col0 + n;
+            float x = 0.f;
+            if (col < DK)
+                x = PL[(size_t)(k0 + kk) * DK + col];
+            else if (col < NC)
+                x = DL[(size_t)(k0 + kk) * DV + col - DK];
+            Bs[kk][n] = x;
+        }
+        __syncthreads();
+        if (active) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            acc[u] += x * Bs[kk][n0 + u];
+            for (int kk = 0; kk < KS; ++kk) {
+                const float4 av = *reinterpret_cast<const float4 *>(&As[kk][4 * ty]);
+                const float4 bv = *reinterpret_cast<const float4 *>(&Bs[kk][4 * tx]);
+                const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        acc[u][w] += ar[u] * br[w];
+            }
+        }
     }
-    const int row = 32 * tr + r;
+    if (!active)
+        return;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int col = 32 * tn + n0 + u;
-        if (col < DK)
-            Phit[self * DK * DK + (size_t)row * DK + col] = acc[u];
-        else
-            Dt[self * DK * DV + (size_t)row * DV + col - DK] = acc[u] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+        const int row = row0 + 4 * ty + u;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int col = col0 + 4 * tx + w;
+            if (col < DK)
+                Phit[self * DK * DK + (size_t)row * DK + col] = acc[u][w];
+            else if (col < NC)
+                Dt[self * DK * DV + (size_t)row * DV + col - DK] =
+                    acc[u][w] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+        }
+    }
+}
+
+// Y[rows][k] (LDS) times B[k][cols] (global, row-major, ldb) for one thread's
+// block: rows r0 + RS*r (r < NR), columns n0 .. n0+3.
+template <int NR, int RS, int DK, int LDY>
+__device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const float *B, int ldb, int r0, int n0,
+                                               float (&acc)[NR][4])
+{
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            acc[r][w] = 0.f;
+    for (int kk = 0; kk < DK; kk += 4) {
+        float4 b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            b[u] = *reinterpret_cast<const float4 *>(B + (size_t)(kk + u) * ldb + n0);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float4 y = *reinterpret_cast<const float4 *>(&Y[r0 + RS * r][kk]);
+            const float yr[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                acc[r][0] += yr[u] * b[u].x;
+                acc[r][1] += yr[u] * b[u].y;
+                acc[r][2] += yr[u] * b[u].z;
+                acc[r][3] += yr[u] * b[u].w;
+            }
+        }
     }
 }
 
@@ -289,7 +338,11 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
                                                      float *__restrict__ out, int Tlen, int L, int N, int NBT)
 {
     constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
-    __shared__ GdnWalkSmem<G> sm;
+    // outputs: 4 columns x NRO4 rows per thread; carried queries: 4 x NRY4
+    constexpr int OCG = DV / 4, ORG = NT / OCG, NRO4 = C / ORG;
+    constexpr int YCG = DK / 4, YRG = NT / YCG, NRY4 = C / YRG;
+    static_assert(NT % OCG == 0 && NT % YCG == 0 && C % ORG == 0 && C % YRG == 0, "walk layout");
+    __shared__ __attribute__((aligned(16))) float Y[2][C][DK + 4];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
     if (c == 0)
@@ -297,15 +350,19 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
     const int t0 = c * C, valid = min(C, Tlen - t0);
     const size_t row0 = (size_t)bh * Tlen + t0;
     const float *qtc = qt + ((size_t)bh * N + c) * C * DK;
-    for (int e = tid; e < C * DK; e += NT)
-        sm.Y[0][e / DK][e % DK] = qtc[e];
+    for (int e = tid; e < C * DK / 4; e += NT) {
+        const int i = e / (DK / 4), d4 = e % (DK / 4);
+        *reinterpret_cast<float4 *>(&Y[0][i][4 * d4]) = *reinterpret_cast<const float4 *>(qtc + (size_t)i * DK + 4 * d4);
+    }
     __syncthreads();
-    const int no = tid % DV, go = tid / DV;   // output column, row group (rows go + r * NT/DV)
-    const int ny = tid % DK, gy = tid / DK;
-    float acc[G::NRO];
+    const int on0 = 4 * (tid % OCG), or0 = tid / OCG;
+    const int yn0 = 4 * (tid % YCG), yr0 = tid / YCG;
+    float acc[NRO4][4];
 #pragma unroll
-    for (int r = 0; r < G::NRO; ++r)
-        acc[r] = 0.f;
+    for (int r = 0; r < NRO4; ++r)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            acc[r][w] = 0.f;
     int cur = 0;
     const int top = bitlen((unsigned)c);
     for (int m = 1; m <= top; ++m) {
@@ -313,48 +370,37 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
             continue;
         const int p = m - 1, jb = (c >> m) << 1;
         const size_t blk = (size_t)bh * NBT + gdn_level_off(N, p) + jb;
-        const float *D = Dt + blk * DK * DV;
-        float tmp[G::NRO];
+        float tmp[NRO4][4];
+        gdn_rows_x_mat<NRO4, ORG, DK, DK + 4>(Y[cur], Dt + blk * DK * DV, DV, or0, on0, tmp);
 #pragma unroll
-        for (int r = 0; r < G::NRO; ++r)
-            tmp[r] = 0.f;
-        for (int kk = 0; kk < DK; ++kk) {
-            const float b = D[(size_t)kk * DV + no];
-#pragma unroll
-            for (int r = 0; r < G::NRO; ++r)
-                tmp[r] += sm.Y[cur][go + r * (NT / DV)][kk] * b;
-        }
-#pragma unroll
-        for (int r = 0; r < G::NRO; ++r) {
-            const int i = go + r * (NT / DV);
+        for (int r = 0; r < NRO4; ++r) {
+            const int i = or0 + ORG * r;
             const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
-            acc[r] += lw * tmp[r];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                acc[r][w] += lw * tmp[r][w];
         }
         if ((c >> m) == 0)
             break;   // no coarser bucket
         // carry the queries through this block: Y' = Y Phi^T
-        const float *P = Phit + blk * DK * DK;
-        float ny_acc[G::NRY];
+        float ny[NRY4][4];
+        gdn_rows_x_mat<NRY4, YRG, DK, DK + 4>(Y[cur], Phit + blk * DK * DK, DK, yr0, yn0, ny);
 #pragma unroll
-        for (int r = 0; r < G::NRY; ++r)
-            ny_acc[r] = 0.f;
-        for (int kk = 0; kk < DK; ++kk) {
-            const float b = P[(size_t)kk * DK + ny];
-#pragma unroll
-            for (int r = 0; r < G::NRY; ++r)
-                ny_acc[r] += sm.Y[cur][gy + r * (NT / DK)][kk] * b;
-        }
-#pragma unroll
-        for (int r = 0; r < G::NRY; ++r)
-            sm.Y[cur ^ 1][gy + r * (NT / DK)][ny] = ny_acc[r];
+        for (int r = 0; r < NRY4; ++r)
+            *reinterpret_cast<float4 *>(&Y[cur ^ 1][yr0 + YRG * r][yn0]) =
+                make_float4(ny[r][0], ny[r][1], ny[r][2], ny[r][3]);
         __syncthreads();
         cur ^= 1;
     }
 #pragma unroll
-    for (int r = 0; r < G::NRO; ++r) {
-        const int i = go + r * (NT / DV);
-        if (i < valid)
-            out[(row0 + i) * DV + no] += acc[r];
+    for (int r = 0; r < NRO4; ++r) {
+        const int i = or0 + ORG * r;
+        if (i < valid) {
+            float4 *o = reinterpret_cast<float4 *>(out + (row0 + i) * DV + on0);
+            float4 x = *o;
+            x.x += acc[r][0]; x.y += acc[r][1]; x.z += acc[r][2]; x.w += acc[r][3];
+            *o = x;
+        }
     }
 }
 
@@ -407,7 +453,8 @@ static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    constexpr int tiles = (DK / 32) * ((DK + DV) / 32);
+    constexpr int TS = DK < 64 ? DK : 64;
+    constexpr int tiles = (DK / TS) * ((DK + DV + TS - 1) / TS);
     for (int p = 1; p <= P.P; ++p) {
         pe = prof_events("ll_gdn_tree");
         hipExtLaunchKernelGGL(ll_gdn_tree<G>, dim3(tiles * (P.N >> p), BH), dim3(256), 0, s, pe.start, pe.stop, 0,
