@@ -46,18 +46,18 @@ template <int DK_, int DV_, int C_>
 struct Gdn {
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr int NT = 256;
-    static constexpr int LDK = DK + 1, LDV = DV + 1, LDC = C + 1;
     static constexpr int LOGC = C == 32 ? 5 : 6;
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
 };
 
 template <class G>
 struct GdnChunkSmem {
-    float QW[G::C][G::LDK];   // Q, then W
-    float Ks[G::C][G::LDK];
-    float Vs[G::C][G::LDV];   // V, then the pseudo-values U
-    float M1[G::C][G::LDC];   // S = Q K^T, then Z (rows in place)
-    float M2[G::C][G::LDC];   // lower (i, j<i): k_i.k_j; upper (j, i), j<i: X[i][j]
+    // rows padded to a multiple of four floats (16-byte rows for float4 reads)
+    __attribute__((aligned(16))) float QW[G::C][G::DK + 4];   // Q, then W
+    __attribute__((aligned(16))) float Ks[G::C][G::DK + 4];
+    __attribute__((aligned(16))) float Vs[G::C][G::DV + 4];   // V, then the pseudo-values U
+    __attribute__((aligned(16))) float M1[G::C][G::C + 4];    // S = Q K^T, then Y -> Z -> weighted A
+    __attribute__((aligned(16))) float M2[G::C][G::C + 4];    // lower (i, j<i): k_i.k_j; upper (j, i), j<i: X[i][j]
     float Aloc[G::C];
     float beta[G::C];
     float wend[G::C];         // exp(Aloc[C-1] - Aloc[s])
@@ -76,6 +76,46 @@ __device__ __forceinline__ size_t gdn_level_off(int N, int p)
     return off;
 }
 
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// 4 x 4 block of A B^T with A, B row-major in LDS (k contiguous, 16-byte rows):
+// acc[u][w] += sum_k A[a0 + u][k] * B[b0 + w][k], k < K (K a multiple of 4).
+template <int K, int LDA, int LDB>
+__device__ __forceinline__ void blk_abt(const float (*A)[LDA], const float (*B)[LDB], int a0, int b0, float (&acc)[4][4])
+{
+    for (int kk = 0; kk < K; kk += 4) {
+        float4 x[4], y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            x[u] = ld4(&A[a0 + u][kk]);
+            y[u] = ld4(&B[b0 + u][kk]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                acc[u][w] += x[u].x * y[w].x + x[u].y * y[w].y + x[u].z * y[w].z + x[u].w * y[w].w;
+    }
+}
+
+// 4 x 4 block of A^T B with A, B row-major in LDS (contraction over rows r):
+// acc[u][w] += sum_r s[r] * A[r][a0 + u] * B[r][b0 + w], r < R.
+template <int R, int LDA, int LDB>
+__device__ __forceinline__ void blk_atb(const float (*A)[LDA], const float (*B)[LDB], const float *s, int a0, int b0,
+                                        float (&acc)[4][4])
+{
+    for (int r = 0; r < R; ++r) {
+        const float4 x = ld4(&A[r][a0]), y = ld4(&B[r][b0]);
+        const float sr = s ? s[r] : 1.f;
+        const float xs[4] = {sr * x.x, sr * x.y, sr * x.z, sr * x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                acc[u][w] += xs[u] * ys[w];
+    }
+}
+
 template <class G>
 __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ a,
@@ -85,6 +125,7 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
                                                       int L, int N, int NBT)
 {
     constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
+    constexpr int CB = C / 4;                    // 4-row blocks per chunk
     __shared__ GdnChunkSmem<G> sm;
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
@@ -93,15 +134,16 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
 
     // ---- stage the chunk (rows past the sequence end: zero keys, values,
     // queries, beta and a, i.e. identity transitions and no writes) ----
-    for (int e = tid; e < C * DK; e += NT) {
-        const int i = e / DK, d = e % DK;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = tid; e < C * DK / 4; e += NT) {
+        const int i = e / (DK / 4), d = 4 * (e % (DK / 4));
         const bool ok = i < valid;
-        sm.QW[i][d] = ok ? q[(row0 + i) * DK + d] : 0.f;
-        sm.Ks[i][d] = ok ? k[(row0 + i) * DK + d] : 0.f;
+        *reinterpret_cast<float4 *>(&sm.QW[i][d]) = ok ? ld4(q + (row0 + i) * DK + d) : z4;
+        *reinterpret_cast<float4 *>(&sm.Ks[i][d]) = ok ? ld4(k + (row0 + i) * DK + d) : z4;
     }
-    for (int e = tid; e < C * DV; e += NT) {
-        const int i = e / DV, cc = e % DV;
-        sm.Vs[i][cc] = i < valid ? v[(row0 + i) * DV + cc] : 0.f;
+    for (int e = tid; e < C * DV / 4; e += NT) {
+        const int i = e / (DV / 4), d = 4 * (e % (DV / 4));
+        *reinterpret_cast<float4 *>(&sm.Vs[i][d]) = i < valid ? ld4(v + (row0 + i) * DV + d) : z4;
     }
     for (int e = tid; e < C * (G::LOGC + 1); e += NT) {
         const int i = e / (G::LOGC + 1), l = e % (G::LOGC + 1);
@@ -112,31 +154,46 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
         sm.Aloc[tid] = tid < valid ? a[row0 + tid] : 0.f;
     }
     __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int i = 0; i < C; ++i) {
-            s += sm.Aloc[i];
-            sm.Aloc[i] = s;
+    if (tid < 64) {
+        // inclusive prefix of a over the chunk (C <= 64), one wave
+        float x = tid < C ? sm.Aloc[tid] : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_up(x, d, 64);
+            if (tid >= d)
+                x += y;
         }
+        if (tid < C)
+            sm.Aloc[tid] = x;
     }
     __syncthreads();
     if (tid < C)
         sm.wend[tid] = __expf(sm.Aloc[C - 1] - sm.Aloc[tid]);
 
-    // ---- S = Q K^T (all pairs), k_i.k_j and X[i][j] for j < i ----
-    for (int e = tid; e < C * C; e += NT) {
-        const int i = e / C, j = e % C;
-        float s = 0.f;
-        for (int d = 0; d < DK; ++d)
-            s += sm.QW[i][d] * sm.Ks[j][d];
-        sm.M1[i][j] = s;
-        if (j < i) {
-            float g = 0.f;
-            for (int d = 0; d < DK; ++d)
-                g += sm.Ks[i][d] * sm.Ks[j][d];
-            sm.M2[i][j] = g;
-            sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * g;
-        }
+    // ---- S = Q K^T, k_i.k_j and X[i][j] (j < i): 4 x 4 blocks ----
+    for (int b = tid; b < 2 * CB * CB; b += NT) {
+        const bool isg = b >= CB * CB;
+        const int bb = isg ? b - CB * CB : b;
+        const int i0 = 4 * (bb / CB), j0 = 4 * (bb % CB);
+        if (isg && j0 > i0 + 3)
+            continue;   // strictly upper block: not needed
+        float acc[4][4] = {};
+        if (isg)
+            blk_abt<DK, DK + 4, DK + 4>(sm.Ks, sm.Ks, i0, j0, acc);
+        else
+            blk_abt<DK, DK + 4, DK + 4>(sm.QW, sm.Ks, i0, j0, acc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int i = i0 + u, j = j0 + w;
+                if (!isg) {
+                    sm.M1[i][j] = acc[u][w];
+                } else if (j < i) {
+                    sm.M2[i][j] = acc[u][w];
+                    sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * acc[u][w];
+                }
+            }
     }
     __syncthreads();
 
@@ -144,46 +201,96 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     if (tid < DK) {
         const int d = tid;
         for (int i = 0; i < C; ++i) {
-            float acc = sm.Ks[i][d];
-            for (int j = 0; j < i; ++j)
-                acc -= sm.M2[i][j] * sm.QW[j][d];
-            sm.QW[i][d] = sm.beta[i] * acc;
+            float p0 = sm.Ks[i][d], p1 = 0.f, p2 = 0.f, p3 = 0.f;
+            int j = 0;
+            for (; j + 3 < i; j += 4) {
+                p0 -= sm.M2[i][j] * sm.QW[j][d];
+                p1 -= sm.M2[i][j + 1] * sm.QW[j + 1][d];
+                p2 -= sm.M2[i][j + 2] * sm.QW[j + 2][d];
+                p3 -= sm.M2[i][j + 3] * sm.QW[j + 3][d];
+            }
+            for (; j < i; ++j)
+                p0 -= sm.M2[i][j] * sm.QW[j][d];
+            sm.QW[i][d] = sm.beta[i] * ((p0 + p1) + (p2 + p3));
         }
     }
     __syncthreads();
 
-    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r) ----
+    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r): 4 rows x 4 columns ----
     float *qtc = qt + ((size_t)bh * N + c) * C * DK;
-    for (int e = tid; e < C * DK; e += NT) {
-        const int i = e / DK, d = e % DK;
-        float acc = i < valid ? q[(row0 + i) * DK + d] : 0.f;
-        for (int r = 0; r <= i; ++r)
-            acc -= sm.M1[i][r] * sm.QW[r][d];
-        qtc[(size_t)i * DK + d] = __expf(sm.Aloc[i]) * acc;
-    }
-    __syncthreads();
-
-    // ---- Z = Y X^{-1}, Y = S ⊙ Gamma (lower), row by row in place:
-    // Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j] ----
-    if (tid < C) {
-        const int i = tid;
-        for (int j = i; j >= 0; --j) {
-            float z = sm.M1[i][j] * __expf(sm.Aloc[i] - sm.Aloc[j]);
-            for (int r = j + 1; r <= i; ++r)
-                z -= sm.M1[i][r] * sm.M2[j][r];
-            sm.M1[i][j] = z;
+    for (int b = tid; b < CB * (DK / 4); b += NT) {
+        const int i0 = 4 * (b / (DK / 4)), d0 = 4 * (b % (DK / 4));
+        float acc[4][4] = {};
+        for (int r = 0; r <= i0 + 3; ++r) {
+            const float4 w = ld4(&sm.QW[r][d0]);
+            const float wr[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float sv = r <= i0 + u ? sm.M1[i0 + u][r] : 0.f;
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    acc[u][x] += sv * wr[x];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            const float4 qv = i < valid ? ld4(q + (row0 + i) * DK + d0) : z4;
+            const float g = __expf(sm.Aloc[i]);
+            *reinterpret_cast<float4 *>(qtc + (size_t)i * DK + d0) =
+                make_float4(g * (qv.x - acc[u][0]), g * (qv.y - acc[u][1]), g * (qv.z - acc[u][2]),
+                            g * (qv.w - acc[u][3]));
         }
     }
     __syncthreads();
 
-    // ---- in-chunk output: o_i = sum_{j<=i} lambda_i[level(i,j)] Z[i][j] beta_j v_j ----
-    for (int e = tid; e < C * DV; e += NT) {
-        const int i = e / DV, cc = e % DV;
-        if (i < valid) {
-            float acc = 0.f;
-            for (int j = 0; j <= i; ++j)
-                acc += sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.M1[i][j] * sm.beta[j] * sm.Vs[j][cc];
-            out[(row0 + i) * DV + cc] = acc;
+    // ---- Y = S ⊙ Gamma (lower, zero above), then Z = Y X^{-1} column by
+    // column from the right: column j is final once the columns right of it
+    // have been subtracted, Z[i][j'] -= Z[i][j] X[j][j'] for j' < j ----
+    for (int e = tid; e < C * C; e += NT) {
+        const int i = e / C, j = e % C;
+        sm.M1[i][j] = j <= i ? sm.M1[i][j] * __expf(sm.Aloc[i] - sm.Aloc[j]) : 0.f;
+    }
+    for (int j = C - 1; j > 0; --j) {
+        __syncthreads();
+        // rows i >= j, columns j' < j
+        const int n = (C - j) * j;
+        for (int e = tid; e < n; e += NT) {
+            const int i = j + e / j, jp = e % j;
+            sm.M1[i][jp] -= sm.M1[i][j] * sm.M2[jp][j];
+        }
+    }
+    __syncthreads();
+
+    // ---- weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
+    for (int e = tid; e < C * C; e += NT) {
+        const int i = e / C, j = e % C;
+        if (j <= i)
+            sm.M1[i][j] *= sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.beta[j];
+    }
+    __syncthreads();
+
+    // ---- in-chunk output O = A' V: 4 rows x 4 columns ----
+    for (int b = tid; b < CB * (DV / 4); b += NT) {
+        const int i0 = 4 * (b / (DV / 4)), c0 = 4 * (b % (DV / 4));
+        float acc[4][4] = {};
+        for (int j = 0; j <= i0 + 3; ++j) {
+            const float4 vv = ld4(&sm.Vs[j][c0]);
+            const float vr[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float av = sm.M1[i0 + u][j];   // zero above the diagonal
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    acc[u][x] += av * vr[x];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            if (i < valid)
+                *reinterpret_cast<float4 *>(out + (row0 + i) * DV + c0) =
+                    make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
         }
     }
     __syncthreads();
@@ -192,32 +299,47 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     if (tid < DV) {
         const int cc = tid;
         for (int i = 0; i < C; ++i) {
-            float u = sm.beta[i] * sm.Vs[i][cc];
-            for (int j = 0; j < i; ++j)
-                u -= sm.M2[j][i] * sm.Vs[j][cc];
-            sm.Vs[i][cc] = u;
+            float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
+            int j = 0;
+            for (; j + 3 < i; j += 4) {
+                p0 -= sm.M2[j][i] * sm.Vs[j][cc];
+                p1 -= sm.M2[j + 1][i] * sm.Vs[j + 1][cc];
+                p2 -= sm.M2[j + 2][i] * sm.Vs[j + 2][cc];
+                p3 -= sm.M2[j + 3][i] * sm.Vs[j + 3][cc];
+            }
+            for (; j < i; ++j)
+                p0 -= sm.M2[j][i] * sm.Vs[j][cc];
+            sm.Vs[i][cc] = (p0 + p1) + (p2 + p3);
         }
     }
     __syncthreads();
 
-    // ---- level-0 tree entries of this chunk: Phi^T and D^T ----
+    // ---- level-0 tree entries of this chunk: Phi^T = gamma_end (I - K^T W), D^T = K^T diag(wend) U ----
     const size_t blk = (size_t)bh * NBT + c;
     float *P = Phit + blk * DK * DK;
     const float gend = __expf(sm.Aloc[C - 1]);
-    for (int e = tid; e < DK * DK; e += NT) {
-        const int kk = e / DK, n = e % DK;   // Phi^T[kk][n] = Phi[n][kk]
-        float acc = 0.f;
-        for (int r = 0; r < C; ++r)
-            acc += sm.QW[r][n] * sm.Ks[r][kk];
-        P[e] = gend * ((kk == n ? 1.f : 0.f) - acc);
+    for (int b = tid; b < (DK / 4) * (DK / 4); b += NT) {
+        const int k0 = 4 * (b / (DK / 4)), n0 = 4 * (b % (DK / 4));   // Phi^T[k][n] = Phi[n][k]
+        float acc[4][4] = {};
+        blk_atb<C, DK + 4, DK + 4>(sm.Ks, sm.QW, nullptr, k0, n0, acc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float r4[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                r4[w] = gend * ((k0 + u == n0 + w ? 1.f : 0.f) - acc[u][w]);
+            *reinterpret_cast<float4 *>(P + (size_t)(k0 + u) * DK + n0) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+        }
     }
     float *D = Dt + blk * DK * DV;
-    for (int e = tid; e < DK * DV; e += NT) {
-        const int d = e / DV, cc = e % DV;   // D^T[d][cc] = H[cc][d]
-        float acc = 0.f;
-        for (int s = 0; s < C; ++s)
-            acc += sm.wend[s] * sm.Vs[s][cc] * sm.Ks[s][d];
-        D[e] = acc;
+    for (int b = tid; b < (DK / 4) * (DV / 4); b += NT) {
+        const int d0 = 4 * (b / (DV / 4)), c0 = 4 * (b % (DV / 4));   // D^T[d][c] = H[c][d]
+        float acc[4][4] = {};
+        blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Vs, sm.wend, d0, c0, acc);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<float4 *>(D + (size_t)(d0 + u) * DV + c0) =
+                make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
     }
 }
 
