@@ -340,6 +340,7 @@ def main():
     ap.add_argument("--group-log2", type=int, default=-1)
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurement")
+    ap.add_argument("--no-grouped", action="store_true", help="skip the shared q/k measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -486,7 +487,8 @@ def main():
         f"{stack_gbs:.1f} GB/s")
 
     # ---- q/k shared across heads: the same forward with fewer q/k heads ----
-    grouped = [measure_grouped(ll, torch, cfg, dsets, args, e0, e1, hq) for hq in (4, 1)]
+    grouped = None if args.no_grouped else [measure_grouped(ll, torch, cfg, dsets, args, e0, e1, hq)
+                                            for hq in (4, 1)]
 
     # ---- Log-Linear Gated DeltaNet forward ----
     gdn_res = None if args.no_gdn else measure_gdn(ll, torch, dev, args, e0, e1)
