@@ -420,10 +420,37 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     }
 }
 
-// Y[rows][k] (LDS) times B[k][cols] (global, row-major, ldb) for one thread's
-// block: rows r0 + RS*r (r < NR), columns n0 .. n0+3.
-template <int NR, int RS, int DK, int LDY>
-__device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const float *B, int ldb, int r0, int n0,
+constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a time
+
+// Four rows kk .. kk+3 of a staged slice (absolute rows k0 + kk ..).
+template <int NR, int RS, int LDY, int NB>
+__device__ __forceinline__ void gdn_rows_step(const float (*Y)[LDY], const float *Bs, int k0, int kk, int r0, int n0,
+                                              float (&acc)[NR][4])
+{
+    float4 b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        b[u] = *reinterpret_cast<const float4 *>(Bs + (kk + u) * NB + n0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float4 y = *reinterpret_cast<const float4 *>(&Y[r0 + RS * r][k0 + kk]);
+        const float yr[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc[r][0] += yr[u] * b[u].x;
+            acc[r][1] += yr[u] * b[u].y;
+            acc[r][2] += yr[u] * b[u].z;
+            acc[r][3] += yr[u] * b[u].w;
+        }
+    }
+}
+
+// Y[rows][k] (LDS) times B[k][cols] (global, row-major, NB columns) for one
+// thread's block: rows r0 + RS*r (r < NR), columns n0 .. n0+3.  B is staged
+// through LDS (Bs) kGdnKS rows at a time, read once per workgroup; every
+// thread of the workgroup must call this.
+template <int NR, int RS, int DK, int LDY, int NB>
+__device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const float *B, float *Bs, int r0, int n0,
                                                float (&acc)[NR][4])
 {
 #pragma unroll
@@ -431,23 +458,14 @@ __device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const floa
 #pragma unroll
         for (int w = 0; w < 4; ++w)
             acc[r][w] = 0.f;
-    for (int kk = 0; kk < DK; kk += 4) {
-        float4 b[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            b[u] = *reinterpret_cast<const float4 *>(B + (size_t)(kk + u) * ldb + n0);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const float4 y = *reinterpret_cast<const float4 *>(&Y[r0 + RS * r][kk]);
-            const float yr[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                acc[r][0] += yr[u] * b[u].x;
-                acc[r][1] += yr[u] * b[u].y;
-                acc[r][2] += yr[u] * b[u].z;
-                acc[r][3] += yr[u] * b[u].w;
-            }
-        }
+    for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
+        __syncthreads();   // the previous slice has been read
+        for (int e = threadIdx.x; e < kGdnKS * NB / 4; e += blockDim.x)
+            *reinterpret_cast<float4 *>(Bs + 4 * e) = *reinterpret_cast<const float4 *>(B + (size_t)k0 * NB + 4 * e);
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kGdnKS; kk += 4)
+            gdn_rows_step<NR, RS, LDY, NB>(Y, Bs, k0, kk, r0, n0, acc);
     }
 }
 
@@ -465,6 +483,7 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
     constexpr int YCG = DK / 4, YRG = NT / YCG, NRY4 = C / YRG;
     static_assert(NT % OCG == 0 && NT % YCG == 0 && C % ORG == 0 && C % YRG == 0, "walk layout");
     __shared__ __attribute__((aligned(16))) float Y[2][C][DK + 4];
+    __shared__ __attribute__((aligned(16))) float Bs[kGdnKS * (DK > DV ? DK : DV)];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
     if (c == 0)
@@ -493,7 +512,7 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
         const int p = m - 1, jb = (c >> m) << 1;
         const size_t blk = (size_t)bh * NBT + gdn_level_off(N, p) + jb;
         float tmp[NRO4][4];
-        gdn_rows_x_mat<NRO4, ORG, DK, DK + 4>(Y[cur], Dt + blk * DK * DV, DV, or0, on0, tmp);
+        gdn_rows_x_mat<NRO4, ORG, DK, DK + 4, DV>(Y[cur], Dt + blk * DK * DV, Bs, or0, on0, tmp);
 #pragma unroll
         for (int r = 0; r < NRO4; ++r) {
             const int i = or0 + ORG * r;
@@ -506,7 +525,7 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ l
             break;   // no coarser bucket
         // carry the queries through this block: Y' = Y Phi^T
         float ny[NRY4][4];
-        gdn_rows_x_mat<NRY4, YRG, DK, DK + 4>(Y[cur], Phit + blk * DK * DK, DK, yr0, yn0, ny);
+        gdn_rows_x_mat<NRY4, YRG, DK, DK + 4, DK>(Y[cur], Phit + blk * DK * DK, Bs, yr0, yn0, ny);
 #pragma unroll
         for (int r = 0; r < NRY4; ++r)
             *reinterpret_cast<float4 *>(&Y[cur ^ 1][yr0 + YRG * r][yn0]) =
