@@ -17,7 +17,8 @@
 //    X = I + strictly-lower(beta_i (gamma_i/gamma_j) k_i.k_j); hence
 //    A = ((Q K^T) ⊙ Gamma ⊙ causal) X^{-1} diag(beta) for the chunk's pairs.
 //    Z = Y X^{-1} is formed row by row, then multiplied by the in-chunk
-//    levels' lambda.
+//    levels' lambda.  The three triangular solves (W below, Z, U) run side by
+//    side, one column or row per thread.
 //  - Product of the chunk's transitions.  Without the scalar decays the
 //    product of (I - beta_r k_r k_r^T) over r = 0..i is I - sum_{r<=i} w_r k_r^T
 //    with w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) (a compact WY form), so
@@ -48,6 +49,11 @@ struct Gdn {
     static constexpr int NT = 256;
     static constexpr int LOGC = C == 32 ? 5 : 6;
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
+    // The three triangular solves (W, Z, U) run side by side, one column or
+    // row per thread, when threads and LDS allow a separate U buffer.
+    static constexpr int SOLVE_LDS = 4 * (C * (DK + 4) * 2 + C * (DV + 4) * 2 + 3 * C * (C + 4) + C * (LOGC + 4));
+    static constexpr bool SEPU = DK + C + DV <= NT && SOLVE_LDS <= 160 * 1024;
+    static_assert(DK + C <= NT, "W and Z solves side by side");
 };
 
 template <class G>
@@ -56,8 +62,10 @@ struct GdnChunkSmem {
     __attribute__((aligned(16))) float QW[G::C][G::DK + 4];   // Q, then W
     __attribute__((aligned(16))) float Ks[G::C][G::DK + 4];
     __attribute__((aligned(16))) float Vs[G::C][G::DV + 4];   // V, then the pseudo-values U
-    __attribute__((aligned(16))) float M1[G::C][G::C + 4];    // S = Q K^T, then Y -> Z -> weighted A
+    __attribute__((aligned(16))) float M1[G::C][G::C + 4];    // S = Q K^T
     __attribute__((aligned(16))) float M2[G::C][G::C + 4];    // lower (i, j<i): k_i.k_j; upper (j, i), j<i: X[i][j]
+    __attribute__((aligned(16))) float M3[G::C][G::C + 4];    // Z, then the weighted A
+    __attribute__((aligned(16))) float Us[G::SEPU ? G::C : 1][G::DV + 4];   // pseudo-values (when separate)
     float Aloc[G::C];
     float beta[G::C];
     float wend[G::C];         // exp(Aloc[C-1] - Aloc[s])
@@ -83,6 +91,7 @@ __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast
 template <int K, int LDA, int LDB>
 __device__ __forceinline__ void blk_abt(const float (*A)[LDA], const float (*B)[LDB], int a0, int b0, float (&acc)[4][4])
 {
+#pragma unroll 1
     for (int kk = 0; kk < K; kk += 4) {
         float4 x[4], y[4];
 #pragma unroll
@@ -104,6 +113,7 @@ template <int R, int LDA, int LDB>
 __device__ __forceinline__ void blk_atb(const float (*A)[LDA], const float (*B)[LDB], const float *s, int a0, int b0,
                                         float (&acc)[4][4])
 {
+#pragma unroll 2
     for (int r = 0; r < R; ++r) {
         const float4 x = ld4(&A[r][a0]), y = ld4(&B[r][b0]);
         const float sr = s ? s[r] : 1.f;
@@ -197,7 +207,10 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     }
     __syncthreads();
 
-    // ---- W (over Q's storage), one column per thread: w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) ----
+    // ---- the triangular solves, side by side (one column or row per thread):
+    //  W (over Q's storage):  w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j)
+    //  Z = Y X^{-1}, Y = S ⊙ Gamma:  Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j]
+    //  U (separate buffer):  u_i = beta_i v_i - sum_{j<i} X[i][j] u_j ----
     if (tid < DK) {
         const int d = tid;
         for (int i = 0; i < C; ++i) {
@@ -213,10 +226,44 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
                 p0 -= sm.M2[i][j] * sm.QW[j][d];
             sm.QW[i][d] = sm.beta[i] * ((p0 + p1) + (p2 + p3));
         }
+    } else if (tid < DK + C) {
+        const int i = tid - DK;
+        const float ai = sm.Aloc[i];
+        for (int j = C - 1; j > i; --j)
+            sm.M3[i][j] = 0.f;
+        for (int j = i; j >= 0; --j) {
+            float z0 = sm.M1[i][j] * __expf(ai - sm.Aloc[j]), z1 = 0.f;
+            int r = j + 1;
+            for (; r + 1 <= i; r += 2) {
+                z0 -= sm.M3[i][r] * sm.M2[j][r];
+                z1 -= sm.M3[i][r + 1] * sm.M2[j][r + 1];
+            }
+            for (; r <= i; ++r)
+                z0 -= sm.M3[i][r] * sm.M2[j][r];
+            sm.M3[i][j] = z0 + z1;
+        }
+    } else if constexpr (G::SEPU) {
+        if (tid < DK + C + DV) {
+            const int cc = tid - DK - C;
+            for (int i = 0; i < C; ++i) {
+                float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
+                int j = 0;
+                for (; j + 3 < i; j += 4) {
+                    p0 -= sm.M2[j][i] * sm.Us[j][cc];
+                    p1 -= sm.M2[j + 1][i] * sm.Us[j + 1][cc];
+                    p2 -= sm.M2[j + 2][i] * sm.Us[j + 2][cc];
+                    p3 -= sm.M2[j + 3][i] * sm.Us[j + 3][cc];
+                }
+                for (; j < i; ++j)
+                    p0 -= sm.M2[j][i] * sm.Us[j][cc];
+                sm.Us[i][cc] = (p0 + p1) + (p2 + p3);
+            }
+        }
     }
     __syncthreads();
 
-    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r): 4 rows x 4 columns ----
+    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r): 4 rows x 4 columns;
+    // weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
     float *qtc = qt + ((size_t)bh * N + c) * C * DK;
     for (int b = tid; b < CB * (DK / 4); b += NT) {
         const int i0 = 4 * (b / (DK / 4)), d0 = 4 * (b % (DK / 4));
@@ -242,31 +289,10 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
                             g * (qv.w - acc[u][3]));
         }
     }
-    __syncthreads();
-
-    // ---- Y = S ⊙ Gamma (lower, zero above), then Z = Y X^{-1} column by
-    // column from the right: column j is final once the columns right of it
-    // have been subtracted, Z[i][j'] -= Z[i][j] X[j][j'] for j' < j ----
-    for (int e = tid; e < C * C; e += NT) {
-        const int i = e / C, j = e % C;
-        sm.M1[i][j] = j <= i ? sm.M1[i][j] * __expf(sm.Aloc[i] - sm.Aloc[j]) : 0.f;
-    }
-    for (int j = C - 1; j > 0; --j) {
-        __syncthreads();
-        // rows i >= j, columns j' < j
-        const int n = (C - j) * j;
-        for (int e = tid; e < n; e += NT) {
-            const int i = j + e / j, jp = e % j;
-            sm.M1[i][jp] -= sm.M1[i][j] * sm.M2[jp][j];
-        }
-    }
-    __syncthreads();
-
-    // ---- weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
     for (int e = tid; e < C * C; e += NT) {
         const int i = e / C, j = e % C;
         if (j <= i)
-            sm.M1[i][j] *= sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.beta[j];
+            sm.M3[i][j] *= sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.beta[j];
     }
     __syncthreads();
 
@@ -279,7 +305,7 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
             const float vr[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float av = sm.M1[i0 + u][j];   // zero above the diagonal
+                const float av = sm.M3[i0 + u][j];   // zero above the diagonal
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
                     acc[u][x] += av * vr[x];
@@ -293,23 +319,25 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
                     make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
         }
     }
-    __syncthreads();
 
-    // ---- pseudo-values in place of V: u_i = beta_i v_i - sum_{j<i} X[i][j] u_j ----
-    if (tid < DV) {
-        const int cc = tid;
-        for (int i = 0; i < C; ++i) {
-            float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
-            int j = 0;
-            for (; j + 3 < i; j += 4) {
-                p0 -= sm.M2[j][i] * sm.Vs[j][cc];
-                p1 -= sm.M2[j + 1][i] * sm.Vs[j + 1][cc];
-                p2 -= sm.M2[j + 2][i] * sm.Vs[j + 2][cc];
-                p3 -= sm.M2[j + 3][i] * sm.Vs[j + 3][cc];
+    // ---- pseudo-values in place of V when they have no buffer of their own ----
+    if constexpr (!G::SEPU) {
+        __syncthreads();
+        if (tid < DV) {
+            const int cc = tid;
+            for (int i = 0; i < C; ++i) {
+                float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
+                int j = 0;
+                for (; j + 3 < i; j += 4) {
+                    p0 -= sm.M2[j][i] * sm.Vs[j][cc];
+                    p1 -= sm.M2[j + 1][i] * sm.Vs[j + 1][cc];
+                    p2 -= sm.M2[j + 2][i] * sm.Vs[j + 2][cc];
+                    p3 -= sm.M2[j + 3][i] * sm.Vs[j + 3][cc];
+                }
+                for (; j < i; ++j)
+                    p0 -= sm.M2[j][i] * sm.Vs[j][cc];
+                sm.Vs[i][cc] = (p0 + p1) + (p2 + p3);
             }
-            for (; j < i; ++j)
-                p0 -= sm.M2[j][i] * sm.Vs[j][cc];
-            sm.Vs[i][cc] = (p0 + p1) + (p2 + p3);
         }
     }
     __syncthreads();
@@ -335,7 +363,10 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     for (int b = tid; b < (DK / 4) * (DV / 4); b += NT) {
         const int d0 = 4 * (b / (DV / 4)), c0 = 4 * (b % (DV / 4));   // D^T[d][c] = H[c][d]
         float acc[4][4] = {};
-        blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Vs, sm.wend, d0, c0, acc);
+        if constexpr (G::SEPU)
+            blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Us, sm.wend, d0, c0, acc);
+        else
+            blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Vs, sm.wend, d0, c0, acc);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             *reinterpret_cast<float4 *>(D + (size_t)(d0 + u) * DV + c0) =
