@@ -126,6 +126,102 @@ __device__ __forceinline__ void blk_atb(const float (*A)[LDA], const float (*B)[
     }
 }
 
+// The chunk's triangular solves, four rows (or columns) per step: the
+// earlier rows' terms for a block of four are summed together (each earlier
+// value loaded once for the four), then the 4 x 4 diagonal block is solved.
+
+// W (one column d of Q's storage): w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j),
+// with k_i.k_j in the lower triangle of M2.
+template <class G, class SM>
+__device__ __forceinline__ void gdn_solve_w(SM &sm, int d)
+{
+    constexpr int C = G::C;
+    for (int ib = 0; ib < C; ib += 4) {
+        float r0 = sm.Ks[ib][d], r1 = sm.Ks[ib + 1][d], r2 = sm.Ks[ib + 2][d], r3 = sm.Ks[ib + 3][d];
+#pragma unroll 4
+        for (int j = 0; j < ib; ++j) {
+            const float w = sm.QW[j][d];
+            r0 -= sm.M2[ib][j] * w;
+            r1 -= sm.M2[ib + 1][j] * w;
+            r2 -= sm.M2[ib + 2][j] * w;
+            r3 -= sm.M2[ib + 3][j] * w;
+        }
+        const float w0 = sm.beta[ib] * r0;
+        const float w1 = sm.beta[ib + 1] * (r1 - sm.M2[ib + 1][ib] * w0);
+        const float w2 = sm.beta[ib + 2] * (r2 - sm.M2[ib + 2][ib] * w0 - sm.M2[ib + 2][ib + 1] * w1);
+        const float w3 =
+            sm.beta[ib + 3] * (r3 - sm.M2[ib + 3][ib] * w0 - sm.M2[ib + 3][ib + 1] * w1 - sm.M2[ib + 3][ib + 2] * w2);
+        sm.QW[ib][d] = w0;
+        sm.QW[ib + 1][d] = w1;
+        sm.QW[ib + 2][d] = w2;
+        sm.QW[ib + 3][d] = w3;
+    }
+}
+
+// U (one column cc): u_i = beta_i v_i - sum_{j<i} X[i][j] u_j, X[i][j] in the
+// upper triangle of M2 at (j, i).  U may be V's own storage.
+template <class G, class SM, int LDV>
+__device__ __forceinline__ void gdn_solve_u(SM &sm, const float (*V)[LDV], float (*U)[LDV], int cc)
+{
+    constexpr int C = G::C;
+    for (int ib = 0; ib < C; ib += 4) {
+        float r0 = sm.beta[ib] * V[ib][cc], r1 = sm.beta[ib + 1] * V[ib + 1][cc];
+        float r2 = sm.beta[ib + 2] * V[ib + 2][cc], r3 = sm.beta[ib + 3] * V[ib + 3][cc];
+#pragma unroll 4
+        for (int j = 0; j < ib; ++j) {
+            const float u = U[j][cc];
+            const float4 x = ld4(&sm.M2[j][ib]);   // X[ib..ib+3][j]
+            r0 -= x.x * u;
+            r1 -= x.y * u;
+            r2 -= x.z * u;
+            r3 -= x.w * u;
+        }
+        const float u0 = r0;
+        const float u1 = r1 - sm.M2[ib][ib + 1] * u0;
+        const float u2 = r2 - sm.M2[ib][ib + 2] * u0 - sm.M2[ib + 1][ib + 2] * u1;
+        const float u3 = r3 - sm.M2[ib][ib + 3] * u0 - sm.M2[ib + 1][ib + 3] * u1 - sm.M2[ib + 2][ib + 3] * u2;
+        U[ib][cc] = u0;
+        U[ib + 1][cc] = u1;
+        U[ib + 2][cc] = u2;
+        U[ib + 3][cc] = u3;
+    }
+}
+
+// Z row i into M3: Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j] with
+// Y = S ⊙ Gamma (S in M1), columns from the right in blocks of four; zero
+// above the diagonal.
+template <class G, class SM>
+__device__ __forceinline__ void gdn_solve_z(SM &sm, int i)
+{
+    constexpr int C = G::C;
+    const float ai = sm.Aloc[i];
+    const int top = i & ~3;
+    for (int j = top + 4; j < C; ++j)
+        sm.M3[i][j] = 0.f;
+    for (int jb = top; jb >= 0; jb -= 4) {
+        float y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            y[k] = jb + k <= i ? sm.M1[i][jb + k] * __expf(ai - sm.Aloc[jb + k]) : 0.f;
+#pragma unroll 4
+        for (int r = jb + 4; r <= i; ++r) {
+            const float z = sm.M3[i][r];
+            y[0] -= z * sm.M2[jb][r];
+            y[1] -= z * sm.M2[jb + 1][r];
+            y[2] -= z * sm.M2[jb + 2][r];
+            y[3] -= z * sm.M2[jb + 3][r];
+        }
+        const float z3 = jb + 3 <= i ? y[3] : 0.f;
+        const float z2 = jb + 2 <= i ? y[2] - z3 * sm.M2[jb + 2][jb + 3] : 0.f;
+        const float z1 = jb + 1 <= i ? y[1] - z2 * sm.M2[jb + 1][jb + 2] - z3 * sm.M2[jb + 1][jb + 3] : 0.f;
+        const float z0 = y[0] - z1 * sm.M2[jb][jb + 1] - z2 * sm.M2[jb][jb + 2] - z3 * sm.M2[jb][jb + 3];
+        sm.M3[i][jb] = z0;
+        sm.M3[i][jb + 1] = z1;
+        sm.M3[i][jb + 2] = z2;
+        sm.M3[i][jb + 3] = z3;
+    }
+}
+
 template <class G>
 __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ a,
@@ -212,53 +308,12 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     //  Z = Y X^{-1}, Y = S ⊙ Gamma:  Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j]
     //  U (separate buffer):  u_i = beta_i v_i - sum_{j<i} X[i][j] u_j ----
     if (tid < DK) {
-        const int d = tid;
-        for (int i = 0; i < C; ++i) {
-            float p0 = sm.Ks[i][d], p1 = 0.f, p2 = 0.f, p3 = 0.f;
-            int j = 0;
-            for (; j + 3 < i; j += 4) {
-                p0 -= sm.M2[i][j] * sm.QW[j][d];
-                p1 -= sm.M2[i][j + 1] * sm.QW[j + 1][d];
-                p2 -= sm.M2[i][j + 2] * sm.QW[j + 2][d];
-                p3 -= sm.M2[i][j + 3] * sm.QW[j + 3][d];
-            }
-            for (; j < i; ++j)
-                p0 -= sm.M2[i][j] * sm.QW[j][d];
-            sm.QW[i][d] = sm.beta[i] * ((p0 + p1) + (p2 + p3));
-        }
+        gdn_solve_w<G>(sm, tid);
     } else if (tid < DK + C) {
-        const int i = tid - DK;
-        const float ai = sm.Aloc[i];
-        for (int j = C - 1; j > i; --j)
-            sm.M3[i][j] = 0.f;
-        for (int j = i; j >= 0; --j) {
-            float z0 = sm.M1[i][j] * __expf(ai - sm.Aloc[j]), z1 = 0.f;
-            int r = j + 1;
-            for (; r + 1 <= i; r += 2) {
-                z0 -= sm.M3[i][r] * sm.M2[j][r];
-                z1 -= sm.M3[i][r + 1] * sm.M2[j][r + 1];
-            }
-            for (; r <= i; ++r)
-                z0 -= sm.M3[i][r] * sm.M2[j][r];
-            sm.M3[i][j] = z0 + z1;
-        }
+        gdn_solve_z<G>(sm, tid - DK);
     } else if constexpr (G::SEPU) {
-        if (tid < DK + C + DV) {
-            const int cc = tid - DK - C;
-            for (int i = 0; i < C; ++i) {
-                float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
-                int j = 0;
-                for (; j + 3 < i; j += 4) {
-                    p0 -= sm.M2[j][i] * sm.Us[j][cc];
-                    p1 -= sm.M2[j + 1][i] * sm.Us[j + 1][cc];
-                    p2 -= sm.M2[j + 2][i] * sm.Us[j + 2][cc];
-                    p3 -= sm.M2[j + 3][i] * sm.Us[j + 3][cc];
-                }
-                for (; j < i; ++j)
-                    p0 -= sm.M2[j][i] * sm.Us[j][cc];
-                sm.Us[i][cc] = (p0 + p1) + (p2 + p3);
-            }
-        }
+        if (tid < DK + C + DV)
+            gdn_solve_u<G, GdnChunkSmem<G>, DV + 4>(sm, sm.Vs, sm.Us, tid - DK - C);
     }
     __syncthreads();
 
@@ -323,22 +378,8 @@ __global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ 
     // ---- pseudo-values in place of V when they have no buffer of their own ----
     if constexpr (!G::SEPU) {
         __syncthreads();
-        if (tid < DV) {
-            const int cc = tid;
-            for (int i = 0; i < C; ++i) {
-                float p0 = sm.beta[i] * sm.Vs[i][cc], p1 = 0.f, p2 = 0.f, p3 = 0.f;
-                int j = 0;
-                for (; j + 3 < i; j += 4) {
-                    p0 -= sm.M2[j][i] * sm.Vs[j][cc];
-                    p1 -= sm.M2[j + 1][i] * sm.Vs[j + 1][cc];
-                    p2 -= sm.M2[j + 2][i] * sm.Vs[j + 2][cc];
-                    p3 -= sm.M2[j + 3][i] * sm.Vs[j + 3][cc];
-                }
-                for (; j < i; ++j)
-                    p0 -= sm.M2[j][i] * sm.Vs[j][cc];
-                sm.Vs[i][cc] = (p0 + p1) + (p2 + p3);
-            }
-        }
+        if (tid < DV)
+            gdn_solve_u<G, GdnChunkSmem<G>, DV + 4>(sm, sm.Vs, sm.Vs, tid);
     }
     __syncthreads();
 
