@@ -91,7 +91,7 @@ __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast
 template <int K, int LDA, int LDB>
 __device__ __forceinline__ void blk_abt(const float (*A)[LDA], const float (*B)[LDB], int a0, int b0, float (&acc)[4][4])
 {
-#pragma unroll 1
+#pragma unroll 2
     for (int kk = 0; kk < K; kk += 4) {
         float4 x[4], y[4];
 #pragma unroll
@@ -113,7 +113,7 @@ template <int R, int LDA, int LDB>
 __device__ __forceinline__ void blk_atb(const float (*A)[LDA], const float (*B)[LDB], const float *s, int a0, int b0,
                                         float (&acc)[4][4])
 {
-#pragma unroll 2
+#pragma unroll 4
     for (int r = 0; r < R; ++r) {
         const float4 x = ld4(&A[r][a0]), y = ld4(&B[r][b0]);
         const float sr = s ? s[r] : 1.f;

@@ -86,7 +86,7 @@ WORKLOADS = {
     "fwd_bf16_T2K": FwdConfig("fwd_bf16_T2K", 2, 8, 2048, 128, 64, 64, "bf16", 0.05, 1001),
     "fwd_bf16_T16K": FwdConfig("fwd_bf16_T16K", 1, 16, 16384, 128, 64, 64, "bf16", 0.05, 1002),
     # Log-Linear Gated DeltaNet forward at the same shape, float32
-    "gdn_f32_T16K": FwdConfig("gdn_f32_T16K", 1, 16, 16384, 128, 64, 32, "f32", 0.05, 1005),
+    "gdn_f32_T16K": FwdConfig("gdn_f32_T16K", 1, 16, 16384, 128, 64, 64, "f32", 0.05, 1005),
     "fwd_bf16_T64K": FwdConfig("fwd_bf16_T64K", 1, 8, 65536, 128, 64, 64, "bf16", 0.01, 1003),
     "decode_bf16_S64": DecodeConfig("decode_bf16_S64", 64, 16, 128, 64, 17, 32768, "bf16", 0.05, 1004),
 }
