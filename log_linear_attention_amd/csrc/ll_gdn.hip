@@ -47,13 +47,14 @@ template <int DK_, int DV_, int C_>
 struct Gdn {
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr int NT = 256;
+    static constexpr int CNT = 512;   // chunk kernel threads (one workgroup per CU: LDS)
     static constexpr int LOGC = C == 32 ? 5 : 6;
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
     // The three triangular solves (W, Z, U) run side by side, one column or
     // row per thread, when threads and LDS allow a separate U buffer.
     static constexpr int SOLVE_LDS = 4 * (C * (DK + 4) * 2 + C * (DV + 4) * 2 + 3 * C * (C + 4) + C * (LOGC + 4));
-    static constexpr bool SEPU = DK + C + DV <= NT && SOLVE_LDS <= 160 * 1024;
-    static_assert(DK + C <= NT, "W and Z solves side by side");
+    static constexpr bool SEPU = DK + C + DV <= CNT && SOLVE_LDS <= 160 * 1024;
+    static_assert(DK + C <= CNT, "W and Z solves side by side");
 };
 
 template <class G>
@@ -223,14 +224,14 @@ __device__ __forceinline__ void gdn_solve_z(SM &sm, int i)
 }
 
 template <class G>
-__global__ __launch_bounds__(G::NT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
+__global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
                                                       const float *__restrict__ v, const float *__restrict__ a,
                                                       const float *__restrict__ beta, const float *__restrict__ lam,
                                                       float *__restrict__ out, float *__restrict__ qt,
                                                       float *__restrict__ Phit, float *__restrict__ Dt, int Tlen,
                                                       int L, int N, int NBT)
 {
-    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
+    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::CNT;
     constexpr int CB = C / 4;                    // 4-row blocks per chunk
     __shared__ GdnChunkSmem<G> sm;
     const int tid = threadIdx.x;
@@ -661,7 +662,7 @@ static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s
     float *Phit = reinterpret_cast<float *>(ws + P.off_phi);
     float *Dt = reinterpret_cast<float *>(ws + P.off_d);
     ProfEvents pe = prof_events("ll_gdn_chunk");
-    hipExtLaunchKernelGGL(ll_gdn_chunk<G>, dim3(BH * P.N), dim3(G::NT), 0, s, pe.start, pe.stop, 0, A.q, A.k, A.v,
+    hipExtLaunchKernelGGL(ll_gdn_chunk<G>, dim3(BH * P.N), dim3(G::CNT), 0, s, pe.start, pe.stop, 0, A.q, A.k, A.v,
                           A.a, A.beta, A.lam, A.out, qt, Phit, Dt, A.T, A.L, P.N, P.NBT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
