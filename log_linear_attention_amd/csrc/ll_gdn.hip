@@ -48,6 +48,8 @@ struct Gdn {
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr int NT = 256;
     static constexpr int CNT = 512;   // chunk kernel threads (one workgroup per CU: LDS)
+    // walk threads: up to 512, at most C rows per 4-column group of either product
+    static constexpr int WNT = C * (DK < DV ? DK : DV) / 4 < 512 ? C * (DK < DV ? DK : DV) / 4 : 512;
     static constexpr int LOGC = C == 32 ? 5 : 6;
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
     // The three triangular solves (W, Z, U) run side by side, one column or
@@ -531,6 +533,7 @@ __device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const floa
 #pragma unroll
         for (int w = 0; w < 4; ++w)
             acc[r][w] = 0.f;
+#pragma unroll 1
     for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
         __syncthreads();   // the previous slice has been read
         for (int e = threadIdx.x; e < kGdnKS * NB / 4; e += blockDim.x)
@@ -546,11 +549,11 @@ __device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const floa
 // lambda_i[log2 C + m] D_m qt_i^(m), with the carried query moved through
 // each used block's transition before the next, coarser one.
 template <class G>
-__global__ __launch_bounds__(G::NT) void ll_gdn_walk(const float *__restrict__ lam, const float *__restrict__ qt,
+__global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ lam, const float *__restrict__ qt,
                                                      const float *__restrict__ Phit, const float *__restrict__ Dt,
                                                      float *__restrict__ out, int Tlen, int L, int N, int NBT)
 {
-    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::NT;
+    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::WNT;
     // outputs: 4 columns x NRO4 rows per thread; carried queries: 4 x NRY4
     constexpr int OCG = DV / 4, ORG = NT / OCG, NRO4 = C / ORG;
     constexpr int YCG = DK / 4, YRG = NT / YCG, NRY4 = C / YRG;
@@ -678,7 +681,7 @@ static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s
     }
     if (P.N > 1) {
         pe = prof_events("ll_gdn_walk");
-        hipExtLaunchKernelGGL(ll_gdn_walk<G>, dim3(BH * P.N), dim3(G::NT), 0, s, pe.start, pe.stop, 0, A.lam,
+        hipExtLaunchKernelGGL(ll_gdn_walk<G>, dim3(BH * P.N), dim3(G::WNT), 0, s, pe.start, pe.stop, 0, A.lam,
                               (const float *)qt, (const float *)Phit, (const float *)Dt, A.out, A.T, A.L, P.N,
                               P.NBT);
         e = hipGetLastError();
