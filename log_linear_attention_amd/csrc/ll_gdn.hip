@@ -243,16 +243,35 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const float *__restrict__
 
     // ---- stage the chunk (rows past the sequence end: zero keys, values,
     // queries, beta and a, i.e. identity transitions and no writes) ----
+    // every load is issued before the first LDS store
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int e = tid; e < C * DK / 4; e += NT) {
-        const int i = e / (DK / 4), d = 4 * (e % (DK / 4));
-        const bool ok = i < valid;
-        *reinterpret_cast<float4 *>(&sm.QW[i][d]) = ok ? ld4(q + (row0 + i) * DK + d) : z4;
-        *reinterpret_cast<float4 *>(&sm.Ks[i][d]) = ok ? ld4(k + (row0 + i) * DK + d) : z4;
+    constexpr int NQ4 = (C * DK / 4 + NT - 1) / NT, NV4 = (C * DV / 4 + NT - 1) / NT;
+    float4 rq[NQ4], rk[NQ4], rv[NV4];
+#pragma unroll
+    for (int u = 0; u < NQ4; ++u) {
+        const int e = tid + u * NT, i = e / (DK / 4), d = 4 * (e % (DK / 4));
+        const bool ok = e < C * DK / 4 && i < valid;
+        rq[u] = ok ? ld4(q + (row0 + i) * DK + d) : z4;
+        rk[u] = ok ? ld4(k + (row0 + i) * DK + d) : z4;
     }
-    for (int e = tid; e < C * DV / 4; e += NT) {
-        const int i = e / (DV / 4), d = 4 * (e % (DV / 4));
-        *reinterpret_cast<float4 *>(&sm.Vs[i][d]) = i < valid ? ld4(v + (row0 + i) * DV + d) : z4;
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+        const int e = tid + u * NT, i = e / (DV / 4), d = 4 * (e % (DV / 4));
+        rv[u] = (e < C * DV / 4 && i < valid) ? ld4(v + (row0 + i) * DV + d) : z4;
+    }
+#pragma unroll
+    for (int u = 0; u < NQ4; ++u) {
+        const int e = tid + u * NT, i = e / (DK / 4), d = 4 * (e % (DK / 4));
+        if (e < C * DK / 4) {
+            *reinterpret_cast<float4 *>(&sm.QW[i][d]) = rq[u];
+            *reinterpret_cast<float4 *>(&sm.Ks[i][d]) = rk[u];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NV4; ++u) {
+        const int e = tid + u * NT, i = e / (DV / 4), d = 4 * (e % (DV / 4));
+        if (e < C * DV / 4)
+            *reinterpret_cast<float4 *>(&sm.Vs[i][d]) = rv[u];
     }
     for (int e = tid; e < C * (G::LOGC + 1); e += NT) {
         const int i = e / (G::LOGC + 1), l = e % (G::LOGC + 1);
