@@ -272,7 +272,7 @@ ll_status loglinear_prefill_varlen(const void *q, const void *k, const void *v,
                                    ll_dtype dtype, void *workspace, size_t workspace_bytes,
                                    void *stream, int group_log2);
 
-/* ---- Log-Linear Gated DeltaNet (forward, float32) -------------------------
+/* ---- Log-Linear Gated DeltaNet (forward, float32 arithmetic) --------------
  * The pages turn a linear-attention model into its log-linear form by
  * multiplying the model's own attention matrix elementwise with the
  * hierarchical mask, P = A ⊙ M_H (Portuguese page §2 "Metodologia",
@@ -282,21 +282,24 @@ ll_status loglinear_prefill_varlen(const void *q, const void *k, const void *v,
  * M_t = exp(a_t) (I - beta_t k_t k_t^T),  o_t = S_t q_t,  this computes
  *   o_t = sum_{s<=t} lambda[t, level(t,s)] * beta_s (k_s^T M_{s+1} ... M_t q_t) * v_s
  * with level() as for loglinear_fwd (lambda = 1 gives Gated DeltaNet).
- *  q, k   [B,H,T,dk]  float32 (k is expected unit-norm, as Gated DeltaNet
+ *  q, k   [B,H,T,dk]  dtype (k is expected unit-norm, as Gated DeltaNet
  *                     normalises it; not checked)
- *  v      [B,H,T,dv]  float32
+ *  v      [B,H,T,dv]  dtype
  *  a      [B,H,T]     float32 log of the gate alpha_t (expected <= 0)
  *  beta   [B,H,T]     float32 write strength (expected in [0, 1])
  *  lambda [B,H,T,L]   float32, L = loglinear_num_levels(T)
- *  out    [B,H,T,dv]  float32, written; must not alias inputs or workspace
- *  chunk  32 or 64; dk, dv in {32, 64, 128}; dtype must be LL_F32
- *         (LL_BF16 returns LL_EUNSUPPORTED); B*H <= 65535.
+ *  out    [B,H,T,dv]  dtype, written; must not alias inputs or workspace
+ *  q, k, v, out must be 16-byte aligned; a, beta, lambda 4-byte aligned.
+ *  chunk  32 or 64; dk, dv in {32, 64, 128}; dtype LL_F32 or LL_BF16 (bf16
+ *         inputs are widened on load, all arithmetic is float32, and out is
+ *         rounded once); B*H <= 65535.
  *  workspace: loglinear_gdn_fwd_workspace_bytes(...) bytes, 256-byte
- *         aligned (about 4*B*H*T*dk + 8*B*H*(T/chunk)*dk*(dk+dv) bytes).
+ *         aligned (about 4*B*H*T*(dk+dv) + 8*B*H*(T/chunk)*dk*(dk+dv) bytes;
+ *         the same for both dtypes).
  * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
 size_t loglinear_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);
-ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v,
-                            const float *a, const float *beta, const float *lambda, float *out,
+ll_status loglinear_gdn_fwd(const void *q, const void *k, const void *v,
+                            const float *a, const float *beta, const float *lambda, void *out,
                             int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
 

@@ -314,9 +314,10 @@ def gdn_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int
 
 
 def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, stream=None):
-    """Log-Linear Gated DeltaNet forward (float32).  q, k [B,H,T,dk],
-    v [B,H,T,dv], a and beta [B,H,T], lam [B,H,T,L] with L = num_levels(T).
-    Returns out [B,H,T,dv].  Asynchronous on ``stream``."""
+    """Log-Linear Gated DeltaNet forward.  q, k [B,H,T,dk], v [B,H,T,dv]
+    (float32 or bfloat16, same dtype; arithmetic in float32), a and beta
+    [B,H,T] and lam [B,H,T,L] float32 with L = num_levels(T).  Returns out
+    [B,H,T,dv] in the input dtype.  Asynchronous on ``stream``."""
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
     B, H, T, dk = q.shape
@@ -324,8 +325,11 @@ def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, st
     L = num_levels(T)
     if tuple(a.shape) != (B, H, T) or tuple(beta.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
         raise ValueError(f"a and beta must be [B,H,T] and lam [B,H,T,{L}]")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
     if out is None:
-        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     need = gdn_fwd_workspace_bytes(B, H, T, dk, dv, chunk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -333,8 +337,8 @@ def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, st
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     f32 = torch.float32
     st = lib().loglinear_gdn_fwd(
-        _dev(q, "q", f32), _dev(k, "k", f32), _dev(v, "v", f32), _dev(a, "a", f32), _dev(beta, "beta", f32),
-        _dev(lam, "lam", f32), _dev(out, "out", f32), B, H, T, dk, dv, chunk, LL_F32, ws_ptr, ws_bytes,
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", f32), _dev(beta, "beta", f32),
+        _dev(lam, "lam", f32), _dev(out, "out", q.dtype), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes,
         _stream(stream))
     _check(st)
     return out

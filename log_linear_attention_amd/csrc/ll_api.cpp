@@ -492,8 +492,8 @@ size_t loglinear_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, in
     return ll::gdn_plan(B, H, T, dk, dv, chunk).bytes;
 }
 
-ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, const float *a, const float *beta,
-                            const float *lambda, float *out, int B, int H, int T, int dk, int dv, int chunk,
+ll_status loglinear_gdn_fwd(const void *q, const void *k, const void *v, const float *a, const float *beta,
+                            const float *lambda, void *out, int B, int H, int T, int dk, int dv, int chunk,
                             ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream)
 {
     const char *who = "loglinear_gdn_fwd";
@@ -502,8 +502,6 @@ ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, cons
     ll_status st = check_fwd_shape(who, B, H, T, dk, dv, chunk);
     if (st != LL_OK)
         return st;
-    if (dtype != LL_F32)
-        return fail(LL_EUNSUPPORTED, "%s: float32 only", who);
     if (!ll::gdn_supported(dk, dv, chunk))
         return fail(LL_EUNSUPPORTED, "%s: no kernel for dk=%d dv=%d chunk=%d", who, dk, dv, chunk);
     if ((int64_t)B * H > 65535)
@@ -519,8 +517,9 @@ ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, cons
     for (int i = 0; i < 7; ++i) {
         if (!ptrs[i])
             return fail(LL_EINVAL, "%s: %s is NULL", who, names[i]);
-        if (!aligned(ptrs[i], 4))
-            return fail(LL_EINVAL, "%s: %s is not 4-byte aligned", who, names[i]);
+        // q, k, v, out are read and written four elements at a time
+        if (!aligned(ptrs[i], (i < 3 || i == 6) ? 16 : 4))
+            return fail(LL_EINVAL, "%s: %s is misaligned", who, names[i]);
     }
     const ll::GdnPlan plan = ll::gdn_plan(B, H, T, dk, dv, chunk);
     if (!workspace)
@@ -529,7 +528,8 @@ ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, cons
         return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, plan.bytes, workspace_bytes);
     if (!aligned(workspace, 256))
         return fail(LL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-    const size_t nq = (size_t)rows * dk * 4, nv = (size_t)rows * dv * 4, na = (size_t)rows * 4,
+    const size_t es = dtype == LL_BF16 ? 2 : 4;
+    const size_t nq = (size_t)rows * dk * es, nv = (size_t)rows * dv * es, na = (size_t)rows * 4,
                  nl = (size_t)rows * L * 4;
     const void *all[] = {q, k, v, a, beta, lambda, workspace};
     const size_t sz[] = {nq, nq, nv, na, na, nl, plan.bytes};
@@ -540,6 +540,7 @@ ll_status loglinear_gdn_fwd(const float *q, const float *k, const float *v, cons
         if (overlaps(workspace, plan.bytes, all[i], sz[i]))
             return fail(LL_EINVAL, "%s: workspace aliases an input", who);
     ll::GdnArgs args{q, k, v, a, beta, lambda, out, B, H, T, dk, dv, chunk, L, workspace};
+    args.bf16 = dtype == LL_BF16;
     hipError_t e = ll::gdn_launch(args, plan, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));

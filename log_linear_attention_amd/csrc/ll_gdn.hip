@@ -38,13 +38,16 @@
 // differences for a <= 0.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "ll_device.h"
 #include "ll_internal.h"
 
 namespace ll {
 
-template <int DK_, int DV_, int C_>
+template <class DT, int DK_, int DV_, int C_>
 struct Gdn {
+    using T = typename DT::T;   // q, k, v and out; everything else is float32
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr int NT = 256;
     static constexpr int CNT = 512;   // chunk kernel threads (one workgroup per CU: LDS)
@@ -88,6 +91,21 @@ __device__ __forceinline__ size_t gdn_level_off(int N, int p)
 }
 
 __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+
+// Four consecutive input elements as float32.
+__device__ __forceinline__ float4 ld4t(const float *p) { return ld4(p); }
+__device__ __forceinline__ float4 ld4t(const __bf16 *p)
+{
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+
+__device__ __forceinline__ void st4t(float *p, const float4 &x) { *reinterpret_cast<float4 *>(p) = x; }
+__device__ __forceinline__ void st4t(__bf16 *p, const float4 &x)
+{
+    const bf16x4 y = {(__bf16)x.x, (__bf16)x.y, (__bf16)x.z, (__bf16)x.w};
+    *reinterpret_cast<bf16x4 *>(p) = y;
+}
 
 // 4 x 4 block of A B^T with A, B row-major in LDS (k contiguous, 16-byte rows):
 // acc[u][w] += sum_k A[a0 + u][k] * B[b0 + w][k], k < K (K a multiple of 4).
@@ -226,8 +244,9 @@ __device__ __forceinline__ void gdn_solve_z(SM &sm, int i)
 }
 
 template <class G>
-__global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const float *__restrict__ q, const float *__restrict__ k,
-                                                      const float *__restrict__ v, const float *__restrict__ a,
+__global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__restrict__ q,
+                                                      const typename G::T *__restrict__ k,
+                                                      const typename G::T *__restrict__ v, const float *__restrict__ a,
                                                       const float *__restrict__ beta, const float *__restrict__ lam,
                                                       float *__restrict__ out, float *__restrict__ qt,
                                                       float *__restrict__ Phit, float *__restrict__ Dt, int Tlen,
@@ -251,13 +270,13 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const float *__restrict__
     for (int u = 0; u < NQ4; ++u) {
         const int e = tid + u * NT, i = e / (DK / 4), d = 4 * (e % (DK / 4));
         const bool ok = e < C * DK / 4 && i < valid;
-        rq[u] = ok ? ld4(q + (row0 + i) * DK + d) : z4;
-        rk[u] = ok ? ld4(k + (row0 + i) * DK + d) : z4;
+        rq[u] = ok ? ld4t(q + (row0 + i) * DK + d) : z4;
+        rk[u] = ok ? ld4t(k + (row0 + i) * DK + d) : z4;
     }
 #pragma unroll
     for (int u = 0; u < NV4; ++u) {
         const int e = tid + u * NT, i = e / (DV / 4), d = 4 * (e % (DV / 4));
-        rv[u] = (e < C * DV / 4 && i < valid) ? ld4(v + (row0 + i) * DV + d) : z4;
+        rv[u] = (e < C * DV / 4 && i < valid) ? ld4t(v + (row0 + i) * DV + d) : z4;
     }
 #pragma unroll
     for (int u = 0; u < NQ4; ++u) {
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const float *__restrict__
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u;
-            const float4 qv = i < valid ? ld4(q + (row0 + i) * DK + d0) : z4;
+            const float4 qv = i < valid ? ld4t(q + (row0 + i) * DK + d0) : z4;
             const float g = __expf(sm.Aloc[i]);
             *reinterpret_cast<float4 *>(qtc + (size_t)i * DK + d0) =
                 make_float4(g * (qv.x - acc[u][0]), g * (qv.y - acc[u][1]), g * (qv.z - acc[u][2]),
@@ -570,7 +589,8 @@ __device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const floa
 template <class G>
 __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ lam, const float *__restrict__ qt,
                                                      const float *__restrict__ Phit, const float *__restrict__ Dt,
-                                                     float *__restrict__ out, int Tlen, int L, int N, int NBT)
+                                                     const float *obuf, typename G::T *out, int Tlen, int L, int N,
+                                                     int NBT)
 {
     constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::WNT;
     // outputs: 4 columns x NRO4 rows per thread; carried queries: 4 x NRY4
@@ -581,10 +601,15 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
     __shared__ __attribute__((aligned(16))) float Bs[kGdnKS * (DK > DV ? DK : DV)];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
-    if (c == 0)
-        return;   // no chunk-level bucket
     const int t0 = c * C, valid = min(C, Tlen - t0);
     const size_t row0 = (size_t)bh * Tlen + t0;
+    if (c == 0) {
+        // no chunk-level bucket: the in-chunk output is the output
+        if constexpr (!std::is_same<typename G::T, float>::value)
+            for (int e = tid; e < valid * DV / 4; e += NT)
+                st4t(out + row0 * DV + 4 * e, ld4(obuf + row0 * DV + 4 * e));
+        return;
+    }
     const float *qtc = qt + ((size_t)bh * N + c) * C * DK;
     for (int e = tid; e < C * DK / 4; e += NT) {
         const int i = e / (DK / 4), d4 = e % (DK / 4);
@@ -632,10 +657,9 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
     for (int r = 0; r < NRO4; ++r) {
         const int i = or0 + ORG * r;
         if (i < valid) {
-            float4 *o = reinterpret_cast<float4 *>(out + (row0 + i) * DV + on0);
-            float4 x = *o;
+            float4 x = ld4(obuf + (row0 + i) * DV + on0);
             x.x += acc[r][0]; x.y += acc[r][1]; x.z += acc[r][2]; x.w += acc[r][3];
-            *o = x;
+            st4t(out + (row0 + i) * DV + on0, x);
         }
     }
 }
@@ -668,24 +692,30 @@ GdnPlan gdn_plan(int B, int H, int T, int dk, int dv, int chunk)
     p.off_qt = 0;
     p.off_phi = (qt + 255) & ~(size_t)255;
     p.off_d = (p.off_phi + ph + 255) & ~(size_t)255;
-    p.bytes = (p.off_d + dd + 255) & ~(size_t)255;
+    p.off_oi = (p.off_d + dd + 255) & ~(size_t)255;   // float32 in-chunk output (bf16 inputs)
+    p.bytes = (p.off_oi + BH * (size_t)T * dv * 4 + 255) & ~(size_t)255;
     return p;
 }
 
 typedef hipError_t (*GdnLauncher)(const GdnArgs &, const GdnPlan &, hipStream_t);
 
-template <int DK, int DV, int C>
+template <class DT, int DK, int DV, int C>
 static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s)
 {
-    using G = Gdn<DK, DV, C>;
+    using G = Gdn<DT, DK, DV, C>;
+    using T = typename G::T;
+    constexpr bool F32 = std::is_same<T, float>::value;
     const int BH = A.B * A.H;
     char *ws = static_cast<char *>(A.workspace);
     float *qt = reinterpret_cast<float *>(ws + P.off_qt);
     float *Phit = reinterpret_cast<float *>(ws + P.off_phi);
     float *Dt = reinterpret_cast<float *>(ws + P.off_d);
+    // float32 outputs are accumulated in place; bf16 ones through a float32 buffer
+    float *obuf = F32 ? static_cast<float *>(A.out) : reinterpret_cast<float *>(ws + P.off_oi);
     ProfEvents pe = prof_events("ll_gdn_chunk");
-    hipExtLaunchKernelGGL(ll_gdn_chunk<G>, dim3(BH * P.N), dim3(G::CNT), 0, s, pe.start, pe.stop, 0, A.q, A.k, A.v,
-                          A.a, A.beta, A.lam, A.out, qt, Phit, Dt, A.T, A.L, P.N, P.NBT);
+    hipExtLaunchKernelGGL(ll_gdn_chunk<G>, dim3(BH * P.N), dim3(G::CNT), 0, s, pe.start, pe.stop, 0,
+                          (const T *)A.q, (const T *)A.k, (const T *)A.v, A.a, A.beta, A.lam, obuf, qt, Phit, Dt,
+                          A.T, A.L, P.N, P.NBT);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -698,52 +728,58 @@ static hipError_t launch_gdn_t(const GdnArgs &A, const GdnPlan &P, hipStream_t s
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
-    if (P.N > 1) {
+    if (P.N > 1 || !F32) {
         pe = prof_events("ll_gdn_walk");
         hipExtLaunchKernelGGL(ll_gdn_walk<G>, dim3(BH * P.N), dim3(G::WNT), 0, s, pe.start, pe.stop, 0, A.lam,
-                              (const float *)qt, (const float *)Phit, (const float *)Dt, A.out, A.T, A.L, P.N,
-                              P.NBT);
+                              (const float *)qt, (const float *)Phit, (const float *)Dt, (const float *)obuf,
+                              (T *)A.out, A.T, A.L, P.N, P.NBT);
         e = hipGetLastError();
     }
     return e;
 }
 
-template <int DK, int DV>
+template <class DT, int DK, int DV>
 static GdnLauncher gdn_pick_c(int chunk)
 {
     switch (chunk) {
-    case 32: return &launch_gdn_t<DK, DV, 32>;
-    case 64: return &launch_gdn_t<DK, DV, 64>;
+    case 32: return &launch_gdn_t<DT, DK, DV, 32>;
+    case 64: return &launch_gdn_t<DT, DK, DV, 64>;
     default: return nullptr;
     }
 }
 
-template <int DK>
+template <class DT, int DK>
 static GdnLauncher gdn_pick_dv(int dv, int chunk)
 {
     switch (dv) {
-    case 32: return gdn_pick_c<DK, 32>(chunk);
-    case 64: return gdn_pick_c<DK, 64>(chunk);
-    case 128: return gdn_pick_c<DK, 128>(chunk);
+    case 32: return gdn_pick_c<DT, DK, 32>(chunk);
+    case 64: return gdn_pick_c<DT, DK, 64>(chunk);
+    case 128: return gdn_pick_c<DT, DK, 128>(chunk);
     default: return nullptr;
     }
 }
 
-static GdnLauncher find_gdn(int dk, int dv, int chunk)
+template <class DT>
+static GdnLauncher gdn_pick(int dk, int dv, int chunk)
 {
     switch (dk) {
-    case 32: return gdn_pick_dv<32>(dv, chunk);
-    case 64: return gdn_pick_dv<64>(dv, chunk);
-    case 128: return gdn_pick_dv<128>(dv, chunk);
+    case 32: return gdn_pick_dv<DT, 32>(dv, chunk);
+    case 64: return gdn_pick_dv<DT, 64>(dv, chunk);
+    case 128: return gdn_pick_dv<DT, 128>(dv, chunk);
     default: return nullptr;
     }
 }
 
-bool gdn_supported(int dk, int dv, int chunk) { return find_gdn(dk, dv, chunk) != nullptr; }
+static GdnLauncher find_gdn(bool bf16, int dk, int dv, int chunk)
+{
+    return bf16 ? gdn_pick<TBF16>(dk, dv, chunk) : gdn_pick<TF32>(dk, dv, chunk);
+}
+
+bool gdn_supported(int dk, int dv, int chunk) { return find_gdn(false, dk, dv, chunk) != nullptr; }
 
 hipError_t gdn_launch(const GdnArgs &args, const GdnPlan &plan, hipStream_t stream)
 {
-    GdnLauncher f = find_gdn(args.dk, args.dv, args.chunk);
+    GdnLauncher f = find_gdn(args.bf16, args.dk, args.dv, args.chunk);
     if (!f)
         return hipErrorInvalidValue;
     return f(args, plan, stream);

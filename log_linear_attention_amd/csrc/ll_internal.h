@@ -119,13 +119,16 @@ bool bwd_supported(bool bf16, int dk, int dv, int chunk);
 hipError_t bwd_launch(const BwdArgs &args, const BwdPlan &plan, hipStream_t stream);
 hipError_t stack_launch(const StackArgs &args, hipStream_t stream);
 
-// Log-Linear Gated DeltaNet forward (float32): q, k [BH, T, dk], v and out
-// [BH, T, dv], a and beta [BH, T], lam [BH, T, L].
+// Log-Linear Gated DeltaNet forward (float32 arithmetic; q, k, v, out in
+// float32 or bf16): q, k [BH, T, dk], v and out [BH, T, dv], a and beta
+// [BH, T], lam [BH, T, L].
 struct GdnArgs {
-    const float *q, *k, *v, *a, *beta, *lam;
-    float *out;
+    const void *q, *k, *v;       // input dtype
+    const float *a, *beta, *lam;
+    void *out;                   // input dtype
     int B, H, T, dk, dv, chunk, L;
     void *workspace;
+    bool bf16 = false;
 };
 
 // Workspace: carried queries [BH][N*C][dk], then the tree over chunks
@@ -133,7 +136,7 @@ struct GdnArgs {
 // [dk][dk] and transposed states [dk][dv].
 struct GdnPlan {
     int N = 0, P = 0, NBT = 0;
-    size_t off_qt = 0, off_phi = 0, off_d = 0, bytes = 0;
+    size_t off_qt = 0, off_phi = 0, off_d = 0, off_oi = 0, bytes = 0;
 };
 
 GdnPlan gdn_plan(int B, int H, int T, int dk, int dv, int chunk);

@@ -331,7 +331,8 @@ def test_gdn_rejects_bad_arguments(L):
                                    args["out"], args["B"], args["H"], args["T"], args["dk"], args["dv"],
                                    args["chunk"], args["dtype"], args["ws"], args["wsb"], args["stream"])
 
-    assert call(dtype=ll.LL_BF16) == ll.LL_EUNSUPPORTED
+    assert call(dtype=7) == ll.LL_EINVAL
+    assert call(q=FAKE + 4) == ll.LL_EINVAL                         # q is read four elements at a time
     assert call(chunk=16) == ll.LL_EUNSUPPORTED
     assert call(dk=16) == ll.LL_EUNSUPPORTED
     assert call(beta=None) == ll.LL_EINVAL

@@ -86,3 +86,40 @@ def test_gdn_16k_workload_sampled():
     e = rel_l2(g, ref)
     print(f"rel_l2 {e:.3e} over {len(rows)} rows")
     assert e <= TOL["f32"]
+
+
+def _to_bf16(inp):
+    d = dict(inp)
+    for n in ("q", "k", "v"):
+        d[n] = inp[n].to(torch.bfloat16).contiguous()
+    return d
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 64), (65, 64), (1000, 32), (2049, 64)])
+def test_gdn_bf16_inputs(T, chunk):
+    """bf16 q, k, v (float32 arithmetic, bf16 output) against the oracle on
+    the same bf16 values."""
+    cfg = synth.FwdConfig("gdn_bf16", 1, 2, T, 128, 64, chunk, "bf16", 0.05, 9400 + T)
+    announce(f"gdn bf16 T={T} chunk={chunk}")
+    inp = _to_bf16(synth.make_gdn_inputs(cfg))
+    out = _run(inp, chunk)
+    assert out.dtype == torch.bfloat16
+    ref = gdn.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], inp["lam"])
+    got = f64(out)
+    e = max(rel_l2(got, ref), per_head_max(got, ref))
+    print(f"rel_l2 {e:.3e}")
+    assert np.all(np.isfinite(got)) and e <= TOL["bf16"], e
+
+
+def test_gdn_bf16_16k_sampled():
+    cfg = synth.WORKLOADS["gdn_f32_T16K"]
+    announce(f"{cfg.name} with bf16 inputs")
+    inp = _to_bf16(synth.make_gdn_inputs(cfg))
+    out = _run(inp, cfg.chunk)
+    rows = synth.sample_rows(cfg.B, cfg.H, cfg.T, cfg.chunk, 6, seed=94)
+    ref = gdn.gdn_fwd_rows(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], inp["lam"], rows)
+    got = f64(out).reshape(cfg.B * cfg.H, cfg.T, cfg.dv)
+    g = np.stack([got[bh, t] for bh, t in rows])
+    e = rel_l2(g, ref)
+    print(f"rel_l2 {e:.3e} over {len(rows)} rows")
+    assert e <= TOL["bf16"]
