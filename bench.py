@@ -216,7 +216,7 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     }
 
 
-def gdn_algorithmic(cfg):
+def gdn_algorithmic(cfg, es: int = 4):
     """Algorithmic flops per kernel of the Log-Linear Gated DeltaNet forward
     and its mandatory bytes.  Per chunk of C (dk, dv): Q K^T and K K^T
     (lower half), the W solve, the carried queries, the in-chunk solve
@@ -237,17 +237,21 @@ def gdn_algorithmic(cfg):
         pc = bin(c).count("1")
         walk += pc * 2 * C * dk * dv + (pc - 1) * 2 * C * dk * dk
     flops = {"ll_gdn_chunk": BH * N * chunk, "ll_gdn_tree": BH * tree, "ll_gdn_walk": BH * walk}
-    nbytes = BH * T * (2 * dk + dv + 2 + L + dv) * 4
+    nbytes = BH * T * ((2 * dk + 2 * dv) * es + (2 + L) * 4)   # q, k, v, out in the input dtype
     return flops, nbytes
 
 
-def measure_gdn(ll, torch, dev, args, e0, e1):
-    """The Log-Linear Gated DeltaNet forward (float32) at the 16K shape."""
+def measure_gdn(ll, torch, dev, args, e0, e1, bf16=False):
+    """The Log-Linear Gated DeltaNet forward at the 16K shape: float32
+    inputs, or the same inputs rounded to bf16 (float32 arithmetic)."""
     import synth
 
     cfg = synth.WORKLOADS["gdn_f32_T16K"]
     d = {k: v.to(dev) for k, v in synth.make_gdn_inputs(cfg).items()}
-    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=torch.float32, device=dev)
+    if bf16:
+        for n in ("q", "k", "v"):
+            d[n] = d[n].to(torch.bfloat16)
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=d["q"].dtype, device=dev)
     ws = torch.empty(ll.gdn_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
                      device=dev)
 
@@ -271,13 +275,14 @@ def measure_gdn(ll, torch, dev, args, e0, e1):
     torch.cuda.synchronize()
     stats = ll.profile_end()
     ks = {k: v[1] / n for k, v in stats.items()}   # per step (the tree kernel runs once per level)
-    flops, nbytes = gdn_algorithmic(cfg)
+    flops, nbytes = gdn_algorithmic(cfg, 2 if bf16 else 4)
     dom = max(ks, key=ks.get)
     launches = stats[dom][0] / n
     achieved = flops[dom] / (ks[dom] * 1e-3) / 1e12
-    log(f"gdn: {ms:.4f} ms/step; kernels (ms per step): { {k: round(v, 4) for k, v in ks.items()} }")
+    log(f"gdn ({'bf16' if bf16 else 'f32'} inputs): {ms:.4f} ms/step; kernels (ms per step): "
+        f"{ {k: round(v, 4) for k, v in ks.items()} }")
     return {
-        "workload": cfg.name, "dtype": "f32", "ms_per_step": round(ms, 5),
+        "workload": cfg.name, "dtype": "f32", "inputs": "bf16" if bf16 else "f32", "ms_per_step": round(ms, 5),
         "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
         "kernels_ms_per_step": {k: round(v, 5) for k, v in ks.items()},
         "algorithmic_flops": flops, "mandatory_bytes": nbytes,
@@ -491,7 +496,7 @@ def main():
                                             for hq in (4, 1)]
 
     # ---- Log-Linear Gated DeltaNet forward ----
-    gdn_res = None if args.no_gdn else measure_gdn(ll, torch, dev, args, e0, e1)
+    gdn_res = None if args.no_gdn else [measure_gdn(ll, torch, dev, args, e0, e1, bf16=b) for b in (False, True)]
 
     # ---- backward: gradients of the forward on the same workload ----
     backward = None if args.no_bwd else measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1)
