@@ -123,3 +123,29 @@ def test_gdn_bf16_16k_sampled():
     e = rel_l2(g, ref)
     print(f"rel_l2 {e:.3e} over {len(rows)} rows")
     assert e <= TOL["bf16"]
+
+
+def test_gdn_padded_batch_rows_do_not_see_padding():
+    """Prompts of different lengths padded to one T: the form is causal, so
+    the real rows of each sequence match the oracle on that sequence alone
+    and do not change, bit for bit, when the padding changes."""
+    T, lens = 700, [700, 333, 64, 1]
+    cfg = synth.FwdConfig("gdn_pad", len(lens), 2, T, 64, 32, 32, "f32", 0.05, 9500)
+    announce(f"gdn padded batch lens={lens}")
+    inp = synth.make_gdn_inputs(cfg)
+    junk = synth.make_gdn_inputs(cfg, seed=9501)
+    pad1 = {n: x.clone() for n, x in inp.items()}
+    pad2 = {n: x.clone() for n, x in inp.items()}
+    for b, Tb in enumerate(lens):
+        for n in inp:
+            pad1[n][b, :, Tb:] = junk[n][b, :, Tb:]
+            pad2[n][b, :, Tb:] = 0.0
+    out1 = _run(pad1, 32)
+    out2 = _run(pad2, 32)
+    for b, Tb in enumerate(lens):
+        assert torch.equal(out1[b, :, :Tb], out2[b, :, :Tb]), b
+        s = {n: x[b:b + 1, :, :Tb].contiguous() for n, x in inp.items()}
+        ref = gdn.gdn_fwd(s["q"], s["k"], s["v"], s["a"], s["beta"], s["lam"])
+        e = rel_l2(f64(out1[b:b + 1, :, :Tb]), ref)
+        print(f"seq {b} (len {Tb}): rel_l2 {e:.3e}")
+        assert e <= TOL["f32"]
