@@ -533,73 +533,59 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     }
 }
 
-constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a time
+constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a time (one fp32 MFMA unit)
 
-// Four rows kk .. kk+3 of a staged slice (absolute rows k0 + kk ..).
-template <int NR, int RS, int LDY, int NB>
-__device__ __forceinline__ void gdn_rows_step(const float (*Y)[LDY], const float *Bs, int k0, int kk, int r0, int n0,
-                                              float (&acc)[NR][4])
+// Tiles of Y B (Y: C x DK rows in LDS, B: DK x NB row-major in global memory)
+// on fp32 MFMA, 16 x 16 output tiles t = w, w + NW, ... of wave w; B is
+// staged through LDS (Bs) one 16-row unit at a time, read once per
+// workgroup.  Every thread of the workgroup must call this.  acc tile j of
+// the wave holds rows 16 * (t / (NB/16)) + 4*qd + r, column 16 * (t % (NB/16)) + li.
+template <int NTW, int NW, int C, int DK, int LDY, int NB>
+__device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float *B, float *Bs, int w, int li, int qd,
+                                              floatx4 (&acc)[NTW])
 {
-    float4 b[4];
+    constexpr int TN = NB / 16, TT = (C / 16) * TN;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-        b[u] = *reinterpret_cast<const float4 *>(Bs + (kk + u) * NB + n0);
+    for (int j = 0; j < NTW; ++j)
+        acc[j] = zero4();
+#pragma unroll 1
+    for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
+        __syncthreads();   // the previous unit has been read
+        for (int e = threadIdx.x; e < kGdnKS * NB / 4; e += blockDim.x)
+            *reinterpret_cast<float4 *>(Bs + 4 * e) = *reinterpret_cast<const float4 *>(B + (size_t)k0 * NB + 4 * e);
+        __syncthreads();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        const float4 y = *reinterpret_cast<const float4 *>(&Y[r0 + RS * r][k0 + kk]);
-        const float yr[4] = {y.x, y.y, y.z, y.w};
+        for (int j = 0; j < NTW; ++j) {
+            const int t = w + NW * j;
+            if (t < TT) {
+                const int it = t / TN, nt = t % TN;
+                const floatx4 af = lds_frag(&Y[0][0], LDY, 16 * it + li, k0, qd);
+                floatx4 bf;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc[r][0] += yr[u] * b[u].x;
-            acc[r][1] += yr[u] * b[u].y;
-            acc[r][2] += yr[u] * b[u].z;
-            acc[r][3] += yr[u] * b[u].w;
+                for (int e = 0; e < 4; ++e)
+                    bf[e] = Bs[(4 * qd + e) * NB + 16 * nt + li];
+                mma_unit(acc[j], af, bf);
+            }
         }
     }
 }
 
-// Y[rows][k] (LDS) times B[k][cols] (global, row-major, NB columns) for one
-// thread's block: rows r0 + RS*r (r < NR), columns n0 .. n0+3.  B is staged
-// through LDS (Bs) kGdnKS rows at a time, read once per workgroup; every
-// thread of the workgroup must call this.
-template <int NR, int RS, int DK, int LDY, int NB>
-__device__ __forceinline__ void gdn_rows_x_mat(const float (*Y)[LDY], const float *B, float *Bs, int r0, int n0,
-                                               float (&acc)[NR][4])
-{
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            acc[r][w] = 0.f;
-#pragma unroll 1
-    for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
-        __syncthreads();   // the previous slice has been read
-        for (int e = threadIdx.x; e < kGdnKS * NB / 4; e += blockDim.x)
-            *reinterpret_cast<float4 *>(Bs + 4 * e) = *reinterpret_cast<const float4 *>(B + (size_t)k0 * NB + 4 * e);
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < kGdnKS; kk += 4)
-            gdn_rows_step<NR, RS, LDY, NB>(Y, Bs, k0, kk, r0, n0, acc);
-    }
-}
-
-// Chunk-level buckets: out[i] += sum over set bits m-1 of c of
+// Chunk-level buckets: out[i] = obuf[i] + sum over set bits m-1 of c of
 // lambda_i[log2 C + m] D_m qt_i^(m), with the carried query moved through
-// each used block's transition before the next, coarser one.
+// each used block's transition before the next, coarser one.  The products
+// run on fp32 MFMA.
 template <class G>
 __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ lam, const float *__restrict__ qt,
                                                      const float *__restrict__ Phit, const float *__restrict__ Dt,
                                                      const float *obuf, typename G::T *out, int Tlen, int L, int N,
                                                      int NBT)
 {
-    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::WNT;
-    // outputs: 4 columns x NRO4 rows per thread; carried queries: 4 x NRY4
-    constexpr int OCG = DV / 4, ORG = NT / OCG, NRO4 = C / ORG;
-    constexpr int YCG = DK / 4, YRG = NT / YCG, NRY4 = C / YRG;
-    static_assert(NT % OCG == 0 && NT % YCG == 0 && C % ORG == 0 && C % YRG == 0, "walk layout");
+    constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::WNT, NW = NT / 64;
+    constexpr int T1 = (C / 16) * (DV / 16), T2 = (C / 16) * (DK / 16);
+    constexpr int N1 = (T1 + NW - 1) / NW, N2 = (T2 + NW - 1) / NW;
     __shared__ __attribute__((aligned(16))) float Y[2][C][DK + 4];
     __shared__ __attribute__((aligned(16))) float Bs[kGdnKS * (DK > DV ? DK : DV)];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
     const int t0 = c * C, valid = min(C, Tlen - t0);
     const size_t row0 = (size_t)bh * Tlen + t0;
@@ -615,15 +601,10 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
         const int i = e / (DK / 4), d4 = e % (DK / 4);
         *reinterpret_cast<float4 *>(&Y[0][i][4 * d4]) = *reinterpret_cast<const float4 *>(qtc + (size_t)i * DK + 4 * d4);
     }
-    __syncthreads();
-    const int on0 = 4 * (tid % OCG), or0 = tid / OCG;
-    const int yn0 = 4 * (tid % YCG), yr0 = tid / YCG;
-    float acc[NRO4][4];
+    floatx4 acc[N1];
 #pragma unroll
-    for (int r = 0; r < NRO4; ++r)
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            acc[r][w] = 0.f;
+    for (int j = 0; j < N1; ++j)
+        acc[j] = zero4();
     int cur = 0;
     const int top = bitlen((unsigned)c);
     for (int m = 1; m <= top; ++m) {
@@ -631,35 +612,52 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
             continue;
         const int p = m - 1, jb = (c >> m) << 1;
         const size_t blk = (size_t)bh * NBT + gdn_level_off(N, p) + jb;
-        float tmp[NRO4][4];
-        gdn_rows_x_mat<NRO4, ORG, DK, DK + 4, DV>(Y[cur], Dt + blk * DK * DV, Bs, or0, on0, tmp);
+        floatx4 tmp[N1];
+        gdn_tiles_mma<N1, NW, C, DK, DK + 4, DV>(Y[cur], Dt + blk * DK * DV, Bs, w, li, qd, tmp);
 #pragma unroll
-        for (int r = 0; r < NRO4; ++r) {
-            const int i = or0 + ORG * r;
-            const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
+        for (int j = 0; j < N1; ++j) {
+            const int t = w + NW * j;
+            if (t < T1) {
+                const int ib = 16 * (t / (DV / 16)) + 4 * qd;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                acc[r][w] += lw * tmp[r][w];
+                for (int r = 0; r < 4; ++r) {
+                    const int i = ib + r;
+                    const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
+                    acc[j][r] += lw * tmp[j][r];
+                }
+            }
         }
         if ((c >> m) == 0)
             break;   // no coarser bucket
         // carry the queries through this block: Y' = Y Phi^T
-        float ny[NRY4][4];
-        gdn_rows_x_mat<NRY4, YRG, DK, DK + 4, DK>(Y[cur], Phit + blk * DK * DK, Bs, yr0, yn0, ny);
+        floatx4 ny[N2];
+        gdn_tiles_mma<N2, NW, C, DK, DK + 4, DK>(Y[cur], Phit + blk * DK * DK, Bs, w, li, qd, ny);
 #pragma unroll
-        for (int r = 0; r < NRY4; ++r)
-            *reinterpret_cast<float4 *>(&Y[cur ^ 1][yr0 + YRG * r][yn0]) =
-                make_float4(ny[r][0], ny[r][1], ny[r][2], ny[r][3]);
+        for (int j = 0; j < N2; ++j) {
+            const int t = w + NW * j;
+            if (t < T2) {
+                const int ib = 16 * (t / (DK / 16)) + 4 * qd, n = 16 * (t % (DK / 16)) + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Y[cur ^ 1][ib + r][n] = ny[j][r];
+            }
+        }
         __syncthreads();
         cur ^= 1;
     }
 #pragma unroll
-    for (int r = 0; r < NRO4; ++r) {
-        const int i = or0 + ORG * r;
-        if (i < valid) {
-            float4 x = ld4(obuf + (row0 + i) * DV + on0);
-            x.x += acc[r][0]; x.y += acc[r][1]; x.z += acc[r][2]; x.w += acc[r][3];
-            st4t(out + (row0 + i) * DV + on0, x);
+    for (int j = 0; j < N1; ++j) {
+        const int t = w + NW * j;
+        if (t < T1) {
+            const int ib = 16 * (t / (DV / 16)) + 4 * qd, n = 16 * (t % (DV / 16)) + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = ib + r;
+                if (i < valid) {
+                    const size_t o = (row0 + i) * DV + n;
+                    out[o] = from_f32<typename G::T>(obuf[o] + acc[j][r]);
+                }
+            }
         }
     }
 }
