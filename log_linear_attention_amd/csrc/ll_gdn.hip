@@ -458,8 +458,10 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 
 // One tree level p >= 1: block j from its children 2j (L) and 2j+1 (R) at
 // level p-1:  Phi^T = Phi_R^T Phi_L^T,  D^T = Phi_R^T D_L^T + D_R^T.
-// Output [DK rows] x [DK + DV columns] in 64 x 64 tiles, the contraction in
-// slices of 16 staged through LDS; each thread accumulates a 4 x 4 block.
+// Output [DK rows] x [DK + DV columns] in 64 x 64 tiles (rows x columns;
+// DK < 64: DK rows) on fp32 MFMA, 16 x 16 subtiles spread over the four
+// waves; both operands staged through LDS one 16-wide contraction unit at a
+// time.
 template <class G>
 __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, float *__restrict__ Dt, int N, int NBT,
                                                    int p)
@@ -467,11 +469,11 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     constexpr int DK = G::DK, DV = G::DV, NC = DK + DV;
     constexpr int TS = DK < 64 ? DK : 64;            // tile edge (rows and columns)
     constexpr int TR = DK / TS, TN = (NC + TS - 1) / TS;
-    constexpr int KS = 16;                            // contraction slice
-    constexpr int TPR = TS / 4;                       // threads per tile row of 4-column groups
-    __shared__ __attribute__((aligned(16))) float As[KS][TS + 4];   // As[k][r] = Phi_R^T[row0 + r][k0 + k]
+    constexpr int KS = 16;                            // contraction unit
+    constexpr int SR = TS / 16, ST = SR * SR, NSW = (ST + 3) / 4;   // 16 x 16 subtiles, per wave
+    __shared__ __attribute__((aligned(16))) float As[TS][KS + 4];   // As[r][k] = Phi_R^T[row0 + r][k0 + k]
     __shared__ __attribute__((aligned(16))) float Bs[KS][TS + 4];   // Bs[k][n] = [Phi_L^T | D_L^T][k0 + k][col0 + n]
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.y;
     const int tile = blockIdx.x % (TR * TN), j = blockIdx.x / (TR * TN);
     const int tr = tile / TN, tn = tile % TN;
@@ -482,15 +484,16 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     const float *PL = Phit + L * DK * DK;
     const float *DL = Dt + L * DK * DV;
     const int row0 = TS * tr, col0 = TS * tn;
-    // thread block of outputs: rows 4*ty .. +3, columns 4*tx .. +3 (TS = 64: 16 x 16 threads)
-    const int tx = tid % TPR, ty = tid / TPR;
-    const bool active = ty < TS / 4;
-    float acc[4][4] = {};
+    floatx4 acc[NSW];
+#pragma unroll
+    for (int x = 0; x < NSW; ++x)
+        acc[x] = zero4();
     for (int k0 = 0; k0 < DK; k0 += KS) {
         __syncthreads();
-        for (int e = tid; e < KS * TS; e += 256) {
-            const int r = e / KS, kk = e % KS;
-            As[kk][r] = PR[(size_t)(row0 + r) * DK + k0 + kk];
+        for (int e = tid; e < TS * KS / 4; e += 256) {
+            const int r = e / (KS / 4), k4 = 4 * (e % (KS / 4));
+            *reinterpret_cast<float4 *>(&As[r][k4]) =
+                *reinterpret_cast<const float4 *>(PR + (size_t)(row0 + r) * DK + k0 + k4);
         }
         for (int e = tid; e < KS * TS; e += 256) {
             const int kk = e / TS, n = e % TS, col = col0 + n;
@@ -502,33 +505,35 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
             Bs[kk][n] = x;
         }
         __syncthreads();
-        if (active) {
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const float4 av = *reinterpret_cast<const float4 *>(&As[kk][4 * ty]);
-                const float4 bv = *reinterpret_cast<const float4 *>(&Bs[kk][4 * tx]);
-                const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+        for (int x = 0; x < NSW; ++x) {
+            const int st = w + 4 * x;
+            if (st < ST) {
+                const int sr = st / SR, sc = st % SR;
+                const floatx4 af = lds_frag(&As[0][0], KS + 4, 16 * sr + li, 0, qd);
+                floatx4 bf;
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        acc[u][w] += ar[u] * br[w];
+                for (int e = 0; e < 4; ++e)
+                    bf[e] = Bs[4 * qd + e][16 * sc + li];
+                mma_unit(acc[x], af, bf);
             }
         }
     }
-    if (!active)
-        return;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = row0 + 4 * ty + u;
+    for (int x = 0; x < NSW; ++x) {
+        const int st = w + 4 * x;
+        if (st < ST) {
+            const int sr = st / SR, sc = st % SR;
+            const int col = col0 + 16 * sc + li;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int col = col0 + 4 * tx + w;
-            if (col < DK)
-                Phit[self * DK * DK + (size_t)row * DK + col] = acc[u][w];
-            else if (col < NC)
-                Dt[self * DK * DV + (size_t)row * DV + col - DK] =
-                    acc[u][w] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+            for (int r = 0; r < 4; ++r) {
+                const int row = row0 + 16 * sr + 4 * qd + r;
+                if (col < DK)
+                    Phit[self * DK * DK + (size_t)row * DK + col] = acc[x][r];
+                else if (col < NC)
+                    Dt[self * DK * DV + (size_t)row * DV + col - DK] =
+                        acc[x][r] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+            }
         }
     }
 }
