@@ -107,46 +107,6 @@ __device__ __forceinline__ void st4t(__bf16 *p, const float4 &x)
     *reinterpret_cast<bf16x4 *>(p) = y;
 }
 
-// 4 x 4 block of A B^T with A, B row-major in LDS (k contiguous, 16-byte rows):
-// acc[u][w] += sum_k A[a0 + u][k] * B[b0 + w][k], k < K (K a multiple of 4).
-template <int K, int LDA, int LDB>
-__device__ __forceinline__ void blk_abt(const float (*A)[LDA], const float (*B)[LDB], int a0, int b0, float (&acc)[4][4])
-{
-#pragma unroll 2
-    for (int kk = 0; kk < K; kk += 4) {
-        float4 x[4], y[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            x[u] = ld4(&A[a0 + u][kk]);
-            y[u] = ld4(&B[b0 + u][kk]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                acc[u][w] += x[u].x * y[w].x + x[u].y * y[w].y + x[u].z * y[w].z + x[u].w * y[w].w;
-    }
-}
-
-// 4 x 4 block of A^T B with A, B row-major in LDS (contraction over rows r):
-// acc[u][w] += sum_r s[r] * A[r][a0 + u] * B[r][b0 + w], r < R.
-template <int R, int LDA, int LDB>
-__device__ __forceinline__ void blk_atb(const float (*A)[LDA], const float (*B)[LDB], const float *s, int a0, int b0,
-                                        float (&acc)[4][4])
-{
-#pragma unroll 4
-    for (int r = 0; r < R; ++r) {
-        const float4 x = ld4(&A[r][a0]), y = ld4(&B[r][b0]);
-        const float sr = s ? s[r] : 1.f;
-        const float xs[4] = {sr * x.x, sr * x.y, sr * x.z, sr * x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                acc[u][w] += xs[u] * ys[w];
-    }
-}
-
 // The chunk's triangular solves, four rows (or columns) per step: the
 // earlier rows' terms for a block of four are summed together (each earlier
 // value loaded once for the four), then the 4 x 4 diagonal block is solved.
@@ -253,7 +213,6 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
                                                       int L, int N, int NBT)
 {
     constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::CNT;
-    constexpr int CB = C / 4;                    // 4-row blocks per chunk
     __shared__ GdnChunkSmem<G> sm;
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / N, c = blockIdx.x % N;
@@ -317,30 +276,33 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     if (tid < C)
         sm.wend[tid] = __expf(sm.Aloc[C - 1] - sm.Aloc[tid]);
 
-    // ---- S = Q K^T, k_i.k_j and X[i][j] (j < i): 4 x 4 blocks ----
-    for (int b = tid; b < 2 * CB * CB; b += NT) {
-        const bool isg = b >= CB * CB;
-        const int bb = isg ? b - CB * CB : b;
-        const int i0 = 4 * (bb / CB), j0 = 4 * (bb % CB);
-        if (isg && j0 > i0 + 3)
-            continue;   // strictly upper block: not needed
-        float acc[4][4] = {};
-        if (isg)
-            blk_abt<DK, DK + 4, DK + 4>(sm.Ks, sm.Ks, i0, j0, acc);
-        else
-            blk_abt<DK, DK + 4, DK + 4>(sm.QW, sm.Ks, i0, j0, acc);
+    // ---- S = Q K^T, k_i.k_j and X[i][j] (j < i): 16 x 16 tiles on fp32 MFMA,
+    // one tile per wave at a time (the strictly upper tiles of K K^T skipped) ----
+    {
+        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
+        constexpr int NWV = NT / 64, TB = C / 16;
+        for (int b = wv; b < 2 * TB * TB; b += NWV) {
+            const bool isg = b >= TB * TB;
+            const int bb = isg ? b - TB * TB : b;
+            const int si = bb / TB, sj = bb % TB;
+            if (isg && sj > si)
+                continue;
+            floatx4 acc = zero4();
+            const float *A = isg ? &sm.Ks[0][0] : &sm.QW[0][0];
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 16)
+                mma_unit(acc, lds_frag(A, DK + 4, 16 * si + li, k0, qd), lds_frag(&sm.Ks[0][0], DK + 4, 16 * sj + li, k0, qd));
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int i = i0 + u, j = j0 + w;
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * si + 4 * qd + r, j = 16 * sj + li;
                 if (!isg) {
-                    sm.M1[i][j] = acc[u][w];
+                    sm.M1[i][j] = acc[r];
                 } else if (j < i) {
-                    sm.M2[i][j] = acc[u][w];
-                    sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * acc[u][w];
+                    sm.M2[i][j] = acc[r];
+                    sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * acc[r];
                 }
             }
+        }
     }
     __syncthreads();
 
@@ -361,28 +323,30 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r): 4 rows x 4 columns;
     // weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
     float *qtc = qt + ((size_t)bh * N + c) * C * DK;
-    for (int b = tid; b < CB * (DK / 4); b += NT) {
-        const int i0 = 4 * (b / (DK / 4)), d0 = 4 * (b % (DK / 4));
-        float acc[4][4] = {};
-        for (int r = 0; r <= i0 + 3; ++r) {
-            const float4 w = ld4(&sm.QW[r][d0]);
-            const float wr[4] = {w.x, w.y, w.z, w.w};
+    {
+        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
+        constexpr int NWV = NT / 64, TB = C / 16, TD = DK / 16;
+        for (int b = wv; b < TB * TD; b += NWV) {
+            const int si = b / TD, sd = b % TD;
+            floatx4 acc = zero4();
+            const int i = 16 * si + li;   // this lane's row of the A operand
+            for (int r0 = 0; r0 <= 16 * si; r0 += 16) {
+                floatx4 af = lds_frag(&sm.M1[0][0], C + 4, i, r0, qd), bf;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float sv = r <= i0 + u ? sm.M1[i0 + u][r] : 0.f;
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    acc[u][x] += sv * wr[x];
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r0 + 4 * qd + e;
+                    if (r > i)
+                        af[e] = 0.f;   // S is used on and below the diagonal
+                    bf[e] = sm.QW[r][16 * sd + li];
+                }
+                mma_unit(acc, af, bf);
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u;
-            const float4 qv = i < valid ? ld4t(q + (row0 + i) * DK + d0) : z4;
-            const float g = __expf(sm.Aloc[i]);
-            *reinterpret_cast<float4 *>(qtc + (size_t)i * DK + d0) =
-                make_float4(g * (qv.x - acc[u][0]), g * (qv.y - acc[u][1]), g * (qv.z - acc[u][2]),
-                            g * (qv.w - acc[u][3]));
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * si + 4 * qd + rr, d = 16 * sd + li;
+                const float qv = row < valid ? to_f32(q[(row0 + row) * DK + d]) : 0.f;
+                qtc[(size_t)row * DK + d] = __expf(sm.Aloc[row]) * (qv - acc[rr]);
+            }
         }
     }
     for (int e = tid; e < C * C; e += NT) {
@@ -392,27 +356,26 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     }
     __syncthreads();
 
-    // ---- in-chunk output O = A' V: 4 rows x 4 columns ----
-    for (int b = tid; b < CB * (DV / 4); b += NT) {
-        const int i0 = 4 * (b / (DV / 4)), c0 = 4 * (b % (DV / 4));
-        float acc[4][4] = {};
-        for (int j = 0; j <= i0 + 3; ++j) {
-            const float4 vv = ld4(&sm.Vs[j][c0]);
-            const float vr[4] = {vv.x, vv.y, vv.z, vv.w};
+    // ---- in-chunk output O = A' V: 16 x 16 tiles on fp32 MFMA ----
+    {
+        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
+        constexpr int NWV = NT / 64, TB = C / 16, TV = DV / 16;
+        for (int b = wv; b < TB * TV; b += NWV) {
+            const int si = b / TV, sc = b % TV;
+            floatx4 acc = zero4();
+            for (int j0 = 0; j0 <= 16 * si; j0 += 16) {   // A' is zero above the diagonal
+                floatx4 bf;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float av = sm.M3[i0 + u][j];   // zero above the diagonal
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    acc[u][x] += av * vr[x];
+                for (int e = 0; e < 4; ++e)
+                    bf[e] = sm.Vs[j0 + 4 * qd + e][16 * sc + li];
+                mma_unit(acc, lds_frag(&sm.M3[0][0], C + 4, 16 * si + li, j0, qd), bf);
             }
-        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = i0 + u;
-            if (i < valid)
-                *reinterpret_cast<float4 *>(out + (row0 + i) * DV + c0) =
-                    make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * si + 4 * qd + r;
+                if (i < valid)
+                    out[(row0 + i) * DV + 16 * sc + li] = acc[r];
+            }
         }
     }
 
@@ -427,32 +390,38 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     // ---- level-0 tree entries of this chunk: Phi^T = gamma_end (I - K^T W), D^T = K^T diag(wend) U ----
     const size_t blk = (size_t)bh * NBT + c;
     float *P = Phit + blk * DK * DK;
-    const float gend = __expf(sm.Aloc[C - 1]);
-    for (int b = tid; b < (DK / 4) * (DK / 4); b += NT) {
-        const int k0 = 4 * (b / (DK / 4)), n0 = 4 * (b % (DK / 4));   // Phi^T[k][n] = Phi[n][k]
-        float acc[4][4] = {};
-        blk_atb<C, DK + 4, DK + 4>(sm.Ks, sm.QW, nullptr, k0, n0, acc);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            float r4[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                r4[w] = gend * ((k0 + u == n0 + w ? 1.f : 0.f) - acc[u][w]);
-            *reinterpret_cast<float4 *>(P + (size_t)(k0 + u) * DK + n0) = make_float4(r4[0], r4[1], r4[2], r4[3]);
-        }
-    }
     float *D = Dt + blk * DK * DV;
-    for (int b = tid; b < (DK / 4) * (DV / 4); b += NT) {
-        const int d0 = 4 * (b / (DV / 4)), c0 = 4 * (b % (DV / 4));   // D^T[d][c] = H[c][d]
-        float acc[4][4] = {};
-        if constexpr (G::SEPU)
-            blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Us, sm.wend, d0, c0, acc);
-        else
-            blk_atb<C, DK + 4, DV + 4>(sm.Ks, sm.Vs, sm.wend, d0, c0, acc);
+    const float gend = __expf(sm.Aloc[C - 1]);
+    {
+        // Phi^T[k][n] = gend (delta - sum_r K[r][k] W[r][n]);  D^T[d][c] = sum_s wend[s] K[s][d] U[s][c]
+        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
+        constexpr int NWV = NT / 64, TK = DK / 16, TV = DV / 16;
+        const float (*U)[DV + 4] = G::SEPU ? sm.Us : sm.Vs;
+        for (int b = wv; b < TK * TK + TK * TV; b += NWV) {
+            const bool isd = b >= TK * TK;
+            const int bb = isd ? b - TK * TK : b;
+            const int sk = isd ? bb / TV : bb / TK, sn = isd ? bb % TV : bb % TK;
+            floatx4 acc = zero4();
+#pragma unroll 4
+            for (int r0 = 0; r0 < C; r0 += 16) {
+                floatx4 af, bf;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<float4 *>(D + (size_t)(d0 + u) * DV + c0) =
-                make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+                for (int e = 0; e < 4; ++e) {
+                    const int r = r0 + 4 * qd + e;
+                    af[e] = isd ? sm.wend[r] * sm.Ks[r][16 * sk + li] : sm.Ks[r][16 * sk + li];
+                    bf[e] = isd ? U[r][16 * sn + li] : sm.QW[r][16 * sn + li];
+                }
+                mma_unit(acc, af, bf);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = 16 * sk + 4 * qd + rr, col = 16 * sn + li;
+                if (isd)
+                    D[(size_t)row * DV + col] = acc[rr];
+                else
+                    P[(size_t)row * DK + col] = gend * ((row == col ? 1.f : 0.f) - acc[rr]);
+            }
+        }
     }
 }
 
