@@ -401,6 +401,8 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
             const bool isd = b >= TK * TK;
             const int bb = isd ? b - TK * TK : b;
             const int sk = isd ? bb / TV : bb / TK, sn = isd ? bb % TV : bb % TK;
+            // the tile is formed transposed (rows n, columns k) so that each
+            // lane holds four consecutive columns of a stored row: one 16-byte store
             floatx4 acc = zero4();
 #pragma unroll 4
             for (int r0 = 0; r0 < C; r0 += 16) {
@@ -408,18 +410,21 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = r0 + 4 * qd + e;
-                    af[e] = isd ? sm.wend[r] * sm.Ks[r][16 * sk + li] : sm.Ks[r][16 * sk + li];
-                    bf[e] = isd ? U[r][16 * sn + li] : sm.QW[r][16 * sn + li];
+                    af[e] = isd ? U[r][16 * sn + li] : sm.QW[r][16 * sn + li];
+                    bf[e] = isd ? sm.wend[r] * sm.Ks[r][16 * sk + li] : sm.Ks[r][16 * sk + li];
                 }
                 mma_unit(acc, af, bf);
             }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = 16 * sk + 4 * qd + rr, col = 16 * sn + li;
-                if (isd)
-                    D[(size_t)row * DV + col] = acc[rr];
-                else
-                    P[(size_t)row * DK + col] = gend * ((row == col ? 1.f : 0.f) - acc[rr]);
+            const int row = 16 * sk + li, col = 16 * sn + 4 * qd;   // acc[rr]: (row, col + rr)
+            if (isd) {
+                *reinterpret_cast<float4 *>(D + (size_t)row * DV + col) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else {
+                float4 x;
+                x.x = gend * ((row == col ? 1.f : 0.f) - acc[0]);
+                x.y = gend * ((row == col + 1 ? 1.f : 0.f) - acc[1]);
+                x.z = gend * ((row == col + 2 ? 1.f : 0.f) - acc[2]);
+                x.w = gend * ((row == col + 3 ? 1.f : 0.f) - acc[3]);
+                *reinterpret_cast<float4 *>(P + (size_t)row * DK + col) = x;
             }
         }
     }
