@@ -119,13 +119,16 @@ __device__ __forceinline__ void gdn_solve_w(SM &sm, int d)
     constexpr int C = G::C;
     for (int ib = 0; ib < C; ib += 4) {
         float r0 = sm.Ks[ib][d], r1 = sm.Ks[ib + 1][d], r2 = sm.Ks[ib + 2][d], r3 = sm.Ks[ib + 3][d];
-#pragma unroll 4
-        for (int j = 0; j < ib; ++j) {
-            const float w = sm.QW[j][d];
-            r0 -= sm.M2[ib][j] * w;
-            r1 -= sm.M2[ib + 1][j] * w;
-            r2 -= sm.M2[ib + 2][j] * w;
-            r3 -= sm.M2[ib + 3][j] * w;
+        // four earlier rows at a time: their k_i.k_j as one 16-byte read per row of the block
+#pragma unroll 2
+        for (int j = 0; j < ib; j += 4) {
+            const float w0 = sm.QW[j][d], w1 = sm.QW[j + 1][d], w2 = sm.QW[j + 2][d], w3 = sm.QW[j + 3][d];
+            const float4 m0 = ld4(&sm.M2[ib][j]), m1 = ld4(&sm.M2[ib + 1][j]);
+            const float4 m2 = ld4(&sm.M2[ib + 2][j]), m3 = ld4(&sm.M2[ib + 3][j]);
+            r0 -= m0.x * w0 + m0.y * w1 + m0.z * w2 + m0.w * w3;
+            r1 -= m1.x * w0 + m1.y * w1 + m1.z * w2 + m1.w * w3;
+            r2 -= m2.x * w0 + m2.y * w1 + m2.z * w2 + m2.w * w3;
+            r3 -= m3.x * w0 + m3.y * w1 + m3.z * w2 + m3.w * w3;
         }
         const float w0 = sm.beta[ib] * r0;
         const float w1 = sm.beta[ib + 1] * (r1 - sm.M2[ib + 1][ib] * w0);
@@ -184,8 +187,17 @@ __device__ __forceinline__ void gdn_solve_z(SM &sm, int i)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             y[k] = jb + k <= i ? sm.M1[i][jb + k] * __expf(ai - sm.Aloc[jb + k]) : 0.f;
-#pragma unroll 4
-        for (int r = jb + 4; r <= i; ++r) {
+        int r = jb + 4;
+        // four later columns at a time while they are all on or left of the diagonal
+        for (; r + 3 <= i; r += 4) {
+            const float4 z = ld4(&sm.M3[i][r]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 x = ld4(&sm.M2[jb + k][r]);
+                y[k] -= z.x * x.x + z.y * x.y + z.z * x.z + z.w * x.w;
+            }
+        }
+        for (; r <= i; ++r) {
             const float z = sm.M3[i][r];
             y[0] -= z * sm.M2[jb][r];
             y[1] -= z * sm.M2[jb + 1][r];
