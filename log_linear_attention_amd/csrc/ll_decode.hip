@@ -68,6 +68,80 @@ __device__ __forceinline__ void decode_slot(const float4 *x, float4 *M, float *p
     }
 }
 
+// Slots a step at position t reads: slot 0 and one per set bit of t - 1
+// (none for t = 0 or a position the stack cannot hold).
+__device__ __forceinline__ int decode_occ(int64_t t, int Lcap)
+{
+    if (t <= 0 || t >= ((int64_t)1 << (Lcap - 1)))
+        return 0;
+    return 1 + __popcll((unsigned long long)(t - 1));
+}
+
+// The (sequence, head) this workgroup serves.  The work of a step grows with
+// the slots a sequence reads (1 to Lcap), and the workgroups of one launch
+// are spread over the CUs in rounds of 256, workgroup b landing beside
+// b + 256, b + 512, ...  The sequences are ranked by slot count (heaviest
+// first, ties by index) and dealt out in a snake over the rounds (round r
+// runs backwards when r is odd), so that each CU gets heavy and light
+// sequences alike.  All threads of the workgroup must call this; it returns
+// the same value to each.
+__device__ int decode_item(const int64_t *__restrict__ pos, int S, int H, int Lcap, int *hist, int *sel)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nwv = blockDim.x >> 6;
+    const int b = blockIdx.x, SH = S * H;
+    const int r = b >> 8, c = b & 255;
+    const int rho = ((r & 1) && r * 256 + 255 < SH) ? r * 256 + 255 - c : b;
+    const int target = rho / H;   // rank of the sequence wanted
+    if (tid == 0)
+        *sel = target;   // replaced below; the ranks are a permutation of the sequences
+    // histogram of slot counts: lane l of each wave counts count l
+    int cnt = 0;
+    for (int g = wv; g * 64 < S; g += nwv) {
+        const int sq = g * 64 + lane;
+        const int o = sq < S ? decode_occ(pos[sq], Lcap) : -1;
+        for (int k = 0; k <= Lcap; ++k) {
+            const unsigned long long m = __ballot(o == k);
+            if (lane == k)
+                cnt += __popcll(m);
+        }
+    }
+    if (lane <= Lcap)
+        hist[wv * 33 + lane] = cnt;
+    __syncthreads();
+    if (tid < 64) {
+        // bucket of the target rank (heaviest bucket first), then the index
+        // of the sequence within it
+        int start = 0, cstar = 0, jrem = 0;
+        for (int k = Lcap; k >= 0; --k) {
+            int n = 0;
+            for (int w = 0; w < nwv; ++w)
+                n += hist[w * 33 + k];
+            if (target < start + n) {
+                cstar = k;
+                jrem = target - start;
+                break;
+            }
+            start += n;
+        }
+        for (int g = 0; g * 64 < S; ++g) {
+            const int sq = g * 64 + lane;
+            const int o = sq < S ? decode_occ(pos[sq], Lcap) : -1;
+            unsigned long long m = __ballot(o == cstar);
+            const int n = __popcll(m);
+            if (jrem < n) {
+                for (int q = 0; q < jrem; ++q)
+                    m &= m - 1;
+                if (lane == 0)
+                    *sel = g * 64 + __ffsll((long long)m) - 1;
+                break;
+            }
+            jrem -= n;
+        }
+    }
+    __syncthreads();
+    return *sel * H + rho % H;
+}
+
 template <class D>
 __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict__ q,
                                                  const typename D::T *__restrict__ k,
@@ -85,9 +159,11 @@ __global__ __launch_bounds__(256) void ll_decode(const typename D::T *__restrict
     __shared__ int slots[kMaxLevels];
     __shared__ int nslots;
     __shared__ float qk_s;
+    __shared__ int hist[4 * 33];
+    __shared__ int sel;
 
     const int tid = threadIdx.x;
-    const int sh = blockIdx.x;          // sequence * H + head
+    const int sh = decode_item(pos, gridDim.x / H, H, Lcap, hist, &sel);   // sequence * H + head
     const int s = sh / H;
     const int64_t t = pos[s];
     T *o = out + (size_t)sh * DV;
