@@ -176,3 +176,37 @@ def test_ragged_backward(dtype, chunk):
             if tail.size:
                 bound = 1e-5 * float(np.abs(r).max()) if n == "da" else 0.0
                 assert float(np.abs(tail).max()) <= bound, (b, n, float(np.abs(tail).max()))
+
+
+def test_ragged_prefill_with_shared_qk_heads():
+    """Prompts of different lengths whose heads share one q/k head: each
+    sequence's stack against the oracle on that sequence alone, with its k
+    repeated over the heads."""
+    T, lens, H, Lcap = 500, [500, 250, 1], 4, 17
+    cfg = synth.FwdConfig("ragged_grouped", len(lens), H, T, 64, 32, 32, "f32", 0.05, 8400)
+    announce(f"ragged prefill, 1 q/k head for {H} heads, lens={lens}")
+    draw, pad = _padded(cfg, T, lens)
+    for n in ("q", "k"):
+        draw[n] = draw[n][:, :1].contiguous()
+        pad[n] = pad[n][:, :1].contiguous()
+    d = to_dev(pad)
+    B = len(lens)
+    state = torch.full((B, H, Lcap, 64, 32), float("nan"), device="cuda")
+    logscale = torch.full((B, H, Lcap), float("nan"), device="cuda")
+    out = ll.prefill(d["q"], d["k"], d["v"], d["a"], d["lam"], state, logscale, chunk=32,
+                     lengths=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    st, ls = f64(state), f64(logscale)
+    for b, Tb in enumerate(lens):
+        kb = draw["k"][b:b + 1, :, :Tb].repeat_interleave(H, dim=1)
+        ref, occ = oracle.prefill_stack(kb, draw["v"][b:b + 1, :, :Tb], draw["a"][b:b + 1, :, :Tb], Lcap)
+        for l in range(Lcap):
+            if occ[l]:
+                got = np.exp(ls[b, :, l])[:, None, None] * st[b, :, l]
+                e = _err(got, ref[0, :, l])
+                assert e <= TOL["f32"], (b, l, e)
+        s = _seq(pad, b, Tb)
+        ref_o = oracle.fwd_grouped(s["q"], s["k"], s["v"], s["a"], s["lam"])
+        e = _err(f64(out[b:b + 1, :, :Tb]), ref_o)
+        print(f"seq {b} (len {Tb}): out rel_l2 {e:.3e}")
+        assert e <= TOL["f32"]
