@@ -16,14 +16,18 @@
 //    for a zero incoming state), u solves X u = diag(beta) v where
 //    X = I + strictly-lower(beta_i (gamma_i/gamma_j) k_i.k_j); hence
 //    A = ((Q K^T) ⊙ Gamma ⊙ causal) X^{-1} diag(beta) for the chunk's pairs.
-//    Z = Y X^{-1} is formed row by row, then multiplied by the in-chunk
-//    levels' lambda.  The three triangular solves (W below, Z, U) run side by
-//    side, one column or row per thread.
+//    Z = Y X^{-1} is multiplied by the in-chunk levels' lambda.
 //  - Product of the chunk's transitions.  Without the scalar decays the
 //    product of (I - beta_r k_r k_r^T) over r = 0..i is I - sum_{r<=i} w_r k_r^T
-//    with w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) (a compact WY form), so
+//    with w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j) (a compact WY form),
+//    i.e. X0 W = diag(beta) K with X0 = I + strictly-lower(beta_i k_i.k_j), so
 //    Phi_c = M_0 .. M_{C-1} = gamma_{C-1} (I - W^T K) and the query carried to
 //    the chunk start is qt_i = M_0 .. M_i q_i = gamma_i (q_i - sum_{r<=i} (q_i.k_r) w_r).
+//  - X = Gamma X0 Gamma^{-1}, so one inverse serves the three systems:
+//    T = X0^{-1} is formed by 16 x 16 blocks (diagonal blocks by
+//    substitution, the others from block rows of X0 T = I on MFMA), then
+//    W = T diag(beta) K, U = X^{-1} diag(beta) V and Z are MFMA products,
+//    with X^{-1}[i][j] = (gamma_i/gamma_j) T[i][j].
 //  - Chunk state (keys of the chunk, at its end): H = sum_s (gamma_end/gamma_s) u_s k_s^T.
 //  - Tree over chunks (left child L, right child R): D = D_L Phi_R + D_R,
 //    Phi = Phi_L Phi_R.  Stored transposed (Phi^T [dk][dk], D^T [dk][dv]) so
@@ -34,8 +38,8 @@
 //    through the finer buckets' blocks: qt^(m') = Phi(block m) qt^(m) for
 //    the next set bit m' > m.
 //
-// All arithmetic is float32 FMA; decays enter only as exp of non-positive
-// differences for a <= 0.
+// All arithmetic is float32 (FMA and fp32 MFMA); decays enter only as exp
+// of non-positive differences for a <= 0.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -55,11 +59,11 @@ struct Gdn {
     static constexpr int WNT = C * (DK < DV ? DK : DV) / 4 < 512 ? C * (DK < DV ? DK : DV) / 4 : 512;
     static constexpr int LOGC = C == 32 ? 5 : 6;
     static_assert(C * DV % NT == 0 && C * DK % NT == 0 && NT % DV == 0 && NT % DK == 0, "thread layout");
-    // The three triangular solves (W, Z, U) run side by side, one column or
-    // row per thread, when threads and LDS allow a separate U buffer.
-    static constexpr int SOLVE_LDS = 4 * (C * (DK + 4) * 2 + C * (DV + 4) * 2 + 3 * C * (C + 4) + C * (LOGC + 4));
-    static constexpr bool SEPU = DK + C + DV <= CNT && SOLVE_LDS <= 160 * 1024;
-    static_assert(DK + C <= CNT, "W and Z solves side by side");
+    // The pseudo-values U get a buffer of their own (and are formed beside W
+    // and Z) when the chunk kernel's LDS allows one.
+    static constexpr int LDS_WITH_U = 4 * (C * (DK + 4) * 2 + C * (DV + 4) * 2 + 3 * C * (C + 4) + C * (LOGC + 4));
+    static constexpr bool SEPU = LDS_WITH_U <= 160 * 1024;
+    static_assert(C / 16 <= CNT / 64, "one wave per off-diagonal block of the inverse");
 };
 
 template <class G>
@@ -69,8 +73,8 @@ struct GdnChunkSmem {
     __attribute__((aligned(16))) float Ks[G::C][G::DK + 4];
     __attribute__((aligned(16))) float Vs[G::C][G::DV + 4];   // V, then the pseudo-values U
     __attribute__((aligned(16))) float M1[G::C][G::C + 4];    // S = Q K^T
-    __attribute__((aligned(16))) float M2[G::C][G::C + 4];    // lower (i, j<i): k_i.k_j; upper (j, i), j<i: X[i][j]
-    __attribute__((aligned(16))) float M3[G::C][G::C + 4];    // Z, then the weighted A
+    __attribute__((aligned(16))) float M2[G::C][G::C + 4];    // X0 (lower) and blocks of the inverse (upper); then Z, the weighted A
+    __attribute__((aligned(16))) float M3[G::C][G::C + 4];    // T = X0^{-1} (lower)
     __attribute__((aligned(16))) float Us[G::SEPU ? G::C : 1][G::DV + 4];   // pseudo-values (when separate)
     float Aloc[G::C];
     float beta[G::C];
@@ -107,112 +111,28 @@ __device__ __forceinline__ void st4t(__bf16 *p, const float4 &x)
     *reinterpret_cast<bf16x4 *>(p) = y;
 }
 
-// The chunk's triangular solves, four rows (or columns) per step: the
-// earlier rows' terms for a block of four are summed together (each earlier
-// value loaded once for the four), then the 4 x 4 diagonal block is solved.
-
-// W (one column d of Q's storage): w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j),
-// with k_i.k_j in the lower triangle of M2.
+// U tile (si, sc) of U = X^{-1} diag(beta) V, with X^{-1}[i][j] =
+// (gamma_i / gamma_j) T[i][j] (T = X0^{-1} in M3, lower triangle), the decay
+// applied to each T element as it is loaded (the factor is exp of a
+// non-positive difference on and below the diagonal; zero above it).
 template <class G, class SM>
-__device__ __forceinline__ void gdn_solve_w(SM &sm, int d)
+__device__ __forceinline__ floatx4 gdn_u_tile(const SM &sm, int si, int sc, int li, int qd)
 {
     constexpr int C = G::C;
-    for (int ib = 0; ib < C; ib += 4) {
-        float r0 = sm.Ks[ib][d], r1 = sm.Ks[ib + 1][d], r2 = sm.Ks[ib + 2][d], r3 = sm.Ks[ib + 3][d];
-        // four earlier rows at a time: their k_i.k_j as one 16-byte read per row of the block
-#pragma unroll 2
-        for (int j = 0; j < ib; j += 4) {
-            const float w0 = sm.QW[j][d], w1 = sm.QW[j + 1][d], w2 = sm.QW[j + 2][d], w3 = sm.QW[j + 3][d];
-            const float4 m0 = ld4(&sm.M2[ib][j]), m1 = ld4(&sm.M2[ib + 1][j]);
-            const float4 m2 = ld4(&sm.M2[ib + 2][j]), m3 = ld4(&sm.M2[ib + 3][j]);
-            r0 -= m0.x * w0 + m0.y * w1 + m0.z * w2 + m0.w * w3;
-            r1 -= m1.x * w0 + m1.y * w1 + m1.z * w2 + m1.w * w3;
-            r2 -= m2.x * w0 + m2.y * w1 + m2.z * w2 + m2.w * w3;
-            r3 -= m3.x * w0 + m3.y * w1 + m3.z * w2 + m3.w * w3;
-        }
-        const float w0 = sm.beta[ib] * r0;
-        const float w1 = sm.beta[ib + 1] * (r1 - sm.M2[ib + 1][ib] * w0);
-        const float w2 = sm.beta[ib + 2] * (r2 - sm.M2[ib + 2][ib] * w0 - sm.M2[ib + 2][ib + 1] * w1);
-        const float w3 =
-            sm.beta[ib + 3] * (r3 - sm.M2[ib + 3][ib] * w0 - sm.M2[ib + 3][ib + 1] * w1 - sm.M2[ib + 3][ib + 2] * w2);
-        sm.QW[ib][d] = w0;
-        sm.QW[ib + 1][d] = w1;
-        sm.QW[ib + 2][d] = w2;
-        sm.QW[ib + 3][d] = w3;
-    }
-}
-
-// U (one column cc): u_i = beta_i v_i - sum_{j<i} X[i][j] u_j, X[i][j] in the
-// upper triangle of M2 at (j, i).  U may be V's own storage.
-template <class G, class SM, int LDV>
-__device__ __forceinline__ void gdn_solve_u(SM &sm, const float (*V)[LDV], float (*U)[LDV], int cc)
-{
-    constexpr int C = G::C;
-    for (int ib = 0; ib < C; ib += 4) {
-        float r0 = sm.beta[ib] * V[ib][cc], r1 = sm.beta[ib + 1] * V[ib + 1][cc];
-        float r2 = sm.beta[ib + 2] * V[ib + 2][cc], r3 = sm.beta[ib + 3] * V[ib + 3][cc];
-#pragma unroll 4
-        for (int j = 0; j < ib; ++j) {
-            const float u = U[j][cc];
-            const float4 x = ld4(&sm.M2[j][ib]);   // X[ib..ib+3][j]
-            r0 -= x.x * u;
-            r1 -= x.y * u;
-            r2 -= x.z * u;
-            r3 -= x.w * u;
-        }
-        const float u0 = r0;
-        const float u1 = r1 - sm.M2[ib][ib + 1] * u0;
-        const float u2 = r2 - sm.M2[ib][ib + 2] * u0 - sm.M2[ib + 1][ib + 2] * u1;
-        const float u3 = r3 - sm.M2[ib][ib + 3] * u0 - sm.M2[ib + 1][ib + 3] * u1 - sm.M2[ib + 2][ib + 3] * u2;
-        U[ib][cc] = u0;
-        U[ib + 1][cc] = u1;
-        U[ib + 2][cc] = u2;
-        U[ib + 3][cc] = u3;
-    }
-}
-
-// Z row i into M3: Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j] with
-// Y = S ⊙ Gamma (S in M1), columns from the right in blocks of four; zero
-// above the diagonal.
-template <class G, class SM>
-__device__ __forceinline__ void gdn_solve_z(SM &sm, int i)
-{
-    constexpr int C = G::C;
+    floatx4 acc = zero4();
+    const int i = 16 * si + li;   // this lane's row of the A operand
     const float ai = sm.Aloc[i];
-    const int top = i & ~3;
-    for (int j = top + 4; j < C; ++j)
-        sm.M3[i][j] = 0.f;
-    for (int jb = top; jb >= 0; jb -= 4) {
-        float y[4];
+    for (int j0 = 0; j0 <= 16 * si; j0 += 16) {
+        floatx4 af = lds_frag(&sm.M3[0][0], C + 4, i, j0, qd), bf;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            y[k] = jb + k <= i ? sm.M1[i][jb + k] * __expf(ai - sm.Aloc[jb + k]) : 0.f;
-        int r = jb + 4;
-        // four later columns at a time while they are all on or left of the diagonal
-        for (; r + 3 <= i; r += 4) {
-            const float4 z = ld4(&sm.M3[i][r]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 x = ld4(&sm.M2[jb + k][r]);
-                y[k] -= z.x * x.x + z.y * x.y + z.z * x.z + z.w * x.w;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + 4 * qd + e;
+            af[e] = j <= i ? af[e] * __expf(ai - sm.Aloc[j]) : 0.f;
+            bf[e] = sm.beta[j] * sm.Vs[j][16 * sc + li];
         }
-        for (; r <= i; ++r) {
-            const float z = sm.M3[i][r];
-            y[0] -= z * sm.M2[jb][r];
-            y[1] -= z * sm.M2[jb + 1][r];
-            y[2] -= z * sm.M2[jb + 2][r];
-            y[3] -= z * sm.M2[jb + 3][r];
-        }
-        const float z3 = jb + 3 <= i ? y[3] : 0.f;
-        const float z2 = jb + 2 <= i ? y[2] - z3 * sm.M2[jb + 2][jb + 3] : 0.f;
-        const float z1 = jb + 1 <= i ? y[1] - z2 * sm.M2[jb + 1][jb + 2] - z3 * sm.M2[jb + 1][jb + 3] : 0.f;
-        const float z0 = y[0] - z1 * sm.M2[jb][jb + 1] - z2 * sm.M2[jb][jb + 2] - z3 * sm.M2[jb][jb + 3];
-        sm.M3[i][jb] = z0;
-        sm.M3[i][jb + 1] = z1;
-        sm.M3[i][jb + 2] = z2;
-        sm.M3[i][jb + 3] = z3;
+        mma_unit(acc, af, bf);
     }
+    return acc;
 }
 
 template <class G>
@@ -288,11 +208,12 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     if (tid < C)
         sm.wend[tid] = __expf(sm.Aloc[C - 1] - sm.Aloc[tid]);
 
-    // ---- S = Q K^T, k_i.k_j and X[i][j] (j < i): 16 x 16 tiles on fp32 MFMA,
+    const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
+    constexpr int NWV = NT / 64, TB = C / 16;
+
+    // ---- S = Q K^T and X0[i][j] = beta_i k_i.k_j (j < i): 16 x 16 tiles on fp32 MFMA,
     // one tile per wave at a time (the strictly upper tiles of K K^T skipped) ----
     {
-        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
-        constexpr int NWV = NT / 64, TB = C / 16;
         for (int b = wv; b < 2 * TB * TB; b += NWV) {
             const bool isg = b >= TB * TB;
             const int bb = isg ? b - TB * TB : b;
@@ -307,28 +228,127 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * si + 4 * qd + r, j = 16 * sj + li;
-                if (!isg) {
+                if (!isg)
                     sm.M1[i][j] = acc[r];
-                } else if (j < i) {
-                    sm.M2[i][j] = acc[r];
-                    sm.M2[j][i] = sm.beta[i] * __expf(sm.Aloc[i] - sm.Aloc[j]) * acc[r];
-                }
+                else if (j < i)
+                    sm.M2[i][j] = sm.beta[i] * acc[r];
             }
         }
     }
     __syncthreads();
 
-    // ---- the triangular solves, side by side (one column or row per thread):
-    //  W (over Q's storage):  w_i = beta_i (k_i - sum_{j<i} (k_i.k_j) w_j)
-    //  Z = Y X^{-1}, Y = S ⊙ Gamma:  Z[i][j] = Y[i][j] - sum_{r=j+1..i} Z[i][r] X[r][j]
-    //  U (separate buffer):  u_i = beta_i v_i - sum_{j<i} X[i][j] u_j ----
-    if (tid < DK) {
-        gdn_solve_w<G>(sm, tid);
-    } else if (tid < DK + C) {
-        gdn_solve_z<G>(sm, tid - DK);
-    } else if constexpr (G::SEPU) {
-        if (tid < DK + C + DV)
-            gdn_solve_u<G, GdnChunkSmem<G>, DV + 4>(sm, sm.Vs, sm.Us, tid - DK - C);
+    // ---- T = X0^{-1} (unit lower triangular) into M3, by 16 x 16 blocks.
+    // Diagonal blocks by substitution, one column per thread:
+    //   T_bb[r][c] = delta_rc - sum_{m<r} X0_bb[r][m] T_bb[m][c] ----
+    if (tid < C) {
+        const int b0 = 16 * (tid >> 4), cc = tid & 15;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = r == cc ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m)
+                x -= sm.M2[b0 + r][b0 + m] * t[m];
+            t[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sm.M3[b0 + r][b0 + cc] = t[r];
+    }
+    __syncthreads();
+    // Blocks below the diagonal, one block distance dd = i - j at a time, one
+    // wave per block: T_ij = -T_ii R with R = sum_{m=j}^{i-1} X0_im T_mj (from
+    // block row i of X0 T = I).  R waits in M2's strictly upper block (j, i),
+    // which holds nothing else.
+    for (int dd = 1; dd < TB; ++dd) {
+        if (wv < TB - dd) {
+            const int j = wv, i = wv + dd;
+            floatx4 acc = zero4();
+            for (int m = j; m < i; ++m) {
+                floatx4 bf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    bf[e] = sm.M3[16 * m + 4 * qd + e][16 * j + li];
+                mma_unit(acc, lds_frag(&sm.M2[0][0], C + 4, 16 * i + li, 16 * m, qd), bf);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.M2[16 * j + 4 * qd + r][16 * i + li] = acc[r];
+        }
+        __syncthreads();
+        if (wv < TB - dd) {
+            const int j = wv, i = wv + dd;
+            floatx4 acc = zero4(), bf;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bf[e] = sm.M2[16 * j + 4 * qd + e][16 * i + li];
+            mma_unit(acc, lds_frag(&sm.M3[0][0], C + 4, 16 * i + li, 16 * i, qd), bf);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sm.M3[16 * i + 4 * qd + r][16 * j + li] = -acc[r];
+        }
+        __syncthreads();
+    }
+
+    // ---- products of T, side by side on fp32 MFMA (T's blocks above the
+    // diagonal are never read):
+    //  W = T diag(beta) K over Q's storage;
+    //  U = X^{-1} diag(beta) V into its own buffer (when there is one);
+    //  Z = Y X^{-1} into M2, Z[i][j] = (gamma_i / gamma_j) sum_{j<=r<=i} S[i][r] T[r][j]
+    //  (the decays of Y = S ⊙ Gamma and of X^{-1} meet in one factor per element) ----
+    {
+        constexpr int TD = DK / 16, TV = DV / 16;
+        constexpr int NWT = TB * TD, NUT = G::SEPU ? TB * TV : 0, NZT = TB * (TB + 1) / 2;
+        for (int b = wv; b < NWT + NUT + NZT; b += NWV) {
+            if (b < NWT) {
+                const int si = b / TD, sd = b % TD;
+                floatx4 acc = zero4();
+                for (int j0 = 0; j0 <= 16 * si; j0 += 16) {
+                    floatx4 bf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = j0 + 4 * qd + e;
+                        bf[e] = sm.beta[r] * sm.Ks[r][16 * sd + li];
+                    }
+                    mma_unit(acc, lds_frag(&sm.M3[0][0], C + 4, 16 * si + li, j0, qd), bf);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.QW[16 * si + 4 * qd + r][16 * sd + li] = acc[r];
+            } else if (b < NWT + NUT) {
+                if constexpr (G::SEPU) {
+                    const int si = (b - NWT) / TV, sc = (b - NWT) % TV;
+                    const floatx4 acc = gdn_u_tile<G>(sm, si, sc, li, qd);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sm.Us[16 * si + 4 * qd + r][16 * sc + li] = acc[r];
+                }
+            } else {
+                int sj = b - NWT - NUT, si = 0;   // lower tile (si, sj), sj <= si
+                while (sj > si) {
+                    sj -= si + 1;
+                    ++si;
+                }
+                const int i = 16 * si + li;
+                floatx4 acc = zero4();
+                for (int rb = sj; rb <= si; ++rb) {
+                    floatx4 af = lds_frag(&sm.M1[0][0], C + 4, i, 16 * rb, qd), bf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rb + 4 * qd + e;
+                        if (r > i)
+                            af[e] = 0.f;   // S is used on and below the diagonal
+                        bf[e] = sm.M3[r][16 * sj + li];
+                    }
+                    mma_unit(acc, af, bf);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ii = 16 * si + 4 * qd + r, jj = 16 * sj + li;
+                    sm.M2[ii][jj] = jj <= ii ? __expf(sm.Aloc[ii] - sm.Aloc[jj]) * acc[r] : 0.f;
+                }
+            }
+        }
     }
     __syncthreads();
 
@@ -336,8 +356,7 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     // weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
     float *qtc = qt + ((size_t)bh * N + c) * C * DK;
     {
-        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
-        constexpr int NWV = NT / 64, TB = C / 16, TD = DK / 16;
+        constexpr int TD = DK / 16;
         for (int b = wv; b < TB * TD; b += NWV) {
             const int si = b / TD, sd = b % TD;
             floatx4 acc = zero4();
@@ -364,14 +383,13 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     for (int e = tid; e < C * C; e += NT) {
         const int i = e / C, j = e % C;
         if (j <= i)
-            sm.M3[i][j] *= sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.beta[j];
+            sm.M2[i][j] *= sm.lam[i][bitlen((unsigned)(i ^ j))] * sm.beta[j];
     }
     __syncthreads();
 
     // ---- in-chunk output O = A' V: 16 x 16 tiles on fp32 MFMA ----
     {
-        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
-        constexpr int NWV = NT / 64, TB = C / 16, TV = DV / 16;
+        constexpr int TV = DV / 16;
         for (int b = wv; b < TB * TV; b += NWV) {
             const int si = b / TV, sc = b % TV;
             floatx4 acc = zero4();
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     bf[e] = sm.Vs[j0 + 4 * qd + e][16 * sc + li];
-                mma_unit(acc, lds_frag(&sm.M3[0][0], C + 4, 16 * si + li, j0, qd), bf);
+                mma_unit(acc, lds_frag(&sm.M2[0][0], C + 4, 16 * si + li, j0, qd), bf);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -391,11 +409,27 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
         }
     }
 
-    // ---- pseudo-values in place of V when they have no buffer of their own ----
+    // ---- pseudo-values in place of V when they have no buffer of their own:
+    // every U tile held in registers until all reads of V are done ----
     if constexpr (!G::SEPU) {
+        constexpr int TV = DV / 16, NUT = TB * TV, PER = (NUT + NWV - 1) / NWV;
+        floatx4 ut[PER];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int b = wv + p * NWV;
+            if (b < NUT)
+                ut[p] = gdn_u_tile<G>(sm, b / TV, b % TV, li, qd);
+        }
         __syncthreads();
-        if (tid < DV)
-            gdn_solve_u<G, GdnChunkSmem<G>, DV + 4>(sm, sm.Vs, sm.Vs, tid);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int b = wv + p * NWV;
+            if (b < NUT) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.Vs[16 * (b / TV) + 4 * qd + r][16 * (b % TV) + li] = ut[p][r];
+            }
+        }
     }
     __syncthreads();
 
@@ -406,8 +440,7 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     const float gend = __expf(sm.Aloc[C - 1]);
     {
         // Phi^T[k][n] = gend (delta - sum_r K[r][k] W[r][n]);  D^T[d][c] = sum_s wend[s] K[s][d] U[s][c]
-        const int lane = tid & 63, wv = tid >> 6, qd = lane >> 4, li = lane & 15;
-        constexpr int NWV = NT / 64, TK = DK / 16, TV = DV / 16;
+        constexpr int TK = DK / 16, TV = DV / 16;
         const float (*U)[DV + 4] = G::SEPU ? sm.Us : sm.Vs;
         for (int b = wv; b < TK * TK + TK * TV; b += NWV) {
             const bool isd = b >= TK * TK;

@@ -53,6 +53,37 @@ def test_gdn_head_dims(dk, dv):
     _case(cfg, 32)
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (32, 64)])
+def test_gdn_head_dims_chunk64(dk, dv):
+    """Chunks of 64: (128, 128) leaves no LDS for a separate pseudo-value
+    buffer, so U is formed in registers and written over V."""
+    cfg = synth.FwdConfig("gdn_dims64", 1, 2, 500, dk, dv, 64, "f32", 0.05, 9150 + dk + dv)
+    announce(f"gdn f32 dk={dk} dv={dv} chunk=64")
+    _case(cfg, 64)
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_gdn_near_duplicate_keys(chunk):
+    """Keys close to one direction, beta in [0.9, 1) and strong decay: the
+    chunk's triangular systems far from the identity (large k_i.k_j), the
+    transitions close to projections."""
+    cfg = synth.FwdConfig("gdn_dup", 1, 2, 300, 64, 32, chunk, "f32", 1.0, 9160 + chunk)
+    announce(f"gdn f32 near-duplicate keys chunk={chunk}")
+    inp = synth.make_gdn_inputs(cfg)
+    rng = np.random.Generator(np.random.PCG64(9170 + chunk))
+    k = inp["k"].double()
+    k = k[:, :, :1] + 0.2 * k
+    inp["k"] = (k / k.norm(dim=-1, keepdim=True)).float().contiguous()
+    inp["beta"] = torch.from_numpy(rng.uniform(0.9, 1.0, inp["beta"].shape).astype(np.float32))
+    out = _run(inp, chunk)
+    ref = gdn.gdn_fwd(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], inp["lam"])
+    got = f64(out)
+    assert np.all(np.isfinite(got))
+    e = max(rel_l2(got, ref), per_head_max(got, ref))
+    print(f"rel_l2 {e:.3e}")
+    assert e <= TOL["f32"], e
+
+
 def test_gdn_many_levels():
     """2600 tokens in chunks of 32: 82 chunks, chunk-level buckets up to
     level 7 of the tree, with a ragged tail."""
