@@ -220,11 +220,18 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
             const int si = bb / TB, sj = bb % TB;
             if (isg && sj > si)
                 continue;
-            floatx4 acc = zero4();
+            // two independent accumulators over alternate 16-wide units
+            floatx4 acc = zero4(), acc1 = zero4();
             const float *A = isg ? &sm.Ks[0][0] : &sm.QW[0][0];
-#pragma unroll 4
-            for (int k0 = 0; k0 < DK; k0 += 16)
+#pragma unroll 2
+            for (int k0 = 0; k0 < DK; k0 += 32) {
                 mma_unit(acc, lds_frag(A, DK + 4, 16 * si + li, k0, qd), lds_frag(&sm.Ks[0][0], DK + 4, 16 * sj + li, k0, qd));
+                mma_unit(acc1, lds_frag(A, DK + 4, 16 * si + li, k0 + 16, qd),
+                         lds_frag(&sm.Ks[0][0], DK + 4, 16 * sj + li, k0 + 16, qd));
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] += acc1[r];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * si + 4 * qd + r, j = 16 * sj + li;
@@ -439,38 +446,55 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     float *D = Dt + blk * DK * DV;
     const float gend = __expf(sm.Aloc[C - 1]);
     {
-        // Phi^T[k][n] = gend (delta - sum_r K[r][k] W[r][n]);  D^T[d][c] = sum_s wend[s] K[s][d] U[s][c]
-        constexpr int TK = DK / 16, TV = DV / 16;
+        // Phi^T[k][n] = gend (delta - sum_r K[r][k] W[r][n]);  D^T[d][c] = sum_s wend[s] K[s][d] U[s][c].
+        // One 32 x 32 block (2 x 2 tiles) per wave at a time: each operand
+        // fragment serves two tiles, and the four accumulators are independent.
+        constexpr int TK = DK / 16, TV = DV / 16, NPB = (TK / 2) * (TK / 2), NDB = (TK / 2) * (TV / 2);
+        static_assert(TK % 2 == 0 && TV % 2 == 0, "2 x 2 tiles");
         const float (*U)[DV + 4] = G::SEPU ? sm.Us : sm.Vs;
-        for (int b = wv; b < TK * TK + TK * TV; b += NWV) {
-            const bool isd = b >= TK * TK;
-            const int bb = isd ? b - TK * TK : b;
-            const int sk = isd ? bb / TV : bb / TK, sn = isd ? bb % TV : bb % TK;
-            // the tile is formed transposed (rows n, columns k) so that each
-            // lane holds four consecutive columns of a stored row: one 16-byte store
-            floatx4 acc = zero4();
-#pragma unroll 4
+        for (int b = wv; b < NPB + NDB; b += NWV) {
+            const bool isd = b >= NPB;
+            const int bb = isd ? b - NPB : b, tn = isd ? TV / 2 : TK / 2;
+            const int sk = 2 * (bb / tn), sn = 2 * (bb % tn);
+            // tiles formed transposed (rows k, columns n) so that each lane
+            // holds four consecutive columns of a stored row: one 16-byte store
+            floatx4 acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+#pragma unroll 2
             for (int r0 = 0; r0 < C; r0 += 16) {
-                floatx4 af, bf;
+                floatx4 af[2], bf[2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = r0 + 4 * qd + e;
-                    af[e] = isd ? U[r][16 * sn + li] : sm.QW[r][16 * sn + li];
-                    bf[e] = isd ? sm.wend[r] * sm.Ks[r][16 * sk + li] : sm.Ks[r][16 * sk + li];
+                    const float wk = isd ? sm.wend[r] : 1.f;
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        af[x][e] = isd ? U[r][16 * (sn + x) + li] : sm.QW[r][16 * (sn + x) + li];
+                        bf[x][e] = wk * sm.Ks[r][16 * (sk + x) + li];
+                    }
                 }
-                mma_unit(acc, af, bf);
+#pragma unroll
+                for (int y = 0; y < 2; ++y)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+                        mma_unit(acc[y][x], af[x], bf[y]);
             }
-            const int row = 16 * sk + li, col = 16 * sn + 4 * qd;   // acc[rr]: (row, col + rr)
-            if (isd) {
-                *reinterpret_cast<float4 *>(D + (size_t)row * DV + col) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            } else {
-                float4 x;
-                x.x = gend * ((row == col ? 1.f : 0.f) - acc[0]);
-                x.y = gend * ((row == col + 1 ? 1.f : 0.f) - acc[1]);
-                x.z = gend * ((row == col + 2 ? 1.f : 0.f) - acc[2]);
-                x.w = gend * ((row == col + 3 ? 1.f : 0.f) - acc[3]);
-                *reinterpret_cast<float4 *>(P + (size_t)row * DK + col) = x;
-            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y)
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int row = 16 * (sk + y) + li, col = 16 * (sn + x) + 4 * qd;   // acc[rr]: (row, col + rr)
+                    const floatx4 &v = acc[y][x];
+                    if (isd) {
+                        *reinterpret_cast<float4 *>(D + (size_t)row * DV + col) = make_float4(v[0], v[1], v[2], v[3]);
+                    } else {
+                        float4 o;
+                        o.x = gend * ((row == col ? 1.f : 0.f) - v[0]);
+                        o.y = gend * ((row == col + 1 ? 1.f : 0.f) - v[1]);
+                        o.z = gend * ((row == col + 2 ? 1.f : 0.f) - v[2]);
+                        o.w = gend * ((row == col + 3 ? 1.f : 0.f) - v[3]);
+                        *reinterpret_cast<float4 *>(P + (size_t)row * DK + col) = o;
+                    }
+                }
         }
     }
 }
