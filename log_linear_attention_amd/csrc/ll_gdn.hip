@@ -503,8 +503,9 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 // level p-1:  Phi^T = Phi_R^T Phi_L^T,  D^T = Phi_R^T D_L^T + D_R^T.
 // Output [DK rows] x [DK + DV columns] in 64 x 64 tiles (rows x columns;
 // DK < 64: DK rows) on fp32 MFMA, 16 x 16 subtiles spread over the four
-// waves; both operands staged through LDS one 16-wide contraction unit at a
-// time.
+// waves.  Both operands are staged through LDS 32 contraction rows at a
+// time with 16-byte loads; the next slice is loaded into registers before
+// the current one is multiplied, so its latency overlaps the MFMAs.
 template <class G>
 __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, float *__restrict__ Dt, int N, int NBT,
                                                    int p)
@@ -512,8 +513,10 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     constexpr int DK = G::DK, DV = G::DV, NC = DK + DV;
     constexpr int TS = DK < 64 ? DK : 64;            // tile edge (rows and columns)
     constexpr int TR = DK / TS, TN = (NC + TS - 1) / TS;
-    constexpr int KS = 16;                            // contraction unit
+    constexpr int KS = 32;                            // contraction rows per stage (two MFMA units)
+    static_assert(DK % KS == 0, "stage width divides dk");
     constexpr int SR = TS / 16, ST = SR * SR, NSW = (ST + 3) / 4;   // 16 x 16 subtiles, per wave
+    constexpr int NA = (TS * KS / 4 + 255) / 256, NB = (KS * TS / 4 + 255) / 256;   // float4 loads per thread
     __shared__ __attribute__((aligned(16))) float As[TS][KS + 4];   // As[r][k] = Phi_R^T[row0 + r][k0 + k]
     __shared__ __attribute__((aligned(16))) float Bs[KS][TS + 4];   // Bs[k][n] = [Phi_L^T | D_L^T][k0 + k][col0 + n]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
@@ -527,44 +530,87 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     const float *PL = Phit + L * DK * DK;
     const float *DL = Dt + L * DK * DV;
     const int row0 = TS * tr, col0 = TS * tn;
+
+    float4 ra[NA], rb[NB];
+    // Slice k0 of both operands into registers.  Columns come in groups of
+    // four that never straddle the Phi / D boundary (dk and dv are multiples
+    // of 16); columns past DK + DV read as zero.
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int e = tid + 256 * i;
+            if (e < TS * KS / 4) {
+                const int r = e / (KS / 4), k4 = 4 * (e % (KS / 4));
+                ra[i] = ld4(PR + (size_t)(row0 + r) * DK + k0 + k4);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            if (e < KS * TS / 4) {
+                const int kk = e / (TS / 4), col = col0 + 4 * (e % (TS / 4));
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (col < DK)
+                    x = ld4(PL + (size_t)(k0 + kk) * DK + col);
+                else if (col < NC)
+                    x = ld4(DL + (size_t)(k0 + kk) * DV + col - DK);
+                rb[i] = x;
+            }
+        }
+    };
+
     floatx4 acc[NSW];
 #pragma unroll
     for (int x = 0; x < NSW; ++x)
         acc[x] = zero4();
+    gload(0);
     for (int k0 = 0; k0 < DK; k0 += KS) {
         __syncthreads();
-        for (int e = tid; e < TS * KS / 4; e += 256) {
-            const int r = e / (KS / 4), k4 = 4 * (e % (KS / 4));
-            *reinterpret_cast<float4 *>(&As[r][k4]) =
-                *reinterpret_cast<const float4 *>(PR + (size_t)(row0 + r) * DK + k0 + k4);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int e = tid + 256 * i;
+            if (e < TS * KS / 4)
+                *reinterpret_cast<float4 *>(&As[e / (KS / 4)][4 * (e % (KS / 4))]) = ra[i];
         }
-        for (int e = tid; e < KS * TS; e += 256) {
-            const int kk = e / TS, n = e % TS, col = col0 + n;
-            float x = 0.f;
-            if (col < DK)
-                x = PL[(size_t)(k0 + kk) * DK + col];
-            else if (col < NC)
-                x = DL[(size_t)(k0 + kk) * DV + col - DK];
-            Bs[kk][n] = x;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int e = tid + 256 * i;
+            if (e < KS * TS / 4)
+                *reinterpret_cast<float4 *>(&Bs[e / (TS / 4)][4 * (e % (TS / 4))]) = rb[i];
         }
         __syncthreads();
+        if (k0 + KS < DK)
+            gload(k0 + KS);
 #pragma unroll
-        for (int x = 0; x < NSW; ++x) {
-            const int st = w + 4 * x;
-            if (st < ST) {
-                const int sr = st / SR, sc = st % SR;
-                const floatx4 af = lds_frag(&As[0][0], KS + 4, 16 * sr + li, 0, qd);
+        for (int ku = 0; ku < KS; ku += 16) {
+            if constexpr (SR == 4) {
+                // wave w: column subtile w, row subtiles 0..3 (one B fragment per unit)
                 floatx4 bf;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    bf[e] = Bs[4 * qd + e][16 * sc + li];
-                mma_unit(acc[x], af, bf);
+                    bf[e] = Bs[ku + 4 * qd + e][16 * w + li];
+#pragma unroll
+                for (int x = 0; x < NSW; ++x)
+                    mma_unit(acc[x], lds_frag(&As[0][0], KS + 4, 16 * x + li, ku, qd), bf);
+            } else {
+#pragma unroll
+                for (int x = 0; x < NSW; ++x) {
+                    const int st = w + 4 * x;
+                    if (st < ST) {
+                        const int sr = st / SR, sc = st % SR;
+                        floatx4 bf;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bf[e] = Bs[ku + 4 * qd + e][16 * sc + li];
+                        mma_unit(acc[x], lds_frag(&As[0][0], KS + 4, 16 * sr + li, ku, qd), bf);
+                    }
+                }
             }
         }
     }
 #pragma unroll
     for (int x = 0; x < NSW; ++x) {
-        const int st = w + 4 * x;
+        const int st = SR == 4 ? 4 * x + w : w + 4 * x;   // row subtile x, column subtile w when SR == 4
         if (st < ST) {
             const int sr = st / SR, sc = st % SR;
             const int col = col0 + 16 * sc + li;
