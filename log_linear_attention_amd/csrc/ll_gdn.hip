@@ -632,33 +632,65 @@ constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a tim
 // Tiles of Y B (Y: C x DK rows in LDS, B: DK x NB row-major in global memory)
 // on fp32 MFMA, 16 x 16 output tiles t = w, w + NW, ... of wave w; B is
 // staged through LDS (Bs) one 16-row unit at a time, read once per
-// workgroup.  Every thread of the workgroup must call this.  acc tile j of
-// the wave holds rows 16 * (t / (NB/16)) + 4*qd + r, column 16 * (t % (NB/16)) + li.
+// workgroup, and the next unit is loaded into registers before the current
+// one is multiplied.  Every thread of the workgroup (NW waves) must call
+// this.  acc tile j of the wave holds rows 16 * (t / (NB/16)) + 4*qd + r,
+// column 16 * (t % (NB/16)) + li.
 template <int NTW, int NW, int C, int DK, int LDY, int NB>
 __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float *B, float *Bs, int w, int li, int qd,
                                               floatx4 (&acc)[NTW])
 {
     constexpr int TN = NB / 16, TT = (C / 16) * TN;
+    constexpr int NTH = 64 * NW, NE = kGdnKS * NB / 4, NR = (NE + NTH - 1) / NTH;   // float4 per thread and unit
+    const int tid = threadIdx.x;
+    float4 rb[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+        if (tid + NTH * i < NE)
+            rb[i] = ld4(B + 4 * (tid + NTH * i));
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
         acc[j] = zero4();
 #pragma unroll 1
     for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
         __syncthreads();   // the previous unit has been read
-        for (int e = threadIdx.x; e < kGdnKS * NB / 4; e += blockDim.x)
-            *reinterpret_cast<float4 *>(Bs + 4 * e) = *reinterpret_cast<const float4 *>(B + (size_t)k0 * NB + 4 * e);
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            if (tid + NTH * i < NE)
+                *reinterpret_cast<float4 *>(Bs + 4 * (tid + NTH * i)) = rb[i];
         __syncthreads();
+        if (k0 + kGdnKS < DK) {
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-            const int t = w + NW * j;
-            if (t < TT) {
-                const int it = t / TN, nt = t % TN;
-                const floatx4 af = lds_frag(&Y[0][0], LDY, 16 * it + li, k0, qd);
-                floatx4 bf;
+            for (int i = 0; i < NR; ++i)
+                if (tid + NTH * i < NE)
+                    rb[i] = ld4(B + (size_t)(k0 + kGdnKS) * NB + 4 * (tid + NTH * i));
+        }
+        if constexpr (NW % TN == 0) {
+            // the wave's column tile is the same for all its tiles: one B fragment
+            const int nt = w % TN;
+            floatx4 bf;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    bf[e] = Bs[(4 * qd + e) * NB + 16 * nt + li];
-                mma_unit(acc[j], af, bf);
+            for (int e = 0; e < 4; ++e)
+                bf[e] = Bs[(4 * qd + e) * NB + 16 * nt + li];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int t = w + NW * j;
+                if (t < TT)
+                    mma_unit(acc[j], lds_frag(&Y[0][0], LDY, 16 * (t / TN) + li, k0, qd), bf);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int t = w + NW * j;
+                if (t < TT) {
+                    const int it = t / TN, nt = t % TN;
+                    const floatx4 af = lds_frag(&Y[0][0], LDY, 16 * it + li, k0, qd);
+                    floatx4 bf;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        bf[e] = Bs[(4 * qd + e) * NB + 16 * nt + li];
+                    mma_unit(acc[j], af, bf);
+                }
             }
         }
     }
