@@ -82,6 +82,16 @@ struct GdnChunkSmem {
     float lam[G::C][G::LOGC + 1];
 };
 
+// Workgroups b, b + 8, b + 16, ... run on one XCD (workgroups are dealt
+// round-robin over the eight XCDs).  This numbering gives each XCD a
+// contiguous range of the nb items, so items that read the same data share
+// that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int nb)
+{
+    const int per = nb >> 3, rem = nb & 7, xcd = bid & 7;
+    return xcd * per + min(xcd, rem) + (bid >> 3);
+}
+
 __device__ __forceinline__ int bitlen(unsigned x) { return x ? 32 - __builtin_clz(x) : 0; }
 
 // Tree offsets: level p holds N >> p blocks; levels are stored one after
@@ -521,7 +531,9 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     __shared__ __attribute__((aligned(16))) float Bs[KS][TS + 4];   // Bs[k][n] = [Phi_L^T | D_L^T][k0 + k][col0 + n]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
     const int bh = blockIdx.y;
-    const int tile = blockIdx.x % (TR * TN), j = blockIdx.x / (TR * TN);
+    // the tiles of one merge, and neighbouring merges, on one XCD
+    const int bx = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int tile = bx % (TR * TN), j = bx / (TR * TN);
     const int tr = tile / TN, tn = tile % TN;
     const size_t child0 = (size_t)bh * NBT + gdn_level_off(N, p - 1);
     const size_t L = child0 + 2 * (size_t)j, R = L + 1;
@@ -712,7 +724,9 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
     __shared__ __attribute__((aligned(16))) float Y[2][C][DK + 4];
     __shared__ __attribute__((aligned(16))) float Bs[kGdnKS * (DK > DV ? DK : DV)];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.x / N, c = blockIdx.x % N;
+    // neighbouring chunks of a head (which read the same finer blocks) on one XCD
+    const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bh = item / N, c = item % N;
     const int t0 = c * C, valid = min(C, Tlen - t0);
     const size_t row0 = (size_t)bh * Tlen + t0;
     if (c == 0) {
