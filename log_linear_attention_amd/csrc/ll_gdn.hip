@@ -54,7 +54,9 @@ struct Gdn {
     using T = typename DT::T;   // q, k, v and out; everything else is float32
     static constexpr int DK = DK_, DV = DV_, C = C_;
     static constexpr int NT = 256;
-    static constexpr int CNT = 512;   // chunk kernel threads (one workgroup per CU: LDS)
+    // chunk kernel threads: its LDS allows one workgroup per CU at chunk 64
+    // (16 waves) and two at chunk 32 (8 waves each)
+    static constexpr int CNT = C == 64 ? 1024 : 512;
     // walk threads: up to 512, at most C rows per 4-column group of either product
     static constexpr int WNT = C * (DK < DV ? DK : DV) / 4 < 512 ? C * (DK < DV ? DK : DV) / 4 : 512;
     static constexpr int LOGC = C == 32 ? 5 : 6;
