@@ -47,17 +47,20 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 vector, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_chunk_walk_fwd_bf16_T16K.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
                   for f in ("ll_fwd.hip", "ll_device.h")]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_decode_bf16_S64.txt")
+DECODE_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
+                  for f in ("ll_decode.hip", "ll_device.h", "ll_internal.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(sources=None) -> str:
     """Hash of the kernel sources' code (comments and layout ignored)."""
     import re
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES if sources is None else sources:
         with open(p, encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -136,18 +139,19 @@ def bwd_algorithmic(cfg):
     return cfg.B * cfg.H * per_bh
 
 
-def read_traffic():
-    """Counter-measured HBM bytes per ll_chunk_walk launch from the committed
-    profile summary, or None if absent or taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(path=TRAFFIC_FILE, sources=None):
+    """Counter-measured HBM bytes per launch of a kernel (ll_chunk_walk by
+    default) from its committed profile summary, or None if absent or taken
+    on different kernel sources."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != source_hash():
+    if vals.get("kernel_source_sha") != source_hash(sources):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -531,7 +535,8 @@ def main():
             "ms_per_step": round(dec_ms, 5), "tokens_per_s": round(dcfg.S / (dec_ms * 1e-3), 1),
             "algorithmic_bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES),
                          "kernel": "ll_decode", "kernel_avg_ms": round(dec_kernel_ms, 5)},
         },
         "prefill": {

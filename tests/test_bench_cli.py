@@ -32,3 +32,22 @@ def test_bench_algorithmic_counts():
     gflops, gbytes = bench.gdn_algorithmic(synth.WORKLOADS["gdn_f32_T16K"])
     assert set(gflops) == {"ll_gdn_chunk", "ll_gdn_tree", "ll_gdn_walk"}
     assert bench.gdn_algorithmic(synth.WORKLOADS["gdn_f32_T16K"], 2)[1] < gbytes
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path):
+    """A counter summary carries the hash of the kernel sources it was taken
+    on; bench.py reports its traffic only while the sources still hash to it."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = tmp_path / "k.hip"
+    src.write_text("__global__ void k(float *x) { x[0] = 1.f; }  // a comment\n")
+    summary = tmp_path / "traffic.txt"
+    summary.write_text(f"# summary\nkernel_source_sha: {bench.source_hash([str(src)])}\n"
+                       "traffic_bytes_per_launch: 12345\n")
+    assert bench.read_traffic(str(summary), [str(src)]) == 12345.0
+    src.write_text("__global__ void k(float *x) { x[0] = 1.f; }  // another comment\n")   # comments do not count
+    assert bench.read_traffic(str(summary), [str(src)]) == 12345.0
+    src.write_text("__global__ void k(float *x) { x[0] = 2.f; }\n")
+    assert bench.read_traffic(str(summary), [str(src)]) is None
+    assert bench.read_traffic(str(tmp_path / "absent.txt"), [str(src)]) is None
