@@ -515,8 +515,10 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 // level p-1:  Phi^T = Phi_R^T Phi_L^T,  D^T = Phi_R^T D_L^T + D_R^T.
 // Output [DK rows] x [DK + DV columns] in 64 x 64 tiles (rows x columns;
 // DK < 64: DK rows) on fp32 MFMA, 16 x 16 subtiles spread over the four
-// waves.  Both operands are staged through LDS 32 contraction rows at a
-// time with 16-byte loads; the next slice is loaded into registers before
+// waves, each formed transposed (B^T A^T) so that a lane holds four
+// consecutive columns of a row and writes them with one 16-byte store.
+// Both operands are staged through LDS 32 contraction rows at a time with
+// 16-byte loads; the next slice is loaded into registers before
 // the current one is multiplied, so its latency overlaps the MFMAs.
 template <class G>
 __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, float *__restrict__ Dt, int N, int NBT,
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
                     bf[e] = Bs[ku + 4 * qd + e][16 * w + li];
 #pragma unroll
                 for (int x = 0; x < NSW; ++x)
-                    mma_unit(acc[x], lds_frag(&As[0][0], KS + 4, 16 * x + li, ku, qd), bf);
+                    mma_unit(acc[x], bf, lds_frag(&As[0][0], KS + 4, 16 * x + li, ku, qd));
             } else {
 #pragma unroll
                 for (int x = 0; x < NSW; ++x) {
@@ -616,7 +618,7 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             bf[e] = Bs[ku + 4 * qd + e][16 * sc + li];
-                        mma_unit(acc[x], lds_frag(&As[0][0], KS + 4, 16 * sr + li, ku, qd), bf);
+                        mma_unit(acc[x], bf, lds_frag(&As[0][0], KS + 4, 16 * sr + li, ku, qd));
                     }
                 }
             }
@@ -627,15 +629,15 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
         const int st = SR == 4 ? 4 * x + w : w + 4 * x;   // row subtile x, column subtile w when SR == 4
         if (st < ST) {
             const int sr = st / SR, sc = st % SR;
-            const int col = col0 + 16 * sc + li;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 16 * sr + 4 * qd + r;
-                if (col < DK)
-                    Phit[self * DK * DK + (size_t)row * DK + col] = acc[x][r];
-                else if (col < NC)
-                    Dt[self * DK * DV + (size_t)row * DV + col - DK] =
-                        acc[x][r] + Dt[R * DK * DV + (size_t)row * DV + col - DK];
+            // transposed tile: lane (li, qd) holds row li, columns 4qd .. 4qd + 3
+            const int row = row0 + 16 * sr + li, col = col0 + 16 * sc + 4 * qd;
+            float4 o = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+            if (col < DK) {
+                *reinterpret_cast<float4 *>(Phit + self * DK * DK + (size_t)row * DK + col) = o;
+            } else if (col < NC) {
+                const float4 d = ld4(Dt + R * DK * DV + (size_t)row * DV + col - DK);
+                o.x += d.x; o.y += d.y; o.z += d.z; o.w += d.w;
+                *reinterpret_cast<float4 *>(Dt + self * DK * DV + (size_t)row * DV + col - DK) = o;
             }
         }
     }
