@@ -650,8 +650,8 @@ constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a tim
 // staged through LDS (Bs) one 16-row unit at a time, read once per
 // workgroup, and the next unit is loaded into registers before the current
 // one is multiplied.  Every thread of the workgroup (NW waves) must call
-// this.  acc tile j of the wave holds rows 16 * (t / (NB/16)) + 4*qd + r,
-// column 16 * (t % (NB/16)) + li.
+// this.  Tiles are formed transposed (B^T Y^T), so acc tile j of the wave
+// holds row 16 * (t / (NB/16)) + li, columns 16 * (t % (NB/16)) + 4*qd + r.
 template <int NTW, int NW, int C, int DK, int LDY, int NB>
 __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float *B, float *Bs, int w, int li, int qd,
                                               floatx4 (&acc)[NTW])
@@ -692,7 +692,7 @@ __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float
             for (int j = 0; j < NTW; ++j) {
                 const int t = w + NW * j;
                 if (t < TT)
-                    mma_unit(acc[j], lds_frag(&Y[0][0], LDY, 16 * (t / TN) + li, k0, qd), bf);
+                    mma_unit(acc[j], bf, lds_frag(&Y[0][0], LDY, 16 * (t / TN) + li, k0, qd));
             }
         } else {
 #pragma unroll
@@ -705,7 +705,7 @@ __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         bf[e] = Bs[(4 * qd + e) * NB + 16 * nt + li];
-                    mma_unit(acc[j], af, bf);
+                    mma_unit(acc[j], bf, af);
                 }
             }
         }
@@ -762,13 +762,11 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
         for (int j = 0; j < N1; ++j) {
             const int t = w + NW * j;
             if (t < T1) {
-                const int ib = 16 * (t / (DV / 16)) + 4 * qd;
+                const int i = 16 * (t / (DV / 16)) + li;
+                const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = ib + r;
-                    const float lw = i < valid ? lam[(row0 + i) * L + G::LOGC + m] : 0.f;
+                for (int r = 0; r < 4; ++r)
                     acc[j][r] += lw * tmp[j][r];
-                }
             }
         }
         if ((c >> m) == 0)
@@ -780,10 +778,8 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
         for (int j = 0; j < N2; ++j) {
             const int t = w + NW * j;
             if (t < T2) {
-                const int ib = 16 * (t / (DK / 16)) + 4 * qd, n = 16 * (t % (DK / 16)) + li;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    Y[cur ^ 1][ib + r][n] = ny[j][r];
+                const int i = 16 * (t / (DK / 16)) + li, n = 16 * (t % (DK / 16)) + 4 * qd;
+                *reinterpret_cast<float4 *>(&Y[cur ^ 1][i][n]) = make_float4(ny[j][0], ny[j][1], ny[j][2], ny[j][3]);
             }
         }
         __syncthreads();
@@ -793,14 +789,11 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
     for (int j = 0; j < N1; ++j) {
         const int t = w + NW * j;
         if (t < T1) {
-            const int ib = 16 * (t / (DV / 16)) + 4 * qd, n = 16 * (t % (DV / 16)) + li;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = ib + r;
-                if (i < valid) {
-                    const size_t o = (row0 + i) * DV + n;
-                    out[o] = from_f32<typename G::T>(obuf[o] + acc[j][r]);
-                }
+            const int i = 16 * (t / (DV / 16)) + li, n = 16 * (t % (DV / 16)) + 4 * qd;
+            if (i < valid) {
+                const size_t o = (row0 + i) * DV + n;
+                const float4 b = ld4(obuf + o);
+                st4t(out + o, make_float4(b.x + acc[j][0], b.y + acc[j][1], b.z + acc[j][2], b.w + acc[j][3]));
             }
         }
     }
