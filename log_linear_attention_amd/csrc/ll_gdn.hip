@@ -371,7 +371,8 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
     }
     __syncthreads();
 
-    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r): 4 rows x 4 columns;
+    // ---- carried queries qt_i = gamma_i (q_i - sum_{r<=i} S[i][r] w_r), 16 x 16 tiles
+    // formed transposed so that a lane writes four consecutive columns of its row;
     // weighted in-chunk attention A'[i][j] = lambda_i[level(i,j)] Z[i][j] beta_j (j <= i) ----
     float *qtc = qt + ((size_t)bh * N + c) * C * DK;
     {
@@ -389,14 +390,13 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
                         af[e] = 0.f;   // S is used on and below the diagonal
                     bf[e] = sm.QW[r][16 * sd + li];
                 }
-                mma_unit(acc, af, bf);
+                mma_unit(acc, bf, af);   // transposed tile: row i, columns 4qd .. 4qd + 3
             }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = 16 * si + 4 * qd + rr, d = 16 * sd + li;
-                const float qv = row < valid ? to_f32(q[(row0 + row) * DK + d]) : 0.f;
-                qtc[(size_t)row * DK + d] = __expf(sm.Aloc[row]) * (qv - acc[rr]);
-            }
+            const int d = 16 * sd + 4 * qd;
+            const float4 qv = i < valid ? ld4t(q + (row0 + i) * DK + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float gq = __expf(sm.Aloc[i]);
+            *reinterpret_cast<float4 *>(qtc + (size_t)i * DK + d) =
+                make_float4(gq * (qv.x - acc[0]), gq * (qv.y - acc[1]), gq * (qv.z - acc[2]), gq * (qv.w - acc[3]));
         }
     }
     for (int e = tid; e < C * C; e += NT) {
@@ -417,14 +417,12 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     bf[e] = sm.Vs[j0 + 4 * qd + e][16 * sc + li];
-                mma_unit(acc, lds_frag(&sm.M2[0][0], C + 4, 16 * si + li, j0, qd), bf);
+                mma_unit(acc, bf, lds_frag(&sm.M2[0][0], C + 4, 16 * si + li, j0, qd));   // transposed tile
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * si + 4 * qd + r;
-                if (i < valid)
-                    out[(row0 + i) * DV + 16 * sc + li] = acc[r];
-            }
+            const int i = 16 * si + li;
+            if (i < valid)
+                *reinterpret_cast<float4 *>(out + (row0 + i) * DV + 16 * sc + 4 * qd) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
 
