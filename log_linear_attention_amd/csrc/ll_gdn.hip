@@ -329,11 +329,10 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
                         const int r = j0 + 4 * qd + e;
                         bf[e] = sm.beta[r] * sm.Ks[r][16 * sd + li];
                     }
-                    mma_unit(acc, lds_frag(&sm.M3[0][0], C + 4, 16 * si + li, j0, qd), bf);
+                    mma_unit(acc, bf, lds_frag(&sm.M3[0][0], C + 4, 16 * si + li, j0, qd));   // transposed tile
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.QW[16 * si + 4 * qd + r][16 * sd + li] = acc[r];
+                *reinterpret_cast<float4 *>(&sm.QW[16 * si + li][16 * sd + 4 * qd]) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
             } else if (b < NWT + NUT) {
                 if constexpr (G::SEPU) {
                     const int si = (b - NWT) / TV, sc = (b - NWT) % TV;
@@ -359,13 +358,16 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
                             af[e] = 0.f;   // S is used on and below the diagonal
                         bf[e] = sm.M3[r][16 * sj + li];
                     }
-                    mma_unit(acc, af, bf);
+                    mma_unit(acc, bf, af);   // transposed tile: row i, columns 4qd .. 4qd + 3
                 }
+                float4 z;
+                float *zp = &z.x;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int ii = 16 * si + 4 * qd + r, jj = 16 * sj + li;
-                    sm.M2[ii][jj] = jj <= ii ? __expf(sm.Aloc[ii] - sm.Aloc[jj]) * acc[r] : 0.f;
+                    const int jj = 16 * sj + 4 * qd + r;
+                    zp[r] = jj <= i ? __expf(sm.Aloc[i] - sm.Aloc[jj]) * acc[r] : 0.f;
                 }
+                *reinterpret_cast<float4 *>(&sm.M2[i][16 * sj + 4 * qd]) = z;
             }
         }
     }
