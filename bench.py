@@ -170,14 +170,36 @@ def cpu_baseline(inp, cfg, n_rows: int, seed: int):
     t0 = time.perf_counter()
     oracle.fwd_rows(q, k, v, a, lam, rows)
     dt = time.perf_counter() - t0
+    # A token of the forward's `value` is one position of one sequence over
+    # all H heads, i.e. H (head, position) rows.
     return {
-        "value": n_rows / dt,
+        "value": round(n_rows / cfg.H / dt, 2),
         "unit": "tokens/s",
+        "head_rows_per_s": round(n_rows / dt, 1),
         "cores": oracle.num_threads(),
         "kind": "oracle",
         "sample": f"{n_rows} uniformly drawn (head, position) rows of the fwd_bf16_T16K workload "
-                  f"(fp64 O(T^2) row sums, mean cost equal to a full-workload row); {dt:.1f} s",
+                  f"(fp64 O(T^2) row sums, mean cost equal to a full-workload row) = {n_rows / cfg.H:.0f} "
+                  f"tokens of {cfg.H} heads; {dt:.1f} s",
     }
+
+
+def step_stats(torch, step, n):
+    """Per-step device times of n calls of step(i), from one timing event
+    recorded between consecutive steps on the current stream (a separate pass
+    from the bracketed one that gives the mean): median, p10 and p90 in ms."""
+    import numpy as np
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        step(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+    return {"median_ms": round(float(np.median(d)), 5), "p10_ms": round(float(np.percentile(d, 10)), 5),
+            "p90_ms": round(float(np.percentile(d, 90)), 5), "n": n}
 
 
 def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
@@ -202,6 +224,7 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     e1.record()
     torch.cuda.synchronize()
     bwd_ms = e0.elapsed_time(e1) / bsteps
+    bwd_stats = step_stats(torch, bstep, bsteps)
     ll.profile_begin(16 * bsteps + 16)
     torch.cuda.synchronize()
     for i in range(bsteps):
@@ -211,7 +234,7 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     bbytes = bwd_algorithmic(cfg)
     log(f"backward: {bwd_ms:.4f} ms/step; kernels: { {k: round(v * 1e3, 1) for k, v in bk.items()} }")
     return {
-        "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5),
+        "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5), "timing": bwd_stats,
         "tokens_per_s": round(cfg.B * cfg.T / (bwd_ms * 1e-3), 1),
         "algorithmic_bytes": bbytes,
         "kernels_ms": {k: round(v, 5) for k, v in bk.items()},
@@ -272,6 +295,7 @@ def measure_gdn(ll, torch, dev, args, e0, e1, bf16=False):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
+    gstats = step_stats(torch, lambda i: step(), n)
     ll.profile_begin(16 * n + 16)
     torch.cuda.synchronize()
     for _ in range(n):
@@ -287,6 +311,7 @@ def measure_gdn(ll, torch, dev, args, e0, e1, bf16=False):
         f"{ {k: round(v, 4) for k, v in ks.items()} }")
     return {
         "workload": cfg.name, "dtype": "f32", "inputs": "bf16" if bf16 else "f32", "ms_per_step": round(ms, 5),
+        "timing": gstats,
         "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
         "kernels_ms_per_step": {k: round(v, 5) for k, v in ks.items()},
         "algorithmic_flops": flops, "mandatory_bytes": nbytes,
@@ -318,6 +343,7 @@ def measure_grouped(ll, torch, cfg, dsets, args, e0, e1, Hqk):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    qstats = step_stats(torch, step, args.steps)
     ll.profile_begin(8 * args.steps + 8)
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -331,10 +357,78 @@ def measure_grouped(ll, torch, cfg, dsets, args, e0, e1, Hqk):
     log(f"grouped forward Hqk={Hqk}: {ms:.4f} ms/step; walk {ks['ll_chunk_walk'] * 1e3:.1f} us, {walk_gbs:.1f} GB/s")
     return {
         "workload": f"fwd_bf16_T16K with {Hqk} q/k heads for {cfg.H} heads", "Hqk": Hqk,
-        "ms_per_step": round(ms, 5), "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 5), "timing": qstats, "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
         "algorithmic_bytes": gbytes, "kernels_ms": {k: round(v, 5) for k, v in ks.items()},
         "walk_hbm_frac": round(walk_gbs / HBM_PEAK_GBS, 4),
     }
+
+
+def measure_fwd_workload(ll, torch, dev, name, args, e0, e1, wall=False):
+    """The forward on another workload (the 2K batch or the 64K long
+    context): K timed steps over rotating input sets whose combined size
+    exceeds 512 MB (so no step finds its inputs in the 256 MB MALL), the
+    per-step distribution, per-kernel times, and for small workloads the host
+    wall-clock of one call followed by a stream synchronisation."""
+    import synth
+
+    cfg = synth.WORKLOADS[name]
+    base = {k: v.to(dev) for k, v in synth.make_fwd_inputs(cfg).items()}
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    nsets = max(3, -(-(512 << 20) // set_bytes) + 1)
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(nsets - 1)]
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), dtype=cfg.torch_dtype, device=dev)
+    ws = ll.alloc_workspace(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk)
+
+    def step(i):
+        d = sets[i % nsets]
+        ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=cfg.chunk, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    stats = step_stats(torch, step, args.steps)
+    ll.profile_begin(8 * args.steps + 8)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ks = {k: v[1] / v[0] for k, v in ll.profile_end().items()}
+    fbytes, fflops = fwd_algorithmic(cfg)
+    dom = max(ks, key=ks.get)
+    dom_gbs = fbytes / (ks[dom] * 1e-3) / 1e9
+    res = {
+        "workload": name, "B": cfg.B, "H": cfg.H, "T": cfg.T, "a_scale": cfg.a_scale,
+        "ms_per_step": round(ms, 5), "timing": stats, "tokens_per_s": round(cfg.B * cfg.T / (ms * 1e-3), 1),
+        "input_sets": nsets, "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
+        "hbm_frac_whole_call": round(fbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "mfma_frac_whole_call": round(fflops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "kernels_ms": {k: round(v, 5) for k, v in ks.items()},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                     "kernel_avg_ms": round(ks[dom], 5)},
+    }
+    if wall:
+        import numpy as np
+
+        w = []
+        for i in range(args.steps):
+            t0 = time.perf_counter()
+            step(i)
+            torch.cuda.synchronize()
+            w.append((time.perf_counter() - t0) * 1e3)
+        res["host_wall_ms_per_call"] = {"median": round(float(np.median(w)), 4),
+                                        "p10": round(float(np.percentile(w, 10)), 4),
+                                        "p90": round(float(np.percentile(w, 90)), 4)}
+    log(f"{name}: {ms:.4f} ms/step, {res['tokens_per_s'] / 1e6:.1f} M tokens/s; kernels {res['kernels_ms']}")
+    del sets, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -350,6 +444,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet measurement")
     ap.add_argument("--no-grouped", action="store_true", help="skip the shared q/k measurement")
+    ap.add_argument("--no-other-workloads", action="store_true", help="skip the 2K and 64K forward workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -400,6 +495,7 @@ def main():
     torch.cuda.synchronize()
     w1 = time.perf_counter()
     fwd_ms = e0.elapsed_time(e1) / args.steps
+    fwd_stats = step_stats(torch, fwd, args.steps)
     # Per-kernel durations: the same K steps again, with HIP events recorded
     # around each launch on the launch stream by the library's profiler.
     ll.profile_begin(8 * args.steps + 8)
@@ -450,6 +546,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / args.steps
+    dec_stats = step_stats(torch, dstep, args.steps)
     ll.profile_begin(4 * args.steps + 4)
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -482,6 +579,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     pre_ms = e0.elapsed_time(e1) / args.steps
+    pre_stats = step_stats(torch, pstep, args.steps)
     ll.profile_begin(8 * args.steps + 8)
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -494,6 +592,12 @@ def main():
     stack_gbs = sbytes / (stack_ms * 1e-3) / 1e9
     log(f"prefill: {pre_ms:.4f} ms/step (forward alone {fwd_ms:.4f}); stack kernel {stack_ms:.4f} ms, "
         f"{stack_gbs:.1f} GB/s")
+
+    # ---- the other forward workloads: the 2K batch and the 64K long context ----
+    others = None
+    if not args.no_other_workloads:
+        others = {"fwd_bf16_T2K": measure_fwd_workload(ll, torch, dev, "fwd_bf16_T2K", args, e0, e1, wall=True),
+                  "fwd_bf16_T64K": measure_fwd_workload(ll, torch, dev, "fwd_bf16_T64K", args, e0, e1)}
 
     # ---- q/k shared across heads: the same forward with fewer q/k heads ----
     grouped = None if args.no_grouped else [measure_grouped(ll, torch, cfg, dsets, args, e0, e1, hq)
@@ -524,6 +628,7 @@ def main():
             "inputs": "q,k,v bf16; a,lambda fp32; out bf16",
         },
         "roofline": roofline,
+        "timing": fwd_stats,
         "forward": {
             "kernels_ms": {k: round(v[1] / v[0], 5) for k, v in kstats.items()},
             "algorithmic_bytes": fbytes, "algorithmic_flops": fflops,
@@ -532,7 +637,8 @@ def main():
         },
         "decode": {
             "workload": "decode_bf16_S64", "metric": "decode GB/s", "value": round(dec_gbs, 1), "unit": "GB/s",
-            "ms_per_step": round(dec_ms, 5), "tokens_per_s": round(dcfg.S / (dec_ms * 1e-3), 1),
+            "ms_per_step": round(dec_ms, 5), "timing": dec_stats,
+            "tokens_per_s": round(dcfg.S / (dec_ms * 1e-3), 1),
             "algorithmic_bytes": dbytes,
             "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
@@ -540,13 +646,14 @@ def main():
                          "kernel": "ll_decode", "kernel_avg_ms": round(dec_kernel_ms, 5)},
         },
         "prefill": {
-            "workload": "fwd_bf16_T16K + stack (Lcap 17)", "ms_per_step": round(pre_ms, 5),
+            "workload": "fwd_bf16_T16K + stack (Lcap 17)", "ms_per_step": round(pre_ms, 5), "timing": pre_stats,
             "tokens_per_s": round(cfg.B * cfg.T / (pre_ms * 1e-3), 1),
             "stack_algorithmic_bytes": sbytes,
             "roofline": {"bound": "hbm", "achieved": round(stack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(stack_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "ll_prefill_stack", "kernel_avg_ms": round(stack_ms, 5)},
         },
+        "other_workloads": others,
         "grouped_qk": grouped,
         "gated_deltanet": gdn_res,
         "backward": backward,

@@ -57,7 +57,12 @@ typedef enum {
 
 typedef enum {
     LL_F32 = 0, /* q, k, v, out are float32                                  */
-    LL_BF16 = 1 /* q, k, v, out are bfloat16; accumulation is float32        */
+    LL_BF16 = 1, /* q, k, v, out are bfloat16; accumulation is float32       */
+    /* Not dtypes.  They widen the enum's range to every 32-bit int, so a
+     * caller's out-of-range value is a valid ll_dtype in C++ too and reaches
+     * the library's own check (LL_EINVAL) instead of being undefined. */
+    LL_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+    LL_DTYPE_RANGE_MAX_ = 0x7fffffff
 } ll_dtype;
 
 /* Number of lambda entries per token for a sequence of T tokens:
@@ -85,8 +90,8 @@ size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
  *         loglinear_fwd_workspace_bytes(...) bytes (may be NULL when that is
  *         0).  Its contents on entry do not matter and are clobbered.
  * Supported: dtype F32 with dk, dv in {16, 32, 64, 128}; dtype BF16 with
- * dk in {32, 64, 128} and dv in {16, 32, 64, 128}; T < 2^31.  Anything else
- * returns LL_EUNSUPPORTED.
+ * dk in {32, 64, 128} and dv in {16, 32, 64, 128}; T < 2^31; B*H <= 65535.
+ * Anything else returns LL_EUNSUPPORTED.
  * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
 ll_status loglinear_fwd(const void *q, const void *k, const void *v,
                         const float *a, const float *lambda, void *out,
@@ -185,8 +190,11 @@ ll_status loglinear_bwd(const void *q, const void *k, const void *v,
  *  logscale [B,H,Lcap] float32, written for the occupied slots (each slot is
  *           stored decayed to its own last key; g is the decay from there to
  *           position T-1).
- *  Lcap     slots per (sequence, head): 2 <= Lcap <= 32 and
- *           Lcap >= loglinear_num_levels(T) (else LL_EINVAL).
+ *  Lcap     slots per (sequence, head): 2 <= Lcap <= 32 (else
+ *           LL_EUNSUPPORTED) and Lcap >= loglinear_num_levels(T + 1) =
+ *           1 + bit_length(T) (else LL_EINVAL): the stack of position T-1
+ *           needs loglinear_num_levels(T) slots, and the decode step at
+ *           position T needs T < 2^(Lcap-1).
  * Sequence b of the forward is decode sequence b: call
  * loglinear_decode_step next with pos[b] = T.  T == 0 leaves an empty stack
  * (pos = 0) and writes nothing.  state and logscale must not alias the
@@ -313,8 +321,10 @@ const char *loglinear_last_error(void);
  * (hipExtLaunchKernelGGL; timing-only events without a system-scope fence,
  * no synchronisation).
  * loglinear_profile_end synchronises those events and returns, per kernel
- * name, the number of launches and the summed device time.  Process-wide
- * state, not thread-safe; meant for benchmarks.  Creating the event pool in
+ * name, the number of launches and the summed device time.  The profiler is
+ * process-wide: while it is on, launches from every thread are recorded (a
+ * mutex guards its records; with profiling off a launch only reads one
+ * atomic flag).  Meant for benchmarks.  Creating the event pool in
  * loglinear_profile_begin may allocate host/driver resources. */
 typedef struct {
     char name[48];

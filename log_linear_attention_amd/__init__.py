@@ -15,7 +15,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libloglinear.so")
+# LOGLINEAR_LIB names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("LOGLINEAR_LIB") or os.path.join(_HERE, "libloglinear.so")
 
 LL_OK, LL_EINVAL, LL_EUNSUPPORTED, LL_EDEVICE, LL_EWORKSPACE = 0, -1, -2, -3, -4
 LL_F32, LL_BF16 = 0, 1
@@ -138,6 +140,27 @@ def _stream(stream) -> int:
     return int(stream)
 
 
+def _keep_for_stream(t, stream) -> None:
+    """Tie a tensor that this module allocated to the launch stream.
+
+    The caching allocator reuses a freed block as soon as the stream it was
+    allocated on is done with it.  The tensors allocated here (workspaces and
+    default outputs) are allocated on torch's current stream, while the
+    kernels run asynchronously on ``stream``; recording that stream keeps the
+    block from being handed out again before the kernels that use it finish."""
+    if t is None or stream is None:
+        return
+    if isinstance(stream, torch.cuda.Stream):
+        ts = stream
+    else:
+        handle = int(stream)
+        if handle == torch.cuda.current_stream().cuda_stream:
+            return
+        ts = torch.cuda.ExternalStream(handle)
+    if ts.cuda_stream != torch.cuda.current_stream().cuda_stream:
+        t.record_stream(ts)
+
+
 def _qkv_shapes(q, k, v):
     """(B, H, Hqk, T, dk, dv) from q, k [B,Hqk,T,dk] and v [B,H,T,dv]; H must
     be a multiple of Hqk (Hqk = H: one q/k head per head)."""
@@ -170,13 +193,16 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
     L = num_levels(T)
     if tuple(a.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
         raise ValueError(f"a must be [B,H,T] and lam [B,H,T,{L}]")
+    own = []
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+        own.append(out)
     elif tuple(out.shape) != (B, H, T, dv) or out.dtype != q.dtype:
         raise ValueError("out has the wrong shape or dtype")
     need = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if Hqk == H:
@@ -187,6 +213,8 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
         st = lib().loglinear_fwd_grouped(
             _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
             _dev(out, "out"), B, H, Hqk, T, dk, dv, chunk, code, ws_ptr, ws_bytes, _stream(stream), group_log2)
+    for t in own:
+        _keep_for_stream(t, stream)
     _check(st)
     return out
 
@@ -213,13 +241,16 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
     Lcap = state.shape[2]
     if tuple(state.shape) != (B, H, Lcap, dk, dv) or tuple(logscale.shape) != (B, H, Lcap):
         raise ValueError("state must be [B,H,Lcap,dk,dv] and logscale [B,H,Lcap]")
+    own = []
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+        own.append(out)
     elif tuple(out.shape) != (B, H, T, dv) or out.dtype != q.dtype:
         raise ValueError("out has the wrong shape or dtype")
     need = fwd_workspace_bytes(B, H, T, dk, dv, chunk, group_log2)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
@@ -235,6 +266,8 @@ def prefill(q, k, v, a, lam, state, logscale, chunk: int = 64, out=None, workspa
     else:
         st = lib().loglinear_prefill_grouped(*ptrs, B, H, Hqk, T, dk, dv, chunk, Lcap, code, ws_ptr, ws_bytes,
                                              _stream(stream), group_log2)
+    for t in own:
+        _keep_for_stream(t, stream)
     _check(st)
     return out
 
@@ -262,9 +295,11 @@ def bwd(q, k, v, a, lam, dout, chunk: int = 64, workspace=None, stream=None):
     dv_ = torch.empty_like(v)
     da = torch.empty_like(a)
     dlam = torch.empty_like(lam)
+    own = [dq, dk_, dv_, da, dlam]
     need = bwd_workspace_bytes(B, H, T, dk, dv, chunk, Hqk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
@@ -275,6 +310,8 @@ def bwd(q, k, v, a, lam, dout, chunk: int = 64, workspace=None, stream=None):
     else:
         st = lib().loglinear_bwd_grouped(*ptrs, B, H, Hqk, T, dk, dv, chunk, code, ws_ptr, ws_bytes,
                                          _stream(stream))
+    for t in own:
+        _keep_for_stream(t, stream)
     _check(st)
     return dq, dk_, dv_, da, dlam
 
@@ -296,8 +333,10 @@ def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
         raise ValueError("state must be [S,H,Lcap,dk,dv] and logscale [S,H,Lcap]")
     if tuple(lam.shape) != (S, H, Lcap) or tuple(a.shape) != (S, H) or tuple(pos.shape) != (S,):
         raise ValueError("lam must be [S,H,Lcap], a [S,H], pos [S]")
+    own = []
     if out is None:
         out = torch.empty((S, H, dv), dtype=q.dtype, device=q.device)
+        own.append(out)
     ptrs = (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
             _dev(state, "state", torch.float32), _dev(logscale, "logscale", torch.float32),
             _dev(pos, "pos", torch.int64), _dev(out, "out"))
@@ -305,6 +344,8 @@ def decode_step(q, k, v, a, lam, state, logscale, pos, out=None, stream=None):
         st = lib().loglinear_decode_step(*ptrs, S, H, dk, dv, Lcap, code, _stream(stream))
     else:
         st = lib().loglinear_decode_step_grouped(*ptrs, S, H, Hqk, dk, dv, Lcap, code, _stream(stream))
+    for t in own:
+        _keep_for_stream(t, stream)
     _check(st)
     return out
 
@@ -328,11 +369,14 @@ def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, st
     code = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+    own = []
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+        own.append(out)
     need = gdn_fwd_workspace_bytes(B, H, T, dk, dv, chunk)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     f32 = torch.float32
@@ -340,6 +384,8 @@ def gdn_fwd(q, k, v, a, beta, lam, chunk: int = 64, out=None, workspace=None, st
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", f32), _dev(beta, "beta", f32),
         _dev(lam, "lam", f32), _dev(out, "out", q.dtype), B, H, T, dk, dv, chunk, code, ws_ptr, ws_bytes,
         _stream(stream))
+    for t in own:
+        _keep_for_stream(t, stream)
     _check(st)
     return out
 

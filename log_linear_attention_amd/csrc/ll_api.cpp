@@ -4,7 +4,9 @@
 // path can be exercised on a machine without a GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -60,13 +62,17 @@ struct ProfRecord {
 };
 
 struct Profiler {
-    bool on = false;
     int used = 0;
     bool overflow = false;
     std::vector<hipEvent_t> pool;
     std::vector<ProfRecord> recs;
 };
 
+// The profiler is shared by every thread of the process.  Launches test the
+// atomic flag without locking (one relaxed load when profiling is off); the
+// event pool and the records are only touched under the mutex.
+std::atomic<bool> g_prof_on{false};
+std::mutex g_prof_mu;
 Profiler g_prof;
 
 }  // namespace
@@ -75,7 +81,10 @@ namespace ll {
 
 ProfEvents prof_events(const char *name)
 {
-    if (!g_prof.on)
+    if (!g_prof_on.load(std::memory_order_relaxed))
+        return {};
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on.load(std::memory_order_relaxed))
         return {};
     if (g_prof.used + 2 > (int)g_prof.pool.size()) {
         g_prof.overflow = true;
@@ -156,6 +165,8 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
         return st;
     if (group_log2 > ll::kMaxGroupLog2)
         return fail(LL_EUNSUPPORTED, "%s: group_log2 %d above %d", who, group_log2, ll::kMaxGroupLog2);
+    if ((int64_t)B * H > 65535)
+        return fail(LL_EUNSUPPORTED, "%s: B*H above 65535", who);
     const bool bf16 = dtype == LL_BF16;
     if (!ll::fwd_supported(bf16, dk, dv, chunk))
         return fail(LL_EUNSUPPORTED, "%s: no kernel for dtype=%s dk=%d dv=%d chunk=%d", who,
@@ -165,9 +176,12 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
             return fail(LL_EINVAL, "%s: Lcap must be >= 1 (got %d)", who, so->Lcap);
         if (so->Lcap < 2 || so->Lcap > ll::kMaxLevels)
             return fail(LL_EUNSUPPORTED, "%s: Lcap must be in [2, %d] (got %d)", who, ll::kMaxLevels, so->Lcap);
-        if (levels_for(T) > so->Lcap)
-            return fail(LL_EINVAL, "%s: the stack of position %d needs %d slots, Lcap is %d", who, T - 1,
-                        levels_for(T), so->Lcap);
+        // The stack of position T-1 needs levels_for(T) slots, and the decode
+        // step that continues at position T needs T < 2^(Lcap-1), i.e.
+        // Lcap >= 1 + bit_length(T) = levels_for(T + 1).
+        if (levels_for((int64_t)T + 1) > so->Lcap)
+            return fail(LL_EINVAL, "%s: decoding position %d after the prompt needs Lcap >= %d, got %d", who, T,
+                        levels_for((int64_t)T + 1), so->Lcap);
         if (!ll::stack_supported(bf16, dk, dv))
             return fail(LL_EUNSUPPORTED, "%s: no stack kernel for dk=%d dv=%d", who, dk, dv);
         if ((int64_t)B * H * (dk / 16) > INT_MAX)
@@ -456,10 +470,15 @@ static ll_status run_decode(const void *q, const void *k, const void *v, const f
     const size_t sh = (size_t)S * H;
     const size_t es = bf16 ? 2 : 4;
     const size_t nst = sh * Lcap * dk * dv * 4, nout = sh * dv * es, nq = (size_t)S * Hqk * dk * es;
-    if (overlaps(state, nst, out, nout) || overlaps(state, nst, logscale, sh * Lcap * 4) ||
-        overlaps(out, nout, q, nq) || overlaps(out, nout, k, nq) ||
-        overlaps(out, nout, v, nout) || overlaps(out, nout, logscale, sh * Lcap * 4))
-        return fail(LL_EINVAL, "loglinear_decode_step: state, logscale and out must not alias each other or inputs");
+    // Every written buffer (state, logscale, out) must be disjoint from every
+    // other buffer of the call.
+    const void *all[] = {state, logscale, out, q, k, v, a, lambda, pos};
+    const size_t sz[] = {nst, sh * Lcap * 4, nout, nq, nq, nout, sh * 4, sh * Lcap * 4, (size_t)S * 8};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 9; ++j)
+            if (j != i && overlaps(all[i], sz[i], all[j], sz[j]))
+                return fail(LL_EINVAL,
+                            "loglinear_decode_step: state, logscale and out must not alias each other or inputs");
     ll::DecodeArgs args{q, k, v, a, lambda, state, logscale, pos, out, S, H, dk, dv, Lcap, bf16};
     args.rqk = H / Hqk;
     hipError_t e = ll::decode_launch(args, static_cast<hipStream_t>(stream));
@@ -553,6 +572,8 @@ ll_status loglinear_profile_begin(int max_launches)
 {
     if (max_launches <= 0)
         return fail(LL_EINVAL, "loglinear_profile_begin: max_launches must be positive");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false, std::memory_order_relaxed);
     for (hipEvent_t e : g_prof.pool)
         (void)hipEventDestroy(e);
     g_prof = Profiler();
@@ -567,15 +588,16 @@ ll_status loglinear_profile_begin(int max_launches)
         }
     }
     g_prof.recs.reserve(max_launches);
-    g_prof.on = true;
+    g_prof_on.store(true, std::memory_order_relaxed);
     return ok();
 }
 
 ll_status loglinear_profile_end(ll_kernel_stat *stats, int max_stats, int *n_stats)
 {
-    if (!g_prof.on)
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on.load(std::memory_order_relaxed))
         return fail(LL_EINVAL, "loglinear_profile_end: profiling is not on");
-    g_prof.on = false;
+    g_prof_on.store(false, std::memory_order_relaxed);
     std::vector<ll_kernel_stat> out;
     for (const ProfRecord &r : g_prof.recs) {
         hipError_t e = hipEventSynchronize(r.stop);

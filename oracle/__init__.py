@@ -56,7 +56,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ll_oracle.c")
-_LIB = os.path.join(_HERE, "libll_oracle.so")
+# ORACLE_LIB names another build of the same C source (the host-sanitizer
+# build of the CPU tests); by default the in-tree build is loaded.
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "libll_oracle.so")
 _lib = None
 
 

@@ -185,10 +185,42 @@ def test_prefill_rejects_bad_arguments(L, kw, status):
 
 
 def test_prefill_lcap_fits_exactly(L):
-    # position 127 uses slots 0..7: Lcap = 8 passes validation (B = 0, so
-    # nothing is launched), Lcap = 7 does not
-    assert _pre(L, T=128, Lcap=8, B=0) == ll.LL_OK
+    # After a prompt of T tokens decoding continues at position T, which the
+    # decode step represents only when T < 2^(Lcap-1): Lcap >= 1 + bit_length(T).
+    # B = 0, so nothing is launched and only validation runs.
+    assert _pre(L, T=127, Lcap=8, B=0) == ll.LL_OK    # position 127 < 2^7
+    assert _pre(L, T=128, Lcap=9, B=0) == ll.LL_OK    # position 128 < 2^8
+    # num_levels(T) slots hold the stack of position T-1, but for a power of
+    # two T the next position needs one more: the old minimum is rejected
+    for T in (16, 128, 1024, 16384):
+        assert _pre(L, T=T, Lcap=ll.num_levels(T), B=0) == ll.LL_EINVAL
+        assert _pre(L, T=T, Lcap=ll.num_levels(T + 1), B=0) == ll.LL_OK
     assert _pre(L, T=128, Lcap=7, B=0) == ll.LL_EINVAL
+
+
+def test_fwd_rejects_too_many_heads_before_any_launch(L):
+    # B*H above 65535 is refused on the host (no launch is attempted, so the
+    # fake pointers are never touched)
+    need = ll.fwd_workspace_bytes(1, 70000, 1000, 128, 64, 64)
+    assert _fwd(L, B=1, H=70000, T=1000, ws=FAKE + 0x10000000, wsb=max(need, 1 << 30)) == ll.LL_EUNSUPPORTED
+    assert "65535" in ll.last_error()
+
+
+@pytest.mark.parametrize("kw", [
+    dict(state=FAKE),                    # state over q
+    dict(state=FAKE + 0x100000),         # state over k
+    dict(logscale=FAKE + 0x300000),      # logscale over a
+    dict(logscale=FAKE + 0x400000),      # logscale over lambda
+    dict(logscale=FAKE + 0xa000000),     # logscale over pos
+    dict(out=FAKE + 0x300000),           # out over a
+    dict(out=FAKE + 0x400000),           # out over lambda
+    dict(out=FAKE + 0xa000000),          # out over pos
+    dict(state=FAKE + 0x400000),         # state over lambda
+    dict(state=FAKE + 0xa000000 - 0x100),  # state running into pos
+])
+def test_decode_rejects_every_output_alias(L, kw):
+    assert _dec(L, **kw) == ll.LL_EINVAL
+    assert "alias" in ll.last_error()
 
 
 def test_prefill_empty_prompt_is_a_no_op(L):

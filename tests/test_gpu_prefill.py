@@ -162,3 +162,17 @@ def test_prefill_empty_prompt_writes_nothing():
     _, out, state, logscale = _prefill(p, 16, 4)
     assert out.numel() == 0
     assert torch.isnan(state).all() and torch.isnan(logscale).all()
+
+
+@pytest.mark.parametrize("T,dtype,chunk", [(16, "f32", 16), (1024, "f32", 64), (1024, "bf16", 64),
+                                           (64, "bf16", 64)])
+def test_prefill_with_the_smallest_lcap_then_decode(T, dtype, chunk):
+    """Lcap = 1 + bit_length(T), the smallest the prefill accepts: for a
+    power-of-two T the stack of position T-1 fits in one slot less, but the
+    decode step at position T needs this one.  Stack, then three decode
+    steps, against the oracle."""
+    Lcap = synth.num_levels(T + 1)
+    dk, dv = (128, 64) if dtype == "bf16" else (64, 32)
+    cfg = synth.FwdConfig("min_lcap", 1, 2, T, dk, dv, chunk, dtype, 0.05, 5600 + T)
+    announce(f"prefill {dtype} T={T} chunk={chunk} Lcap={Lcap} then decode")
+    _case(cfg, T, chunk, Lcap=Lcap)
