@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libloglinear.so")
-SOURCES = ["ll_api.cpp", "ll_fwd.hip", "ll_decode.hip", "ll_stack.hip", "ll_bwd.hip", "ll_gdn.hip"]
+SOURCES = ["ll_api.cpp", "ll_fwd.hip", "ll_fused.hip", "ll_decode.hip", "ll_stack.hip", "ll_bwd.hip", "ll_gdn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <algorithm>
 #include <climits>
 #include <mutex>
 #include <cstdarg>
@@ -136,7 +137,11 @@ size_t loglinear_fwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int
         return 0;
     if ((int64_t)B * H * T == 0)
         return 0;
-    return ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4).bytes;
+    size_t bytes = ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4).bytes;
+    // the one-launch forward may serve this shape (the query has no dtype)
+    if (group_log2 < 0 && ll::fused_supported(true, dk, dv, T, levels_for(T)))
+        bytes = std::max(bytes, ll::fused_workspace_bytes(B, H, T, dk, dv));
+    return bytes;
 }
 
 size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk)
@@ -212,16 +217,20 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
         overlaps(out, nv, a, na) || overlaps(out, nv, lambda, nl))
         return fail(LL_EINVAL, "%s: out aliases an input", who);
     const ll::FwdPlan plan = ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4);
-    if (plan.bytes > 0) {
+    // The plain forward with automatic groups runs as one launch where it can.
+    const bool fused = !so && group_log2 < 0 && ll::fused_supported(bf16, dk, dv, T, L);
+    const size_t need = fused ? ll::fused_workspace_bytes(B, H, T, dk, dv) : plan.bytes;
+    if (need > 0) {
         if (!workspace)
-            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, plan.bytes);
-        if (workspace_bytes < plan.bytes)
-            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, plan.bytes,
+            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, need);
+        if (workspace_bytes < need)
+            return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need,
                         workspace_bytes);
         if (!aligned(workspace, 256))
             return fail(LL_EINVAL, "%s: workspace must be 256-byte aligned", who);
-        if (overlaps(workspace, plan.bytes, out, nv) || overlaps(workspace, plan.bytes, q, nq) ||
-            overlaps(workspace, plan.bytes, k, nq) || overlaps(workspace, plan.bytes, v, nv))
+        if (overlaps(workspace, need, out, nv) || overlaps(workspace, need, q, nq) ||
+            overlaps(workspace, need, k, nq) || overlaps(workspace, need, v, nv) ||
+            overlaps(workspace, need, a, na) || overlaps(workspace, need, lambda, nl))
             return fail(LL_EINVAL, "%s: workspace aliases an input or the output", who);
     }
     const size_t bh = (size_t)B * H;
@@ -247,6 +256,12 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
     ll::FwdArgs args{q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, L, bf16, workspace};
     args.rqk = H / Hqk;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fused) {
+        hipError_t e = ll::fused_launch(args, s);
+        if (e != hipSuccess)
+            return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+        return ok();
+    }
     bool nat = false;
     hipError_t e = ll::fwd_launch(args, plan, s, &nat);
     if (e != hipSuccess)

@@ -56,6 +56,14 @@ bool fwd_supported(bool bf16, int dk, int dv, int chunk);
 // of unit u holds dk KB*u + 8*qd + e), false for unit_row's.
 hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stream, bool *nat_blocks = nullptr);
 
+// One-launch forward (bf16, dk = 128, dv = 64): groups of 128 tokens, the
+// levels above a group from Fenwick nodes that the work items publish to each
+// other through the workspace.  Used for the plain forward with automatic
+// group size; fused_workspace_bytes is its workspace (any dtype).
+size_t fused_workspace_bytes(int B, int H, int T, int dk, int dv);
+bool fused_supported(bool bf16, int dk, int dv, int T, int L);
+hipError_t fused_launch(const FwdArgs &args, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *a, *lam;

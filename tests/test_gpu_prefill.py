@@ -4,7 +4,8 @@ stack of the prompt's last position.
 Checks, against the fp64 oracle on the same seeded inputs:
   - every occupied slot, materialised as exp(g) * hat S, against the oracle's
     bucket sums (free slots must stay unwritten: they start as NaN);
-  - the prefill's output against the plain forward (same kernels: identical);
+  - the prefill's output against the oracle, and against the plain forward
+    (bit for bit where both run the same kernels);
   - decode of tokens T, T+1, ... from the written stack against rows T, T+1,
     ... of the oracle forward over the longer sequence.
 """
@@ -90,11 +91,23 @@ def _case(cfg, T, chunk, group_log2=-1, steps=3, Lcap=17):
     p = _prompt(full, T)
     d, out, state, logscale = _prefill(p, chunk, Lcap, group_log2)
     _check_stack(p, state, logscale, cfg.dtype)
-    # the prefill's output is the plain forward's
+    ref_full = oracle.fwd(full["q"], full["k"], full["v"], full["a"], full["lam"])
+    got = f64(out)
+    e = max(rel_l2(got, ref_full[:, :, :T]), per_head_max(got, ref_full[:, :, :T]))
+    assert np.all(np.isfinite(got)) and e <= TOL[cfg.dtype], e
+    # The prefill's output is the plain forward's, bit for bit, where both
+    # run the chunk walk.  With automatic grouping, bf16 heads of dk = 128,
+    # dv = 64 over more than one 128-token group take the one-launch forward
+    # instead, whose rounding order differs: there the oracle check above is
+    # the bar.
     ref_out = ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=chunk, group_log2=group_log2)
     torch.cuda.synchronize()
-    assert torch.equal(out, ref_out)
-    ref_rows = oracle.fwd(full["q"], full["k"], full["v"], full["a"], full["lam"])[:, :, T:T + steps]
+    one_launch = group_log2 < 0 and cfg.dtype == "bf16" and cfg.dk == 128 and cfg.dv == 64 and T > 128
+    if not one_launch:
+        assert torch.equal(out, ref_out)
+    else:
+        assert rel_l2(f64(ref_out), got) <= TOL[cfg.dtype]
+    ref_rows = ref_full[:, :, T:T + steps]
     _decode_steps(full, state, logscale, T, steps, [ref_rows[:, :, i] for i in range(steps)], cfg.dtype)
 
 
