@@ -113,6 +113,32 @@ ll_status loglinear_fwd_ex(const void *q, const void *k, const void *v,
                            ll_dtype dtype, void *workspace, size_t workspace_bytes,
                            void *stream, int group_log2);
 
+/* Device scratch that loglinear_fwd_noalloc holds on every GPU it runs on. */
+#define LL_FWD_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+
+/* loglinear_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation and kernels as loglinear_fwd (automatic group size); its
+ * workspace comes from a scratch array of LL_FWD_NOALLOC_SCRATCH_BYTES in the
+ * library's device code object (each GPU holds its own copy from the load of
+ * the library's kernels until the process ends) instead of an argument.  The
+ * call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  The caller passes the inputs and out as for loglinear_fwd.
+ *  stream  must belong to the current device (NULL: its null stream).
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (each call clears what it needs cleared with a kernel of
+ * its own): calls that overlap on one GPU (several streams, or threads
+ * without ordering) race and give wrong results; calls ordered on one stream
+ * are safe.
+ * Errors: those of loglinear_fwd; LL_EWORKSPACE when the shape needs more
+ * than LL_FWD_NOALLOC_SCRATCH_BYTES of workspace (it needs at most
+ * loglinear_fwd_workspace_bytes(...)); LL_EINVAL for a stream of another
+ * device. */
+ll_status loglinear_fwd_noalloc(const void *q, const void *k, const void *v,
+                                const float *a, const float *lambda, void *out,
+                                int B, int H, int T, int dk, int dv, int chunk,
+                                ll_dtype dtype, void *stream);
+
 /* One decode step for S sequences x H heads (the recurrent form).
  * Stack convention: for a sequence whose previous token sat at position p,
  * slot 0 holds that token's own state k v^T and slot l >= 1 holds the

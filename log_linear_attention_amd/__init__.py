@@ -21,6 +21,7 @@ LIB_PATH = os.environ.get("LOGLINEAR_LIB") or os.path.join(_HERE, "libloglinear.
 
 LL_OK, LL_EINVAL, LL_EUNSUPPORTED, LL_EDEVICE, LL_EWORKSPACE = 0, -1, -2, -3, -4
 LL_F32, LL_BF16 = 0, 1
+FWD_NOALLOC_SCRATCH_BYTES = 80 << 20   # LL_FWD_NOALLOC_SCRATCH_BYTES
 
 _STATUS_NAMES = {
     LL_EINVAL: "LL_EINVAL",
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.loglinear_fwd.restype = I
         L.loglinear_fwd_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_fwd_ex.restype = I
+        L.loglinear_fwd_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        L.loglinear_fwd_noalloc.restype = I
         L.loglinear_prefill.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, Z, P, I]
         L.loglinear_prefill.restype = I
         L.loglinear_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -216,6 +219,29 @@ def fwd(q, k, v, a, lam, chunk: int = 64, out=None, workspace=None, group_log2: 
     for t in own:
         _keep_for_stream(t, stream)
     _check(st)
+    return out
+
+
+def fwd_noalloc(q, k, v, a, lam, out, chunk: int = 64, stream=None):
+    """loglinear_fwd_noalloc: the forward with the library's per-GPU scratch
+    as its workspace, for callers that cannot allocate.  Same arguments as
+    fwd with one q/k head per head; out [B,H,T,dv] is required (nothing is
+    allocated).  Calls that overlap on one GPU race on the scratch.
+    Asynchronous on ``stream``."""
+    B, H, Hqk, T, dk, dv = _qkv_shapes(q, k, v)
+    if Hqk != H:
+        raise ValueError("fwd_noalloc takes one q/k head per head")
+    code = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    L = num_levels(T)
+    if tuple(a.shape) != (B, H, T) or tuple(lam.shape) != (B, H, T, L):
+        raise ValueError(f"a must be [B,H,T] and lam [B,H,T,{L}]")
+    if tuple(out.shape) != (B, H, T, dv) or out.dtype != q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check(lib().loglinear_fwd_noalloc(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(a, "a", torch.float32), _dev(lam, "lam", torch.float32),
+        _dev(out, "out"), B, H, T, dk, dv, chunk, code, _stream(stream)))
     return out
 
 

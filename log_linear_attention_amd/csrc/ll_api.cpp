@@ -1,7 +1,8 @@
 // C ABI of the log-linear attention library: argument validation, error
 // reporting, dispatch to the gfx950 kernels and optional launch profiling.
 // Validation runs entirely on the host and makes no HIP call, so every error
-// path can be exercised on a machine without a GPU.
+// path can be exercised on a machine without a GPU (the forward without
+// allocation looks up its scratch only after every argument check).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -149,6 +150,57 @@ size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
     return loglinear_fwd_workspace_bytes_ex(B, H, T, dk, dv, chunk, -1);
 }
 
+}  // extern "C"
+
+// ---- scratch of the forward for callers that cannot allocate ---------------
+// Each GPU that loads the library's kernels holds its own copy.  On the host,
+// `scratch` names a host-side stand-in, not device memory: kernels get the
+// address that hipGetSymbolAddress returns for the device in question.
+static __device__ __align__(256) unsigned char scratch[LL_FWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current.  The launch stream must belong to it.
+ll_status scratch_address(const char *who, void *stream, void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(LL_EDEVICE, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess)
+            return fail(LL_EDEVICE, "%s: hipStreamGetDevice failed: %s", who, hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(LL_EINVAL, "%s: the stream belongs to device %d but device %d is current", who, (int)sdev,
+                        dev);
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(LL_EUNSUPPORTED, "%s: device %d beyond the %d this entry point serves", who, dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(LL_EDEVICE, "%s: hipGetSymbolAddress of the scratch failed: %s", who,
+                        hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return LL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 // Decode stack a prefill writes (NULL: a plain forward).
 struct StackOut {
     float *state, *logscale;
@@ -159,7 +211,7 @@ struct StackOut {
 static ll_status run_fwd(const char *who, const void *q, const void *k, const void *v, const float *a,
                          const float *lambda, void *out, int B, int H, int Hqk, int T, int dk, int dv, int chunk,
                          ll_dtype dtype, void *workspace, size_t workspace_bytes, void *stream, int group_log2,
-                         const StackOut *so)
+                         const StackOut *so, bool use_scratch = false)
 {
     if (dtype != LL_F32 && dtype != LL_BF16)
         return fail(LL_EINVAL, "%s: unknown dtype %d", who, (int)dtype);
@@ -220,6 +272,15 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
     // The plain forward with automatic groups runs as one launch where it can.
     const bool fused = !so && group_log2 < 0 && ll::fused_supported(bf16, dk, dv, T, L);
     const size_t need = fused ? ll::fused_workspace_bytes(B, H, T, dk, dv) : plan.bytes;
+    if (use_scratch && need > 0) {
+        // the library's own scratch stands in for the workspace argument
+        if (need > LL_FWD_NOALLOC_SCRATCH_BYTES)
+            return fail(LL_EWORKSPACE, "%s: this shape needs %zu bytes of scratch, above the %zu the library holds",
+                        who, need, (size_t)LL_FWD_NOALLOC_SCRATCH_BYTES);
+        if ((st = scratch_address(who, stream, &workspace)) != LL_OK)
+            return st;
+        workspace_bytes = LL_FWD_NOALLOC_SCRATCH_BYTES;
+    }
     if (need > 0) {
         if (!workspace)
             return fail(LL_EWORKSPACE, "%s: workspace of %zu bytes required, got NULL", who, need);
@@ -340,6 +401,14 @@ ll_status loglinear_fwd(const void *q, const void *k, const void *v, const float
 {
     return loglinear_fwd_ex(q, k, v, a, lambda, out, B, H, T, dk, dv, chunk, dtype, workspace, workspace_bytes,
                             stream, -1);
+}
+
+ll_status loglinear_fwd_noalloc(const void *q, const void *k, const void *v, const float *a, const float *lambda,
+                                void *out, int B, int H, int T, int dk, int dv, int chunk, ll_dtype dtype,
+                                void *stream)
+{
+    return run_fwd("loglinear_fwd_noalloc", q, k, v, a, lambda, out, B, H, H, T, dk, dv, chunk, dtype, nullptr, 0,
+                   stream, -1, nullptr, true);
 }
 
 size_t loglinear_bwd_grouped_workspace_bytes(int B, int H, int Hqk, int T, int dk, int dv, int chunk)

@@ -206,6 +206,21 @@ def test_fwd_rejects_too_many_heads_before_any_launch(L):
     assert "65535" in ll.last_error()
 
 
+def test_fwd_noalloc_checks_arguments_before_any_device_call(L):
+    # 64 heads of 64K tokens need far more workspace than the library's
+    # scratch: LL_EWORKSPACE, found on the host (fake pointers 4 GiB apart so
+    # that no alias check fires first; nothing is launched)
+    B, H, T, dk, dv = 1, 64, 65536, 128, 64
+    assert ll.fwd_workspace_bytes(B, H, T, dk, dv, 64) > ll.FWD_NOALLOC_SCRATCH_BYTES
+    p = [FAKE + i * (1 << 32) for i in range(6)]
+    assert L.loglinear_fwd_noalloc(*p, B, H, T, dk, dv, 64, ll.LL_BF16, None) == ll.LL_EWORKSPACE
+    assert "scratch" in ll.last_error()
+    # argument errors come before the scratch lookup (which would need a GPU)
+    assert L.loglinear_fwd_noalloc(None, *p[1:], B, H, 1000, dk, dv, 64, ll.LL_BF16, None) == ll.LL_EINVAL
+    assert L.loglinear_fwd_noalloc(*p, B, H, 1000, dk, dv, 48, ll.LL_BF16, None) == ll.LL_EUNSUPPORTED
+    assert L.loglinear_fwd_noalloc(*p, B, H, 1000, dk, dv, 64, 7, None) == ll.LL_EINVAL
+
+
 @pytest.mark.parametrize("kw", [
     dict(state=FAKE),                    # state over q
     dict(state=FAKE + 0x100000),         # state over k
