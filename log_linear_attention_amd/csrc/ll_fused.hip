@@ -25,12 +25,12 @@
 // at group granularity.
 //
 // The grid holds two kinds of work items, one workgroup each, in rounds of
-// 16 groups: a round's state items (group j's state, merged with the nodes
-// of j's trailing bits, published as node j), then its output items (the
-// in-group part and the levels above the group, read from the published
-// nodes).  The chains of nodes (N_j waits for N_{j-1}, N_{j-2}, N_{j-4},
-// ...) thus run among light items that do nothing else, ahead of the output
-// items that read them.
+// a few groups: state items (group j's state, merged with the nodes of j's
+// trailing bits, published as node j) and output items (the in-group part
+// and the levels above the group, read from the published nodes), the state
+// items dispatched a round ahead of the output items.  The chains of nodes
+// (N_j waits for N_{j-1}, N_{j-2}, N_{j-4}, ...) thus run among light items
+// that do nothing else, ahead of the output items that read them.
 //
 // Nodes live in the workspace (bf16, in the MFMA fragment order their
 // readers load, with their total log-decay in float32) and carry a ready
@@ -191,8 +191,11 @@ __device__ __forceinline__ bool wait_flag(const int *f)
     return false;
 }
 
-// Groups per round of the workgroup order (state items, then output items).
-constexpr int kRound = 16;
+// Items of one kind per round of the workgroup order (the groups of a round
+// are this many over the heads, at least one), and the rounds by which the
+// state items run ahead of the output items.
+constexpr int kRoundItems = 64;
+constexpr int kLag = 2;
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -360,42 +363,59 @@ template <class F>
 __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void ll_fused_fwd(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ k, const __bf16 *__restrict__ v,
     const float *__restrict__ a, const float *__restrict__ lam, __bf16 *__restrict__ out, int BH, int Tlen, int L,
-    int nG, int rqk, Ws ws)
+    int nG, int rqk, int kRound, Ws ws)
 {
     __shared__ Smem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
 
     // ---- work item of this workgroup ----
     // Workgroups are dispatched in the order of their index, and every item
-    // waits only for items of the same head with a smaller group index, which
-    // map to smaller workgroup indices: those were dispatched first, so every
-    // wait ends.  With a multiple of 8 heads, workgroup b = 8r + x (it runs
-    // on XCD x when workgroups are dealt round-robin over the 8 XCDs) takes
-    // head x + 8 (r mod nh), group r / nh: all items of a head share one XCD
-    // and its L2.  Otherwise the order is plainly group-major.
-    // Workgroups come in rounds of kRound groups (all heads): first the state
-    // items of the round (group state, published as a Fenwick node; the
-    // chains of nodes run among these light items), then its output items
-    // (the in-group part and the levels above the group, read from the
-    // nodes).  An output item waits only for nodes of earlier or same-round
-    // groups, whose state items have smaller workgroup indices.  Within a
-    // round, with a multiple of 8 heads, item i = 8r + x (it runs on XCD x
-    // when workgroups are dealt round-robin over the 8 XCDs) is head
+    // waits only for items with smaller workgroup indices (below): those were
+    // dispatched first, so every wait ends.
+    // Workgroups come in rounds of kRound groups (all heads; about
+    // kRoundItems items of each kind), the state
+    // items running kLag rounds ahead of the output items:
+    //     S_0 .. S_{kLag-1}, then S_{m+kLag}, O_m for m = 0, 1, ..., then the
+    //     last output rounds.
+    // A state item publishes its group's Fenwick node (the chains of nodes
+    // run among these light items); an output item does the in-group part
+    // and reads the nodes of earlier groups of its head, published rounds
+    // before.  Every wait is thus for a smaller workgroup index.
+    // Within a round, with a multiple of 8 heads, item i = 8r + x (it runs
+    // on XCD x when workgroups are dealt round-robin over the 8 XCDs) is head
     // x + 8 (r mod nh), group r / nh of the round: all items of a head share
     // one XCD and its L2.  Otherwise the order is group-major.
     bool state_item;
     int bh, j;
     {
-        const int b = blockIdx.x;
-        const int rs = BH * kRound;                 // items of each kind in a full round
-        const int m = b / (2 * rs);                 // round
-        const int g0 = m * kRound;                  // its first group
-        const int ng = min(kRound, nG - g0);        // its groups
-        const int cs = BH * ng;
-        int i = b - m * 2 * rs;
-        state_item = i < cs;
-        if (!state_item)
-            i -= cs;
+        int b = blockIdx.x, m, i;
+        const int rs = BH * kRound;                          // items of one kind in a full round
+        const int M = (nG + kRound - 1) / kRound;            // rounds
+        const int cl = BH * (nG - (M - 1) * kRound);         // items of one kind in the last round
+        // the leading state rounds (the last of them may be the short one)
+        const int nA = min(kLag, M);
+        const int lenA = (nA - 1) * rs + (kLag >= M ? cl : rs);
+        const int P = max(M - kLag, 0);                      // pairs (S_{m+kLag}, O_m)
+        const int lenB = P > 0 ? (P - 1) * 2 * rs + cl + rs : 0;
+        if (b < lenA) {
+            state_item = true;
+            m = b / rs;
+            i = b - m * rs;
+        } else if ((b -= lenA) < lenB) {
+            const int p = b / (2 * rs);
+            const int ssz = p == P - 1 ? cl : rs;            // only the last pair holds the short state round
+            i = b - p * 2 * rs;
+            state_item = i < ssz;
+            m = state_item ? p + kLag : p;
+            if (!state_item)
+                i -= ssz;
+        } else {
+            b -= lenB;
+            state_item = false;
+            m = P + b / rs;
+            i = b - (m - P) * rs;
+        }
+        const int g0 = m * kRound;
         if ((BH & 7) == 0) {
             const int nh = BH >> 3, x = i & 7, r = i >> 3;
             bh = x + 8 * (r % nh);
@@ -409,7 +429,17 @@ __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
     const int qbh = bh / rqk;
     const size_t hrow = (size_t)bh * Tlen, qrow = (size_t)qbh * Tlen;
 
-    // ---- stage K and V of the group (swizzled); Q, lambda and a to registers ----
+    // ---- stage K and V of the group (swizzled); Q, lambda and a to
+    //      registers.  Every load is issued before the one wait below, so
+    //      the phase costs a single memory round trip. ----
+    // decay of tokens lane and 64 + lane (wave 0 scans them)
+    float a0 = 0.f, a1 = 0.f;
+    if (w == 0) {
+        if (t0 + lane < Tlen)
+            a0 = a[hrow + t0 + lane];
+        if (t0 + 64 + lane < Tlen)
+            a1 = a[hrow + t0 + 64 + lane];
+    }
     {
         const __amdgpu_buffer_rsrc_t rk = rsrc(k + (qrow + t0) * F::DK, (uint32_t)(Tlen - t0) * F::DK * 2);
         const __amdgpu_buffer_rsrc_t rv = rsrc(v + (hrow + t0) * F::DV, (uint32_t)(Tlen - t0) * F::DV * 2);
@@ -446,16 +476,30 @@ __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         const float *lp = lam + (hrow + tc) * L;
         lamr[x] = Lam3{lp[5], lp[6], lp[7]};
     }
-    // lambda levels 0 .. 4 of the group's tokens (level-major; 0 past the end)
-    for (int i = tid; i < 5 * F::TG; i += F::NT) {
-        const int r = i / 5, l = i - 5 * r;
-        sm.lamd[l][r] = t0 + r < Tlen ? lam[(hrow + t0 + r) * L + l] : 0.f;
     }
+    // lambda levels 0 .. 4 of the group's tokens (0 past the end): entry
+    // i = tid + NT x is token i / 5, level i mod 5
+    // (entries past the table repeat its last one: loads and stores stay
+    // unconditional, so no load is sunk below the wait)
+    constexpr int NLD = (5 * F::TG + F::NT - 1) / F::NT;
+    float lv[NLD];
+    if (!state_item) {
+#pragma unroll
+        for (int x = 0; x < NLD; ++x) {
+            const int i = min(tid + x * F::NT, 5 * F::TG - 1), r = i / 5;
+            lv[x] = lam[(hrow + min(t0 + r, Tlen - 1)) * L + (i - 5 * r)];
+        }
     }
-    // decay prefix of the group (wave 0): a of tokens lane and 64 + lane
+    wait_vm0();
+    if (!state_item) {
+#pragma unroll
+        for (int x = 0; x < NLD; ++x) {
+            const int i = min(tid + x * F::NT, 5 * F::TG - 1), r = i / 5;
+            sm.lamd[i - 5 * r][r] = t0 + r < Tlen ? lv[x] : 0.f;
+        }
+    }
+    // decay prefix of the group (wave 0)
     if (w == 0) {
-        const float a0 = t0 + lane < Tlen ? a[hrow + t0 + lane] : 0.f;
-        const float a1 = t0 + 64 + lane < Tlen ? a[hrow + t0 + 64 + lane] : 0.f;
         const float x0 = wave_scan(a0);
         const float tot0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x0), 63));
         const float x1 = wave_scan(a1) + tot0;
@@ -464,7 +508,6 @@ __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         if (lane == 63)
             sm.gam = x1;
     }
-    wait_vm0();
     __syncthreads();
     const float gam = sm.gam;
 
@@ -567,6 +610,22 @@ __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
 
     // ---- levels above the group: one node per set bit of j ----
     if (npop > 0) {
+        // Level weights of the first four set bits for both rows, loaded
+        // before the waits so that their memory latency overlaps them.
+        float lwp[2][4];
+        {
+            unsigned bits = (unsigned)j;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int kb = bits ? __builtin_ctz(bits) : 0;
+                bits &= bits - 1;
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int tq = t0 + 16 * F::qtile(w, x) + li;
+                    lwp[x][n] = lam[(hrow + (tq < Tlen ? tq : Tlen - 1)) * L + min(F::LTG + 1 + kb, L - 1)];
+                }
+            }
+        }
         // Wave 0 waits for every node at once (lane kb for bit kb) and forms
         // the decay from each node's end to the group start: the totals of
         // the finer nodes between, an exclusive prefix over the set bits.
@@ -618,8 +677,15 @@ __global__ __launch_bounds__(F::NT) __attribute__((amdgpu_waves_per_eu(3, 3))) v
         for (int n = 0; n < npop; ++n) {
             const int slot = n % 3;
             const int kb = slot == 0 ? kbs[0] : slot == 1 ? kbs[1] : kbs[2];
-            // the level weights of this node, loaded before the wait
-            const float lw0 = lrow[0][F::LTG + 1 + kb], lw1 = lrow[1][F::LTG + 1 + kb];
+            // the level weights of this node (preloaded for the first four)
+            float lw0, lw1;
+            if (n < 4) {
+                lw0 = n == 0 ? lwp[0][0] : n == 1 ? lwp[0][1] : n == 2 ? lwp[0][2] : lwp[0][3];
+                lw1 = n == 0 ? lwp[1][0] : n == 1 ? lwp[1][1] : n == 2 ? lwp[1][2] : lwp[1][3];
+            } else {
+                lw0 = lrow[0][F::LTG + 1 + kb];
+                lw1 = lrow[1][F::LTG + 1 + kb];
+            }
             const int ahead = issued - n - 1;   // stages issued after node n's
             if (ahead >= 2)
                 wait_vm<2 * PER>();
@@ -731,7 +797,7 @@ hipError_t fused_launch(const FwdArgs &A, hipStream_t s)
     pe = prof_events("ll_fused_fwd");
     hipExtLaunchKernelGGL(fz::ll_fused_fwd<F>, dim3(2 * BH * nG), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
                           (const __bf16 *)A.q, (const __bf16 *)A.k, (const __bf16 *)A.v, A.a, A.lam,
-                          (__bf16 *)A.out, BH, A.T, A.L, nG, A.rqk, ws);
+                          (__bf16 *)A.out, BH, A.T, A.L, nG, A.rqk, std::max(1, fz::kRoundItems / BH), ws);
     return hipGetLastError();
 }
 
