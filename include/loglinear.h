@@ -91,7 +91,8 @@ size_t loglinear_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
  *         0).  Its contents on entry do not matter and are clobbered.
  * Supported: dtype F32 with dk, dv in {16, 32, 64, 128}; dtype BF16 with
  * dk in {32, 64, 128} and dv in {16, 32, 64, 128}; T < 2^31; B*H <= 65535.
- * Anything else returns LL_EUNSUPPORTED.
+ * Anything else (every other head size, e.g. 48, 96 or 256) returns
+ * LL_EUNSUPPORTED: the kernels are compiled for these power-of-two tiles.
  * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
 ll_status loglinear_fwd(const void *q, const void *k, const void *v,
                         const float *a, const float *lambda, void *out,
@@ -189,9 +190,10 @@ ll_status loglinear_decode_step(const void *q, const void *k, const void *v,
  *  workspace: caller-owned device scratch of loglinear_bwd_workspace_bytes
  *         bytes, 256-byte aligned; contents on entry do not matter.
  * Outputs must not alias each other, the inputs or the workspace.
- * Supported: chunk 32 or 64; dk, dv in {32, 64, 128}; both dtypes, where the
- * kernels fit in LDS (bf16 chunk 64 and 32; float32 chunk 32).  Anything
- * else returns LL_EUNSUPPORTED.  Accumulation is float32 throughout; in bf16
+ * Supported: dk, dv in {32, 64, 128} with chunk 32 or 64 in bf16, and with
+ * chunk 32 in float32 (float32 chunk 64 only for dk = dv = 32: the larger
+ * chunk kernels do not fit in LDS).  Anything else, including every other
+ * multiple of 16 up to 256, returns LL_EUNSUPPORTED.  Accumulation is float32 throughout; in bf16
  * the operands of the matrix products are bf16, as in the forward.
  * Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_EWORKSPACE, LL_EDEVICE. */
 size_t loglinear_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk);

@@ -391,3 +391,79 @@ def test_gdn_rejects_bad_arguments(L):
     n = ll.gdn_fwd_workspace_bytes(1, 16, 16384, 128, 64, 64)
     assert n > 0 and n % 256 == 0
     assert ll.gdn_fwd_workspace_bytes(1, 16, 16384, 128, 64, 16) == 0
+
+
+# ---- the shape support matrix, checked exhaustively on the host --------------
+# Every dk, dv that is a multiple of 16 up to 256, both dtypes, every chunk:
+# with an empty batch (B = 0, or S = 0 for decode) nothing is launched, and the
+# call returns LL_OK exactly for the shapes the header lists as supported and
+# LL_EUNSUPPORTED for every other one.
+DIMS = list(range(16, 257, 16))
+P4 = {16, 32, 64, 128}
+
+
+def _fwd_ok(dtype, dk, dv, chunk):
+    if dtype == ll.LL_F32:
+        return dk in P4 and dv in P4
+    return dk in {32, 64, 128} and dv in P4
+
+
+@pytest.mark.parametrize("dtype", [ll.LL_F32, ll.LL_BF16])
+def test_forward_support_matrix(L, dtype):
+    for chunk in (16, 32, 64):
+        for dk in DIMS:
+            for dv in DIMS:
+                st = _fwd(L, B=0, q=None, k=None, v=None, out=None, a=None, lam=None, dk=dk, dv=dv, chunk=chunk,
+                          dtype=dtype)
+                want = ll.LL_OK if _fwd_ok(dtype, dk, dv, chunk) else ll.LL_EUNSUPPORTED
+                assert st == want, (dtype, dk, dv, chunk, st, ll.last_error())
+
+
+@pytest.mark.parametrize("dtype", [ll.LL_F32, ll.LL_BF16])
+def test_decode_support_matrix(L, dtype):
+    for dk in DIMS:
+        for dv in DIMS:
+            st = _dec(L, S=0, q=None, k=None, v=None, a=None, lam=None, state=None, logscale=None, pos=None,
+                      out=None, dk=dk, dv=dv, dtype=dtype)
+            want = ll.LL_OK if dk in P4 and dv in P4 else ll.LL_EUNSUPPORTED
+            assert st == want, (dtype, dk, dv, st, ll.last_error())
+
+
+def _bwd_ok(dtype, dk, dv, chunk):
+    if dk not in {32, 64, 128} or dv not in {32, 64, 128}:
+        return False
+    if dtype == ll.LL_BF16:
+        return chunk in (32, 64)
+    return chunk == 32 or (chunk == 64 and dk == dv == 32)
+
+
+@pytest.mark.parametrize("dtype", [ll.LL_F32, ll.LL_BF16])
+def test_backward_support_matrix(L, dtype):
+    for chunk in (16, 32, 64):
+        for dk in DIMS:
+            for dv in DIMS:
+                st = _bwd(L, B=0, q=None, k=None, v=None, a=None, lam=None, do=None, dq=None, dk=None, dv=None,
+                          da=None, dlam=None, ws=None, wsb=0, dk_=dk, dv_=dv, chunk=chunk, dtype=dtype)
+                want = ll.LL_OK if _bwd_ok(dtype, dk, dv, chunk) else ll.LL_EUNSUPPORTED
+                assert st == want, (dtype, dk, dv, chunk, st, ll.last_error())
+
+
+@pytest.mark.parametrize("dtype", [ll.LL_F32, ll.LL_BF16])
+def test_gdn_support_matrix(L, dtype):
+    for chunk in (16, 32, 64):
+        for dk in DIMS:
+            for dv in DIMS:
+                st = L.loglinear_gdn_fwd(None, None, None, None, None, None, None, 0, 1, 64, dk, dv, chunk, dtype,
+                                         None, 0, None)
+                ok = dk in {32, 64, 128} and dv in {32, 64, 128} and chunk in (32, 64)
+                assert st == (ll.LL_OK if ok else ll.LL_EUNSUPPORTED), (dtype, dk, dv, chunk, st, ll.last_error())
+
+
+@pytest.mark.parametrize("dtype", [ll.LL_F32, ll.LL_BF16])
+def test_prefill_support_matrix(L, dtype):
+    for dk in DIMS:
+        for dv in DIMS:
+            st = _pre(L, B=0, q=None, k=None, v=None, out=None, a=None, lam=None, state=None, logscale=None,
+                      dk=dk, dv=dv, dtype=dtype)
+            want = ll.LL_OK if _fwd_ok(dtype, dk, dv, 64) else ll.LL_EUNSUPPORTED
+            assert st == want, (dtype, dk, dv, st, ll.last_error())

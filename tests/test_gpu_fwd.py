@@ -84,6 +84,19 @@ def test_bf16_other_head_dims(dk, dv):
     _check_full(inp, _run(inp, 64), "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_supported_head_size(dtype):
+    # every (dk, dv) the forward accepts, each chunk size, one ragged length
+    dks = (16, 32, 64, 128) if dtype == "f32" else (32, 64, 128)
+    for dk in dks:
+        for dv in (16, 32, 64, 128):
+            for chunk in (16, 32, 64):
+                cfg = synth.FwdConfig("dims", 1, 1, 333, dk, dv, chunk, dtype, 0.05, 7000 + dk + dv + chunk)
+                announce(f"{dtype} dk={dk} dv={dv} chunk={chunk}")
+                inp = synth.make_fwd_inputs(cfg)
+                _check_full(inp, _run(inp, chunk), dtype)
+
+
 def test_bf16_T2K_workload():
     cfg = synth.WORKLOADS["fwd_bf16_T2K"]
     announce(cfg.name)
