@@ -142,6 +142,16 @@ def bwd_algorithmic(cfg):
     return cfg.B * cfg.H * per_bh
 
 
+def bwd_chunk_algorithmic(cfg):
+    """Mandatory HBM bytes of one ll_bwd_chunk launch: q, k, v, do, a and
+    lambda of every token in, dk, dv, dlambda and the in-chunk part of da out
+    (the level states it reads are intermediate, not counted)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    T, dk, dv, L = cfg.T, cfg.dk, cfg.dv, cfg.L
+    per_bh = T * (2 * dk + 2 * dv) * e + 4 * T + 4 * T * L + T * (dk + dv) * e + 4 * T * L + 4 * T
+    return cfg.B * cfg.H * per_bh
+
+
 def read_traffic(path=TRAFFIC_FILE, sources=None):
     """Counter-measured HBM bytes per launch of a kernel (ll_chunk_walk by
     default) from its committed profile summary, or None if absent or taken
@@ -236,13 +246,20 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
     bk = {k: v[1] / v[0] for k, v in ll.profile_end().items()}
     bbytes = bwd_algorithmic(cfg)
     log(f"backward: {bwd_ms:.4f} ms/step; kernels: { {k: round(v * 1e3, 1) for k, v in bk.items()} }")
+    dom = max(bk, key=bk.get)
+    # roofline of the chunk kernel (the dominant one): its mandatory bytes
+    # per launch over its mean launch time
+    cbytes, cms = bwd_chunk_algorithmic(cfg), bk["ll_bwd_chunk"]
     return {
         "workload": "fwd_bf16_T16K gradients", "ms_per_step": round(bwd_ms, 5), "timing": bwd_stats,
         "tokens_per_s": round(cfg.B * cfg.T / (bwd_ms * 1e-3), 1),
         "algorithmic_bytes": bbytes,
         "kernels_ms": {k: round(v, 5) for k, v in bk.items()},
         "hbm_frac_whole_call": round(bbytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "dominant_kernel": max(bk, key=bk.get),
+        "dominant_kernel": dom,
+        "roofline": {"bound": "hbm", "achieved": round(cbytes / (cms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "ll_bwd_chunk", "kernel_avg_ms": round(cms, 5), "algorithmic_bytes": cbytes},
     }
 
 
