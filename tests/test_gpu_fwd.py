@@ -258,6 +258,28 @@ def test_bf16_walk_exact_on_exactly_representable_inputs(T, chunk, group_log2):
     assert e <= 1e-5
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 16, 16384), (1, 3, 5000), (2, 8, 2048)])
+def test_one_launch_forward_publishes_every_node(B, H, T):
+    # White-box check of the one-launch forward's workspace after a run: every
+    # group's ready flag is up and no bounded wait gave up.  Layout: bf16
+    # nodes [B*H][nG][128*64], fp32 node totals [B*H][nG], int32 flags
+    # [B*H][nG], one int32 count of failed waits (each part 256-byte aligned).
+    cfg = synth.FwdConfig("nodes", B, H, T, 128, 64, 64, "bf16", 0.05, 600 + T)
+    announce(f"one-launch forward flags B={B} H={H} T={T}")
+    d = to_dev(synth.make_fwd_inputs(cfg))
+    ws = ll.alloc_workspace(B, H, T, 128, 64, 64)
+    ws.fill_(0xAB)
+    ll.fwd(d["q"], d["k"], d["v"], d["a"], d["lam"], chunk=64, workspace=ws)
+    torch.cuda.synchronize()
+    al = lambda x: (x + 255) // 256 * 256
+    BH, nG = B * H, (T + 127) // 128
+    off = al(BH * nG * 128 * 64 * 2) + al(BH * nG * 4)
+    flags = ws[off:off + BH * nG * 4].view(torch.int32)
+    fails = ws[off + al(BH * nG * 4):off + al(BH * nG * 4) + 4].view(torch.int32)
+    assert int(fails.item()) == 0
+    assert bool((flags == 1).all()), int((flags != 1).sum())
+
+
 @pytest.mark.parametrize("as_handle", [False, True])
 def test_side_stream_workspace_is_not_reused_early(as_handle, monkeypatch):
     """The binding allocates the workspace on torch's current stream and the
