@@ -114,19 +114,27 @@ def auto_group_log2(cfg) -> int:
     return g
 
 
-def stack_algorithmic(cfg, g: int, Lcap: int):
+def one_launch(cfg, group_log2: int) -> bool:
+    """Whether the library runs this forward (and prefill) as its one-launch
+    kernel: bf16, dk 128, dv 64, more than one 128-token group, automatic
+    groups."""
+    return group_log2 < 0 and cfg.dtype == "bf16" and cfg.dk == 128 and cfg.dv == 64 and cfg.T > 128
+
+
+def stack_algorithmic(cfg, g: int, Lcap: int, fused: bool = False):
     """Algorithmic bytes of the prefill's stack export for the prompt's last
     position p = T-1: one stored block state (input dtype) per occupied
     bucket of whole groups, the group decay totals between those buckets and
-    the last group, k, v and a of the keys of the last group (the finer
-    buckets and the decays inside it), and the occupied slots and their
-    log-scales written in fp32."""
+    the last group (after the one-launch forward, whose groups are 128
+    tokens: one Fenwick node total per such bucket), k, v and a of the keys
+    of the last group (the finer buckets and the decays inside it), and the
+    occupied slots and their log-scales written in fp32."""
     e = 2 if cfg.dtype == "bf16" else 4
     p = cfg.T - 1
-    lgc = (cfg.chunk << g).bit_length() - 1
+    lgc = 7 if fused else (cfg.chunk << g).bit_length() - 1
     t0 = (p >> lgc) << lgc
-    n_groups = t0 >> lgc
     whole = bin(p >> lgc).count("1")
+    n_groups = whole if fused else t0 >> lgc
     occ = 1 + bin(p).count("1")
     per_head = whole * cfg.dk * cfg.dv * e + 4 * n_groups + (p + 1 - t0) * ((cfg.dk + cfg.dv) * e + 4) \
         + occ * (cfg.dk * cfg.dv * 4 + 4)
@@ -611,7 +619,7 @@ def main():
     pstats = ll.profile_end()
     sl, sms = pstats["ll_prefill_stack"]
     stack_ms = sms / sl
-    sbytes = stack_algorithmic(cfg, g_used, Lcap)
+    sbytes = stack_algorithmic(cfg, g_used, Lcap, fused=one_launch(cfg, args.group_log2))
     stack_gbs = sbytes / (stack_ms * 1e-3) / 1e9
     log(f"prefill: {pre_ms:.4f} ms/step (forward alone {fwd_ms:.4f}); stack kernel {stack_ms:.4f} ms, "
         f"{stack_gbs:.1f} GB/s")

@@ -269,8 +269,9 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
         overlaps(out, nv, a, na) || overlaps(out, nv, lambda, nl))
         return fail(LL_EINVAL, "%s: out aliases an input", who);
     const ll::FwdPlan plan = ll::fwd_plan(B, H, T, dk, dv, chunk, group_log2, 4);
-    // The plain forward with automatic groups runs as one launch where it can.
-    const bool fused = !so && group_log2 < 0 && ll::fused_supported(bf16, dk, dv, T, L);
+    // The forward with automatic groups runs as one launch where it can (the
+    // prefill's stack then reads the one-launch forward's Fenwick nodes).
+    const bool fused = group_log2 < 0 && ll::fused_supported(bf16, dk, dv, T, L);
     const size_t need = fused ? ll::fused_workspace_bytes(B, H, T, dk, dv) : plan.bytes;
     if (use_scratch && need > 0) {
         // the library's own scratch stands in for the workspace argument
@@ -302,7 +303,7 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
             return fail(LL_EINVAL, "%s: state must be 16-byte and logscale 4-byte aligned", who);
         const size_t nst = bh * so->Lcap * dk * dv * 4, nls = bh * so->Lcap * 4;
         const void *others[] = {q, k, v, a, lambda, out, workspace};
-        const size_t sizes[] = {nq, nq, nv, na, nl, nv, plan.bytes};
+        const size_t sizes[] = {nq, nq, nv, na, nl, nv, need};
         for (int i = 0; i < 7; ++i)
             if (overlaps(so->state, nst, others[i], sizes[i]) || overlaps(so->logscale, nls, others[i], sizes[i]))
                 return fail(LL_EINVAL, "%s: state and logscale must not alias the inputs, out or the workspace", who);
@@ -321,6 +322,18 @@ static ll_status run_fwd(const char *who, const void *q, const void *k, const vo
         hipError_t e = ll::fused_launch(args, s);
         if (e != hipSuccess)
             return fail(LL_EDEVICE, "%s: launch failed: %s", who, hipGetErrorString(e));
+        if (so) {
+            const ll::FusedNodes fn = ll::fused_nodes(args);
+            ll::StackArgs sa{k, v, a, fn.node, fn.gamN, so->state, so->logscale, (int)bh, T, dk, dv, fn.lg, fn.nG,
+                             0, 0, so->Lcap, bf16, true};
+            sa.rqk = H / Hqk;
+            sa.lens = so->lens;
+            sa.H = H;
+            sa.fused = true;
+            e = ll::stack_launch(sa, s);
+            if (e != hipSuccess)
+                return fail(LL_EDEVICE, "%s: stack launch failed: %s", who, hipGetErrorString(e));
+        }
         return ok();
     }
     bool nat = false;

@@ -772,6 +772,16 @@ bool fused_supported(bool bf16, int dk, int dv, int T, int L)
            (int64_t)T * 128 * 2 < ((int64_t)1 << 31) && (int64_t)T * L * 4 < ((int64_t)1 << 31);
 }
 
+FusedNodes fused_nodes(const FwdArgs &A)
+{
+    using F = fz::Cfg<128, 64>;
+    const size_t BH = (size_t)A.B * A.H;
+    const int nG = (A.T + F::TG - 1) / F::TG;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const char *p = static_cast<const char *>(A.workspace);
+    return FusedNodes{p, reinterpret_cast<const float *>(p + al(BH * nG * F::NODE * 2)), nG, F::LTG};
+}
+
 hipError_t fused_launch(const FwdArgs &A, hipStream_t s)
 {
     using F = fz::Cfg<128, 64>;

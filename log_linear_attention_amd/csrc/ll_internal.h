@@ -63,6 +63,15 @@ hipError_t fwd_launch(const FwdArgs &args, const FwdPlan &plan, hipStream_t stre
 size_t fused_workspace_bytes(int B, int H, int T, int dk, int dv);
 bool fused_supported(bool bf16, int dk, int dv, int T, int L);
 hipError_t fused_launch(const FwdArgs &args, hipStream_t stream);
+// After fused_launch: the Fenwick nodes (bf16, fragment order, dk natural
+// inside a fragment lane, each decayed to its last group's end) and their
+// log-decay totals, [BH][nG] each, in the launch's workspace.
+struct FusedNodes {
+    const void *node;
+    const float *gamN;
+    int nG, lg;   // groups, log2 of the group length in tokens
+};
+FusedNodes fused_nodes(const FwdArgs &args);
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -94,6 +103,10 @@ struct StackArgs {
     // Per-sequence prompt lengths [BH / H] on the device (NULL: all T).
     const int *lens = nullptr;
     int H = 1;
+    // Dg and Gam are the one-launch forward's Fenwick nodes and node totals
+    // (a bucket of whole groups is the node of its last group; lgc = log2 of
+    // the group length, nG groups; nL, nLeft unused; nat must be true).
+    bool fused = false;
 };
 
 bool stack_supported(bool bf16, int dk, int dv);

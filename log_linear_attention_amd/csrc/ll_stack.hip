@@ -14,7 +14,8 @@
 //
 // A bucket of at least one group (G*C keys) is exactly one of the left-child
 // block states the forward's tree has stored for its chunk walk (decayed to
-// the block's end, in fragment order and the input dtype), so it is copied
+// the block's end, in fragment order and the input dtype), or, after the
+// one-launch forward, the Fenwick node of its last group, so it is copied
 // out in row-major order.  A smaller bucket lies inside the prompt's last
 // group and is summed from k, v and a: the decay-weighted keys and the values
 // are staged in LDS and contracted over keys with fp32 MFMA.
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
                                                         const float *__restrict__ Gam, int Tlen, int lgc, int nG,
                                                         int nL, int nLeft, int nat, float *__restrict__ state,
                                                         float *__restrict__ logscale, int Lcap, int rqk,
-                                                        const int *__restrict__ lens, int H)
+                                                        const int *__restrict__ lens, int H, int fused)
 {
     using T = typename D::T;
     constexpr int DK = D::DK, DV = D::DV, VEC = D::VEC;
@@ -162,8 +163,16 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
     float gt = 0.f;
     if (whole) {
         const int gl = p >> lgc;
-        for (int j = (hi >> lgc) + tid; j < gl; j += D::NT)
-            gt += Gam[(size_t)bh * nG + j];
+        if (fused) {
+            // the groups between the bucket and p's group are the Fenwick
+            // nodes of the set bits of gl below the bucket's bit
+            for (int kk = tid; kk < l - lgc - 1; kk += D::NT)
+                if ((gl >> kk) & 1)
+                    gt += Gam[(size_t)bh * nG + ((gl >> (kk + 1)) << (kk + 1)) + (1 << kk) - 1];
+        } else {
+            for (int j = (hi >> lgc) + tid; j < gl; j += D::NT)
+                gt += Gam[(size_t)bh * nG + j];
+        }
     }
     for (int t = max(hi, t0) + tid; t <= p; t += D::NT)
         gt += a[head + t];
@@ -198,10 +207,16 @@ __global__ __launch_bounds__(256) void ll_prefill_stack(const typename D::T *__r
         // index 2 * (gl >> (pl + 1)); the tree stores level pl's left children
         // after those of the levels below it.
         const int pl = l - lgc - 1, gl = p >> lgc;
-        size_t off = 0;
-        for (int r = 0; r < pl; ++r)
-            off += ((nL >> r) + 1) >> 1;
-        const T *blk = Dg + ((size_t)bh * nLeft + off + (gl >> (pl + 1))) * DK * DV;
+        const T *blk;
+        if (fused) {
+            // the node of the bucket's last group (2^pl groups ending there)
+            blk = Dg + ((size_t)bh * nG + ((gl >> (pl + 1)) << (pl + 1)) + (1 << pl) - 1) * DK * DV;
+        } else {
+            size_t off = 0;
+            for (int r = 0; r < pl; ++r)
+                off += ((nL >> r) + 1) >> 1;
+            blk = Dg + ((size_t)bh * nLeft + off + (gl >> (pl + 1))) * DK * DV;
+        }
         const int r = tid / (DV / D::NE), c0 = (tid % (DV / D::NE)) * D::NE;
         const int row = row0 + r, u = row / D::KB;
         int qd, e;
@@ -333,7 +348,7 @@ static hipError_t launch_stack_t(const StackArgs &A, hipStream_t s)
     const dim3 grid(A.BH * (DK / D::RS), A.Lcap);
     hipExtLaunchKernelGGL(ll_prefill_stack<D>, grid, dim3(D::NT), 0, s, pe.start, pe.stop, 0, (const T *)A.k,
                           (const T *)A.v, A.a, (const T *)A.Dg, A.Gam, A.T, A.lgc, A.nG, A.nL, A.nLeft, (int)A.nat,
-                          A.state, A.logscale, A.Lcap, A.rqk, A.lens, A.H);
+                          A.state, A.logscale, A.Lcap, A.rqk, A.lens, A.H, (int)A.fused);
     return hipGetLastError();
 }
 
