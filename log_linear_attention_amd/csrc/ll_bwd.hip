@@ -13,9 +13,13 @@
 // parts (Portuguese page §2 "Forma Recorrente e Paralela").
 //
 // How each part is computed:
-//  - dq is the forward itself with the roles q <- do, k <- v, v <- k (it
-//    weights by lambda of the output position, as dq does); the host runs the
-//    forward kernels for it.
+//  - dq: with bf16 inputs the chunk kernel forms it.  Inside the chunk,
+//    dQ = (M.dP) K from the same masked matrix as dk; at a chunk level where
+//    the chunk reads a left block, Y = D do_t from that block's state D gives
+//    both dlambda_t = exp(decay) q_t . Y_t and dq_t += lambda_t exp(decay) Y_t.
+//    Otherwise dq is the forward itself with the roles q <- do, k <- v,
+//    v <- k (it weights by lambda of the output position, as dq does), run on
+//    the forward kernels.
 //  - Inside a chunk, the masked C x C matrices S = Q K^T and dP = dO V^T give
 //    dk and dv ((M.dP)^T Q, (M.S)^T dO) and the in-chunk levels of dlambda
 //    (row sums of exp(decay) S dP over each level's key range).
@@ -117,6 +121,14 @@ struct BwSmem : BwSmemBase<B> {
     __attribute__((aligned(16))) typename B::T st[BwSt<B>::SST ? B::SSZ : 8];
 };
 
+// bf16 with the level states staged in LDS: the chunk kernel also forms dq
+// (the in-chunk part from (M . dP) K, the chunk levels from the left block
+// states it reads for dlambda), so no separate dq pass runs.
+template <class B>
+struct BwDq {
+    static constexpr bool on = B::TRD && BwSt<B>::SST;
+};
+
 // Operand fragment: EPL consecutive elements of row `row` starting at unit u.
 template <class B>
 __device__ __forceinline__ typename B::Frag frag(const typename B::T *base, int ld, int row, int u, int qd)
@@ -182,7 +194,8 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     const typename B::T *__restrict__ q, const typename B::T *__restrict__ k, const typename B::T *__restrict__ v,
     const typename B::T *__restrict__ dout, const float *__restrict__ a, const float *__restrict__ lamg,
     const typename B::T *__restrict__ Dg, const double *__restrict__ Gp, const typename B::T *__restrict__ W1,
-    const typename B::T *__restrict__ W2, typename B::T *__restrict__ dkg, typename B::T *__restrict__ dvg,
+    const typename B::T *__restrict__ W2, typename B::T *__restrict__ dqg, typename B::T *__restrict__ dkg,
+    typename B::T *__restrict__ dvg,
     float *__restrict__ dlamg, float *__restrict__ daloc, float *__restrict__ Mq, float *__restrict__ Mk, int Tlen,
     int L, int N, int nL, int nLeft, int NB)
 {
@@ -389,6 +402,23 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     }
     // The accumulators hold dK^T and dV^T tiles: A = columns (dk / dv index,
     // rows 4*qd+i), B = keys (column li).
+    constexpr bool FDQ = BwDq<B>::on;
+    // dq of this wave's token tile (as a query) and dk tiles: in-chunk
+    // dQ^T = K^T (M . dP)^T, contraction over the keys s (rows of K and of
+    // (M . dP)^T, both read with transpose reads)
+    floatx4 dQ[B::KPW];
+#pragma unroll
+    for (int j = 0; j < B::KPW; ++j)
+        dQ[j] = zero4();
+    if constexpr (FDQ) {
+#pragma unroll
+        for (int u = 0; u < B::NUC; ++u) {
+            const Frag pdt = tr_frag(&sm.PdT[0][0], B::LC, B::KB * u, 16 * kt, li, qd);
+#pragma unroll
+            for (int j = 0; j < B::KPW; ++j)
+                mma_unit(dQ[j], tr_frag(&sm.Ks[0][0], B::LQ, B::KB * u, 16 * (cg + B::NCG * j), li, qd), pdt);
+        }
+    }
 
     // ---- chunk levels -------------------------------------------------------
     // pki: this lane's part of k_s . (dk_s from later chunks), fp32
@@ -452,7 +482,14 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                     const int i = tid + B::NTC * j;
                     if (i < np) {
                         T *dst;
-                        if (kind == 1) {
+                        if (kind == 1 && FDQ) {
+                            // the block state as a row-major [dv][dk] tile: piece i is
+                            // fragment f = i / 64 (dv tile f / NUK, dk unit f % NUK), lane
+                            // i % 64 (dv row, 8 consecutive dk)
+                            const int f = i >> 6, l = i & 63;
+                            const int e = 16 * (f / B::NUK) + (l & 15), d0 = B::KB * (f % B::NUK) + VEC * (l >> 4);
+                            dst = sm.st + e * B::LW2 + d0;
+                        } else if (kind == 1) {
                             dst = sm.st + (size_t)i * VEC;                       // fragment order
                         } else if (i < HP) {
                             const int e0 = i * VEC;
@@ -484,7 +521,36 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         } else if (kind != 0) {
             state_ptr(m, kind, g1, g2);
         }
-        if (kind == 1) {
+        if (kind == 1 && FDQ) {
+            if constexpr (FDQ) {
+                // query side -> dlambda level LOGC + m and dq.  Y^T = D dO^T: A = D
+                // (rows d, transpose reads of the [dv][dk] copy), B = dO (columns
+                // t); this wave takes query tile kt and dk tiles cg, cg + NCG, ...
+                // dlambda_t = exp(A_t + off) q_t . Y_t; dq_t += lambda_t exp(A_t + off) Y_t.
+                const int t = 16 * kt + li;
+                const float fac = sm.lam[t][B::LOGC + m] * __expf(sm.Aloc[t] + sm.off[m]);
+                float xs = 0.f;
+#pragma unroll
+                for (int j = 0; j < B::KPW; ++j) {
+                    const int dt = cg + B::NCG * j;
+                    floatx4 Y = zero4();
+#pragma unroll
+                    for (int u = 0; u < B::NUV; ++u)
+                        mma_unit(Y, tr_frag(sm.st, B::LW2, B::KB * u, 16 * dt, li, qd),
+                                 lds_frag(&sm.dOs[0][0], B::LV, t, B::KB * u, qd));
+                    // Y[i] = (D dO^T)[d = 16 dt + 4 qd + i][t]
+                    const floatx4 q4 = ld4(&sm.Qs[t][16 * dt + 4 * qd]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xs += Y[i] * q4[i];
+                    dQ[j] += fac * Y;
+                }
+                xs += __shfl_xor(xs, 16, 64);
+                xs += __shfl_xor(xs, 32, 64);
+                if (qd == 0)
+                    sm.lpart[m][cg][t] = xs;
+            }
+        } else if (kind == 1) {
             // query side -> dlambda level LOGC + m.  X^T = D^T Q^T: A = D^T
             // (rows e), B = Q (columns t); this wave takes query tile kt and
             // value tiles cg, cg + NCG, ...
@@ -577,6 +643,11 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     const int s = 16 * kt + li;
     float pk = pki;
     if (s < nv) {
+        if constexpr (FDQ) {
+#pragma unroll
+            for (int j = 0; j < B::KPW; ++j)
+                put4(&dqg[(row0 + s) * DK + 16 * (cg + B::NCG * j) + 4 * qd], dQ[j]);
+        }
 #pragma unroll
         for (int j = 0; j < B::KPW; ++j)
             put4(&dkg[(row0 + s) * DK + 16 * (cg + B::NCG * j) + 4 * qd], dK[j]);
@@ -1095,11 +1166,14 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     hipError_t e = fwd_launch(tree, P.tree, s, nullptr);
     if (e != hipSuccess)
         return e;
-    // 2. dq: the forward with q <- do, k <- v, v <- k
-    FwdArgs fq{A.dout, A.v, A.k, A.a, A.lam, A.gq, A.B, A.H, A.T, DV, DK, C, A.L, A.bf16, ws + P.off_fq};
-    e = fwd_launch(fq, P.fq, s, nullptr);
-    if (e != hipSuccess)
-        return e;
+    // 2. dq: the forward with q <- do, k <- v, v <- k (unless the chunk
+    //    kernel forms it)
+    if (!BwDq<B>::on) {
+        FwdArgs fq{A.dout, A.v, A.k, A.a, A.lam, A.gq, A.B, A.H, A.T, DV, DK, C, A.L, A.bf16, ws + P.off_fq};
+        e = fwd_launch(fq, P.fq, s, nullptr);
+        if (e != hipSuccess)
+            return e;
+    }
     const float *Gam = reinterpret_cast<const float *>(ws + P.off_tree + P.tree.off_Gam);
     const T *Dg = reinterpret_cast<const T *>(ws + P.off_tree + P.tree.off_Dg);
     float *Wp = reinterpret_cast<float *>(ws + P.off_wp);
@@ -1134,7 +1208,7 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     ProfEvents pe = prof_events("ll_bwd_chunk");
     hipExtLaunchKernelGGL(ll_bwd_chunk<B>, dim3(BH * N), dim3(B::NTC), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
                           (const T *)A.k, (const T *)A.v, (const T *)A.dout, A.a, A.lam, Dg, (const double *)Gp, (const T *)W1,
-                          (const T *)W2, (T *)A.gk, (T *)A.gv, A.glam, daloc, Mq, Mk, A.T, A.L, N, P.tree.nL,
+                          (const T *)W2, (T *)A.gq, (T *)A.gk, (T *)A.gv, A.glam, daloc, Mq, Mk, A.T, A.L, N, P.tree.nL,
                           P.tree.nLeft, P.NB);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
