@@ -193,7 +193,8 @@ template <class B>
 __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     const typename B::T *__restrict__ q, const typename B::T *__restrict__ k, const typename B::T *__restrict__ v,
     const typename B::T *__restrict__ dout, const float *__restrict__ a, const float *__restrict__ lamg,
-    const typename B::T *__restrict__ Dg, const double *__restrict__ Gp, const typename B::T *__restrict__ W1,
+    const typename B::T *__restrict__ Dg, const typename B::T *__restrict__ Nd, int gq,
+    const double *__restrict__ Gp, const typename B::T *__restrict__ W1,
     const typename B::T *__restrict__ W2, typename B::T *__restrict__ dqg, typename B::T *__restrict__ dkg,
     typename B::T *__restrict__ dvg,
     float *__restrict__ dlamg, float *__restrict__ daloc, float *__restrict__ Mq, float *__restrict__ Mk, int Tlen,
@@ -448,10 +449,18 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     };
     auto state_ptr = [&](int m, int kind, const T *&p1, const T *&p2) {
         if (kind == 1) {
-            size_t offp = 0;
-            for (int r = 0; r < m - 1; ++r)
-                offp += ((nL >> r) + 1) >> 1;
-            p1 = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
+            if (m <= gq) {
+                // inside a group of 2^gq chunks: the Fenwick node of the left
+                // block's last chunk
+                const int e = ((c >> m) << m) + (1 << (m - 1)) - 1;
+                p1 = Nd + ((size_t)bh * N + e) * DK * DV;
+            } else {
+                // a left block of the tree over groups, at level m - 1 - gq
+                size_t offp = 0;
+                for (int r = 0; r < m - 1 - gq; ++r)
+                    offp += ((nL >> r) + 1) >> 1;
+                p1 = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
+            }
             p2 = p1;
         } else {
             size_t ob = 0;
@@ -1159,11 +1168,19 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     const int BH = A.B * A.H;
     char *ws = static_cast<char *>(A.workspace);
     const int N = (A.T + C - 1) / C;
-    // 1. group states (one chunk per group) and the tree over chunks
+    // 1. left block states: with the chunk kernel forming dq (bf16), a tree
+    //    over groups of up to 8 chunks plus the Fenwick nodes inside each
+    //    group; otherwise a tree over chunks (one chunk per group)
+    const bool g8 = BwDq<B>::on;
+    const FwdPlan &TP = g8 ? P.tree8 : P.tree;
     FwdArgs tree{nullptr, A.k, A.v, A.a, A.lam, nullptr, A.B, A.H, A.T, DK, DV, C, A.L, A.bf16, ws + P.off_tree};
     tree.tree_only = true;
     tree.tree_nat = A.bf16;
-    hipError_t e = fwd_launch(tree, P.tree, s, nullptr);
+    if (g8) {
+        tree.tree_nodes = ws + P.off_tree + P.off_nd;
+        tree.tree_gamc = reinterpret_cast<float *>(ws + P.off_tree + P.off_gamc);
+    }
+    hipError_t e = fwd_launch(tree, TP, s, nullptr);
     if (e != hipSuccess)
         return e;
     // 2. dq: the forward with q <- do, k <- v, v <- k (unless the chunk
@@ -1174,8 +1191,11 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
         if (e != hipSuccess)
             return e;
     }
-    const float *Gam = reinterpret_cast<const float *>(ws + P.off_tree + P.tree.off_Gam);
-    const T *Dg = reinterpret_cast<const T *>(ws + P.off_tree + P.tree.off_Dg);
+    // chunk totals (the tree's leaves are chunks, or the node pass wrote them)
+    const float *Gam = g8 ? reinterpret_cast<const float *>(ws + P.off_tree + P.off_gamc)
+                          : reinterpret_cast<const float *>(ws + P.off_tree + P.tree.off_Gam);
+    const T *Dg = reinterpret_cast<const T *>(ws + P.off_tree + TP.off_Dg);
+    const T *Nd = g8 ? reinterpret_cast<const T *>(ws + P.off_tree + P.off_nd) : nullptr;
     float *Wp = reinterpret_cast<float *>(ws + P.off_wp);
     T *W1 = reinterpret_cast<T *>(ws + P.off_w1);
     T *W2 = reinterpret_cast<T *>(ws + P.off_w2);
@@ -1207,9 +1227,9 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     // 4. chunk kernel
     ProfEvents pe = prof_events("ll_bwd_chunk");
     hipExtLaunchKernelGGL(ll_bwd_chunk<B>, dim3(BH * N), dim3(B::NTC), 0, s, pe.start, pe.stop, 0, (const T *)A.q,
-                          (const T *)A.k, (const T *)A.v, (const T *)A.dout, A.a, A.lam, Dg, (const double *)Gp, (const T *)W1,
-                          (const T *)W2, (T *)A.gq, (T *)A.gk, (T *)A.gv, A.glam, daloc, Mq, Mk, A.T, A.L, N, P.tree.nL,
-                          P.tree.nLeft, P.NB);
+                          (const T *)A.k, (const T *)A.v, (const T *)A.dout, A.a, A.lam, Dg, Nd, g8 ? TP.g : 0,
+                          (const double *)Gp, (const T *)W1, (const T *)W2, (T *)A.gq, (T *)A.gk, (T *)A.gv, A.glam,
+                          daloc, Mq, Mk, A.T, A.L, N, TP.nL, TP.nLeft, P.NB);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     // 5. da
@@ -1291,11 +1311,16 @@ BwdPlan bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int rqk)
     const size_t BH = (size_t)B * H;
     const int N = (T + chunk - 1) / chunk;
     p.tree = fwd_plan(B, H, T, dk, dv, chunk, 0, 4);
+    p.g8 = N >= 8 ? 3 : N >= 4 ? 2 : N >= 2 ? 1 : 0;
+    p.tree8 = fwd_plan(B, H, T, dk, dv, chunk, p.g8, 4);
+    p.off_nd = al256(p.tree8.bytes);
+    p.off_gamc = al256(p.off_nd + BH * (size_t)N * dk * dv * 2);
+    const size_t tree_bytes = std::max(p.tree.bytes, al256(p.off_gamc + BH * (size_t)N * 4));
     p.fq = fwd_plan(B, H, T, dv, dk, chunk, -1, 4);
     bwd_counts(N, p.NP, p.NB, 8);
     const size_t st = (size_t)dk * dv;
     p.off_tree = 0;
-    p.off_fq = al256(p.off_tree + p.tree.bytes);
+    p.off_fq = al256(p.off_tree + tree_bytes);
     p.off_wp = al256(p.off_fq + p.fq.bytes);
     p.off_w1 = al256(p.off_wp + BH * p.NP * st * 4);
     p.off_w2 = al256(p.off_w1 + BH * p.NB * st * 4);

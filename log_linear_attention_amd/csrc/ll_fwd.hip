@@ -336,26 +336,27 @@ struct StateRegs {
     float a;
 };
 
+// nrows: valid rows of the chunk (rows past it read as zero).
 template <class F>
 __device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T *k, const typename F::T *v,
-                                           const float *a, size_t row0, size_t krow0, int tid)
+                                           const float *a, size_t row0, size_t krow0, int tid, int nrows = F::C)
 {
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
 #pragma unroll
     for (int i = 0; i < F::NQ; ++i) {
         const int idx = tid + i * F::NT;
         r.k[i] = zero16();
-        if (idx < F::QVEC)
+        if (idx < F::QVEC && idx / KPR < nrows)
             r.k[i] = *reinterpret_cast<const uint4 *>(k + (krow0 + idx / KPR) * F::DK + (idx % KPR) * F::VEC);
     }
 #pragma unroll
     for (int i = 0; i < F::NV; ++i) {
         const int idx = tid + i * F::NT;
         r.v[i] = zero16();
-        if (idx < F::VVEC)
+        if (idx < F::VVEC && idx / VPR < nrows)
             r.v[i] = *reinterpret_cast<const uint4 *>(v + (row0 + idx / VPR) * F::DV + (idx % VPR) * F::VEC);
     }
-    r.a = (tid < F::C) ? a[row0 + tid] : 0.f;
+    r.a = (tid < F::C && tid < nrows) ? a[row0 + tid] : 0.f;
 }
 
 template <class F>
@@ -363,12 +364,17 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
                                                         const typename F::T *__restrict__ v,
                                                         const float *__restrict__ a, int Tlen, int g, int nG,
                                                         int nL, int rqk, float *__restrict__ Sg,
-                                                        float *__restrict__ Gam)
+                                                        float *__restrict__ Gam, typename F::T *__restrict__ Nd,
+                                                        float *__restrict__ GamC, int N)
 {
     using Frag = typename F::Frag;
     __shared__ StateSmem<F> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
-    const int bh = blockIdx.x / nL, sg = blockIdx.x % nL;
+    // Node mode (Nd set): every group is walked (nG workgroups per head), the
+    // Fenwick nodes inside the group and the chunk totals are written, and
+    // the group state only for the nL groups that are tree leaves.
+    const int ngw = Nd ? nG : nL;
+    const int bh = blockIdx.x / ngw, sg = blockIdx.x % ngw;
     const int G = 1 << g;
     const size_t hrow = (size_t)bh * Tlen, krow = (size_t)(bh / rqk) * Tlen;   // k is shared by rqk heads
     constexpr int KPR = F::DK / F::VEC, VPR = F::DV / F::VEC;
@@ -387,9 +393,17 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
         S[rt] = zero4();
     float gsum = 0.f;
 
+    // node mode: the previous chunk's own state (for nodes of two chunks)
+    floatx4 Xp[F::NDT];
+#pragma unroll
+    for (int rt = 0; rt < F::NDT; ++rt)
+        Xp[rt] = zero4();
+    const int nci = Nd ? min(G, N - sg * G) : G;   // chunks of this group
+    auto rows_of = [&](int ci) { return min(F::C, Tlen - (sg * G + ci) * F::C); };
+
     StateRegs<F> pf;
-    state_load<F>(pf, k, v, a, hrow + (size_t)sg * G * F::C, krow + (size_t)sg * G * F::C, tid);
-    for (int ci = 0; ci < G; ++ci) {
+    state_load<F>(pf, k, v, a, hrow + (size_t)sg * G * F::C, krow + (size_t)sg * G * F::C, tid, rows_of(0));
+    for (int ci = 0; ci < nci; ++ci) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < F::NQ; ++i) {
@@ -404,9 +418,9 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
                 store_row_vec<F>(sm.Vs, F::LDV, sm.Vts, idx / VPR, idx % VPR, pf.v[i]);
         }
         scan_decay<F>(pf.a, sm.Aloc, &sm.gch, tid);
-        if (ci + 1 < G)
+        if (ci + 1 < nci)
             state_load<F>(pf, k, v, a, hrow + ((size_t)sg * G + ci + 1) * F::C, krow + ((size_t)sg * G + ci + 1) * F::C,
-                          tid);
+                          tid, rows_of(ci + 1));
         __syncthreads();
         const float gch = sm.gch;
         const float dec = __expf(gch);
@@ -414,15 +428,54 @@ __global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__r
 #pragma unroll
         for (int u = 0; u < F::NUC; ++u)
             vs[u] = scale_tokens<F>(v_frag<F>(sm, w, u, li, qd), u, sm.Aloc, gch, qd);
+        if (!Nd) {
 #pragma unroll
-        for (int rt = 0; rt < F::NDT; ++rt) {
-            S[rt] *= dec;
+            for (int rt = 0; rt < F::NDT; ++rt) {
+                S[rt] *= dec;
 #pragma unroll
-            for (int u = 0; u < F::NUC; ++u)
-                mma_unit(S[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
+                for (int u = 0; u < F::NUC; ++u)
+                    mma_unit(S[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
+            }
+        } else if constexpr (F::TR) {
+            // this chunk's own state X, then S = exp(gch) S + X; the Fenwick
+            // node of chunk ci inside the group: X (ci even), X + exp(gch) X of
+            // the previous chunk (ci = 1 mod 4), S (ci = 3, chunks 0 .. 3)
+            floatx4 X[F::NDT];
+#pragma unroll
+            for (int rt = 0; rt < F::NDT; ++rt) {
+                X[rt] = zero4();
+#pragma unroll
+                for (int u = 0; u < F::NUC; ++u)
+                    mma_unit(X[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
+                S[rt] = dec * S[rt] + X[rt];
+            }
+            const int cc = sg * G + ci;   // chunk index
+            if (tid == 0)
+                GamC[(size_t)bh * N + cc] = gch;
+            if (ci < G - 1 && cc < N - 1) {
+                // natural fragment order: fragment (dv tile w, dk unit rt / 2), lane
+                // li + 16 (2 (rt & 1) + qd / 2), elements 4 (qd & 1) ..
+                typename F::T *nd = Nd + ((size_t)bh * N + cc) * F::DK * F::DV;
+#pragma unroll
+                for (int rt = 0; rt < F::NDT; ++rt) {
+                    floatx4 x = (ci & 1) == 0 ? X[rt] : (ci & 3) == 1 ? X[rt] + dec * Xp[rt] : S[rt];
+                    const int f = w * F::NUK + rt / 2;
+                    const int l = li + 16 * (2 * (rt & 1) + (qd >> 1));
+                    bf16x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o[r] = (__bf16)x[r];
+                    *reinterpret_cast<bf16x4 *>(nd + (size_t)(f * 64 + l) * 8 + 4 * (qd & 1)) = o;
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < F::NDT; ++rt)
+                Xp[rt] = X[rt];
         }
         gsum += gch;
     }
+    if (sg >= nL)
+        return;   // the last group (node mode): not a tree leaf
     float *dst = Sg + ((size_t)bh * nL + sg) * F::DK * F::DV;
 #pragma unroll
     for (int rt = 0; rt < F::NDT; ++rt)
@@ -2168,10 +2221,12 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         use_ws = A.tree_nat;
     if (nat_blocks)
         *nat_blocks = use_ws;
-    if (P.nL > 0) {
+    if (P.nL > 0 || (A.tree_only && A.tree_nodes)) {
         ProfEvents pe = prof_events("ll_group_state");
-        hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * P.nL), dim3(F::NT), 0, s, pe.start, pe.stop, 0,
-                              (const T *)A.k, (const T *)A.v, A.a, A.T, P.g, P.nG, P.nL, A.rqk, Sg, Gam);
+        const bool nodes = A.tree_only && A.tree_nodes;
+        hipExtLaunchKernelGGL(ll_group_state<F>, dim3(BH * (nodes ? P.nG : P.nL)), dim3(F::NT), 0, s, pe.start,
+                              pe.stop, 0, (const T *)A.k, (const T *)A.v, A.a, A.T, P.g, P.nG, P.nL, A.rqk, Sg, Gam,
+                              nodes ? (T *)A.tree_nodes : nullptr, nodes ? A.tree_gamc : nullptr, P.N);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -2183,6 +2238,7 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
                           reinterpret_cast<float *>(ws + P.off_gtot) + (size_t)BH * ntile_max};
         const float *leaves = Sg, *gleaves = Gam;
         int nleaves = P.nL, lstride = P.nL, gstride = P.nG, p0 = 0, ping = 0;
+        // (node mode with a single group: no tree)
         while (nleaves > 0) {
             const int ntiles = (nleaves + 63) / 64;
             const int complete = nleaves / 64;

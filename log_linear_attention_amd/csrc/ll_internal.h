@@ -36,6 +36,13 @@ struct FwdArgs {
     // when tree_nat is set (bf16 only).
     bool tree_only = false;
     bool tree_nat = false;
+    // With tree_only, bf16 and groups of at most 8 chunks: also the Fenwick
+    // nodes inside each group (the node of chunk e covers the 2^z chunks
+    // ending at e, z its trailing one bits; bf16 [B*H][N][dk*dv] in the
+    // natural fragment order) and every chunk's total log-decay
+    // ([B*H][N] float32); every group, the last one included, is walked.
+    void *tree_nodes = nullptr;
+    float *tree_gamc = nullptr;
     // Heads that share one q/k head: q and k are [B, H / rqk, T, dk] and
     // head h reads q/k head h / rqk.
     int rqk = 1;
@@ -128,8 +135,12 @@ struct BwdArgs {
 // k, v; the forward that forms dq; the W pieces and sums; the in-chunk part
 // of da and the per-level pair masses of every chunk.
 struct BwdPlan {
-    FwdPlan tree, fq;
-    int NP = 0, NB = 0;
+    // tree: one chunk per group (float32 inputs); tree8: groups of up to 8
+    // chunks with the Fenwick nodes inside each group (bf16 inputs), its
+    // nodes and chunk totals at off_nd and off_gamc inside the tree region
+    FwdPlan tree, tree8, fq;
+    int NP = 0, NB = 0, g8 = 0;
+    size_t off_nd = 0, off_gamc = 0;
     size_t off_tree = 0, off_fq = 0, off_wp = 0, off_w1 = 0, off_w2 = 0, off_pq = 0, off_mq = 0, off_mk = 0, off_gp = 0, bytes = 0;
     // shared q/k (rqk > 1): per-head copies of q, k and per-head dq, dk
     size_t off_qx = 0, off_kx = 0, off_gqx = 0, off_gkx = 0;
