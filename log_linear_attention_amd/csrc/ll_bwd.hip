@@ -470,7 +470,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             }
             const size_t wi = (size_t)bh * NB + ob + (c >> m);
             p1 = W1 + wi * DK * DV;   // W,   [dk][dv]
-            p2 = W2 + wi * DK * DV;   // W^T, [dv][dk]
+            p2 = W2 ? W2 + wi * DK * DV : p1;   // W^T, [dv][dk] (when stored)
         }
     };
     constexpr bool SST = BwSt<B>::SST;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         if constexpr (SST) {
             __syncthreads();   // the previous level's reads of the copy are done
             if (kind != 0) {
-                const int np = kind == 1 ? HP : 2 * HP;
+                const int np = kind == 1 || FDQ ? HP : 2 * HP;
 #pragma unroll
                 for (int j = 0; j < NSPT; ++j) {
                     const int i = tid + B::NTC * j;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 if (nk != 0) {
                     const T *p1, *p2;
                     state_ptr(m + 1, nk, p1, p2);
-                    const int np = nk == 1 ? HP : 2 * HP;
+                    const int np = nk == 1 || FDQ ? HP : 2 * HP;
 #pragma unroll
                     for (int j = 0; j < NSPT; ++j) {
                         const int i = tid + B::NTC * j;
@@ -612,9 +612,16 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 floatx4 X = zero4();
 #pragma unroll
                 for (int u = 0; u < B::NUK; ++u) {
-                    const Frag fw = SST ? frag<B>(sm.st + DK * B::LW1, B::LW2, 16 * et + li, u, qd)
-                                        : frag<B>(g2, DK, 16 * et + li, u, qd);
-                    mma_unit(X, fw, frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
+                    if constexpr (FDQ) {
+                        // W^T (rows e) by transpose reads of the W copy, k in the
+                        // permuted order on both operands
+                        mma_unit(X, tr_frag(sm.st, B::LW1, B::KB * u, 16 * et, li, qd),
+                                 lds_frag(&sm.Ks[0][0], B::LQ, 16 * kt + li, B::KB * u, qd));
+                    } else {
+                        const Frag fw = SST ? frag<B>(sm.st + DK * B::LW1, B::LW2, 16 * et + li, u, qd)
+                                            : frag<B>(g2, DK, 16 * et + li, u, qd);
+                        mma_unit(X, fw, frag<B>(&sm.Ks[0][0], B::LQ, 16 * kt + li, u, qd));
+                    }
                 }
                 dV[j] += dec * X;
             }
@@ -771,6 +778,8 @@ __device__ __forceinline__ void write_w(const float (*Wt)[B::DV + 4], typename B
         const int d = i / B::DV, e = i % B::DV;
         put(&w1[i], Wt[d][e]);
     }
+    if (!w2)
+        return;   // W^T not needed (the chunk kernel transposes W as it reads it)
     for (int i = tid; i < B::DK * B::DV; i += B::NT) {
         const int e = i / B::DK, d = i % B::DK;
         put(&w2[i], Wt[d][e]);
@@ -949,7 +958,7 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
     __syncthreads();
     if (np == 1) {
         const size_t wi = (size_t)bh * NB + bbase + j;
-        write_w<B>(sm.Wt, W1 + wi * DK * DV, W2 + wi * DK * DV, tid);
+        write_w<B>(sm.Wt, W1 + wi * DK * DV, W2 ? W2 + wi * DK * DV : nullptr, tid);
     } else {
         float *dst = Wp + ((size_t)bh * NP + blockIdx.x) * DK * DV;
         for (int i = tid; i < DK * DV; i += B::NT)
@@ -1009,7 +1018,7 @@ __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp,
     }
     __syncthreads();
     const size_t wi = (size_t)bh * NB + blockIdx.x;
-    write_w<B>(Wt, W1 + wi * DK * DV, W2 + wi * DK * DV, threadIdx.x);
+    write_w<B>(Wt, W1 + wi * DK * DV, W2 ? W2 + wi * DK * DV : nullptr, threadIdx.x);
 }
 
 // fp64 exclusive prefix of the chunk log-decay totals: Gp[c] = sum of
@@ -1198,7 +1207,7 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     const T *Nd = g8 ? reinterpret_cast<const T *>(ws + P.off_tree + P.off_nd) : nullptr;
     float *Wp = reinterpret_cast<float *>(ws + P.off_wp);
     T *W1 = reinterpret_cast<T *>(ws + P.off_w1);
-    T *W2 = reinterpret_cast<T *>(ws + P.off_w2);
+    T *W2 = g8 ? nullptr : reinterpret_cast<T *>(ws + P.off_w2);   // W^T, when the chunk kernel needs it
     float *daloc = reinterpret_cast<float *>(ws + P.off_pq);
     double *Gp = reinterpret_cast<double *>(ws + P.off_gp);
     if (N > 1) {
