@@ -966,6 +966,201 @@ __global__ __launch_bounds__(256) void ll_bwd_wpiece(const typename B::T *__rest
     }
 }
 
+// W states from spans (bf16): one workgroup of 8 waves per (head, aligned
+// span of WP chunks) reads each chunk's q, do, lambda and a once, and forms
+// for every level m at which the chunk lies in a right block R its share of
+//     W(R) = sum over R's queries of exp(A_t - A_e) lambda_t[LOGC + m] q_t do_t^T
+// (e the last key before R).  Blocks of at most WP chunks lie inside one span:
+// their W is written whole (bf16).  A larger block takes a float32 partial
+// from each of its spans, the pieces ll_bwd_wsum adds, at the index the piece
+// enumeration gives.  The levels are taken NL at a time (a further pass
+// re-reads the span).  Products W^T = dO^T (w q) on MFMA: wave w owns dk tile
+// w and every dv tile; q and do are read with transpose reads, and each
+// level's per-token weights scale the q fragment in registers.
+// Grid: (spans, BH).
+template <class B>
+struct WsSmem {
+    using T = typename B::T;
+    static constexpr int NL = 8;   // levels per pass (one per wave in the weight table)
+    __attribute__((aligned(16))) T Qs[B::C][B::LQ];
+    __attribute__((aligned(16))) T dOs[B::C][B::LV];
+    __attribute__((aligned(16))) float wt[NL][B::C];   // per level and token: exp(decay) lambda (0: no share)
+    float Aloc[B::C];
+};
+
+template <class B>
+__global__ __launch_bounds__(512) void ll_bwd_wspan(const typename B::T *__restrict__ q,
+                                                    const typename B::T *__restrict__ dout,
+                                                    const float *__restrict__ a, const float *__restrict__ lamg,
+                                                    const double *__restrict__ Gp, float *__restrict__ Wp,
+                                                    typename B::T *__restrict__ W1, int Tlen, int L, int N, int NP,
+                                                    int NB)
+{
+    using T = typename B::T;
+    using S = WsSmem<B>;
+    constexpr int C = B::C, DK = B::DK, DV = B::DV, VEC = B::VEC, NL = S::NL;
+    constexpr int NTW = 512;
+    static_assert(B::TRD && C <= 64 && DK == 16 * 8, "bf16, one dk tile per wave of eight");
+    static_assert(NL * 64 == NTW, "one weight per thread");
+    __shared__ S sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, qd = lane >> 4;
+    const int bh = blockIdx.y, sp = blockIdx.x;
+    const int cA = sp * B::WP, cB = min(cA + B::WP, N);
+    const int mtop = bitlen_u32((uint32_t)(N - 1));
+    const double *gp = Gp + (size_t)bh * N;
+    // first W index and first piece index of each level
+    auto bbase_of = [&](int m) {
+        int x = 0;
+        for (int r = 1; r < m; ++r)
+            x += wnblk(N, r);
+        return x;
+    };
+    auto pbase_of = [&](int m) {
+        int x = 0;
+        for (int r = 1; r < m; ++r)
+            x += wnblk(N, r) * (((1 << (r - 1)) + B::WP - 1) / B::WP);
+        return x;
+    };
+    constexpr int QP = C * DK / VEC, VP = C * DV / VEC;
+    constexpr int NQP = (QP + NTW - 1) / NTW, NVP = (VP + NTW - 1) / NTW;
+    uint4 rq[NQP], ro[NVP];
+    float av = 0.f, lv = 0.f;
+    for (int m0 = 1; m0 <= mtop; m0 += NL) {
+        floatx4 acc[NL][B::DVT];
+#pragma unroll
+        for (int l = 0; l < NL; ++l)
+#pragma unroll
+            for (int ct = 0; ct < B::DVT; ++ct)
+                acc[l][ct] = zero4();
+        // chunk cc's inputs into registers (its lambda at level m0 + wave)
+        auto issue = [&](int cc) {
+            const int t0 = cc * C, nv = min(C, Tlen - t0);
+            const size_t row0 = (size_t)bh * Tlen + t0;
+            const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int j = 0; j < NQP; ++j) {
+                const int i = tid + NTW * j;
+                rq[j] = z4;
+                if (i < QP && i / (DK / VEC) < nv)
+                    rq[j] = *reinterpret_cast<const uint4 *>(q + row0 * DK + (size_t)i * VEC);
+            }
+#pragma unroll
+            for (int j = 0; j < NVP; ++j) {
+                const int i = tid + NTW * j;
+                ro[j] = z4;
+                if (i < VP && i / (DV / VEC) < nv)
+                    ro[j] = *reinterpret_cast<const uint4 *>(dout + row0 * DV + (size_t)i * VEC);
+            }
+            const int m = m0 + w;
+            lv = (lane < nv && m <= mtop) ? lamg[(row0 + lane) * L + B::LOGC + m] : 0.f;
+            av = (w == 0 && lane < nv) ? a[row0 + lane] : 0.f;
+        };
+        issue(cA);
+        for (int cc = cA; cc < cB; ++cc) {
+            __syncthreads();   // the previous chunk's products are done with the tiles
+#pragma unroll
+            for (int j = 0; j < NQP; ++j) {
+                const int i = tid + NTW * j;
+                if (i < QP)
+                    *reinterpret_cast<uint4 *>(&sm.Qs[i / (DK / VEC)][(i % (DK / VEC)) * VEC]) = rq[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NVP; ++j) {
+                const int i = tid + NTW * j;
+                if (i < VP)
+                    *reinterpret_cast<uint4 *>(&sm.dOs[i / (DV / VEC)][(i % (DV / VEC)) * VEC]) = ro[j];
+            }
+            if (w == 0) {
+                float y = av;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float z = __shfl_up(y, d, 64);
+                    if (lane >= d)
+                        y += z;
+                }
+                if (lane < C)
+                    sm.Aloc[lane] = y;
+            }
+            const float lvc = lv;
+            __syncthreads();
+            // weight of token `lane` at level m = m0 + w: zero unless the chunk
+            // lies in the right block R of that level (R0 its first chunk)
+            {
+                const int m = m0 + w;
+                float x = 0.f;
+                if (m <= mtop && ((cc >> (m - 1)) & 1) && lane < C) {
+                    const int R0 = ((cc >> m) << m) + (1 << (m - 1));
+                    x = __expf((float)(gp[cc] - gp[R0]) + sm.Aloc[lane]) * lvc;
+                }
+                if (lane < C)
+                    sm.wt[w][lane] = x;
+            }
+            if (cc + 1 < cB)
+                issue(cc + 1);
+            __syncthreads();
+            // products: the do fragments (A, rows e) are shared by the levels
+#pragma unroll
+            for (int u = 0; u < B::NUC; ++u) {
+                bf16x8 fa[B::DVT];
+#pragma unroll
+                for (int ct = 0; ct < B::DVT; ++ct)
+                    fa[ct] = tr_frag(&sm.dOs[0][0], B::LV, B::KB * u, 16 * ct, li, qd);
+                const bf16x8 fq = tr_frag(&sm.Qs[0][0], B::LQ, B::KB * u, 16 * w, li, qd);
+#pragma unroll
+                for (int l = 0; l < NL; ++l) {
+                    const int m = m0 + l;
+                    if (m > mtop || !((cc >> (m - 1)) & 1))
+                        continue;
+                    // token of element e: KB u + 16 (e / 4) + 4 qd + e % 4
+                    const floatx4 w0 = *reinterpret_cast<const floatx4 *>(&sm.wt[l][B::KB * u + 4 * qd]);
+                    const floatx4 w1 = *reinterpret_cast<const floatx4 *>(&sm.wt[l][B::KB * u + 16 + 4 * qd]);
+                    bf16x8 fb;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        fb[e] = (__bf16)((float)fq[e] * w0[e]);
+                        fb[e + 4] = (__bf16)((float)fq[e + 4] * w1[e]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < B::DVT; ++ct)
+                        acc[l][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[ct], fb, acc[l][ct], 0, 0, 0);
+                }
+            }
+            // blocks that end with this chunk (levels whose blocks fit the span)
+#pragma unroll
+            for (int l = 0; l < NL; ++l) {
+                const int m = m0 + l;
+                if (m > mtop || (1 << (m - 1)) > B::WP || !((cc >> (m - 1)) & 1))
+                    continue;
+                const int last = ((cc >> m) << m) + (1 << m) - 1;
+                if (cc != last && cc != N - 1)
+                    continue;
+                // acc[l][ct][r] = W[d = 16 w + li][e = 16 ct + 4 qd + r]
+                const size_t wi = (size_t)bh * NB + bbase_of(m) + (cc >> m);
+                T *dst = W1 + wi * DK * DV + (size_t)(16 * w + li) * DV + 4 * qd;
+#pragma unroll
+                for (int ct = 0; ct < B::DVT; ++ct) {
+                    put4(dst + 16 * ct, acc[l][ct]);
+                    acc[l][ct] = zero4();
+                }
+            }
+        }
+        // partials of the larger blocks (the whole span lies in one block)
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int m = m0 + l;
+            if (m > mtop || (1 << (m - 1)) <= B::WP || !((cA >> (m - 1)) & 1))
+                continue;
+            const int j = cA >> m, R0 = (j << m) + (1 << (m - 1));
+            const int np = ((1 << (m - 1)) + B::WP - 1) / B::WP;
+            const size_t pi = (size_t)bh * NP + pbase_of(m) + (size_t)j * np + (cA - R0) / B::WP;
+            float *dst = Wp + pi * DK * DV + (size_t)(16 * w + li) * DV + 4 * qd;
+#pragma unroll
+            for (int ct = 0; ct < B::DVT; ++ct)
+                *reinterpret_cast<floatx4 *>(dst + 16 * ct) = acc[l][ct];
+        }
+    }
+}
+
 // Sum of a multi-piece block's partials, written as W and W^T.
 template <class B>
 __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp, typename B::T *__restrict__ W1,
@@ -1219,7 +1414,22 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     float *Mq = reinterpret_cast<float *>(ws + P.off_mq);
     float *Mk = reinterpret_cast<float *>(ws + P.off_mk);
     // 3. W pieces and their sums
-    if (P.NP > 0) {
+    if (P.NP > 0 && g8) {
+        if constexpr (BwDq<B>::on && B::DK == 128 && B::C <= 64) {
+            ProfEvents pe = prof_events("ll_bwd_wspan");
+            hipExtLaunchKernelGGL(ll_bwd_wspan<B>, dim3((N + B::WP - 1) / B::WP, BH), dim3(512), 0, s, pe.start,
+                                  pe.stop, 0, (const T *)A.q, (const T *)A.dout, A.a, A.lam, (const double *)Gp, Wp,
+                                  W1, A.T, A.L, N, P.NP, P.NB);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+            pe = prof_events("ll_bwd_wsum");
+            hipExtLaunchKernelGGL(ll_bwd_wsum<B>, dim3(P.NB, BH), dim3(256), 0, s, pe.start, pe.stop, 0,
+                                  (const float *)Wp, W1, W2, N, P.NP, P.NB);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
+    }
+    if (P.NP > 0 && !(g8 && BwDq<B>::on && B::DK == 128 && B::C <= 64)) {
         ProfEvents pe = prof_events("ll_bwd_wpiece");
         hipExtLaunchKernelGGL(ll_bwd_wpiece<B>, dim3(P.NP, BH), dim3(256), 0, s, pe.start, pe.stop, 0,
                               (const T *)A.q, (const T *)A.dout, A.a, A.lam, (const double *)Gp, Wp, W1, W2, A.T,
