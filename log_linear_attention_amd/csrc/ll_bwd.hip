@@ -186,6 +186,17 @@ __device__ __forceinline__ void put4(__bf16 *p, const floatx4 &x)
     *reinterpret_cast<bf16x4 *>(p) = y;
 }
 
+// Buffer resource over `bytes` bytes at p: loads past the range return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bw_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bw_load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // ---------------------------------------------------------------------------
 // Chunk kernel: one workgroup per (head, chunk).
 // ---------------------------------------------------------------------------
@@ -218,33 +229,193 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
 
     const int mtop = bitlen_u32((uint32_t)(N - 1));
 
+    // Level sources: kind 1 = query side (the left block is a stored block
+    // state), 2 = key side (the right block R exists), 0 = nothing.
+    auto kind_of = [&](int m) __attribute__((always_inline)) {
+        if (m > mtop)
+            return 0;
+        if ((c >> (m - 1)) & 1)
+            return 1;
+        return ((c >> m) << m) + (1 << (m - 1)) < N ? 2 : 0;
+    };
+    // level m's state in global memory: p1 (the block state, or W) and p2
+    // (W^T when stored, else p1)
+    struct StatePtr {
+        const T *p1, *p2;
+    };
+    auto state_ptr = [&](int m, int kind) __attribute__((always_inline)) {
+        // the bases read up front and chosen by value (a choice between the
+        // addresses of the captured pointers would keep them in scratch)
+        const T *const nd = Nd, *const dg = Dg, *const w1 = W1, *const w2 = W2;
+        size_t o;
+        int src;
+        if (kind == 1) {
+            if (m <= gq) {
+                // inside a group of 2^gq chunks: the Fenwick node of the left
+                // block's last chunk
+                const int e = ((c >> m) << m) + (1 << (m - 1)) - 1;
+                o = (size_t)bh * N + e;
+                src = 0;
+            } else {
+                // a left block of the tree over groups, at level m - 1 - gq
+                size_t offp = 0;
+                for (int r = 0; r < m - 1 - gq; ++r)
+                    offp += ((nL >> r) + 1) >> 1;
+                o = (size_t)bh * nLeft + offp + (c >> m);
+                src = 1;
+            }
+        } else {
+            size_t ob = 0;
+            for (int r = 1; r < m; ++r) {
+                const int hr = 1 << (r - 1);
+                ob += N > hr ? (N - hr + (1 << r) - 1) >> r : 0;
+            }
+            o = (size_t)bh * NB + ob + (c >> m);
+            src = 2;
+        }
+        o *= (size_t)DK * DV;
+        const T *p1 = (src == 0 ? nd : src == 1 ? dg : w1) + o;   // block state, or W [dk][dv]
+        const T *p2 = src == 2 && w2 ? w2 + o : p1;                 // W^T [dv][dk] when stored
+        return StatePtr{p1, p2};
+    };
+
+    // bf16 with staged level states: the key-side levels (kind 2) are not
+    // multiplied one by one.  With delta_s = exp(A_end - A_s) and rho_m the
+    // decay from the chunk's end to R_m's start, the key-side terms of all
+    // levels are delta_s (sum_m rho_m W_m) v_s for dk and the transposed
+    // product for dv; the level's pair mass is rho_m <W_m, X>, where
+    // X = sum_s delta_s k_s v_s^T.  So the W_m are read straight into
+    // registers (in X's accumulator layout: row d, four consecutive e),
+    // summed in fp32, and one product with the sum replaces a product per
+    // level.
+    constexpr bool KS = BwDq<B>::on;
+    constexpr int NXT = (B::DKT * B::DVT + B::NW - 1) / B::NW;   // X tiles per wave
+    constexpr int PRE = KS ? (16 / NXT < 1 ? 1 : 16 / NXT > 4 ? 4 : 16 / NXT) : 1;   // levels per batch
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    uint32_t k2 = 0;   // the key-side levels, bit m
+    if constexpr (KS) {
+        for (int m = 1; m <= mtop; ++m)
+            if (kind_of(m) == 2)
+                k2 |= 1u << m;
+    }
+    u32x2 wr[PRE][NXT];
+    // loads the first PRE levels of `mask` into wr
+    auto load_k2 = [&](uint32_t mask) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) {
+            // a slot past the last level reads nothing (an empty range)
+            const int m = mask ? __builtin_ctz(mask) : 1;
+            const __amdgpu_buffer_rsrc_t r = bw_rsrc(state_ptr(m, 2).p1, mask ? DK * DV * (int)sizeof(T) : 0);
+            mask &= mask - 1;
+#pragma unroll
+            for (int t = 0; t < NXT; ++t) {
+                const int ti = wv * NXT + t;
+                const int d = 16 * (ti / B::DVT) + li, e0 = 16 * (ti % B::DVT) + 4 * qd;
+                const int off = ti < B::DKT * B::DVT ? (d * DV + e0) * (int)sizeof(T) : DK * DV * (int)sizeof(T);
+                wr[j][t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+            }
+        }
+    };
+
     // ---- stage the chunk: 16-byte pieces, every load issued first ------------
+    // All of the item's loads go out together, so that it waits for one round
+    // trip: q, k, v, dO, lambda rows (contiguous, C*L floats), a, the fp64
+    // chunk prefix for the level offsets, the key-side level states and the
+    // first query-side level state.  They are buffer loads over the valid
+    // range (zero beyond it) issued on every path: a load skipped on some
+    // path would make the compiler wait for all loads before the first use.
     constexpr int VEC = B::VEC, QP = C * DK / VEC, VP = C * DV / VEC;
     constexpr int NQP = (QP + B::NTC - 1) / B::NTC, NVP = (VP + B::NTC - 1) / B::NTC;
     uint4 rq[NQP], rk[NQP], rv[NVP], ro[NVP];
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    {
+        const uint32_t nq = (uint32_t)(nv * DK * sizeof(T)), nvb = (uint32_t)(nv * DV * sizeof(T));
+        const __amdgpu_buffer_rsrc_t r_q = bw_rsrc(q + row0 * DK, nq), r_k = bw_rsrc(k + row0 * DK, nq);
+        const __amdgpu_buffer_rsrc_t r_v = bw_rsrc(v + row0 * DV, nvb), r_o = bw_rsrc(dout + row0 * DV, nvb);
 #pragma unroll
-    for (int j = 0; j < NQP; ++j) {
-        const int i = tid + B::NTC * j, t = i / (DK / VEC);
-        const bool ok = i < QP && t < nv;
-        rq[j] = z4;
-        rk[j] = z4;
-        if (ok) {
-            rq[j] = *reinterpret_cast<const uint4 *>(q + row0 * DK + (size_t)i * VEC);
-            rk[j] = *reinterpret_cast<const uint4 *>(k + row0 * DK + (size_t)i * VEC);
+        for (int j = 0; j < NQP; ++j) {
+            const int off = (tid + B::NTC * j) * 16;
+            rq[j] = bw_load16(r_q, off);
+            rk[j] = bw_load16(r_k, off);
+        }
+#pragma unroll
+        for (int j = 0; j < NVP; ++j) {
+            const int off = (tid + B::NTC * j) * 16;
+            rv[j] = bw_load16(r_v, off);
+            ro[j] = bw_load16(r_o, off);
         }
     }
+    static_assert(C <= 64, "one wave scans a");
+    constexpr int NLL = C * kMaxLevels / B::NTC;
+    float lv[NLL];
+    {
+        const __amdgpu_buffer_rsrc_t r_l = bw_rsrc(lamg + row0 * L, (uint32_t)(nv * L * 4));
 #pragma unroll
-    for (int j = 0; j < NVP; ++j) {
-        const int i = tid + B::NTC * j, t = i / (DV / VEC);
-        const bool ok = i < VP && t < nv;
-        rv[j] = z4;
-        ro[j] = z4;
-        if (ok) {
-            rv[j] = *reinterpret_cast<const uint4 *>(v + row0 * DV + (size_t)i * VEC);
-            ro[j] = *reinterpret_cast<const uint4 *>(dout + row0 * DV + (size_t)i * VEC);
-        }
+        for (int j = 0; j < NLL; ++j)
+            lv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_l, (tid + B::NTC * j) * 4, 0, 0));
     }
+    const float av = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(bw_rsrc(a + row0, (uint32_t)(nv * 4)), lane * 4, 0, 0));
+    // Per level: the log-decay between this chunk and the other block, from
+    // the fp64 prefix of chunk totals (query side: from the left block's end
+    // to this chunk's start; key side: from this chunk's end to R's start).
+    // Thread m reads the two prefix entries of level m (none: past the end).
+    double gpa, gpb;
+    {
+        int ia = N, ib = N;
+        if (tid >= 1 && tid <= mtop) {
+            const int m = tid, half = 1 << (m - 1), b0 = (c >> m) << m;
+            if ((c >> (m - 1)) & 1) {
+                ia = c;
+                ib = b0 + half;
+            } else if (b0 + half < N) {
+                ia = b0 + half;
+                ib = c + 1;
+            }
+        }
+        const __amdgpu_buffer_rsrc_t r_g = bw_rsrc(Gp + (size_t)bh * N, (uint32_t)N * 8);
+        gpa = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r_g, ia * 8, 0, 0));
+        gpb = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r_g, ib * 8, 0, 0));
+    }
+    if constexpr (KS)
+        load_k2(k2);
+    constexpr bool SST = BwSt<B>::SST;
+    constexpr int HP = DK * DV / VEC;   // pieces of one state
+    // pieces of one level's LDS copy: the state (W and W^T when both are kept)
+    constexpr int NSPT = ((BwDq<B>::on ? HP : 2 * HP) + B::NTC - 1) / B::NTC;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    // the next level's state pieces of the level loop (loaded one level ahead)
+    u32x4 sp[NSPT];
+    // the levels the level loop takes (bit m)
+    auto loop_kind = [&](int m) __attribute__((always_inline)) {
+        const int kd = kind_of(m);
+        return KS && kd == 2 ? 0 : kd;
+    };
+    uint32_t lmask = 0;
+    for (int m = 1; m <= mtop; ++m)
+        if (loop_kind(m) != 0)
+            lmask |= 1u << m;
+    // loads level mn's state into sp (mn = 0: none, zeros)
+    auto load_sp = [&](int mn) __attribute__((always_inline)) {
+        const int nk = mn ? loop_kind(mn) : 0;
+        const StatePtr sq = state_ptr(mn ? mn : 1, nk ? nk : 1);
+        const bool two = nk == 2 && !BwDq<B>::on;   // W and W^T
+        const __amdgpu_buffer_rsrc_t r1 = bw_rsrc(sq.p1, nk ? HP * 16 : 0), r2 = bw_rsrc(sq.p2, two ? HP * 16 : 0);
+#pragma unroll
+        for (int j = 0; j < NSPT; ++j) {
+            const int i = tid + B::NTC * j;
+            if (B::NTC * (j + 1) <= HP) {
+                sp[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, i * 16, 0, 0));
+            } else if (B::NTC * j >= HP) {
+                sp[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, (i - HP) * 16, 0, 0));
+            } else {
+                // pieces on both sides of HP: one of the two loads is out of range
+                sp[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, i * 16, 0, 0)) |
+                        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, (i - HP) * 16, 0, 0));
+            }
+        }
+    };
+    if constexpr (SST)
+        load_sp(lmask ? __builtin_ctz(lmask) : 0);
 #pragma unroll
     for (int j = 0; j < NQP; ++j) {
         const int i = tid + B::NTC * j;
@@ -277,15 +448,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         reinterpret_cast<uint4 *>(&sm.PdT[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
         reinterpret_cast<uint4 *>(&sm.PsT[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    // lambda rows of the chunk are contiguous: C*L floats, loaded together
     {
-        constexpr int NLL = C * kMaxLevels / B::NTC;
-        float lv[NLL];
-#pragma unroll
-        for (int j = 0; j < NLL; ++j) {
-            const int i = tid + B::NTC * j;
-            lv[j] = i < nv * L ? lamg[row0 * L + i] : 0.f;
-        }
         for (int i = tid; i < C * (kMaxLevels + 1); i += B::NTC) {
             (&sm.lam[0][0])[i] = 0.f;
             (&sm.dlam[0][0])[i] = 0.f;
@@ -300,22 +463,44 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     }
     if (tid < kMaxLevels)
         sm.km[tid] = 0.f;
+    if (tid >= 1 && tid <= mtop)
+        sm.off[tid] = (float)(gpa - gpb);
     if (wv == 0) {
         // inclusive prefix of a over the chunk (zero past the end)
-        for (int base = 0; base < C; base += 64) {
-            float x = (base + lane < nv) ? a[row0 + base + lane] : 0.f;
+        float x = av;
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const float y = __shfl_up(x, d, 64);
-                if (lane >= d)
-                    x += y;
-            }
-            const float carry = base > 0 ? sm.Aloc[base - 1] : 0.f;
-            if (base + lane < C)
-                sm.Aloc[base + lane] = x + carry;
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_up(x, d, 64);
+            if (lane >= d)
+                x += y;
         }
+        if (lane < C)
+            sm.Aloc[lane] = x;
     }
     __syncthreads();
+    if constexpr (KS) {
+        static_assert(C * B::LV <= B::SSZ, "delta V fits the state buffer");
+        // delta_s v_s (bf16) into the state buffer, for X
+#pragma unroll
+        for (int j = 0; j < NVP; ++j) {
+            const int i = tid + B::NTC * j;
+            if (i < VP) {
+                const int t = i / (DV / VEC), e0 = (i % (DV / VEC)) * VEC;
+                const float dl = __expf(sm.Aloc[C - 1] - sm.Aloc[t]);
+                const uint4 x = rv[j];
+                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float lo = __uint_as_float(w[h] << 16) * dl, hi = __uint_as_float(w[h] & 0xffff0000u) * dl;
+                    const __bf16 blo = (__bf16)lo, bhi = (__bf16)hi;
+                    o[h] = (uint32_t)__builtin_bit_cast(unsigned short, blo) |
+                           ((uint32_t)__builtin_bit_cast(unsigned short, bhi) << 16);
+                }
+                *reinterpret_cast<uint4 *>(sm.st + t * B::LV + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
 
     // ---- in-chunk scores: S = Q K^T, dP = dO V^T, causal tile pairs ---------
     for (int pr = wv; pr < B::CT * (B::CT + 1) / 2; pr += B::NW) {
@@ -420,67 +605,73 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 mma_unit(dQ[j], tr_frag(&sm.Ks[0][0], B::LQ, B::KB * u, 16 * (cg + B::NCG * j), li, qd), pdt);
         }
     }
+    // X = sum_s delta_s k_s v_s^T, tiles wv*NXT + t: Xc[t][i] = X[d][e] with
+    // d = 16 (tile / DVT) + li, e = 16 (tile % DVT) + 4 qd + i (A = delta V^T,
+    // B = K^T, both by transpose reads over the tokens)
+    floatx4 Xc[NXT], Wt[NXT];
+#pragma unroll
+    for (int t = 0; t < NXT; ++t) {
+        Xc[t] = zero4();
+        Wt[t] = zero4();
+    }
+    if constexpr (KS) {
+#pragma unroll
+        for (int t = 0; t < NXT; ++t) {
+            const int ti = wv * NXT + t;
+            if (ti < B::DKT * B::DVT) {
+#pragma unroll
+                for (int u = 0; u < B::NUC; ++u)
+                    mma_unit(Xc[t], tr_frag(sm.st, B::LV, B::KB * u, 16 * (ti % B::DVT), li, qd),
+                             tr_frag(&sm.Ks[0][0], B::LQ, B::KB * u, 16 * (ti / B::DVT), li, qd));
+            }
+        }
+    }
+    // adds the levels loaded into wr (the first PRE of `rest`, which drops
+    // them): Wt += rho_m W_m, and the level's pair mass per wave
+    auto add_k2 = [&](uint32_t &rest) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) {
+            if (rest) {
+                const int m = __builtin_ctz(rest);
+                rest &= rest - 1;
+                const float rho = __expf(sm.off[m]);
+                float x = 0.f;
+#pragma unroll
+                for (int t = 0; t < NXT; ++t) {
+                    const u32x2 w = wr[j][t];
+                    const floatx4 w4 = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                        __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+                    Wt[t] += rho * w4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        x += w4[i] * Xc[t][i];
+                }
+                x *= rho;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1)
+                    x += __shfl_xor(x, o, 64);
+                if (lane == 0)
+                    sm.lkw[m][wv] = x;
+            }
+        }
+    };
 
     // ---- chunk levels -------------------------------------------------------
     // pki: this lane's part of k_s . (dk_s from later chunks), fp32
     float pki = 0.f;
-    // Per level: the log-decay between this chunk and the other block, from
-    // the fp64 prefix of chunk totals (query side: from the left block's end
-    // to this chunk's start; key side: from this chunk's end to R's start).
-    if (tid >= 1 && tid <= mtop) {
-        const int m = tid, half = 1 << (m - 1), b0 = (c >> m) << m;
-        const double *gp = Gp + (size_t)bh * N;
-        double o = 0.0;
-        if ((c >> (m - 1)) & 1)
-            o = gp[c] - gp[b0 + half];
-        else if (b0 + half < N)
-            o = gp[b0 + half] - gp[c + 1];
-        sm.off[m] = (float)o;
+    uint32_t k2rest = k2;   // key-side levels not yet added
+    if constexpr (KS) {
+        add_k2(k2rest);
+        if (k2rest)
+            load_k2(k2rest);   // in flight during the query-side levels
     }
-    __syncthreads();
-    // Level sources: kind 1 = query side (the left block is a stored block
-    // state), 2 = key side (the right block R exists), 0 = nothing.
-    auto kind_of = [&](int m) {
-        if (m > mtop)
-            return 0;
-        if ((c >> (m - 1)) & 1)
-            return 1;
-        return ((c >> m) << m) + (1 << (m - 1)) < N ? 2 : 0;
-    };
-    auto state_ptr = [&](int m, int kind, const T *&p1, const T *&p2) {
-        if (kind == 1) {
-            if (m <= gq) {
-                // inside a group of 2^gq chunks: the Fenwick node of the left
-                // block's last chunk
-                const int e = ((c >> m) << m) + (1 << (m - 1)) - 1;
-                p1 = Nd + ((size_t)bh * N + e) * DK * DV;
-            } else {
-                // a left block of the tree over groups, at level m - 1 - gq
-                size_t offp = 0;
-                for (int r = 0; r < m - 1 - gq; ++r)
-                    offp += ((nL >> r) + 1) >> 1;
-                p1 = Dg + ((size_t)bh * nLeft + offp + (c >> m)) * DK * DV;
-            }
-            p2 = p1;
-        } else {
-            size_t ob = 0;
-            for (int r = 1; r < m; ++r) {
-                const int hr = 1 << (r - 1);
-                ob += N > hr ? (N - hr + (1 << r) - 1) >> r : 0;
-            }
-            const size_t wi = (size_t)bh * NB + ob + (c >> m);
-            p1 = W1 + wi * DK * DV;   // W,   [dk][dv]
-            p2 = W2 ? W2 + wi * DK * DV : p1;   // W^T, [dv][dk] (when stored)
-        }
-    };
-    constexpr bool SST = BwSt<B>::SST;
-    constexpr int NSPT = (B::NSP + B::NTC - 1) / B::NTC;
-    constexpr int HP = DK * DV / VEC;   // pieces of one state
-    // next level's state pieces, loaded one level ahead (level 0 only loads)
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    u32x4 sp[NSPT];
-    for (int m = SST ? 0 : 1; m <= mtop; ++m) {
-        const int kind = m == 0 ? 0 : kind_of(m);
+    // the level loop: the query-side levels (and the key-side ones when
+    // they are not summed); with the state copy in LDS, each level's state
+    // was loaded one level ahead (the first one with the chunk)
+    for (int m = 1; m <= mtop; ++m) {
+        if (!((lmask >> m) & 1))
+            continue;
+        const int kind = loop_kind(m);
         const T *g1 = nullptr, *g2 = nullptr;   // the state in global memory (no LDS copy)
         if constexpr (SST) {
             __syncthreads();   // the previous level's reads of the copy are done
@@ -512,23 +703,15 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 }
             }
             {
-                const int nk = kind_of(m + 1);
-                if (nk != 0) {
-                    const T *p1, *p2;
-                    state_ptr(m + 1, nk, p1, p2);
-                    const int np = nk == 1 || FDQ ? HP : 2 * HP;
-#pragma unroll
-                    for (int j = 0; j < NSPT; ++j) {
-                        const int i = tid + B::NTC * j;
-                        if (i < np)
-                            sp[j] = *reinterpret_cast<const u32x4 *>(i < HP ? p1 + (size_t)i * VEC
-                                                                             : p2 + (size_t)(i - HP) * VEC);
-                    }
-                }
+                // the next level of the loop
+                const uint32_t above = lmask & ~((2u << m) - 1u);
+                load_sp(above ? __builtin_ctz(above) : 0);
             }
             __syncthreads();
         } else if (kind != 0) {
-            state_ptr(m, kind, g1, g2);
+            const StatePtr sq = state_ptr(m, kind);
+            g1 = sq.p1;
+            g2 = sq.p2;
         }
         if (kind == 1 && FDQ) {
             if constexpr (FDQ) {
@@ -632,6 +815,51 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 km += __shfl_xor(km, o, 64);
             if (lane == 0)
                 sm.lkw[m][wv] = km;
+        }
+    }
+    if constexpr (KS) {
+        // the remaining key-side levels, then one product with their sum
+        while (k2rest) {
+            add_k2(k2rest);
+            if (k2rest)
+                load_k2(k2rest);
+        }
+        if (k2) {
+            __syncthreads();   // the loop's reads of the state copy are done
+#pragma unroll
+            for (int t = 0; t < NXT; ++t) {
+                const int ti = wv * NXT + t;
+                if (ti < B::DKT * B::DVT)
+                    put4(sm.st + (16 * (ti / B::DVT) + li) * B::LW1 + 16 * (ti % B::DVT) + 4 * qd, Wt[t]);
+            }
+            __syncthreads();
+            const float dec = __expf(sm.Aloc[C - 1] - sm.Aloc[16 * kt + li]);
+            float km = 0.f;
+#pragma unroll
+            for (int j = 0; j < B::KPW; ++j) {
+                const int dt = cg + B::NCG * j;
+                floatx4 X = zero4();
+#pragma unroll
+                for (int u = 0; u < B::NUV; ++u)
+                    mma_unit(X, frag<B>(sm.st, B::LW1, 16 * dt + li, u, qd),
+                             frag<B>(&sm.Vs[0][0], B::LV, 16 * kt + li, u, qd));
+                dK[j] += dec * X;
+                const floatx4 k4 = ld4(&sm.Ks[16 * kt + li][16 * dt + 4 * qd]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    km += dec * X[i] * k4[i];
+            }
+#pragma unroll
+            for (int j = 0; j < B::VPW; ++j) {
+                const int et = cg + B::NCG * j;
+                floatx4 X = zero4();
+#pragma unroll
+                for (int u = 0; u < B::NUK; ++u)
+                    mma_unit(X, tr_frag(sm.st, B::LW1, B::KB * u, 16 * et, li, qd),
+                             lds_frag(&sm.Ks[0][0], B::LQ, 16 * kt + li, B::KB * u, qd));
+                dV[j] += dec * X;
+            }
+            pki += km;
         }
     }
     __syncthreads();
