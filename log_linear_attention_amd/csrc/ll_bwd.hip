@@ -917,7 +917,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 const int lev = t == tk ? 0 : bitlen_u32((uint32_t)(t ^ tk));
                 pki_in += sm.lam[t][lev] * sm.G[t][tk];
             }
-            for (int l = qq; l < kMaxLevels; l += 4)
+            for (int l = qq; l < L; l += 4)
                 pq += sm.lam[tk][l] * sm.dlam[tk][l];
         }
         pki_in += __shfl_xor(pki_in, 1, 64);
