@@ -1444,6 +1444,70 @@ __global__ __launch_bounds__(256) void ll_bwd_wsum(const float *__restrict__ Wp,
     write_w<B>(Wt, W1 + wi * DK * DV, W2 ? W2 + wi * DK * DV : nullptr, threadIdx.x);
 }
 
+// The same sums when only W is kept (the spans kernel's pieces): each block
+// is split over WQ workgroups by rows, and a thread adds its 16-byte slices
+// of four pieces at a time, so that four loads per slice are in flight.
+// Grid: (NB * WQ, BH).
+template <class B>
+__global__ __launch_bounds__(256) void ll_bwd_wsum_rows(const float *__restrict__ Wp, typename B::T *__restrict__ W1,
+                                                        int N, int NP, int NB)
+{
+    constexpr int DK = B::DK, DV = B::DV, WQ = 4;
+    constexpr int PER = DK * DV / WQ / 4 / 256;   // float4 slices per thread and piece
+    static_assert(PER >= 1 && DK * DV == PER * 4 * 256 * WQ, "thread layout");
+    const int bh = blockIdx.y, qt = blockIdx.x % WQ;
+    int x = blockIdx.x / WQ, m = 1, pbase = 0;
+    const int mtop = bitlen_u32((uint32_t)(N - 1));
+    int nb = 0, np = 0;
+    for (; m <= mtop; ++m) {
+        nb = wnblk(N, m);
+        np = ((1 << (m - 1)) + B::WP - 1) / B::WP;
+        if (x < nb)
+            break;
+        x -= nb;
+        pbase += nb * np;
+    }
+    if (np == 1)
+        return;   // written by its only piece
+    const int j = x, R0 = j * (1 << m) + (1 << (m - 1));
+    int npv = 0;   // pieces that start inside the sequence
+    for (int pi = 0; pi < np; ++pi)
+        if (R0 + pi * B::WP < N)
+            npv = pi + 1;
+    const float *src = Wp + ((size_t)bh * NP + pbase + (size_t)j * np) * DK * DV + (size_t)qt * (DK * DV / WQ);
+    float4 acc[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+        acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < npv; p0 += 4) {
+        float4 x4[4][PER];
+        float f[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const int pi = p0 + h;
+            const bool ok = pi < npv;
+            const float4 *sp = reinterpret_cast<const float4 *>(src + (size_t)(ok ? pi : 0) * DK * DV);
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+                x4[h][r] = sp[threadIdx.x + 256 * r];
+            f[h] = ok ? 1.f : 0.f;   // a past-the-end slot re-reads piece 0 and adds nothing
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int r = 0; r < PER; ++r) {
+                acc[r].x += f[h] * x4[h][r].x;
+                acc[r].y += f[h] * x4[h][r].y;
+                acc[r].z += f[h] * x4[h][r].z;
+                acc[r].w += f[h] * x4[h][r].w;
+            }
+    }
+    typename B::T *dst = W1 + ((size_t)bh * NB + blockIdx.x / WQ) * DK * DV + (size_t)qt * (DK * DV / WQ);
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+        put4(dst + 4 * (threadIdx.x + 256 * r), floatx4{acc[r].x, acc[r].y, acc[r].z, acc[r].w});
+}
+
 // fp64 exclusive prefix of the chunk log-decay totals: Gp[c] = sum of
 // gam[c'] over c' < c, c in [0, N) (gam is defined for the first N-1 chunks).
 // One workgroup per head.
@@ -1651,8 +1715,8 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
             if ((e = hipGetLastError()) != hipSuccess)
                 return e;
             pe = prof_events("ll_bwd_wsum");
-            hipExtLaunchKernelGGL(ll_bwd_wsum<B>, dim3(P.NB, BH), dim3(256), 0, s, pe.start, pe.stop, 0,
-                                  (const float *)Wp, W1, W2, N, P.NP, P.NB);
+            hipExtLaunchKernelGGL(ll_bwd_wsum_rows<B>, dim3(P.NB * 4, BH), dim3(256), 0, s, pe.start, pe.stop,
+                                  0, (const float *)Wp, W1, N, P.NP, P.NB);
             if ((e = hipGetLastError()) != hipSuccess)
                 return e;
         }

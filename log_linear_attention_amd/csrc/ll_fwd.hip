@@ -360,7 +360,7 @@ __device__ __forceinline__ void state_load(StateRegs<F> &r, const typename F::T 
 }
 
 template <class F>
-__global__ __launch_bounds__(F::NT) void ll_group_state(const typename F::T *__restrict__ k,
+__global__ __launch_bounds__(F::NT, (F::TR && F::NW >= 4) ? 2 : 1) void ll_group_state(const typename F::T *__restrict__ k,
                                                         const typename F::T *__restrict__ v,
                                                         const float *__restrict__ a, int Tlen, int g, int nG,
                                                         int nL, int rqk, float *__restrict__ Sg,
