@@ -100,8 +100,18 @@ def test_bf16_bwd_head_dims(dk, dv):
 def test_bf16_bwd_16k_workload_sampled():
     """The 16K forward workload: sampled query and key rows against the
     oracle, and da at sampled positions against its windowed oracle."""
-    cfg = synth.WORKLOADS["fwd_bf16_T16K"]
-    announce(f"bwd {cfg.name}")
+    _sampled(synth.WORKLOADS["fwd_bf16_T16K"])
+
+
+def test_bf16_bwd_nine_key_levels_sampled():
+    """258 chunks of 32: the first chunks' keys are seen from nine chunk
+    levels, more than two batches of the key-side levels the chunk kernel
+    loads into registers (four per batch)."""
+    _sampled(synth.FwdConfig("bf16_bwd_258", 1, 2, 8256, 128, 64, 32, "bf16", 0.05, 6500))
+
+
+def _sampled(cfg):
+    announce(f"bwd {cfg.name} (sampled rows)")
     inp = synth.make_fwd_inputs(cfg)
     dout = _dout(cfg, cfg.T, cfg.seed + 7)
     got = _run(inp, dout, cfg.chunk)
