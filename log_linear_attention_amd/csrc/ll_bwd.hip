@@ -108,6 +108,7 @@ struct BwSmemBase {
     float lpart[kMaxLevels - B::LOGC][B::NCG][B::C];
     float lkw[kMaxLevels - B::LOGC][B::NW];
     float u[B::C], w[B::C];                             // per-token terms of the in-chunk part of da
+    float kin[B::CT][B::C];                             // in-chunk pair masses of each key, per query tile
 };
 
 // The shared level-state buffer when it fits next to the rest.
@@ -522,6 +523,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         // accumulator lane layout (A = keys, B = queries): rows 4*qd+i are
         // keys s, column li is query t
         const int t = 16 * tt + li;
+        float kin[4];   // the in-chunk pair masses P(t, s) of key s, summed over this tile's queries below
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 16 * st + 4 * qd + i;
@@ -535,7 +537,18 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             put(&sm.PdT[s][t], m * dpv);
             put(&sm.PsT[s][t], m * sv);
             sm.G[t][s] = g;
+            kin[i] = m * sv * dpv;
         }
+        // sum over the 16 queries of the tile (lanes li of one lane quad)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                kin[i] += __shfl_xor(kin[i], o, 64);
+        if (li == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sm.kin[tt][16 * st + 4 * qd + i] = kin[i];
     }
     __syncthreads();
 
@@ -908,15 +921,14 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         // da inside the chunk, for r = t0 + i:
         //   sum_{t >= r} (sum of P(t, s) over s <= t) - sum_{s >= r} (in-chunk P(., s))
         //   + sum_{s < r} (P(., s) over later chunks)
-        // The in-chunk sums of both sides come from the same fp32 products.
+        // The in-chunk sums of both sides come from the same fp32 scores S, dP.
         // Four threads per token (quarters of the key / level ranges).
         const int tk = tid >> 2, qq = tid & 3;
         float pki_in = 0.f, pq = 0.f;
         if (tk < C) {
-            for (int t = tk + qq; t < C; t += 4) {
-                const int lev = t == tk ? 0 : bitlen_u32((uint32_t)(t ^ tk));
-                pki_in += sm.lam[t][lev] * sm.G[t][tk];
-            }
+            // key tk's in-chunk pair masses: the query tiles from its own on
+            for (int tt = tk / 16 + qq; tt < B::CT; tt += 4)
+                pki_in += sm.kin[tt][tk];
             for (int l = qq; l < L; l += 4)
                 pq += sm.lam[tk][l] * sm.dlam[tk][l];
         }
