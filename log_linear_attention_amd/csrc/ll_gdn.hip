@@ -49,6 +49,18 @@
 
 namespace ll {
 
+// Buffer resource over `bytes` bytes at p (loads past the range return zero)
+// and a 16-byte load through it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gdn_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ float4 gdn_load16(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 template <class DT, int DK_, int DV_, int C_>
 struct Gdn {
     using T = typename DT::T;   // q, k, v and out; everything else is float32
@@ -551,27 +563,30 @@ __global__ __launch_bounds__(256) void ll_gdn_tree(float *__restrict__ Phit, flo
     // Slice k0 of both operands into registers.  Columns come in groups of
     // four that never straddle the Phi / D boundary (dk and dv are multiples
     // of 16); columns past DK + DV read as zero.
+    // The loads are issued on every path (the pieces past the operands, and
+    // the columns past DK + DV, read as zero from buffer loads past their
+    // range): a load skipped on some path would make the compiler wait for
+    // every outstanding load, the prefetched slice included, at the next use.
+    const __amdgpu_buffer_rsrc_t rPR = gdn_rsrc(PR, DK * DK * 4), rPL = gdn_rsrc(PL, DK * DK * 4),
+                                 rDL = gdn_rsrc(DL, DK * DV * 4);
     auto gload = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
             const int e = tid + 256 * i;
-            if (e < TS * KS / 4) {
-                const int r = e / (KS / 4), k4 = 4 * (e % (KS / 4));
-                ra[i] = ld4(PR + (size_t)(row0 + r) * DK + k0 + k4);
-            }
+            const int r = e / (KS / 4), k4 = 4 * (e % (KS / 4));
+            const int off = e < TS * KS / 4 ? ((row0 + r) * DK + k0 + k4) * 4 : DK * DK * 4;
+            ra[i] = gdn_load16(rPR, off);
         }
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int e = tid + 256 * i;
-            if (e < KS * TS / 4) {
-                const int kk = e / (TS / 4), col = col0 + 4 * (e % (TS / 4));
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (col < DK)
-                    x = ld4(PL + (size_t)(k0 + kk) * DK + col);
-                else if (col < NC)
-                    x = ld4(DL + (size_t)(k0 + kk) * DV + col - DK);
-                rb[i] = x;
-            }
+            const int kk = e / (TS / 4), col = col0 + 4 * (e % (TS / 4));
+            const bool in = e < KS * TS / 4;
+            // one of the two loads is past its range (or both, past the columns)
+            const int offL = in && col < DK ? ((k0 + kk) * DK + col) * 4 : DK * DK * 4;
+            const int offD = in && col >= DK && col < NC ? ((k0 + kk) * DV + col - DK) * 4 : DK * DV * 4;
+            const float4 a = gdn_load16(rPL, offL), b = gdn_load16(rDL, offD);
+            rb[i] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
         }
     };
 
