@@ -663,8 +663,8 @@ constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a tim
 // Tiles of Y B (Y: C x DK rows in LDS, B: DK x NB row-major in global memory)
 // on fp32 MFMA, 16 x 16 output tiles t = w, w + NW, ... of wave w; B is
 // staged through LDS (Bs) one 16-row unit at a time, read once per
-// workgroup, and the next unit is loaded into registers before the current
-// one is multiplied.  Every thread of the workgroup (NW waves) must call
+// workgroup, with the next three units in flight in registers while the
+// current one is multiplied.  Every thread of the workgroup (NW waves) must call
 // this.  Tiles are formed transposed (B^T Y^T), so acc tile j of the wave
 // holds row 16 * (t / (NB/16)) + li, columns 16 * (t % (NB/16)) + 4*qd + r.
 template <int NTW, int NW, int C, int DK, int LDY, int NB>
@@ -673,29 +673,37 @@ __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float
 {
     constexpr int TN = NB / 16, TT = (C / 16) * TN;
     constexpr int NTH = 64 * NW, NE = kGdnKS * NB / 4, NR = (NE + NTH - 1) / NTH;   // float4 per thread and unit
+    constexpr int NU = DK / kGdnKS, PD = NU < 3 ? NU : 3;   // units, and units in flight
     const int tid = threadIdx.x;
-    float4 rb[NR];
+    // unit k of B into registers: buffer loads issued on every path (past the
+    // unit's elements: past the range, zero), so the compiler waits for
+    // exactly the unit it stores and the later ones stay in flight
+    const __amdgpu_buffer_rsrc_t rB = gdn_rsrc(B, DK * NB * 4);
+    float4 rb[PD][NR];
+    auto ld_unit = [&](int k, float4 (&r)[NR]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i)
-        if (tid + NTH * i < NE)
-            rb[i] = ld4(B + 4 * (tid + NTH * i));
+        for (int i = 0; i < NR; ++i) {
+            const int e = tid + NTH * i;
+            r[i] = gdn_load16(rB, e < NE ? (k * kGdnKS * NB + 4 * e) * 4 : DK * NB * 4);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < PD; ++k)
+        ld_unit(k, rb[k]);
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
         acc[j] = zero4();
-#pragma unroll 1
-    for (int k0 = 0; k0 < DK; k0 += kGdnKS) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+        const int k0 = k * kGdnKS;
         __syncthreads();   // the previous unit has been read
 #pragma unroll
         for (int i = 0; i < NR; ++i)
             if (tid + NTH * i < NE)
-                *reinterpret_cast<float4 *>(Bs + 4 * (tid + NTH * i)) = rb[i];
+                *reinterpret_cast<float4 *>(Bs + 4 * (tid + NTH * i)) = rb[k % PD][i];
         __syncthreads();
-        if (k0 + kGdnKS < DK) {
-#pragma unroll
-            for (int i = 0; i < NR; ++i)
-                if (tid + NTH * i < NE)
-                    rb[i] = ld4(B + (size_t)(k0 + kGdnKS) * NB + 4 * (tid + NTH * i));
-        }
+        if (k + PD < NU)
+            ld_unit(k + PD, rb[k % PD]);
         if constexpr (NW % TN == 0) {
             // the wave's column tile is the same for all its tiles: one B fragment
             const int nt = w % TN;
