@@ -667,7 +667,7 @@ constexpr int kGdnKS = 16;   // rows of the walk's right operand staged at a tim
 // current one is multiplied.  Every thread of the workgroup (NW waves) must call
 // this.  Tiles are formed transposed (B^T Y^T), so acc tile j of the wave
 // holds row 16 * (t / (NB/16)) + li, columns 16 * (t % (NB/16)) + 4*qd + r.
-template <int NTW, int NW, int C, int DK, int LDY, int NB>
+template <int NTW, int NW, int C, int DK, int LDY, int NB, bool DIRECT>
 __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float *B, float *Bs, int w, int li, int qd,
                                               floatx4 (&acc)[NTW])
 {
@@ -675,6 +675,41 @@ __device__ __forceinline__ void gdn_tiles_mma(const float (*Y)[LDY], const float
     constexpr int NTH = 64 * NW, NE = kGdnKS * NB / 4, NR = (NE + NTH - 1) / NTH;   // float4 per thread and unit
     constexpr int NU = DK / kGdnKS, PD = NU < 3 ? NU : 3;   // units, and units in flight
     const int tid = threadIdx.x;
+    if constexpr (DIRECT && NW % TN == 0) {
+        // The wave's column tile nt is fixed: it reads its own B fragments
+        // (rows k0 + 4 qd + e, column 16 nt + li) straight from global memory,
+        // three units ahead, with no LDS stage and no barrier.  Y must be
+        // visible to every wave on entry.
+        constexpr int PB = NU < 3 ? NU : 3;
+        const __amdgpu_buffer_rsrc_t rB = gdn_rsrc(B, DK * NB * 4);
+        const int col = 16 * (w % TN) + li;
+        floatx4 bq[PB];
+        auto ldb = [&](int k, floatx4 &r) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r[e] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(rB, ((k * kGdnKS + 4 * qd + e) * NB + col) * 4, 0, 0));
+        };
+#pragma unroll
+        for (int k = 0; k < PB; ++k)
+            ldb(k, bq[k]);
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+            acc[j] = zero4();
+#pragma unroll
+        for (int k = 0; k < NU; ++k) {
+            const floatx4 bf = bq[k % PB];
+            if (k + PB < NU)
+                ldb(k + PB, bq[k % PB]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int t = w + NW * j;
+                if (t < TT)
+                    mma_unit(acc[j], bf, lds_frag(&Y[0][0], LDY, 16 * (t / TN) + li, k * kGdnKS, qd));
+            }
+        }
+        return;
+    }
     // unit k of B into registers: buffer loads issued on every path (past the
     // unit's elements: past the range, zero), so the compiler waits for
     // exactly the unit it stores and the later ones stay in flight
@@ -748,6 +783,10 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
     constexpr int C = G::C, DK = G::DK, DV = G::DV, NT = G::WNT, NW = NT / 64;
     constexpr int T1 = (C / 16) * (DV / 16), T2 = (C / 16) * (DK / 16);
     constexpr int N1 = (T1 + NW - 1) / NW, N2 = (T2 + NW - 1) / NW;
+    // right operands read straight from global memory (no LDS stage) for
+    // states of at most 128 x 64 (larger ones would take more registers than
+    // two workgroups per CU allow)
+    constexpr bool DIRECT = DK * DV <= 128 * 64;
     __shared__ __attribute__((aligned(16))) float Y[2][C][DK + 4];
     __shared__ __attribute__((aligned(16))) float Bs[kGdnKS * (DK > DV ? DK : DV)];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, qd = lane >> 4, li = lane & 15;
@@ -768,6 +807,7 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
         const int i = e / (DK / 4), d4 = e % (DK / 4);
         *reinterpret_cast<float4 *>(&Y[0][i][4 * d4]) = *reinterpret_cast<const float4 *>(qtc + (size_t)i * DK + 4 * d4);
     }
+    __syncthreads();   // Y[0] visible to every wave
     floatx4 acc[N1];
 #pragma unroll
     for (int j = 0; j < N1; ++j)
@@ -780,7 +820,7 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
         const int p = m - 1, jb = (c >> m) << 1;
         const size_t blk = (size_t)bh * NBT + gdn_level_off(N, p) + jb;
         floatx4 tmp[N1];
-        gdn_tiles_mma<N1, NW, C, DK, DK + 4, DV>(Y[cur], Dt + blk * DK * DV, Bs, w, li, qd, tmp);
+        gdn_tiles_mma<N1, NW, C, DK, DK + 4, DV, DIRECT>(Y[cur], Dt + blk * DK * DV, Bs, w, li, qd, tmp);
 #pragma unroll
         for (int j = 0; j < N1; ++j) {
             const int t = w + NW * j;
@@ -796,7 +836,7 @@ __global__ __launch_bounds__(G::WNT) void ll_gdn_walk(const float *__restrict__ 
             break;   // no coarser bucket
         // carry the queries through this block: Y' = Y Phi^T
         floatx4 ny[N2];
-        gdn_tiles_mma<N2, NW, C, DK, DK + 4, DK>(Y[cur], Phit + blk * DK * DK, Bs, w, li, qd, ny);
+        gdn_tiles_mma<N2, NW, C, DK, DK + 4, DK, DIRECT>(Y[cur], Phit + blk * DK * DK, Bs, w, li, qd, ny);
 #pragma unroll
         for (int j = 0; j < N2; ++j) {
             const int t = w + NW * j;
