@@ -128,6 +128,18 @@ __device__ __forceinline__ float4 ld4t(const __bf16 *p)
     return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
 }
 
+// The same through a buffer resource (zero past its range): elements
+// 4 e4 .. 4 e4 + 3 of the resource's base.
+__device__ __forceinline__ float4 ld4b(__amdgpu_buffer_rsrc_t r, int e4, const float *)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * e4, 0, 0));
+}
+__device__ __forceinline__ float4 ld4b(__amdgpu_buffer_rsrc_t r, int e4, const __bf16 *)
+{
+    const bf16x4 x = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * e4, 0, 0));
+    return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+
 __device__ __forceinline__ void st4t(float *p, const float4 &x) { *reinterpret_cast<float4 *>(p) = x; }
 __device__ __forceinline__ void st4t(__bf16 *p, const float4 &x)
 {
@@ -177,21 +189,40 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
 
     // ---- stage the chunk (rows past the sequence end: zero keys, values,
     // queries, beta and a, i.e. identity transitions and no writes) ----
-    // every load is issued before the first LDS store
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // every load is issued before the first LDS store, as buffer loads over
+    // the valid rows (zero past them) on every path, so that the chunk waits
+    // for one round trip
+    using T = typename G::T;
     constexpr int NQ4 = (C * DK / 4 + NT - 1) / NT, NV4 = (C * DV / 4 + NT - 1) / NT;
+    constexpr int NL = (C * (G::LOGC + 1) + NT - 1) / NT;
     float4 rq[NQ4], rk[NQ4], rv[NV4];
+    float rl[NL], rbeta, ra;
+    {
+        const int es = (int)sizeof(T);
+        const __amdgpu_buffer_rsrc_t r_q = gdn_rsrc(q + row0 * DK, valid * DK * es);
+        const __amdgpu_buffer_rsrc_t r_k = gdn_rsrc(k + row0 * DK, valid * DK * es);
+        const __amdgpu_buffer_rsrc_t r_v = gdn_rsrc(v + row0 * DV, valid * DV * es);
+        const __amdgpu_buffer_rsrc_t r_l = gdn_rsrc(lam + row0 * L, valid * L * 4);
 #pragma unroll
-    for (int u = 0; u < NQ4; ++u) {
-        const int e = tid + u * NT, i = e / (DK / 4), d = 4 * (e % (DK / 4));
-        const bool ok = e < C * DK / 4 && i < valid;
-        rq[u] = ok ? ld4t(q + (row0 + i) * DK + d) : z4;
-        rk[u] = ok ? ld4t(k + (row0 + i) * DK + d) : z4;
-    }
+        for (int u = 0; u < NQ4; ++u) {
+            const int e = tid + u * NT;
+            const int e4 = e < C * DK / 4 ? e : C * DK / 4;   // past the tile: past the range
+            rq[u] = ld4b(r_q, e4, q);
+            rk[u] = ld4b(r_k, e4, k);
+        }
 #pragma unroll
-    for (int u = 0; u < NV4; ++u) {
-        const int e = tid + u * NT, i = e / (DV / 4), d = 4 * (e % (DV / 4));
-        rv[u] = (e < C * DV / 4 && i < valid) ? ld4t(v + (row0 + i) * DV + d) : z4;
+        for (int u = 0; u < NV4; ++u) {
+            const int e = tid + u * NT;
+            rv[u] = ld4b(r_v, e < C * DV / 4 ? e : C * DV / 4, v);
+        }
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = tid + u * NT, i = e / (G::LOGC + 1), l = e % (G::LOGC + 1);
+            const int off = (e < C * (G::LOGC + 1) && l < L) ? (i * L + l) * 4 : valid * L * 4;
+            rl[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_l, off, 0, 0));
+        }
+        rbeta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gdn_rsrc(beta + row0, valid * 4), tid * 4, 0, 0));
+        ra = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gdn_rsrc(a + row0, valid * 4), tid * 4, 0, 0));
     }
 #pragma unroll
     for (int u = 0; u < NQ4; ++u) {
@@ -207,13 +238,15 @@ __global__ __launch_bounds__(G::CNT) void ll_gdn_chunk(const typename G::T *__re
         if (e < C * DV / 4)
             *reinterpret_cast<float4 *>(&sm.Vs[i][d]) = rv[u];
     }
-    for (int e = tid; e < C * (G::LOGC + 1); e += NT) {
-        const int i = e / (G::LOGC + 1), l = e % (G::LOGC + 1);
-        sm.lam[i][l] = (i < valid && l < L) ? lam[(row0 + i) * L + l] : 0.f;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const int e = tid + u * NT;
+        if (e < C * (G::LOGC + 1))
+            sm.lam[e / (G::LOGC + 1)][e % (G::LOGC + 1)] = rl[u];
     }
     if (tid < C) {
-        sm.beta[tid] = tid < valid ? beta[row0 + tid] : 0.f;
-        sm.Aloc[tid] = tid < valid ? a[row0 + tid] : 0.f;
+        sm.beta[tid] = rbeta;
+        sm.Aloc[tid] = ra;
     }
     __syncthreads();
     if (tid < 64) {
