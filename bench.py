@@ -224,8 +224,8 @@ def step_stats(torch, step, n):
 
 
 def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
-    """loglinear_bwd on the forward's workload: K/4 timed steps, then the same
-    steps with per-kernel events."""
+    """loglinear_bwd on the forward's workload: K/2 timed steps after up to
+    three warm-up steps, then the same steps with per-kernel events."""
     bws = torch.empty(ll.bwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.chunk), dtype=torch.uint8,
                       device=dev)
     dout = torch.randn((cfg.B, cfg.H, cfg.T, cfg.dv), device=dev, generator=torch.Generator(device=dev).manual_seed(5)
@@ -235,8 +235,8 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
         d = dsets[i % 3]
         ll.bwd(d["q"], d["k"], d["v"], d["a"], d["lam"], dout, chunk=cfg.chunk, workspace=bws)
 
-    bsteps = max(1, args.steps // 4)
-    for i in range(min(args.warmup, 2)):
+    bsteps = max(2, args.steps // 2)
+    for i in range(min(args.warmup, 3)):
         bstep(i)
     torch.cuda.synchronize()
     e0.record()
@@ -313,8 +313,8 @@ def measure_gdn(ll, torch, dev, args, e0, e1, bf16=False):
     def step():
         ll.gdn_fwd(d["q"], d["k"], d["v"], d["a"], d["beta"], d["lam"], chunk=cfg.chunk, out=out, workspace=ws)
 
-    n = max(1, args.steps // 4)
-    for _ in range(min(args.warmup, 2)):
+    n = max(2, args.steps // 2)
+    for _ in range(min(args.warmup, 3)):
         step()
     torch.cuda.synchronize()
     e0.record()
