@@ -382,7 +382,8 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     constexpr bool SST = BwSt<B>::SST;
     constexpr int HP = DK * DV / VEC;   // pieces of one state
     // pieces of one level's LDS copy: the state (W and W^T when both are kept)
-    constexpr int NSPT = ((BwDq<B>::on ? HP : 2 * HP) + B::NTC - 1) / B::NTC;
+    // (not used when dq is formed here)
+    constexpr int NSPT = BwDq<B>::on ? 1 : (2 * HP + B::NTC - 1) / B::NTC;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     // the next level's state pieces of the level loop (loaded one level ahead)
     u32x4 sp[NSPT];
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
     auto load_sp = [&](int mn) __attribute__((always_inline)) {
         const int nk = mn ? loop_kind(mn) : 0;
         const StatePtr sq = state_ptr(mn ? mn : 1, nk ? nk : 1);
-        const bool two = nk == 2 && !BwDq<B>::on;   // W and W^T
+        const bool two = nk == 2;   // W and W^T
         const __amdgpu_buffer_rsrc_t r1 = bw_rsrc(sq.p1, nk ? HP * 16 : 0), r2 = bw_rsrc(sq.p2, two ? HP * 16 : 0);
 #pragma unroll
         for (int j = 0; j < NSPT; ++j) {
@@ -415,8 +416,8 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             }
         }
     };
-    if constexpr (SST)
-        load_sp(lmask ? __builtin_ctz(lmask) : 0);
+    if constexpr (SST && !BwDq<B>::on)
+        load_sp(lmask ? __builtin_ctz(lmask) : 0);   // (with dq formed here: in the level loop)
 #pragma unroll
     for (int j = 0; j < NQP; ++j) {
         const int i = tid + B::NTC * j;
@@ -679,30 +680,51 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
             load_k2(k2rest);   // in flight during the query-side levels
     }
     // the level loop: the query-side levels (and the key-side ones when
-    // they are not summed); with the state copy in LDS, each level's state
-    // was loaded one level ahead (the first one with the chunk)
+    // they are not summed).  With dq formed here, the block states are
+    // stored in the A-operand fragment order of the product below, and each
+    // wave reads its fragments straight into registers, one level ahead (no
+    // LDS copy, no barriers); otherwise, with the state copy in LDS, each
+    // level's state was loaded one level ahead (the first one with the
+    // chunk).
+    Frag dnx[FDQ ? B::KPW : 1][FDQ ? B::NUV : 1];
+    // loads level mn's fragments of this wave's dk tiles into dnx (mn = 0:
+    // none, zeros); fragment (dk tile dt, dv unit u) is 64 lanes x 16 bytes
+    auto load_df = [&](int mn) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = bw_rsrc(state_ptr(mn ? mn : 1, 1).p1, mn ? HP * 16 : 0);
+#pragma unroll
+        for (int j = 0; j < B::KPW; ++j)
+#pragma unroll
+            for (int u = 0; u < B::NUV; ++u)
+                dnx[j][u] = __builtin_bit_cast(
+                    Frag, __builtin_amdgcn_raw_buffer_load_b128(r, (((cg + B::NCG * j) * B::NUV + u) * 64 + lane) * 16,
+                                                                0, 0));
+    };
+    if constexpr (FDQ)
+        load_df(lmask ? __builtin_ctz(lmask) : 0);
     for (int m = 1; m <= mtop; ++m) {
         if (!((lmask >> m) & 1))
             continue;
         const int kind = loop_kind(m);
         const T *g1 = nullptr, *g2 = nullptr;   // the state in global memory (no LDS copy)
-        if constexpr (SST) {
+        Frag dcur[FDQ ? B::KPW : 1][FDQ ? B::NUV : 1];
+        if constexpr (FDQ) {
+#pragma unroll
+            for (int j = 0; j < B::KPW; ++j)
+#pragma unroll
+                for (int u = 0; u < B::NUV; ++u)
+                    dcur[j][u] = dnx[j][u];
+            const uint32_t above = lmask & ~((2u << m) - 1u);
+            load_df(above ? __builtin_ctz(above) : 0);
+        } else if constexpr (SST) {
             __syncthreads();   // the previous level's reads of the copy are done
             if (kind != 0) {
-                const int np = kind == 1 || FDQ ? HP : 2 * HP;
+                const int np = kind == 1 ? HP : 2 * HP;
 #pragma unroll
                 for (int j = 0; j < NSPT; ++j) {
                     const int i = tid + B::NTC * j;
                     if (i < np) {
                         T *dst;
-                        if (kind == 1 && FDQ) {
-                            // the block state as a row-major [dv][dk] tile: piece i is
-                            // fragment f = i / 64 (dv tile f / NUK, dk unit f % NUK), lane
-                            // i % 64 (dv row, 8 consecutive dk)
-                            const int f = i >> 6, l = i & 63;
-                            const int e = 16 * (f / B::NUK) + (l & 15), d0 = B::KB * (f % B::NUK) + VEC * (l >> 4);
-                            dst = sm.st + e * B::LW2 + d0;
-                        } else if (kind == 1) {
+                        if (kind == 1) {
                             dst = sm.st + (size_t)i * VEC;                       // fragment order
                         } else if (i < HP) {
                             const int e0 = i * VEC;
@@ -729,8 +751,8 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
         if (kind == 1 && FDQ) {
             if constexpr (FDQ) {
                 // query side -> dlambda level LOGC + m and dq.  Y^T = D dO^T: A = D
-                // (rows d, transpose reads of the [dv][dk] copy), B = dO (columns
-                // t); this wave takes query tile kt and dk tiles cg, cg + NCG, ...
+                // (rows d, the fragments read above), B = dO (columns t); this
+                // wave takes query tile kt and dk tiles cg, cg + NCG, ...
                 // dlambda_t = exp(A_t + off) q_t . Y_t; dq_t += lambda_t exp(A_t + off) Y_t.
                 const int t = 16 * kt + li;
                 const float fac = sm.lam[t][B::LOGC + m] * __expf(sm.Aloc[t] + sm.off[m]);
@@ -741,8 +763,7 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                     floatx4 Y = zero4();
 #pragma unroll
                     for (int u = 0; u < B::NUV; ++u)
-                        mma_unit(Y, tr_frag(sm.st, B::LW2, B::KB * u, 16 * dt, li, qd),
-                                 lds_frag(&sm.dOs[0][0], B::LV, t, B::KB * u, qd));
+                        mma_unit(Y, dcur[j][u], lds_frag(&sm.dOs[0][0], B::LV, t, B::KB * u, qd));
                     // Y[i] = (D dO^T)[d = 16 dt + 4 qd + i][t]
                     const floatx4 q4 = ld4(&sm.Qs[t][16 * dt + 4 * qd]);
 #pragma unroll
@@ -1685,6 +1706,9 @@ static hipError_t launch_bwd_t(const BwdArgs &A, const BwdPlan &P, hipStream_t s
     tree.tree_only = true;
     tree.tree_nat = A.bf16;
     if (g8) {
+        // block states and nodes in the A-operand fragment order of the
+        // chunk kernel's query-side product
+        tree.tree_yfrag = true;
         tree.tree_nodes = ws + P.off_tree + P.off_nd;
         tree.tree_gamc = reinterpret_cast<float *>(ws + P.off_tree + P.off_gamc);
     }

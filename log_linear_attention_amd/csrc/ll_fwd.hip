@@ -436,36 +436,37 @@ __global__ __launch_bounds__(F::NT, (F::TR && F::NW >= 4) ? 2 : 1) void ll_group
                 for (int u = 0; u < F::NUC; ++u)
                     mma_unit(S[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
             }
-        } else if constexpr (F::TR) {
+        } else if constexpr (F::TR && F::DV % 32 == 0) {
             // this chunk's own state X, then S = exp(gch) S + X; the Fenwick
             // node of chunk ci inside the group: X (ci even), X + exp(gch) X of
-            // the previous chunk (ci = 1 mod 4), S (ci = 3, chunks 0 .. 3)
+            // the previous chunk (ci = 1 mod 4), S (ci = 3, chunks 0 .. 3).
+            // Here the tiles are transposed (A = V^T, B = K): X[rt][r] is
+            // element (dk 16 rt + li, dv 16 w + 4 qd + r).
             floatx4 X[F::NDT];
 #pragma unroll
             for (int rt = 0; rt < F::NDT; ++rt) {
                 X[rt] = zero4();
 #pragma unroll
                 for (int u = 0; u < F::NUC; ++u)
-                    mma_unit(X[rt], kt_frag<F>(sm, rt, u, li, qd), vs[u]);
+                    mma_unit(X[rt], vs[u], kt_frag<F>(sm, rt, u, li, qd));
                 S[rt] = dec * S[rt] + X[rt];
             }
             const int cc = sg * G + ci;   // chunk index
             if (tid == 0)
                 GamC[(size_t)bh * N + cc] = gch;
             if (ci < G - 1 && cc < N - 1) {
-                // natural fragment order: fragment (dv tile w, dk unit rt / 2), lane
-                // li + 16 (2 (rt & 1) + qd / 2), elements 4 (qd & 1) ..
                 typename F::T *nd = Nd + ((size_t)bh * N + cc) * F::DK * F::DV;
 #pragma unroll
                 for (int rt = 0; rt < F::NDT; ++rt) {
                     floatx4 x = (ci & 1) == 0 ? X[rt] : (ci & 3) == 1 ? X[rt] + dec * Xp[rt] : S[rt];
-                    const int f = w * F::NUK + rt / 2;
-                    const int l = li + 16 * (2 * (rt & 1) + (qd >> 1));
+                    // the backward's A-operand order: fragment (dk tile rt, dv
+                    // unit w / 2), this lane, elements 4 (w & 1) ..
                     bf16x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         o[r] = (__bf16)x[r];
-                    *reinterpret_cast<bf16x4 *>(nd + (size_t)(f * 64 + l) * 8 + 4 * (qd & 1)) = o;
+                    *reinterpret_cast<bf16x4 *>(nd + ((size_t)(rt * (F::DV / 32) + (w >> 1)) * 64 + lane) * 8 +
+                                                4 * (w & 1)) = o;
                 }
             }
 #pragma unroll
@@ -477,11 +478,18 @@ __global__ __launch_bounds__(F::NT, (F::TR && F::NW >= 4) ? 2 : 1) void ll_group
     if (sg >= nL)
         return;   // the last group (node mode): not a tree leaf
     float *dst = Sg + ((size_t)bh * nL + sg) * F::DK * F::DV;
+    if (F::TR && Nd) {
+        // node mode: transposed tiles
 #pragma unroll
-    for (int rt = 0; rt < F::NDT; ++rt)
+        for (int rt = 0; rt < F::NDT; ++rt)
+            *reinterpret_cast<floatx4 *>(dst + (16 * rt + li) * F::DV + 16 * w + 4 * qd) = S[rt];
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            dst[(16 * rt + 4 * qd + r) * F::DV + 16 * w + li] = S[rt][r];
+        for (int rt = 0; rt < F::NDT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[(16 * rt + 4 * qd + r) * F::DV + 16 * w + li] = S[rt][r];
+    }
     if (tid == 0)
         Gam[(size_t)bh * nG + sg] = gsum;
 }
@@ -498,10 +506,11 @@ __global__ __launch_bounds__(F::NT, (F::TR && F::NW >= 4) ? 2 : 1) void ll_group
 // half) * left + right).  Every complete left child is staged in LDS in
 // fragment order and then written with 16-byte stores, and the tile total
 // goes out for the next launch.  A block J at level p is complete when it
-// ends at or before the last complete group: (J + 1) * 2^p <= nL.  NAT
-// selects the dk order of a fragment lane: the natural one (lane quad qd
-// holds dk 32u + 8qd ..; the specialised bf16 walk) or unit_row's (the other
-// walks).
+// ends at or before the last complete group: (J + 1) * 2^p <= nL.  MODE
+// selects the stored order: 1 the natural dk order of a fragment lane (lane
+// quad qd holds dk 32u + 8qd ..; the specialised bf16 walk), 0 unit_row's
+// (the other walks), 2 the backward's order (fragments over dv for each dk
+// column; see FwdArgs::tree_yfrag), gathered from the staged lanes.
 // ---------------------------------------------------------------------------
 template <class F>
 struct TreeGeom {
@@ -512,7 +521,7 @@ struct TreeGeom {
     static_assert(CHUNK == 16, "one fragment lane is 16 bytes");
 };
 
-template <class F, bool NAT>
+template <class F, int MODE>
 __global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
     const float *__restrict__ leaves, const float *__restrict__ gleaves, int nleaves, int lstride, int gstride,
     int p0, int nL, int nLeft, typename F::T *__restrict__ Dg, float *__restrict__ tot, float *__restrict__ gtot,
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
     int dd[TG::NE];
 #pragma unroll
     for (int h = 0; h < TG::NE; ++h)
-        dd[h] = F::KB * u + (NAT ? 8 * qd + r + 4 * h : unit_row(r + 4 * h, qd));
+        dd[h] = F::KB * u + (MODE != 0 ? 8 * qd + r + 4 * h : unit_row(r + 4 * h, qd));
     if (tid < 64)
         gsh[tid] = (base + tid < nleaves) ? gleaves[(size_t)bh * gstride + base + tid] : 0.f;
     float x[TG::NE][64];
@@ -595,9 +604,23 @@ __global__ __launch_bounds__(TreeGeom<F>::NTH) void ll_left_tree(
         size_t offp = offp0;
         for (int pp = p0; pp < p; ++pp)
             offp += ((nL >> pp) + 1) >> 1;
-        const int fv = ((cc >> 4) * F::NUK + u) * 64 + qd * 16 + (cc & 15);
-        *reinterpret_cast<uint4 *>(Dg + ((size_t)bh * nLeft + offp + (J >> 1)) * DKV + (size_t)fv * F::EPL) =
-            stage[idx];
+        T *blk = Dg + ((size_t)bh * nLeft + offp + (J >> 1)) * DKV;
+        if constexpr (MODE == 2) {
+            // piece (dk row d of this workgroup's eight, dv group pg): the
+            // eight dv rows 32u' + 16(k/4) + 4qd' + k%4 of dk column d
+            static_assert(F::EPL == 8 && F::DV % 32 == 0, "bf16 pieces over dv");
+            const int dl = cc / (F::DV / 8), pg = cc % (F::DV / 8), uv = pg >> 2, qv = pg & 3;
+            const int d = F::KB * u + 8 * qd + dl;
+            bf16x8 y;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                y[k] = st[((size_t)s * F::DV + 32 * uv + 16 * (k >> 2) + 4 * qv + (k & 3)) * F::EPL + dl];
+            const int fo = ((d >> 4) * (F::DV / 32) + uv) * 64 + (d & 15) + 16 * qv;
+            *reinterpret_cast<bf16x8 *>(blk + (size_t)fo * 8) = y;
+        } else {
+            const int fv = ((cc >> 4) * F::NUK + u) * 64 + qd * 16 + (cc & 15);
+            *reinterpret_cast<uint4 *>(blk + (size_t)fv * F::EPL) = stage[idx];
+        }
     }
 }
 
@@ -2221,6 +2244,10 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
         use_ws = A.tree_nat;
     if (nat_blocks)
         *nat_blocks = use_ws;
+    if (A.tree_yfrag && (!F::TR || F::DV % 32 != 0 || !A.tree_only || !A.tree_nat))
+        return hipErrorInvalidValue;   // the backward's fragment order: bf16, dv units of 32
+    if (A.tree_nodes && !A.tree_yfrag)
+        return hipErrorInvalidValue;   // nodes come only in the backward's fragment order
     if (P.nL > 0 || (A.tree_only && A.tree_nodes)) {
         ProfEvents pe = prof_events("ll_group_state");
         const bool nodes = A.tree_only && A.tree_nodes;
@@ -2248,12 +2275,15 @@ static hipError_t launch_fwd_t(const FwdArgs &A, const FwdPlan &P, hipStream_t s
             bool nat = false;
             if constexpr (F::TR) {
                 nat = use_ws;
-                if (nat)
-                    hipExtLaunchKernelGGL(ll_left_tree<F, true>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
+                if (nat && A.tree_yfrag)
+                    hipExtLaunchKernelGGL(ll_left_tree<F, (F::DV % 32 == 0) ? 2 : 1>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
+                                          nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg, tt, gtot[ping], ntiles);
+                else if (nat)
+                    hipExtLaunchKernelGGL(ll_left_tree<F, 1>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
                                           nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg, tt, gtot[ping], ntiles);
             }
             if (!nat)
-                hipExtLaunchKernelGGL(ll_left_tree<F, false>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
+                hipExtLaunchKernelGGL(ll_left_tree<F, 0>, tg, tb, 0, s, pe.start, pe.stop, 0, leaves, gleaves,
                                       nleaves, lstride, gstride, p0, P.nL, P.nLeft, Dg, tt, gtot[ping], ntiles);
             e = hipGetLastError();
             if (e != hipSuccess)

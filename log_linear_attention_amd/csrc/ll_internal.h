@@ -36,10 +36,15 @@ struct FwdArgs {
     // when tree_nat is set (bf16 only).
     bool tree_only = false;
     bool tree_nat = false;
+    // With tree_nat (bf16): the block states in the backward's fragment
+    // order instead: fragment (dk tile dt, dv unit u) of 64 lanes x 8
+    // elements, lane li + 16 qd holding dv rows 32u + 16(k/4) + 4qd + k%4
+    // (k = 0..7) of dk column 16 dt + li.  Required with tree_nodes.
+    bool tree_yfrag = false;
     // With tree_only, bf16 and groups of at most 8 chunks: also the Fenwick
     // nodes inside each group (the node of chunk e covers the 2^z chunks
     // ending at e, z its trailing one bits; bf16 [B*H][N][dk*dv] in the
-    // natural fragment order) and every chunk's total log-decay
+    // backward's fragment order) and every chunk's total log-decay
     // ([B*H][N] float32); every group, the last one included, is walked.
     void *tree_nodes = nullptr;
     float *tree_gamc = nullptr;
