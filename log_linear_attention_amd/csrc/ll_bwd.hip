@@ -699,8 +699,19 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                     Frag, __builtin_amdgcn_raw_buffer_load_b128(r, (((cg + B::NCG * j) * B::NUV + u) * 64 + lane) * 16,
                                                                 0, 0));
     };
-    if constexpr (FDQ)
+    // the same for every query-side level: this wave's dO fragments (B
+    // operand, query tile kt) and q rows of its dk tiles
+    Frag dof[FDQ ? B::NUV : 1];
+    floatx4 qrow[FDQ ? B::KPW : 1];
+    if constexpr (FDQ) {
         load_df(lmask ? __builtin_ctz(lmask) : 0);
+#pragma unroll
+        for (int u = 0; u < B::NUV; ++u)
+            dof[u] = lds_frag(&sm.dOs[0][0], B::LV, 16 * kt + li, B::KB * u, qd);
+#pragma unroll
+        for (int j = 0; j < B::KPW; ++j)
+            qrow[j] = ld4(&sm.Qs[16 * kt + li][16 * (cg + B::NCG * j) + 4 * qd]);
+    }
     for (int m = 1; m <= mtop; ++m) {
         if (!((lmask >> m) & 1))
             continue;
@@ -759,16 +770,14 @@ __global__ __launch_bounds__(B::NTC) void ll_bwd_chunk(
                 float xs = 0.f;
 #pragma unroll
                 for (int j = 0; j < B::KPW; ++j) {
-                    const int dt = cg + B::NCG * j;
                     floatx4 Y = zero4();
 #pragma unroll
                     for (int u = 0; u < B::NUV; ++u)
-                        mma_unit(Y, dcur[j][u], lds_frag(&sm.dOs[0][0], B::LV, t, B::KB * u, qd));
-                    // Y[i] = (D dO^T)[d = 16 dt + 4 qd + i][t]
-                    const floatx4 q4 = ld4(&sm.Qs[t][16 * dt + 4 * qd]);
+                        mma_unit(Y, dcur[j][u], dof[u]);
+                    // Y[i] = (D dO^T)[d = 16 (cg + NCG j) + 4 qd + i][t]
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        xs += Y[i] * q4[i];
+                        xs += Y[i] * qrow[j][i];
                     dQ[j] += fac * Y;
                 }
                 xs += __shfl_xor(xs, 16, 64);
