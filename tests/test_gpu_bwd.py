@@ -97,6 +97,17 @@ def test_bf16_bwd_head_dims(dk, dv):
     _case(cfg, 64)
 
 
+@pytest.mark.parametrize("dk,dv,chunk", [(32, 32, 32), (64, 128, 64), (128, 128, 32)])
+def test_bf16_bwd_head_dims_deep_tree(dk, dv, chunk):
+    # 94 or 47 chunks: groups of 8 chunks form a tree of three or four levels
+    # over groups, so the stored left block states of every level (and the
+    # nodes inside each group) are read in the product's fragment order for
+    # these head dims, not only the first level's
+    cfg = synth.FwdConfig("bf16_bwd_deep", 1, 2, 3000, dk, dv, chunk, "bf16", 0.05, 6600 + dk + dv + chunk)
+    announce(f"bwd bf16 deep tree dk={dk} dv={dv} chunk={chunk}")
+    _case(cfg, chunk)
+
+
 def test_bf16_bwd_16k_workload_sampled():
     """The 16K forward workload: sampled query and key rows against the
     oracle, and da at sampled positions against its windowed oracle."""
