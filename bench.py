@@ -51,6 +51,9 @@ FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_fused_fwd_bf16_T
 FUSED_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
                  for f in ("ll_fused.hip", "ll_device.h")]
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_decode_bf16_S64.txt")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ll_bwd_chunk_fwd_bf16_T16K.txt")
+BWD_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
+               for f in ("ll_bwd.hip", "ll_fwd.hip", "ll_device.h", "ll_internal.h")]
 DECODE_SOURCES = [os.path.join(ROOT, "log_linear_attention_amd", "csrc", f)
                   for f in ("ll_decode.hip", "ll_device.h", "ll_internal.h")]
 
@@ -266,7 +269,8 @@ def measure_backward(ll, torch, dev, cfg, dsets, args, e0, e1):
         "hbm_frac_whole_call": round(bbytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "dominant_kernel": dom,
         "roofline": {"bound": "hbm", "achieved": round(cbytes / (cms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(cbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES),
                      "kernel": "ll_bwd_chunk", "kernel_avg_ms": round(cms, 5), "algorithmic_bytes": cbytes},
     }
 
